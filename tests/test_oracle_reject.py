@@ -1,0 +1,394 @@
+"""Pins of the rejection-sampling oracle against what the pages and the
+mathematics fix (no GPU).
+
+(a) greedy verification emits exactly the target's own greedy stream;
+(b) the emitted tokens have the target's law (losslessness), empirically;
+(c) the mean number of emitted tokens per verify is (1 - a^{K+1}) / (1 - a);
+(d) on tiny inputs, brute-force enumeration of every draft and every
+    uniform cell reproduces the closed-form joint law exactly;
+plus the accept / residual rules of the pages' worked steps and the KV
+commit arithmetic of their exercise.
+"""
+
+import itertools
+import zlib
+
+import numpy as np
+import pytest
+
+from oracle import exact_law
+from oracle import reject as orj
+from synth import gen
+
+
+def _probs(logits, t=1.0):
+    # Test-side softmax used only to build inputs and closed-form laws.
+    z = np.asarray(logits, dtype=np.float64) / t
+    z = z - z.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+# --------------------------------------------------------------------------
+# Single rules, as the pages' worked steps state them.
+# --------------------------------------------------------------------------
+
+def _one(target, draft, d, u, t=1.0):
+    target = np.asarray(target, dtype=np.float64)[None]
+    draft = np.asarray(draft, dtype=np.float64)[None]
+    return orj.reject_sample(target, draft, np.asarray(d)[None],
+                             np.asarray(u, dtype=np.float64)[None], np.array([t]))
+
+
+def test_accept_rule_strict_less_and_u_zero():
+    # q = (0.75, 0.25), p = (0.25, 0.75): r(d=1) = 1/3.
+    lq = np.log([0.75, 0.25])
+    lp = np.log([0.25, 0.75])
+    tgt = np.stack([lq, lq])
+    drf = lp[None]
+    r = 0.25 / 0.75
+    assert _one(tgt, drf, [1], [0.0, 0.5])["num_accepted"][0] == 1      # u = 0 accepts
+    assert _one(tgt, drf, [1], [r - 1e-9, 0.5])["num_accepted"][0] == 1
+    assert _one(tgt, drf, [1], [r + 1e-9, 0.5])["num_accepted"][0] == 0
+    # q/p > 1 accepts for every u < 1.
+    assert _one(tgt, drf, [0], [1 - 2 ** -24, 0.5])["num_accepted"][0] == 1
+
+
+def test_accept_rule_rejects_at_equality():
+    # q(d) = 0 gives r = 0: u = 0 is not < 0, so the draft is rejected.
+    tgt = np.array([[0.0, -np.inf], [0.0, 0.0]])
+    drf = np.array([[0.0, 0.0]])
+    res = _one(tgt, drf, [1], [0.0, 0.5])
+    assert res["num_accepted"][0] == 0 and res["out_tokens"][0, 0] == 0
+
+
+def test_accept_when_draft_prob_zero():
+    # p(d) = 0 (draft logit -inf at d): always accepted, whatever u.
+    tgt = np.log(np.array([[0.5, 0.5], [0.5, 0.5]]))
+    drf = np.array([[0.0, -np.inf]])
+    res = _one(tgt, drf, [1], [0.999, 0.1])
+    assert res["num_accepted"][0] == 1 and res["out_tokens"][0, 0] == 1
+
+
+def test_residual_is_positive_part_of_q_minus_p():
+    # Rejection at position 1: the draw follows (q - p)_+ / Z.
+    q = np.array([0.1, 0.6, 0.3])
+    p = np.array([0.5, 0.2, 0.3])
+    tgt = np.log(np.stack([q, q]))
+    drf = np.log(p)[None]
+    w = np.maximum(0, q - p)  # (0, 0.4, 0): only token 1 can be drawn
+    for uk in (0.0, 0.3, 0.999):
+        res = _one(tgt, drf, [0], [0.99, uk])      # r = 0.2 < 0.99 rejects
+        assert res["num_accepted"][0] == 0
+        assert res["out_tokens"][0, 0] == 1
+        assert (res["out_tokens"][0, 1:] == -1).all()
+    assert w.sum() > 0
+
+
+def test_residual_zero_mass_falls_back_to_q():
+    # q == p on row 1 but the draft token is rejected by construction of u
+    # (r = 1 cannot reject; use r < 1 at row 1 while the residual of row 1
+    # is forced to zero by identical rows elsewhere is impossible in exact
+    # arithmetic), so exercise the fallback through the inverse-CDF helper.
+    w = np.zeros((1, 4))
+    q = np.array([[0.1, 0.2, 0.3, 0.4]])
+    ww = np.where(w.sum(-1, keepdims=True) == 0, q, w)
+    tok, _ = orj._inverse_cdf(ww, np.array([0.35]), 1e-5)
+    assert tok[0] == 2   # C = .1 .3 .6 1.0; first C > 0.35 is index 2
+
+
+def test_inverse_cdf_boundary_and_fallback():
+    w = np.array([[0.25, 0.0, 0.25, 0.5, 0.0]])
+    tok, _ = orj._inverse_cdf(w, np.array([0.0]), 1e-5)
+    assert tok[0] == 0
+    tok, _ = orj._inverse_cdf(w, np.array([0.25]), 1e-5)    # C(0) = .25 not > .25
+    assert tok[0] == 2                                      # skips zero-weight 1
+    tok, _ = orj._inverse_cdf(w, np.array([1.0]), 1e-5)     # no C > Z: fallback
+    assert tok[0] == 3                                      # last positive weight
+
+
+def test_bonus_token_when_all_accepted():
+    v = 5
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((3, v))
+    tgt = x
+    drf = x[:2]                                          # p == q: r = 1, all accepted
+    q3 = _probs(x[2])
+    c = np.cumsum(q3)
+    for uk in (0.05, 0.5, 0.97):
+        res = _one(tgt, drf, [1, 3], [0.9, 0.9, uk])
+        assert res["num_accepted"][0] == 2
+        assert list(res["out_tokens"][0, :2]) == [1, 3]
+        assert res["out_tokens"][0, 2] == int(np.argmax(c > uk))
+
+
+def test_first_rejection_discards_later_drafts():
+    v = 4
+    lq = np.log(np.array([0.7, 0.1, 0.1, 0.1]))
+    lp = np.log(np.array([0.1, 0.7, 0.1, 0.1]))
+    tgt = np.stack([lq, lq, lq, lq])
+    drf = np.stack([lq, lp, lq])
+    # d_1 accepted (p == q), d_2 = 1 has r = 1/7, u = 0.5 rejects; d_3 would be
+    # accepted but must be discarded.
+    res = _one(tgt, drf, [2, 1, 0], [0.9, 0.5, 0.0, 0.2])
+    assert res["num_accepted"][0] == 1
+    assert res["out_tokens"][0, 0] == 2
+    assert res["out_tokens"][0, 1] == 0      # residual (q-p)_+ = (0.6,0,0,0)
+    assert res["out_tokens"][0, 2] == -1 and res["out_tokens"][0, 3] == -1
+    assert v == 4
+
+
+def test_greedy_lowest_index_tie():
+    tgt = np.array([[[1.0, 3.0, 3.0, 0.0], [2.0, 2.0, 2.0, 2.0]]])
+    res = orj.reject_sample(tgt, None, np.array([[1]]), np.zeros((1, 2)), np.array([0.0]))
+    assert res["num_accepted"][0] == 1 and list(res["out_tokens"][0]) == [1, 0]
+    res = orj.reject_sample(tgt, None, np.array([[2]]), np.zeros((1, 2)), np.array([0.0]))
+    assert res["num_accepted"][0] == 0 and list(res["out_tokens"][0]) == [1, -1]
+
+
+def test_bf16_bits_are_widened_exactly():
+    x = np.array([1.0, -2.5, 3.140625, 1e-3], dtype=np.float32)
+    bits = gen.bf16_bits(x)
+    w = orj.widen(bits)
+    assert np.all(w == gen.bf16_to_f32(bits).astype(np.float64))
+    assert w[0] == 1.0 and w[1] == -2.5 and w[2] == 3.140625
+
+
+def test_commit_two_sequences_exercise():
+    # Sequence A accepts every draft, sequence B rejects at position 2
+    # ([AIE] exercise on the KV rollback simulator).
+    k, l0 = 4, np.array([100, 57])
+    v = 3
+    lq = np.log(np.array([0.6, 0.3, 0.1]))
+    lp = np.log(np.array([0.1, 0.3, 0.6]))
+    tgt = np.broadcast_to(lq, (2, k + 1, v)).copy()
+    drf = np.broadcast_to(lq, (2, k, v)).copy()
+    drf[1, 1] = lp                             # position 2 of B: q/p(d=2) = 1/6
+    d = np.array([[0, 1, 2, 0], [0, 2, 0, 0]])
+    u = np.array([[0.5] * 5, [0.5, 0.9, 0.5, 0.5, 0.5]])
+    res = orj.reject_sample(tgt, drf, d, u, np.array([1.0, 1.0]))
+    assert list(res["num_accepted"]) == [4, 1]
+    assert list(orj.commit_kv_len(l0, res["num_accepted"])) == [105, 59]
+
+
+# --------------------------------------------------------------------------
+# (d) brute force on tiny inputs against the closed-form joint law.
+# --------------------------------------------------------------------------
+
+def _brute_force_law(tgt, drf, t):
+    """Enumerate every draft tuple and every cell of the uniforms; weight each
+    oracle output by prob(draft tuple) * cell volume."""
+    q = _probs(tgt, t)
+    p = _probs(drf, t)
+    k1, v = q.shape
+    k = k1 - 1
+    # Candidate CDF edges of the final draw: every weight vector it can use.
+    edges = {0.0, 1.0}
+    for wv in [np.maximum(0, q[i] - p[i]) for i in range(k)] + [q[i] for i in range(k1)]:
+        if wv.sum() > 0:
+            edges.update((np.cumsum(wv) / wv.sum()).tolist())
+    edges = np.array(sorted(e for e in edges if 0.0 <= e <= 1.0))
+    uk_mid = 0.5 * (edges[1:] + edges[:-1])
+    uk_w = edges[1:] - edges[:-1]
+    keep = uk_w > 1e-15
+    uk_mid, uk_w = uk_mid[keep], uk_w[keep]
+
+    rows_d, rows_u, weights = [], [], []
+    for ds in itertools.product(range(v), repeat=k):
+        pw = np.prod([p[i, ds[i]] for i in range(k)])
+        if pw == 0:
+            continue
+        cells = []
+        for i in range(k):
+            r = min(1.0, q[i, ds[i]] / p[i, ds[i]])
+            cells.append([(r / 2, r), ((1 + r) / 2, 1 - r)])
+        for choice in itertools.product(*cells):
+            vol = np.prod([c[1] for c in choice])
+            if vol <= 0:
+                continue
+            for um, uw in zip(uk_mid, uk_w):
+                rows_d.append(ds)
+                rows_u.append([c[0] for c in choice] + [um])
+                weights.append(pw * vol * uw)
+    n_rows = len(rows_d)
+    res = orj.reject_sample(np.broadcast_to(tgt, (n_rows,) + tgt.shape),
+                            np.broadcast_to(drf, (n_rows,) + drf.shape),
+                            np.array(rows_d), np.array(rows_u),
+                            np.full(n_rows, t))
+    law = {}
+    for j in range(n_rows):
+        m = int(res["num_accepted"][j])
+        toks = res["out_tokens"][j]
+        key = (m, tuple(int(x) for x in toks[:m]), int(toks[m]))
+        law[key] = law.get(key, 0.0) + weights[j]
+    return law, q, p
+
+
+@pytest.mark.parametrize("seed,v,k,t", [(1, 3, 2, 1.0), (2, 4, 2, 0.7), (3, 3, 3, 1.3),
+                                        (4, 2, 3, 1.0), (5, 4, 1, 2.0)])
+def test_brute_force_matches_closed_form(seed, v, k, t):
+    rng = np.random.default_rng(seed)
+    tgt = rng.standard_normal((k + 1, v)) * 1.5
+    drf = tgt[:k] + rng.standard_normal((k, v)) * 0.8
+    law, q, p = _brute_force_law(tgt, drf, t)
+    ref = exact_law.joint_law(q, p)
+    keys = set(law) | set(ref)
+    err = max(abs(law.get(key, 0.0) - ref.get(key, 0.0)) for key in keys)
+    assert err < 1e-12
+    assert abs(sum(ref.values()) - 1.0) < 1e-12
+    # Losslessness of the closed form itself: first token ~ q_1.
+    assert np.max(np.abs(exact_law.first_token_law(ref, v) - q[0])) < 1e-12
+
+
+def test_brute_force_special_cases():
+    rng = np.random.default_rng(11)
+    v, k = 3, 2
+    tgt = rng.standard_normal((k + 1, v))
+    # p == q: every draft accepted, bonus from q_{K+1}.
+    law, q, _ = _brute_force_law(tgt, tgt[:k].copy(), 1.0)
+    assert all(m == k for (m, _, _) in law)
+    bonus = np.zeros(v)
+    for (m, ds, y), pr in law.items():
+        bonus[y] += pr
+    assert np.max(np.abs(bonus - q[k])) < 1e-12
+    # Disjoint supports: nothing accepted, first token ~ q_1.
+    tgt2 = np.array([[0.0, 0.5, -np.inf], [0.0, 0.5, -np.inf], [1.0, 0.0, 0.0]])
+    drf2 = np.array([[-np.inf, -np.inf, 0.0], [-np.inf, -np.inf, 0.0]])
+    law2, q2, _ = _brute_force_law(tgt2, drf2, 1.0)
+    assert all(m == 0 for (m, _, _) in law2)
+    first = np.zeros(v)
+    for (m, ds, y), pr in law2.items():
+        first[y] += pr
+    assert np.max(np.abs(first - q2[0])) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# (b) losslessness, empirically: TV < 0.005 over 1e6 trials at V = 32.
+# --------------------------------------------------------------------------
+
+def test_losslessness_tv_1e6_trials():
+    k, v, trials, chunk = 4, 32, 1_000_000, 100_000
+    inp = gen.make_reject_inputs(seed=900, B=trials, K=k, V=v, dtype="f32",
+                                 logit_std=1.0, draft_sigma=0.5,
+                                 temperature=1.0, shared_rows=True)
+    q = _probs(inp["target"][0])
+    p = _probs(inp["draft"][0])
+    counts = np.zeros((k + 1, v))
+    present = np.zeros(k + 1)
+    n_hist = np.zeros(k + 1)
+    for c0 in range(0, trials, chunk):
+        sl = slice(c0, c0 + chunk)
+        res = orj.reject_sample(inp["target"][sl], inp["draft"][sl],
+                                inp["draft_tokens"][sl], inp["uniforms"][sl],
+                                inp["temperature"][sl])
+        out = res["out_tokens"]
+        for s in range(k + 1):
+            m = out[:, s] >= 0
+            present[s] += m.sum()
+            counts[s] += np.bincount(out[m, s], minlength=v)
+        n_hist += np.bincount(res["num_accepted"], minlength=k + 1)
+    # Slot 0 has exactly the law q_1; slot s, when present, has law q_{s+1}.
+    tv0 = 0.5 * np.abs(counts[0] / present[0] - q[0]).sum()
+    assert tv0 < 0.005, tv0
+    for s in range(1, k + 1):
+        frac = present[s] / trials
+        tv = 0.5 * np.abs(counts[s] / present[s] - q[s]).sum()
+        assert tv < 0.005 / np.sqrt(frac), (s, tv)
+    # P(n >= i) = prod_{j<=i} alpha_j.
+    alpha = np.minimum(p, q[:k]).sum(axis=-1)
+    tail = np.cumsum(n_hist[::-1])[::-1] / trials
+    for i in range(1, k + 1):
+        expect = np.prod(alpha[:i])
+        assert abs(tail[i] - expect) < 5 * np.sqrt(expect * (1 - expect) / trials) + 1e-4
+
+
+# --------------------------------------------------------------------------
+# (c) mean emitted tokens per verify = (1 - a^{K+1}) / (1 - a), within 1%.
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("alpha,k", [(0.6, 4), (0.8, 7), (0.9, 5), (0.5, 2)])
+def test_mean_emitted_closed_form(alpha, k):
+    v, trials = 16, 100_000
+    rng = np.random.default_rng(int(alpha * 100) + k)
+    # p = alpha * q + (1 - alpha) * s with q, s on disjoint supports: then
+    # sum_v min(p, q) = alpha exactly at every position.
+    q = np.zeros((k + 1, v))
+    s = np.zeros((k, v))
+    for i in range(k + 1):
+        q[i, :8] = rng.dirichlet(np.ones(8))
+    for i in range(k):
+        s[i, 8:] = rng.dirichlet(np.ones(8))
+    p = alpha * q[:k] + (1 - alpha) * s
+    with np.errstate(divide="ignore"):
+        tl, dl = np.log(q), np.log(p)
+    assert np.allclose(np.minimum(p, q[:k]).sum(-1), alpha, atol=1e-15)
+    d = np.empty((trials, k), dtype=np.int64)
+    for i in range(k):
+        d[:, i] = rng.choice(v, size=trials, p=p[i])
+    u = gen.uniforms24(rng, (trials, k + 1)).astype(np.float64)
+    res = orj.reject_sample(np.broadcast_to(tl, (trials, k + 1, v)),
+                            np.broadcast_to(dl, (trials, k, v)), d, u,
+                            np.ones(trials))
+    mean = (res["num_accepted"] + 1).mean()
+    expect = exact_law.expected_emitted(alpha, k)
+    assert abs(mean / expect - 1) < 0.01, (mean, expect)
+    # Per-position acceptance a_i = P(n >= i) = alpha^i.
+    for i in range(1, k + 1):
+        a_i = (res["num_accepted"] >= i).mean()
+        assert abs(a_i - alpha ** i) < 5 * np.sqrt(alpha ** i / trials) + 2e-3
+
+
+def test_expected_emitted_geometric_sum():
+    for a in (0.3, 0.8, 0.95):
+        for k in range(0, 9):
+            assert abs(exact_law.expected_emitted(a, k) - sum(a ** i for i in range(k + 1))) < 1e-12
+    assert exact_law.expected_emitted(1.0, 7) == 8.0
+
+
+# --------------------------------------------------------------------------
+# (a) greedy verification == the target's own greedy decoding, multi-step.
+# --------------------------------------------------------------------------
+
+V_TOY = 32
+
+
+def _toy_logits(prefix, salt):
+    """A context-dependent toy 'model': logits seeded by a hash of the prefix,
+    rounded to bf16 and coarsened so that ties occur."""
+    h = zlib.crc32(np.asarray(prefix, dtype=np.int64).tobytes() + salt)
+    x = np.random.default_rng(h).standard_normal(V_TOY).astype(np.float32)
+    x = np.round(x * 2) / 2
+    return gen.bf16_to_f32(gen.bf16_bits(x))
+
+
+def _target(prefix):
+    return _toy_logits(prefix, b"target")
+
+
+def _draft(prefix):
+    t = _target(prefix).astype(np.float64)
+    noise = np.random.default_rng(zlib.crc32(np.asarray(prefix).tobytes() + b"n")).standard_normal(V_TOY)
+    return (t + 0.8 * noise).astype(np.float32)
+
+
+@pytest.mark.parametrize("k", [1, 4, 7])
+def test_greedy_equals_target_only_decoding(k):
+    prompt = [3, 1, 4]
+    n_tokens = 200
+    plain = list(prompt)
+    while len(plain) < len(prompt) + n_tokens:
+        plain.append(int(np.argmax(_target(plain))))
+    seq = list(prompt)
+    calls = 0
+    while len(seq) < len(prompt) + n_tokens:
+        drafts = []
+        for _ in range(k):
+            drafts.append(int(np.argmax(_draft(seq + drafts))))
+        tgt = np.stack([_target(seq + drafts[:i]) for i in range(k + 1)])[None]
+        res = orj.reject_sample(gen.bf16_bits(tgt), None, np.array([drafts]),
+                                np.zeros((1, k + 1)), np.array([0.0]))
+        n = int(res["num_accepted"][0])
+        seq.extend(int(x) for x in res["out_tokens"][0, :n + 1])
+        calls += 1
+    assert seq[:len(plain)] == plain
+    assert calls < n_tokens       # some drafts were accepted
