@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Throughput of the speculative-decoding verify step on one MI355X.
+
+One step = spec_verify_attn (one attention layer over the paged KV cache)
+followed by spec_reject_sample (full-vocabulary verifier + KV commit) for one
+batch.  Default workload: the Llama-3-8B-shaped serving batch (B=64, K=7,
+V=128256, 32 q / 8 kv heads, D=128, contexts U[2048, 8192], bf16, T=1,
+draft noise giving alpha ~ 0.8).
+
+Inputs are resident in device memory before the timed region.  Three logit
+sets rotate between steps (the logits of one set, 246 MB, are about the size
+of the 256 MB Infinity Cache); every step gets its own pre-copied kv_len
+buffer, because the verifier commits into it.
+
+Prints one JSON line.  ``value`` = committed tokens per second: the sum over
+sequences of (accepted drafts + 1) per step, divided by the wall time of the
+timed steps.  ``roofline`` is for the dominant kernel (the attention call),
+from HIP events on the launch stream; ``cpu_baseline`` times the float64
+oracle on a bounded sample of the same workload on the host cores.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified tokens/sec at batch 64, K=7, V=128256; % of peak HBM GB/s"
+PEAK_HBM_GBS = 8000.0
+
+
+def _file_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(kernel_src, launches_bytes):
+    """HBM traffic per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "attn_llama8b_b64_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != _file_hash(kernel_src):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="llama8b_b64")
+    p.add_argument("--temp", type=float, default=1.0)
+    p.add_argument("--seed", type=int, default=2024)
+    p.add_argument("--cpu-sample", type=int, default=12,
+                   help="sequences in the oracle's timed sample (0 disables)")
+    p.add_argument("--sets", type=int, default=3, help="rotating logit sets")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the verify step here runs on a single "
+              "MI355X (no collectives); --gpus %d is not supported." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import speculative_decoding_verification_verify_amd as sv
+    from synth import CONFIGS, gen
+    from synth.device import to_device, from_device, make_attn_inputs_device
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    sv.load()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    cfg = CONFIGS[args.config]
+    B, K, V = cfg.B, cfg.K, cfg.V
+    K1 = K + 1
+    print("bench: %s B=%d K=%d V=%d T=%.2f steps=%d warmup=%d" %
+          (cfg.name, B, K, V, args.temp, args.steps, args.warmup), file=sys.stderr, flush=True)
+
+    # ---- inputs, resident before timing ---------------------------------
+    attn = make_attn_inputs_device(args.seed, B, K, cfg.Hq, cfg.Hkv, cfg.D, cfg.ctx, dev)
+    kv0 = attn["kv_len"]
+    max_kv = int(from_device(kv0).max())
+    rsets = []
+    for j in range(args.sets):
+        inp = gen.make_reject_inputs(seed=args.seed + 1 + j, B=B, K=K, V=V,
+                                     dtype=cfg.logit_dtype, logit_std=cfg.logit_std,
+                                     draft_sigma=cfg.draft_sigma, temperature=args.temp)
+        rsets.append({"host": inp, "dev": {k: to_device(v, dev) for k, v in inp.items()}})
+    n_total = args.warmup + args.steps
+    kv_bufs = [kv0.clone() for _ in range(n_total)]
+    attn_out = torch.empty_like(attn["q"])
+    attn_ws = torch.empty(max(256, sv.verify_attn_workspace_bytes(B, K, cfg.Hq, cfg.Hkv, cfg.D,
+                                                                  max_kv)),
+                          dtype=torch.uint8, device=dev)
+    rej_ws = torch.empty(sv.reject_sample_workspace_bytes(B, K, V), dtype=torch.uint8, device=dev)
+    out_tok = [torch.empty((B, K1), dtype=torch.int32, device=dev) for _ in range(args.sets)]
+    n_acc = [torch.empty((B,), dtype=torch.int32, device=dev) for _ in range(args.sets)]
+    torch.cuda.synchronize()
+
+    def step(s):
+        r = rsets[s % args.sets]["dev"]
+        sv.verify_attn(attn["q"], attn["k_cache"], attn["v_cache"], attn["block_table"], kv0,
+                       out=attn_out, max_kv_len=max_kv, workspace=attn_ws)
+        mid = torch.cuda.Event(enable_timing=True)
+        mid.record()
+        sv.reject_sample(r["target"], r["draft"], r["draft_tokens"], r["uniforms"],
+                         r["temperature"], kv_bufs[s], out_tokens=out_tok[s % args.sets],
+                         num_accepted=n_acc[s % args.sets], workspace=rej_ws)
+        return mid
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    emitted = [int(from_device(n_acc[j]).astype(np.int64).sum()) + B for j in range(args.sets)]
+
+    # ---- timed region ----------------------------------------------------
+    starts, mids, ends = [], [], []
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for s in range(args.warmup, n_total):
+        a = torch.cuda.Event(enable_timing=True)
+        a.record()
+        m = step(s)
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        starts.append(a), mids.append(m), ends.append(e)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    attn_ms = np.array([a.elapsed_time(m) for a, m in zip(starts, mids)])
+    rej_ms = np.array([m.elapsed_time(e) for m, e in zip(mids, ends)])
+    tokens = sum(emitted[s % args.sets] for s in range(args.warmup, n_total))
+    value = tokens / (total_ms / 1e3)
+
+    # Committed lengths must be L0 + n + 1 for the last step's set.
+    last = n_total - 1
+    assert np.array_equal(from_device(kv_bufs[last]),
+                          from_device(kv0) + from_device(n_acc[last % args.sets]) + 1)
+
+    # ---- roofline of the attention call (dominant kernel) ----------------
+    kvl = from_device(kv0).astype(np.int64)
+    kv_bytes = int((kvl + K1).sum()) * cfg.Hkv * cfg.D * 2 * 2
+    qo_bytes = B * K1 * cfg.Hq * cfg.D * 2 * 2
+    attn_bytes = kv_bytes + qo_bytes
+    attn_us = float(attn_ms.mean() * 1e3)
+    achieved = attn_bytes / (attn_us * 1e-6) / 1e9
+    attn_src = os.path.join(ROOT, "speculative_decoding_verification_verify_amd", "csrc",
+                            "verify_attn.hip")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": _traffic(attn_src, attn_bytes),
+                "kernel": "spec_verify_attn (k_attn_mfma + k_attn_combine)",
+                "algorithmic_bytes": attn_bytes, "avg_us": round(attn_us, 2)}
+    rej_bytes = B * (2 * K + 1) * V * 2 if args.temp > 0 else B * K1 * V * 2
+    rej_us = float(rej_ms.mean() * 1e3)
+    rej_gbs = rej_bytes / (rej_us * 1e-6) / 1e9
+
+    # ---- CPU baseline: the oracle on a bounded sample ---------------------
+    cpu = None
+    if args.cpu_sample > 0:
+        cpu = cpu_baseline(args, cfg, attn, rsets[0]["host"], from_device)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: B=%d K=%d V=%d, %dq/%dkv heads D=%d, ctx U[%d,%d], "
+                               "bf16 logits N(0,2), draft sigma %.2f, T=%.2f" %
+                               (cfg.name, B, K, V, cfg.Hq, cfg.Hkv, cfg.D, cfg.ctx[0], cfg.ctx[1],
+                                cfg.draft_sigma, args.temp),
+                   "global_batch": B, "K": K, "V": V, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": {
+            "attn": {"avg_us": round(attn_us, 2), "gbs": round(achieved, 1),
+                     "frac_hbm": round(achieved / PEAK_HBM_GBS, 4), "bytes": attn_bytes},
+            "reject": {"avg_us": round(rej_us, 2), "gbs": round(rej_gbs, 1),
+                       "frac_hbm": round(rej_gbs / PEAK_HBM_GBS, 4), "bytes": rej_bytes},
+        },
+        "tokens_per_step": round(tokens / args.steps, 2),
+        "positions_per_s": round(B * K1 * args.steps / (total_ms / 1e3), 1),
+        "mean_accept_len": round(tokens / args.steps / B, 4),
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(args, cfg, attn, host_rej, from_device):
+    """Time the oracle (as it stands) on the first ``cpu_sample`` sequences."""
+    import torch
+    from oracle import attention as oat
+    from oracle import reject as orj
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    n = min(args.cpu_sample, cfg.B)
+    idx = np.arange(n)
+    kvl = from_device(attn["kv_len"])[:n]
+    bt = from_device(attn["block_table"])[:n]
+    pages = np.unique(np.concatenate([bt[b, :(kvl[b] + cfg.K + 1 + 15) // 16] for b in range(n)]))
+    remap = np.zeros(int(pages.max()) + 1, dtype=np.int32)
+    remap[pages] = np.arange(len(pages), dtype=np.int32)
+    sel = torch.from_numpy(pages).long().to(attn["k_cache"].device)
+    kc = from_device(attn["k_cache"][sel])
+    vc = from_device(attn["v_cache"][sel])
+    q = from_device(attn["q"][:n])
+    bt_local = np.zeros_like(bt)
+    for b in range(n):
+        m = (kvl[b] + cfg.K + 1 + 15) // 16
+        bt_local[b, :m] = remap[bt[b, :m]]
+    t0 = time.perf_counter()
+    oat.verify_attention(q, kc, vc, bt_local, kvl)
+    t_attn = time.perf_counter() - t0
+    h = host_rej
+    t0 = time.perf_counter()
+    res = orj.reject_sample(h["target"][idx], h["draft"][idx], h["draft_tokens"][idx],
+                            h["uniforms"][idx], h["temperature"][idx])
+    t_rej = time.perf_counter() - t0
+    tokens = int(res["num_accepted"].astype(np.int64).sum()) + n
+    return {"value": round(tokens / (t_attn + t_rej), 2), "unit": "tokens/s",
+            "cores": int(blas_threads), "kind": "oracle",
+            "sample": "first %d of %d sequences of the same workload: float64 numpy oracle, "
+                      "attention %.2f s + reject %.2f s" % (n, cfg.B, t_attn, t_rej),
+            "host_cores_available": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

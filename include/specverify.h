@@ -1,0 +1,161 @@
+/*
+ * specverify.h -- C ABI of the speculative-decoding verify step for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Two calls make one verify step:
+ *
+ *   spec_verify_attn    grouped-query attention of the K+1 verifier query
+ *                       positions (the last accepted token x0 and the drafts
+ *                       d_1..d_K) over a paged KV cache, causal inside the
+ *                       draft window.  The verifier checks every draft in
+ *                       one forward pass over prefix + drafts (AI
+ *                       Engineering from Scratch, "Speculative decoding and
+ *                       EAGLE-3", section "Concept"; devpost "phoenix",
+ *                       "What it does").
+ *
+ *   spec_reject_sample  the lossless rejection-sampling verifier over the
+ *                       full vocabulary, then the commit of each sequence's
+ *                       logical KV length (same lesson: "Concept", "Rolling
+ *                       back the KV cache", "Build it" steps 1-4;
+ *                       quickscale.ai "Quand et pourquoi utiliser le
+ *                       speculative decoding", section 2).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is device memory owned by the caller.  The
+ *    library allocates nothing, frees nothing and keeps no mutable global
+ *    state; scratch memory is the caller's workspace.
+ *  - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the
+ *    default stream).  Argument errors are detected on the host and
+ *    returned before anything is launched.  A failed launch returns
+ *    SV_ERR_HIP.  Device faults surface at the caller's next
+ *    synchronisation.
+ *  - Return value: SV_OK (0) or a negative sv_status.
+ *  - dtype: SV_F32 or SV_BF16 (bf16 carried as 16-bit patterns).  All
+ *    floating tensors of one call share the dtype.
+ *  - Out-of-range indices in the inputs (block ids, draft tokens) never
+ *    make the kernels read outside the buffers described here: they are
+ *    clamped, and the results for such inputs are unspecified.
+ */
+#ifndef SPECVERIFY_H_
+#define SPECVERIFY_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SV_OK = 0,
+  SV_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad enum       */
+  SV_ERR_UNSUPPORTED = -2, /* a shape outside the supported set          */
+  SV_ERR_WORKSPACE = -3,   /* workspace smaller than the *_workspace_bytes */
+  SV_ERR_HIP = -4          /* a HIP runtime call or launch failed         */
+} sv_status;
+
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+#define SV_BLOCK_SIZE 16 /* tokens per KV page */
+#define SV_MAX_K 16      /* largest draft length accepted */
+
+/*
+ * spec_verify_attn -- window-causal GQA of the K+1 verify positions.
+ *
+ * For sequence b with committed length L0 = kv_len[b], query position
+ * i in [0, K] sits at absolute position t = L0 + i and attends keys
+ * j in [0, t].  Query head h reads KV head g = h / (Hq / Hkv).
+ * out = softmax(scale * q k^T) v, softmax in fp32.  The caller has already
+ * written the window's own K/V (positions L0..L0+K) into the cache.
+ *
+ * Layouts (row-major, contiguous):
+ *   q, out       [B, K+1, Hq, D]
+ *   k_cache      [num_blocks, Hkv, D/X, 16, X]   X = 16 bytes / element
+ *                (8 for bf16, 4 for fp32): 16-byte chunks of one key's
+ *                head vector, the 16 tokens of a page side by side
+ *   v_cache      [num_blocks, Hkv, D, 16]        one value coordinate of
+ *                the 16 tokens of a page side by side
+ *   block_table  [B, max_blocks_per_seq] int32: token j of sequence b is
+ *                slot j % 16 of page block_table[b][j / 16]
+ *   kv_len       [B] int32, L0 per sequence (read only here)
+ *
+ * Sizes: 1 <= K <= SV_MAX_K; D in {64, 128}; block_size == 16;
+ *   Hq % Hkv == 0 and (Hq / Hkv) * (K + 1) <= 64; B >= 0 (B == 0 is a
+ *   no-op); kv_len[b] + K + 1 <= min(max_kv_len + K + 1,
+ *   16 * max_blocks_per_seq) for every b.
+ * scale <= 0 selects 1 / sqrt(D).
+ * workspace: at least spec_verify_attn_workspace_bytes(...) bytes of device
+ *   memory (any content; 256-byte aligned), or NULL when that size is 0.
+ */
+int spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_table, const int32_t* kv_len,
+                     void* out, int B, int K, int Hq, int Hkv, int D,
+                     int block_size, int num_blocks, int max_blocks_per_seq,
+                     int max_kv_len, float scale, int dtype, void* workspace,
+                     size_t workspace_bytes, void* hip_stream);
+
+size_t spec_verify_attn_workspace_bytes(int B, int K, int Hq, int Hkv, int D,
+                                        int max_kv_len);
+
+/*
+ * spec_reject_sample -- lossless verifier over the full vocabulary plus the
+ * KV-length commit.
+ *
+ * Rows: target row i (i = 0..K) is q_{i+1}, the verifier's distribution
+ * after x0, d_1..d_i; draft row i (i = 0..K-1) is p_{i+1}, the law d_{i+1}
+ * was drawn from.  Both share one vocabulary of size V.
+ *
+ * Sampling (temperature[b] > 0): q = softmax(target / T), p =
+ * softmax(draft / T).  d_i is accepted iff p_i(d_i) == 0 or
+ * u[i-1] < min(1, q_i(d_i) / p_i(d_i)); n = the number of leading accepts.
+ * If n < K the emitted token is drawn from (q_{n+1} - p_{n+1})_+ (from
+ * q_{n+1} if that has zero mass); if n == K from q_{K+1} (bonus).  The draw
+ * is the smallest v with C(v) > u[K] * Z, C the inclusive prefix sum of the
+ * weights and Z their total (the largest positive-weight v if rounding
+ * leaves none).
+ * Greedy (temperature[b] <= 0, or draft_logits == NULL): d_i is accepted iff
+ * it equals argmax(target row i-1) (lowest index on ties); the emitted
+ * token is argmax(target row n).  Draft logits are not read.
+ *
+ * Outputs: out_tokens[b] = d_1..d_n, the emitted token, then -1;
+ * num_accepted[b] = n; kv_len[b] += n + 1 (x0 plus the accepted drafts stay,
+ * the K - n rejected slots are rolled back).  The call is therefore NOT
+ * idempotent: retrying it needs kv_len restored first.
+ * counters (optional, NULL to skip): counters[0] += K and
+ * counters[1] += n for every sequence (proposed / accepted drafts).
+ *
+ * Layouts (row-major, contiguous):
+ *   target_logits [B, K+1, V]; draft_logits [B, K, V] (dtype)
+ *   draft_tokens  [B, K] int32 in [0, V)
+ *   uniforms      [B, K+1] float32 in [0, 1)
+ *   temperature   [B] float32
+ *   out_tokens    [B, K+1] int32; num_accepted [B] int32; kv_len [B] int32
+ * Preconditions: every row holds at least one finite logit and no NaN or
+ * +inf; -inf logits are allowed (probability 0).
+ * Sizes: 1 <= K <= SV_MAX_K; 1 <= V < 2^31 / 4; B >= 0 (B == 0 is a no-op);
+ *   B * (2K+1) < 2^31.
+ * workspace: at least spec_reject_sample_workspace_bytes(B, K, V) bytes of
+ *   device memory (any content; 256-byte aligned).
+ */
+int spec_reject_sample(const void* target_logits, const void* draft_logits,
+                       const int32_t* draft_tokens, const float* uniforms,
+                       const float* temperature, int32_t* out_tokens,
+                       int32_t* num_accepted, int32_t* kv_len,
+                       unsigned long long* counters, int B, int K, int V,
+                       int dtype, void* workspace, size_t workspace_bytes,
+                       void* hip_stream);
+
+size_t spec_reject_sample_workspace_bytes(int B, int K, int V);
+
+/* Static description of a status code. */
+const char* spec_status_string(int status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int spec_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H_ */

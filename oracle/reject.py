@@ -42,9 +42,12 @@ Readings where the pages are silent (each also listed in the design notes):
 
 Boundary flags (parity bands, reported, never used to decide):
   F1  some examined accept test (positions 1..min(n+1, K)) has
-      |u_{i-1} - q_i(d_i)/p_i(d_i)| < eps;
-  F2  the final draw's target u_K * Z lies within eps (probability mass)
-      of C(t-1) or C(t) for the chosen token t.
+      |u_{i-1} - q_i(d_i)/p_i(d_i)| < eps_accept (1e-5);
+  F2  the final draw's target u_K * Z lies within eps_sample (1e-10
+      probability mass) of C(t-1) or C(t) for the chosen token t.  Adjacent
+      CDF edges of a 128K-entry vocabulary are ~1e-5 apart, so this band has
+      to be far narrower than F1's; it is sized for an implementation that
+      computes the final draw's weights and sums in float64.
 """
 
 import numpy as np
@@ -124,7 +127,7 @@ def _inverse_cdf(w, u, eps):
 
 
 def reject_sample(target_logits, draft_logits, draft_tokens, uniforms,
-                  temperature, eps=1e-5):
+                  temperature, eps_accept=1e-5, eps_sample=1e-10):
     """One verify call for a batch of sequences.
 
     Args:
@@ -134,7 +137,8 @@ def reject_sample(target_logits, draft_logits, draft_tokens, uniforms,
       uniforms:      [B, K+1] in [0, 1): u[:, :K] accept tests, u[:, K]
                      the residual or bonus draw.
       temperature:   [B]; T_b <= 0 selects greedy for sequence b.
-      eps:           half-width of the parity bands F1 / F2.
+      eps_accept:    half-width of the F1 band (on u - q/p).
+      eps_sample:    half-width of the F2 band (probability mass).
 
     Returns a dict with
       out_tokens   [B, K+1] int32, -1 padded
@@ -187,7 +191,7 @@ def reject_sample(target_logits, draft_logits, draft_tokens, uniforms,
 
         # F1: accept tests actually examined are positions 1..min(n+1, K).
         examined = np.arange(k)[None, :] <= np.minimum(n, k - 1)[:, None]
-        f1[si] = (examined & (np.abs(u[si, :k] - r) < eps)).any(axis=-1)
+        f1[si] = (examined & (np.abs(u[si, :k] - r) < eps_accept)).any(axis=-1)
 
         # Residual (n < K) or bonus (n == K) weights.
         q_row = q[rows, n]                                  # q_{n+1}
@@ -196,7 +200,7 @@ def reject_sample(target_logits, draft_logits, draft_tokens, uniforms,
         w = np.where((n < k)[:, None], resid, q_row)
         zero_mass = w.sum(axis=-1) == 0
         w = np.where(zero_mass[:, None], q_row, w)          # [AIE] step 2 fallback
-        tok, flag = _inverse_cdf(w, u[si, k], eps)
+        tok, flag = _inverse_cdf(w, u[si, k], eps_sample)
         f2[si] = flag
         n_acc[si] = n
         ratio[si] = r

@@ -1,0 +1,199 @@
+"""Speculative-decoding verify step on AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libspecverify.so`` (C ABI declared in
+``include/specverify.h``).  The functions here only marshal arguments:
+torch tensors provide device pointers and the current HIP stream, every step
+of the verify path runs in the library's HIP kernels.  There is no fallback:
+if the library is missing, :func:`load` raises.
+
+    verify_attn(q, k_cache, v_cache, block_table, kv_len, ...)
+        window-causal GQA of the K+1 verify positions over a paged KV cache
+    reject_sample(target, draft, draft_tokens, uniforms, temperature, kv_len, ...)
+        lossless verifier over the full vocabulary + KV-length commit
+"""
+
+import ctypes
+import os
+
+__all__ = ["load", "lib_path", "exported_symbols", "verify_attn", "reject_sample",
+           "verify_attn_workspace_bytes", "reject_sample_workspace_bytes",
+           "SpecVerifyError", "SV_F32", "SV_BF16", "STATUS", "EXPORTS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+SV_F32, SV_BF16 = 0, 1
+STATUS = {0: "SV_OK", -1: "SV_ERR_INVALID_ARG", -2: "SV_ERR_UNSUPPORTED",
+          -3: "SV_ERR_WORKSPACE", -4: "SV_ERR_HIP"}
+EXPORTS = ("spec_verify_attn", "spec_verify_attn_workspace_bytes",
+           "spec_reject_sample", "spec_reject_sample_workspace_bytes",
+           "spec_status_string", "spec_version")
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__("%s returned %d (%s)" % (fn, status, STATUS.get(status, "?")))
+
+
+def lib_path():
+    return os.path.join(_HERE, "libspecverify.so")
+
+
+def load():
+    """Load the in-tree HIP library (raises OSError when it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise OSError("libspecverify.so not built at %s: run "
+                      "python -m speculative_decoding_verification_verify_amd.build" % path)
+    lib = ctypes.CDLL(path)
+    vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    lib.spec_verify_attn.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                     i32, i32, f32, i32, vp, sz, vp]
+    lib.spec_verify_attn.restype = i32
+    lib.spec_verify_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.spec_verify_attn_workspace_bytes.restype = sz
+    lib.spec_reject_sample.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                       vp, sz, vp]
+    lib.spec_reject_sample.restype = i32
+    lib.spec_reject_sample_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.spec_reject_sample_workspace_bytes.restype = sz
+    lib.spec_status_string.argtypes = [i32]
+    lib.spec_status_string.restype = ctypes.c_char_p
+    lib.spec_version.argtypes = []
+    lib.spec_version.restype = i32
+    _LIB = lib
+    return lib
+
+
+def exported_symbols():
+    lib = load()
+    return {name: hasattr(lib, name) for name in EXPORTS}
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    if t.dtype == torch.float32:
+        return SV_F32
+    raise TypeError("unsupported dtype %s (bfloat16 or float32)" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn, status):
+    if status != 0:
+        raise SpecVerifyError(fn, status)
+
+
+def _need(t, name, dtype=None, cuda=True):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if cuda and t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+
+
+def verify_attn_workspace_bytes(B, K, Hq, Hkv, D, max_kv_len):
+    return int(load().spec_verify_attn_workspace_bytes(B, K, Hq, Hkv, D, max_kv_len))
+
+
+def reject_sample_workspace_bytes(B, K, V):
+    return int(load().spec_reject_sample_workspace_bytes(B, K, V))
+
+
+def verify_attn(q, k_cache, v_cache, block_table, kv_len, out=None, max_kv_len=None,
+                scale=0.0, workspace=None, stream=None):
+    """Window-causal GQA of the K+1 verify positions (see ``spec_verify_attn``).
+
+    q [B, K+1, Hq, D]; k_cache [NB, Hkv, D/X, 16, X]; v_cache [NB, Hkv, D, 16]
+    (bf16 or fp32, X = 8 or 4); block_table [B, max_blocks] int32; kv_len [B]
+    int32 (committed lengths, read only).  ``max_kv_len`` bounds kv_len; it
+    defaults to the block table's capacity.  Returns ``out``.
+    """
+    import torch
+    lib = load()
+    _need(q, "q")
+    dt = _dtype_code(q)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, name, q.dtype)
+    _need(block_table, "block_table", torch.int32)
+    _need(kv_len, "kv_len", torch.int32)
+    B, K1, Hq, D = q.shape
+    NB, Hkv = k_cache.shape[0], k_cache.shape[1]
+    if k_cache.dim() != 5 or v_cache.dim() != 4:
+        raise ValueError("k_cache must be [NB,Hkv,D/X,16,X] and v_cache [NB,Hkv,D,16]")
+    block_size = k_cache.shape[3]
+    mbps = block_table.shape[1]
+    if max_kv_len is None:
+        max_kv_len = max(0, mbps * block_size - K1)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", q.dtype)
+    ws_bytes = verify_attn_workspace_bytes(B, K1 - 1, Hq, Hkv, D, max_kv_len)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.spec_verify_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                              _ptr(kv_len), _ptr(out), B, K1 - 1, Hq, Hkv, D, block_size, NB,
+                              mbps, int(max_kv_len), float(scale), dt, _ptr(workspace),
+                              ws_have, _stream(stream))
+    _check("spec_verify_attn", st)
+    return out
+
+
+def reject_sample(target, draft, draft_tokens, uniforms, temperature, kv_len,
+                  out_tokens=None, num_accepted=None, counters=None, workspace=None,
+                  stream=None):
+    """Lossless verifier + KV commit (see ``spec_reject_sample``).
+
+    target [B, K+1, V], draft [B, K, V] or None (greedy for every sequence);
+    draft_tokens [B, K] int32; uniforms [B, K+1] float32; temperature [B]
+    float32; kv_len [B] int32, updated in place to kv_len + n + 1.
+    Returns (out_tokens [B, K+1] int32, num_accepted [B] int32).
+    """
+    import torch
+    lib = load()
+    _need(target, "target")
+    dt = _dtype_code(target)
+    if draft is not None:
+        _need(draft, "draft", target.dtype)
+    _need(draft_tokens, "draft_tokens", torch.int32)
+    _need(uniforms, "uniforms", torch.float32)
+    _need(temperature, "temperature", torch.float32)
+    _need(kv_len, "kv_len", torch.int32)
+    B, K1, V = target.shape
+    K = K1 - 1
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K1), dtype=torch.int32, device=target.device)
+    if num_accepted is None:
+        num_accepted = torch.empty((B,), dtype=torch.int32, device=target.device)
+    if counters is not None:
+        _need(counters, "counters", torch.int64)
+    ws_bytes = reject_sample_workspace_bytes(B, K, V)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=target.device)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.spec_reject_sample(_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(uniforms),
+                                _ptr(temperature), _ptr(out_tokens), _ptr(num_accepted),
+                                _ptr(kv_len), _ptr(counters), B, K, V, dt, _ptr(workspace),
+                                ws_have, _stream(stream))
+    _check("spec_reject_sample", st)
+    return out_tokens, num_accepted

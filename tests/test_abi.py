@@ -1,0 +1,104 @@
+"""The C-ABI library: it loads, exports every symbol the header declares, and
+its host-side checks return the documented status codes (no GPU needed: every
+case here returns before anything is launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import speculative_decoding_verification_verify_amd as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sv.lib_path()):
+        from speculative_decoding_verification_verify_amd import build
+        build.build()
+    return sv.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|size_t|const char\*)\s+(spec_\w+)\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) == 6
+    assert set(names) == set(sv.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(lib):
+    assert lib.spec_status_string(0) == b"ok"
+    assert lib.spec_status_string(-3) == b"workspace too small"
+    assert lib.spec_status_string(99) == b"unknown status"
+    assert lib.spec_version() >= 100
+
+
+def test_workspace_sizes(lib):
+    assert sv.reject_sample_workspace_bytes(0, 7, 128256) == 0
+    assert sv.reject_sample_workspace_bytes(64, 0, 128256) == 0
+    a = sv.reject_sample_workspace_bytes(64, 7, 128256)
+    assert a > 0 and a % 256 == 0
+    # 15 rows x 32 chunks x 8 B per sequence for the row statistics at least.
+    assert a >= 64 * 15 * 32 * 8
+    assert sv.reject_sample_workspace_bytes(128, 7, 128256) > a
+    w = sv.verify_attn_workspace_bytes(64, 7, 32, 8, 128, 8192)
+    assert w % 256 == 0 and w > 0
+    assert sv.verify_attn_workspace_bytes(1, 1, 1, 1, 64, 0) == 0   # one split: no partials
+
+
+def _reject(lib, B=4, K=3, V=100, dtype=1, ws_bytes=1 << 20, ptrs=True, draft=True):
+    p = FAKE if ptrs else None
+    return lib.spec_reject_sample(p, p if draft else None, p, p, p, p, p, p, None, B, K, V, dtype,
+                                  p, ws_bytes, None)
+
+
+def test_reject_validation(lib):
+    assert _reject(lib, B=-1) == -1
+    assert _reject(lib, K=0) == -1
+    assert _reject(lib, V=0) == -1
+    assert _reject(lib, dtype=7) == -1
+    assert _reject(lib, K=17) == -2
+    assert _reject(lib, B=1 << 27, K=16) == -2           # grid rows over 2^31
+    assert _reject(lib, ptrs=False) == -1
+    assert _reject(lib, ws_bytes=16) == -3
+    assert _reject(lib, B=0, ptrs=False) == 0            # empty batch: no-op
+
+
+def _attn(lib, B=2, K=7, Hq=32, Hkv=8, D=128, bs=16, nb=10, mbps=600, mkl=8192, dtype=1,
+          ptrs=True, ws=1 << 30):
+    p = FAKE if ptrs else None
+    return lib.spec_verify_attn(p, p, p, p, p, p, B, K, Hq, Hkv, D, bs, nb, mbps, mkl,
+                                ctypes.c_float(0.0), dtype, p, ws, None)
+
+
+def test_attn_validation(lib):
+    assert _attn(lib, B=-1) == -1
+    assert _attn(lib, K=0) == -1
+    assert _attn(lib, dtype=3) == -1
+    assert _attn(lib, K=17) == -2
+    assert _attn(lib, D=96) == -2
+    assert _attn(lib, bs=32) == -2
+    assert _attn(lib, Hq=30, Hkv=8) == -2                # Hq % Hkv != 0
+    assert _attn(lib, Hq=72, Hkv=8) == -2                # 9 * 8 rows > 64
+    assert _attn(lib, mbps=10, mkl=8192) == -1           # table too short for max_kv_len
+    assert _attn(lib, ptrs=False) == -1
+    assert _attn(lib, ws=100) == -3
+    assert _attn(lib, B=0, ptrs=False) == 0
+
+
+def test_python_wrapper_rejects_cpu_tensors(lib):
+    import torch
+    q = torch.zeros((1, 2, 1, 64))
+    with pytest.raises(ValueError):
+        sv.verify_attn(q, q, q, q.int(), q.int())
