@@ -21,14 +21,23 @@ __device__ __forceinline__ float exp2_dev(float x) { return __builtin_amdgcn_exp
 // 16-byte vector loads of logits, widened to float.
 template <typename T> struct Vec16;
 
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 template <> struct Vec16<uint16_t> {
   static constexpr int N = 8;
-  __device__ __forceinline__ static void load(const uint16_t* p, float (&f)[8]) {
-    const uint4 r = *reinterpret_cast<const uint4*>(p);
+  __device__ __forceinline__ static void widen(const u32x4_t r, float (&f)[8]) {
     f[0] = bf16_lo(r.x); f[1] = bf16_hi(r.x);
     f[2] = bf16_lo(r.y); f[3] = bf16_hi(r.y);
     f[4] = bf16_lo(r.z); f[5] = bf16_hi(r.z);
     f[6] = bf16_lo(r.w); f[7] = bf16_hi(r.w);
+  }
+  __device__ __forceinline__ static void load(const uint16_t* p, float (&f)[8]) {
+    widen(*reinterpret_cast<const u32x4_t*>(p), f);
+  }
+  // Nontemporal: data streamed once (keeps it from displacing reused lines).
+  __device__ __forceinline__ static void load_nt(const uint16_t* p, float (&f)[8]) {
+    widen(__builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)), f);
   }
   __device__ __forceinline__ static float one(const uint16_t* p) { return bf16_to_f32(*p); }
 };
@@ -37,6 +46,10 @@ template <> struct Vec16<float> {
   static constexpr int N = 4;
   __device__ __forceinline__ static void load(const float* p, float (&f)[4]) {
     const float4 r = *reinterpret_cast<const float4*>(p);
+    f[0] = r.x; f[1] = r.y; f[2] = r.z; f[3] = r.w;
+  }
+  __device__ __forceinline__ static void load_nt(const float* p, float (&f)[4]) {
+    const f32x4_t r = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
     f[0] = r.x; f[1] = r.y; f[2] = r.z; f[3] = r.w;
   }
   __device__ __forceinline__ static float one(const float* p) { return *p; }

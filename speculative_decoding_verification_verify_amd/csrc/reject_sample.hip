@@ -45,6 +45,7 @@ constexpr int kThreads = 256;
 constexpr int kSweepChunk = 4096;   // elements per wave in k_sweep
 constexpr int kResChunk = 8192;     // elements per block in k_decide / k_locate
 constexpr int kMaxRows = 2 * SV_MAX_K + 1;
+constexpr int kPartStage = 4096;    // row statistics staged in LDS per sequence (32 KB)
 constexpr double kLog2eD = 1.4426950408889634074;
 
 struct Decision {
@@ -59,6 +60,14 @@ struct ChunkSums {
   double a, b;    // the same sums over entries with q > p
 };
 
+// The same sums for each 256-entry sub-chunk (a, b as above, q = sum e_q);
+// the final draw narrows chunk -> sub-chunk -> entry.
+constexpr int kSub = 256;
+constexpr int kSubPerChunk = kResChunk / kSub;
+struct SubSums {
+  double a, b, q;
+};
+
 __host__ __device__ inline int sweep_chunks(int V) { return (V + kSweepChunk - 1) / kSweepChunk; }
 __host__ __device__ inline int res_chunks(int V) { return (V + kResChunk - 1) / kResChunk; }
 
@@ -67,13 +76,14 @@ __device__ __forceinline__ float temp_of(const float* temp, int b, int force_gre
 }
 
 // Load VN logits at [e, e + VN) of a row, -inf past V.
-template <typename T, bool kAligned>
+template <typename T, bool kAligned, bool kNT = false>
 __device__ __forceinline__ void load_vec(const T* __restrict__ row, int e, int V,
                                          float (&x)[Vec16<T>::N]) {
   constexpr int VN = Vec16<T>::N;
   if (kAligned) {
     if (e < V) {
-      Vec16<T>::load(row + e, x);
+      if (kNT) Vec16<T>::load_nt(row + e, x);
+      else Vec16<T>::load(row + e, x);
     } else {
 #pragma unroll
       for (int k = 0; k < VN; ++k) x[k] = -INFINITY;
@@ -109,20 +119,39 @@ __global__ __launch_bounds__(kThreads) void k_sweep(
   constexpr int VN = Vec16<T>::N;
   constexpr int IT = kSweepChunk / (64 * VN);
   const int base = chunk * kSweepChunk + lane * VN;
+  // Every chunk but a row's last lies wholly inside the vocabulary: that
+  // (wave-uniform) case needs no per-entry range checks.
+  const bool full = kAligned && (chunk + 1) * kSweepChunk <= V;
   float x[IT][VN];
+  if (full) {
 #pragma unroll
-  for (int it = 0; it < IT; ++it) load_vec<T, kAligned>(src, base + it * 64 * VN, V, x[it]);
+    for (int it = 0; it < IT; ++it) Vec16<T>::load_nt(src + base + it * 64 * VN, x[it]);
+  } else {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) load_vec<T, kAligned, true>(src, base + it * 64 * VN, V, x[it]);
+  }
   float2 res;
   if (greedy) {
     float mv = -INFINITY;
     int mi = INT32_MAX;
+    if (full) {
+      // Entries visited in increasing index: strict > keeps the lowest index.
+      mv = x[0][0];
+      mi = base;
 #pragma unroll
-    for (int it = 0; it < IT; ++it)
+      for (int it = 0; it < IT; ++it)
 #pragma unroll
-      for (int k = 0; k < VN; ++k) {
-        const int e = base + it * 64 * VN + k;
-        if (e < V && (x[it][k] > mv || mi == INT32_MAX)) { mv = x[it][k]; mi = e; }
-      }
+        for (int k = 0; k < VN; ++k)
+          if (x[it][k] > mv) { mv = x[it][k]; mi = base + it * 64 * VN + k; }
+    } else {
+#pragma unroll
+      for (int it = 0; it < IT; ++it)
+#pragma unroll
+        for (int k = 0; k < VN; ++k) {
+          const int e = base + it * 64 * VN + k;
+          if (e < V && (x[it][k] > mv || mi == INT32_MAX)) { mv = x[it][k]; mi = e; }
+        }
+    }
     wave_am_reduce(mv, mi);
     res = make_float2(mv, __int_as_float(mi));
   } else {
@@ -199,9 +228,41 @@ __device__ __forceinline__ void emit(int b, int K, int n, int tok, const int32_t
   }
 }
 
-// Unnormalised float64 weight 2^((x - xmax) c) of one entry.
-__device__ __forceinline__ double expw(float x, float xmax, double c) {
-  return exp2(((double)x - (double)xmax) * c);
+// Float64 2^a for a <= 0, to a few ulp, at a fraction of the library
+// routine's cost.  With k = round(-16 a) (taken with the 2^52 + 2^51 shifter,
+// whose low word then holds k), 2^a = 2^(-k/16) * 2^r where r = a + k/16 is
+// exact and |r| <= 1/32.  2^(-k/16) comes from a table the block fills with
+// the device's float64 exp2; 2^r is the Taylor series of e^(r ln 2) to degree
+// 7, Horner form in r (first dropped term < 2e-18).  Arguments below -64 are
+// clamped there: such entries weigh < 5.4e-20 of the row maximum (whose
+// weight is 1), far below every tolerance; -inf gives exactly 0.
+constexpr int kExpTable = 1025;                  // 2^(-k/16), k = 0..1024
+
+__device__ __forceinline__ void fill_exp_table(double* tab) {
+  for (int k = threadIdx.x; k < kExpTable; k += blockDim.x) tab[k] = exp2(-(double)k * 0.0625);
+}
+
+__device__ __forceinline__ double exp2_neg(double a, const double* __restrict__ tab) {
+  const double ac = fmax(a, -64.0);
+  const double shifter = 6755399441055744.0;               // 2^52 + 2^51
+  const double t = fma(ac, -16.0, shifter);                // shifter + k
+  const int k = __double2loint(t);
+  const double r = fma(t - shifter, 0.0625, ac);           // a + k/16, exact
+  double p = 1.5252733804059838e-05;                       // ln2^7 / 7!
+  p = fma(p, r, 1.5403530393381606e-04);                   // ln2^6 / 6!
+  p = fma(p, r, 1.3333558146428441e-03);                   // ln2^5 / 5!
+  p = fma(p, r, 9.618129107628477e-03);                   // ln2^4 / 4!
+  p = fma(p, r, 5.5504108664821576e-02);                   // ln2^3 / 3!
+  p = fma(p, r, 2.402265069591007e-01);                   // ln2^2 / 2!
+  p = fma(p, r, 6.931471805599453e-01);                   // ln2
+  p = fma(p, r, 1.0);
+  const double v = tab[k] * p;
+  return (a == -INFINITY) ? 0.0 : v;
+}
+
+// Unnormalised float64 weight 2^((x - xmax) c) of one entry (x <= xmax).
+__device__ __forceinline__ double expw(float x, double xmax, double c, const double* __restrict__ tab) {
+  return exp2_neg(((double)x - xmax) * c, tab);
 }
 
 __device__ __forceinline__ double wave_sum_d(double x) {
@@ -218,11 +279,15 @@ __global__ __launch_bounds__(kThreads) void k_decide(
     const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ dtok,
     const float* __restrict__ uni, const float* __restrict__ temp, int K, int V, int nc, int ncr,
     int force_greedy, const float2* __restrict__ part, ChunkSums* __restrict__ csum,
-    Decision* __restrict__ dec, int32_t* __restrict__ out, int32_t* __restrict__ nacc,
-    int32_t* __restrict__ kv_len, unsigned long long* counters) {
+    SubSums* __restrict__ csub, Decision* __restrict__ dec, int32_t* __restrict__ out,
+    int32_t* __restrict__ nacc, int32_t* __restrict__ kv_len, unsigned long long* counters) {
   __shared__ float s_a[kMaxRows], s_b[kMaxRows];
+  __shared__ float2 s_part[kPartStage];
+  __shared__ float s_xq[SV_MAX_K], s_xp[SV_MAX_K];
+  __shared__ int s_d[SV_MAX_K];
   __shared__ int s_n;
   __shared__ double s_red[4][kThreads / 64];
+  __shared__ double s_exp[kExpTable];
   const int b = blockIdx.x;
   const int cr = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -231,22 +296,38 @@ __global__ __launch_bounds__(kThreads) void k_decide(
   const bool greedy = !(t > 0.f);
   const int rows = greedy ? K + 1 : R;
   const float c = greedy ? 0.f : kLog2e / t;
+  // All independent loads first: the row statistics of this sequence (into
+  // LDS when they fit) and the drafted tokens' logits.
+  const float2* pb = part + (size_t)b * R * nc;
+  const bool staged = rows * nc <= kPartStage;
+  if (staged)
+    for (int k = tid; k < rows * nc; k += kThreads) s_part[k] = pb[k];
+  if (!greedy) fill_exp_table(s_exp);
+  if (tid < K) {
+    const int d = clampi(dtok[(size_t)b * K + tid], 0, V - 1);
+    s_d[tid] = d;
+    if (!greedy) {
+      s_xq[tid] = Vec16<T>::one(tgt + ((size_t)b * (K + 1) + tid) * (size_t)V + d);
+      s_xp[tid] = Vec16<T>::one(drf + ((size_t)b * K + tid) * (size_t)V + d);
+    }
+  }
+  __syncthreads();
   for (int r = wave; r < rows; r += kThreads / 64) {
     float a, bb;
-    merge_row(part + ((size_t)b * R + r) * nc, nc, greedy, c, lane, a, bb);
+    merge_row(staged ? s_part + r * nc : pb + (size_t)r * nc, nc, greedy, c, lane, a, bb);
     if (lane == 0) { s_a[r] = a; s_b[r] = bb; }
   }
   __syncthreads();
   if (tid == 0) {
     int n = 0;
     for (int i = 0; i < K; ++i) {
-      const int d = clampi(dtok[(size_t)b * K + i], 0, V - 1);
+      const int d = s_d[i];
       bool acc;
       if (greedy) {
         acc = (d == __float_as_int(s_b[i]));
       } else {
-        const float xq = Vec16<T>::one(tgt + ((size_t)b * (K + 1) + i) * (size_t)V + d);
-        const float xp = Vec16<T>::one(drf + ((size_t)b * K + i) * (size_t)V + d);
+        const float xq = s_xq[i];
+        const float xp = s_xp[i];
         if (xp == -INFINITY) {
           acc = true;                                   // p(d) == 0
         } else {
@@ -290,7 +371,10 @@ __global__ __launch_bounds__(kThreads) void k_decide(
   const T* drow = bonus ? trow : drf + ((size_t)b * K + n) * (size_t)V;
   constexpr int VN = Vec16<T>::N;
   constexpr int IT = kResChunk / (kThreads * VN);
+  constexpr int kSubLanes = kSub / VN;            // lanes covering one sub-chunk per step
   const int lo = cr * kResChunk;
+  const double xmqd = (double)xmq, xmpd = (double)xmp;
+  SubSums* sub = csub + ((size_t)b * ncr + cr) * kSubPerChunk;
   double eq = 0.0, ep = 0.0, sa = 0.0, sb = 0.0;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -298,18 +382,31 @@ __global__ __launch_bounds__(kThreads) void k_decide(
     float xq[VN], xp[VN];
     load_vec<T, kAligned>(trow, e, V, xq);
     if (!bonus) load_vec<T, kAligned>(drow, e, V, xp);
+    double tq = 0.0, ta = 0.0, tb = 0.0;
 #pragma unroll
     for (int k = 0; k < VN; ++k) {
       if (e + k < V) {
-        const double wq = expw(xq[k], xmq, cd);
-        eq += wq;
+        const double wq = expw(xq[k], xmqd, cd, s_exp);
+        tq += wq;
         if (!bonus) {
-          const double wp = expw(xp[k], xmp, cd);
+          const double wp = expw(xp[k], xmpd, cd, s_exp);
           ep += wp;
-          if (wq * sp_approx > wp * sq_approx) { sa += wq; sb += wp; }
+          if (wq * sp_approx > wp * sq_approx) { ta += wq; tb += wp; }
         }
       }
     }
+    eq += tq;
+    sa += ta;
+    sb += tb;
+    // Sub-chunk sums: kSubLanes consecutive lanes cover one 256-entry run.
+#pragma unroll
+    for (int off = kSubLanes / 2; off > 0; off >>= 1) {
+      tq += __shfl_xor(tq, off, 64);
+      ta += __shfl_xor(ta, off, 64);
+      tb += __shfl_xor(tb, off, 64);
+    }
+    if ((lane & (kSubLanes - 1)) == 0)
+      sub[it * (kThreads * VN / kSub) + (tid * VN) / kSub] = SubSums{ta, tb, tq};
   }
   eq = wave_sum_d(eq);
   ep = wave_sum_d(ep);
@@ -327,34 +424,47 @@ __global__ __launch_bounds__(kThreads) void k_decide(
 }
 
 // ---------------------------------------------------------------------------
-// k_locate: grid (B); block 256.  Sampling sequences only.
+// k_locate: grid (B); block 256.  Sampling sequences only.  Narrows the draw
+// chunk -> sub-chunk (from the stored sums) -> entry (exact weights of one
+// 256-entry run, one per thread, scanned in fixed order).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ double chunk_mass(const ChunkSums& cs, bool qonly, double isq, double isp) {
   return qonly ? cs.eq * isq : fmax(0.0, cs.a * isq - cs.b * isp);
+}
+__device__ __forceinline__ double sub_mass(const SubSums& ss, bool qonly, double isq, double isp) {
+  return qonly ? ss.q * isq : fmax(0.0, ss.a * isq - ss.b * isp);
 }
 
 template <typename T, bool kAligned>
 __global__ __launch_bounds__(kThreads) void k_locate(
     const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ dtok,
     const float* __restrict__ uni, const float* __restrict__ temp, int K, int V, int ncr,
-    int force_greedy, const ChunkSums* __restrict__ csum, const Decision* __restrict__ dec,
-    int32_t* __restrict__ out, int32_t* __restrict__ nacc, int32_t* __restrict__ kv_len,
-    unsigned long long* counters) {
-  constexpr int kPer = kResChunk / kThreads;                 // 32 contiguous entries per thread
-  __shared__ double s_w[kThreads * (kPer + 1)];              // padded against bank conflicts
-  __shared__ double s_tot[kThreads];
-  __shared__ int s_chunk, s_fallback, s_useq, s_first, s_lastpos;
+    int force_greedy, const ChunkSums* __restrict__ csum, const SubSums* __restrict__ csub,
+    const Decision* __restrict__ dec, int32_t* __restrict__ out, int32_t* __restrict__ nacc,
+    int32_t* __restrict__ kv_len, unsigned long long* counters) {
+  static_assert(kSub == kThreads, "one sub-chunk entry per thread");
+  __shared__ ChunkSums s_cs[kThreads];
+  __shared__ SubSums s_ss[kSubPerChunk];
+  __shared__ double s_exp[kExpTable];
+  __shared__ double s_wtot[kThreads / 64];
+  __shared__ int s_chunk, s_sub, s_fallback, s_useq, s_first, s_lastpos;
   __shared__ double s_base, s_target, s_isq, s_isp;
   const int b = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float t = temp_of(temp, b, force_greedy);
   if (!(t > 0.f)) return;
   const double cd = kLog2eD / (double)t;
   const Decision d = dec[b];
   const int n = d.n;
   const bool bonus = (n == K);
+  // Chunk sums are loaded in parallel, then walked in order by thread 0.
+  const ChunkSums* cg = csum + (size_t)b * ncr;
+  const bool cstaged = ncr <= kThreads;
+  if (cstaged && tid < ncr) s_cs[tid] = cg[tid];
+  fill_exp_table(s_exp);
+  __syncthreads();
   if (tid == 0) {
-    const ChunkSums* cs = csum + (size_t)b * ncr;
+    const ChunkSums* cs = cstaged ? s_cs : cg;
     double sq = 0.0, sp = 0.0;
     for (int i = 0; i < ncr; ++i) { sq += cs[i].eq; sp += cs[i].ep; }
     const double isq = 1.0 / sq;
@@ -387,61 +497,61 @@ __global__ __launch_bounds__(kThreads) void k_locate(
   const int ch = s_chunk;
   const bool qonly = bonus || (s_useq != 0);
   const double isq = s_isq, isp = s_isp;
+  if (tid < kSubPerChunk) s_ss[tid] = csub[((size_t)b * ncr + ch) * kSubPerChunk + tid];
+  __syncthreads();
+  if (tid == 0) {
+    int sc = -1;
+    double p = s_base, base = s_base;
+    if (!s_fallback) {
+      for (int j = 0; j < kSubPerChunk; ++j) {
+        const double p2 = p + sub_mass(s_ss[j], qonly, isq, isp);
+        if (p2 > s_target) { sc = j; base = p; break; }
+        p = p2;
+      }
+    }
+    if (sc < 0) {                                             // no crossing left: last positive run
+      s_fallback = 1;
+      for (int j = kSubPerChunk - 1; j >= 0; --j)
+        if (sub_mass(s_ss[j], qonly, isq, isp) > 0.0) { sc = j; break; }
+      if (sc < 0) sc = 0;
+    }
+    s_sub = sc;
+    s_base = base;
+  }
+  __syncthreads();
   const T* trow = tgt + ((size_t)b * (K + 1) + n) * (size_t)V;
   const T* drow = bonus ? trow : drf + ((size_t)b * K + n) * (size_t)V;
-  constexpr int VN = Vec16<T>::N;
-  constexpr int IT = kResChunk / (kThreads * VN);
-  const int lo = ch * kResChunk;
-  // Stage the chunk's float64 weights in LDS in vocabulary order.
+  const int e = ch * kResChunk + s_sub * kSub + tid;
+  double w = 0.0;
+  if (e < V) {
+    const double q = expw(Vec16<T>::one(trow + e), (double)d.xmq, cd, s_exp) * isq;
+    w = qonly ? q : fmax(0.0, q - expw(Vec16<T>::one(drow + e), (double)d.xmp, cd, s_exp) * isp);
+  }
+  // Inclusive prefix over the 256 entries in vocabulary order: a wave scan
+  // plus the totals of the waves before (fixed order).
+  double incl = w;
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int off = it * kThreads * VN + tid * VN;
-    const int e = lo + off;
-    float xq[VN], xp[VN];
-    load_vec<T, kAligned>(trow, e, V, xq);
-    if (!qonly) load_vec<T, kAligned>(drow, e, V, xp);
-#pragma unroll
-    for (int k = 0; k < VN; ++k) {
-      const int o = off + k;
-      double w = 0.0;
-      if (e + k < V) {
-        const double q = expw(xq[k], d.xmq, cd) * isq;
-        w = qonly ? q : fmax(0.0, q - expw(xp[k], d.xmp, cd) * isp);
-      }
-      s_w[(o / kPer) * (kPer + 1) + (o % kPer)] = w;
-    }
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
   }
+  if (lane == 63) s_wtot[wave] = incl;
   __syncthreads();
-  const double* mine = s_w + tid * (kPer + 1);
-  double tot = 0.0;
-  int lastpos = -1;
-  for (int i = 0; i < kPer; ++i) {
-    tot += mine[i];
-    if (mine[i] > 0.0) lastpos = lo + tid * kPer + i;
-  }
-  s_tot[tid] = tot;
-  if (lastpos >= 0) atomicMax(&s_lastpos, lastpos);
-  __syncthreads();
-  if (!s_fallback) {
-    double run = s_base;
-    for (int i = 0; i < tid; ++i) run += s_tot[i];           // fixed order
-    const double target = s_target;
-    for (int i = 0; i < kPer; ++i) {
-      run += mine[i];
-      if (run > target) { atomicMin(&s_first, lo + tid * kPer + i); break; }
-    }
-  }
+  double run = s_base + incl;
+  for (int ww = 0; ww < wave; ++ww) run += s_wtot[ww];
+  if (!s_fallback && run > s_target) atomicMin(&s_first, e);
+  if (w > 0.0) atomicMax(&s_lastpos, e);
   __syncthreads();
   if (tid == 0) {
     int tok = s_first;
     if (tok == INT32_MAX) tok = s_lastpos;                   // no crossing: last positive weight
-    if (tok < 0) tok = clampi(lo, 0, V - 1);
+    if (tok < 0) tok = clampi(ch * kResChunk + s_sub * kSub, 0, V - 1);
     emit(b, K, n, tok, dtok, out, nacc, kv_len, counters);
   }
 }
 
 struct RejectPlan {
-  size_t part_off, csum_off, dec_off, total;
+  size_t part_off, csum_off, csub_off, dec_off, total;
 };
 
 static inline RejectPlan reject_plan(int B, int K, int V) {
@@ -450,7 +560,8 @@ static inline RejectPlan reject_plan(int B, int K, int V) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   p.part_off = 0;
   p.csum_off = up((size_t)B * R * sweep_chunks(V) * sizeof(float2));
-  p.dec_off = p.csum_off + up((size_t)B * res_chunks(V) * sizeof(ChunkSums));
+  p.csub_off = p.csum_off + up((size_t)B * res_chunks(V) * sizeof(ChunkSums));
+  p.dec_off = p.csub_off + up((size_t)B * res_chunks(V) * kSubPerChunk * sizeof(SubSums));
   p.total = p.dec_off + up((size_t)B * sizeof(Decision));
   return p;
 }
@@ -466,15 +577,16 @@ static hipError_t launch_all(const void* tgt, const void* drf, const int32_t* dt
   const RejectPlan p = reject_plan(B, K, V);
   float2* part = reinterpret_cast<float2*>(ws + p.part_off);
   ChunkSums* csum = reinterpret_cast<ChunkSums*>(ws + p.csum_off);
+  SubSums* csub = reinterpret_cast<SubSums*>(ws + p.csub_off);
   Decision* dec = reinterpret_cast<Decision*>(ws + p.dec_off);
   const T* t = static_cast<const T*>(tgt);
   const T* d = static_cast<const T*>(drf);
   hipLaunchKernelGGL((k_sweep<T, kAligned>), dim3(B * R, (nc + 3) / 4), dim3(kThreads), 0, st, t, d,
                      temp, K, V, nc, force_greedy, part);
   hipLaunchKernelGGL((k_decide<T, kAligned>), dim3(B, ncr), dim3(kThreads), 0, st, t, d, dtok, uni,
-                     temp, K, V, nc, ncr, force_greedy, part, csum, dec, out, nacc, kv_len, counters);
+                     temp, K, V, nc, ncr, force_greedy, part, csum, csub, dec, out, nacc, kv_len, counters);
   hipLaunchKernelGGL((k_locate<T, kAligned>), dim3(B), dim3(kThreads), 0, st, t, d, dtok, uni, temp,
-                     K, V, ncr, force_greedy, csum, dec, out, nacc, kv_len, counters);
+                     K, V, ncr, force_greedy, csum, csub, dec, out, nacc, kv_len, counters);
   return hipGetLastError();
 }
 

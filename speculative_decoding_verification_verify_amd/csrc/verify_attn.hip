@@ -8,22 +8,32 @@
 // "Quand et pourquoi utiliser le speculative decoding", section 1), so the
 // kernel is built to stream K and V once at full HBM bandwidth.
 //
-// bf16 path (k_attn_mfma): one workgroup = 4 waves per (sequence, KV head,
-// key split).  All G = Hq/Hkv query heads of the KV head and all K+1
-// positions form the rows of one or two 32-row tiles, so each K/V byte is
-// read once for the whole group.  Each wave walks page pairs (32 keys) of its
-// split with its own online softmax:
+// bf16 path (k_attn_stream): a persistent grid of about two 4-wave workgroups
+// per CU.  The work list is every page pair (32 keys) of every (sequence, KV
+// head), in that order; each workgroup takes an equal contiguous share of it
+// (stream-K), so sequences of very different lengths still keep every CU busy
+// to the end.  Inside a share, each (sequence, KV head) segment is one online
+// softmax over all G = Hq/Hkv query heads and all K+1 positions of that KV
+// head (one or two 32-row tiles), so each K/V byte is read once.  Its 4 waves
+// take alternate page pairs:
 //   S^T (32 keys x 32 rows) = K . Q^T   8 x v_mfma_f32_32x32x16_bf16 (D=128)
 //   O^T (32 d x 32 rows)   += V^T . P^T 2 x 4 MFMAs per pair
 // The MFMA key order is permuted so that the C registers of S^T are exactly
 // the B operand of the P.V product (lane l holds tokens 8*(l/32)..+7 of each
-// page for row l%32), and so that every K and V load is a 16-byte vector with
-// the 64 lanes of one instruction reading 512 contiguous bytes from each page.
-// No LDS is touched in the key loop; the 4 waves merge through LDS at the end.
-// Splits are merged by k_attn_combine (log-sum-exp weights, fixed order).
+// page for row l%32), and so that every K and V load is a 16-byte nontemporal
+// vector with the 64 lanes of one instruction reading 512 contiguous bytes of
+// each page.  No LDS is touched in the key loop; the next pair's K is
+// requested right after this pair's scores and its V right after P.V, so
+// loads stay in flight through the softmax.  The waves merge through LDS at
+// the end of a segment.  A segment a workgroup covers entirely is written out
+// directly; the at most two partial segments of a workgroup go to the
+// workspace and k_attn_stream_combine merges them (log-sum-exp weights, fixed
+// order).
 //
 // fp32 path (k_attn_valu): plain VALU kernel, one wave per query row; used for
 // fp32 caches (the correctness configuration).
+
+#include <algorithm>
 
 #include "common.h"
 
@@ -31,67 +41,258 @@ namespace sv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kAttnThreads = 256;
 constexpr int kPairKeys = 32;
+constexpr int kStreamMaxWG = 1024;   // workspace is sized for this many workgroups
 
-// Keys per split for the bf16 path, chosen from the launch shape alone so the
-// workspace size is a pure function of the arguments.
-static inline int attn_split_keys(int B, int Hkv, int max_len) {
-  const long long work = (long long)max_len * B * Hkv;
-  long long per = work / 4096;                 // aim for ~4096 workgroup slots
-  per = (per + 127) / 128 * 128;               // whole page pairs for all 4 waves
-  if (per < 128) per = 128;
-  if (per > (1 << 20)) per = 1 << 20;
-  return (int)per;
+// Tuning knobs (compile-time).
+#ifndef SV_ATTN_NT_LOADS
+#define SV_ATTN_NT_LOADS 1      // nontemporal K/V loads: streamed once, keep them out of L2
+#endif
+#ifndef SV_ATTN_WG_PER_CU
+#define SV_ATTN_WG_PER_CU 2     // persistent workgroups per CU
+#endif
+#ifndef SV_ATTN_MIN_PAIRS_PER_WG
+#define SV_ATTN_MIN_PAIRS_PER_WG 4
+#endif
+#ifndef SV_ATTN_DYN
+#define SV_ATTN_DYN 0           // waves claim page pairs from an LDS counter (not bitwise reproducible)
+#endif
+#ifndef SV_ATTN_LAZY
+#define SV_ATTN_LAZY 8.0f       // rescale O only when the row max grows by > 2^8
+#endif
+#ifndef SV_ATTN_WAVES_1T
+#define SV_ATTN_WAVES_1T 2      // waves per SIMD the one-tile kernel must fit
+#endif
+
+__device__ __forceinline__ bf16x8 load_kv(const uint16_t* p) {
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+#if SV_ATTN_NT_LOADS
+  return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(q));
+#else
+  return __builtin_bit_cast(bf16x8, *q);
+#endif
 }
 
-static inline int attn_tiles(int G, int K1) { return (G * K1 + 31) / 32; }
+__device__ __forceinline__ void pair_blocks(int (&blk)[2], int pr, const int32_t* __restrict__ btb,
+                                            int mbps, int num_blocks) {
+#pragma unroll
+  for (int sg = 0; sg < 2; ++sg) blk[sg] = clampi(btb[min(2 * pr + sg, mbps - 1)], 0, num_blocks - 1);
+}
 
-// ---------------------------------------------------------------------------
-// bf16 MFMA kernel.  grid (nsplit, Hkv, B), block 256.
-// Partials: opart[((b*Hkv + g)*nsplit + s)*rows_pad*D + row*D + d] (fp32,
-// scaled to the split max) and ml[(b*Hkv + g)*nsplit + s)*rows_pad + row] =
-// (max, sum), base-2 scaled scores.
-// ---------------------------------------------------------------------------
+// K operand of a page pair: lane holds key k_tok of page k_page, chunks 2kk+hh.
+template <int D>
+__device__ __forceinline__ void load_k(bf16x8 (&kf)[D / 16], const int (&blk)[2],
+                                       const uint16_t* __restrict__ kc, int Hkv, int g, int k_page,
+                                       int k_tok, int hh) {
+  const uint16_t* kpage = kc + ((size_t)(k_page ? blk[1] : blk[0]) * Hkv + g) * ((size_t)D * 16);
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) kf[kk] = load_kv(kpage + ((2 * kk + hh) * 16 + k_tok) * 8);
+}
+
+// V operand of a page pair: lane holds tokens 8hh..8hh+7 of value coordinate 32j + l32.
+template <int D>
+__device__ __forceinline__ void load_v(bf16x8 (&vf)[2][D / 32], const int (&blk)[2],
+                                       const uint16_t* __restrict__ vc, int Hkv, int g, int l32, int hh) {
+#pragma unroll
+  for (int sg = 0; sg < 2; ++sg) {
+    const uint16_t* vpage = vc + ((size_t)blk[sg] * Hkv + g) * ((size_t)D * 16);
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) vf[sg][j] = load_kv(vpage + (32 * j + l32) * 16 + 8 * hh);
+  }
+}
+
+// Zero the V entries of keys past the sequence end: those slots may hold
+// anything (even NaN); their probability is 0, but 0 * NaN would reach O.
+template <int D>
+__device__ __forceinline__ void mask_v_tail(bf16x8 (&vf)[2][D / 32], int pr, int L, int hh) {
+  const int key0 = pr * kPairKeys + 8 * hh;
+  if (pr * kPairKeys + kPairKeys > L) {
+#pragma unroll
+    for (int sg = 0; sg < 2; ++sg)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (key0 + sg * 16 + e >= L)
+#pragma unroll
+          for (int j = 0; j < D / 32; ++j) vf[sg][j][e] = (__bf16)0.f;
+  }
+}
+
+// Scores of one page pair for tile nt, window-causal mask, online-softmax
+// update of (m, l, O) and the bf16 probabilities for the P.V product.
 template <int D, int NT>
-__global__ __launch_bounds__(kAttnThreads) void k_attn_mfma(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
-    const int32_t* __restrict__ bt, const int32_t* __restrict__ kv_len, uint16_t* __restrict__ out,
-    int K1, int Hq, int Hkv, int num_blocks, int mbps, int split_keys, int nsplit, float sl2,
-    float* __restrict__ opart, float2* __restrict__ ml) {
-  constexpr int KK = D / 16;         // MFMA k-steps for S
-  constexpr int DT = D / 32;         // d tiles for O
-  constexpr int ROWS = 32 * NT;
-  constexpr int OPAD = D + 4;        // LDS row stride (floats)
-  __shared__ float s_o[4][32][OPAD];
-  __shared__ float s_m[4][ROWS], s_l[4][ROWS];
+__device__ __forceinline__ void score_pair(const bf16x8 (&kf)[D / 16], int pr, int hh, int nt,
+                                           const bf16x8 (&qf)[NT][D / 16], const int (&lim)[NT],
+                                           float sl2, f32x16 (&o)[NT][D / 32], float (&m_run)[NT],
+                                           float (&l_run)[NT], bf16x8 (&pf)[2]) {
+  constexpr int KK = D / 16, DT = D / 32;
+  const int key0 = pr * kPairKeys + 8 * hh;     // key of reg r: key0 + (r>>3)*16 + (r&7)
+  f32x16 s;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[nt][kk], s, 0, 0, 0);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = key0 + (r >> 3) * 16 + (r & 7);
+    const float v = (key <= lim[nt]) ? s[r] * sl2 : -INFINITY;
+    s[r] = v;
+    mx = fmaxf(mx, v);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  // Lazy rescaling: keep the running reference unless the row max grows by
+  // more than SV_ATTN_LAZY (so p <= 2^SV_ATTN_LAZY); O / l is unchanged.
+  const bool need = mx > m_run[nt] + SV_ATTN_LAZY;
+  if (__ballot(need)) {
+    const float m_new = need ? mx : m_run[nt];
+    const float alpha = need ? exp2_dev(m_run[nt] - m_new) : 1.f;
+    l_run[nt] *= alpha;
+    m_run[nt] = m_new;
+#pragma unroll
+    for (int j = 0; j < DT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[nt][j][r] *= alpha;
+  }
+  const float m_use = (m_run[nt] == -INFINITY) ? 0.f : m_run[nt];
+  float rs = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s[r] = exp2_dev(s[r] - m_use);
+    rs += s[r];
+  }
+  rs += __shfl_xor(rs, 32, 64);
+  l_run[nt] += rs;
+#pragma unroll
+  for (int sg = 0; sg < 2; ++sg)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pf[sg][e] = (__bf16)s[8 * sg + e];
+}
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int G = Hq / Hkv;
-  const int rows = G * K1;
-  const int L0 = kv_len[b];
-  const int L = L0 + K1;
-  // kv_len above the max_kv_len the grid was sized for is a precondition
-  // violation: its extra keys are dropped, never read out of bounds.
-  const int my_splits = min(nsplit, (L + split_keys - 1) / split_keys);
-  if (split >= my_splits) return;
+template <int D, int NT>
+__device__ __forceinline__ void pv_pair(const bf16x8 (&vf)[2][D / 32], int nt, const bf16x8 (&pf)[2],
+                                        f32x16 (&o)[NT][D / 32]) {
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j)
+#pragma unroll
+    for (int sg = 0; sg < 2; ++sg)
+      o[nt][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[sg][j], pf[sg], o[nt][j], 0, 0, 0);
+}
+
+// Page pairs of sequence b, capped by the grid's max_kv_len.
+__device__ __forceinline__ int npairs_of(const int32_t* __restrict__ kv_len, int b, int K1, int np_cap) {
+  const int L = kv_len[b] + K1;
+  return min(np_cap, max(1, (L + kPairKeys - 1) / kPairKeys));
+}
+
+// Block-wide sum of one value per thread (fixed order; all threads get it).
+__device__ __forceinline__ long long block_sum_ll(long long v, long long* s_red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) s_red[wave] = v;
+  __syncthreads();
+  long long t = 0;
+#pragma unroll
+  for (int w = 0; w < kAttnThreads / 64; ++w) t += s_red[w];
+  return t;
+}
+
+// The sequence b holding work item u and the index of its first item,
+// Hkv * sum_{b' < b} npairs(b').  All threads return the same values.
+__device__ void locate_work(const int32_t* __restrict__ kv_len, int B, int K1, int np_cap, int Hkv,
+                            long long u, int& b_out, long long& off_out, long long* s_wsum,
+                            long long* s_res, int* s_found) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int l32 = lane & 31, hh = lane >> 5;
+  __syncthreads();
+  if (tid == 0) { s_found[0] = B; s_res[0] = 0; }
+  long long carry = 0;
+  for (int base = 0; base < B; base += kAttnThreads) {
+    const int b = base + tid;
+    const long long v = (b < B) ? (long long)npairs_of(kv_len, b, K1, np_cap) * Hkv : 0;
+    long long incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const long long t = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += t;
+    }
+    __syncthreads();
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    long long ex = carry + incl - v;
+    for (int ww = 0; ww < wave; ++ww) ex += s_wsum[ww];
+    if (b < B && ex <= u && u < ex + v) { s_found[0] = b; s_res[0] = ex; }
+    long long tile = 0;
+#pragma unroll
+    for (int ww = 0; ww < kAttnThreads / 64; ++ww) tile += s_wsum[ww];
+    carry += tile;
+    __syncthreads();
+    if (s_found[0] < B) break;
+  }
+  b_out = s_found[0];
+  off_out = s_res[0];
+  __syncthreads();
+}
 
-  // Q operand (B of S^T = K Q^T): lane holds Q[row = nt*32 + l32][kk*16 + hh*8 .. +8].
-  bf16x8 qf[NT][KK];
-  int lim[NT];
+__host__ __device__ inline long long stream_start(int w, long long U, int W) { return (long long)w * U / W; }
+
+// Work item u belongs to the last workgroup whose share starts at or before u.
+__host__ __device__ inline int stream_owner(long long u, long long U, int W) {
+  return (int)(((u + 1) * W - 1) / U);
+}
+
+// One (sequence, KV head) piece of a workgroup's share: pairs [p_lo, p_hi)
+// of sequence b, KV head g.  Wave-uniform.
+struct Seg {
+  int b, g, np, off, p_lo, p_hi, end, slot, L0;
+  bool full;
+};
+
+// The piece after s in the share that ends at u1, if any.
+__device__ __forceinline__ bool next_segment(const Seg& s, Seg& n, int u1, int B, int Hkv, int K1,
+                                             int np_cap, const int32_t* __restrict__ kv_len) {
+  n = s;
+  if (s.end >= u1) return false;
+  int nb = s.b, ng = s.g + 1, off = s.off, np = s.np;
+  if (ng == Hkv) {
+    ng = 0;
+    off += s.np * Hkv;
+    if (++nb >= B) return false;
+    np = npairs_of(kv_len, nb, K1, np_cap);
+  }
+  n.b = nb;
+  n.g = ng;
+  n.off = off;
+  n.np = np;
+  n.p_lo = 0;
+  n.end = min(u1, off + (ng + 1) * np);
+  n.p_hi = n.end - (off + ng * np);
+  n.slot = 1;
+  n.full = (n.p_hi == np);
+  n.L0 = kv_len[nb];
+  return true;
+}
+
+// Q operand (B of S^T = K Q^T) of a piece: lane holds Q[row = nt*32 + l32]
+// [kk*16 + hh*8 .. +8]; rows past G*(K+1) are zero.  lim = last visible key.
+template <int D, int NT>
+__device__ __forceinline__ void load_q(bf16x8 (&qf)[NT][D / 16], int (&lim)[NT],
+                                       const uint16_t* __restrict__ q, const Seg& s, int K1, int Hq,
+                                       int G, int rows, int l32, int hh) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int row = nt * 32 + l32;
     const bool valid = row < rows;
     const int hq = valid ? row / K1 : 0;
     const int i = valid ? row - hq * K1 : K1 - 1;
-    lim[nt] = L0 + i;                             // last visible key
-    const uint16_t* qp = q + (((size_t)b * K1 + i) * Hq + (size_t)g * G + hq) * D;
+    lim[nt] = s.L0 + i;
+    const uint16_t* qp = q + (((size_t)s.b * K1 + i) * Hq + (size_t)s.g * G + hq) * D;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
+    for (int kk = 0; kk < D / 16; ++kk) {
       if (valid) {
         qf[nt][kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16 + hh * 8);
       } else {
@@ -100,204 +301,280 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_mfma(
       }
     }
   }
+}
 
-  f32x16 o[NT][DT];
-  float m_run[NT], l_run[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m_run[nt] = -INFINITY;
-    l_run[nt] = 0.f;
-#pragma unroll
-    for (int j = 0; j < DT; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[nt][j][r] = 0.f;
+// ---------------------------------------------------------------------------
+// bf16 stream-K kernel.  grid (W), block 256.
+// Partial slots: opart[((w * 2 + slot) * ROWS + row) * D + d] (fp32, scaled to
+// the slot's max) and ml[(w * 2 + slot) * ROWS + row] = (max, sum), scores in
+// base-2 units.  Slot 0: the segment that starts the workgroup's share;
+// slot 1: a segment that starts later and runs past its end.
+// ---------------------------------------------------------------------------
+template <int D, int NT>
+__global__ __launch_bounds__(kAttnThreads, NT == 1 ? SV_ATTN_WAVES_1T : 1) void k_attn_stream(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int32_t* __restrict__ bt, const int32_t* __restrict__ kv_len, uint16_t* __restrict__ out,
+    int B, int K1, int Hq, int Hkv, int num_blocks, int mbps, int np_cap, float sl2, int W,
+    float* __restrict__ opart, float2* __restrict__ ml) {
+  constexpr int KK = D / 16;         // MFMA k-steps for S
+  constexpr int DT = D / 32;         // d tiles for O
+  constexpr int ROWS = 32 * NT;
+  constexpr int OPAD = D + 4;        // LDS row stride (floats)
+  constexpr int DPT = D / 8;         // output d's per thread in the epilogue
+  __shared__ float s_o[32][OPAD];
+  __shared__ float s_m[4][32], s_l[4][32];
+  __shared__ long long s_red[kAttnThreads / 64];
+  __shared__ long long s_res[1];
+  __shared__ int s_found[1];
+  __shared__ int s_ctr[1];          // next unclaimed page pair of the current piece
+
+  const int w = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar pair indices
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int G = Hq / Hkv;
+  const int rows = G * K1;
+
+  // Total work first: the share [u0, u1) depends on it.
+  long long tot = 0;
+  for (int bb = tid; bb < B; bb += kAttnThreads) tot += (long long)npairs_of(kv_len, bb, K1, np_cap) * Hkv;
+  // The host bounds the work list below 2^30 items, so it fits int; values
+  // that come back through LDS are made wave-uniform (scalar registers).
+  const int U = __builtin_amdgcn_readfirstlane((int)block_sum_ll(tot, s_red));
+  const int u0 = (int)stream_start(w, U, W), u1 = (int)stream_start(w + 1, U, W);
+  if (u0 >= u1) return;
+  int b;
+  int off_b;
+  {
+    long long off;
+    locate_work(kv_len, B, K1, np_cap, Hkv, u0, b, off, s_red, s_res, s_found);
+    b = __builtin_amdgcn_readfirstlane(b);
+    off_b = __builtin_amdgcn_readfirstlane((int)off);
   }
-
+  if (b >= B) return;                       // u0 < U always finds a sequence
   // K operand row of this lane: MFMA key mk = l32 -> page mk>>4, token below.
   const int k_page = l32 >> 4;
   const int k_tok = 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
-  const size_t page_elems = (size_t)D * 16;
-  const int32_t* btb = bt + (size_t)b * mbps;
 
-  const int npairs = (L + kPairKeys - 1) / kPairKeys;
-  const int split_pairs = split_keys / kPairKeys;
-  const int p_lo = split * split_pairs;
-  const int p_hi = min(npairs, p_lo + split_pairs);
+  // The share's first segment.
+  Seg cur;
+  cur.b = b;
+  cur.np = npairs_of(kv_len, b, K1, np_cap);
+  cur.g = (u0 - off_b) / cur.np;
+  cur.off = off_b;
+  cur.p_lo = (u0 - off_b) - cur.g * cur.np;
+  cur.end = min(u1, off_b + (cur.g + 1) * cur.np);
+  cur.p_hi = cur.p_lo + (cur.end - u0);
+  cur.slot = 0;
+  cur.full = (cur.p_lo == 0) && (cur.p_hi == cur.np);
+  cur.L0 = kv_len[b];
 
-  for (int pr = p_lo + wave; pr < p_hi; pr += 4) {
+  // Each wave's first pair of a piece is p_lo + wave; the rest are claimed
+  // from s_ctr in order of need, so the waves finish a piece together.
+  if (tid == 0) s_ctr[0] = cur.p_lo + 4;
+  __syncthreads();
+
+  bf16x8 qf[NT][KK];
+  int lim[NT];
+  load_q<D, NT>(qf, lim, q, cur, K1, Hq, G, rows, l32, hh);
+  bf16x8 kf[KK];
+  bf16x8 vf[2][DT];
+  int pr = cur.p_lo + wave;
+  if (pr < cur.p_hi) {
     int blk[2];
-#pragma unroll
-    for (int sg = 0; sg < 2; ++sg) {
-      const int pg = min(2 * pr + sg, mbps - 1);
-      blk[sg] = clampi(btb[pg], 0, num_blocks - 1);
-    }
-    const uint16_t* kpage = kc + ((size_t)blk[k_page] * Hkv + g) * page_elems;
-    bf16x8 kf[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      kf[kk] = *reinterpret_cast<const bf16x8*>(kpage + ((2 * kk + hh) * 16 + k_tok) * 8);
-    bf16x8 vf[2][DT];
-#pragma unroll
-    for (int sg = 0; sg < 2; ++sg) {
-      const uint16_t* vpage = vc + ((size_t)blk[sg] * Hkv + g) * page_elems;
-#pragma unroll
-      for (int j = 0; j < DT; ++j)
-        vf[sg][j] = *reinterpret_cast<const bf16x8*>(vpage + (32 * j + l32) * 16 + 8 * hh);
-    }
-    const int key0 = pr * kPairKeys + 8 * hh;     // key of reg r: key0 + (r>>3)*16 + (r&7)
-    if (pr * kPairKeys + kPairKeys > L) {
-      // Slots past the sequence end may hold anything (even NaN); their
-      // probability is 0, but 0 * NaN would still reach O, so zero them.
-#pragma unroll
-      for (int sg = 0; sg < 2; ++sg)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (key0 + sg * 16 + e >= L)
-#pragma unroll
-            for (int j = 0; j < DT; ++j) vf[sg][j][e] = (__bf16)0.f;
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x16 s;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[nt][kk], s, 0, 0, 0);
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + (r >> 3) * 16 + (r & 7);
-        const float v = (key <= lim[nt]) ? s[r] * sl2 : -INFINITY;
-        s[r] = v;
-        mx = fmaxf(mx, v);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[nt], mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2_dev(m_run[nt] - m_use);
-      float rs = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = exp2_dev(s[r] - m_use);
-        rs += s[r];
-      }
-      rs += __shfl_xor(rs, 32, 64);
-      l_run[nt] = l_run[nt] * alpha + rs;
-      m_run[nt] = m_new;
-      bf16x8 pf[2];
-#pragma unroll
-      for (int sg = 0; sg < 2; ++sg)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[sg][e] = (__bf16)s[8 * sg + e];
-#pragma unroll
-      for (int j = 0; j < DT; ++j) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[nt][j][r] *= alpha;
-#pragma unroll
-        for (int sg = 0; sg < 2; ++sg)
-          o[nt][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[sg][j], pf[sg], o[nt][j], 0, 0, 0);
-      }
-    }
+    pair_blocks(blk, pr, bt + (size_t)cur.b * mbps, mbps, num_blocks);
+    load_k<D>(kf, blk, kc, Hkv, cur.g, k_page, k_tok, hh);
+    load_v<D>(vf, blk, vc, Hkv, cur.g, l32, hh);
   }
 
-  // Merge the 4 waves, one 32-row tile at a time, then write the output (one
-  // split) or this split's partial.
-  const int G_rows = rows;
-  const size_t part_base = ((size_t)(b * Hkv + g) * nsplit + split) * ROWS;
+  while (true) {
+    Seg nxt;
+    const bool has_next = next_segment(cur, nxt, u1, B, Hkv, K1, np_cap, kv_len);
+    const int nxt_first = nxt.p_lo + wave;        // this wave's first pair of nxt
+    const bool nxt_mine = has_next && nxt_first < nxt.p_hi;
+
+    f32x16 o[NT][DT];
+    float m_run[NT], l_run[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    if (lane < 32) { s_m[wave][nt * 32 + l32] = m_run[nt]; s_l[wave][nt * 32 + l32] = l_run[nt]; }
-    __syncthreads();
-    float mall = -INFINITY;
+    for (int nt = 0; nt < NT; ++nt) {
+      m_run[nt] = -INFINITY;
+      l_run[nt] = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) mall = fmaxf(mall, s_m[w][nt * 32 + l32]);
-    const float muse = (mall == -INFINITY) ? 0.f : mall;
-    const float f = exp2_dev(m_run[nt] - muse);
+      for (int j = 0; j < DT; ++j)
 #pragma unroll
-    for (int j = 0; j < DT; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int d = 32 * j + 8 * (r >> 2) + 4 * hh + (r & 3);
-        s_o[wave][l32][d] = o[nt][j][r] * f;
-      }
-    __syncthreads();
-    // 256 threads: row = tid / 8, 16 consecutive d per thread (D = 128) or 8 (D = 64).
-    constexpr int DPT = D / 8;
-    const int row_l = tid >> 3;
-    const int d0 = (tid & 7) * DPT;
-    const int row = nt * 32 + row_l;
-    float mrow = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) mrow = fmaxf(mrow, s_m[w][row]);
-    const float mu = (mrow == -INFINITY) ? 0.f : mrow;
-    float lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) lsum += s_l[w][row] * exp2_dev(s_m[w][row] - mu);
-    float acc[DPT];
-#pragma unroll
-    for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-#pragma unroll
-      for (int e = 0; e < DPT; ++e) acc[e] += s_o[w][row_l][d0 + e];
-    if (row < G_rows) {
-      if (my_splits == 1) {
-        const int hq = row / K1, i = row - hq * K1;
-        uint16_t* op = out + (((size_t)b * K1 + i) * Hq + (size_t)g * G + hq) * D + d0;
-        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-#pragma unroll
-        for (int e = 0; e < DPT; e += 2) {
-          const __bf16 lo = (__bf16)(acc[e] * inv);
-          const __bf16 hi = (__bf16)(acc[e + 1] * inv);
-          const uint32_t w = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                             ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-          *reinterpret_cast<uint32_t*>(op + e) = w;
-        }
-      } else {
-        float* pp = opart + (part_base + row) * D + d0;
-#pragma unroll
-        for (int e = 0; e < DPT; e += 4)
-          *reinterpret_cast<float4*>(pp + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
-        if ((tid & 7) == 0) ml[part_base + row] = make_float2(mrow, lsum);
-      }
+        for (int r = 0; r < 16; ++r) o[nt][j][r] = 0.f;
     }
+
+    // Staggered pipeline over this wave's pairs (4 apart): the next pair's K
+    // is requested right after this pair's scores and its V right after P.V.
+    // After the last pair of the segment, the "next pair" is this wave's
+    // first pair of the next segment, so its loads fly during the merge.
+    const int32_t* btb = bt + (size_t)cur.b * mbps;
+    const int L = cur.L0 + K1;
+    bool prefetched = false;
+    while (pr < cur.p_hi) {
+#if SV_ATTN_DYN
+      int claim = 0;
+      if (lane == 0) claim = atomicAdd(&s_ctr[0], 1);
+      const int nx = __builtin_amdgcn_readfirstlane(__shfl(claim, 0, 64));
+#else
+      const int nx = pr + 4;
+#endif
+      const bool in_seg = nx < cur.p_hi;
+      const bool cross = !in_seg && nxt_mine;
+      int nblk[2] = {0, 0};
+      if (in_seg) pair_blocks(nblk, nx, btb, mbps, num_blocks);
+      else if (cross) pair_blocks(nblk, nxt_first, bt + (size_t)nxt.b * mbps, mbps, num_blocks);
+      const int ng = cross ? nxt.g : cur.g;
+      bf16x8 pf[NT][2];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        score_pair<D, NT>(kf, pr, hh, nt, qf, lim, sl2, o, m_run, l_run, pf[nt]);
+      if (in_seg || cross) load_k<D>(kf, nblk, kc, Hkv, ng, k_page, k_tok, hh);
+      mask_v_tail<D>(vf, pr, L, hh);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) pv_pair<D, NT>(vf, nt, pf[nt], o);
+      if (in_seg || cross) load_v<D>(vf, nblk, vc, Hkv, ng, l32, hh);
+      prefetched |= cross;
+      pr = in_seg ? nx : cur.p_hi;
+    }
+    if (nxt_mine && !prefetched) {                 // no pair of mine in cur
+      int nblk[2];
+      pair_blocks(nblk, nxt_first, bt + (size_t)nxt.b * mbps, mbps, num_blocks);
+      load_k<D>(kf, nblk, kc, Hkv, nxt.g, k_page, k_tok, hh);
+      load_v<D>(vf, nblk, vc, Hkv, nxt.g, l32, hh);
+    }
+
+    // Merge the 4 waves one 32-row tile at a time (fixed order 0..3 into one
+    // LDS buffer), then write the output rows (whole segment) or the partial.
+    const size_t part_base = ((size_t)w * 2 + cur.slot) * ROWS;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      if (lane < 32) { s_m[wave][l32] = m_run[nt]; s_l[wave][l32] = l_run[nt]; }
+      __syncthreads();
+      float mall = -INFINITY;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) mall = fmaxf(mall, s_m[ww][l32]);
+      const float f = exp2_dev(m_run[nt] - ((mall == -INFINITY) ? 0.f : mall));
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        if (wave == ww) {
+#pragma unroll
+          for (int j = 0; j < DT; ++j)
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+              // regs 4qd..4qd+3 hold d = 32j + 8qd + 4hh + 0..3
+              float4* dst = reinterpret_cast<float4*>(&s_o[l32][32 * j + 8 * qd + 4 * hh]);
+              float4 v = make_float4(o[nt][j][4 * qd] * f, o[nt][j][4 * qd + 1] * f,
+                                     o[nt][j][4 * qd + 2] * f, o[nt][j][4 * qd + 3] * f);
+              if (ww != 0) {
+                const float4 a = *dst;
+                v.x += a.x; v.y += a.y; v.z += a.z; v.w += a.w;
+              }
+              *dst = v;
+            }
+        }
+        __syncthreads();
+      }
+      const int row_l = tid >> 3;
+      const int d0 = (tid & 7) * DPT;
+      const int row = nt * 32 + row_l;
+      const float mrow = fmaxf(fmaxf(s_m[0][row_l], s_m[1][row_l]), fmaxf(s_m[2][row_l], s_m[3][row_l]));
+      const float mu = (mrow == -INFINITY) ? 0.f : mrow;
+      float lsum = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) lsum += s_l[ww][row_l] * exp2_dev(s_m[ww][row_l] - mu);
+      float acc[DPT];
+#pragma unroll
+      for (int e = 0; e < DPT; e += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(&s_o[row_l][d0 + e]);
+        acc[e] = v.x; acc[e + 1] = v.y; acc[e + 2] = v.z; acc[e + 3] = v.w;
+      }
+      if (row < rows) {
+        if (cur.full) {
+          const int hq = row / K1, i = row - hq * K1;
+          uint16_t* op = out + (((size_t)cur.b * K1 + i) * Hq + (size_t)cur.g * G + hq) * D + d0;
+          const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+          for (int e = 0; e < DPT; e += 2) {
+            const __bf16 lo = (__bf16)(acc[e] * inv);
+            const __bf16 hi = (__bf16)(acc[e + 1] * inv);
+            const uint32_t wd = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+            *reinterpret_cast<uint32_t*>(op + e) = wd;
+          }
+        } else {
+          float* pp = opart + (part_base + row) * D + d0;
+#pragma unroll
+          for (int e = 0; e < DPT; e += 4)
+            *reinterpret_cast<float4*>(pp + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+          if ((tid & 7) == 0) ml[part_base + row] = make_float2(mrow, lsum);
+        }
+      }
+      __syncthreads();
+    }
+
+    if (!has_next) break;
+    // Every wave has stopped claiming (the merge barriers are behind us);
+    // arm the counter for the next piece before anyone can claim from it.
+    if (tid == 0) s_ctr[0] = nxt.p_lo + 4;
     __syncthreads();
+    cur = nxt;
+    // Q of the new segment (the loads of its first pair are already in flight).
+    load_q<D, NT>(qf, lim, q, cur, K1, Hq, G, rows, l32, hh);
+    pr = cur.p_lo + wave;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Split combine.  grid (Hkv, B), block 256: row = tid / 8, D/8 d's per thread.
+// Merge of the segments that span several workgroups.  grid (Hkv, B), block
+// 256: row = tid / 8, D/8 d's per thread.  Shares are visited in order.
 // ---------------------------------------------------------------------------
 template <int D, int NT>
-__global__ __launch_bounds__(kAttnThreads) void k_attn_combine(
+__global__ __launch_bounds__(kAttnThreads) void k_attn_stream_combine(
     const float* __restrict__ opart, const float2* __restrict__ ml, const int32_t* __restrict__ kv_len,
-    uint16_t* __restrict__ out, int K1, int Hq, int Hkv, int split_keys, int nsplit) {
+    uint16_t* __restrict__ out, int B, int K1, int Hq, int Hkv, int np_cap, int W) {
   constexpr int ROWS = 32 * NT;
   constexpr int DPT = D / 8;
+  __shared__ long long s_red[kAttnThreads / 64];
   const int g = blockIdx.x, b = blockIdx.y;
-  const int L = kv_len[b] + K1;
-  const int my_splits = min(nsplit, (L + split_keys - 1) / split_keys);
-  if (my_splits <= 1) return;
+  const int tid = threadIdx.x;
+  long long tot = 0, before = 0;
+  for (int bb = tid; bb < B; bb += kAttnThreads) {
+    const long long v = (long long)npairs_of(kv_len, bb, K1, np_cap) * Hkv;
+    tot += v;
+    if (bb < b) before += v;
+  }
+  const long long U = block_sum_ll(tot, s_red);
+  const long long off_b = block_sum_ll(before, s_red);
+  const int np = npairs_of(kv_len, b, K1, np_cap);
+  const long long ua = off_b + (long long)g * np, ub = ua + np;
+  const int wa = stream_owner(ua, U, W), wb = stream_owner(ub - 1, U, W);
+  if (wa == wb) return;                       // written whole by its workgroup
   const int G = Hq / Hkv;
   const int rows = G * K1;
-  const int tid = threadIdx.x;
   const int d0 = (tid & 7) * DPT;
   for (int row = tid >> 3; row < ROWS; row += kAttnThreads / 8) {
     if (row >= rows) break;
-    const size_t base = (size_t)(b * Hkv + g) * nsplit * ROWS + row;
     float m = -INFINITY;
-    for (int s = 0; s < my_splits; ++s) m = fmaxf(m, ml[base + (size_t)s * ROWS].x);
+    for (int ww = wa; ww <= wb; ++ww) {
+      if (stream_start(ww, U, W) >= stream_start(ww + 1, U, W)) continue;   // empty share
+      const int slot = (ww == wa && stream_start(wa, U, W) != ua) ? 1 : 0;
+      m = fmaxf(m, ml[((size_t)ww * 2 + slot) * ROWS + row].x);
+    }
     const float mu = (m == -INFINITY) ? 0.f : m;
     float lsum = 0.f;
     float acc[DPT];
 #pragma unroll
     for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
-    for (int s = 0; s < my_splits; ++s) {
-      const float2 st = ml[base + (size_t)s * ROWS];
+    for (int ww = wa; ww <= wb; ++ww) {
+      if (stream_start(ww, U, W) >= stream_start(ww + 1, U, W)) continue;
+      const int slot = (ww == wa && stream_start(wa, U, W) != ua) ? 1 : 0;
+      const size_t idx = ((size_t)ww * 2 + slot) * ROWS + row;
+      const float2 st = ml[idx];
       const float f = exp2_dev(st.x - mu);
       lsum += st.y * f;
-      const float* pp = opart + (base + (size_t)s * ROWS) * D + d0;
+      const float* pp = opart + idx * D + d0;
 #pragma unroll
       for (int e = 0; e < DPT; e += 4) {
         const float4 v = *reinterpret_cast<const float4*>(pp + e);
@@ -311,9 +588,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_combine(
     for (int e = 0; e < DPT; e += 2) {
       const __bf16 lo = (__bf16)(acc[e] * inv);
       const __bf16 hi = (__bf16)(acc[e + 1] * inv);
-      const uint32_t w = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                         ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-      *reinterpret_cast<uint32_t*>(op + e) = w;
+      const uint32_t wd = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      *reinterpret_cast<uint32_t*>(op + e) = wd;
     }
   }
 }
@@ -382,38 +659,59 @@ __global__ __launch_bounds__(64) void k_attn_valu(
   }
 }
 
+static inline int attn_tiles(int G, int K1) { return (G * K1 + 31) / 32; }
+
 struct AttnPlan {
-  int split_keys, nsplit, tiles;
+  int W, tiles, np_cap;
+  bool too_big;
   size_t opart_bytes, ml_bytes;
 };
 
-static inline AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int max_kv_len) {
+// The workspace depends on the arguments only: partial slots for the largest
+// grid.  The grid adds the device's CU count.
+static inline AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int max_kv_len, int n_cu) {
   AttnPlan p{};
   const int K1 = K + 1;
-  const int max_len = max_kv_len + K1;
-  p.split_keys = attn_split_keys(B, Hkv, max_len);
-  p.nsplit = (max_len + p.split_keys - 1) / p.split_keys;
   p.tiles = attn_tiles(Hq / Hkv, K1);
-  const size_t parts = (size_t)B * Hkv * p.nsplit * 32 * p.tiles;
-  p.opart_bytes = p.nsplit > 1 ? ((parts * D * sizeof(float) + 255) & ~(size_t)255) : 0;
-  p.ml_bytes = p.nsplit > 1 ? ((parts * sizeof(float2) + 255) & ~(size_t)255) : 0;
+  p.np_cap = (max_kv_len + K1 + kPairKeys - 1) / kPairKeys;
+  const long long u_max = (long long)B * Hkv * p.np_cap;
+  p.too_big = u_max >= (1LL << 30);
+  // Largest grid these arguments can get (argument-only, sizes the workspace),
+  // then the grid for this device.
+  const long long w_max = std::max<long long>(
+      1, std::min<long long>(u_max / SV_ATTN_MIN_PAIRS_PER_WG, kStreamMaxWG));
+  p.W = (int)std::min<long long>(w_max, (long long)SV_ATTN_WG_PER_CU * std::max(1, n_cu));
+  const size_t slots = w_max > 1 ? (size_t)w_max * 2 * 32 * p.tiles : 0;
+  p.opart_bytes = (slots * D * sizeof(float) + 255) & ~(size_t)255;
+  p.ml_bytes = (slots * sizeof(float2) + 255) & ~(size_t)255;
   return p;
 }
 
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cached[dev] = n;      // every caller stores the same value
+  return n;
+}
+
 template <int D, int NT>
-static hipError_t launch_mfma(const void* q, const void* kc, const void* vc, const int32_t* bt,
-                              const int32_t* kv_len, void* out, int B, int K1, int Hq, int Hkv,
-                              int num_blocks, int mbps, float sl2, const AttnPlan& p, char* ws,
-                              hipStream_t st) {
+static hipError_t launch_stream(const void* q, const void* kc, const void* vc, const int32_t* bt,
+                                const int32_t* kv_len, void* out, int B, int K1, int Hq, int Hkv,
+                                int num_blocks, int mbps, float sl2, const AttnPlan& p, char* ws,
+                                hipStream_t st) {
   float* opart = reinterpret_cast<float*>(ws);
   float2* ml = reinterpret_cast<float2*>(ws + p.opart_bytes);
-  hipLaunchKernelGGL((k_attn_mfma<D, NT>), dim3(p.nsplit, Hkv, B), dim3(kAttnThreads), 0, st,
+  hipLaunchKernelGGL((k_attn_stream<D, NT>), dim3(p.W), dim3(kAttnThreads), 0, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
-                     static_cast<const uint16_t*>(vc), bt, kv_len, static_cast<uint16_t*>(out), K1, Hq,
-                     Hkv, num_blocks, mbps, p.split_keys, p.nsplit, sl2, opart, ml);
-  if (p.nsplit > 1)
-    hipLaunchKernelGGL((k_attn_combine<D, NT>), dim3(Hkv, B), dim3(kAttnThreads), 0, st, opart, ml,
-                       kv_len, static_cast<uint16_t*>(out), K1, Hq, Hkv, p.split_keys, p.nsplit);
+                     static_cast<const uint16_t*>(vc), bt, kv_len, static_cast<uint16_t*>(out), B, K1,
+                     Hq, Hkv, num_blocks, mbps, p.np_cap, sl2, p.W, opart, ml);
+  if (p.W > 1)
+    hipLaunchKernelGGL((k_attn_stream_combine<D, NT>), dim3(Hkv, B), dim3(kAttnThreads), 0, st, opart,
+                       ml, kv_len, static_cast<uint16_t*>(out), B, K1, Hq, Hkv, p.np_cap, p.W);
   return hipGetLastError();
 }
 
@@ -422,7 +720,7 @@ static hipError_t launch_mfma(const void* q, const void* kc, const void* vc, con
 extern "C" size_t spec_verify_attn_workspace_bytes(int B, int K, int Hq, int Hkv, int D,
                                                    int max_kv_len) {
   if (B <= 0 || K < 1 || Hq < 1 || Hkv < 1 || D < 1 || max_kv_len < 0) return 0;
-  const sv::AttnPlan p = sv::attn_plan(B, K, Hq, Hkv, D, max_kv_len);
+  const sv::AttnPlan p = sv::attn_plan(B, K, Hq, Hkv, D, max_kv_len, 1);
   return p.opart_bytes + p.ml_bytes;
 }
 
@@ -455,8 +753,9 @@ extern "C" int spec_verify_attn(const void* q, const void* k_cache, const void* 
                        static_cast<float*>(out), K1, Hq, Hkv, D, num_blocks, max_blocks_per_seq, sl2);
     e = hipGetLastError();
   } else {
-    const sv::AttnPlan p = sv::attn_plan(B, K, Hq, Hkv, D, max_kv_len);
-    if (p.opart_bytes + p.ml_bytes > 0) {
+    const sv::AttnPlan p = sv::attn_plan(B, K, Hq, Hkv, D, max_kv_len, sv::device_cus());
+    if (p.too_big) return SV_ERR_UNSUPPORTED;
+    if (p.W > 1) {
       if (!workspace) return SV_ERR_INVALID_ARG;
       if (workspace_bytes < p.opart_bytes + p.ml_bytes) return SV_ERR_WORKSPACE;
       if (reinterpret_cast<uintptr_t>(workspace) & 255) return SV_ERR_INVALID_ARG;
@@ -466,15 +765,15 @@ extern "C" int spec_verify_attn(const void* q, const void* k_cache, const void* 
     if (al & 15) return SV_ERR_INVALID_ARG;
     char* ws = static_cast<char*>(workspace);
     if (D == 128) {
-      e = p.tiles == 1 ? sv::launch_mfma<128, 1>(q, k_cache, v_cache, block_table, kv_len, out, B, K1,
-                                                 Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, st)
-                       : sv::launch_mfma<128, 2>(q, k_cache, v_cache, block_table, kv_len, out, B, K1,
-                                                 Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, st);
+      e = p.tiles == 1 ? sv::launch_stream<128, 1>(q, k_cache, v_cache, block_table, kv_len, out, B, K1,
+                                                   Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, st)
+                       : sv::launch_stream<128, 2>(q, k_cache, v_cache, block_table, kv_len, out, B, K1,
+                                                   Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, st);
     } else {
-      e = p.tiles == 1 ? sv::launch_mfma<64, 1>(q, k_cache, v_cache, block_table, kv_len, out, B, K1,
-                                                Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, st)
-                       : sv::launch_mfma<64, 2>(q, k_cache, v_cache, block_table, kv_len, out, B, K1,
-                                                Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, st);
+      e = p.tiles == 1 ? sv::launch_stream<64, 1>(q, k_cache, v_cache, block_table, kv_len, out, B, K1,
+                                                  Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, st)
+                       : sv::launch_stream<64, 2>(q, k_cache, v_cache, block_table, kv_len, out, B, K1,
+                                                  Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, st);
     }
   }
   return e == hipSuccess ? SV_OK : SV_ERR_HIP;
