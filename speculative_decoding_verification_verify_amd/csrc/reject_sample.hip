@@ -7,34 +7,35 @@
 // passes), "Build it" steps 1-2 (p(d) <= 0 accepts; a zero-mass residual falls
 // back to q) and "Rolling back the KV cache" (logical length reset).
 //
-// Three kernels on the caller's stream:
-//   k_sweep   one pass over every logit row (the HBM-bound part): per 4096-
-//             entry chunk, the raw maximum and sum_v 2^(x_v c - m) in fp32
-//             (c = log2(e) / T), or the chunk argmax for greedy sequences.
-//             16-byte coalesced loads, one wave per chunk, butterfly
-//             reductions, no LDS.  These statistics feed the accept tests,
-//             whose decisions are only sensitive at the 1e-5 level.
-//   k_decide  per (sequence, 8192-entry chunk): merge the row statistics in a
-//             fixed order, run the accept tests and the first-rejection scan
-//             (every block of a sequence redundantly and bit-identically),
-//             then summarise its chunk of the one row pair the final draw
-//             needs (target and draft row n, or target row K for the bonus)
-//             in float64: sum e_q, sum e_p, and the same two sums over the
-//             entries with q > p, with e = 2^((x - xmax) c) from the float64
-//             exp2.  Those four sums give both the exact normalisers and the
-//             residual mass of the chunk, so the row pair is read once here.
-//             Greedy sequences are finished here.
-//   k_locate  per sampling sequence: float64 prefix over the chunk masses,
-//             pick the chunk holding u_K * Z, stage its float64 weights in LDS,
-//             scan them, emit the tokens and commit kv_len.
-// The final draw is therefore computed to ~1e-14 in probability mass, so it
-// agrees with a float64 reference except within a vanishing band around the
-// CDF edges.  No floating-point atomics and fixed merge orders: results are
-// bitwise reproducible run to run.
+// Four kernels on the caller's stream:
+//   k_sweep     one pass over every logit row (the HBM-bound part): per 4096-
+//               entry chunk, the raw maximum and sum_v 2^(x_v c - m) in fp32
+//               (c = log2(e) / T), or the chunk argmax for greedy sequences.
+//               One wave per chunk, 16-byte nontemporal loads (1 KB
+//               contiguous per instruction), butterfly reductions, no LDS.
+//               These statistics feed the accept tests, whose decisions are
+//               only sensitive at the 1e-5 level.
+//   k_decide    per sequence: merge the row statistics in a fixed order, run
+//               the K accept tests in parallel and take the first rejection;
+//               finish a greedy sequence, or record the decision.
+//   k_residual  per (sequence, 8192-entry chunk): summarise its chunk of the
+//               one row pair the final draw needs (target and draft row n, or
+//               target row K for the bonus) in float64, per 256-entry
+//               sub-chunk and per chunk: sum e_q, sum e_p and the same two
+//               sums over the entries with q > p, with e = 2^((x - xmax) c)
+//               to a few ulp.  They give the exact normalisers and residual
+//               masses, so the row pair is read only once more.
+//   k_locate    per sampling sequence: float64 prefix scans over the chunk
+//               masses, then the sub-chunk masses, then one 256-entry run of
+//               exact weights; emit the tokens and commit kv_len.
+// The final draw is computed to ~1e-14 in probability mass, so it agrees with
+// a float64 reference except within a vanishing band around the CDF edges.
+// No floating-point atomics and fixed reduction orders: results are bitwise
+// reproducible run to run.
 
-// Contraction off: the weights recomputed by k_locate must equal the ones of
-// k_decide bit for bit, and merges must stay symmetric in their operands.
-// Fused multiply-adds that are wanted are written out.
+// Contraction off: merges must stay symmetric in their operands, and the
+// weights of k_locate must equal those of k_residual bit for bit.  Fused
+// multiply-adds that are wanted are written out.
 #pragma clang fp contract(off)
 
 #include "common.h"
@@ -42,30 +43,33 @@
 namespace sv {
 
 constexpr int kThreads = 256;
-constexpr int kSweepChunk = 4096;   // elements per wave in k_sweep
-constexpr int kResChunk = 8192;     // elements per block in k_decide / k_locate
+constexpr int kDecideThreads = 1024;  // one wave per row statistic merge
+constexpr int kSweepChunk = 4096;     // entries per wave in k_sweep
+constexpr int kResChunk = 8192;       // entries per block in k_residual
 constexpr int kMaxRows = 2 * SV_MAX_K + 1;
-constexpr int kPartStage = 4096;    // row statistics staged in LDS per sequence (32 KB)
+constexpr int kPartStage = 4096;      // row statistics staged in LDS per sequence (32 KB)
 constexpr double kLog2eD = 1.4426950408889634074;
 
+// What k_decide leaves for the final draw of a sampling sequence.
 struct Decision {
-  int n;          // accepted drafts
-  float xmq;      // raw maximum of target row n
-  float xmp;      // raw maximum of draft row n (unused when n == K)
+  int n;             // accepted drafts
+  float xmq, xmp;    // raw maxima of target row n and draft row n (xmp unused when n == K)
   float pad;
+  double theta;      // log2(sq / sp) of the sweep's normalisers: q > p iff aq - ap > theta
 };
 
+// Per-chunk float64 sums (e = unnormalised weight in the 2^((x - xmax) c) frame).
 struct ChunkSums {
   double eq, ep;  // sum of e_q, e_p over the chunk
-  double a, b;    // the same sums over entries with q > p
+  double a, b;    // the same sums over the entries with q > p
 };
 
-// The same sums for each 256-entry sub-chunk (a, b as above, q = sum e_q);
-// the final draw narrows chunk -> sub-chunk -> entry.
+// The same sums per 256-entry sub-chunk; the final draw narrows
+// chunk -> sub-chunk -> entry.
 constexpr int kSub = 256;
 constexpr int kSubPerChunk = kResChunk / kSub;
 struct SubSums {
-  double a, b, q;
+  double a, b, q, p;
 };
 
 __host__ __device__ inline int sweep_chunks(int V) { return (V + kSweepChunk - 1) / kSweepChunk; }
@@ -91,6 +95,46 @@ __device__ __forceinline__ void load_vec(const T* __restrict__ row, int e, int V
   } else {
 #pragma unroll
     for (int k = 0; k < VN; ++k) x[k] = (e + k < V) ? Vec16<T>::one(row + e + k) : -INFINITY;
+  }
+}
+
+// Raw 16-byte vector of a row at entry e (a multiple of the vector width),
+// read without a branch: past V the load goes to the row start and the
+// result is replaced by -inf bit patterns, so the loads of a lane can all be
+// in flight at once.
+template <typename T>
+__device__ __forceinline__ u32x4_t load_raw(const T* __restrict__ row, int e, int V) {
+  constexpr unsigned kNegInf = sizeof(T) == 2 ? 0xFF80FF80u : 0xFF800000u;
+  const bool in = e < V;
+  const u32x4_t r = *reinterpret_cast<const u32x4_t*>(row + (in ? e : 0));
+  return in ? r : u32x4_t{kNegInf, kNegInf, kNegInf, kNegInf};
+}
+
+template <typename T>
+__device__ __forceinline__ void widen_raw(const u32x4_t r, float (&f)[Vec16<T>::N]) {
+  if constexpr (sizeof(T) == 2) {
+    Vec16<uint16_t>::widen(r, f);
+  } else {
+    f[0] = __uint_as_float(r.x); f[1] = __uint_as_float(r.y);
+    f[2] = __uint_as_float(r.z); f[3] = __uint_as_float(r.w);
+  }
+}
+
+// Element loads for rows that are not 16-byte aligned, repacked as raw
+// vectors (exact: the values are logits of type T or -inf).
+template <typename T>
+__device__ __forceinline__ u32x4_t load_raw_unaligned(const T* __restrict__ row, int e, int V) {
+  float x[Vec16<T>::N];
+  load_vec<T, false>(row, e, V, x);
+  if constexpr (sizeof(T) == 2) {
+    unsigned w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = (__float_as_uint(x[2 * k]) >> 16) | (__float_as_uint(x[2 * k + 1]) & 0xffff0000u);
+    return u32x4_t{w[0], w[1], w[2], w[3]};
+  } else {
+    return u32x4_t{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                   __float_as_uint(x[3])};
   }
 }
 
@@ -211,85 +255,39 @@ __device__ __forceinline__ void merge_row(const float2* __restrict__ pr, int nc,
   }
 }
 
-__device__ __forceinline__ void emit(int b, int K, int n, int tok, const int32_t* __restrict__ dtok,
+// Write the K+1 output slots (threads 0..K of the block), the accepted count
+// and the committed length (thread 0).  The drafted tokens come from `sd`.
+__device__ __forceinline__ void emit(int b, int K, int n, int tok, const int* __restrict__ sd,
                                      int32_t* __restrict__ out, int32_t* __restrict__ nacc,
                                      int32_t* __restrict__ kv_len, unsigned long long* counters) {
-  for (int i = 0; i <= K; ++i) {
-    int v = -1;
-    if (i < n) v = dtok[(size_t)b * K + i];
-    else if (i == n) v = tok;
-    out[(size_t)b * (K + 1) + i] = v;
-  }
-  nacc[b] = n;
-  kv_len[b] = kv_len[b] + n + 1;
-  if (counters) {
-    atomicAdd(&counters[0], (unsigned long long)K);
-    atomicAdd(&counters[1], (unsigned long long)n);
+  const int i = threadIdx.x;
+  if (i <= K) out[(size_t)b * (K + 1) + i] = (i < n) ? sd[i] : (i == n ? tok : -1);
+  if (i == 0) {
+    nacc[b] = n;
+    kv_len[b] = kv_len[b] + n + 1;
+    if (counters) {
+      atomicAdd(&counters[0], (unsigned long long)K);
+      atomicAdd(&counters[1], (unsigned long long)n);
+    }
   }
 }
 
-// Float64 2^a for a <= 0, to a few ulp, at a fraction of the library
-// routine's cost.  With k = round(-16 a) (taken with the 2^52 + 2^51 shifter,
-// whose low word then holds k), 2^a = 2^(-k/16) * 2^r where r = a + k/16 is
-// exact and |r| <= 1/32.  2^(-k/16) comes from a table the block fills with
-// the device's float64 exp2; 2^r is the Taylor series of e^(r ln 2) to degree
-// 7, Horner form in r (first dropped term < 2e-18).  Arguments below -64 are
-// clamped there: such entries weigh < 5.4e-20 of the row maximum (whose
-// weight is 1), far below every tolerance; -inf gives exactly 0.
-constexpr int kExpTable = 1025;                  // 2^(-k/16), k = 0..1024
-
-__device__ __forceinline__ void fill_exp_table(double* tab) {
-  for (int k = threadIdx.x; k < kExpTable; k += blockDim.x) tab[k] = exp2(-(double)k * 0.0625);
-}
-
-__device__ __forceinline__ double exp2_neg(double a, const double* __restrict__ tab) {
-  const double ac = fmax(a, -64.0);
-  const double shifter = 6755399441055744.0;               // 2^52 + 2^51
-  const double t = fma(ac, -16.0, shifter);                // shifter + k
-  const int k = __double2loint(t);
-  const double r = fma(t - shifter, 0.0625, ac);           // a + k/16, exact
-  double p = 1.5252733804059838e-05;                       // ln2^7 / 7!
-  p = fma(p, r, 1.5403530393381606e-04);                   // ln2^6 / 6!
-  p = fma(p, r, 1.3333558146428441e-03);                   // ln2^5 / 5!
-  p = fma(p, r, 9.618129107628477e-03);                   // ln2^4 / 4!
-  p = fma(p, r, 5.5504108664821576e-02);                   // ln2^3 / 3!
-  p = fma(p, r, 2.402265069591007e-01);                   // ln2^2 / 2!
-  p = fma(p, r, 6.931471805599453e-01);                   // ln2
-  p = fma(p, r, 1.0);
-  const double v = tab[k] * p;
-  return (a == -INFINITY) ? 0.0 : v;
-}
-
-// Unnormalised float64 weight 2^((x - xmax) c) of one entry (x <= xmax).
-__device__ __forceinline__ double expw(float x, double xmax, double c, const double* __restrict__ tab) {
-  return exp2_neg(((double)x - xmax) * c, tab);
-}
-
-__device__ __forceinline__ double wave_sum_d(double x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
-
 // ---------------------------------------------------------------------------
-// k_decide: grid (B, ncr); block 256.
+// k_decide: grid (B); block 1024.
 // ---------------------------------------------------------------------------
-template <typename T, bool kAligned>
-__global__ __launch_bounds__(kThreads) void k_decide(
+template <typename T>
+__global__ __launch_bounds__(kDecideThreads) void k_decide(
     const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ dtok,
-    const float* __restrict__ uni, const float* __restrict__ temp, int K, int V, int nc, int ncr,
-    int force_greedy, const float2* __restrict__ part, ChunkSums* __restrict__ csum,
-    SubSums* __restrict__ csub, Decision* __restrict__ dec, int32_t* __restrict__ out,
-    int32_t* __restrict__ nacc, int32_t* __restrict__ kv_len, unsigned long long* counters) {
+    const float* __restrict__ uni, const float* __restrict__ temp, int K, int V, int nc,
+    int force_greedy, const float2* __restrict__ part, Decision* __restrict__ dec,
+    int32_t* __restrict__ out, int32_t* __restrict__ nacc, int32_t* __restrict__ kv_len,
+    unsigned long long* counters) {
   __shared__ float s_a[kMaxRows], s_b[kMaxRows];
   __shared__ float2 s_part[kPartStage];
-  __shared__ float s_xq[SV_MAX_K], s_xp[SV_MAX_K];
-  __shared__ int s_d[SV_MAX_K];
+  __shared__ float s_xq[SV_MAX_K], s_xp[SV_MAX_K], s_u[SV_MAX_K];
+  __shared__ int s_d[SV_MAX_K], s_draw[SV_MAX_K];
   __shared__ int s_n;
-  __shared__ double s_red[4][kThreads / 64];
-  __shared__ double s_exp[kExpTable];
   const int b = blockIdx.x;
-  const int cr = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int R = 2 * K + 1;
   const float t = temp_of(temp, b, force_greedy);
@@ -297,136 +295,221 @@ __global__ __launch_bounds__(kThreads) void k_decide(
   const int rows = greedy ? K + 1 : R;
   const float c = greedy ? 0.f : kLog2e / t;
   // All independent loads first: the row statistics of this sequence (into
-  // LDS when they fit) and the drafted tokens' logits.
+  // LDS when they fit), the drafted tokens, their logits and the uniforms.
   const float2* pb = part + (size_t)b * R * nc;
   const bool staged = rows * nc <= kPartStage;
   if (staged)
-    for (int k = tid; k < rows * nc; k += kThreads) s_part[k] = pb[k];
-  if (!greedy) fill_exp_table(s_exp);
+    for (int k = tid; k < rows * nc; k += kDecideThreads) s_part[k] = pb[k];
   if (tid < K) {
-    const int d = clampi(dtok[(size_t)b * K + tid], 0, V - 1);
+    const int draw = dtok[(size_t)b * K + tid];
+    const int d = clampi(draw, 0, V - 1);
+    s_draw[tid] = draw;
     s_d[tid] = d;
     if (!greedy) {
       s_xq[tid] = Vec16<T>::one(tgt + ((size_t)b * (K + 1) + tid) * (size_t)V + d);
       s_xp[tid] = Vec16<T>::one(drf + ((size_t)b * K + tid) * (size_t)V + d);
+      s_u[tid] = uni[(size_t)b * (K + 1) + tid];
     }
   }
   __syncthreads();
-  for (int r = wave; r < rows; r += kThreads / 64) {
+  for (int r = wave; r < rows; r += kDecideThreads / 64) {
     float a, bb;
     merge_row(staged ? s_part + r * nc : pb + (size_t)r * nc, nc, greedy, c, lane, a, bb);
     if (lane == 0) { s_a[r] = a; s_b[r] = bb; }
   }
   __syncthreads();
-  if (tid == 0) {
-    int n = 0;
-    for (int i = 0; i < K; ++i) {
-      const int d = s_d[i];
-      bool acc;
+  // Accept tests of all K drafts at once (lanes of wave 0), then the first
+  // rejection.
+  if (wave == 0) {
+    bool acc = false;
+    if (lane < K) {
+      const int i = lane;
       if (greedy) {
-        acc = (d == __float_as_int(s_b[i]));
+        acc = (s_d[i] == __float_as_int(s_b[i]));
+      } else if (s_xp[i] == -INFINITY) {
+        acc = true;                                   // p(d) == 0
       } else {
-        const float xq = s_xq[i];
-        const float xp = s_xp[i];
-        if (xp == -INFINITY) {
-          acc = true;                                   // p(d) == 0
-        } else {
-          // q/p = 2^((xq c - mq) - (xp c - mp)) * sp / sq with m = fl(xmax c),
-          // taken in the log domain so small probabilities do not underflow.
-          const double mq = (double)(s_a[i] * c), mp = (double)(s_a[K + 1 + i] * c);
-          const double ly = ((double)xq * (double)c - mq) - ((double)xp * (double)c - mp);
-          const double r = exp2(ly) * ((double)s_b[K + 1 + i] / (double)s_b[i]);
-          acc = (double)uni[(size_t)b * (K + 1) + i] < fmin(1.0, r);
-        }
+        // q/p = 2^((xq c - mq) - (xp c - mp)) * sp / sq with m = fl(xmax c),
+        // taken in the log domain so small probabilities do not underflow.
+        const double mq = (double)(s_a[i] * c), mp = (double)(s_a[K + 1 + i] * c);
+        const double ly = ((double)s_xq[i] * (double)c - mq) - ((double)s_xp[i] * (double)c - mp);
+        const double r = exp2(ly) * ((double)s_b[K + 1 + i] / (double)s_b[i]);
+        acc = (double)s_u[i] < fmin(1.0, r);
       }
-      if (!acc) break;
-      ++n;
     }
-    s_n = n;
-    if (greedy) {
-      if (cr == 0) emit(b, K, n, __float_as_int(s_b[n]), dtok, out, nacc, kv_len, counters);
-    } else if (cr == 0) {
-      Decision dd;
-      dd.n = n;
-      dd.xmq = s_a[n];
-      dd.xmp = (n < K) ? s_a[K + 1 + n] : 0.f;
-      dd.pad = 0.f;
-      dec[b] = dd;
-    }
+    const unsigned long long rej = __ballot(lane < K && !acc);
+    if (lane == 0) s_n = rej ? (int)__builtin_ctzll(rej) : K;
   }
   __syncthreads();
-  if (greedy) return;
   const int n = s_n;
+  if (greedy) {
+    emit(b, K, n, __float_as_int(s_b[n]), s_draw, out, nacc, kv_len, counters);
+    return;
+  }
+  if (tid != 0) return;
+  const double cd = kLog2eD / (double)t;
+  Decision dd;
+  dd.n = n;
+  dd.xmq = s_a[n];
+  dd.xmp = (n < K) ? s_a[K + 1 + n] : 0.f;
+  dd.pad = 0.f;
+  dd.theta = 0.0;
+  if (n < K) {
+    // The sweep's normalisers, moved from the fl(xmax c) frame to the
+    // 2^((x - xmax) c) frame of the exact pass.
+    const double sq = (double)s_b[n] * exp2((double)(dd.xmq * c) - (double)dd.xmq * cd);
+    const double sp = (double)s_b[K + 1 + n] * exp2((double)(dd.xmp * c) - (double)dd.xmp * cd);
+    dd.theta = log2(sq) - log2(sp);
+  }
+  dec[b] = dd;
+}
+
+// Float64 2^a for a <= 0 (a slightly above 0 is fine too), to a few ulp.
+// With k = round(256 a) (taken with the 2^52 + 2^51 shifter, whose low word
+// then holds k), 2^a = 2^floor(k/256) * 2^((k mod 256)/256) * 2^r, where
+// r = a - k/256 is exact and |r| <= 1/512.  The middle factor comes from a
+// 256-entry table the block fills with the device's float64 exp2; 2^r is the
+// Taylor series of e^(r ln 2) to degree 4 (first dropped term < 4e-17); the
+// power of two is applied exactly by ldexp.  Arguments are clamped at -1100,
+// where ldexp underflows to exactly 0, so -inf weighs 0 and every other
+// entry gets its float64 value (denormal included).
+constexpr int kExpTable = 256;
+
+__device__ __forceinline__ void fill_exp_table(double* tab) {
+  for (int j = threadIdx.x; j < kExpTable; j += blockDim.x) tab[j] = exp2((double)j * (1.0 / 256));
+}
+
+__device__ __forceinline__ double exp2_neg(double a, const double* __restrict__ tab) {
+  const double ac = fmax(a, -1100.0);
+  const double shifter = 6755399441055744.0;               // 2^52 + 2^51
+  const double t = fma(ac, 256.0, shifter);                // shifter + k
+  const int k = __double2loint(t);
+  const double r = fma(t - shifter, -1.0 / 256, ac);       // a - k/256, exact
+  double p = 9.618129107628477e-03;                        // ln2^4 / 4!
+  p = fma(p, r, 5.550410866482158e-02);                    // ln2^3 / 3!
+  p = fma(p, r, 2.4022650695910072e-01);                   // ln2^2 / 2!
+  p = fma(p, r, 6.931471805599453e-01);                    // ln2
+  p = fma(p, r, 1.0);
+  return ldexp(tab[k & (kExpTable - 1)] * p, k >> 8);
+}
+
+// Exponent (x - xmax) c of one entry, as x c - fl(xmax c): the rounding of
+// fl(xmax c) is one factor common to the whole row, so it cancels in every
+// normalised weight.
+__device__ __forceinline__ double expo(float x, double c, double xmc) {
+  return fma((double)x, c, -xmc);
+}
+
+__device__ __forceinline__ double shfl_xor_d(double x, int off) { return __shfl_xor(x, off, 64); }
+
+// ---------------------------------------------------------------------------
+// k_residual: grid (B, ncr); block 256.  Sampling sequences only.
+//
+// Lane mapping: the 8 lanes of group g = lane / 8 in wave w own sub-chunk
+// w * 8 + g (256 entries).  Each of their loads covers one 128-byte line of it,
+// so an instruction of the wave still reads 8 whole lines, and a sub-chunk's
+// sums need only 3 butterfly steps.
+// ---------------------------------------------------------------------------
+template <typename T, bool kAligned>
+__global__ __launch_bounds__(kThreads) void k_residual(
+    const T* __restrict__ tgt, const T* __restrict__ drf, const float* __restrict__ temp, int K,
+    int V, int ncr, int force_greedy, const Decision* __restrict__ dec,
+    ChunkSums* __restrict__ csum, SubSums* __restrict__ csub) {
+  constexpr int VN = Vec16<T>::N;
+  constexpr int kLine = 8 * VN;                   // entries per 8-lane load (128 bytes)
+  constexpr int IT = kSub / kLine;                // loads per lane per row
+  static_assert(kThreads / 8 == kSubPerChunk, "one 8-lane group per sub-chunk");
+  __shared__ double s_exp[kExpTable];
+  __shared__ SubSums s_sub[kSubPerChunk];
+  const int b = blockIdx.x;
+  const int cr = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int sub_i = tid >> 3, s = tid & 7;
+  const float t = temp_of(temp, b, force_greedy);
+  if (!(t > 0.f)) return;
+  const Decision d = dec[b];
+  const int n = d.n;
   const bool bonus = (n == K);
   const double cd = kLog2eD / (double)t;
-  const float xmq = s_a[n];
-  const float xmp = bonus ? 0.f : s_a[K + 1 + n];
-  // Approximate normalisers (sweep precision, moved to the 2^((x - xmax) c)
-  // reference) only decide which entries count as q > p; an entry they
-  // misclassify has |q - p| ~ 1e-6 q, so the chunk masses move by ~1e-12.
-  const double sq_approx = (double)s_b[n] * exp2((double)(xmq * c) - (double)xmq * cd);
-  const double sp_approx =
-      bonus ? 1.0 : (double)s_b[K + 1 + n] * exp2((double)(xmp * c) - (double)xmp * cd);
   const T* trow = tgt + ((size_t)b * (K + 1) + n) * (size_t)V;
-  const T* drow = bonus ? trow : drf + ((size_t)b * K + n) * (size_t)V;
-  constexpr int VN = Vec16<T>::N;
-  constexpr int IT = kResChunk / (kThreads * VN);
-  constexpr int kSubLanes = kSub / VN;            // lanes covering one sub-chunk per step
-  const int lo = cr * kResChunk;
-  const double xmqd = (double)xmq, xmpd = (double)xmp;
-  SubSums* sub = csub + ((size_t)b * ncr + cr) * kSubPerChunk;
-  double eq = 0.0, ep = 0.0, sa = 0.0, sb = 0.0;
+  const T* drow = drf + ((size_t)b * K + (bonus ? 0 : n)) * (size_t)V;
+  const int e0 = cr * kResChunk + sub_i * kSub + s * VN;
+  // Loads first, so they are in flight while the table is filled.
+  u32x4_t rq[IT], rp[IT];
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int e = lo + it * kThreads * VN + tid * VN;
-    float xq[VN], xp[VN];
-    load_vec<T, kAligned>(trow, e, V, xq);
-    if (!bonus) load_vec<T, kAligned>(drow, e, V, xp);
-    double tq = 0.0, ta = 0.0, tb = 0.0;
+  for (int i = 0; i < IT; ++i)
+    rq[i] = kAligned ? load_raw<T>(trow, e0 + i * kLine, V) : load_raw_unaligned<T>(trow, e0 + i * kLine, V);
+  if (!bonus) {
 #pragma unroll
-    for (int k = 0; k < VN; ++k) {
-      if (e + k < V) {
-        const double wq = expw(xq[k], xmqd, cd, s_exp);
-        tq += wq;
-        if (!bonus) {
-          const double wp = expw(xp[k], xmpd, cd, s_exp);
-          ep += wp;
-          if (wq * sp_approx > wp * sq_approx) { ta += wq; tb += wp; }
-        }
+    for (int i = 0; i < IT; ++i)
+      rp[i] = kAligned ? load_raw<T>(drow, e0 + i * kLine, V) : load_raw_unaligned<T>(drow, e0 + i * kLine, V);
+  }
+  fill_exp_table(s_exp);
+  __syncthreads();
+  const double xmcq = (double)d.xmq * cd, xmcp = (double)d.xmp * cd;
+  // Entries past V hold -inf: weight exactly 0, and never classed q > p.
+  double sq = 0.0, sp = 0.0, sa = 0.0, sb = 0.0;
+  if (bonus) {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      float xq[VN];
+      widen_raw<T>(rq[i], xq);
+#pragma unroll
+      for (int k = 0; k < VN; ++k) sq += exp2_neg(expo(xq[k], cd, xmcq), s_exp);
+    }
+  } else {
+    const double theta = d.theta;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      float xq[VN], xp[VN];
+      widen_raw<T>(rq[i], xq);
+      widen_raw<T>(rp[i], xp);
+#pragma unroll
+      for (int k = 0; k < VN; ++k) {
+        const double aq = expo(xq[k], cd, xmcq);
+        const double ap = expo(xp[k], cd, xmcp);
+        const double wq = exp2_neg(aq, s_exp);
+        const double wp = exp2_neg(ap, s_exp);
+        sq += wq;
+        sp += wp;
+        // The sweep's normalisers only decide which entries count as q > p;
+        // an entry they misclassify has |q - p| ~ 1e-6 q, so the masses move
+        // by ~1e-12.  (-inf - -inf is NaN: not counted, weights are 0.)
+        const double f = (aq - ap > theta) ? 1.0 : 0.0;
+        sa = fma(wq, f, sa);
+        sb = fma(wp, f, sb);
       }
     }
-    eq += tq;
-    sa += ta;
-    sb += tb;
-    // Sub-chunk sums: kSubLanes consecutive lanes cover one 256-entry run.
-#pragma unroll
-    for (int off = kSubLanes / 2; off > 0; off >>= 1) {
-      tq += __shfl_xor(tq, off, 64);
-      ta += __shfl_xor(ta, off, 64);
-      tb += __shfl_xor(tb, off, 64);
-    }
-    if ((lane & (kSubLanes - 1)) == 0)
-      sub[it * (kThreads * VN / kSub) + (tid * VN) / kSub] = SubSums{ta, tb, tq};
   }
-  eq = wave_sum_d(eq);
-  ep = wave_sum_d(ep);
-  sa = wave_sum_d(sa);
-  sb = wave_sum_d(sb);
-  if (lane == 0) { s_red[0][wave] = eq; s_red[1][wave] = ep; s_red[2][wave] = sa; s_red[3][wave] = sb; }
+#pragma unroll
+  for (int off = 4; off > 0; off >>= 1) {
+    sq += shfl_xor_d(sq, off);
+    sp += shfl_xor_d(sp, off);
+    sa += shfl_xor_d(sa, off);
+    sb += shfl_xor_d(sb, off);
+  }
+  if (s == 0) {
+    const SubSums ss{sa, sb, sq, sp};
+    csub[((size_t)b * ncr + cr) * kSubPerChunk + sub_i] = ss;
+    s_sub[sub_i] = ss;
+  }
   __syncthreads();
-  if (tid == 0) {
-    ChunkSums cs{0.0, 0.0, 0.0, 0.0};
-    for (int w = 0; w < kThreads / 64; ++w) {
-      cs.eq += s_red[0][w]; cs.ep += s_red[1][w]; cs.a += s_red[2][w]; cs.b += s_red[3][w];
-    }
-    csum[(size_t)b * ncr + cr] = cs;
+  // Chunk sums: one component per thread, sub-chunks in order.  Component
+  // tid of ChunkSums {eq, ep, a, b} is component (tid + 2) % 4 of SubSums
+  // {a, b, q, p}.
+  if (tid < 4) {
+    const int comp = (tid + 2) & 3;
+    double acc = 0.0;
+    for (int j = 0; j < kSubPerChunk; ++j) acc += reinterpret_cast<const double*>(&s_sub[j])[comp];
+    reinterpret_cast<double*>(csum + (size_t)b * ncr + cr)[tid] = acc;
   }
 }
 
 // ---------------------------------------------------------------------------
 // k_locate: grid (B); block 256.  Sampling sequences only.  Narrows the draw
 // chunk -> sub-chunk (from the stored sums) -> entry (exact weights of one
-// 256-entry run, one per thread, scanned in fixed order).
+// 256-entry run, one per thread), each level by an inclusive float64 scan in
+// vocabulary order.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ double chunk_mass(const ChunkSums& cs, bool qonly, double isq, double isp) {
   return qonly ? cs.eq * isq : fmax(0.0, cs.a * isq - cs.b * isp);
@@ -435,7 +518,52 @@ __device__ __forceinline__ double sub_mass(const SubSums& ss, bool qonly, double
   return qonly ? ss.q * isq : fmax(0.0, ss.a * isq - ss.b * isp);
 }
 
-template <typename T, bool kAligned>
+// Inclusive scan of one wave, in lane order.
+__device__ __forceinline__ double wave_scan_d(double x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ double wave_sum_d(double x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// One wave walks `cnt` masses (mass(i)) in order: returns the first index
+// whose running sum from `base` exceeds `target` (or -1) and leaves in `base`
+// the running sum before it; `lastpos` gets the last index of positive mass
+// (-1 if none).
+template <typename F>
+__device__ __forceinline__ int wave_find(int cnt, F mass, double target, double& base, int& lastpos,
+                                         int lane) {
+  lastpos = -1;
+  int found = -1;
+  double carry = base;
+  for (int s0 = 0; s0 < cnt; s0 += 64) {
+    const int i = s0 + lane;
+    const double m = i < cnt ? mass(i) : 0.0;
+    const double incl = wave_scan_d(m, lane) + carry;
+    const unsigned long long pos = __ballot(m > 0.0);
+    if (pos) lastpos = s0 + 63 - (int)__builtin_clzll(pos);
+    const unsigned long long hit = __ballot(i < cnt && incl > target);
+    const double ex = __shfl_up(incl, 1, 64);
+    if (found < 0 && hit) {
+      const int l = (int)__builtin_ctzll(hit);
+      found = s0 + l;
+      const double exl = __shfl(ex, l, 64);
+      base = (l == 0) ? carry : exl;
+    }
+    carry = __shfl(incl, 63, 64);
+  }
+  return found;
+}
+
+template <typename T>
 __global__ __launch_bounds__(kThreads) void k_locate(
     const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ dtok,
     const float* __restrict__ uni, const float* __restrict__ temp, int K, int V, int ncr,
@@ -444,10 +572,10 @@ __global__ __launch_bounds__(kThreads) void k_locate(
     int32_t* __restrict__ kv_len, unsigned long long* counters) {
   static_assert(kSub == kThreads, "one sub-chunk entry per thread");
   __shared__ ChunkSums s_cs[kThreads];
-  __shared__ SubSums s_ss[kSubPerChunk];
   __shared__ double s_exp[kExpTable];
   __shared__ double s_wtot[kThreads / 64];
-  __shared__ int s_chunk, s_sub, s_fallback, s_useq, s_first, s_lastpos;
+  __shared__ int s_draw[SV_MAX_K];
+  __shared__ int s_chunk, s_sub, s_fallback, s_qonly, s_first, s_lastpos;
   __shared__ double s_base, s_target, s_isq, s_isp;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -457,84 +585,74 @@ __global__ __launch_bounds__(kThreads) void k_locate(
   const Decision d = dec[b];
   const int n = d.n;
   const bool bonus = (n == K);
-  // Chunk sums are loaded in parallel, then walked in order by thread 0.
+  if (tid < K) s_draw[tid] = dtok[(size_t)b * K + tid];
+  // Chunk sums staged in LDS when they fit (V <= 2^21), read in place otherwise.
   const ChunkSums* cg = csum + (size_t)b * ncr;
-  const bool cstaged = ncr <= kThreads;
-  if (cstaged && tid < ncr) s_cs[tid] = cg[tid];
+  const bool staged = ncr <= kThreads;
+  if (staged && tid < ncr) s_cs[tid] = cg[tid];
   fill_exp_table(s_exp);
   __syncthreads();
-  if (tid == 0) {
-    const ChunkSums* cs = cstaged ? s_cs : cg;
+  const ChunkSums* cs = staged ? s_cs : cg;
+  if (wave == 0) {
+    // Exact normalisers, then the residual (or q) masses of the chunks.
     double sq = 0.0, sp = 0.0;
-    for (int i = 0; i < ncr; ++i) { sq += cs[i].eq; sp += cs[i].ep; }
+    for (int i = lane; i < ncr; i += 64) { sq += cs[i].eq; sp += cs[i].ep; }
+    sq = wave_sum_d(sq);
+    sp = wave_sum_d(sp);
     const double isq = 1.0 / sq;
     const double isp = bonus ? 0.0 : 1.0 / sp;
+    bool qonly = bonus;
     double z = 0.0;
-    for (int i = 0; i < ncr; ++i) z += chunk_mass(cs[i], bonus, isq, isp);
-    const bool useq = !bonus && !(z > 0.0);                  // zero-mass residual: draw from q
-    const bool qonly = bonus || useq;
-    if (useq) { z = 0.0; for (int i = 0; i < ncr; ++i) z += chunk_mass(cs[i], true, isq, isp); }
-    const double target = (double)uni[(size_t)b * (K + 1) + K] * z;
-    double p = 0.0, base = 0.0;
-    int ch = -1;
-    for (int i = 0; i < ncr; ++i) {
-      const double p2 = p + chunk_mass(cs[i], qonly, isq, isp);
-      if (p2 > target) { ch = i; base = p; break; }
-      p = p2;
+    for (int i = lane; i < ncr; i += 64) z += chunk_mass(cs[i], qonly, isq, isp);
+    z = wave_sum_d(z);
+    if (!qonly && !(z > 0.0)) {                              // zero-mass residual: draw from q
+      qonly = true;
+      z = 0.0;
+      for (int i = lane; i < ncr; i += 64) z += chunk_mass(cs[i], true, isq, isp);
+      z = wave_sum_d(z);
     }
+    const double target = (double)uni[(size_t)b * (K + 1) + K] * z;
+    double base = 0.0;
+    int lastpos;
+    int ch = wave_find(ncr, [&](int i) { return chunk_mass(cs[i], qonly, isq, isp); }, target, base,
+                       lastpos, lane);
     int fb = 0;
     if (ch < 0) {                                             // rounding at u -> 1
       fb = 1;
-      for (int i = ncr - 1; i >= 0; --i)
-        if (chunk_mass(cs[i], qonly, isq, isp) > 0.0) { ch = i; break; }
-      if (ch < 0) ch = 0;
+      ch = lastpos < 0 ? 0 : lastpos;
     }
-    s_chunk = ch; s_fallback = fb; s_useq = useq ? 1 : 0;
-    s_base = base; s_target = target; s_isq = isq; s_isp = isp;
-    s_first = INT32_MAX; s_lastpos = -1;
+    // Sub-chunk level, same wave (no crossing is looked for once in fallback).
+    const SubSums* ss = csub + ((size_t)b * ncr + ch) * kSubPerChunk;
+    double base2 = base;
+    int lastsub;
+    int sc = wave_find(kSubPerChunk, [&](int j) { return sub_mass(ss[j], qonly, isq, isp); },
+                       fb ? (double)INFINITY : target, base2, lastsub, lane);
+    if (sc < 0) {                                             // no crossing left: last positive run
+      fb = 1;
+      sc = lastsub < 0 ? 0 : lastsub;
+    }
+    if (lane == 0) {
+      s_chunk = ch; s_sub = sc; s_fallback = fb; s_qonly = qonly ? 1 : 0;
+      s_base = base2; s_target = target; s_isq = isq; s_isp = isp;
+      s_first = INT32_MAX; s_lastpos = -1;
+    }
   }
   __syncthreads();
   const int ch = s_chunk;
-  const bool qonly = bonus || (s_useq != 0);
+  const bool qonly = s_qonly != 0;
   const double isq = s_isq, isp = s_isp;
-  if (tid < kSubPerChunk) s_ss[tid] = csub[((size_t)b * ncr + ch) * kSubPerChunk + tid];
-  __syncthreads();
-  if (tid == 0) {
-    int sc = -1;
-    double p = s_base, base = s_base;
-    if (!s_fallback) {
-      for (int j = 0; j < kSubPerChunk; ++j) {
-        const double p2 = p + sub_mass(s_ss[j], qonly, isq, isp);
-        if (p2 > s_target) { sc = j; base = p; break; }
-        p = p2;
-      }
-    }
-    if (sc < 0) {                                             // no crossing left: last positive run
-      s_fallback = 1;
-      for (int j = kSubPerChunk - 1; j >= 0; --j)
-        if (sub_mass(s_ss[j], qonly, isq, isp) > 0.0) { sc = j; break; }
-      if (sc < 0) sc = 0;
-    }
-    s_sub = sc;
-    s_base = base;
-  }
-  __syncthreads();
   const T* trow = tgt + ((size_t)b * (K + 1) + n) * (size_t)V;
-  const T* drow = bonus ? trow : drf + ((size_t)b * K + n) * (size_t)V;
+  const T* drow = drf + ((size_t)b * K + (bonus ? 0 : n)) * (size_t)V;
   const int e = ch * kResChunk + s_sub * kSub + tid;
   double w = 0.0;
   if (e < V) {
-    const double q = expw(Vec16<T>::one(trow + e), (double)d.xmq, cd, s_exp) * isq;
-    w = qonly ? q : fmax(0.0, q - expw(Vec16<T>::one(drow + e), (double)d.xmp, cd, s_exp) * isp);
+    const double q = exp2_neg(expo(Vec16<T>::one(trow + e), cd, (double)d.xmq * cd), s_exp) * isq;
+    w = qonly ? q
+              : fmax(0.0, q - exp2_neg(expo(Vec16<T>::one(drow + e), cd, (double)d.xmp * cd), s_exp) * isp);
   }
   // Inclusive prefix over the 256 entries in vocabulary order: a wave scan
   // plus the totals of the waves before (fixed order).
-  double incl = w;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
+  const double incl = wave_scan_d(w, lane);
   if (lane == 63) s_wtot[wave] = incl;
   __syncthreads();
   double run = s_base + incl;
@@ -542,12 +660,10 @@ __global__ __launch_bounds__(kThreads) void k_locate(
   if (!s_fallback && run > s_target) atomicMin(&s_first, e);
   if (w > 0.0) atomicMax(&s_lastpos, e);
   __syncthreads();
-  if (tid == 0) {
-    int tok = s_first;
-    if (tok == INT32_MAX) tok = s_lastpos;                   // no crossing: last positive weight
-    if (tok < 0) tok = clampi(ch * kResChunk + s_sub * kSub, 0, V - 1);
-    emit(b, K, n, tok, dtok, out, nacc, kv_len, counters);
-  }
+  int tok = s_first;
+  if (tok == INT32_MAX) tok = s_lastpos;                     // no crossing: last positive weight
+  if (tok < 0) tok = clampi(ch * kResChunk + s_sub * kSub, 0, V - 1);
+  emit(b, K, n, tok, s_draw, out, nacc, kv_len, counters);
 }
 
 struct RejectPlan {
@@ -583,10 +699,12 @@ static hipError_t launch_all(const void* tgt, const void* drf, const int32_t* dt
   const T* d = static_cast<const T*>(drf);
   hipLaunchKernelGGL((k_sweep<T, kAligned>), dim3(B * R, (nc + 3) / 4), dim3(kThreads), 0, st, t, d,
                      temp, K, V, nc, force_greedy, part);
-  hipLaunchKernelGGL((k_decide<T, kAligned>), dim3(B, ncr), dim3(kThreads), 0, st, t, d, dtok, uni,
-                     temp, K, V, nc, ncr, force_greedy, part, csum, csub, dec, out, nacc, kv_len, counters);
-  hipLaunchKernelGGL((k_locate<T, kAligned>), dim3(B), dim3(kThreads), 0, st, t, d, dtok, uni, temp,
-                     K, V, ncr, force_greedy, csum, csub, dec, out, nacc, kv_len, counters);
+  hipLaunchKernelGGL((k_decide<T>), dim3(B), dim3(kDecideThreads), 0, st, t, d, dtok, uni, temp, K, V,
+                     nc, force_greedy, part, dec, out, nacc, kv_len, counters);
+  hipLaunchKernelGGL((k_residual<T, kAligned>), dim3(B, ncr), dim3(kThreads), 0, st, t, d, temp, K, V,
+                     ncr, force_greedy, dec, csum, csub);
+  hipLaunchKernelGGL((k_locate<T>), dim3(B), dim3(kThreads), 0, st, t, d, dtok, uni, temp, K, V, ncr,
+                     force_greedy, csum, csub, dec, out, nacc, kv_len, counters);
   return hipGetLastError();
 }
 
@@ -607,7 +725,9 @@ extern "C" int spec_reject_sample(const void* target_logits, const void* draft_l
   if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_INVALID_ARG;
   if (K > SV_MAX_K) return SV_ERR_UNSUPPORTED;
   if ((long long)V >= (1LL << 31) / 4) return SV_ERR_UNSUPPORTED;
-  if ((long long)B * (2 * K + 1) > 0x7fffffffLL || (V + 16383) / 16384 > 65535)
+  // Grid limits: rows on x (31 bits), chunk groups and residual chunks on y (16 bits).
+  if ((long long)B * (2 * K + 1) > 0x7fffffffLL || (sv::sweep_chunks(V) + 3) / 4 > 65535 ||
+      sv::res_chunks(V) > 65535)
     return SV_ERR_UNSUPPORTED;
   if (B == 0) return SV_OK;
   if (!target_logits || !draft_tokens || !uniforms || !temperature || !out_tokens ||

@@ -687,17 +687,6 @@ static inline AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int max_k
   return p;
 }
 
-static int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64 && cached[dev] > 0) return cached[dev];
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-  if (dev < 64) cached[dev] = n;      // every caller stores the same value
-  return n;
-}
-
 template <int D, int NT>
 static hipError_t launch_stream(const void* q, const void* kc, const void* vc, const int32_t* bt,
                                 const int32_t* kv_len, void* out, int B, int K1, int Hq, int Hkv,

@@ -3,7 +3,7 @@
 Accepted lengths, emitted tokens and the committed kv_len must be bit-exact
 with the float64 oracle, except sequences the oracle flags as boundary
 trials: F1 (|u - q/p| < 1e-5 at an examined accept test) or F2 (the final
-draw's u*Z within 1e-5 probability mass of a CDF edge).  Flagged sequences
+draw's u*Z within 1e-10 probability mass of a CDF edge).  Flagged sequences
 are excluded from the exact comparison, counted and printed, and still
 checked for validity.  Greedy sequences have no flags: bit-exact always,
 lowest index on ties.
@@ -143,6 +143,15 @@ def test_mixed_temperatures_in_one_batch(gpu_lib, dev):
 def test_ragged_vocab(gpu_lib, dev, V, dtype):
     for temp in (1.0, 0.0):
         _case(gpu_lib, dev, 800 + V, 6, 3, V, dtype=dtype, sigma=0.8, temp=temp)
+
+
+@pytest.mark.parametrize("V", [600_000, 2_200_000])
+@pytest.mark.parametrize("sigma", [0.25, 1.05])
+def test_large_vocab(gpu_lib, dev, V, sigma):
+    # More than 64 residual chunks (the chunk scan spans several wave
+    # segments) and, at 2.2M, more than 256 (chunk sums read in place).
+    # sigma 0.25 accepts nearly every draft, so the bonus row is drawn too.
+    _case(gpu_lib, dev, 950 + V // 100_000, 3, 2, V, sigma=sigma, temp=1.0)
 
 
 @pytest.mark.parametrize("K", [1, 16])
