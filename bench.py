@@ -35,20 +35,27 @@ METRIC = "verified tokens/sec at batch 64, K=7, V=128256; % of peak HBM GB/s"
 PEAK_HBM_GBS = 8000.0
 
 
-def _file_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def _files_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def _traffic(kernel_src, launches_bytes):
-    """HBM traffic per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; else None."""
+def _traffic():
+    """HBM bytes per attention call from the committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size), if they
+    were taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "attn_llama8b_b64_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha256_16") != _file_hash(kernel_src):
+    try:
+        if rec.get("source_sha256_16") != _files_hash(rec["source_files"]):
+            return None
+    except (KeyError, OSError):
         return None
     return rec.get("bytes_per_launch")
 
@@ -61,8 +68,13 @@ def parse():
     p.add_argument("--config", default="llama8b_b64")
     p.add_argument("--temp", type=float, default=1.0)
     p.add_argument("--seed", type=int, default=2024)
-    p.add_argument("--cpu-sample", type=int, default=12,
+    p.add_argument("--cpu-sample", type=int, default=64,
                    help="sequences in the oracle's timed sample (0 disables)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="repeat the oracle over the sample until this much CPU time has passed")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="instead of the bench: copy MIB MiB device to device 8 times (the "
+                        "known-size kernel that scales the HBM byte counters), then exit")
     p.add_argument("--sets", type=int, default=3, help="rotating logit sets")
     return p.parse_args()
 
@@ -82,6 +94,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     sv.load()
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -163,12 +178,10 @@ def main():
     attn_bytes = kv_bytes + qo_bytes
     attn_us = float(attn_ms.mean() * 1e3)
     achieved = attn_bytes / (attn_us * 1e-6) / 1e9
-    attn_src = os.path.join(ROOT, "speculative_decoding_verification_verify_amd", "csrc",
-                            "verify_attn.hip")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": _traffic(attn_src, attn_bytes),
-                "kernel": "spec_verify_attn (k_attn_mfma + k_attn_combine)",
+                "traffic": _traffic(),
+                "kernel": "spec_verify_attn call = k_attn_stream + k_attn_stream_combine",
                 "algorithmic_bytes": attn_bytes, "avg_us": round(attn_us, 2)}
     rej_bytes = B * (2 * K + 1) * V * 2 if args.temp > 0 else B * K1 * V * 2
     rej_us = float(rej_ms.mean() * 1e3)
@@ -213,8 +226,23 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
+def copy_calibration(mib):
+    """A plain device-to-device copy of known size: its FETCH_SIZE / WRITE_SIZE
+    counters give the scale from counter units to bytes."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(8):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 8}), flush=True)
+
+
 def cpu_baseline(args, cfg, attn, host_rej, from_device):
-    """Time the oracle (as it stands) on the first ``cpu_sample`` sequences."""
+    """Time the oracle (as it stands) on the first ``cpu_sample`` sequences of
+    the same workload, repeated until ``cpu_seconds`` have passed."""
     import torch
     from oracle import attention as oat
     from oracle import reject as orj
@@ -238,19 +266,24 @@ def cpu_baseline(args, cfg, attn, host_rej, from_device):
     for b in range(n):
         m = (kvl[b] + cfg.K + 1 + 15) // 16
         bt_local[b, :m] = remap[bt[b, :m]]
-    t0 = time.perf_counter()
-    oat.verify_attention(q, kc, vc, bt_local, kvl)
-    t_attn = time.perf_counter() - t0
     h = host_rej
-    t0 = time.perf_counter()
-    res = orj.reject_sample(h["target"][idx], h["draft"][idx], h["draft_tokens"][idx],
-                            h["uniforms"][idx], h["temperature"][idx])
-    t_rej = time.perf_counter() - t0
-    tokens = int(res["num_accepted"].astype(np.int64).sum()) + n
+    t_attn = t_rej = 0.0
+    passes = tokens = 0
+    while passes == 0 or t_attn + t_rej < args.cpu_seconds:
+        t0 = time.perf_counter()
+        oat.verify_attention(q, kc, vc, bt_local, kvl)
+        t_attn += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        res = orj.reject_sample(h["target"][idx], h["draft"][idx], h["draft_tokens"][idx],
+                                h["uniforms"][idx], h["temperature"][idx])
+        t_rej += time.perf_counter() - t0
+        tokens += int(res["num_accepted"].astype(np.int64).sum()) + n
+        passes += 1
     return {"value": round(tokens / (t_attn + t_rej), 2), "unit": "tokens/s",
             "cores": int(blas_threads), "kind": "oracle",
-            "sample": "first %d of %d sequences of the same workload: float64 numpy oracle, "
-                      "attention %.2f s + reject %.2f s" % (n, cfg.B, t_attn, t_rej),
+            "sample": "first %d of %d sequences of the same workload (attention + reject), %d "
+                      "pass(es): float64 numpy oracle, attention %.2f s + reject %.2f s" %
+                      (n, cfg.B, passes, t_attn, t_rej),
             "host_cores_available": len(os.sched_getaffinity(0))}
 
 
