@@ -13,10 +13,12 @@ of the 256 MB Infinity Cache); every step gets its own pre-copied kv_len
 buffer, because the verifier commits into it.
 
 Prints one JSON line.  ``value`` = committed tokens per second: the sum over
-sequences of (accepted drafts + 1) per step, divided by the wall time of the
-timed steps.  ``roofline`` is for the dominant kernel (the attention call),
-from HIP events on the launch stream; ``cpu_baseline`` times the float64
-oracle on a bounded sample of the same workload on the host cores.
+sequences of (accepted drafts + 1) per step, divided by the time of the timed
+steps (HIP events around the whole loop; nothing else is in the stream).
+``roofline`` is for the dominant call (attention), timed afterwards over the
+same number of back-to-back launches with HIP events on the launch stream;
+``kernels`` gives the same for the reject call; ``cpu_baseline`` times the
+float64 oracle on a bounded sample of the same workload on the host cores.
 """
 
 import argparse
@@ -127,42 +129,37 @@ def main():
     n_acc = [torch.empty((B,), dtype=torch.int32, device=dev) for _ in range(args.sets)]
     torch.cuda.synchronize()
 
-    def step(s):
-        r = rsets[s % args.sets]["dev"]
+    def attn_call():
         sv.verify_attn(attn["q"], attn["k_cache"], attn["v_cache"], attn["block_table"], kv0,
                        out=attn_out, max_kv_len=max_kv, workspace=attn_ws)
-        mid = torch.cuda.Event(enable_timing=True)
-        mid.record()
+
+    def reject_call(s, kv):
+        r = rsets[s % args.sets]["dev"]
         sv.reject_sample(r["target"], r["draft"], r["draft_tokens"], r["uniforms"],
-                         r["temperature"], kv_bufs[s], out_tokens=out_tok[s % args.sets],
+                         r["temperature"], kv, out_tokens=out_tok[s % args.sets],
                          num_accepted=n_acc[s % args.sets], workspace=rej_ws)
-        return mid
+
+    def step(s):
+        attn_call()
+        reject_call(s, kv_bufs[s])
 
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
     emitted = [int(from_device(n_acc[j]).astype(np.int64).sum()) + B for j in range(args.sets)]
 
-    # ---- timed region ----------------------------------------------------
-    starts, mids, ends = [], [], []
+    # ---- timed region: whole verify steps, nothing else in the stream -----
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
     for s in range(args.warmup, n_total):
-        a = torch.cuda.Event(enable_timing=True)
-        a.record()
-        m = step(s)
-        e = torch.cuda.Event(enable_timing=True)
-        e.record()
-        starts.append(a), mids.append(m), ends.append(e)
+        step(s)
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t0.elapsed_time(t1)
-    attn_ms = np.array([a.elapsed_time(m) for a, m in zip(starts, mids)])
-    rej_ms = np.array([m.elapsed_time(e) for m, e in zip(mids, ends)])
     tokens = sum(emitted[s % args.sets] for s in range(args.warmup, n_total))
     value = tokens / (total_ms / 1e3)
 
@@ -171,12 +168,29 @@ def main():
     assert np.array_equal(from_device(kv_bufs[last]),
                           from_device(kv0) + from_device(n_acc[last % args.sets]) + 1)
 
+    # ---- each call alone: the same number of back-to-back launches, bracketed
+    # by HIP events on the launch stream (torch's current stream) -------------
+    def timed(fn):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for s in range(args.steps):
+            fn(s)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    attn_ms = timed(lambda s: attn_call())
+    kv_scratch = kv0.clone()
+    rej_ms = timed(lambda s: reject_call(s, kv_scratch))
+
     # ---- roofline of the attention call (dominant kernel) ----------------
     kvl = from_device(kv0).astype(np.int64)
     kv_bytes = int((kvl + K1).sum()) * cfg.Hkv * cfg.D * 2 * 2
     qo_bytes = B * K1 * cfg.Hq * cfg.D * 2 * 2
     attn_bytes = kv_bytes + qo_bytes
-    attn_us = float(attn_ms.mean() * 1e3)
+    attn_us = float(attn_ms * 1e3)
     achieved = attn_bytes / (attn_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
@@ -184,7 +198,7 @@ def main():
                 "kernel": "spec_verify_attn call = k_attn_stream + k_attn_stream_combine",
                 "algorithmic_bytes": attn_bytes, "avg_us": round(attn_us, 2)}
     rej_bytes = B * (2 * K + 1) * V * 2 if args.temp > 0 else B * K1 * V * 2
-    rej_us = float(rej_ms.mean() * 1e3)
+    rej_us = float(rej_ms * 1e3)
     rej_gbs = rej_bytes / (rej_us * 1e-6) / 1e9
 
     # ---- CPU baseline: the oracle on a bounded sample ---------------------

@@ -8,14 +8,16 @@
 // "Quand et pourquoi utiliser le speculative decoding", section 1), so the
 // kernel is built to stream K and V once at full HBM bandwidth.
 //
-// bf16 path (k_attn_stream): a persistent grid of about two 4-wave workgroups
-// per CU.  The work list is every page pair (32 keys) of every (sequence, KV
-// head), in that order; each workgroup takes an equal contiguous share of it
+// bf16 path (k_attn_stream): a persistent grid, every workgroup resident from
+// the start (one 8-wave workgroup per CU for 32-row tiles; the 64-row variant
+// needs about 480 registers per lane and runs one 4-wave workgroup per CU).
+// The work list is every page pair (32 keys) of every (sequence, KV head), in
+// that order; each workgroup takes an equal contiguous share of it
 // (stream-K), so sequences of very different lengths still keep every CU busy
 // to the end.  Inside a share, each (sequence, KV head) segment is one online
 // softmax over all G = Hq/Hkv query heads and all K+1 positions of that KV
-// head (one or two 32-row tiles), so each K/V byte is read once.  Its 4 waves
-// take alternate page pairs:
+// head (one or two 32-row tiles), so each K/V byte is read once.  The waves
+// of a workgroup take every NW-th page pair:
 //   S^T (32 keys x 32 rows) = K . Q^T   8 x v_mfma_f32_32x32x16_bf16 (D=128)
 //   O^T (32 d x 32 rows)   += V^T . P^T 2 x 4 MFMAs per pair
 // The MFMA key order is permuted so that the C registers of S^T are exactly
@@ -24,16 +26,18 @@
 // vector with the 64 lanes of one instruction reading 512 contiguous bytes of
 // each page.  No LDS is touched in the key loop; the next pair's K is
 // requested right after this pair's scores and its V right after P.V, so
-// loads stay in flight through the softmax.  The waves merge through LDS at
-// the end of a segment.  A segment a workgroup covers entirely is written out
-// directly; the at most two partial segments of a workgroup go to the
-// workspace and k_attn_stream_combine merges them (log-sum-exp weights, fixed
-// order).
+// loads stay in flight through the softmax.  At the end of a segment each
+// wave stores its O, rescaled to the common row maximum, in its own LDS
+// buffer, and the buffers are summed in fixed wave order.  A segment a
+// workgroup covers entirely is written out directly; the at most two partial
+// segments of a workgroup go to the workspace and k_attn_stream_combine
+// merges them (log-sum-exp weights, fixed order).
 //
 // fp32 path (k_attn_valu): plain VALU kernel, one wave per query row; used for
 // fp32 caches (the correctness configuration).
 
 #include <algorithm>
+#include <atomic>
 
 #include "common.h"
 
@@ -43,7 +47,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kAttnThreads = 256;
+#ifndef SV_ATTN_WAVES
+#define SV_ATTN_WAVES 8         // waves per workgroup of the one-tile stream kernel
+#endif
+// Waves per workgroup: the two-tile kernel needs about 480 registers per
+// lane, so only one wave per SIMD fits and it keeps four waves.
+template <int NT> constexpr int stream_waves() { return NT == 1 ? SV_ATTN_WAVES : 4; }
+constexpr int kCombineThreads = 256;
 constexpr int kPairKeys = 32;
 constexpr int kStreamMaxWG = 1024;   // workspace is sized for this many workgroups
 
@@ -51,14 +61,8 @@ constexpr int kStreamMaxWG = 1024;   // workspace is sized for this many workgro
 #ifndef SV_ATTN_NT_LOADS
 #define SV_ATTN_NT_LOADS 1      // nontemporal K/V loads: streamed once, keep them out of L2
 #endif
-#ifndef SV_ATTN_WG_PER_CU
-#define SV_ATTN_WG_PER_CU 2     // persistent workgroups per CU
-#endif
 #ifndef SV_ATTN_MIN_PAIRS_PER_WG
 #define SV_ATTN_MIN_PAIRS_PER_WG 4
-#endif
-#ifndef SV_ATTN_DYN
-#define SV_ATTN_DYN 0           // waves claim page pairs from an LDS counter (not bitwise reproducible)
 #endif
 #ifndef SV_ATTN_LAZY
 #define SV_ATTN_LAZY 8.0f       // rescale O only when the row max grows by > 2^8
@@ -78,8 +82,11 @@ __device__ __forceinline__ bf16x8 load_kv(const uint16_t* p) {
 
 __device__ __forceinline__ void pair_blocks(int (&blk)[2], int pr, const int32_t* __restrict__ btb,
                                             int mbps, int num_blocks) {
-#pragma unroll
-  for (int sg = 0; sg < 2; ++sg) blk[sg] = clampi(btb[min(2 * pr + sg, mbps - 1)], 0, num_blocks - 1);
+  // Both table entries are requested before either is used (one wait).
+  const int e0 = btb[min(2 * pr, mbps - 1)];
+  const int e1 = btb[min(2 * pr + 1, mbps - 1)];
+  blk[0] = clampi(e0, 0, num_blocks - 1);
+  blk[1] = clampi(e1, 0, num_blocks - 1);
 }
 
 // K operand of a page pair: lane holds key k_tok of page k_page, chunks 2kk+hh.
@@ -182,13 +189,18 @@ __device__ __forceinline__ void pv_pair(const bf16x8 (&vf)[2][D / 32], int nt, c
       o[nt][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[sg][j], pf[sg], o[nt][j], 0, 0, 0);
 }
 
-// Page pairs of sequence b, capped by the grid's max_kv_len.
-__device__ __forceinline__ int npairs_of(const int32_t* __restrict__ kv_len, int b, int K1, int np_cap) {
-  const int L = kv_len[b] + K1;
+// Page pairs of a sequence with committed length L0, capped by the grid's
+// max_kv_len.
+__device__ __forceinline__ int npairs_from_len(int L0, int K1, int np_cap) {
+  const int L = L0 + K1;
   return min(np_cap, max(1, (L + kPairKeys - 1) / kPairKeys));
+}
+__device__ __forceinline__ int npairs_of(const int32_t* __restrict__ kv_len, int b, int K1, int np_cap) {
+  return npairs_from_len(kv_len[b], K1, np_cap);
 }
 
 // Block-wide sum of one value per thread (fixed order; all threads get it).
+template <int NTH>
 __device__ __forceinline__ long long block_sum_ll(long long v, long long* s_red) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
@@ -198,12 +210,13 @@ __device__ __forceinline__ long long block_sum_ll(long long v, long long* s_red)
   __syncthreads();
   long long t = 0;
 #pragma unroll
-  for (int w = 0; w < kAttnThreads / 64; ++w) t += s_red[w];
+  for (int w = 0; w < NTH / 64; ++w) t += s_red[w];
   return t;
 }
 
 // The sequence b holding work item u and the index of its first item,
 // Hkv * sum_{b' < b} npairs(b').  All threads return the same values.
+template <int NTH>
 __device__ void locate_work(const int32_t* __restrict__ kv_len, int B, int K1, int np_cap, int Hkv,
                             long long u, int& b_out, long long& off_out, long long* s_wsum,
                             long long* s_res, int* s_found) {
@@ -211,7 +224,7 @@ __device__ void locate_work(const int32_t* __restrict__ kv_len, int B, int K1, i
   __syncthreads();
   if (tid == 0) { s_found[0] = B; s_res[0] = 0; }
   long long carry = 0;
-  for (int base = 0; base < B; base += kAttnThreads) {
+  for (int base = 0; base < B; base += NTH) {
     const int b = base + tid;
     const long long v = (b < B) ? (long long)npairs_of(kv_len, b, K1, np_cap) * Hkv : 0;
     long long incl = v;
@@ -228,7 +241,7 @@ __device__ void locate_work(const int32_t* __restrict__ kv_len, int B, int K1, i
     if (b < B && ex <= u && u < ex + v) { s_found[0] = b; s_res[0] = ex; }
     long long tile = 0;
 #pragma unroll
-    for (int ww = 0; ww < kAttnThreads / 64; ++ww) tile += s_wsum[ww];
+    for (int ww = 0; ww < NTH / 64; ++ww) tile += s_wsum[ww];
     carry += tile;
     __syncthreads();
     if (s_found[0] < B) break;
@@ -311,7 +324,7 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[NT][D / 16], int (&lim)[NT],
 // slot 1: a segment that starts later and runs past its end.
 // ---------------------------------------------------------------------------
 template <int D, int NT>
-__global__ __launch_bounds__(kAttnThreads, NT == 1 ? SV_ATTN_WAVES_1T : 1) void k_attn_stream(
+__global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T * 4 / stream_waves<NT>() : 1) void k_attn_stream(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ kv_len, uint16_t* __restrict__ out,
     int B, int K1, int Hq, int Hkv, int num_blocks, int mbps, int np_cap, float sl2, int W,
@@ -320,13 +333,16 @@ __global__ __launch_bounds__(kAttnThreads, NT == 1 ? SV_ATTN_WAVES_1T : 1) void 
   constexpr int DT = D / 32;         // d tiles for O
   constexpr int ROWS = 32 * NT;
   constexpr int OPAD = D + 4;        // LDS row stride (floats)
-  constexpr int DPT = D / 8;         // output d's per thread in the epilogue
-  __shared__ float s_o[32][OPAD];
-  __shared__ float s_m[4][32], s_l[4][32];
-  __shared__ long long s_red[kAttnThreads / 64];
+  constexpr int NW = stream_waves<NT>();
+  constexpr int kStreamThreads = 64 * NW;
+  constexpr int TPR = kStreamThreads / 32;   // epilogue threads per output row
+  constexpr int DPT = D / TPR;               // output d's per thread in the epilogue
+  __shared__ float s_o[NW][32][OPAD];        // one buffer per wave for the segment merge
+  __shared__ float s_m[NW][32], s_l[NW][32];
+  __shared__ long long s_red[NW];
   __shared__ long long s_res[1];
-  __shared__ int s_found[1];
-  __shared__ int s_ctr[1];          // next unclaimed page pair of the current piece
+  __shared__ int s_found[3];
+  __shared__ int s_wsum[NW];
 
   const int w = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -335,21 +351,51 @@ __global__ __launch_bounds__(kAttnThreads, NT == 1 ? SV_ATTN_WAVES_1T : 1) void 
   const int G = Hq / Hkv;
   const int rows = G * K1;
 
-  // Total work first: the share [u0, u1) depends on it.
-  long long tot = 0;
-  for (int bb = tid; bb < B; bb += kAttnThreads) tot += (long long)npairs_of(kv_len, bb, K1, np_cap) * Hkv;
-  // The host bounds the work list below 2^30 items, so it fits int; values
-  // that come back through LDS are made wave-uniform (scalar registers).
-  const int U = __builtin_amdgcn_readfirstlane((int)block_sum_ll(tot, s_red));
-  const int u0 = (int)stream_start(w, U, W), u1 = (int)stream_start(w + 1, U, W);
-  if (u0 >= u1) return;
-  int b;
-  int off_b;
-  {
+  // The share [u0, u1) needs the total work U, and its first item's
+  // sequence b with that sequence's first item off_b.  The host bounds the
+  // work list below 2^30 items, so these fit int; values that come back
+  // through LDS are made wave-uniform (scalar registers).
+  int U, u0, u1, b, off_b, L0b;
+  if (B <= kStreamThreads) {
+    // One read of kv_len and one block scan give all of it.
+    const int kvb = tid < B ? kv_len[tid] : 0;
+    const int v = tid < B ? npairs_from_len(kvb, K1, np_cap) * Hkv : 0;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += t;
+    }
+    if (lane == 63) s_wsum[tid >> 6] = incl;
+    if (tid == 0) s_found[0] = B;
+    __syncthreads();
+    int ex = incl - v, tot = 0;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      ex += (ww < (tid >> 6)) ? s_wsum[ww] : 0;
+      tot += s_wsum[ww];
+    }
+    U = __builtin_amdgcn_readfirstlane(tot);
+    u0 = (int)stream_start(w, U, W);
+    u1 = (int)stream_start(w + 1, U, W);
+    if (tid < B && ex <= u0 && u0 < ex + v) { s_found[0] = tid; s_found[1] = ex; s_found[2] = kvb; }
+    __syncthreads();
+    if (u0 >= u1) return;
+    b = __builtin_amdgcn_readfirstlane(s_found[0]);
+    off_b = __builtin_amdgcn_readfirstlane(s_found[1]);
+    L0b = __builtin_amdgcn_readfirstlane(s_found[2]);
+  } else {
+    long long tot = 0;
+    for (int bb = tid; bb < B; bb += kStreamThreads) tot += (long long)npairs_of(kv_len, bb, K1, np_cap) * Hkv;
+    U = __builtin_amdgcn_readfirstlane((int)block_sum_ll<kStreamThreads>(tot, s_red));
+    u0 = (int)stream_start(w, U, W);
+    u1 = (int)stream_start(w + 1, U, W);
+    if (u0 >= u1) return;
     long long off;
-    locate_work(kv_len, B, K1, np_cap, Hkv, u0, b, off, s_red, s_res, s_found);
+    locate_work<kStreamThreads>(kv_len, B, K1, np_cap, Hkv, u0, b, off, s_red, s_res, s_found);
     b = __builtin_amdgcn_readfirstlane(b);
     off_b = __builtin_amdgcn_readfirstlane((int)off);
+    L0b = b < B ? kv_len[b] : 0;
   }
   if (b >= B) return;                       // u0 < U always finds a sequence
   // K operand row of this lane: MFMA key mk = l32 -> page mk>>4, token below.
@@ -367,16 +413,10 @@ __global__ __launch_bounds__(kAttnThreads, NT == 1 ? SV_ATTN_WAVES_1T : 1) void 
   cur.p_hi = cur.p_lo + (cur.end - u0);
   cur.slot = 0;
   cur.full = (cur.p_lo == 0) && (cur.p_hi == cur.np);
-  cur.L0 = kv_len[b];
+  cur.L0 = L0b;
 
-  // Each wave's first pair of a piece is p_lo + wave; the rest are claimed
-  // from s_ctr in order of need, so the waves finish a piece together.
-  if (tid == 0) s_ctr[0] = cur.p_lo + 4;
-  __syncthreads();
-
-  bf16x8 qf[NT][KK];
-  int lim[NT];
-  load_q<D, NT>(qf, lim, q, cur, K1, Hq, G, rows, l32, hh);
+  // Wave v takes pairs p_lo + v, p_lo + v + NW, ... of each piece.
+  // First K/V as early as possible: page table, then the pages, then Q.
   bf16x8 kf[KK];
   bf16x8 vf[2][DT];
   int pr = cur.p_lo + wave;
@@ -386,6 +426,10 @@ __global__ __launch_bounds__(kAttnThreads, NT == 1 ? SV_ATTN_WAVES_1T : 1) void 
     load_k<D>(kf, blk, kc, Hkv, cur.g, k_page, k_tok, hh);
     load_v<D>(vf, blk, vc, Hkv, cur.g, l32, hh);
   }
+  bf16x8 qf[NT][KK];
+  int lim[NT];
+  load_q<D, NT>(qf, lim, q, cur, K1, Hq, G, rows, l32, hh);
+  __syncthreads();
 
   while (true) {
     Seg nxt;
@@ -413,13 +457,7 @@ __global__ __launch_bounds__(kAttnThreads, NT == 1 ? SV_ATTN_WAVES_1T : 1) void 
     const int L = cur.L0 + K1;
     bool prefetched = false;
     while (pr < cur.p_hi) {
-#if SV_ATTN_DYN
-      int claim = 0;
-      if (lane == 0) claim = atomicAdd(&s_ctr[0], 1);
-      const int nx = __builtin_amdgcn_readfirstlane(__shfl(claim, 0, 64));
-#else
-      const int nx = pr + 4;
-#endif
+      const int nx = pr + NW;
       const bool in_seg = nx < cur.p_hi;
       const bool cross = !in_seg && nxt_mine;
       int nblk[2] = {0, 0};
@@ -445,8 +483,10 @@ __global__ __launch_bounds__(kAttnThreads, NT == 1 ? SV_ATTN_WAVES_1T : 1) void 
       load_v<D>(vf, nblk, vc, Hkv, nxt.g, l32, hh);
     }
 
-    // Merge the 4 waves one 32-row tile at a time (fixed order 0..3 into one
-    // LDS buffer), then write the output rows (whole segment) or the partial.
+    // Merge the 4 waves one 32-row tile at a time: each wave stores its O,
+    // rescaled to the common row max, in its own LDS buffer; the sum over
+    // waves is taken in fixed order 0..3.  Then the output rows (whole
+    // segment) or the partial are written.
     const size_t part_base = ((size_t)w * 2 + cur.slot) * ROWS;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -454,40 +494,37 @@ __global__ __launch_bounds__(kAttnThreads, NT == 1 ? SV_ATTN_WAVES_1T : 1) void 
       __syncthreads();
       float mall = -INFINITY;
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) mall = fmaxf(mall, s_m[ww][l32]);
+      for (int ww = 0; ww < NW; ++ww) mall = fmaxf(mall, s_m[ww][l32]);
       const float f = exp2_dev(m_run[nt] - ((mall == -INFINITY) ? 0.f : mall));
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
-        if (wave == ww) {
+      for (int j = 0; j < DT; ++j)
 #pragma unroll
-          for (int j = 0; j < DT; ++j)
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-              // regs 4qd..4qd+3 hold d = 32j + 8qd + 4hh + 0..3
-              float4* dst = reinterpret_cast<float4*>(&s_o[l32][32 * j + 8 * qd + 4 * hh]);
-              float4 v = make_float4(o[nt][j][4 * qd] * f, o[nt][j][4 * qd + 1] * f,
-                                     o[nt][j][4 * qd + 2] * f, o[nt][j][4 * qd + 3] * f);
-              if (ww != 0) {
-                const float4 a = *dst;
-                v.x += a.x; v.y += a.y; v.z += a.z; v.w += a.w;
-              }
-              *dst = v;
-            }
+        for (int qd = 0; qd < 4; ++qd) {
+          // regs 4qd..4qd+3 hold d = 32j + 8qd + 4hh + 0..3
+          *reinterpret_cast<float4*>(&s_o[wave][l32][32 * j + 8 * qd + 4 * hh]) =
+              make_float4(o[nt][j][4 * qd] * f, o[nt][j][4 * qd + 1] * f,
+                          o[nt][j][4 * qd + 2] * f, o[nt][j][4 * qd + 3] * f);
         }
-        __syncthreads();
-      }
-      const int row_l = tid >> 3;
-      const int d0 = (tid & 7) * DPT;
+      __syncthreads();
+      const int row_l = tid / TPR;
+      const int d0 = (tid % TPR) * DPT;
       const int row = nt * 32 + row_l;
-      const float mrow = fmaxf(fmaxf(s_m[0][row_l], s_m[1][row_l]), fmaxf(s_m[2][row_l], s_m[3][row_l]));
+      float mrow = s_m[0][row_l];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) mrow = fmaxf(mrow, s_m[ww][row_l]);
       const float mu = (mrow == -INFINITY) ? 0.f : mrow;
       float lsum = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) lsum += s_l[ww][row_l] * exp2_dev(s_m[ww][row_l] - mu);
+      for (int ww = 0; ww < NW; ++ww) lsum += s_l[ww][row_l] * exp2_dev(s_m[ww][row_l] - mu);
       float acc[DPT];
 #pragma unroll
       for (int e = 0; e < DPT; e += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(&s_o[row_l][d0 + e]);
+        float4 v = *reinterpret_cast<const float4*>(&s_o[0][row_l][d0 + e]);
+#pragma unroll
+        for (int ww = 1; ww < NW; ++ww) {
+          const float4 a = *reinterpret_cast<const float4*>(&s_o[ww][row_l][d0 + e]);
+          v.x = a.x + v.x; v.y = a.y + v.y; v.z = a.z + v.z; v.w = a.w + v.w;
+        }
         acc[e] = v.x; acc[e + 1] = v.y; acc[e + 2] = v.z; acc[e + 3] = v.w;
       }
       if (row < rows) {
@@ -508,17 +545,13 @@ __global__ __launch_bounds__(kAttnThreads, NT == 1 ? SV_ATTN_WAVES_1T : 1) void 
 #pragma unroll
           for (int e = 0; e < DPT; e += 4)
             *reinterpret_cast<float4*>(pp + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
-          if ((tid & 7) == 0) ml[part_base + row] = make_float2(mrow, lsum);
+          if (tid % TPR == 0) ml[part_base + row] = make_float2(mrow, lsum);
         }
       }
       __syncthreads();
     }
 
     if (!has_next) break;
-    // Every wave has stopped claiming (the merge barriers are behind us);
-    // arm the counter for the next piece before anyone can claim from it.
-    if (tid == 0) s_ctr[0] = nxt.p_lo + 4;
-    __syncthreads();
     cur = nxt;
     // Q of the new segment (the loads of its first pair are already in flight).
     load_q<D, NT>(qf, lim, q, cur, K1, Hq, G, rows, l32, hh);
@@ -531,22 +564,22 @@ __global__ __launch_bounds__(kAttnThreads, NT == 1 ? SV_ATTN_WAVES_1T : 1) void 
 // 256: row = tid / 8, D/8 d's per thread.  Shares are visited in order.
 // ---------------------------------------------------------------------------
 template <int D, int NT>
-__global__ __launch_bounds__(kAttnThreads) void k_attn_stream_combine(
+__global__ __launch_bounds__(kCombineThreads) void k_attn_stream_combine(
     const float* __restrict__ opart, const float2* __restrict__ ml, const int32_t* __restrict__ kv_len,
     uint16_t* __restrict__ out, int B, int K1, int Hq, int Hkv, int np_cap, int W) {
   constexpr int ROWS = 32 * NT;
   constexpr int DPT = D / 8;
-  __shared__ long long s_red[kAttnThreads / 64];
+  __shared__ long long s_red[kCombineThreads / 64];
   const int g = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x;
   long long tot = 0, before = 0;
-  for (int bb = tid; bb < B; bb += kAttnThreads) {
+  for (int bb = tid; bb < B; bb += kCombineThreads) {
     const long long v = (long long)npairs_of(kv_len, bb, K1, np_cap) * Hkv;
     tot += v;
     if (bb < b) before += v;
   }
-  const long long U = block_sum_ll(tot, s_red);
-  const long long off_b = block_sum_ll(before, s_red);
+  const long long U = block_sum_ll<kCombineThreads>(tot, s_red);
+  const long long off_b = block_sum_ll<kCombineThreads>(before, s_red);
   const int np = npairs_of(kv_len, b, K1, np_cap);
   const long long ua = off_b + (long long)g * np, ub = ua + np;
   const int wa = stream_owner(ua, U, W), wb = stream_owner(ub - 1, U, W);
@@ -554,7 +587,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_stream_combine(
   const int G = Hq / Hkv;
   const int rows = G * K1;
   const int d0 = (tid & 7) * DPT;
-  for (int row = tid >> 3; row < ROWS; row += kAttnThreads / 8) {
+  for (int row = tid >> 3; row < ROWS; row += kCombineThreads / 8) {
     if (row >= rows) break;
     float m = -INFINITY;
     for (int ww = wa; ww <= wb; ++ww) {
@@ -662,29 +695,41 @@ __global__ __launch_bounds__(64) void k_attn_valu(
 static inline int attn_tiles(int G, int K1) { return (G * K1 + 31) / 32; }
 
 struct AttnPlan {
-  int W, tiles, np_cap;
+  int w_max, tiles, np_cap;
   bool too_big;
   size_t opart_bytes, ml_bytes;
 };
 
 // The workspace depends on the arguments only: partial slots for the largest
-// grid.  The grid adds the device's CU count.
-static inline AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int max_kv_len, int n_cu) {
+// grid these arguments can get.  The grid itself also depends on the device.
+static inline AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int max_kv_len) {
   AttnPlan p{};
   const int K1 = K + 1;
   p.tiles = attn_tiles(Hq / Hkv, K1);
   p.np_cap = (max_kv_len + K1 + kPairKeys - 1) / kPairKeys;
   const long long u_max = (long long)B * Hkv * p.np_cap;
   p.too_big = u_max >= (1LL << 30);
-  // Largest grid these arguments can get (argument-only, sizes the workspace),
-  // then the grid for this device.
   const long long w_max = std::max<long long>(
       1, std::min<long long>(u_max / SV_ATTN_MIN_PAIRS_PER_WG, kStreamMaxWG));
-  p.W = (int)std::min<long long>(w_max, (long long)SV_ATTN_WG_PER_CU * std::max(1, n_cu));
+  p.w_max = (int)w_max;
   const size_t slots = w_max > 1 ? (size_t)w_max * 2 * 32 * p.tiles : 0;
   p.opart_bytes = (slots * D * sizeof(float) + 255) & ~(size_t)255;
   p.ml_bytes = (slots * sizeof(float2) + 255) & ~(size_t)255;
   return p;
+}
+
+// Workgroups of k_attn_stream<D, NT> that are resident on one CU at once
+// (queried once per process; every caller stores the same value).
+template <int D, int NT>
+static int stream_blocks_per_cu() {
+  static std::atomic<int> cached{0};
+  int nb = cached.load(std::memory_order_relaxed);
+  if (nb > 0) return nb;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(&k_attn_stream<D, NT>),
+                                                   64 * stream_waves<NT>(), 0) != hipSuccess || nb <= 0)
+    nb = 1;
+  cached.store(nb, std::memory_order_relaxed);
+  return nb;
 }
 
 template <int D, int NT>
@@ -692,15 +737,18 @@ static hipError_t launch_stream(const void* q, const void* kc, const void* vc, c
                                 const int32_t* kv_len, void* out, int B, int K1, int Hq, int Hkv,
                                 int num_blocks, int mbps, float sl2, const AttnPlan& p, char* ws,
                                 hipStream_t st) {
+  // Persistent grid: every workgroup resident from the start.
+  const int W = (int)std::min<long long>(
+      p.w_max, (long long)stream_blocks_per_cu<D, NT>() * std::max(1, device_cus()));
   float* opart = reinterpret_cast<float*>(ws);
   float2* ml = reinterpret_cast<float2*>(ws + p.opart_bytes);
-  hipLaunchKernelGGL((k_attn_stream<D, NT>), dim3(p.W), dim3(kAttnThreads), 0, st,
+  hipLaunchKernelGGL((k_attn_stream<D, NT>), dim3(W), dim3(64 * stream_waves<NT>()), 0, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                      static_cast<const uint16_t*>(vc), bt, kv_len, static_cast<uint16_t*>(out), B, K1,
-                     Hq, Hkv, num_blocks, mbps, p.np_cap, sl2, p.W, opart, ml);
-  if (p.W > 1)
-    hipLaunchKernelGGL((k_attn_stream_combine<D, NT>), dim3(Hkv, B), dim3(kAttnThreads), 0, st, opart,
-                       ml, kv_len, static_cast<uint16_t*>(out), B, K1, Hq, Hkv, p.np_cap, p.W);
+                     Hq, Hkv, num_blocks, mbps, p.np_cap, sl2, W, opart, ml);
+  if (W > 1)
+    hipLaunchKernelGGL((k_attn_stream_combine<D, NT>), dim3(Hkv, B), dim3(kCombineThreads), 0, st, opart,
+                       ml, kv_len, static_cast<uint16_t*>(out), B, K1, Hq, Hkv, p.np_cap, W);
   return hipGetLastError();
 }
 
@@ -709,7 +757,7 @@ static hipError_t launch_stream(const void* q, const void* kc, const void* vc, c
 extern "C" size_t spec_verify_attn_workspace_bytes(int B, int K, int Hq, int Hkv, int D,
                                                    int max_kv_len) {
   if (B <= 0 || K < 1 || Hq < 1 || Hkv < 1 || D < 1 || max_kv_len < 0) return 0;
-  const sv::AttnPlan p = sv::attn_plan(B, K, Hq, Hkv, D, max_kv_len, 1);
+  const sv::AttnPlan p = sv::attn_plan(B, K, Hq, Hkv, D, max_kv_len);
   return p.opart_bytes + p.ml_bytes;
 }
 
@@ -742,9 +790,9 @@ extern "C" int spec_verify_attn(const void* q, const void* k_cache, const void* 
                        static_cast<float*>(out), K1, Hq, Hkv, D, num_blocks, max_blocks_per_seq, sl2);
     e = hipGetLastError();
   } else {
-    const sv::AttnPlan p = sv::attn_plan(B, K, Hq, Hkv, D, max_kv_len, sv::device_cus());
+    const sv::AttnPlan p = sv::attn_plan(B, K, Hq, Hkv, D, max_kv_len);
     if (p.too_big) return SV_ERR_UNSUPPORTED;
-    if (p.W > 1) {
+    if (p.w_max > 1) {
       if (!workspace) return SV_ERR_INVALID_ARG;
       if (workspace_bytes < p.opart_bytes + p.ml_bytes) return SV_ERR_WORKSPACE;
       if (reinterpret_cast<uintptr_t>(workspace) & 255) return SV_ERR_INVALID_ARG;
