@@ -14,10 +14,12 @@
 //               One wave per chunk, 16-byte nontemporal loads (1 KB
 //               contiguous per instruction), butterfly reductions, no LDS.
 //               These statistics feed the accept tests, whose decisions are
-//               only sensitive at the 1e-5 level.
+//               only sensitive at the 1e-5 level.  The wave whose chunk holds
+//               a row's drafted token also records that token's logit.
 //   k_decide    per sequence: merge the row statistics in a fixed order, run
-//               the K accept tests in parallel and take the first rejection;
-//               finish a greedy sequence, or record the decision.
+//               the K accept tests in parallel on the recorded logits and
+//               take the first rejection; finish a greedy sequence, or record
+//               the decision.
 //   k_residual  per (sequence, 8192-entry chunk): summarise its chunk of the
 //               one row pair the final draw needs (target and draft row n, or
 //               target row K for the bonus) in float64, per 256-entry
@@ -28,8 +30,12 @@
 //   k_locate    per sampling sequence: float64 prefix scans over the chunk
 //               masses, then the sub-chunk masses, then one 256-entry run of
 //               exact weights; emit the tokens and commit kv_len.
-// The final draw is computed to ~1e-14 in probability mass, so it agrees with
-// a float64 reference except within a vanishing band around the CDF edges.
+// The final draw's weights are exact to 2e-13 relative, so the draw agrees
+// with a float64 reference except within ~1e-12 of probability mass around
+// the CDF edges.  (Handing a sequence from its last k_residual block to the
+// draw inside one kernel would need device-scope fences per block, which
+// write back and invalidate each XCD's L2; measured, a kernel boundary is
+// far cheaper.)
 // No floating-point atomics and fixed reduction orders: results are bitwise
 // reproducible run to run.
 
@@ -44,11 +50,15 @@ namespace sv {
 
 constexpr int kThreads = 256;
 constexpr int kDecideThreads = 1024;  // one wave per row statistic merge
-constexpr int kSweepChunk = 4096;     // entries per wave in k_sweep
+#ifndef SV_SWEEP_CHUNK
+#define SV_SWEEP_CHUNK 4096
+#endif
+constexpr int kSweepChunk = SV_SWEEP_CHUNK;   // entries per wave in k_sweep
 constexpr int kResChunk = 8192;       // entries per block in k_residual
 constexpr int kMaxRows = 2 * SV_MAX_K + 1;
 constexpr int kPartStage = 4096;      // row statistics staged in LDS per sequence (32 KB)
 constexpr double kLog2eD = 1.4426950408889634074;
+
 
 // What k_decide leaves for the final draw of a sampling sequence.
 struct Decision {
@@ -145,8 +155,9 @@ __device__ __forceinline__ u32x4_t load_raw_unaligned(const T* __restrict__ row,
 // ---------------------------------------------------------------------------
 template <typename T, bool kAligned>
 __global__ __launch_bounds__(kThreads) void k_sweep(
-    const T* __restrict__ tgt, const T* __restrict__ drf, const float* __restrict__ temp,
-    int K, int V, int nc, int force_greedy, float2* __restrict__ part) {
+    const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ dtok,
+    const float* __restrict__ temp, int K, int V, int nc, int force_greedy,
+    float2* __restrict__ part, float* __restrict__ xd) {
   const int R = 2 * K + 1;
   const int row = blockIdx.x;
   const int b = row / R;
@@ -173,6 +184,25 @@ __global__ __launch_bounds__(kThreads) void k_sweep(
   } else {
 #pragma unroll
     for (int it = 0; it < IT; ++it) load_vec<T, kAligned, true>(src, base + it * 64 * VN, V, x[it]);
+  }
+  if (!greedy) {
+    // The logit of the drafted token d_jj in this row (target row jj < K or
+    // draft row jj), for the accept test: written by the lane that holds it.
+    const int jj = (j <= K) ? j : j - K - 1;
+    if (jj < K) {
+      const int dd = clampi(dtok[(size_t)b * K + jj], 0, V - 1);
+      const int off = dd - chunk * kSweepChunk;
+      if (off >= 0 && off < kSweepChunk && lane == (off / VN) % 64) {
+        const int it_d = off / (64 * VN), k_d = off % VN;
+        float v = 0.f;
+#pragma unroll
+        for (int it = 0; it < IT; ++it)
+#pragma unroll
+          for (int k = 0; k < VN; ++k)
+            if (it == it_d && k == k_d) v = x[it][k];
+        xd[((size_t)b * K + jj) * 2 + (j > K ? 1 : 0)] = v;
+      }
+    }
   }
   float2 res;
   if (greedy) {
@@ -275,11 +305,10 @@ __device__ __forceinline__ void emit(int b, int K, int n, int tok, const int* __
 // ---------------------------------------------------------------------------
 // k_decide: grid (B); block 1024.
 // ---------------------------------------------------------------------------
-template <typename T>
 __global__ __launch_bounds__(kDecideThreads) void k_decide(
-    const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ dtok,
-    const float* __restrict__ uni, const float* __restrict__ temp, int K, int V, int nc,
-    int force_greedy, const float2* __restrict__ part, Decision* __restrict__ dec,
+    const int32_t* __restrict__ dtok, const float* __restrict__ uni, const float* __restrict__ temp,
+    int K, int V, int nc, int force_greedy, const float2* __restrict__ part,
+    const float* __restrict__ xd, Decision* __restrict__ dec,
     int32_t* __restrict__ out, int32_t* __restrict__ nacc, int32_t* __restrict__ kv_len,
     unsigned long long* counters) {
   __shared__ float s_a[kMaxRows], s_b[kMaxRows];
@@ -294,8 +323,9 @@ __global__ __launch_bounds__(kDecideThreads) void k_decide(
   const bool greedy = !(t > 0.f);
   const int rows = greedy ? K + 1 : R;
   const float c = greedy ? 0.f : kLog2e / t;
-  // All independent loads first: the row statistics of this sequence (into
-  // LDS when they fit), the drafted tokens, their logits and the uniforms.
+  // All loads are independent: the row statistics of this sequence (into
+  // LDS when they fit), the drafted tokens, their logits (recorded by the
+  // sweep) and the uniforms.
   const float2* pb = part + (size_t)b * R * nc;
   const bool staged = rows * nc <= kPartStage;
   if (staged)
@@ -306,8 +336,8 @@ __global__ __launch_bounds__(kDecideThreads) void k_decide(
     s_draw[tid] = draw;
     s_d[tid] = d;
     if (!greedy) {
-      s_xq[tid] = Vec16<T>::one(tgt + ((size_t)b * (K + 1) + tid) * (size_t)V + d);
-      s_xp[tid] = Vec16<T>::one(drf + ((size_t)b * K + tid) * (size_t)V + d);
+      s_xq[tid] = xd[((size_t)b * K + tid) * 2];
+      s_xp[tid] = xd[((size_t)b * K + tid) * 2 + 1];
       s_u[tid] = uni[(size_t)b * (K + 1) + tid];
     }
   }
@@ -364,146 +394,67 @@ __global__ __launch_bounds__(kDecideThreads) void k_decide(
   dec[b] = dd;
 }
 
-// Float64 2^a for a <= 0 (a slightly above 0 is fine too), to a few ulp.
-// With k = round(256 a) (taken with the 2^52 + 2^51 shifter, whose low word
-// then holds k), 2^a = 2^floor(k/256) * 2^((k mod 256)/256) * 2^r, where
-// r = a - k/256 is exact and |r| <= 1/512.  The middle factor comes from a
-// 256-entry table the block fills with the device's float64 exp2; 2^r is the
-// Taylor series of e^(r ln 2) to degree 4 (first dropped term < 4e-17); the
-// power of two is applied exactly by ldexp.  Arguments are clamped at -1100,
-// where ldexp underflows to exactly 0, so -inf weighs 0 and every other
-// entry gets its float64 value (denormal included).
+// Float64 2^a for a <= 0 (a slightly above 0 is fine too), to a relative
+// error below 2e-13.  With k = round(256 a) (taken with the 2^52 + 2^51
+// shifter, whose low word then holds k), 2^a = 2^floor(k/256) *
+// 2^((k mod 256)/256) * 2^r, where r = a - k/256 is exact and |r| <= 1/512.
+// The middle factor comes from a 256-entry table the block fills with the
+// device's float64 exp2; 2^r is the Taylor series of e^(r ln 2) to degree 3
+// (first dropped term (r ln 2)^4 / 24 < 1.4e-13); the power of two is applied
+// exactly by ldexp.  Arguments are clamped at -1100, where ldexp underflows
+// to exactly 0, so -inf weighs 0.  The final draw needs the weights to ~1e-10
+// of the total mass at most, so 2e-13 leaves a wide margin.
+//
+// Callers pass A = 256 a, computed as x (256 c) - 256 fl(xmax c): scaling by
+// 256 is exact, so A is exactly 256 times the unscaled exponent, the
+// round(256 a) step becomes a plain add of the shifter, and the polynomial
+// takes R = 256 r with its coefficients scaled by 2^-8n (also exact): every
+// intermediate is the unscaled one times a power of two.  Split in two steps
+// so a caller can issue the table reads of several entries before it needs
+// any of them.
 constexpr int kExpTable = 256;
 
 __device__ __forceinline__ void fill_exp_table(double* tab) {
   for (int j = threadIdx.x; j < kExpTable; j += blockDim.x) tab[j] = exp2((double)j * (1.0 / 256));
 }
 
-__device__ __forceinline__ double exp2_neg(double a, const double* __restrict__ tab) {
-  const double ac = fmax(a, -1100.0);
+struct Exp2Arg {
+  double r;   // 256 a - k
+  int k;      // round(256 a)
+};
+
+__device__ __forceinline__ Exp2Arg exp2_reduce(double A) {
+  const double ac = fmax(A, -1100.0 * 256);
   const double shifter = 6755399441055744.0;               // 2^52 + 2^51
-  const double t = fma(ac, 256.0, shifter);                // shifter + k
-  const int k = __double2loint(t);
-  const double r = fma(t - shifter, -1.0 / 256, ac);       // a - k/256, exact
-  double p = 9.618129107628477e-03;                        // ln2^4 / 4!
-  p = fma(p, r, 5.550410866482158e-02);                    // ln2^3 / 3!
-  p = fma(p, r, 2.4022650695910072e-01);                   // ln2^2 / 2!
-  p = fma(p, r, 6.931471805599453e-01);                    // ln2
-  p = fma(p, r, 1.0);
-  return ldexp(tab[k & (kExpTable - 1)] * p, k >> 8);
+  const double t = ac + shifter;                           // shifter + k
+  Exp2Arg e;
+  e.k = __double2loint(t);
+  e.r = ac - (t - shifter);                                // exact
+  return e;
 }
 
-// Exponent (x - xmax) c of one entry, as x c - fl(xmax c): the rounding of
+__device__ __forceinline__ double exp2_finish(const Exp2Arg& e, double tab_k) {
+  double p = 3.3083026805413713e-09;                       // ln2^3 / 3! / 2^24
+  p = fma(p, e.r, 3.6655655969101062e-06);                 // ln2^2 / 2! / 2^16
+  p = fma(p, e.r, 2.7076061740622863e-03);                 // ln2 / 2^8
+  p = fma(p, e.r, 1.0);
+  return ldexp(tab_k * p, e.k >> 8);
+}
+
+__device__ __forceinline__ double exp2_neg(double A, const double* __restrict__ tab) {
+  const Exp2Arg e = exp2_reduce(A);
+  return exp2_finish(e, tab[e.k & (kExpTable - 1)]);
+}
+
+// Scaled exponent 256 (x - xmax) c of one entry, as x (256 c) - 256 fl(xmax c)
+// (c256 = 256 c, xmc256 = 256 fl(xmax c), both exact): the rounding of
 // fl(xmax c) is one factor common to the whole row, so it cancels in every
 // normalised weight.
-__device__ __forceinline__ double expo(float x, double c, double xmc) {
-  return fma((double)x, c, -xmc);
+__device__ __forceinline__ double expo(float x, double c256, double xmc256) {
+  return fma((double)x, c256, -xmc256);
 }
 
 __device__ __forceinline__ double shfl_xor_d(double x, int off) { return __shfl_xor(x, off, 64); }
-
-// ---------------------------------------------------------------------------
-// k_residual: grid (B, ncr); block 256.  Sampling sequences only.
-//
-// Lane mapping: the 8 lanes of group g = lane / 8 in wave w own sub-chunk
-// w * 8 + g (256 entries).  Each of their loads covers one 128-byte line of it,
-// so an instruction of the wave still reads 8 whole lines, and a sub-chunk's
-// sums need only 3 butterfly steps.
-// ---------------------------------------------------------------------------
-template <typename T, bool kAligned>
-__global__ __launch_bounds__(kThreads) void k_residual(
-    const T* __restrict__ tgt, const T* __restrict__ drf, const float* __restrict__ temp, int K,
-    int V, int ncr, int force_greedy, const Decision* __restrict__ dec,
-    ChunkSums* __restrict__ csum, SubSums* __restrict__ csub) {
-  constexpr int VN = Vec16<T>::N;
-  constexpr int kLine = 8 * VN;                   // entries per 8-lane load (128 bytes)
-  constexpr int IT = kSub / kLine;                // loads per lane per row
-  static_assert(kThreads / 8 == kSubPerChunk, "one 8-lane group per sub-chunk");
-  __shared__ double s_exp[kExpTable];
-  __shared__ SubSums s_sub[kSubPerChunk];
-  const int b = blockIdx.x;
-  const int cr = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int sub_i = tid >> 3, s = tid & 7;
-  const float t = temp_of(temp, b, force_greedy);
-  if (!(t > 0.f)) return;
-  const Decision d = dec[b];
-  const int n = d.n;
-  const bool bonus = (n == K);
-  const double cd = kLog2eD / (double)t;
-  const T* trow = tgt + ((size_t)b * (K + 1) + n) * (size_t)V;
-  const T* drow = drf + ((size_t)b * K + (bonus ? 0 : n)) * (size_t)V;
-  const int e0 = cr * kResChunk + sub_i * kSub + s * VN;
-  // Loads first, so they are in flight while the table is filled.
-  u32x4_t rq[IT], rp[IT];
-#pragma unroll
-  for (int i = 0; i < IT; ++i)
-    rq[i] = kAligned ? load_raw<T>(trow, e0 + i * kLine, V) : load_raw_unaligned<T>(trow, e0 + i * kLine, V);
-  if (!bonus) {
-#pragma unroll
-    for (int i = 0; i < IT; ++i)
-      rp[i] = kAligned ? load_raw<T>(drow, e0 + i * kLine, V) : load_raw_unaligned<T>(drow, e0 + i * kLine, V);
-  }
-  fill_exp_table(s_exp);
-  __syncthreads();
-  const double xmcq = (double)d.xmq * cd, xmcp = (double)d.xmp * cd;
-  // Entries past V hold -inf: weight exactly 0, and never classed q > p.
-  double sq = 0.0, sp = 0.0, sa = 0.0, sb = 0.0;
-  if (bonus) {
-#pragma unroll
-    for (int i = 0; i < IT; ++i) {
-      float xq[VN];
-      widen_raw<T>(rq[i], xq);
-#pragma unroll
-      for (int k = 0; k < VN; ++k) sq += exp2_neg(expo(xq[k], cd, xmcq), s_exp);
-    }
-  } else {
-    const double theta = d.theta;
-#pragma unroll
-    for (int i = 0; i < IT; ++i) {
-      float xq[VN], xp[VN];
-      widen_raw<T>(rq[i], xq);
-      widen_raw<T>(rp[i], xp);
-#pragma unroll
-      for (int k = 0; k < VN; ++k) {
-        const double aq = expo(xq[k], cd, xmcq);
-        const double ap = expo(xp[k], cd, xmcp);
-        const double wq = exp2_neg(aq, s_exp);
-        const double wp = exp2_neg(ap, s_exp);
-        sq += wq;
-        sp += wp;
-        // The sweep's normalisers only decide which entries count as q > p;
-        // an entry they misclassify has |q - p| ~ 1e-6 q, so the masses move
-        // by ~1e-12.  (-inf - -inf is NaN: not counted, weights are 0.)
-        const double f = (aq - ap > theta) ? 1.0 : 0.0;
-        sa = fma(wq, f, sa);
-        sb = fma(wp, f, sb);
-      }
-    }
-  }
-#pragma unroll
-  for (int off = 4; off > 0; off >>= 1) {
-    sq += shfl_xor_d(sq, off);
-    sp += shfl_xor_d(sp, off);
-    sa += shfl_xor_d(sa, off);
-    sb += shfl_xor_d(sb, off);
-  }
-  if (s == 0) {
-    const SubSums ss{sa, sb, sq, sp};
-    csub[((size_t)b * ncr + cr) * kSubPerChunk + sub_i] = ss;
-    s_sub[sub_i] = ss;
-  }
-  __syncthreads();
-  // Chunk sums: one component per thread, sub-chunks in order.  Component
-  // tid of ChunkSums {eq, ep, a, b} is component (tid + 2) % 4 of SubSums
-  // {a, b, q, p}.
-  if (tid < 4) {
-    const int comp = (tid + 2) & 3;
-    double acc = 0.0;
-    for (int j = 0; j < kSubPerChunk; ++j) acc += reinterpret_cast<const double*>(&s_sub[j])[comp];
-    reinterpret_cast<double*>(csum + (size_t)b * ncr + cr)[tid] = acc;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // k_locate: grid (B); block 256.  Sampling sequences only.  Narrows the draw
@@ -563,26 +514,23 @@ __device__ __forceinline__ int wave_find(int cnt, F mass, double target, double&
   return found;
 }
 
+// The final draw of sampling sequence b (block of kThreads threads), given
+// its decision d, all its chunk and sub-chunk sums, and the filled table.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_locate(
-    const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ dtok,
-    const float* __restrict__ uni, const float* __restrict__ temp, int K, int V, int ncr,
-    int force_greedy, const ChunkSums* __restrict__ csum, const SubSums* __restrict__ csub,
-    const Decision* __restrict__ dec, int32_t* __restrict__ out, int32_t* __restrict__ nacc,
+__device__ __forceinline__ void locate_seq(
+    int b, const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ dtok,
+    const float* __restrict__ uni, float t, int K, int V, int ncr,
+    const ChunkSums* __restrict__ csum, const SubSums* __restrict__ csub, const Decision& d,
+    const double* __restrict__ s_exp, int32_t* __restrict__ out, int32_t* __restrict__ nacc,
     int32_t* __restrict__ kv_len, unsigned long long* counters) {
   static_assert(kSub == kThreads, "one sub-chunk entry per thread");
   __shared__ ChunkSums s_cs[kThreads];
-  __shared__ double s_exp[kExpTable];
   __shared__ double s_wtot[kThreads / 64];
   __shared__ int s_draw[SV_MAX_K];
   __shared__ int s_chunk, s_sub, s_fallback, s_qonly, s_first, s_lastpos;
   __shared__ double s_base, s_target, s_isq, s_isp;
-  const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float t = temp_of(temp, b, force_greedy);
-  if (!(t > 0.f)) return;
   const double cd = kLog2eD / (double)t;
-  const Decision d = dec[b];
   const int n = d.n;
   const bool bonus = (n == K);
   if (tid < K) s_draw[tid] = dtok[(size_t)b * K + tid];
@@ -590,7 +538,6 @@ __global__ __launch_bounds__(kThreads) void k_locate(
   const ChunkSums* cg = csum + (size_t)b * ncr;
   const bool staged = ncr <= kThreads;
   if (staged && tid < ncr) s_cs[tid] = cg[tid];
-  fill_exp_table(s_exp);
   __syncthreads();
   const ChunkSums* cs = staged ? s_cs : cg;
   if (wave == 0) {
@@ -646,9 +593,11 @@ __global__ __launch_bounds__(kThreads) void k_locate(
   const int e = ch * kResChunk + s_sub * kSub + tid;
   double w = 0.0;
   if (e < V) {
-    const double q = exp2_neg(expo(Vec16<T>::one(trow + e), cd, (double)d.xmq * cd), s_exp) * isq;
+    const double c256 = cd * 256.0;
+    const double q = exp2_neg(expo(Vec16<T>::one(trow + e), c256, ((double)d.xmq * cd) * 256.0), s_exp) * isq;
     w = qonly ? q
-              : fmax(0.0, q - exp2_neg(expo(Vec16<T>::one(drow + e), cd, (double)d.xmp * cd), s_exp) * isp);
+              : fmax(0.0, q - exp2_neg(expo(Vec16<T>::one(drow + e), c256, ((double)d.xmp * cd) * 256.0),
+                                       s_exp) * isp);
   }
   // Inclusive prefix over the 256 entries in vocabulary order: a wave scan
   // plus the totals of the waves before (fixed order).
@@ -666,8 +615,153 @@ __global__ __launch_bounds__(kThreads) void k_locate(
   emit(b, K, n, tok, s_draw, out, nacc, kv_len, counters);
 }
 
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_locate(
+    const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ dtok,
+    const float* __restrict__ uni, const float* __restrict__ temp, int K, int V, int ncr,
+    int force_greedy, const ChunkSums* __restrict__ csum, const SubSums* __restrict__ csub,
+    const Decision* __restrict__ dec, int32_t* __restrict__ out, int32_t* __restrict__ nacc,
+    int32_t* __restrict__ kv_len, unsigned long long* counters) {
+  __shared__ double s_exp[kExpTable];
+  const int b = blockIdx.x;
+  const float t = temp_of(temp, b, force_greedy);
+  if (!(t > 0.f)) return;
+  const Decision d = dec[b];
+  fill_exp_table(s_exp);
+  locate_seq<T>(b, tgt, drf, dtok, uni, t, K, V, ncr, csum, csub, d, s_exp, out, nacc, kv_len, counters);
+}
+
+// ---------------------------------------------------------------------------
+// k_residual: grid (B, ncr); block 256.  Sampling sequences only.
+//
+// Lane mapping: the 8 lanes of group g = lane / 8 in wave w own sub-chunk
+// w * 8 + g (256 entries).  Each of their loads covers one 128-byte line of it,
+// so an instruction of the wave still reads 8 whole lines, and a sub-chunk's
+// sums need only 3 butterfly steps.
+// ---------------------------------------------------------------------------
+template <typename T, bool kAligned>
+__global__ __launch_bounds__(kThreads, 4) void k_residual(
+    const T* __restrict__ tgt, const T* __restrict__ drf, const float* __restrict__ temp, int K,
+    int V, int ncr, int force_greedy, const Decision* __restrict__ dec,
+    ChunkSums* __restrict__ csum, SubSums* __restrict__ csub) {
+  constexpr int VN = Vec16<T>::N;
+  constexpr int kLine = 8 * VN;                   // entries per 8-lane load (128 bytes)
+  constexpr int IT = kSub / kLine;                // loads per lane per row
+  static_assert(kThreads / 8 == kSubPerChunk, "one 8-lane group per sub-chunk");
+  __shared__ double s_exp[kExpTable];
+  __shared__ SubSums s_sub[kSubPerChunk];
+  const int b = blockIdx.x;
+  const int cr = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int sub_i = tid >> 3, s = tid & 7;
+  const float t = temp_of(temp, b, force_greedy);
+  if (!(t > 0.f)) return;
+  const Decision d = dec[b];
+  const int n = d.n;
+  const bool bonus = (n == K);
+  const double cd = kLog2eD / (double)t;
+  const T* trow = tgt + ((size_t)b * (K + 1) + n) * (size_t)V;
+  const T* drow = drf + ((size_t)b * K + (bonus ? 0 : n)) * (size_t)V;
+  const int e0 = cr * kResChunk + sub_i * kSub + s * VN;
+  // Loads first, so they are in flight while the table is filled.
+  u32x4_t rq[IT], rp[IT];
+#pragma unroll
+  for (int i = 0; i < IT; ++i)
+    rq[i] = kAligned ? load_raw<T>(trow, e0 + i * kLine, V) : load_raw_unaligned<T>(trow, e0 + i * kLine, V);
+  if (!bonus) {
+#pragma unroll
+    for (int i = 0; i < IT; ++i)
+      rp[i] = kAligned ? load_raw<T>(drow, e0 + i * kLine, V) : load_raw_unaligned<T>(drow, e0 + i * kLine, V);
+  }
+  fill_exp_table(s_exp);
+  __syncthreads();
+  // Exponents scaled by 256 (see exp2_reduce); all three scalings are exact.
+  const double c256 = cd * 256.0;
+  const double xmcq = ((double)d.xmq * cd) * 256.0, xmcp = ((double)d.xmp * cd) * 256.0;
+  // Entries past V hold -inf: weight exactly 0, and never classed q > p.
+  double sq = 0.0, sp = 0.0, sa = 0.0, sb = 0.0;
+  // Per vector: reduce every exponent and issue all table reads, then the
+  // polynomials (the reads' latency overlaps the reductions).
+  if (bonus) {
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      float xq[VN];
+      widen_raw<T>(rq[i], xq);
+      Exp2Arg eq[VN];
+      double tq[VN];
+#pragma unroll
+      for (int k = 0; k < VN; ++k) {
+        eq[k] = exp2_reduce(expo(xq[k], c256, xmcq));
+        tq[k] = s_exp[eq[k].k & (kExpTable - 1)];
+      }
+#pragma unroll
+      for (int k = 0; k < VN; ++k) sq += exp2_finish(eq[k], tq[k]);
+    }
+  } else {
+    const double theta = d.theta * 256.0;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      float xq[VN], xp[VN];
+      widen_raw<T>(rq[i], xq);
+      widen_raw<T>(rp[i], xp);
+      constexpr int HB = VN / 2;                  // entries per batch
+#pragma unroll
+      for (int h = 0; h < VN; h += HB) {
+      Exp2Arg eq[HB], ep[HB];
+      double tq[HB], tp[HB];
+      bool act[HB];
+#pragma unroll
+      for (int k = 0; k < HB; ++k) {
+        const double aq = expo(xq[h + k], c256, xmcq);
+        const double ap = expo(xp[h + k], c256, xmcp);
+        eq[k] = exp2_reduce(aq);
+        ep[k] = exp2_reduce(ap);
+        tq[k] = s_exp[eq[k].k & (kExpTable - 1)];
+        tp[k] = s_exp[ep[k].k & (kExpTable - 1)];
+        act[k] = aq - ap > theta;
+      }
+#pragma unroll
+      for (int k = 0; k < HB; ++k) {
+        const double wq = exp2_finish(eq[k], tq[k]);
+        const double wp = exp2_finish(ep[k], tp[k]);
+        sq += wq;
+        sp += wp;
+        // The sweep's normalisers only decide which entries count as q > p;
+        // an entry they misclassify has |q - p| ~ 1e-6 q, so the masses move
+        // by ~1e-12.  (-inf - -inf is NaN: not counted, weights are 0.)
+        const double f = act[k] ? 1.0 : 0.0;
+        sa = fma(wq, f, sa);
+        sb = fma(wp, f, sb);
+      }
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 4; off > 0; off >>= 1) {
+    sq += shfl_xor_d(sq, off);
+    sp += shfl_xor_d(sp, off);
+    sa += shfl_xor_d(sa, off);
+    sb += shfl_xor_d(sb, off);
+  }
+  if (s == 0) {
+    const SubSums ss{sa, sb, sq, sp};
+    csub[((size_t)b * ncr + cr) * kSubPerChunk + sub_i] = ss;
+    s_sub[sub_i] = ss;
+  }
+  __syncthreads();
+  // Chunk sums: one component per thread, sub-chunks in order.  Component
+  // tid of ChunkSums {eq, ep, a, b} is component (tid + 2) % 4 of SubSums
+  // {a, b, q, p}.
+  if (tid < 4) {
+    const int comp = (tid + 2) & 3;
+    double acc = 0.0;
+    for (int j = 0; j < kSubPerChunk; ++j) acc += reinterpret_cast<const double*>(&s_sub[j])[comp];
+    reinterpret_cast<double*>(csum + (size_t)b * ncr + cr)[tid] = acc;
+  }
+}
+
 struct RejectPlan {
-  size_t part_off, csum_off, csub_off, dec_off, total;
+  size_t part_off, csum_off, csub_off, dec_off, xd_off, total;
 };
 
 static inline RejectPlan reject_plan(int B, int K, int V) {
@@ -678,7 +772,8 @@ static inline RejectPlan reject_plan(int B, int K, int V) {
   p.csum_off = up((size_t)B * R * sweep_chunks(V) * sizeof(float2));
   p.csub_off = p.csum_off + up((size_t)B * res_chunks(V) * sizeof(ChunkSums));
   p.dec_off = p.csub_off + up((size_t)B * res_chunks(V) * kSubPerChunk * sizeof(SubSums));
-  p.total = p.dec_off + up((size_t)B * sizeof(Decision));
+  p.xd_off = p.dec_off + up((size_t)B * sizeof(Decision));
+  p.total = p.xd_off + up((size_t)B * K * 2 * sizeof(float));
   return p;
 }
 
@@ -695,12 +790,13 @@ static hipError_t launch_all(const void* tgt, const void* drf, const int32_t* dt
   ChunkSums* csum = reinterpret_cast<ChunkSums*>(ws + p.csum_off);
   SubSums* csub = reinterpret_cast<SubSums*>(ws + p.csub_off);
   Decision* dec = reinterpret_cast<Decision*>(ws + p.dec_off);
+  float* xd = reinterpret_cast<float*>(ws + p.xd_off);
   const T* t = static_cast<const T*>(tgt);
   const T* d = static_cast<const T*>(drf);
   hipLaunchKernelGGL((k_sweep<T, kAligned>), dim3(B * R, (nc + 3) / 4), dim3(kThreads), 0, st, t, d,
-                     temp, K, V, nc, force_greedy, part);
-  hipLaunchKernelGGL((k_decide<T>), dim3(B), dim3(kDecideThreads), 0, st, t, d, dtok, uni, temp, K, V,
-                     nc, force_greedy, part, dec, out, nacc, kv_len, counters);
+                     dtok, temp, K, V, nc, force_greedy, part, xd);
+  hipLaunchKernelGGL(k_decide, dim3(B), dim3(kDecideThreads), 0, st, dtok, uni, temp, K, V, nc,
+                     force_greedy, part, xd, dec, out, nacc, kv_len, counters);
   hipLaunchKernelGGL((k_residual<T, kAligned>), dim3(B, ncr), dim3(kThreads), 0, st, t, d, temp, K, V,
                      ncr, force_greedy, dec, csum, csub);
   hipLaunchKernelGGL((k_locate<T>), dim3(B), dim3(kThreads), 0, st, t, d, dtok, uni, temp, K, V, ncr,
