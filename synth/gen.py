@@ -12,7 +12,7 @@ Every generator takes a ``numpy.random.Generator``; callers derive those from
 import numpy as np
 
 __all__ = ["bf16_bits", "bf16_to_f32", "uniforms24", "make_reject_inputs",
-           "make_attn_inputs", "kv_layout_x", "BLOCK"]
+           "make_tree_reject_inputs", "make_attn_inputs", "kv_layout_x", "BLOCK"]
 
 BLOCK = 16  # tokens per KV page
 
@@ -119,6 +119,53 @@ def make_reject_inputs(seed, B, K, V, dtype="bf16", logit_std=2.0,
         toks = _draft_tokens(r_g, _decode(drf_e, dtype), temps)
     u = uniforms24(r_u, (B, K + 1))
     return {"target": tgt_e, "draft": drf_e, "draft_tokens": toks,
+            "uniforms": u, "temperature": temps}
+
+
+def make_tree_reject_inputs(seed, B, parent, V, dtype="bf16", logit_std=2.0,
+                            draft_sigma=0.51, temperature=1.0, shared_rows=False):
+    """Inputs of one tree-verify call over the tree given by ``parent`` (N nodes).
+
+    Rows as in make_reject_inputs, one target and one draft row per node
+    (target [B,N,V], draft [B,N,V]).  Node i's token is a fresh draw from
+    softmax(draft[parent[i]] / T) by the Gumbel-max trick, independently for
+    every child (T > 0); a greedy drafter (T <= 0) gives the children of a
+    node the top-ranked tokens of its draft row, in order.  Token 0 (the
+    root's) is 0 and unused.  uniforms [B,N] float32.
+    """
+    par = np.asarray(parent, dtype=np.int64)
+    n = par.shape[0]
+    ss = np.random.SeedSequence(seed)
+    r_t, r_n, r_g, r_u = [np.random.default_rng(s) for s in ss.spawn(4)]
+    temps = np.broadcast_to(np.asarray(temperature, dtype=np.float32), (B,)).copy()
+    rows_b = 1 if shared_rows else B
+    tgt = r_t.standard_normal((rows_b, n, V), dtype=np.float32) * np.float32(logit_std)
+    drf = tgt + r_n.standard_normal((rows_b, n, V), dtype=np.float32) * np.float32(draft_sigma)
+    tgt_e = _encode(tgt, dtype)
+    drf_e = _encode(drf, dtype)
+    del tgt, drf
+    if shared_rows:
+        tgt_e = np.broadcast_to(tgt_e, (B, n, V))
+        drf_e = np.broadcast_to(drf_e, (B, n, V))
+    toks = np.zeros((B, n), dtype=np.int32)
+    rank = np.zeros(n, dtype=np.int64)          # position of node i among its siblings
+    seen = {}
+    for i in range(1, n):
+        rank[i] = seen.get(int(par[i]), 0)
+        seen[int(par[i])] = rank[i] + 1
+    step = max(1, (1 << 22) // max(1, (n - 1) * V))
+    for s0 in range(0, B, step):
+        sel = np.arange(s0, min(B, s0 + step))
+        vals = _decode(drf_e[sel], dtype).astype(np.float64)          # [S, N, V]
+        pv = vals[:, par[1:], :]                                      # [S, N-1, V]
+        t = temps[sel].astype(np.float64)
+        g = -np.log(-np.log(r_g.random(pv.shape) * (1 - 2e-16) + 1e-16))
+        sampled = np.argmax(pv / np.where(t > 0, t, 1.0)[:, None, None] + g, axis=-1)
+        order = np.argsort(-pv, axis=-1, kind="stable")               # greedy: top-k
+        greedy_tok = np.take_along_axis(order, rank[1:][None, :, None], axis=-1)[..., 0]
+        toks[sel, 1:] = np.where((t > 0)[:, None], sampled, greedy_tok)
+    u = uniforms24(r_u, (B, n))
+    return {"target": tgt_e, "draft": drf_e, "tokens": toks, "parent": par.astype(np.int32),
             "uniforms": u, "temperature": temps}
 
 
