@@ -99,6 +99,32 @@ size_t spec_verify_attn_workspace_bytes(int B, int K, int Hq, int Hkv, int D,
                                         int max_kv_len);
 
 /*
+ * spec_verify_attn_tree -- the same attention over a flattened draft tree
+ * (thakicloud, "speedup went from 1.4x to 0.8x", "Grading every branch in one
+ * pass"; AI Engineering from Scratch, "Speculative decoding and EAGLE-3",
+ * tree attention with a mask that follows the tree).
+ *
+ * The window holds N = K + 1 tree nodes; node 0 is the root (the last
+ * accepted token) and node i's K/V sit at absolute position L0 + i.  Node i
+ * attends keys [0, L0) and the window keys L0 + j for every j whose bit is
+ * set in anc[b][i]: its ancestors and itself.  A chain (anc[b][i] =
+ * 2^(i+1) - 1) is exactly spec_verify_attn.
+ *
+ * anc: [B, N] uint32 device array (bits above N - 1 ignored).  Every other
+ *   argument, layout, size limit and error is as for spec_verify_attn with
+ *   K = N - 1; the workspace is spec_verify_attn_workspace_bytes(B, N - 1,
+ *   Hq, Hkv, D, max_kv_len).  anc == NULL with B > 0, or N < 2, is
+ *   SV_ERR_INVALID_ARG.
+ */
+int spec_verify_attn_tree(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, const int32_t* kv_len,
+                          const uint32_t* anc, void* out, int B, int N, int Hq,
+                          int Hkv, int D, int block_size, int num_blocks,
+                          int max_blocks_per_seq, int max_kv_len, float scale,
+                          int dtype, void* workspace, size_t workspace_bytes,
+                          void* hip_stream);
+
+/*
  * spec_reject_sample -- lossless verifier over the full vocabulary plus the
  * KV-length commit.
  *

@@ -15,7 +15,7 @@ if the library is missing, :func:`load` raises.
 import ctypes
 import os
 
-__all__ = ["load", "lib_path", "exported_symbols", "verify_attn", "reject_sample",
+__all__ = ["verify_attn_tree", "load", "lib_path", "exported_symbols", "verify_attn", "reject_sample",
            "verify_attn_workspace_bytes", "reject_sample_workspace_bytes",
            "SpecVerifyError", "SV_F32", "SV_BF16", "STATUS", "EXPORTS"]
 
@@ -25,7 +25,7 @@ _LIB = None
 SV_F32, SV_BF16 = 0, 1
 STATUS = {0: "SV_OK", -1: "SV_ERR_INVALID_ARG", -2: "SV_ERR_UNSUPPORTED",
           -3: "SV_ERR_WORKSPACE", -4: "SV_ERR_HIP"}
-EXPORTS = ("spec_verify_attn", "spec_verify_attn_workspace_bytes",
+EXPORTS = ("spec_verify_attn", "spec_verify_attn_workspace_bytes", "spec_verify_attn_tree",
            "spec_reject_sample", "spec_reject_sample_workspace_bytes",
            "spec_status_string", "spec_version")
 
@@ -54,6 +54,9 @@ def load():
     lib.spec_verify_attn.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                      i32, i32, f32, i32, vp, sz, vp]
     lib.spec_verify_attn.restype = i32
+    lib.spec_verify_attn_tree.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                          i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.spec_verify_attn_tree.restype = i32
     lib.spec_verify_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.spec_verify_attn_workspace_bytes.restype = sz
     lib.spec_reject_sample.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
@@ -127,6 +130,27 @@ def verify_attn(q, k_cache, v_cache, block_table, kv_len, out=None, max_kv_len=N
     int32 (committed lengths, read only).  ``max_kv_len`` bounds kv_len; it
     defaults to the block table's capacity.  Returns ``out``.
     """
+    return _verify_attn(q, k_cache, v_cache, block_table, kv_len, None, out, max_kv_len, scale,
+                        workspace, stream)
+
+
+def verify_attn_tree(q, k_cache, v_cache, block_table, kv_len, anc, out=None, max_kv_len=None,
+                     scale=0.0, workspace=None, stream=None):
+    """Attention over a flattened draft tree (see ``spec_verify_attn_tree``).
+
+    As ``verify_attn`` with N = q.shape[1] tree nodes, plus anc [B, N] int32
+    (the uint32 ancestor-or-self bit set of each node, bit j = node j).
+    """
+    import torch
+    _need(anc, "anc", torch.int32)
+    if tuple(anc.shape) != (q.shape[0], q.shape[1]):
+        raise ValueError("anc must be [B, N]")
+    return _verify_attn(q, k_cache, v_cache, block_table, kv_len, anc, out, max_kv_len, scale,
+                        workspace, stream)
+
+
+def _verify_attn(q, k_cache, v_cache, block_table, kv_len, anc, out, max_kv_len, scale,
+                 workspace, stream):
     import torch
     lib = load()
     _need(q, "q")
@@ -151,11 +175,18 @@ def verify_attn(q, k_cache, v_cache, block_table, kv_len, out=None, max_kv_len=N
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.spec_verify_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-                              _ptr(kv_len), _ptr(out), B, K1 - 1, Hq, Hkv, D, block_size, NB,
-                              mbps, int(max_kv_len), float(scale), dt, _ptr(workspace),
-                              ws_have, _stream(stream))
-    _check("spec_verify_attn", st)
+    if anc is None:
+        st = lib.spec_verify_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                  _ptr(kv_len), _ptr(out), B, K1 - 1, Hq, Hkv, D, block_size, NB,
+                                  mbps, int(max_kv_len), float(scale), dt, _ptr(workspace),
+                                  ws_have, _stream(stream))
+        _check("spec_verify_attn", st)
+    else:
+        st = lib.spec_verify_attn_tree(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                       _ptr(kv_len), _ptr(anc), _ptr(out), B, K1, Hq, Hkv, D,
+                                       block_size, NB, mbps, int(max_kv_len), float(scale), dt,
+                                       _ptr(workspace), ws_have, _stream(stream))
+        _check("spec_verify_attn_tree", st)
     return out
 
 

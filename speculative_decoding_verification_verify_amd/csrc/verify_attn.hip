@@ -131,9 +131,9 @@ __device__ __forceinline__ void mask_v_tail(bf16x8 (&vf)[2][D / 32], int pr, int
 // update of (m, l, O) and the bf16 probabilities for the P.V product.
 template <int D, int NT>
 __device__ __forceinline__ void score_pair(const bf16x8 (&kf)[D / 16], int pr, int hh, int nt,
-                                           const bf16x8 (&qf)[NT][D / 16], const int (&lim)[NT],
-                                           float sl2, f32x16 (&o)[NT][D / 32], float (&m_run)[NT],
-                                           float (&l_run)[NT], bf16x8 (&pf)[2]) {
+                                           const bf16x8 (&qf)[NT][D / 16], const uint32_t (&am)[NT],
+                                           int L0, float sl2, f32x16 (&o)[NT][D / 32],
+                                           float (&m_run)[NT], float (&l_run)[NT], bf16x8 (&pf)[2]) {
   constexpr int KK = D / 16, DT = D / 32;
   const int key0 = pr * kPairKeys + 8 * hh;     // key of reg r: key0 + (r>>3)*16 + (r&7)
   f32x16 s;
@@ -143,12 +143,24 @@ __device__ __forceinline__ void score_pair(const bf16x8 (&kf)[D / 16], int pr, i
   for (int kk = 0; kk < KK; ++kk)
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[nt][kk], s, 0, 0, 0);
   float mx = -INFINITY;
+  // Prefix keys (< L0) are visible; window key L0 + j is visible iff bit j of
+  // the row's ancestor set is set (a chain's row i has bits 0..i); later keys
+  // have no bit.  One 8-bit word per run of 8 consecutive keys.
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int key = key0 + (r >> 3) * 16 + (r & 7);
-    const float v = (key <= lim[nt]) ? s[r] * sl2 : -INFINITY;
-    s[r] = v;
-    mx = fmaxf(mx, v);
+  for (int grp = 0; grp < 2; ++grp) {
+    const int j0 = key0 + grp * 16 - L0;
+    uint32_t vb;
+    if (j0 >= 32) vb = 0u;
+    else if (j0 >= 0) vb = (am[nt] >> j0) & 0xFFu;
+    else if (j0 <= -8) vb = 0xFFu;
+    else vb = (((1u << -j0) - 1u) | (am[nt] << -j0)) & 0xFFu;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int r = grp * 8 + e;
+      const float v = ((vb >> e) & 1u) ? s[r] * sl2 : -INFINITY;
+      s[r] = v;
+      mx = fmaxf(mx, v);
+    }
   }
   mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
   // Lazy rescaling: keep the running reference unless the row max grows by
@@ -291,18 +303,21 @@ __device__ __forceinline__ bool next_segment(const Seg& s, Seg& n, int u1, int B
 }
 
 // Q operand (B of S^T = K Q^T) of a piece: lane holds Q[row = nt*32 + l32]
-// [kk*16 + hh*8 .. +8]; rows past G*(K+1) are zero.  lim = last visible key.
+// [kk*16 + hh*8 .. +8]; rows past G*(K+1) are zero.  am = the row's window
+// node's ancestor-or-self set: from anc[b][i] for a tree, bits 0..i for the
+// chain (anc == nullptr).
 template <int D, int NT>
-__device__ __forceinline__ void load_q(bf16x8 (&qf)[NT][D / 16], int (&lim)[NT],
-                                       const uint16_t* __restrict__ q, const Seg& s, int K1, int Hq,
-                                       int G, int rows, int l32, int hh) {
+__device__ __forceinline__ void load_q(bf16x8 (&qf)[NT][D / 16], uint32_t (&am)[NT],
+                                       const uint16_t* __restrict__ q,
+                                       const uint32_t* __restrict__ anc, const Seg& s, int K1,
+                                       int Hq, int G, int rows, int l32, int hh) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int row = nt * 32 + l32;
     const bool valid = row < rows;
     const int hq = valid ? row / K1 : 0;
     const int i = valid ? row - hq * K1 : K1 - 1;
-    lim[nt] = s.L0 + i;
+    am[nt] = (anc && valid) ? anc[(size_t)s.b * K1 + i] : ((2u << i) - 1u);
     const uint16_t* qp = q + (((size_t)s.b * K1 + i) * Hq + (size_t)s.g * G + hq) * D;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
@@ -326,7 +341,8 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[NT][D / 16], int (&lim)[NT],
 template <int D, int NT>
 __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T * 4 / stream_waves<NT>() : 1) void k_attn_stream(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
-    const int32_t* __restrict__ bt, const int32_t* __restrict__ kv_len, uint16_t* __restrict__ out,
+    const int32_t* __restrict__ bt, const int32_t* __restrict__ kv_len,
+    const uint32_t* __restrict__ anc, uint16_t* __restrict__ out,
     int B, int K1, int Hq, int Hkv, int num_blocks, int mbps, int np_cap, float sl2, int W,
     float* __restrict__ opart, float2* __restrict__ ml) {
   constexpr int KK = D / 16;         // MFMA k-steps for S
@@ -427,8 +443,8 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
     load_v<D>(vf, blk, vc, Hkv, cur.g, l32, hh);
   }
   bf16x8 qf[NT][KK];
-  int lim[NT];
-  load_q<D, NT>(qf, lim, q, cur, K1, Hq, G, rows, l32, hh);
+  uint32_t am[NT];
+  load_q<D, NT>(qf, am, q, anc, cur, K1, Hq, G, rows, l32, hh);
   __syncthreads();
 
   while (true) {
@@ -467,7 +483,7 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
       bf16x8 pf[NT][2];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        score_pair<D, NT>(kf, pr, hh, nt, qf, lim, sl2, o, m_run, l_run, pf[nt]);
+        score_pair<D, NT>(kf, pr, hh, nt, qf, am, cur.L0, sl2, o, m_run, l_run, pf[nt]);
       if (in_seg || cross) load_k<D>(kf, nblk, kc, Hkv, ng, k_page, k_tok, hh);
       mask_v_tail<D>(vf, pr, L, hh);
 #pragma unroll
@@ -554,7 +570,7 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
     if (!has_next) break;
     cur = nxt;
     // Q of the new segment (the loads of its first pair are already in flight).
-    load_q<D, NT>(qf, lim, q, cur, K1, Hq, G, rows, l32, hh);
+    load_q<D, NT>(qf, am, q, anc, cur, K1, Hq, G, rows, l32, hh);
     pr = cur.p_lo + wave;
   }
 }
@@ -634,14 +650,17 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_stream_combine(
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_attn_valu(
     const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
-    const int32_t* __restrict__ bt, const int32_t* __restrict__ kv_len, float* __restrict__ out,
+    const int32_t* __restrict__ bt, const int32_t* __restrict__ kv_len,
+    const uint32_t* __restrict__ anc, float* __restrict__ out,
     int K1, int Hq, int Hkv, int D, int num_blocks, int mbps, float sl2) {
   __shared__ float s_q[256];
   __shared__ float s_p[64];
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
   const int g = h / (Hq / Hkv);
-  const int t = kv_len[b] + i;                    // last visible key
+  const int L0 = kv_len[b];
+  const int t = L0 + i;                           // last key that can be visible
+  const uint32_t am = anc ? anc[(size_t)b * K1 + i] : ((2u << i) - 1u);
   const float* qp = q + (((size_t)b * K1 + i) * Hq + h) * D;
   for (int d = lane; d < D; d += 64) s_q[d] = qp[d];
   __syncthreads();
@@ -652,7 +671,8 @@ __global__ __launch_bounds__(64) void k_attn_valu(
   for (int j0 = 0; j0 <= t; j0 += 64) {
     const int j = j0 + lane;
     float sc = -INFINITY;
-    if (j <= t) {
+    const unsigned jw = (unsigned)(j - L0);
+    if (j <= t && (jw >= 32u || ((am >> jw) & 1u))) {
       const int blk = clampi(btb[min(j >> 4, mbps - 1)], 0, num_blocks - 1);
       const float* kp = kc + ((size_t)blk * Hkv + g) * page;
       const int tok = j & 15;
@@ -734,7 +754,8 @@ static int stream_blocks_per_cu() {
 
 template <int D, int NT>
 static hipError_t launch_stream(const void* q, const void* kc, const void* vc, const int32_t* bt,
-                                const int32_t* kv_len, void* out, int B, int K1, int Hq, int Hkv,
+                                const int32_t* kv_len, const uint32_t* anc, void* out, int B, int K1,
+                                int Hq, int Hkv,
                                 int num_blocks, int mbps, float sl2, const AttnPlan& p, char* ws,
                                 hipStream_t st) {
   // Persistent grid: every workgroup resident from the start.
@@ -744,8 +765,8 @@ static hipError_t launch_stream(const void* q, const void* kc, const void* vc, c
   float2* ml = reinterpret_cast<float2*>(ws + p.opart_bytes);
   hipLaunchKernelGGL((k_attn_stream<D, NT>), dim3(W), dim3(64 * stream_waves<NT>()), 0, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
-                     static_cast<const uint16_t*>(vc), bt, kv_len, static_cast<uint16_t*>(out), B, K1,
-                     Hq, Hkv, num_blocks, mbps, p.np_cap, sl2, W, opart, ml);
+                     static_cast<const uint16_t*>(vc), bt, kv_len, anc, static_cast<uint16_t*>(out), B,
+                     K1, Hq, Hkv, num_blocks, mbps, p.np_cap, sl2, W, opart, ml);
   if (W > 1)
     hipLaunchKernelGGL((k_attn_stream_combine<D, NT>), dim3(Hkv, B), dim3(kCombineThreads), 0, st, opart,
                        ml, kv_len, static_cast<uint16_t*>(out), B, K1, Hq, Hkv, p.np_cap, W);
@@ -761,11 +782,13 @@ extern "C" size_t spec_verify_attn_workspace_bytes(int B, int K, int Hq, int Hkv
   return p.opart_bytes + p.ml_bytes;
 }
 
-extern "C" int spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
-                                const int32_t* block_table, const int32_t* kv_len, void* out, int B,
-                                int K, int Hq, int Hkv, int D, int block_size, int num_blocks,
-                                int max_blocks_per_seq, int max_kv_len, float scale, int dtype,
-                                void* workspace, size_t workspace_bytes, void* hip_stream) {
+namespace sv {
+
+static int verify_attn_impl(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_table, const int32_t* kv_len, const uint32_t* anc,
+                            void* out, int B, int K, int Hq, int Hkv, int D, int block_size,
+                            int num_blocks, int max_blocks_per_seq, int max_kv_len, float scale,
+                            int dtype, void* workspace, size_t workspace_bytes, void* hip_stream) {
   if (B < 0 || K < 1 || Hq < 1 || Hkv < 1 || D < 1 || max_kv_len < 0 || num_blocks < 1 ||
       max_blocks_per_seq < 1)
     return SV_ERR_INVALID_ARG;
@@ -779,18 +802,18 @@ extern "C" int spec_verify_attn(const void* q, const void* k_cache, const void* 
   if (!q || !k_cache || !v_cache || !block_table || !kv_len || !out) return SV_ERR_INVALID_ARG;
   if (B > 65535 || Hkv > 65535) return SV_ERR_UNSUPPORTED;
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)D);
-  const float sl2 = sc * sv::kLog2e;
+  const float sl2 = sc * kLog2e;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const int K1 = K + 1;
   hipError_t e;
   if (dtype == SV_F32) {
-    hipLaunchKernelGGL(sv::k_attn_valu, dim3(K1, Hq, B), dim3(64), 0, st,
+    hipLaunchKernelGGL(k_attn_valu, dim3(K1, Hq, B), dim3(64), 0, st,
                        static_cast<const float*>(q), static_cast<const float*>(k_cache),
-                       static_cast<const float*>(v_cache), block_table, kv_len,
+                       static_cast<const float*>(v_cache), block_table, kv_len, anc,
                        static_cast<float*>(out), K1, Hq, Hkv, D, num_blocks, max_blocks_per_seq, sl2);
     e = hipGetLastError();
   } else {
-    const sv::AttnPlan p = sv::attn_plan(B, K, Hq, Hkv, D, max_kv_len);
+    const AttnPlan p = attn_plan(B, K, Hq, Hkv, D, max_kv_len);
     if (p.too_big) return SV_ERR_UNSUPPORTED;
     if (p.w_max > 1) {
       if (!workspace) return SV_ERR_INVALID_ARG;
@@ -802,16 +825,41 @@ extern "C" int spec_verify_attn(const void* q, const void* k_cache, const void* 
     if (al & 15) return SV_ERR_INVALID_ARG;
     char* ws = static_cast<char*>(workspace);
     if (D == 128) {
-      e = p.tiles == 1 ? sv::launch_stream<128, 1>(q, k_cache, v_cache, block_table, kv_len, out, B, K1,
-                                                   Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, st)
-                       : sv::launch_stream<128, 2>(q, k_cache, v_cache, block_table, kv_len, out, B, K1,
-                                                   Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, st);
+      e = p.tiles == 1 ? launch_stream<128, 1>(q, k_cache, v_cache, block_table, kv_len, anc, out, B,
+                                               K1, Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, st)
+                       : launch_stream<128, 2>(q, k_cache, v_cache, block_table, kv_len, anc, out, B,
+                                               K1, Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, st);
     } else {
-      e = p.tiles == 1 ? sv::launch_stream<64, 1>(q, k_cache, v_cache, block_table, kv_len, out, B, K1,
-                                                  Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, st)
-                       : sv::launch_stream<64, 2>(q, k_cache, v_cache, block_table, kv_len, out, B, K1,
-                                                  Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, st);
+      e = p.tiles == 1 ? launch_stream<64, 1>(q, k_cache, v_cache, block_table, kv_len, anc, out, B,
+                                              K1, Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, st)
+                       : launch_stream<64, 2>(q, k_cache, v_cache, block_table, kv_len, anc, out, B,
+                                              K1, Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, st);
     }
   }
   return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+}  // namespace sv
+
+extern "C" int spec_verify_attn(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, const int32_t* kv_len, void* out, int B,
+                                int K, int Hq, int Hkv, int D, int block_size, int num_blocks,
+                                int max_blocks_per_seq, int max_kv_len, float scale, int dtype,
+                                void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return sv::verify_attn_impl(q, k_cache, v_cache, block_table, kv_len, nullptr, out, B, K, Hq, Hkv,
+                              D, block_size, num_blocks, max_blocks_per_seq, max_kv_len, scale, dtype,
+                              workspace, workspace_bytes, hip_stream);
+}
+
+extern "C" int spec_verify_attn_tree(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_table, const int32_t* kv_len,
+                                     const uint32_t* anc, void* out, int B, int N, int Hq, int Hkv,
+                                     int D, int block_size, int num_blocks, int max_blocks_per_seq,
+                                     int max_kv_len, float scale, int dtype, void* workspace,
+                                     size_t workspace_bytes, void* hip_stream) {
+  if (B > 0 && !anc) return SV_ERR_INVALID_ARG;
+  if (N < 2) return SV_ERR_INVALID_ARG;
+  return sv::verify_attn_impl(q, k_cache, v_cache, block_table, kv_len, anc, out, B, N - 1, Hq, Hkv,
+                              D, block_size, num_blocks, max_blocks_per_seq, max_kv_len, scale, dtype,
+                              workspace, workspace_bytes, hip_stream);
 }

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 6
+    assert len(names) == len(sv.EXPORTS) >= 7
     assert set(names) == set(sv.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
@@ -102,3 +102,15 @@ def test_python_wrapper_rejects_cpu_tensors(lib):
     q = torch.zeros((1, 2, 1, 64))
     with pytest.raises(ValueError):
         sv.verify_attn(q, q, q, q.int(), q.int())
+
+
+def test_tree_attn_validation(lib):
+    p = FAKE
+    f = lib.spec_verify_attn_tree
+    # anc missing, N < 2, then the shared checks (D unsupported).
+    assert f(p, p, p, p, p, None, p, 2, 8, 32, 8, 128, 16, 10, 600, 8192, 0.0, 1, p, 1 << 30, None) == -1
+    assert f(p, p, p, p, p, p, p, 2, 1, 32, 8, 128, 16, 10, 600, 8192, 0.0, 1, p, 1 << 30, None) == -1
+    assert f(p, p, p, p, p, p, p, 2, 8, 32, 8, 96, 16, 10, 600, 8192, 0.0, 1, p, 1 << 30, None) == -2
+    assert f(p, p, p, p, p, p, p, 2, 18, 32, 8, 128, 16, 10, 600, 8192, 0.0, 1, p, 1 << 30, None) == -2
+    assert f(None, None, None, None, None, None, None, 0, 8, 32, 8, 128, 16, 10, 600, 8192, 0.0, 1,
+             None, 0, None) == 0                               # empty batch: no-op
