@@ -174,6 +174,66 @@ int spec_reject_sample(const void* target_logits, const void* draft_logits,
 
 size_t spec_reject_sample_workspace_bytes(int B, int K, int V);
 
+/*
+ * spec_reject_sample_tree -- the lossless verifier over a flattened draft
+ * tree, plus the KV commit (AI Engineering from Scratch, "Speculative
+ * decoding and EAGLE-3": EAGLE-2's draft tree, the accept test and residual
+ * of "Concept"; thakicloud, "Grading every branch in one pass": every branch
+ * is graded in one forward pass and the surviving path is kept).
+ *
+ * The tree: N nodes, node 0 the root (the last accepted token), parent[i] < i
+ * for i >= 1; its shape is shared by the whole batch.  Target row v is q_v,
+ * the verifier's distribution after the path to node v; draft row v is p_v,
+ * the law node v's children were drawn from (each independently).  Walking
+ * from the root with q' = q_v:
+ *   - the children c of v are tested in increasing index order: accept c iff
+ *     p_v(d_c) <= 0 or u[c] < min(1, q'(d_c) / p_v(d_c));
+ *   - after a rejected child, q' <- (q' - p_v)_+ normalised (recursive
+ *     rejection sampling; a zero-mass residual leaves q' unchanged);
+ *   - the first accepted child is emitted and becomes v (q' <- q_v);
+ *   - when every child of v is rejected, or v is a leaf, the final token is
+ *     drawn from q' by inverse CDF with u[0], as in spec_reject_sample.
+ * The emitted token at every node then has exactly the law q_v.  A chain
+ * (parent[i] = i - 1) gives exactly spec_reject_sample with u[i] <-> u_{i-1}
+ * and u[0] <-> u_K.  Greedy (temperature[b] <= 0, or draft_logits == NULL):
+ * the first child whose token equals argmax(q_v) (lowest index on ties) is
+ * accepted, else argmax(q_v) is emitted and the walk ends.
+ *
+ * Outputs: out_tokens[b] = tokens of the accepted nodes along the path, the
+ * final token, then -1; out_nodes[b] = the accepted node indices, then -1;
+ * num_accepted[b] = n; kv_len[b] += n + 1.  The caller moves the K/V of the
+ * accepted nodes (slots L0 + out_nodes[b][j]) to positions L0 + 1 + j.  Not
+ * idempotent (kv_len).  counters (optional): counters[0] += N - 1 and
+ * counters[1] += n per sequence.
+ *
+ * Layouts (row-major, contiguous):
+ *   parent        [N] int32 HOST array (parent[0] = -1)
+ *   target_logits [B, N, V]; draft_logits [B, N, V] (rows of leaves unread)
+ *   tokens        [B, N] int32 (entry 0 unused), in [0, V)
+ *   uniforms      [B, N] float32 in [0, 1): u[i] tests node i, u[0] the final draw
+ *   temperature   [B] float32
+ *   out_tokens, out_nodes [B, N] int32; num_accepted [B] int32; kv_len [B] int32
+ * Preconditions as for spec_reject_sample.  Sizes: 1 <= N <= SV_MAX_K + 1;
+ *   1 <= V < 2^31 / 4; B >= 0 (B == 0 is a no-op); B * (2N - 1) < 2^31.
+ *   A parent array that is not a tree in topological order is
+ *   SV_ERR_INVALID_ARG.
+ * Work: one exact float64 pass over a node's row pair per rejection (and one
+ *   for a leaf's bonus draw), in rounds; the number of rounds follows from
+ *   the shape (the largest number of passes any walk can need).
+ * workspace: at least spec_reject_sample_tree_workspace_bytes(B, N, V) bytes
+ *   of device memory (any content; 256-byte aligned).
+ */
+int spec_reject_sample_tree(const void* target_logits, const void* draft_logits,
+                            const int32_t* parent, const int32_t* tokens,
+                            const float* uniforms, const float* temperature,
+                            int32_t* out_tokens, int32_t* out_nodes,
+                            int32_t* num_accepted, int32_t* kv_len,
+                            unsigned long long* counters, int B, int N, int V,
+                            int dtype, void* workspace, size_t workspace_bytes,
+                            void* hip_stream);
+
+size_t spec_reject_sample_tree_workspace_bytes(int B, int N, int V);
+
 /* Static description of a status code. */
 const char* spec_status_string(int status);
 

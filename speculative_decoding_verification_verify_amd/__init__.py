@@ -10,13 +10,16 @@ if the library is missing, :func:`load` raises.
         window-causal GQA of the K+1 verify positions over a paged KV cache
     reject_sample(target, draft, draft_tokens, uniforms, temperature, kv_len, ...)
         lossless verifier over the full vocabulary + KV-length commit
+    verify_attn_tree(..., anc) / reject_sample_tree(..., parent, ...)
+        the same two steps over a flattened draft tree
 """
 
 import ctypes
 import os
 
-__all__ = ["verify_attn_tree", "load", "lib_path", "exported_symbols", "verify_attn", "reject_sample",
-           "verify_attn_workspace_bytes", "reject_sample_workspace_bytes",
+__all__ = ["load", "lib_path", "exported_symbols", "verify_attn", "verify_attn_tree",
+           "reject_sample", "reject_sample_tree", "verify_attn_workspace_bytes",
+           "reject_sample_workspace_bytes", "reject_sample_tree_workspace_bytes",
            "SpecVerifyError", "SV_F32", "SV_BF16", "STATUS", "EXPORTS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -27,6 +30,7 @@ STATUS = {0: "SV_OK", -1: "SV_ERR_INVALID_ARG", -2: "SV_ERR_UNSUPPORTED",
           -3: "SV_ERR_WORKSPACE", -4: "SV_ERR_HIP"}
 EXPORTS = ("spec_verify_attn", "spec_verify_attn_workspace_bytes", "spec_verify_attn_tree",
            "spec_reject_sample", "spec_reject_sample_workspace_bytes",
+           "spec_reject_sample_tree", "spec_reject_sample_tree_workspace_bytes",
            "spec_status_string", "spec_version")
 
 
@@ -64,6 +68,11 @@ def load():
     lib.spec_reject_sample.restype = i32
     lib.spec_reject_sample_workspace_bytes.argtypes = [i32, i32, i32]
     lib.spec_reject_sample_workspace_bytes.restype = sz
+    lib.spec_reject_sample_tree.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
+                                            i32, i32, vp, sz, vp]
+    lib.spec_reject_sample_tree.restype = i32
+    lib.spec_reject_sample_tree_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.spec_reject_sample_tree_workspace_bytes.restype = sz
     lib.spec_status_string.argtypes = [i32]
     lib.spec_status_string.restype = ctypes.c_char_p
     lib.spec_version.argtypes = []
@@ -119,6 +128,10 @@ def verify_attn_workspace_bytes(B, K, Hq, Hkv, D, max_kv_len):
 
 def reject_sample_workspace_bytes(B, K, V):
     return int(load().spec_reject_sample_workspace_bytes(B, K, V))
+
+
+def reject_sample_tree_workspace_bytes(B, N, V):
+    return int(load().spec_reject_sample_tree_workspace_bytes(B, N, V))
 
 
 def verify_attn(q, k_cache, v_cache, block_table, kv_len, out=None, max_kv_len=None,
@@ -228,3 +241,53 @@ def reject_sample(target, draft, draft_tokens, uniforms, temperature, kv_len,
                                 ws_have, _stream(stream))
     _check("spec_reject_sample", st)
     return out_tokens, num_accepted
+
+
+def reject_sample_tree(target, draft, parent, tokens, uniforms, temperature, kv_len,
+                       out_tokens=None, out_nodes=None, num_accepted=None, counters=None,
+                       workspace=None, stream=None):
+    """Lossless verifier over a draft tree + KV commit (see ``spec_reject_sample_tree``).
+
+    target [B, N, V], draft [B, N, V] or None (greedy for every sequence);
+    parent: N host integers (parent[0] = -1, parent[i] < i), shared by the
+    batch; tokens [B, N] int32; uniforms [B, N] float32 (u[i] tests node i,
+    u[0] the final draw); temperature [B] float32; kv_len [B] int32, updated
+    in place to kv_len + n + 1.
+    Returns (out_tokens [B, N], out_nodes [B, N], num_accepted [B]), int32.
+    """
+    import torch
+    lib = load()
+    _need(target, "target")
+    dt = _dtype_code(target)
+    if draft is not None:
+        _need(draft, "draft", target.dtype)
+        if tuple(draft.shape) != tuple(target.shape):
+            raise ValueError("draft must have the shape of target [B, N, V]")
+    _need(tokens, "tokens", torch.int32)
+    _need(uniforms, "uniforms", torch.float32)
+    _need(temperature, "temperature", torch.float32)
+    _need(kv_len, "kv_len", torch.int32)
+    B, N, V = target.shape
+    par = [int(x) for x in parent]
+    if len(par) != N:
+        raise ValueError("parent must have N = %d entries" % N)
+    c_par = (ctypes.c_int32 * N)(*par)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, N), dtype=torch.int32, device=target.device)
+    if out_nodes is None:
+        out_nodes = torch.empty((B, N), dtype=torch.int32, device=target.device)
+    if num_accepted is None:
+        num_accepted = torch.empty((B,), dtype=torch.int32, device=target.device)
+    if counters is not None:
+        _need(counters, "counters", torch.int64)
+    ws_bytes = reject_sample_tree_workspace_bytes(B, N, V)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=target.device)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.spec_reject_sample_tree(_ptr(target), _ptr(draft), ctypes.cast(c_par, ctypes.c_void_p),
+                                     _ptr(tokens), _ptr(uniforms), _ptr(temperature),
+                                     _ptr(out_tokens), _ptr(out_nodes), _ptr(num_accepted),
+                                     _ptr(kv_len), _ptr(counters), B, N, V, dt, _ptr(workspace),
+                                     ws_have, _stream(stream))
+    _check("spec_reject_sample_tree", st)
+    return out_tokens, out_nodes, num_accepted

@@ -1,13 +1,17 @@
 // Lossless rejection-sampling verifier over the full vocabulary, plus the
-// commit of the logical KV length.
+// commit of the logical KV length, for a draft chain and for a draft tree.
 //
 // Method: AI Engineering from Scratch, "Speculative decoding and EAGLE-3" --
 // "Concept" (accept d ~ p with probability min(1, q(d)/p(d)); on rejection
 // draw from (q - p)_+ normalised; bonus token from q_{N+1} when every draft
 // passes), "Build it" steps 1-2 (p(d) <= 0 accepts; a zero-mass residual falls
-// back to q) and "Rolling back the KV cache" (logical length reset).
+// back to q) and "Rolling back the KV cache" (logical length reset).  Trees:
+// the same page's EAGLE-2 draft tree and thakicloud, "Grading every branch in
+// one pass": every branch is graded in the one pass and the surviving path is
+// kept; the siblings of a node are tried one after another by recursive
+// rejection sampling, which keeps the output law exact.
 //
-// Four kernels on the caller's stream:
+// Four kernels on the caller's stream (chain):
 //   k_sweep     one pass over every logit row (the HBM-bound part): per 4096-
 //               entry chunk, the raw maximum and sum_v 2^(x_v c - m) in fp32
 //               (c = log2(e) / T), or the chunk argmax for greedy sequences.
@@ -24,7 +28,7 @@
 //               one row pair the final draw needs (target and draft row n, or
 //               target row K for the bonus) in float64, per 256-entry
 //               sub-chunk and per chunk: sum e_q, sum e_p and the same two
-//               sums over the entries with q > p, with e = 2^((x - xmax) c)
+//               sums over the entries with q > c p, with e = 2^((x - xmax) c)
 //               to a few ulp.  They give the exact normalisers and residual
 //               masses, so the row pair is read only once more.
 //   k_locate    per sampling sequence: float64 prefix scans over the chunk
@@ -36,6 +40,16 @@
 // draw inside one kernel would need device-scope fences per block, which
 // write back and invalidate each XCD's L2; measured, a kernel boundary is
 // far cheaper.)
+//
+// Tree: the same sweep over the target rows of all nodes and the draft rows
+// of the nodes with children; k_tree_decide walks down from the root while
+// the first child of each node passes its test (greedy sequences finish
+// there).  After a rejection the next sibling is tested against the residual
+// q' = (q - coef p)_+ / Z, where coef starts at 1 and grows by Z with every
+// further rejection; Z needs one exact pass over the node's row pair.  So the
+// tree runs in rounds of k_residual + k_tree_step, each round one such pass
+// per sequence that still needs one; the host knows from the tree's shape how
+// many rounds the longest walk can take.
 // No floating-point atomics and fixed reduction orders: results are bitwise
 // reproducible run to run.
 
@@ -43,6 +57,8 @@
 // weights of k_locate must equal those of k_residual bit for bit.  Fused
 // multiply-adds that are wanted are written out.
 #pragma clang fp contract(off)
+
+#include <algorithm>
 
 #include "common.h"
 
@@ -60,12 +76,76 @@ constexpr int kPartStage = 4096;      // row statistics staged in LDS per sequen
 constexpr double kLog2eD = 1.4426950408889634074;
 
 
-// What k_decide leaves for the final draw of a sampling sequence.
+// One exact pass over a row pair (and the draw that may follow it), as the
+// decide and step kernels leave it for k_residual.
+enum : int {
+  kModeNone = 0,    // nothing to do: greedy or finished
+  kModeQ = 1,       // target row only: the draw is from q (bonus token)
+  kModeResid = 2,   // target and draft row: weights (q - coef p)_+
+};
 struct Decision {
-  int n;             // accepted drafts
-  float xmq, xmp;    // raw maxima of target row n and draft row n (xmp unused when n == K)
-  float pad;
-  double theta;      // log2(sq / sp) of the sweep's normalisers: q > p iff aq - ap > theta
+  int mode;
+  int n;             // chain: accepted drafts
+  int trow, drow;    // row indices into the target / draft arrays (drow unused in kModeQ)
+  float xmq, xmp;    // raw maxima of those rows: the exp frames of the pass
+  double theta;      // log2(coef sq / sp): q > coef p iff aq - ap > theta
+  double coef;       // residual coefficient (1 after the first rejection at a node)
+  double coef_prev;  // the one before it: a zero-mass residual leaves the law at
+                     // (q - coef_prev p)_+, which is then q (coef_prev = 0) or p
+};
+
+// Shape of a draft tree (nodes in topological order, parent[i] < i), shared
+// by the batch; passed by value as a kernel argument.
+constexpr int kMaxTree = SV_MAX_K + 1;
+struct TreeShape {
+  int n;                           // nodes
+  int n_int;                       // nodes with children
+  int8_t kid_off[kMaxTree + 1];    // children of v: kids[kid_off[v] .. kid_off[v + 1])
+  int8_t kids[kMaxTree];           // in increasing index order
+  int8_t int_node[kMaxTree];       // node whose draft row is swept row n + i
+  int8_t int_idx[kMaxTree];        // i for a node with children, -1 for a leaf
+};
+
+// Where a tree walk stands between rounds.
+struct TreeState {
+  int v;          // current node
+  int pos;        // position among v's children of the next one to test
+  int n;          // accepted nodes so far
+  int fin;        // the scheduled pass feeds the final draw
+  double n_prev;  // residual mass at coef_prev (1: q itself)
+};
+
+// The rows one sequence sweeps, and the tokens recorded in each.  Chain:
+// target rows 0..K, then draft rows 0..K-1; target and draft row j record
+// drafted token j (index b K + j).
+struct ChainRows {
+  int K;
+  __device__ __forceinline__ int count() const { return 2 * K + 1; }
+  __device__ __forceinline__ bool is_draft(int j) const { return j > K; }
+  __device__ __forceinline__ size_t row(int b, int j) const {
+    return j <= K ? (size_t)b * (K + 1) + j : (size_t)b * K + (j - K - 1);
+  }
+  template <class F>
+  __device__ __forceinline__ void for_each_token(int b, int j, F&& f) const {
+    const int jj = j <= K ? j : j - K - 1;
+    if (jj < K) f((size_t)b * K + jj);
+  }
+};
+
+// Tree: target rows of all nodes, then draft rows of the nodes with
+// children; the rows of node v record the tokens of v's children (index
+// b n + child).
+struct TreeRows {
+  TreeShape s;
+  __device__ __forceinline__ int count() const { return s.n + s.n_int; }
+  __device__ __forceinline__ bool is_draft(int j) const { return j >= s.n; }
+  __device__ __forceinline__ int node(int j) const { return j < s.n ? j : s.int_node[j - s.n]; }
+  __device__ __forceinline__ size_t row(int b, int j) const { return (size_t)b * s.n + node(j); }
+  template <class F>
+  __device__ __forceinline__ void for_each_token(int b, int j, F&& f) const {
+    const int v = node(j);
+    for (int k = s.kid_off[v]; k < s.kid_off[v + 1]; ++k) f((size_t)b * s.n + s.kids[k]);
+  }
 };
 
 // Per-chunk float64 sums (e = unnormalised weight in the 2^((x - xmax) c) frame).
@@ -149,28 +229,28 @@ __device__ __forceinline__ u32x4_t load_raw_unaligned(const T* __restrict__ row,
 }
 
 // ---------------------------------------------------------------------------
-// k_sweep: grid (B * (2K+1), ceil(nc / 4)); block 256 = 4 waves, one chunk each.
-// part[row * nc + chunk] = (raw max, sum 2^(x c - fl(max c))) or, greedy,
-// (max value, argmax index bits).
+// k_sweep: grid (B * rows.count(), ceil(nc / 4)); block 256 = 4 waves, one
+// chunk each.  part[row * nc + chunk] = (raw max, sum 2^(x c - fl(max c)))
+// or, greedy, (max value, argmax index bits).
 // ---------------------------------------------------------------------------
-template <typename T, bool kAligned>
+template <typename T, bool kAligned, class Rows>
 __global__ __launch_bounds__(kThreads) void k_sweep(
     const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ dtok,
-    const float* __restrict__ temp, int K, int V, int nc, int force_greedy,
+    const float* __restrict__ temp, Rows rows, int V, int nc, int force_greedy,
     float2* __restrict__ part, float* __restrict__ xd) {
-  const int R = 2 * K + 1;
+  const int R = rows.count();
   const int row = blockIdx.x;
   const int b = row / R;
   const int j = row - b * R;
   const float t = temp_of(temp, b, force_greedy);
   const bool greedy = !(t > 0.f);
-  if (greedy && j > K) return;                 // greedy never reads draft rows
+  const bool is_draft = rows.is_draft(j);
+  if (greedy && is_draft) return;              // greedy never reads draft rows
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int chunk = blockIdx.y * 4 + wave;
   if (chunk >= nc) return;
-  const T* src = (j <= K) ? tgt + ((size_t)b * (K + 1) + j) * (size_t)V
-                          : drf + ((size_t)b * K + (j - K - 1)) * (size_t)V;
+  const T* src = (is_draft ? drf : tgt) + rows.row(b, j) * (size_t)V;
   constexpr int VN = Vec16<T>::N;
   constexpr int IT = kSweepChunk / (64 * VN);
   const int base = chunk * kSweepChunk + lane * VN;
@@ -186,11 +266,10 @@ __global__ __launch_bounds__(kThreads) void k_sweep(
     for (int it = 0; it < IT; ++it) load_vec<T, kAligned, true>(src, base + it * 64 * VN, V, x[it]);
   }
   if (!greedy) {
-    // The logit of the drafted token d_jj in this row (target row jj < K or
-    // draft row jj), for the accept test: written by the lane that holds it.
-    const int jj = (j <= K) ? j : j - K - 1;
-    if (jj < K) {
-      const int dd = clampi(dtok[(size_t)b * K + jj], 0, V - 1);
+    // The logits of the tokens this row tests, for the accept tests: each
+    // written by the lane that holds it (xd[2 token + is_draft]).
+    rows.for_each_token(b, j, [&](size_t ti) {
+      const int dd = clampi(dtok[ti], 0, V - 1);
       const int off = dd - chunk * kSweepChunk;
       if (off >= 0 && off < kSweepChunk && lane == (off / VN) % 64) {
         const int it_d = off / (64 * VN), k_d = off % VN;
@@ -200,9 +279,9 @@ __global__ __launch_bounds__(kThreads) void k_sweep(
 #pragma unroll
           for (int k = 0; k < VN; ++k)
             if (it == it_d && k == k_d) v = x[it][k];
-        xd[((size_t)b * K + jj) * 2 + (j > K ? 1 : 0)] = v;
+        xd[ti * 2 + (is_draft ? 1 : 0)] = v;
       }
-    }
+    });
   }
   float2 res;
   if (greedy) {
@@ -373,17 +452,14 @@ __global__ __launch_bounds__(kDecideThreads) void k_decide(
   __syncthreads();
   const int n = s_n;
   if (greedy) {
+    if (tid == 0) dec[b] = Decision{kModeNone, n, 0, 0, 0.f, 0.f, 0.0, 0.0, 0.0};
     emit(b, K, n, __float_as_int(s_b[n]), s_draw, out, nacc, kv_len, counters);
     return;
   }
   if (tid != 0) return;
   const double cd = kLog2eD / (double)t;
-  Decision dd;
-  dd.n = n;
-  dd.xmq = s_a[n];
-  dd.xmp = (n < K) ? s_a[K + 1 + n] : 0.f;
-  dd.pad = 0.f;
-  dd.theta = 0.0;
+  Decision dd{n < K ? kModeResid : kModeQ, n, b * (K + 1) + n, n < K ? b * K + n : 0,
+              s_a[n], n < K ? s_a[K + 1 + n] : 0.f, 0.0, 1.0, 0.0};
   if (n < K) {
     // The sweep's normalisers, moved from the fl(xmax c) frame to the
     // 2^((x - xmax) c) frame of the exact pass.
@@ -457,16 +533,18 @@ __device__ __forceinline__ double expo(float x, double c256, double xmc256) {
 __device__ __forceinline__ double shfl_xor_d(double x, int off) { return __shfl_xor(x, off, 64); }
 
 // ---------------------------------------------------------------------------
-// k_locate: grid (B); block 256.  Sampling sequences only.  Narrows the draw
-// chunk -> sub-chunk (from the stored sums) -> entry (exact weights of one
-// 256-entry run, one per thread), each level by an inclusive float64 scan in
-// vocabulary order.
+// The final draw: narrows chunk -> sub-chunk (from the stored sums) -> entry
+// (exact weights of one 256-entry run, one per thread), each level by an
+// inclusive float64 scan in vocabulary order.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ double chunk_mass(const ChunkSums& cs, bool qonly, double isq, double isp) {
-  return qonly ? cs.eq * isq : fmax(0.0, cs.a * isq - cs.b * isp);
+// What the draw's weights are: q, p, or (q - coef p)_+ (then isp = coef / sp).
+enum : int { kDrawQ = 0, kDrawP = 1, kDrawResid = 2 };
+
+__device__ __forceinline__ double chunk_mass(const ChunkSums& cs, int m, double isq, double isp) {
+  return m == kDrawQ ? cs.eq * isq : (m == kDrawP ? cs.ep * isp : fmax(0.0, cs.a * isq - cs.b * isp));
 }
-__device__ __forceinline__ double sub_mass(const SubSums& ss, bool qonly, double isq, double isp) {
-  return qonly ? ss.q * isq : fmax(0.0, ss.a * isq - ss.b * isp);
+__device__ __forceinline__ double sub_mass(const SubSums& ss, int m, double isq, double isp) {
+  return m == kDrawQ ? ss.q * isq : (m == kDrawP ? ss.p * isp : fmax(0.0, ss.a * isq - ss.b * isp));
 }
 
 // Inclusive scan of one wave, in lane order.
@@ -514,54 +592,56 @@ __device__ __forceinline__ int wave_find(int cnt, F mass, double target, double&
   return found;
 }
 
-// The final draw of sampling sequence b (block of kThreads threads), given
-// its decision d, all its chunk and sub-chunk sums, and the filled table.
+// Sum of x over the first wave's lanes, chunk i on lane i % 64 (the one
+// fixed order every caller uses).
+template <typename F>
+__device__ __forceinline__ double wave_chunk_sum(int ncr, F f, int lane) {
+  double z = 0.0;
+  for (int i = lane; i < ncr; i += 64) z += f(i);
+  return wave_sum_d(z);
+}
+
+// The draw of one sequence (a block of kThreads threads) from the pass that
+// decision d describes, given the pass's chunk sums cg [ncr] and sub-chunk
+// sums sg [ncr][32], the filled exp table and the uniform u.  Returns the
+// token in every thread.
 template <typename T>
-__device__ __forceinline__ void locate_seq(
-    int b, const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ dtok,
-    const float* __restrict__ uni, float t, int K, int V, int ncr,
-    const ChunkSums* __restrict__ csum, const SubSums* __restrict__ csub, const Decision& d,
-    const double* __restrict__ s_exp, int32_t* __restrict__ out, int32_t* __restrict__ nacc,
-    int32_t* __restrict__ kv_len, unsigned long long* counters) {
+__device__ __forceinline__ int locate_draw(const T* __restrict__ trow, const T* __restrict__ drow,
+                                           const Decision& d, double u, float t, int V, int ncr,
+                                           const ChunkSums* __restrict__ cg,
+                                           const SubSums* __restrict__ sg,
+                                           const double* __restrict__ s_exp) {
   static_assert(kSub == kThreads, "one sub-chunk entry per thread");
   __shared__ ChunkSums s_cs[kThreads];
   __shared__ double s_wtot[kThreads / 64];
-  __shared__ int s_draw[SV_MAX_K];
-  __shared__ int s_chunk, s_sub, s_fallback, s_qonly, s_first, s_lastpos;
+  __shared__ int s_chunk, s_sub, s_fallback, s_mode, s_first, s_lastpos;
   __shared__ double s_base, s_target, s_isq, s_isp;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const double cd = kLog2eD / (double)t;
-  const int n = d.n;
-  const bool bonus = (n == K);
-  if (tid < K) s_draw[tid] = dtok[(size_t)b * K + tid];
   // Chunk sums staged in LDS when they fit (V <= 2^21), read in place otherwise.
-  const ChunkSums* cg = csum + (size_t)b * ncr;
   const bool staged = ncr <= kThreads;
   if (staged && tid < ncr) s_cs[tid] = cg[tid];
   __syncthreads();
   const ChunkSums* cs = staged ? s_cs : cg;
   if (wave == 0) {
-    // Exact normalisers, then the residual (or q) masses of the chunks.
-    double sq = 0.0, sp = 0.0;
-    for (int i = lane; i < ncr; i += 64) { sq += cs[i].eq; sp += cs[i].ep; }
-    sq = wave_sum_d(sq);
-    sp = wave_sum_d(sp);
+    // Exact normalisers, then the masses of the chunks.
+    const double sq = wave_chunk_sum(ncr, [&](int i) { return cs[i].eq; }, lane);
+    const double sp = wave_chunk_sum(ncr, [&](int i) { return cs[i].ep; }, lane);
     const double isq = 1.0 / sq;
-    const double isp = bonus ? 0.0 : 1.0 / sp;
-    bool qonly = bonus;
-    double z = 0.0;
-    for (int i = lane; i < ncr; i += 64) z += chunk_mass(cs[i], qonly, isq, isp);
-    z = wave_sum_d(z);
-    if (!qonly && !(z > 0.0)) {                              // zero-mass residual: draw from q
-      qonly = true;
-      z = 0.0;
-      for (int i = lane; i < ncr; i += 64) z += chunk_mass(cs[i], true, isq, isp);
-      z = wave_sum_d(z);
+    int m = d.mode == kModeQ ? kDrawQ : kDrawResid;
+    double isp = m == kDrawQ ? 0.0 : d.coef / sp;
+    double z = wave_chunk_sum(ncr, [&](int i) { return chunk_mass(cs[i], m, isq, isp); }, lane);
+    if (m == kDrawResid && !(z > 0.0)) {
+      // Zero residual mass: the law stays (q - coef_prev p)_+ normalised, and
+      // with no mass above p it equals p (q itself when coef_prev = 0).
+      m = d.coef_prev == 0.0 ? kDrawQ : kDrawP;
+      isp = 1.0 / sp;
+      z = wave_chunk_sum(ncr, [&](int i) { return chunk_mass(cs[i], m, isq, isp); }, lane);
     }
-    const double target = (double)uni[(size_t)b * (K + 1) + K] * z;
+    const double target = u * z;
     double base = 0.0;
     int lastpos;
-    int ch = wave_find(ncr, [&](int i) { return chunk_mass(cs[i], qonly, isq, isp); }, target, base,
+    int ch = wave_find(ncr, [&](int i) { return chunk_mass(cs[i], m, isq, isp); }, target, base,
                        lastpos, lane);
     int fb = 0;
     if (ch < 0) {                                             // rounding at u -> 1
@@ -569,35 +649,38 @@ __device__ __forceinline__ void locate_seq(
       ch = lastpos < 0 ? 0 : lastpos;
     }
     // Sub-chunk level, same wave (no crossing is looked for once in fallback).
-    const SubSums* ss = csub + ((size_t)b * ncr + ch) * kSubPerChunk;
+    const SubSums* ss = sg + (size_t)ch * kSubPerChunk;
     double base2 = base;
     int lastsub;
-    int sc = wave_find(kSubPerChunk, [&](int j) { return sub_mass(ss[j], qonly, isq, isp); },
+    int sc = wave_find(kSubPerChunk, [&](int j) { return sub_mass(ss[j], m, isq, isp); },
                        fb ? (double)INFINITY : target, base2, lastsub, lane);
     if (sc < 0) {                                             // no crossing left: last positive run
       fb = 1;
       sc = lastsub < 0 ? 0 : lastsub;
     }
     if (lane == 0) {
-      s_chunk = ch; s_sub = sc; s_fallback = fb; s_qonly = qonly ? 1 : 0;
+      s_chunk = ch; s_sub = sc; s_fallback = fb; s_mode = m;
       s_base = base2; s_target = target; s_isq = isq; s_isp = isp;
       s_first = INT32_MAX; s_lastpos = -1;
     }
   }
   __syncthreads();
   const int ch = s_chunk;
-  const bool qonly = s_qonly != 0;
+  const int m = s_mode;
   const double isq = s_isq, isp = s_isp;
-  const T* trow = tgt + ((size_t)b * (K + 1) + n) * (size_t)V;
-  const T* drow = drf + ((size_t)b * K + (bonus ? 0 : n)) * (size_t)V;
   const int e = ch * kResChunk + s_sub * kSub + tid;
   double w = 0.0;
   if (e < V) {
     const double c256 = cd * 256.0;
-    const double q = exp2_neg(expo(Vec16<T>::one(trow + e), c256, ((double)d.xmq * cd) * 256.0), s_exp) * isq;
-    w = qonly ? q
-              : fmax(0.0, q - exp2_neg(expo(Vec16<T>::one(drow + e), c256, ((double)d.xmp * cd) * 256.0),
-                                       s_exp) * isp);
+    const double q = m == kDrawP ? 0.0
+                                 : exp2_neg(expo(Vec16<T>::one(trow + e), c256, ((double)d.xmq * cd) * 256.0),
+                                            s_exp) * isq;
+    if (m == kDrawQ) {
+      w = q;
+    } else {
+      const double p = exp2_neg(expo(Vec16<T>::one(drow + e), c256, ((double)d.xmp * cd) * 256.0), s_exp) * isp;
+      w = m == kDrawP ? p : fmax(0.0, q - p);
+    }
   }
   // Inclusive prefix over the 256 entries in vocabulary order: a wave scan
   // plus the totals of the waves before (fixed order).
@@ -612,9 +695,13 @@ __device__ __forceinline__ void locate_seq(
   int tok = s_first;
   if (tok == INT32_MAX) tok = s_lastpos;                     // no crossing: last positive weight
   if (tok < 0) tok = clampi(ch * kResChunk + s_sub * kSub, 0, V - 1);
-  emit(b, K, n, tok, s_draw, out, nacc, kv_len, counters);
+  return tok;
 }
 
+// ---------------------------------------------------------------------------
+// k_locate: grid (B); block 256.  The chain's final draw (sampling sequences
+// only), then the outputs.
+// ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_locate(
     const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ dtok,
@@ -623,16 +710,23 @@ __global__ __launch_bounds__(kThreads) void k_locate(
     const Decision* __restrict__ dec, int32_t* __restrict__ out, int32_t* __restrict__ nacc,
     int32_t* __restrict__ kv_len, unsigned long long* counters) {
   __shared__ double s_exp[kExpTable];
+  __shared__ int s_draw[SV_MAX_K];
   const int b = blockIdx.x;
-  const float t = temp_of(temp, b, force_greedy);
-  if (!(t > 0.f)) return;
   const Decision d = dec[b];
+  if (d.mode == kModeNone) return;
+  const float t = temp_of(temp, b, force_greedy);
+  if ((int)threadIdx.x < K) s_draw[threadIdx.x] = dtok[(size_t)b * K + threadIdx.x];
   fill_exp_table(s_exp);
-  locate_seq<T>(b, tgt, drf, dtok, uni, t, K, V, ncr, csum, csub, d, s_exp, out, nacc, kv_len, counters);
+  // (locate_draw synchronises the block before it reads either.)
+  const int tok = locate_draw<T>(tgt + (size_t)d.trow * V, drf + (size_t)d.drow * V, d,
+                                 (double)uni[(size_t)b * (K + 1) + K], t, V, ncr,
+                                 csum + (size_t)b * ncr, csub + (size_t)b * ncr * kSubPerChunk, s_exp);
+  emit(b, K, d.n, tok, s_draw, out, nacc, kv_len, counters);
 }
 
 // ---------------------------------------------------------------------------
-// k_residual: grid (B, ncr); block 256.  Sampling sequences only.
+// k_residual: grid (B, ncr); block 256.  The pass each decision asks for
+// (none for greedy or finished sequences).
 //
 // Lane mapping: the 8 lanes of group g = lane / 8 in wave w own sub-chunk
 // w * 8 + g (256 entries).  Each of their loads covers one 128-byte line of it,
@@ -641,7 +735,7 @@ __global__ __launch_bounds__(kThreads) void k_locate(
 // ---------------------------------------------------------------------------
 template <typename T, bool kAligned>
 __global__ __launch_bounds__(kThreads, 4) void k_residual(
-    const T* __restrict__ tgt, const T* __restrict__ drf, const float* __restrict__ temp, int K,
+    const T* __restrict__ tgt, const T* __restrict__ drf, const float* __restrict__ temp,
     int V, int ncr, int force_greedy, const Decision* __restrict__ dec,
     ChunkSums* __restrict__ csum, SubSums* __restrict__ csub) {
   constexpr int VN = Vec16<T>::N;
@@ -654,14 +748,13 @@ __global__ __launch_bounds__(kThreads, 4) void k_residual(
   const int cr = blockIdx.y;
   const int tid = threadIdx.x;
   const int sub_i = tid >> 3, s = tid & 7;
-  const float t = temp_of(temp, b, force_greedy);
-  if (!(t > 0.f)) return;
   const Decision d = dec[b];
-  const int n = d.n;
-  const bool bonus = (n == K);
+  if (d.mode == kModeNone) return;
+  const bool bonus = d.mode == kModeQ;
+  const float t = temp_of(temp, b, force_greedy);
   const double cd = kLog2eD / (double)t;
-  const T* trow = tgt + ((size_t)b * (K + 1) + n) * (size_t)V;
-  const T* drow = drf + ((size_t)b * K + (bonus ? 0 : n)) * (size_t)V;
+  const T* trow = tgt + (size_t)d.trow * (size_t)V;
+  const T* drow = drf + (size_t)d.drow * (size_t)V;
   const int e0 = cr * kResChunk + sub_i * kSub + s * VN;
   // Loads first, so they are in flight while the table is filled.
   u32x4_t rq[IT], rp[IT];
@@ -726,9 +819,10 @@ __global__ __launch_bounds__(kThreads, 4) void k_residual(
         const double wp = exp2_finish(ep[k], tp[k]);
         sq += wq;
         sp += wp;
-        // The sweep's normalisers only decide which entries count as q > p;
-        // an entry they misclassify has |q - p| ~ 1e-6 q, so the masses move
-        // by ~1e-12.  (-inf - -inf is NaN: not counted, weights are 0.)
+        // The normalisers in theta only decide which entries count as
+        // q > coef p; an entry they misclassify has |q - coef p| ~ 1e-6 q, so
+        // the masses move by ~1e-12.  (-inf - -inf is NaN: not counted,
+        // weights are 0.)
         const double f = act[k] ? 1.0 : 0.0;
         sa = fma(wq, f, sa);
         sb = fma(wp, f, sb);
@@ -758,6 +852,252 @@ __global__ __launch_bounds__(kThreads, 4) void k_residual(
     for (int j = 0; j < kSubPerChunk; ++j) acc += reinterpret_cast<const double*>(&s_sub[j])[comp];
     reinterpret_cast<double*>(csum + (size_t)b * ncr + cr)[tid] = acc;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Tree verification.
+// ---------------------------------------------------------------------------
+// Outputs of a finished tree walk (threads 0..n-1 of the block): the final
+// token after the path already written, -1 padding, the accepted count and
+// the committed length.
+__device__ __forceinline__ void emit_tree(int b, int N, int n, int tok, int32_t* __restrict__ out_tok,
+                                          int32_t* __restrict__ out_node, int32_t* __restrict__ nacc,
+                                          int32_t* __restrict__ kv_len, unsigned long long* counters) {
+  const int i = threadIdx.x;
+  if (i < N) {
+    if (i >= n) out_tok[(size_t)b * N + i] = (i == n) ? tok : -1;
+    if (i >= n) out_node[(size_t)b * N + i] = -1;
+  }
+  if (i == 0) {
+    nacc[b] = n;
+    kv_len[b] = kv_len[b] + n + 1;
+    if (counters) {
+      atomicAdd(&counters[0], (unsigned long long)(N - 1));
+      atomicAdd(&counters[1], (unsigned long long)n);
+    }
+  }
+}
+
+// Walks sampling sequence b down from node v (n nodes accepted so far) with
+// the sweep's statistics: the first child of every node is tested against q_v
+// itself.  Accepted nodes are written to the outputs; the walk stops at the
+// first rejection (a pass with coef = 1 follows) or at a leaf (the bonus
+// pass from q_v follows).  One thread; rs(r) gives the merged statistics
+// (raw max, sum) of swept row r.
+template <class RS>
+__device__ void tree_walk(int b, int v, int n, const TreeShape& s, RS rs, const float* __restrict__ xd,
+                          const int32_t* __restrict__ tok, const float* __restrict__ uni, float c,
+                          double cd, int32_t* __restrict__ out_tok, int32_t* __restrict__ out_node,
+                          Decision& dd, TreeState& st) {
+  const int N = s.n;
+  for (;;) {
+    const int k0 = s.kid_off[v], k1 = s.kid_off[v + 1];
+    const float2 rq = rs(v);
+    if (k0 == k1) {
+      dd = Decision{kModeQ, n, b * N + v, 0, rq.x, 0.f, 0.0, 0.0, 0.0};
+      st = TreeState{v, 0, n, 1, 1.0};
+      return;
+    }
+    const float2 rp = rs(N + s.int_idx[v]);
+    const int ch = s.kids[k0];
+    const size_t ci = (size_t)b * N + ch;
+    const float xq = xd[ci * 2], xp = xd[ci * 2 + 1];
+    bool acc;
+    if (xp == -INFINITY) {
+      acc = true;                                   // p(d) == 0
+    } else {
+      // q/p in the log domain, as in the chain's accept tests.
+      const double mq = (double)(rq.x * c), mp = (double)(rp.x * c);
+      const double ly = ((double)xq * (double)c - mq) - ((double)xp * (double)c - mp);
+      const double r = exp2(ly) * ((double)rp.y / (double)rq.y);
+      acc = (double)uni[ci] < fmin(1.0, r);
+    }
+    if (acc) {
+      out_node[(size_t)b * N + n] = ch;
+      out_tok[(size_t)b * N + n] = tok[ci];
+      ++n;
+      v = ch;
+      continue;
+    }
+    // Sweep normalisers moved to the exact pass's frame, for its q > p split.
+    const double sq = (double)rq.y * exp2((double)(rq.x * c) - (double)rq.x * cd);
+    const double sp = (double)rp.y * exp2((double)(rp.x * c) - (double)rp.x * cd);
+    dd = Decision{kModeResid, n, b * N + v, b * N + v, rq.x, rp.x, log2(sq) - log2(sp), 1.0, 0.0};
+    st = TreeState{v, 1, n, (k1 - k0 == 1) ? 1 : 0, 1.0};
+    return;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_tree_decide: grid (B); block 1024.  Merges the row statistics (kept in
+// rowstat for the later rounds), finishes greedy sequences and starts the
+// walk of sampling ones.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kDecideThreads) void k_tree_decide(
+    const int32_t* __restrict__ tok, const float* __restrict__ uni, const float* __restrict__ temp,
+    TreeShape s, int V, int nc, int force_greedy, const float2* __restrict__ part,
+    const float* __restrict__ xd, float2* __restrict__ rowstat, Decision* __restrict__ dec,
+    TreeState* __restrict__ state, int32_t* __restrict__ out_tok, int32_t* __restrict__ out_node,
+    int32_t* __restrict__ nacc, int32_t* __restrict__ kv_len, unsigned long long* counters) {
+  __shared__ float2 s_rs[2 * kMaxTree];
+  __shared__ float2 s_part[kPartStage];
+  __shared__ int s_n, s_tok;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int N = s.n, R = s.n + s.n_int;
+  const float t = temp_of(temp, b, force_greedy);
+  const bool greedy = !(t > 0.f);
+  const int rows = greedy ? N : R;
+  const float c = greedy ? 0.f : kLog2e / t;
+  const float2* pb = part + (size_t)b * R * nc;
+  const bool staged = rows * nc <= kPartStage;
+  if (staged)
+    for (int k = tid; k < rows * nc; k += kDecideThreads) s_part[k] = pb[k];
+  __syncthreads();
+  for (int r = wave; r < rows; r += kDecideThreads / 64) {
+    float a, bb;
+    merge_row(staged ? s_part + r * nc : pb + (size_t)r * nc, nc, greedy, c, lane, a, bb);
+    if (lane == 0) s_rs[r] = make_float2(a, bb);
+  }
+  __syncthreads();
+  if (!greedy && tid < R) rowstat[(size_t)b * R + tid] = s_rs[tid];
+  if (tid == 0) {
+    if (greedy) {
+      // Follow the child whose token is the argmax of q_v (lowest index on
+      // ties), the first such child in index order.
+      int v = 0, n = 0, fin;
+      for (;;) {
+        const int am = __float_as_int(s_rs[v].y);
+        int nxt = -1;
+        for (int k = s.kid_off[v]; k < s.kid_off[v + 1]; ++k)
+          if (clampi(tok[(size_t)b * N + s.kids[k]], 0, V - 1) == am) { nxt = s.kids[k]; break; }
+        if (nxt < 0) { fin = am; break; }
+        out_node[(size_t)b * N + n] = nxt;
+        out_tok[(size_t)b * N + n] = tok[(size_t)b * N + nxt];
+        ++n;
+        v = nxt;
+      }
+      s_n = n;
+      s_tok = fin;
+      dec[b] = Decision{kModeNone, n, 0, 0, 0.f, 0.f, 0.0, 0.0, 0.0};
+    } else {
+      Decision dd;
+      TreeState st;
+      tree_walk(b, 0, 0, s, [&](int r) { return s_rs[r]; }, xd, tok, uni, c, kLog2eD / (double)t,
+                out_tok, out_node, dd, st);
+      dec[b] = dd;
+      state[b] = st;
+    }
+  }
+  if (greedy) {
+    __syncthreads();
+    emit_tree(b, N, s_n, s_tok, out_tok, out_node, nacc, kv_len, counters);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_tree_step: grid (B); block 256.  One round after the pass k_residual made
+// for each active sequence: either the final draw (then the outputs), or the
+// next sibling's test against the exact residual, which schedules the next
+// pass (a further rejection, or a rejection or leaf below an accepted child).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_tree_step(
+    const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ tok,
+    const float* __restrict__ uni, const float* __restrict__ temp, TreeShape s, int V, int ncr,
+    int force_greedy, int last, const float2* __restrict__ rowstat, const float* __restrict__ xd,
+    const ChunkSums* __restrict__ csum, const SubSums* __restrict__ csub,
+    Decision* __restrict__ dec, TreeState* __restrict__ state, int32_t* __restrict__ out_tok,
+    int32_t* __restrict__ out_node, int32_t* __restrict__ nacc, int32_t* __restrict__ kv_len,
+    unsigned long long* counters) {
+  __shared__ double s_exp[kExpTable];
+  __shared__ int s_draw, s_n;
+  const int b = blockIdx.x;
+  const Decision d = dec[b];
+  if (d.mode == kModeNone) return;
+  const TreeState st = state[b];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = s.n, R = s.n + s.n_int;
+  const float t = temp_of(temp, b, force_greedy);
+  const double cd = kLog2eD / (double)t;
+  const ChunkSums* cg = csum + (size_t)b * ncr;
+  fill_exp_table(s_exp);
+  if (wave == 0) {
+    int draw = 1, n = st.n;
+    if (!st.fin) {
+      // The pass ran at coef after a rejection; its exact normalisers and the
+      // residual mass Z (summed exactly as the draw sums it).
+      const double sq = wave_chunk_sum(ncr, [&](int i) { return cg[i].eq; }, lane);
+      const double sp = wave_chunk_sum(ncr, [&](int i) { return cg[i].ep; }, lane);
+      const double isq = 1.0 / sq, isp = d.coef / sp;
+      const double z = wave_chunk_sum(ncr, [&](int i) { return chunk_mass(cg[i], kDrawResid, isq, isp); },
+                                      lane);
+      if (lane == 0) {
+        // A zero-mass residual leaves the law as it was.
+        const bool frozen = !(z > 0.0);
+        const double coef = frozen ? d.coef_prev : d.coef;
+        const double zz = frozen ? st.n_prev : z;
+        const int v = st.v, k0 = s.kid_off[v], nk = s.kid_off[v + 1] - k0;
+        int pos = st.pos;
+        for (;;) {
+          const int ch = s.kids[k0 + pos];
+          const size_t ci = (size_t)b * N + ch;
+          const float xq = xd[ci * 2], xp = xd[ci * 2 + 1];
+          bool acc;
+          if (xp == -INFINITY) {
+            acc = true;
+          } else {
+            // q'(d) / p(d) = (q(d) / p(d) - coef)_+ / Z with the exact normalisers.
+            const double lr = ((double)xq - (double)d.xmq) * cd - ((double)xp - (double)d.xmp) * cd;
+            const double ratio = exp2(lr) * (sp / sq);
+            const double r = fmax(0.0, ratio - coef) / zz;
+            acc = (double)uni[ci] < fmin(1.0, r);
+          }
+          if (acc) {
+            out_node[(size_t)b * N + n] = ch;
+            out_tok[(size_t)b * N + n] = tok[ci];
+            Decision dd;
+            TreeState ns;
+            tree_walk(b, ch, n + 1, s, [&](int r) { return rowstat[(size_t)b * R + r]; }, xd, tok, uni,
+                      kLog2e / t, cd, out_tok, out_node, dd, ns);
+            dec[b] = dd;
+            state[b] = ns;
+            draw = 0;
+            break;
+          }
+          ++pos;
+          if (frozen) {
+            if (pos < nk) continue;
+            break;                                   // every child rejected: draw now
+          }
+          // Next residual step: coef grows by this pass's mass.
+          Decision dd = d;
+          dd.coef = d.coef + z;
+          dd.coef_prev = d.coef;
+          dd.theta = log2(dd.coef) + (log2(sq) - log2(sp));
+          dec[b] = dd;
+          state[b] = TreeState{v, pos, n, pos == nk ? 1 : 0, z};
+          draw = 0;
+          break;
+        }
+        if (!draw && last) {
+          // The shape bounds the rounds, so this is unreachable; flag the
+          // sequence rather than leave stale outputs.
+          nacc[b] = -1;
+          dec[b].mode = kModeNone;
+        }
+      }
+      draw = __shfl(draw, 0, 64);
+    }
+    if (lane == 0) { s_draw = draw; s_n = n; }
+  }
+  __syncthreads();
+  if (!s_draw) return;
+  const int tk = locate_draw<T>(tgt + (size_t)d.trow * V, drf + (size_t)d.drow * V, d,
+                                (double)uni[(size_t)b * N], t, V, ncr, cg,
+                                csub + (size_t)b * ncr * kSubPerChunk, s_exp);
+  emit_tree(b, N, s_n, tk, out_tok, out_node, nacc, kv_len, counters);
+  if (tid == 0) dec[b].mode = kModeNone;
 }
 
 struct RejectPlan {
@@ -793,14 +1133,108 @@ static hipError_t launch_all(const void* tgt, const void* drf, const int32_t* dt
   float* xd = reinterpret_cast<float*>(ws + p.xd_off);
   const T* t = static_cast<const T*>(tgt);
   const T* d = static_cast<const T*>(drf);
-  hipLaunchKernelGGL((k_sweep<T, kAligned>), dim3(B * R, (nc + 3) / 4), dim3(kThreads), 0, st, t, d,
-                     dtok, temp, K, V, nc, force_greedy, part, xd);
+  hipLaunchKernelGGL((k_sweep<T, kAligned, ChainRows>), dim3(B * R, (nc + 3) / 4), dim3(kThreads), 0,
+                     st, t, d, dtok, temp, ChainRows{K}, V, nc, force_greedy, part, xd);
   hipLaunchKernelGGL(k_decide, dim3(B), dim3(kDecideThreads), 0, st, dtok, uni, temp, K, V, nc,
                      force_greedy, part, xd, dec, out, nacc, kv_len, counters);
-  hipLaunchKernelGGL((k_residual<T, kAligned>), dim3(B, ncr), dim3(kThreads), 0, st, t, d, temp, K, V,
+  hipLaunchKernelGGL((k_residual<T, kAligned>), dim3(B, ncr), dim3(kThreads), 0, st, t, d, temp, V,
                      ncr, force_greedy, dec, csum, csub);
   hipLaunchKernelGGL((k_locate<T>), dim3(B), dim3(kThreads), 0, st, t, d, dtok, uni, temp, K, V, ncr,
                      force_greedy, csum, csub, dec, out, nacc, kv_len, counters);
+  return hipGetLastError();
+}
+
+// Tree workspace: the chain's arrays for up to 2N - 1 swept rows, plus the
+// merged row statistics and the walk states.
+struct TreePlan {
+  size_t part_off, rowstat_off, csum_off, csub_off, dec_off, state_off, xd_off, total;
+};
+
+static inline TreePlan tree_plan(int B, int N, int V) {
+  TreePlan p{};
+  const size_t R = 2 * (size_t)N - 1;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  p.part_off = 0;
+  p.rowstat_off = up((size_t)B * R * sweep_chunks(V) * sizeof(float2));
+  p.csum_off = p.rowstat_off + up((size_t)B * R * sizeof(float2));
+  p.csub_off = p.csum_off + up((size_t)B * res_chunks(V) * sizeof(ChunkSums));
+  p.dec_off = p.csub_off + up((size_t)B * res_chunks(V) * kSubPerChunk * sizeof(SubSums));
+  p.state_off = p.dec_off + up((size_t)B * sizeof(Decision));
+  p.xd_off = p.state_off + up((size_t)B * sizeof(TreeState));
+  p.total = p.xd_off + up((size_t)B * N * 2 * sizeof(float));
+  return p;
+}
+
+// Children lists of parent[] (parent[0] = -1, 0 <= parent[i] < i).
+static inline bool build_shape(const int32_t* parent, int N, TreeShape& s) {
+  if (N < 1 || N > kMaxTree || parent[0] != -1) return false;
+  int cnt[kMaxTree] = {0};
+  for (int i = 1; i < N; ++i) {
+    if (parent[i] < 0 || parent[i] >= i) return false;
+    ++cnt[parent[i]];
+  }
+  s = TreeShape{};
+  s.n = N;
+  s.kid_off[0] = 0;
+  for (int v = 0; v < N; ++v) s.kid_off[v + 1] = (int8_t)(s.kid_off[v] + cnt[v]);
+  int fill[kMaxTree];
+  for (int v = 0; v < N; ++v) fill[v] = s.kid_off[v];
+  for (int i = 1; i < N; ++i) s.kids[fill[parent[i]]++] = (int8_t)i;
+  s.n_int = 0;
+  for (int v = 0; v < N; ++v) {
+    s.int_idx[v] = -1;
+    if (cnt[v] > 0) {
+      s.int_idx[v] = (int8_t)s.n_int;
+      s.int_node[s.n_int++] = (int8_t)v;
+    }
+  }
+  return true;
+}
+
+// The most exact passes a walk from v can need: each rejection among v's
+// children costs one (the last one also serves the final draw), a leaf one
+// (the bonus draw); accepting child j after j rejections continues there.
+static int tree_rounds(const TreeShape& s, int v) {
+  const int k0 = s.kid_off[v], m = s.kid_off[v + 1] - k0;
+  if (m == 0) return 1;
+  int best = m;
+  for (int j = 0; j < m; ++j) best = std::max(best, j + tree_rounds(s, s.kids[k0 + j]));
+  return best;
+}
+
+template <typename T, bool kAligned>
+static hipError_t launch_tree(const void* tgt, const void* drf, const TreeShape& shape,
+                              const int32_t* tok, const float* uni, const float* temp,
+                              int32_t* out_tok, int32_t* out_node, int32_t* nacc, int32_t* kv_len,
+                              unsigned long long* counters, int B, int V, int force_greedy, char* ws,
+                              hipStream_t st) {
+  const int N = shape.n;
+  const int nc = sweep_chunks(V);
+  const int ncr = res_chunks(V);
+  const int R = shape.n + shape.n_int;
+  const TreePlan p = tree_plan(B, N, V);
+  float2* part = reinterpret_cast<float2*>(ws + p.part_off);
+  float2* rowstat = reinterpret_cast<float2*>(ws + p.rowstat_off);
+  ChunkSums* csum = reinterpret_cast<ChunkSums*>(ws + p.csum_off);
+  SubSums* csub = reinterpret_cast<SubSums*>(ws + p.csub_off);
+  Decision* dec = reinterpret_cast<Decision*>(ws + p.dec_off);
+  TreeState* state = reinterpret_cast<TreeState*>(ws + p.state_off);
+  float* xd = reinterpret_cast<float*>(ws + p.xd_off);
+  const T* t = static_cast<const T*>(tgt);
+  const T* d = static_cast<const T*>(drf);
+  hipLaunchKernelGGL((k_sweep<T, kAligned, TreeRows>), dim3(B * R, (nc + 3) / 4), dim3(kThreads), 0,
+                     st, t, d, tok, temp, TreeRows{shape}, V, nc, force_greedy, part, xd);
+  hipLaunchKernelGGL(k_tree_decide, dim3(B), dim3(kDecideThreads), 0, st, tok, uni, temp, shape, V, nc,
+                     force_greedy, part, xd, rowstat, dec, state, out_tok, out_node, nacc, kv_len,
+                     counters);
+  const int rounds = force_greedy ? 0 : tree_rounds(shape, 0);
+  for (int r = 1; r <= rounds; ++r) {
+    hipLaunchKernelGGL((k_residual<T, kAligned>), dim3(B, ncr), dim3(kThreads), 0, st, t, d, temp, V,
+                       ncr, force_greedy, dec, csum, csub);
+    hipLaunchKernelGGL((k_tree_step<T>), dim3(B), dim3(kThreads), 0, st, t, d, tok, uni, temp, shape, V,
+                       ncr, force_greedy, r == rounds ? 1 : 0, rowstat, xd, csum, csub, dec, state,
+                       out_tok, out_node, nacc, kv_len, counters);
+  }
   return hipGetLastError();
 }
 
@@ -854,6 +1288,60 @@ extern "C" int spec_reject_sample(const void* target_logits, const void* draft_l
            : sv::launch_all<float, false>(target_logits, drf, draft_tokens, uniforms, temperature,
                                           out_tokens, num_accepted, kv_len, counters, B, K, V,
                                           force_greedy, ws, st);
+  }
+  return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+extern "C" size_t spec_reject_sample_tree_workspace_bytes(int B, int N, int V) {
+  if (B <= 0 || N < 1 || N > sv::kMaxTree || V < 1) return 0;
+  return sv::tree_plan(B, N, V).total;
+}
+
+extern "C" int spec_reject_sample_tree(const void* target_logits, const void* draft_logits,
+                                       const int32_t* parent, const int32_t* tokens,
+                                       const float* uniforms, const float* temperature,
+                                       int32_t* out_tokens, int32_t* out_nodes,
+                                       int32_t* num_accepted, int32_t* kv_len,
+                                       unsigned long long* counters, int B, int N, int V, int dtype,
+                                       void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (B < 0 || N < 1 || V < 1 || !parent) return SV_ERR_INVALID_ARG;
+  if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_INVALID_ARG;
+  if (N > sv::kMaxTree) return SV_ERR_UNSUPPORTED;
+  sv::TreeShape shape;
+  if (!sv::build_shape(parent, N, shape)) return SV_ERR_INVALID_ARG;
+  if ((long long)V >= (1LL << 31) / 4) return SV_ERR_UNSUPPORTED;
+  if ((long long)B * (2 * N - 1) > 0x7fffffffLL || (sv::sweep_chunks(V) + 3) / 4 > 65535 ||
+      sv::res_chunks(V) > 65535)
+    return SV_ERR_UNSUPPORTED;
+  if (B == 0) return SV_OK;
+  if (!target_logits || !tokens || !uniforms || !temperature || !out_tokens || !out_nodes ||
+      !num_accepted || !kv_len || !workspace)
+    return SV_ERR_INVALID_ARG;
+  if (workspace_bytes < spec_reject_sample_tree_workspace_bytes(B, N, V)) return SV_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return SV_ERR_INVALID_ARG;
+  const int force_greedy = draft_logits == nullptr ? 1 : 0;
+  const void* drf = draft_logits ? draft_logits : target_logits;   // never read when greedy
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  char* ws = static_cast<char*>(workspace);
+  const uintptr_t align_bits = reinterpret_cast<uintptr_t>(target_logits) |
+                               reinterpret_cast<uintptr_t>(drf);
+  hipError_t e;
+  if (dtype == SV_BF16) {
+    const bool al = (V % 8 == 0) && (align_bits & 15) == 0;
+    e = al ? sv::launch_tree<uint16_t, true>(target_logits, drf, shape, tokens, uniforms, temperature,
+                                             out_tokens, out_nodes, num_accepted, kv_len, counters, B,
+                                             V, force_greedy, ws, st)
+           : sv::launch_tree<uint16_t, false>(target_logits, drf, shape, tokens, uniforms, temperature,
+                                              out_tokens, out_nodes, num_accepted, kv_len, counters, B,
+                                              V, force_greedy, ws, st);
+  } else {
+    const bool al = (V % 4 == 0) && (align_bits & 15) == 0;
+    e = al ? sv::launch_tree<float, true>(target_logits, drf, shape, tokens, uniforms, temperature,
+                                          out_tokens, out_nodes, num_accepted, kv_len, counters, B, V,
+                                          force_greedy, ws, st)
+           : sv::launch_tree<float, false>(target_logits, drf, shape, tokens, uniforms, temperature,
+                                           out_tokens, out_nodes, num_accepted, kv_len, counters, B, V,
+                                           force_greedy, ws, st);
   }
   return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }

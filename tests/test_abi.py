@@ -114,3 +114,42 @@ def test_tree_attn_validation(lib):
     assert f(p, p, p, p, p, p, p, 2, 18, 32, 8, 128, 16, 10, 600, 8192, 0.0, 1, p, 1 << 30, None) == -2
     assert f(None, None, None, None, None, None, None, 0, 8, 32, 8, 128, 16, 10, 600, 8192, 0.0, 1,
              None, 0, None) == 0                               # empty batch: no-op
+
+
+def _tree_reject(lib, parent=(-1, 0, 0, 1), B=4, V=100, dtype=1, ws_bytes=1 << 24, ptrs=True,
+                 N=None):
+    p = FAKE if ptrs else None
+    n = (4 if parent is None else len(parent)) if N is None else N
+    par = None if parent is None else (ctypes.c_int32 * len(parent))(*parent)
+    return lib.spec_reject_sample_tree(p, p, None if par is None else ctypes.cast(par, ctypes.c_void_p),
+                                       p, p, p, p, p, p, p, None, B, n, V, dtype, p, ws_bytes, None)
+
+
+def test_tree_reject_validation(lib):
+    need = sv.reject_sample_tree_workspace_bytes(4, 4, 100)
+    assert need > 0 and need % 256 == 0
+    assert _tree_reject(lib, ws_bytes=need - 1) == -3
+    assert _tree_reject(lib, parent=None) == -1                  # no topology
+    assert _tree_reject(lib, parent=(0, 0, 1)) == -1             # root must have parent -1
+    assert _tree_reject(lib, parent=(-1, 0, 2)) == -1            # parent[i] >= i
+    assert _tree_reject(lib, parent=(-1, -1, 0)) == -1           # a second root
+    assert _tree_reject(lib, parent=(-1, 0, 0, 5)) == -1         # parent out of range
+    assert _tree_reject(lib, B=-1) == -1
+    assert _tree_reject(lib, V=0) == -1
+    assert _tree_reject(lib, dtype=5) == -1
+    assert _tree_reject(lib, parent=tuple([-1] + list(range(17)))) == -2   # N = 18 > SV_MAX_K + 1
+    assert _tree_reject(lib, ptrs=False) == -1
+    assert _tree_reject(lib, B=0, ptrs=False) == 0               # empty batch: no-op
+    assert _tree_reject(lib, parent=(-1,), B=0, ptrs=False) == 0 # a root alone is a valid tree
+
+
+def test_tree_reject_workspace_matches_chain(lib):
+    # A chain of K + 1 nodes sweeps the same 2K + 1 rows as the chain call;
+    # the tree adds its walk state and merged row statistics.
+    for B, K, V in [(64, 7, 128256), (1, 1, 1000), (3, 16, 152064)]:
+        t = sv.reject_sample_tree_workspace_bytes(B, K + 1, V)
+        c = sv.reject_sample_workspace_bytes(B, K, V)
+        assert t >= c > 0
+    assert sv.reject_sample_tree_workspace_bytes(0, 4, 100) == 0
+    assert sv.reject_sample_tree_workspace_bytes(4, 0, 100) == 0
+    assert sv.reject_sample_tree_workspace_bytes(4, 18, 100) == 0
