@@ -3,7 +3,8 @@
 
 One step = spec_verify_attn (one attention layer over the paged KV cache)
 followed by spec_reject_sample (full-vocabulary verifier + KV commit) for one
-batch.  Default workload: the Llama-3-8B-shaped serving batch (B=64, K=7,
+batch; with --tree SHAPE, spec_verify_attn_tree + spec_reject_sample_tree
+over a draft tree of that shape instead.  Default workload: the Llama-3-8B-shaped serving batch (B=64, K=7,
 V=128256, 32 q / 8 kv heads, D=128, contexts U[2048, 8192], bf16, T=1,
 draft noise giving alpha ~ 0.8).
 
@@ -78,6 +79,10 @@ def parse():
                    help="instead of the bench: copy MIB MiB device to device 8 times (the "
                         "known-size kernel that scales the HBM byte counters), then exit")
     p.add_argument("--sets", type=int, default=3, help="rotating logit sets")
+    p.add_argument("--tree", default="", metavar="SHAPE",
+                   help="verify a draft tree instead of a chain: branching factors per level, "
+                        "e.g. 2,2,2 (15 nodes); times spec_verify_attn_tree + "
+                        "spec_reject_sample_tree on the same serving batch")
     return p.parse_args()
 
 
@@ -104,6 +109,12 @@ def main():
     torch.cuda.set_device(0)
     cfg = CONFIGS[args.config]
     B, K, V = cfg.B, cfg.K, cfg.V
+    parent = None
+    if args.tree:
+        from oracle.tree import tree_parents, tree_masks
+        shape = tuple(int(x) for x in args.tree.split(","))
+        parent = tree_parents(shape)
+        K = len(parent) - 1                       # window of N = K + 1 tree nodes
     K1 = K + 1
     print("bench: %s B=%d K=%d V=%d T=%.2f steps=%d warmup=%d" %
           (cfg.name, B, K, V, args.temp, args.steps, args.warmup), file=sys.stderr, flush=True)
@@ -114,30 +125,55 @@ def main():
     max_kv = int(from_device(kv0).max())
     rsets = []
     for j in range(args.sets):
-        inp = gen.make_reject_inputs(seed=args.seed + 1 + j, B=B, K=K, V=V,
-                                     dtype=cfg.logit_dtype, logit_std=cfg.logit_std,
-                                     draft_sigma=cfg.draft_sigma, temperature=args.temp)
-        rsets.append({"host": inp, "dev": {k: to_device(v, dev) for k, v in inp.items()}})
+        if parent is None:
+            inp = gen.make_reject_inputs(seed=args.seed + 1 + j, B=B, K=K, V=V,
+                                         dtype=cfg.logit_dtype, logit_std=cfg.logit_std,
+                                         draft_sigma=cfg.draft_sigma, temperature=args.temp)
+        else:
+            inp = gen.make_tree_reject_inputs(seed=args.seed + 1 + j, B=B, parent=parent, V=V,
+                                              dtype=cfg.logit_dtype, logit_std=cfg.logit_std,
+                                              draft_sigma=cfg.draft_sigma,
+                                              temperature=args.temp)
+        rsets.append({"host": inp, "dev": {k: to_device(v, dev) for k, v in inp.items()
+                                           if k != "parent"}})
+    anc = None
+    if parent is not None:
+        anc = to_device(np.broadcast_to(tree_masks(parent).astype(np.uint32),
+                                        (B, K1)).copy().view(np.int32), dev)
     n_total = args.warmup + args.steps
     kv_bufs = [kv0.clone() for _ in range(n_total)]
     attn_out = torch.empty_like(attn["q"])
     attn_ws = torch.empty(max(256, sv.verify_attn_workspace_bytes(B, K, cfg.Hq, cfg.Hkv, cfg.D,
                                                                   max_kv)),
                           dtype=torch.uint8, device=dev)
-    rej_ws = torch.empty(sv.reject_sample_workspace_bytes(B, K, V), dtype=torch.uint8, device=dev)
+    rej_ws = torch.empty(sv.reject_sample_workspace_bytes(B, K, V) if parent is None else
+                         sv.reject_sample_tree_workspace_bytes(B, K1, V),
+                         dtype=torch.uint8, device=dev)
     out_tok = [torch.empty((B, K1), dtype=torch.int32, device=dev) for _ in range(args.sets)]
+    out_node = [torch.empty((B, K1), dtype=torch.int32, device=dev) for _ in range(args.sets)]
     n_acc = [torch.empty((B,), dtype=torch.int32, device=dev) for _ in range(args.sets)]
     torch.cuda.synchronize()
+    print("bench: inputs resident", file=sys.stderr, flush=True)
 
     def attn_call():
-        sv.verify_attn(attn["q"], attn["k_cache"], attn["v_cache"], attn["block_table"], kv0,
-                       out=attn_out, max_kv_len=max_kv, workspace=attn_ws)
+        if parent is None:
+            sv.verify_attn(attn["q"], attn["k_cache"], attn["v_cache"], attn["block_table"], kv0,
+                           out=attn_out, max_kv_len=max_kv, workspace=attn_ws)
+        else:
+            sv.verify_attn_tree(attn["q"], attn["k_cache"], attn["v_cache"], attn["block_table"],
+                                kv0, anc, out=attn_out, max_kv_len=max_kv, workspace=attn_ws)
 
     def reject_call(s, kv):
         r = rsets[s % args.sets]["dev"]
-        sv.reject_sample(r["target"], r["draft"], r["draft_tokens"], r["uniforms"],
-                         r["temperature"], kv, out_tokens=out_tok[s % args.sets],
-                         num_accepted=n_acc[s % args.sets], workspace=rej_ws)
+        if parent is None:
+            sv.reject_sample(r["target"], r["draft"], r["draft_tokens"], r["uniforms"],
+                             r["temperature"], kv, out_tokens=out_tok[s % args.sets],
+                             num_accepted=n_acc[s % args.sets], workspace=rej_ws)
+        else:
+            sv.reject_sample_tree(r["target"], r["draft"], parent, r["tokens"], r["uniforms"],
+                                  r["temperature"], kv, out_tokens=out_tok[s % args.sets],
+                                  out_nodes=out_node[s % args.sets],
+                                  num_accepted=n_acc[s % args.sets], workspace=rej_ws)
 
     def step(s):
         attn_call()
@@ -194,17 +230,22 @@ def main():
     achieved = attn_bytes / (attn_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": _traffic(),
-                "kernel": "spec_verify_attn call = k_attn_stream + k_attn_stream_combine",
+                "traffic": _traffic() if parent is None else None,
+                "kernel": "%s call = k_attn_stream + k_attn_stream_combine" %
+                          ("spec_verify_attn" if parent is None else "spec_verify_attn_tree"),
                 "algorithmic_bytes": attn_bytes, "avg_us": round(attn_us, 2)}
-    rej_bytes = B * (2 * K + 1) * V * 2 if args.temp > 0 else B * K1 * V * 2
+    # The sweep reads every target row and the draft rows of the nodes with
+    # children (all K draft rows of a chain); greedy reads target rows only.
+    # The exact passes after rejections come on top and are not counted.
+    n_draft_rows = K if parent is None else len(set(int(x) for x in parent[1:]))
+    rej_bytes = B * (K1 + (n_draft_rows if args.temp > 0 else 0)) * V * 2
     rej_us = float(rej_ms * 1e3)
     rej_gbs = rej_bytes / (rej_us * 1e-6) / 1e9
 
     # ---- CPU baseline: the oracle on a bounded sample ---------------------
     cpu = None
     if args.cpu_sample > 0:
-        cpu = cpu_baseline(args, cfg, attn, rsets[0]["host"], from_device)
+        cpu = cpu_baseline(args, cfg, attn, rsets[0]["host"], from_device, parent)
 
     rec = {
         "metric": METRIC,
@@ -219,9 +260,11 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "%s: B=%d K=%d V=%d, %dq/%dkv heads D=%d, ctx U[%d,%d], "
+        "config": {"workload": "%s: B=%d %s V=%d, %dq/%dkv heads D=%d, ctx U[%d,%d], "
                                "bf16 logits N(0,2), draft sigma %.2f, T=%.2f" %
-                               (cfg.name, B, K, V, cfg.Hq, cfg.Hkv, cfg.D, cfg.ctx[0], cfg.ctx[1],
+                               (cfg.name, B, ("K=%d" % K) if parent is None else
+                                ("draft tree [%s] (%d nodes)" % (args.tree, K1)),
+                                V, cfg.Hq, cfg.Hkv, cfg.D, cfg.ctx[0], cfg.ctx[1],
                                 cfg.draft_sigma, args.temp),
                    "global_batch": B, "K": K, "V": V, "parallelism": "single GPU"},
         "roofline": roofline,
@@ -254,22 +297,25 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 8}), flush=True)
 
 
-def cpu_baseline(args, cfg, attn, host_rej, from_device):
+def cpu_baseline(args, cfg, attn, host_rej, from_device, parent=None):
     """Time the oracle (as it stands) on the first ``cpu_sample`` sequences of
     the same workload, repeated until ``cpu_seconds`` have passed."""
     import torch
     from oracle import attention as oat
     from oracle import reject as orj
+    from oracle import tree as otr
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         blas_threads = 1
-    n = min(args.cpu_sample, cfg.B)
+    K1 = cfg.K + 1 if parent is None else len(parent)
+    # The tree oracle's attention masks every node separately: a smaller sample.
+    n = min(args.cpu_sample if parent is None else max(1, args.cpu_sample // 8), cfg.B)
     idx = np.arange(n)
     kvl = from_device(attn["kv_len"])[:n]
     bt = from_device(attn["block_table"])[:n]
-    pages = np.unique(np.concatenate([bt[b, :(kvl[b] + cfg.K + 1 + 15) // 16] for b in range(n)]))
+    pages = np.unique(np.concatenate([bt[b, :(kvl[b] + K1 + 15) // 16] for b in range(n)]))
     remap = np.zeros(int(pages.max()) + 1, dtype=np.int32)
     remap[pages] = np.arange(len(pages), dtype=np.int32)
     sel = torch.from_numpy(pages).long().to(attn["k_cache"].device)
@@ -278,18 +324,26 @@ def cpu_baseline(args, cfg, attn, host_rej, from_device):
     q = from_device(attn["q"][:n])
     bt_local = np.zeros_like(bt)
     for b in range(n):
-        m = (kvl[b] + cfg.K + 1 + 15) // 16
+        m = (kvl[b] + K1 + 15) // 16
         bt_local[b, :m] = remap[bt[b, :m]]
     h = host_rej
     t_attn = t_rej = 0.0
     passes = tokens = 0
     while passes == 0 or t_attn + t_rej < args.cpu_seconds:
         t0 = time.perf_counter()
-        oat.verify_attention(q, kc, vc, bt_local, kvl)
+        if parent is None:
+            oat.verify_attention(q, kc, vc, bt_local, kvl)
+        else:
+            otr.tree_attention(q, kc, vc, bt_local, kvl, otr.tree_masks(parent))
         t_attn += time.perf_counter() - t0
         t0 = time.perf_counter()
-        res = orj.reject_sample(h["target"][idx], h["draft"][idx], h["draft_tokens"][idx],
-                                h["uniforms"][idx], h["temperature"][idx])
+        if parent is None:
+            res = orj.reject_sample(h["target"][idx], h["draft"][idx], h["draft_tokens"][idx],
+                                    h["uniforms"][idx], h["temperature"][idx])
+        else:
+            res = otr.reject_sample_tree(h["target"][idx], h["draft"][idx], parent,
+                                         h["tokens"][idx], h["uniforms"][idx],
+                                         h["temperature"][idx])
         t_rej += time.perf_counter() - t0
         tokens += int(res["num_accepted"].astype(np.int64).sum()) + n
         passes += 1

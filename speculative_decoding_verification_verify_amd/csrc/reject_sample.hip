@@ -612,15 +612,22 @@ __device__ __forceinline__ int locate_draw(const T* __restrict__ trow, const T* 
                                            const SubSums* __restrict__ sg,
                                            const double* __restrict__ s_exp) {
   static_assert(kSub == kThreads, "one sub-chunk entry per thread");
+  constexpr int kSubStage = 512;                 // sub-chunk sums staged in LDS (16 KB)
   __shared__ ChunkSums s_cs[kThreads];
+  __shared__ SubSums s_ss[kSubStage];
   __shared__ double s_wtot[kThreads / 64];
   __shared__ int s_chunk, s_sub, s_fallback, s_mode, s_first, s_lastpos;
   __shared__ double s_base, s_target, s_isq, s_isp;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const double cd = kLog2eD / (double)t;
-  // Chunk sums staged in LDS when they fit (V <= 2^21), read in place otherwise.
+  // Chunk and sub-chunk sums staged in LDS together when they fit (V <= 2^17
+  // for both, V <= 2^21 for the chunk sums), read in place otherwise: the
+  // sub-chunk level then needs no second round trip to memory.
   const bool staged = ncr <= kThreads;
+  const bool sub_staged = ncr * kSubPerChunk <= kSubStage;
   if (staged && tid < ncr) s_cs[tid] = cg[tid];
+  if (sub_staged)
+    for (int k = tid; k < ncr * kSubPerChunk; k += kThreads) s_ss[k] = sg[k];
   __syncthreads();
   const ChunkSums* cs = staged ? s_cs : cg;
   if (wave == 0) {
@@ -649,7 +656,7 @@ __device__ __forceinline__ int locate_draw(const T* __restrict__ trow, const T* 
       ch = lastpos < 0 ? 0 : lastpos;
     }
     // Sub-chunk level, same wave (no crossing is looked for once in fallback).
-    const SubSums* ss = sg + (size_t)ch * kSubPerChunk;
+    const SubSums* ss = (sub_staged ? s_ss : sg) + (size_t)ch * kSubPerChunk;
     double base2 = base;
     int lastsub;
     int sc = wave_find(kSubPerChunk, [&](int j) { return sub_mass(ss[j], m, isq, isp); },
@@ -883,11 +890,12 @@ __device__ __forceinline__ void emit_tree(int b, int N, int n, int tok, int32_t*
 // itself.  Accepted nodes are written to the outputs; the walk stops at the
 // first rejection (a pass with coef = 1 follows) or at a leaf (the bonus
 // pass from q_v follows).  One thread; rs(r) gives the merged statistics
-// (raw max, sum) of swept row r.
+// (raw max, sum) of swept row r; xd, tok and uni are this sequence's recorded
+// logits [N][2], tokens [N] and uniforms [N], staged in LDS.
 template <class RS>
-__device__ void tree_walk(int b, int v, int n, const TreeShape& s, RS rs, const float* __restrict__ xd,
-                          const int32_t* __restrict__ tok, const float* __restrict__ uni, float c,
-                          double cd, int32_t* __restrict__ out_tok, int32_t* __restrict__ out_node,
+__device__ void tree_walk(int b, int v, int n, const TreeShape& s, RS rs, const float* xd,
+                          const int* tok, const float* uni, float c, double cd,
+                          int32_t* __restrict__ out_tok, int32_t* __restrict__ out_node,
                           Decision& dd, TreeState& st) {
   const int N = s.n;
   for (;;) {
@@ -900,8 +908,7 @@ __device__ void tree_walk(int b, int v, int n, const TreeShape& s, RS rs, const 
     }
     const float2 rp = rs(N + s.int_idx[v]);
     const int ch = s.kids[k0];
-    const size_t ci = (size_t)b * N + ch;
-    const float xq = xd[ci * 2], xp = xd[ci * 2 + 1];
+    const float xq = xd[ch * 2], xp = xd[ch * 2 + 1];
     bool acc;
     if (xp == -INFINITY) {
       acc = true;                                   // p(d) == 0
@@ -910,11 +917,11 @@ __device__ void tree_walk(int b, int v, int n, const TreeShape& s, RS rs, const 
       const double mq = (double)(rq.x * c), mp = (double)(rp.x * c);
       const double ly = ((double)xq * (double)c - mq) - ((double)xp * (double)c - mp);
       const double r = exp2(ly) * ((double)rp.y / (double)rq.y);
-      acc = (double)uni[ci] < fmin(1.0, r);
+      acc = (double)uni[ch] < fmin(1.0, r);
     }
     if (acc) {
       out_node[(size_t)b * N + n] = ch;
-      out_tok[(size_t)b * N + n] = tok[ci];
+      out_tok[(size_t)b * N + n] = tok[ch];
       ++n;
       v = ch;
       continue;
@@ -941,6 +948,8 @@ __global__ __launch_bounds__(kDecideThreads) void k_tree_decide(
     int32_t* __restrict__ nacc, int32_t* __restrict__ kv_len, unsigned long long* counters) {
   __shared__ float2 s_rs[2 * kMaxTree];
   __shared__ float2 s_part[kPartStage];
+  __shared__ float s_xd[2 * kMaxTree], s_u[kMaxTree];
+  __shared__ int s_tk[kMaxTree];
   __shared__ int s_n, s_tok;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -951,8 +960,13 @@ __global__ __launch_bounds__(kDecideThreads) void k_tree_decide(
   const float c = greedy ? 0.f : kLog2e / t;
   const float2* pb = part + (size_t)b * R * nc;
   const bool staged = rows * nc <= kPartStage;
+  // Every load at once: the row statistics, then this sequence's tokens,
+  // uniforms and recorded logits for the walk.
   if (staged)
     for (int k = tid; k < rows * nc; k += kDecideThreads) s_part[k] = pb[k];
+  if (tid < N) s_tk[tid] = tok[(size_t)b * N + tid];
+  if (!greedy && tid < N) s_u[tid] = uni[(size_t)b * N + tid];
+  if (!greedy && tid < 2 * N) s_xd[tid] = xd[(size_t)b * N * 2 + tid];
   __syncthreads();
   for (int r = wave; r < rows; r += kDecideThreads / 64) {
     float a, bb;
@@ -970,10 +984,10 @@ __global__ __launch_bounds__(kDecideThreads) void k_tree_decide(
         const int am = __float_as_int(s_rs[v].y);
         int nxt = -1;
         for (int k = s.kid_off[v]; k < s.kid_off[v + 1]; ++k)
-          if (clampi(tok[(size_t)b * N + s.kids[k]], 0, V - 1) == am) { nxt = s.kids[k]; break; }
+          if (clampi(s_tk[s.kids[k]], 0, V - 1) == am) { nxt = s.kids[k]; break; }
         if (nxt < 0) { fin = am; break; }
         out_node[(size_t)b * N + n] = nxt;
-        out_tok[(size_t)b * N + n] = tok[(size_t)b * N + nxt];
+        out_tok[(size_t)b * N + n] = s_tk[nxt];
         ++n;
         v = nxt;
       }
@@ -983,8 +997,8 @@ __global__ __launch_bounds__(kDecideThreads) void k_tree_decide(
     } else {
       Decision dd;
       TreeState st;
-      tree_walk(b, 0, 0, s, [&](int r) { return s_rs[r]; }, xd, tok, uni, c, kLog2eD / (double)t,
-                out_tok, out_node, dd, st);
+      tree_walk(b, 0, 0, s, [&](int r) { return s_rs[r]; }, s_xd, s_tk, s_u, c,
+                kLog2eD / (double)t, out_tok, out_node, dd, st);
       dec[b] = dd;
       state[b] = st;
     }
@@ -1011,13 +1025,24 @@ __global__ __launch_bounds__(kThreads) void k_tree_step(
     int32_t* __restrict__ out_node, int32_t* __restrict__ nacc, int32_t* __restrict__ kv_len,
     unsigned long long* counters) {
   __shared__ double s_exp[kExpTable];
+  __shared__ float2 s_rs[2 * kMaxTree];
+  __shared__ float s_xd[2 * kMaxTree], s_u[kMaxTree];
+  __shared__ int s_tk[kMaxTree];
   __shared__ int s_draw, s_n;
   const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = s.n, R = s.n + s.n_int;
+  // The walk's inputs, loaded together with the decision (one round trip).
+  if (tid < R) s_rs[tid] = rowstat[(size_t)b * R + tid];
+  if (tid < N) {
+    s_tk[tid] = tok[(size_t)b * N + tid];
+    s_u[tid] = uni[(size_t)b * N + tid];
+  }
+  if (tid < 2 * N) s_xd[tid] = xd[(size_t)b * N * 2 + tid];
   const Decision d = dec[b];
   if (d.mode == kModeNone) return;
   const TreeState st = state[b];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int N = s.n, R = s.n + s.n_int;
+  __syncthreads();
   const float t = temp_of(temp, b, force_greedy);
   const double cd = kLog2eD / (double)t;
   const ChunkSums* cg = csum + (size_t)b * ncr;
@@ -1041,8 +1066,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_step(
         int pos = st.pos;
         for (;;) {
           const int ch = s.kids[k0 + pos];
-          const size_t ci = (size_t)b * N + ch;
-          const float xq = xd[ci * 2], xp = xd[ci * 2 + 1];
+          const float xq = s_xd[ch * 2], xp = s_xd[ch * 2 + 1];
           bool acc;
           if (xp == -INFINITY) {
             acc = true;
@@ -1051,15 +1075,15 @@ __global__ __launch_bounds__(kThreads) void k_tree_step(
             const double lr = ((double)xq - (double)d.xmq) * cd - ((double)xp - (double)d.xmp) * cd;
             const double ratio = exp2(lr) * (sp / sq);
             const double r = fmax(0.0, ratio - coef) / zz;
-            acc = (double)uni[ci] < fmin(1.0, r);
+            acc = (double)s_u[ch] < fmin(1.0, r);
           }
           if (acc) {
             out_node[(size_t)b * N + n] = ch;
-            out_tok[(size_t)b * N + n] = tok[ci];
+            out_tok[(size_t)b * N + n] = s_tk[ch];
             Decision dd;
             TreeState ns;
-            tree_walk(b, ch, n + 1, s, [&](int r) { return rowstat[(size_t)b * R + r]; }, xd, tok, uni,
-                      kLog2e / t, cd, out_tok, out_node, dd, ns);
+            tree_walk(b, ch, n + 1, s, [&](int r) { return s_rs[r]; }, s_xd, s_tk, s_u, kLog2e / t,
+                      cd, out_tok, out_node, dd, ns);
             dec[b] = dd;
             state[b] = ns;
             draw = 0;
@@ -1094,7 +1118,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_step(
   __syncthreads();
   if (!s_draw) return;
   const int tk = locate_draw<T>(tgt + (size_t)d.trow * V, drf + (size_t)d.drow * V, d,
-                                (double)uni[(size_t)b * N], t, V, ncr, cg,
+                                (double)s_u[0], t, V, ncr, cg,
                                 csub + (size_t)b * ncr * kSubPerChunk, s_exp);
   emit_tree(b, N, s_n, tk, out_tok, out_node, nacc, kv_len, counters);
   if (tid == 0) dec[b].mode = kModeNone;
