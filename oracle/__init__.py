@@ -16,6 +16,10 @@ reject     -- the lossless rejection-sampling verifier (accept test,
               and the commit of the logical KV length.
 exact_law  -- the closed-form joint law of one verify call, used to pin the
               oracle by brute-force enumeration.
+tree       -- attention and the lossless verifier over a flattened draft
+              tree.
+kv         -- the window's K/V in the paged cache (append, commit) and the
+              host page pool.
 
 Sources (the pages the method is taken from):
   [AIE]  AI Engineering from Scratch, lesson "Speculative decoding and
@@ -36,4 +40,4 @@ Parity status: every function here is pinned by the CPU tests
 attention); none is "parity unpinned".
 """
 
-from . import attention, reject, exact_law  # noqa: F401
+from . import attention, reject, exact_law, tree, kv  # noqa: F401
