@@ -22,9 +22,11 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- *  - Every pointer argument is device memory owned by the caller.  The
- *    library allocates nothing, frees nothing and keeps no mutable global
- *    state; scratch memory is the caller's workspace.
+ *  - Every pointer argument of the compute calls is device memory owned by
+ *    the caller.  The library allocates no device memory, frees nothing and
+ *    keeps no mutable global state; scratch memory is the caller's
+ *    workspace.  The host page pool (spec_pages_*) is host state owned by
+ *    its handle.
  *  - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the
  *    default stream).  Argument errors are detected on the host and
  *    returned before anything is launched.  A failed launch returns
@@ -52,13 +54,18 @@ typedef enum {
   SV_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad enum       */
   SV_ERR_UNSUPPORTED = -2, /* a shape outside the supported set          */
   SV_ERR_WORKSPACE = -3,   /* workspace smaller than the *_workspace_bytes */
-  SV_ERR_HIP = -4          /* a HIP runtime call or launch failed         */
+  SV_ERR_HIP = -4,         /* a HIP runtime call or launch failed         */
+  SV_ERR_NO_PAGES = -5     /* the page pool has too few free pages        */
 } sv_status;
 
 typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 
 #define SV_BLOCK_SIZE 16 /* tokens per KV page */
 #define SV_MAX_K 16      /* largest draft length accepted */
+
+/* Window source of spec_verify_attn_window. */
+#define SV_WINDOW_READ 0   /* read the window K/V from k_new / v_new only */
+#define SV_WINDOW_APPEND 1 /* ... and store them into their cache slots */
 
 /*
  * spec_verify_attn -- window-causal GQA of the K+1 verify positions.
@@ -123,6 +130,38 @@ int spec_verify_attn_tree(const void* q, const void* k_cache, const void* v_cach
                           int max_blocks_per_seq, int max_kv_len, float scale,
                           int dtype, void* workspace, size_t workspace_bytes,
                           void* hip_stream);
+
+/*
+ * spec_verify_attn_window -- the same attention, with the window's K/V taken
+ * from the projection output instead of the cache (AI Engineering from
+ * Scratch, "Speculative decoding and EAGLE-3", "Rolling back the KV cache":
+ * verification extends the cache by the window, either written into a
+ * scratch buffer and committed on acceptance, or written in place and rolled
+ * back by the logical length; sglang_spec_decode README, the provisional KV
+ * layer).
+ *
+ * k_new, v_new: [B, N, Hkv, D] (dtype), row i = window position L0 + i (chain)
+ *   or tree node i; device memory, 16-byte aligned, read only.
+ * mode SV_WINDOW_READ: the window keys are read from k_new / v_new and the
+ *   cache is not written (the scratch-buffer variant: spec_kv_commit moves
+ *   the accepted rows into the cache afterwards).
+ * mode SV_WINDOW_APPEND: the same, and the kernel also stores row i into its
+ *   cache slot L0 + i (pages from block_table; the caller has reserved them),
+ *   so no separate write pass is needed.  Each element is stored once, by
+ *   the lane that holds it for the product; the cache is never read back.
+ * anc: NULL for a chain (N = K + 1), or [B, N] ancestor sets of a tree as for
+ *   spec_verify_attn_tree.  Everything else as spec_verify_attn with
+ *   K = N - 1 (same workspace).  out and the cache slots L0 .. L0 + N - 1 are
+ *   the only memory written.  N < 2, a bad mode, or NULL k_new / v_new with
+ *   B > 0 is SV_ERR_INVALID_ARG.
+ */
+int spec_verify_attn_window(const void* q, const void* k_new, const void* v_new,
+                            void* k_cache, void* v_cache, const int32_t* block_table,
+                            const int32_t* kv_len, const uint32_t* anc, void* out,
+                            int B, int N, int Hq, int Hkv, int D, int block_size,
+                            int num_blocks, int max_blocks_per_seq, int max_kv_len,
+                            float scale, int dtype, int mode, void* workspace,
+                            size_t workspace_bytes, void* hip_stream);
 
 /*
  * spec_reject_sample -- lossless verifier over the full vocabulary plus the
@@ -233,6 +272,65 @@ int spec_reject_sample_tree(const void* target_logits, const void* draft_logits,
                             void* hip_stream);
 
 size_t spec_reject_sample_tree_workspace_bytes(int B, int N, int V);
+
+/*
+ * spec_kv_commit -- after the verifier, the surviving window rows' K/V into
+ * their committed positions (AI Engineering from Scratch, "Speculative
+ * decoding and EAGLE-3", "Rolling back the KV cache": a scratch buffer
+ * committed on acceptance, or the cache written in place; thakicloud,
+ * "Grading every branch in one pass": the surviving tree path is kept).
+ *
+ * For sequence b, n = num_accepted[b] and L0 = kv_len[b] - n - 1 (kv_len as
+ * the verifier left it).  Surviving row j = 0..n is the root (j = 0), then
+ * the accepted nodes in path order: nodes[b][j - 1] for a tree (out_nodes of
+ * spec_reject_sample_tree), row j for a chain (nodes == NULL).  Row j goes
+ * to position L0 + j, read from k_src / v_src [B, N, Hkv, D] (scratch mode)
+ * or, with k_src == v_src == NULL, from its window slot L0 + row of the
+ * cache (in place: a tree's path is compacted; every source is read before
+ * any slot is written; a chain in place has nothing to move and launches
+ * nothing).  The emitted token's K/V are not committed here: the next
+ * verify call writes them as its root.  Sequences with num_accepted outside
+ * [0, N) are skipped.
+ *
+ * Layouts as spec_verify_attn; nodes [B, N] int32.  Sizes: 1 <= N <=
+ * SV_MAX_K + 1, D in {64, 128}, block_size == 16.  Only the cache slots
+ * L0 .. L0 + n are written.
+ */
+int spec_kv_commit(void* k_cache, void* v_cache, const int32_t* block_table,
+                   const int32_t* kv_len, const int32_t* num_accepted,
+                   const int32_t* nodes, const void* k_src, const void* v_src,
+                   int B, int N, int Hkv, int D, int block_size, int num_blocks,
+                   int max_blocks_per_seq, int dtype, void* hip_stream);
+
+/*
+ * spec_pages_* -- host-side KV page list with provisional window pages (AI
+ * Engineering from Scratch, "Rolling back the KV cache"; sglang_spec_decode
+ * README, the provisional KV layer).  Host memory only, no GPU calls.
+ *
+ * A sequence owns pages for positions [0, 16 * pages).  reserve(seq, len)
+ * grows that to cover positions [0, len) (call it with L0 + N before a
+ * verify; the new pages are provisional), taking the lowest-numbered free
+ * pages first; commit(seq, len) frees every page whose first position is at
+ * or past len (the pages only a rejected tail used, or an explicit rollback)
+ * and keeps the rest; release(seq) frees them all.  block_table() is the
+ * [max_seqs, max_blocks_per_seq] int32 host table the verify calls need
+ * (unused entries 0), valid until the next call on the pool.  check()
+ * verifies that every page is owned exactly once (by one sequence or the
+ * free list).  Errors: SV_ERR_INVALID_ARG (bad sequence or length, a length
+ * past max_blocks_per_seq pages, a commit past the reserved pages),
+ * SV_ERR_NO_PAGES (reserve needs more free pages than there are; nothing is
+ * taken).  Not thread-safe.
+ */
+typedef struct sv_page_pool sv_page_pool;
+sv_page_pool* spec_pages_create(int num_blocks, int max_seqs, int max_blocks_per_seq);
+void spec_pages_destroy(sv_page_pool* pool);
+int spec_pages_reserve(sv_page_pool* pool, int seq, int total_len);
+int spec_pages_commit(sv_page_pool* pool, int seq, int committed_len);
+int spec_pages_release(sv_page_pool* pool, int seq);
+int spec_pages_free_count(const sv_page_pool* pool);
+int spec_pages_seq_blocks(const sv_page_pool* pool, int seq);
+const int32_t* spec_pages_block_table(const sv_page_pool* pool);
+int spec_pages_check(const sv_page_pool* pool);
 
 /* Static description of a status code. */
 const char* spec_status_string(int status);

@@ -12,12 +12,18 @@ if the library is missing, :func:`load` raises.
         lossless verifier over the full vocabulary + KV-length commit
     verify_attn_tree(..., anc) / reject_sample_tree(..., parent, ...)
         the same two steps over a flattened draft tree
+    verify_attn_window(q, k_new, v_new, k_cache, v_cache, ..., mode)
+        attention with the window's K/V from the projection output, stored
+        into the cache in the same kernel (append) or not (scratch)
+    kv_commit(...), PagePool
+        the accepted rows into their committed positions; host page list
 """
 
 import ctypes
 import os
 
 __all__ = ["load", "lib_path", "exported_symbols", "verify_attn", "verify_attn_tree",
+           "verify_attn_window", "kv_commit", "PagePool", "SV_WINDOW_READ", "SV_WINDOW_APPEND",
            "reject_sample", "reject_sample_tree", "verify_attn_workspace_bytes",
            "reject_sample_workspace_bytes", "reject_sample_tree_workspace_bytes",
            "SpecVerifyError", "SV_F32", "SV_BF16", "STATUS", "EXPORTS"]
@@ -26,11 +32,16 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 SV_F32, SV_BF16 = 0, 1
+SV_WINDOW_READ, SV_WINDOW_APPEND = 0, 1
 STATUS = {0: "SV_OK", -1: "SV_ERR_INVALID_ARG", -2: "SV_ERR_UNSUPPORTED",
-          -3: "SV_ERR_WORKSPACE", -4: "SV_ERR_HIP"}
+          -3: "SV_ERR_WORKSPACE", -4: "SV_ERR_HIP", -5: "SV_ERR_NO_PAGES"}
 EXPORTS = ("spec_verify_attn", "spec_verify_attn_workspace_bytes", "spec_verify_attn_tree",
+           "spec_verify_attn_window", "spec_kv_commit",
            "spec_reject_sample", "spec_reject_sample_workspace_bytes",
            "spec_reject_sample_tree", "spec_reject_sample_tree_workspace_bytes",
+           "spec_pages_create", "spec_pages_destroy", "spec_pages_reserve", "spec_pages_commit",
+           "spec_pages_release", "spec_pages_free_count", "spec_pages_seq_blocks",
+           "spec_pages_block_table", "spec_pages_check",
            "spec_status_string", "spec_version")
 
 
@@ -73,6 +84,29 @@ def load():
     lib.spec_reject_sample_tree.restype = i32
     lib.spec_reject_sample_tree_workspace_bytes.argtypes = [i32, i32, i32]
     lib.spec_reject_sample_tree_workspace_bytes.restype = sz
+    lib.spec_verify_attn_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                            i32, i32, i32, i32, i32, f32, i32, i32, vp, sz, vp]
+    lib.spec_verify_attn_window.restype = i32
+    lib.spec_kv_commit.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                   i32, i32, vp]
+    lib.spec_kv_commit.restype = i32
+    lib.spec_pages_create.argtypes = [i32, i32, i32]
+    lib.spec_pages_create.restype = vp
+    lib.spec_pages_destroy.argtypes = [vp]
+    lib.spec_pages_destroy.restype = None
+    for fn in ("spec_pages_reserve", "spec_pages_commit"):
+        getattr(lib, fn).argtypes = [vp, i32, i32]
+        getattr(lib, fn).restype = i32
+    lib.spec_pages_release.argtypes = [vp, i32]
+    lib.spec_pages_release.restype = i32
+    lib.spec_pages_free_count.argtypes = [vp]
+    lib.spec_pages_free_count.restype = i32
+    lib.spec_pages_seq_blocks.argtypes = [vp, i32]
+    lib.spec_pages_seq_blocks.restype = i32
+    lib.spec_pages_block_table.argtypes = [vp]
+    lib.spec_pages_block_table.restype = ctypes.POINTER(ctypes.c_int32)
+    lib.spec_pages_check.argtypes = [vp]
+    lib.spec_pages_check.restype = i32
     lib.spec_status_string.argtypes = [i32]
     lib.spec_status_string.restype = ctypes.c_char_p
     lib.spec_version.argtypes = []
@@ -291,3 +325,119 @@ def reject_sample_tree(target, draft, parent, tokens, uniforms, temperature, kv_
                                      ws_have, _stream(stream))
     _check("spec_reject_sample_tree", st)
     return out_tokens, out_nodes, num_accepted
+
+
+def verify_attn_window(q, k_new, v_new, k_cache, v_cache, block_table, kv_len, anc=None,
+                       mode=SV_WINDOW_APPEND, out=None, max_kv_len=None, scale=0.0,
+                       workspace=None, stream=None):
+    """Verify attention with the window's K/V from k_new / v_new [B, N, Hkv, D]
+    (see ``spec_verify_attn_window``); mode SV_WINDOW_APPEND also stores them
+    into the cache, SV_WINDOW_READ leaves the cache as it is.  anc: None
+    (chain) or [B, N] int32 ancestor sets of a tree.  Returns out."""
+    import torch
+    lib = load()
+    _need(q, "q")
+    dt = _dtype_code(q)
+    for t, name in ((k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, name, q.dtype)
+    _need(block_table, "block_table", torch.int32)
+    _need(kv_len, "kv_len", torch.int32)
+    if anc is not None:
+        _need(anc, "anc", torch.int32)
+    B, N, Hq, D = q.shape
+    NB, Hkv = k_cache.shape[0], k_cache.shape[1]
+    if tuple(k_new.shape) != (B, N, Hkv, D) or tuple(v_new.shape) != (B, N, Hkv, D):
+        raise ValueError("k_new / v_new must be [B, N, Hkv, D]")
+    mbps = block_table.shape[1]
+    if max_kv_len is None:
+        max_kv_len = int(kv_len.max().item()) if B > 0 else 0
+    if out is None:
+        out = torch.empty_like(q)
+    ws_bytes = verify_attn_workspace_bytes(B, N - 1, Hq, Hkv, D, max_kv_len)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.spec_verify_attn_window(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                     _ptr(v_cache), _ptr(block_table), _ptr(kv_len), _ptr(anc),
+                                     _ptr(out), B, N, Hq, Hkv, D, 16, NB, mbps, int(max_kv_len),
+                                     float(scale), dt, int(mode), _ptr(workspace), ws_have,
+                                     _stream(stream))
+    _check("spec_verify_attn_window", st)
+    return out
+
+
+def kv_commit(k_cache, v_cache, block_table, kv_len, num_accepted, nodes=None, k_src=None,
+              v_src=None, N=None, stream=None):
+    """The surviving window rows into positions L0 .. L0 + n (see
+    ``spec_kv_commit``).  nodes: None (chain) or [B, N] int32 (a tree's
+    out_nodes); k_src / v_src: [B, N, Hkv, D] scratch rows, or None to move
+    them in place.  N defaults to nodes.shape[1] or k_src.shape[1]."""
+    import torch
+    lib = load()
+    _need(k_cache, "k_cache")
+    dt = _dtype_code(k_cache)
+    _need(v_cache, "v_cache", k_cache.dtype)
+    _need(block_table, "block_table", torch.int32)
+    _need(kv_len, "kv_len", torch.int32)
+    _need(num_accepted, "num_accepted", torch.int32)
+    if nodes is not None:
+        _need(nodes, "nodes", torch.int32)
+    if k_src is not None:
+        _need(k_src, "k_src", k_cache.dtype)
+        _need(v_src, "v_src", k_cache.dtype)
+    B = num_accepted.shape[0]
+    NB, Hkv = k_cache.shape[0], k_cache.shape[1]
+    D = v_cache.shape[2]
+    if N is None:
+        N = nodes.shape[1] if nodes is not None else (k_src.shape[1] if k_src is not None else 1)
+    st = lib.spec_kv_commit(_ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(kv_len),
+                            _ptr(num_accepted), _ptr(nodes), _ptr(k_src), _ptr(v_src), B, int(N),
+                            Hkv, D, 16, NB, block_table.shape[1], dt, _stream(stream))
+    _check("spec_kv_commit", st)
+
+
+class PagePool:
+    """Host page list with provisional window pages (see ``spec_pages_*``)."""
+
+    def __init__(self, num_blocks, max_seqs, max_blocks_per_seq):
+        self._lib = load()
+        self._h = self._lib.spec_pages_create(num_blocks, max_seqs, max_blocks_per_seq)
+        if not self._h:
+            raise SpecVerifyError("spec_pages_create", -1)
+        self.num_blocks, self.max_seqs, self.mbps = num_blocks, max_seqs, max_blocks_per_seq
+
+    def close(self):
+        if self._h:
+            self._lib.spec_pages_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def reserve(self, seq, total_len):
+        _check("spec_pages_reserve", self._lib.spec_pages_reserve(self._h, seq, total_len))
+
+    def commit(self, seq, length):
+        _check("spec_pages_commit", self._lib.spec_pages_commit(self._h, seq, length))
+
+    def release(self, seq):
+        _check("spec_pages_release", self._lib.spec_pages_release(self._h, seq))
+
+    def free_count(self):
+        return int(self._lib.spec_pages_free_count(self._h))
+
+    def seq_blocks(self, seq):
+        return int(self._lib.spec_pages_seq_blocks(self._h, seq))
+
+    def check(self):
+        return int(self._lib.spec_pages_check(self._h))
+
+    def block_table(self):
+        """A numpy copy of the [max_seqs, max_blocks_per_seq] int32 table."""
+        import numpy as np
+        ptr = self._lib.spec_pages_block_table(self._h)
+        n = self.max_seqs * self.mbps
+        return np.ctypeslib.as_array(ptr, shape=(n,)).copy().reshape(self.max_seqs, self.mbps)

@@ -8,6 +8,7 @@ extern "C" const char* spec_status_string(int status) {
     case SV_ERR_UNSUPPORTED: return "unsupported shape";
     case SV_ERR_WORKSPACE: return "workspace too small";
     case SV_ERR_HIP: return "HIP runtime error";
+    case SV_ERR_NO_PAGES: return "out of KV pages";
     default: return "unknown status";
   }
 }

@@ -127,6 +127,78 @@ __device__ __forceinline__ void mask_v_tail(bf16x8 (&vf)[2][D / 32], int pr, int
   }
 }
 
+// ---- Window taken from the projection output (k_new / v_new [B, K1, Hkv, D])
+// instead of the cache: the pair that holds window keys reads them there,
+// and in append mode stores them into their cache slots as well.  Each
+// window element is held by exactly one lane of the wave that processes its
+// pair, in the MFMA operand layout, so each is loaded once and stored once
+// and the cache is never read back.
+
+// True (wave-uniform) when pair pr of a sequence with committed length L0
+// holds window keys L0 .. L0 + K1 - 1.
+__device__ __forceinline__ bool pair_has_window(int pr, int L0, int K1) {
+  return pr * kPairKeys < L0 + K1 && pr * kPairKeys + kPairKeys > L0;
+}
+
+// K operand of a pair with window keys: a window key's 16-byte chunks come
+// from k_new (one address per lane: the chunk stride differs, 16 elements
+// there, 256 in the page).
+template <int D>
+__device__ __forceinline__ void load_k_window(bf16x8 (&kf)[D / 16], const int (&blk)[2],
+                                              const uint16_t* __restrict__ kc,
+                                              const uint16_t* __restrict__ kn, int b, int K1,
+                                              int Hkv, int g, int L0, int pr, int k_page, int k_tok,
+                                              int hh) {
+  const int i = pr * kPairKeys + k_page * 16 + k_tok - L0;
+  const bool win = (unsigned)i < (unsigned)K1;
+  const uint16_t* base =
+      win ? kn + (((size_t)b * K1 + i) * Hkv + g) * D + hh * 8
+          : kc + ((size_t)(k_page ? blk[1] : blk[0]) * Hkv + g) * ((size_t)D * 16) + (hh * 16 + k_tok) * 8;
+  const int step = win ? 16 : 256;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(base + kk * step);
+}
+
+// Append mode: this lane's window K chunks into their page slots.
+template <int D>
+__device__ __forceinline__ void store_k_window(const bf16x8 (&kf)[D / 16], const int (&blk)[2],
+                                               uint16_t* __restrict__ kc, int K1, int Hkv, int g,
+                                               int L0, int pr, int k_page, int k_tok, int hh) {
+  const int i = pr * kPairKeys + k_page * 16 + k_tok - L0;
+  if ((unsigned)i < (unsigned)K1) {
+    uint16_t* kpage = kc + ((size_t)(k_page ? blk[1] : blk[0]) * Hkv + g) * ((size_t)D * 16);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      *reinterpret_cast<bf16x8*>(kpage + ((2 * kk + hh) * 16 + k_tok) * 8) = kf[kk];
+  }
+}
+
+// V operand of a pair with window keys: the window tokens' entries replaced
+// by v_new (strided there, so element loads; one pair per segment), and in
+// append mode stored into the page.
+template <int D>
+__device__ __forceinline__ void window_v(bf16x8 (&vf)[2][D / 32], const int (&blk)[2],
+                                         uint16_t* __restrict__ vc, const uint16_t* __restrict__ vn,
+                                         bool store, int b, int K1, int Hkv, int g, int L0, int pr,
+                                         int l32, int hh) {
+#pragma unroll
+  for (int sg = 0; sg < 2; ++sg)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = pr * kPairKeys + sg * 16 + 8 * hh + e - L0;
+      if ((unsigned)i < (unsigned)K1) {
+        const uint16_t* src = vn + (((size_t)b * K1 + i) * Hkv + g) * D + l32;
+        uint16_t* dst = vc + ((size_t)blk[sg] * Hkv + g) * ((size_t)D * 16) + l32 * 16 + 8 * hh + e;
+#pragma unroll
+        for (int j = 0; j < D / 32; ++j) {
+          const uint16_t x = src[32 * j];
+          vf[sg][j][e] = __builtin_bit_cast(__bf16, x);
+          if (store) dst[32 * j * 16] = x;
+        }
+      }
+    }
+}
+
 // Scores of one page pair for tile nt, window-causal mask, online-softmax
 // update of (m, l, O) and the bf16 probabilities for the P.V product.
 template <int D, int NT>
@@ -338,13 +410,14 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[NT][D / 16], uint32_t (&am)[
 // base-2 units.  Slot 0: the segment that starts the workgroup's share;
 // slot 1: a segment that starts later and runs past its end.
 // ---------------------------------------------------------------------------
-template <int D, int NT>
+template <int D, int NT, bool WIN>
 __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T * 4 / stream_waves<NT>() : 1) void k_attn_stream(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ kv_len,
     const uint32_t* __restrict__ anc, uint16_t* __restrict__ out,
     int B, int K1, int Hq, int Hkv, int num_blocks, int mbps, int np_cap, float sl2, int W,
-    float* __restrict__ opart, float2* __restrict__ ml) {
+    float* __restrict__ opart, float2* __restrict__ ml, const uint16_t* __restrict__ kn,
+    const uint16_t* __restrict__ vn, int store_win) {
   constexpr int KK = D / 16;         // MFMA k-steps for S
   constexpr int DT = D / 32;         // d tiles for O
   constexpr int ROWS = 32 * NT;
@@ -439,7 +512,10 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
   if (pr < cur.p_hi) {
     int blk[2];
     pair_blocks(blk, pr, bt + (size_t)cur.b * mbps, mbps, num_blocks);
-    load_k<D>(kf, blk, kc, Hkv, cur.g, k_page, k_tok, hh);
+    if (WIN && pair_has_window(pr, cur.L0, K1))
+      load_k_window<D>(kf, blk, kc, kn, cur.b, K1, Hkv, cur.g, cur.L0, pr, k_page, k_tok, hh);
+    else
+      load_k<D>(kf, blk, kc, Hkv, cur.g, k_page, k_tok, hh);
     load_v<D>(vf, blk, vc, Hkv, cur.g, l32, hh);
   }
   bf16x8 qf[NT][KK];
@@ -484,7 +560,21 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         score_pair<D, NT>(kf, pr, hh, nt, qf, am, cur.L0, sl2, o, m_run, l_run, pf[nt]);
-      if (in_seg || cross) load_k<D>(kf, nblk, kc, Hkv, ng, k_page, k_tok, hh);
+      const bool win_here = WIN && pair_has_window(pr, cur.L0, K1);
+      int cblk[2] = {0, 0};                        // pages of this pair (window pairs only)
+      if (WIN && win_here) pair_blocks(cblk, pr, btb, mbps, num_blocks);
+      if (WIN && win_here && store_win)
+        store_k_window<D>(kf, cblk, kc, K1, Hkv, cur.g, cur.L0, pr, k_page, k_tok, hh);
+      if (in_seg || cross) {
+        const int npr = cross ? nxt_first : nx;
+        const int nb_ = cross ? nxt.b : cur.b, nl0 = cross ? nxt.L0 : cur.L0;
+        if (WIN && pair_has_window(npr, nl0, K1))
+          load_k_window<D>(kf, nblk, kc, kn, nb_, K1, Hkv, ng, nl0, npr, k_page, k_tok, hh);
+        else
+          load_k<D>(kf, nblk, kc, Hkv, ng, k_page, k_tok, hh);
+      }
+      if (WIN && win_here)
+        window_v<D>(vf, cblk, vc, vn, store_win != 0, cur.b, K1, Hkv, cur.g, cur.L0, pr, l32, hh);
       mask_v_tail<D>(vf, pr, L, hh);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) pv_pair<D, NT>(vf, nt, pf[nt], o);
@@ -495,7 +585,10 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
     if (nxt_mine && !prefetched) {                 // no pair of mine in cur
       int nblk[2];
       pair_blocks(nblk, nxt_first, bt + (size_t)nxt.b * mbps, mbps, num_blocks);
-      load_k<D>(kf, nblk, kc, Hkv, nxt.g, k_page, k_tok, hh);
+      if (WIN && pair_has_window(nxt_first, nxt.L0, K1))
+        load_k_window<D>(kf, nblk, kc, kn, nxt.b, K1, Hkv, nxt.g, nxt.L0, nxt_first, k_page, k_tok, hh);
+      else
+        load_k<D>(kf, nblk, kc, Hkv, nxt.g, k_page, k_tok, hh);
       load_v<D>(vf, nblk, vc, Hkv, nxt.g, l32, hh);
     }
 
@@ -646,13 +739,17 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_stream_combine(
 
 // ---------------------------------------------------------------------------
 // fp32 VALU kernel: grid (K1, Hq, B), block 64 (one wave per query row).
-// k_cache [NB, Hkv, D/4, 16, 4], v_cache [NB, Hkv, D, 16].
+// k_cache [NB, Hkv, D/4, 16, 4], v_cache [NB, Hkv, D, 16].  With kn / vn the
+// window keys are read from there (never from the cache), and with store_win
+// the block of row 0 of each KV head's first query head also writes them
+// into the cache.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_attn_valu(
-    const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
+    const float* __restrict__ q, float* __restrict__ kc, float* __restrict__ vc,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ kv_len,
     const uint32_t* __restrict__ anc, float* __restrict__ out,
-    int K1, int Hq, int Hkv, int D, int num_blocks, int mbps, float sl2) {
+    int K1, int Hq, int Hkv, int D, int num_blocks, int mbps, float sl2,
+    const float* __restrict__ kn, const float* __restrict__ vn, int store_win) {
   __shared__ float s_q[256];
   __shared__ float s_p[64];
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -666,6 +763,16 @@ __global__ __launch_bounds__(64) void k_attn_valu(
   __syncthreads();
   const int32_t* btb = bt + (size_t)b * mbps;
   const size_t page = (size_t)D * 16;
+  if (kn && store_win && i == 0 && h % (Hq / Hkv) == 0) {
+    for (int e = lane; e < K1 * D; e += 64) {
+      const int ii = e / D, d = e - ii * D;
+      const int p = L0 + ii;
+      const int blk = clampi(btb[min(p >> 4, mbps - 1)], 0, num_blocks - 1);
+      const size_t src = (((size_t)b * K1 + ii) * Hkv + g) * D + d;
+      kc[((size_t)blk * Hkv + g) * page + ((d >> 2) * 16 + (p & 15)) * 4 + (d & 3)] = kn[src];
+      vc[((size_t)blk * Hkv + g) * page + d * 16 + (p & 15)] = vn[src];
+    }
+  }
   float m_run = -INFINITY, l_run = 0.f;
   float o[4] = {0.f, 0.f, 0.f, 0.f};              // d = lane + 64 * c
   for (int j0 = 0; j0 <= t; j0 += 64) {
@@ -673,11 +780,16 @@ __global__ __launch_bounds__(64) void k_attn_valu(
     float sc = -INFINITY;
     const unsigned jw = (unsigned)(j - L0);
     if (j <= t && (jw >= 32u || ((am >> jw) & 1u))) {
-      const int blk = clampi(btb[min(j >> 4, mbps - 1)], 0, num_blocks - 1);
-      const float* kp = kc + ((size_t)blk * Hkv + g) * page;
-      const int tok = j & 15;
       float acc = 0.f;
-      for (int d = 0; d < D; ++d) acc += s_q[d] * kp[((d >> 2) * 16 + tok) * 4 + (d & 3)];
+      if (kn && j >= L0) {
+        const float* kp = kn + (((size_t)b * K1 + (j - L0)) * Hkv + g) * D;
+        for (int d = 0; d < D; ++d) acc += s_q[d] * kp[d];
+      } else {
+        const int blk = clampi(btb[min(j >> 4, mbps - 1)], 0, num_blocks - 1);
+        const float* kp = kc + ((size_t)blk * Hkv + g) * page;
+        const int tok = j & 15;
+        for (int d = 0; d < D; ++d) acc += s_q[d] * kp[((d >> 2) * 16 + tok) * 4 + (d & 3)];
+      }
       sc = acc * sl2;
     }
     float mx = sc;
@@ -695,12 +807,20 @@ __global__ __launch_bounds__(64) void k_attn_valu(
     const int nk = min(64, t + 1 - j0);
     for (int jj = 0; jj < nk; ++jj) {
       const int jk = j0 + jj;
-      const int blk = clampi(btb[min(jk >> 4, mbps - 1)], 0, num_blocks - 1);
-      const float* vp = vc + ((size_t)blk * Hkv + g) * page;
       const float pj = s_p[jj];
-      for (int c = 0; c < 4; ++c) {
-        const int d = lane + 64 * c;
-        if (d < D) o[c] += pj * vp[d * 16 + (jk & 15)];
+      if (kn && jk >= L0) {
+        const float* vp = vn + (((size_t)b * K1 + (jk - L0)) * Hkv + g) * D;
+        for (int c = 0; c < 4; ++c) {
+          const int d = lane + 64 * c;
+          if (d < D) o[c] += pj * vp[d];
+        }
+      } else {
+        const int blk = clampi(btb[min(jk >> 4, mbps - 1)], 0, num_blocks - 1);
+        const float* vp = vc + ((size_t)blk * Hkv + g) * page;
+        for (int c = 0; c < 4; ++c) {
+          const int d = lane + 64 * c;
+          if (d < D) o[c] += pj * vp[d * 16 + (jk & 15)];
+        }
       }
     }
     __syncthreads();
@@ -740,37 +860,56 @@ static inline AttnPlan attn_plan(int B, int K, int Hq, int Hkv, int D, int max_k
 
 // Workgroups of k_attn_stream<D, NT> that are resident on one CU at once
 // (queried once per process; every caller stores the same value).
-template <int D, int NT>
+template <int D, int NT, bool WIN>
 static int stream_blocks_per_cu() {
   static std::atomic<int> cached{0};
   int nb = cached.load(std::memory_order_relaxed);
   if (nb > 0) return nb;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(&k_attn_stream<D, NT>),
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(&k_attn_stream<D, NT, WIN>),
                                                    64 * stream_waves<NT>(), 0) != hipSuccess || nb <= 0)
     nb = 1;
   cached.store(nb, std::memory_order_relaxed);
   return nb;
 }
 
-template <int D, int NT>
-static hipError_t launch_stream(const void* q, const void* kc, const void* vc, const int32_t* bt,
-                                const int32_t* kv_len, const uint32_t* anc, void* out, int B, int K1,
-                                int Hq, int Hkv,
-                                int num_blocks, int mbps, float sl2, const AttnPlan& p, char* ws,
-                                hipStream_t st) {
+// Window source: kn / vn == nullptr means the window is already in the cache.
+struct WindowArgs {
+  const void* kn;
+  const void* vn;
+  int store;
+};
+
+template <int D, int NT, bool WIN>
+static hipError_t launch_stream_t(const void* q, void* kc, void* vc, const int32_t* bt,
+                                  const int32_t* kv_len, const uint32_t* anc, void* out, int B, int K1,
+                                  int Hq, int Hkv, int num_blocks, int mbps, float sl2,
+                                  const AttnPlan& p, char* ws, const WindowArgs& win, hipStream_t st) {
   // Persistent grid: every workgroup resident from the start.
   const int W = (int)std::min<long long>(
-      p.w_max, (long long)stream_blocks_per_cu<D, NT>() * std::max(1, device_cus()));
+      p.w_max, (long long)stream_blocks_per_cu<D, NT, WIN>() * std::max(1, device_cus()));
   float* opart = reinterpret_cast<float*>(ws);
   float2* ml = reinterpret_cast<float2*>(ws + p.opart_bytes);
-  hipLaunchKernelGGL((k_attn_stream<D, NT>), dim3(W), dim3(64 * stream_waves<NT>()), 0, st,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
-                     static_cast<const uint16_t*>(vc), bt, kv_len, anc, static_cast<uint16_t*>(out), B,
-                     K1, Hq, Hkv, num_blocks, mbps, p.np_cap, sl2, W, opart, ml);
+  hipLaunchKernelGGL((k_attn_stream<D, NT, WIN>), dim3(W), dim3(64 * stream_waves<NT>()), 0, st,
+                     static_cast<const uint16_t*>(q), static_cast<uint16_t*>(kc),
+                     static_cast<uint16_t*>(vc), bt, kv_len, anc, static_cast<uint16_t*>(out), B,
+                     K1, Hq, Hkv, num_blocks, mbps, p.np_cap, sl2, W, opart, ml,
+                     static_cast<const uint16_t*>(win.kn), static_cast<const uint16_t*>(win.vn),
+                     win.store);
   if (W > 1)
     hipLaunchKernelGGL((k_attn_stream_combine<D, NT>), dim3(Hkv, B), dim3(kCombineThreads), 0, st, opart,
                        ml, kv_len, static_cast<uint16_t*>(out), B, K1, Hq, Hkv, p.np_cap, W);
   return hipGetLastError();
+}
+
+template <int D, int NT>
+static hipError_t launch_stream(const void* q, void* kc, void* vc, const int32_t* bt,
+                                const int32_t* kv_len, const uint32_t* anc, void* out, int B, int K1,
+                                int Hq, int Hkv, int num_blocks, int mbps, float sl2,
+                                const AttnPlan& p, char* ws, const WindowArgs& win, hipStream_t st) {
+  return win.kn ? launch_stream_t<D, NT, true>(q, kc, vc, bt, kv_len, anc, out, B, K1, Hq, Hkv,
+                                               num_blocks, mbps, sl2, p, ws, win, st)
+                : launch_stream_t<D, NT, false>(q, kc, vc, bt, kv_len, anc, out, B, K1, Hq, Hkv,
+                                                num_blocks, mbps, sl2, p, ws, win, st);
 }
 
 }  // namespace sv
@@ -784,11 +923,12 @@ extern "C" size_t spec_verify_attn_workspace_bytes(int B, int K, int Hq, int Hkv
 
 namespace sv {
 
-static int verify_attn_impl(const void* q, const void* k_cache, const void* v_cache,
+static int verify_attn_impl(const void* q, void* k_cache, void* v_cache,
                             const int32_t* block_table, const int32_t* kv_len, const uint32_t* anc,
                             void* out, int B, int K, int Hq, int Hkv, int D, int block_size,
                             int num_blocks, int max_blocks_per_seq, int max_kv_len, float scale,
-                            int dtype, void* workspace, size_t workspace_bytes, void* hip_stream) {
+                            int dtype, void* workspace, size_t workspace_bytes, void* hip_stream,
+                            const WindowArgs& win = WindowArgs{nullptr, nullptr, 0}) {
   if (B < 0 || K < 1 || Hq < 1 || Hkv < 1 || D < 1 || max_kv_len < 0 || num_blocks < 1 ||
       max_blocks_per_seq < 1)
     return SV_ERR_INVALID_ARG;
@@ -800,6 +940,7 @@ static int verify_attn_impl(const void* q, const void* k_cache, const void* v_ca
     return SV_ERR_INVALID_ARG;
   if (B == 0) return SV_OK;
   if (!q || !k_cache || !v_cache || !block_table || !kv_len || !out) return SV_ERR_INVALID_ARG;
+  if ((win.kn == nullptr) != (win.vn == nullptr)) return SV_ERR_INVALID_ARG;
   if (B > 65535 || Hkv > 65535) return SV_ERR_UNSUPPORTED;
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)D);
   const float sl2 = sc * kLog2e;
@@ -808,9 +949,10 @@ static int verify_attn_impl(const void* q, const void* k_cache, const void* v_ca
   hipError_t e;
   if (dtype == SV_F32) {
     hipLaunchKernelGGL(k_attn_valu, dim3(K1, Hq, B), dim3(64), 0, st,
-                       static_cast<const float*>(q), static_cast<const float*>(k_cache),
-                       static_cast<const float*>(v_cache), block_table, kv_len, anc,
-                       static_cast<float*>(out), K1, Hq, Hkv, D, num_blocks, max_blocks_per_seq, sl2);
+                       static_cast<const float*>(q), static_cast<float*>(k_cache),
+                       static_cast<float*>(v_cache), block_table, kv_len, anc,
+                       static_cast<float*>(out), K1, Hq, Hkv, D, num_blocks, max_blocks_per_seq, sl2,
+                       static_cast<const float*>(win.kn), static_cast<const float*>(win.vn), win.store);
     e = hipGetLastError();
   } else {
     const AttnPlan p = attn_plan(B, K, Hq, Hkv, D, max_kv_len);
@@ -821,19 +963,20 @@ static int verify_attn_impl(const void* q, const void* k_cache, const void* v_ca
       if (reinterpret_cast<uintptr_t>(workspace) & 255) return SV_ERR_INVALID_ARG;
     }
     const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
-                         reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(out);
+                         reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(out) |
+                         reinterpret_cast<uintptr_t>(win.kn) | reinterpret_cast<uintptr_t>(win.vn);
     if (al & 15) return SV_ERR_INVALID_ARG;
     char* ws = static_cast<char*>(workspace);
     if (D == 128) {
       e = p.tiles == 1 ? launch_stream<128, 1>(q, k_cache, v_cache, block_table, kv_len, anc, out, B,
-                                               K1, Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, st)
+                                               K1, Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, win, st)
                        : launch_stream<128, 2>(q, k_cache, v_cache, block_table, kv_len, anc, out, B,
-                                               K1, Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, st);
+                                               K1, Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, win, st);
     } else {
       e = p.tiles == 1 ? launch_stream<64, 1>(q, k_cache, v_cache, block_table, kv_len, anc, out, B,
-                                              K1, Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, st)
+                                              K1, Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, win, st)
                        : launch_stream<64, 2>(q, k_cache, v_cache, block_table, kv_len, anc, out, B,
-                                              K1, Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, st);
+                                              K1, Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, win, st);
     }
   }
   return e == hipSuccess ? SV_OK : SV_ERR_HIP;
@@ -846,7 +989,8 @@ extern "C" int spec_verify_attn(const void* q, const void* k_cache, const void* 
                                 int K, int Hq, int Hkv, int D, int block_size, int num_blocks,
                                 int max_blocks_per_seq, int max_kv_len, float scale, int dtype,
                                 void* workspace, size_t workspace_bytes, void* hip_stream) {
-  return sv::verify_attn_impl(q, k_cache, v_cache, block_table, kv_len, nullptr, out, B, K, Hq, Hkv,
+  return sv::verify_attn_impl(q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), block_table,
+                              kv_len, nullptr, out, B, K, Hq, Hkv,
                               D, block_size, num_blocks, max_blocks_per_seq, max_kv_len, scale, dtype,
                               workspace, workspace_bytes, hip_stream);
 }
@@ -859,7 +1003,24 @@ extern "C" int spec_verify_attn_tree(const void* q, const void* k_cache, const v
                                      size_t workspace_bytes, void* hip_stream) {
   if (B > 0 && !anc) return SV_ERR_INVALID_ARG;
   if (N < 2) return SV_ERR_INVALID_ARG;
-  return sv::verify_attn_impl(q, k_cache, v_cache, block_table, kv_len, anc, out, B, N - 1, Hq, Hkv,
+  return sv::verify_attn_impl(q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), block_table,
+                              kv_len, anc, out, B, N - 1, Hq, Hkv,
                               D, block_size, num_blocks, max_blocks_per_seq, max_kv_len, scale, dtype,
                               workspace, workspace_bytes, hip_stream);
+}
+
+extern "C" int spec_verify_attn_window(const void* q, const void* k_new, const void* v_new,
+                                       void* k_cache, void* v_cache, const int32_t* block_table,
+                                       const int32_t* kv_len, const uint32_t* anc, void* out, int B,
+                                       int N, int Hq, int Hkv, int D, int block_size, int num_blocks,
+                                       int max_blocks_per_seq, int max_kv_len, float scale, int dtype,
+                                       int mode, void* workspace, size_t workspace_bytes,
+                                       void* hip_stream) {
+  if (N < 2) return SV_ERR_INVALID_ARG;
+  if (mode != SV_WINDOW_READ && mode != SV_WINDOW_APPEND) return SV_ERR_INVALID_ARG;
+  if (B > 0 && (!k_new || !v_new)) return SV_ERR_INVALID_ARG;
+  return sv::verify_attn_impl(q, k_cache, v_cache, block_table, kv_len, anc, out, B, N - 1, Hq, Hkv, D,
+                              block_size, num_blocks, max_blocks_per_seq, max_kv_len, scale, dtype,
+                              workspace, workspace_bytes, hip_stream,
+                              sv::WindowArgs{k_new, v_new, mode == SV_WINDOW_APPEND ? 1 : 0});
 }

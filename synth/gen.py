@@ -12,7 +12,8 @@ Every generator takes a ``numpy.random.Generator``; callers derive those from
 import numpy as np
 
 __all__ = ["bf16_bits", "bf16_to_f32", "uniforms24", "make_reject_inputs",
-           "make_tree_reject_inputs", "make_attn_inputs", "kv_layout_x", "BLOCK"]
+           "make_tree_reject_inputs", "make_attn_inputs", "make_window_kv", "kv_layout_x",
+           "BLOCK"]
 
 BLOCK = 16  # tokens per KV page
 
@@ -167,6 +168,15 @@ def make_tree_reject_inputs(seed, B, parent, V, dtype="bf16", logit_std=2.0,
     u = uniforms24(r_u, (B, n))
     return {"target": tgt_e, "draft": drf_e, "tokens": toks, "parent": par.astype(np.int32),
             "uniforms": u, "temperature": temps}
+
+
+def make_window_kv(seed, B, N, Hkv, D, dtype="bf16"):
+    """The window's K/V as the projection produces them: k_new, v_new
+    [B, N, Hkv, D], N(0, 1), bf16 bits or float32."""
+    r_k, r_v = [np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(2)]
+    kn = r_k.standard_normal((B, N, Hkv, D), dtype=np.float32)
+    vn = r_v.standard_normal((B, N, Hkv, D), dtype=np.float32)
+    return _encode(kn, dtype), _encode(vn, dtype)
 
 
 def kv_layout_x(dtype):

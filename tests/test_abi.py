@@ -26,7 +26,7 @@ def lib():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:int|size_t|const char\*)\s+(spec_\w+)\(", text, re.M)))
+    return sorted(set(re.findall(r"^[A-Za-z_][\w ]*[\s*]+(spec_\w+)\(", text, re.M)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -153,3 +153,39 @@ def test_tree_reject_workspace_matches_chain(lib):
     assert sv.reject_sample_tree_workspace_bytes(0, 4, 100) == 0
     assert sv.reject_sample_tree_workspace_bytes(4, 0, 100) == 0
     assert sv.reject_sample_tree_workspace_bytes(4, 18, 100) == 0
+
+
+def _win(lib, B=2, N=8, mode=1, kn=True, D=128, dtype=1, ws=1 << 30):
+    p = FAKE
+    k = p if kn else None
+    return lib.spec_verify_attn_window(p, k, k, p, p, p, p, None, p, B, N, 32, 8, D, 16, 10, 600,
+                                       8192, ctypes.c_float(0.0), dtype, mode, p, ws, None)
+
+
+def test_window_attn_validation(lib):
+    assert _win(lib, N=1) == -1                          # a window needs the root and a draft
+    assert _win(lib, mode=2) == -1
+    assert _win(lib, kn=False) == -1
+    assert _win(lib, D=96) == -2                         # then the shared checks
+    assert _win(lib, N=18) == -2
+    assert _win(lib, ws=10) == -3
+    assert _win(lib, B=0, kn=False) == 0                 # empty batch: no-op
+
+
+def _commit(lib, B=2, N=8, nodes=True, src=0, D=128, dtype=1):
+    p = FAKE
+    s = p if src else None
+    return lib.spec_kv_commit(p, p, p, p, p, p if nodes else None, s, p if src == 2 else s, B, N, 8,
+                              D, 16, 10, 600, dtype, None)
+
+
+def test_kv_commit_validation(lib):
+    assert _commit(lib, B=-1) == -1
+    assert _commit(lib, N=0) == -1
+    assert _commit(lib, dtype=4) == -1
+    assert lib.spec_kv_commit(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 2, 8, 8, 128, 16, 10,
+                              600, 1, None) == -1          # only one of k_src / v_src
+    assert _commit(lib, N=18) == -2
+    assert _commit(lib, D=80) == -2
+    assert _commit(lib, B=0) == 0
+    assert _commit(lib, nodes=False, src=0) == 0          # chain in place: nothing to move
