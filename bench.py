@@ -79,6 +79,11 @@ def parse():
                    help="instead of the bench: copy MIB MiB device to device 8 times (the "
                         "known-size kernel that scales the HBM byte counters), then exit")
     p.add_argument("--sets", type=int, default=3, help="rotating logit sets")
+    p.add_argument("--window", default="none", choices=["none", "append", "scratch", "separate"],
+                   help="where the window's K/V come from: already in the cache (none); from "
+                        "the projection output, stored into the cache by the attention kernel "
+                        "(append) or committed afterwards by spec_kv_commit (scratch); or a "
+                        "separate copy pass before the plain attention (separate)")
     p.add_argument("--tree", default="", metavar="SHAPE",
                    help="verify a draft tree instead of a chain: branching factors per level, "
                         "e.g. 2,2,2 (15 nodes); times spec_verify_attn_tree + "
@@ -136,6 +141,10 @@ def main():
                                               temperature=args.temp)
         rsets.append({"host": inp, "dev": {k: to_device(v, dev) for k, v in inp.items()
                                            if k != "parent"}})
+    kn = vn = None
+    if args.window != "none":
+        kn_h, vn_h = gen.make_window_kv(args.seed + 99, B, K1, cfg.Hkv, cfg.D)
+        kn, vn = to_device(kn_h, dev), to_device(vn_h, dev)
     anc = None
     if parent is not None:
         anc = to_device(np.broadcast_to(tree_masks(parent).astype(np.uint32),
@@ -155,7 +164,21 @@ def main():
     torch.cuda.synchronize()
     print("bench: inputs resident", file=sys.stderr, flush=True)
 
+    all_acc = torch.full((B,), K, dtype=torch.int32, device=dev)
+    kv_full = kv0 + K1                                   # lengths as if every row survived
+
     def attn_call():
+        if args.window in ("append", "scratch"):
+            sv.verify_attn_window(attn["q"], kn, vn, attn["k_cache"], attn["v_cache"],
+                                  attn["block_table"], kv0, anc=anc,
+                                  mode=sv.SV_WINDOW_APPEND if args.window == "append"
+                                  else sv.SV_WINDOW_READ,
+                                  out=attn_out, max_kv_len=max_kv, workspace=attn_ws)
+            return
+        if args.window == "separate":
+            # The window copied into its slots by its own pass (every row kept).
+            sv.kv_commit(attn["k_cache"], attn["v_cache"], attn["block_table"], kv_full, all_acc,
+                         k_src=kn, v_src=vn, N=K1)
         if parent is None:
             sv.verify_attn(attn["q"], attn["k_cache"], attn["v_cache"], attn["block_table"], kv0,
                            out=attn_out, max_kv_len=max_kv, workspace=attn_ws)
@@ -175,9 +198,20 @@ def main():
                                   out_nodes=out_node[s % args.sets],
                                   num_accepted=n_acc[s % args.sets], workspace=rej_ws)
 
+    def commit_call(s, kv):
+        # Scratch window: the surviving rows into the cache; a tree appended in
+        # place: its path compacted.  A chain appended in place has nothing to move.
+        if args.window == "scratch" or (args.window == "append" and parent is not None):
+            sv.kv_commit(attn["k_cache"], attn["v_cache"], attn["block_table"], kv,
+                         n_acc[s % args.sets],
+                         nodes=out_node[s % args.sets] if parent is not None else None,
+                         k_src=kn if args.window == "scratch" else None,
+                         v_src=vn if args.window == "scratch" else None, N=K1)
+
     def step(s):
         attn_call()
         reject_call(s, kv_bufs[s])
+        commit_call(s, kv_bufs[s])
 
     for s in range(args.warmup):
         step(s)
@@ -220,19 +254,27 @@ def main():
     attn_ms = timed(lambda s: attn_call())
     kv_scratch = kv0.clone()
     rej_ms = timed(lambda s: reject_call(s, kv_scratch))
+    commits = args.window == "scratch" or (args.window == "append" and parent is not None)
+    commit_ms = (timed(lambda s: commit_call(n_total - 1, kv_bufs[n_total - 1]))
+                 if commits else None)
 
     # ---- roofline of the attention call (dominant kernel) ----------------
     kvl = from_device(kv0).astype(np.int64)
     kv_bytes = int((kvl + K1).sum()) * cfg.Hkv * cfg.D * 2 * 2
     qo_bytes = B * K1 * cfg.Hq * cfg.D * 2 * 2
-    attn_bytes = kv_bytes + qo_bytes
+    # The window's K/V are read once whatever their source; append also
+    # writes them into the cache.
+    win_write = B * K1 * cfg.Hkv * cfg.D * 2 * 2 if args.window == "append" else 0
+    attn_bytes = kv_bytes + qo_bytes + win_write
     attn_us = float(attn_ms * 1e3)
     achieved = attn_bytes / (attn_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": _traffic() if parent is None else None,
+                "traffic": _traffic() if parent is None and args.window == "none" else None,
                 "kernel": "%s call = k_attn_stream + k_attn_stream_combine" %
-                          ("spec_verify_attn" if parent is None else "spec_verify_attn_tree"),
+                          ("spec_verify_attn_window (%s)" % args.window
+                           if args.window in ("append", "scratch") else
+                           "spec_verify_attn" if parent is None else "spec_verify_attn_tree"),
                 "algorithmic_bytes": attn_bytes, "avg_us": round(attn_us, 2)}
     # The sweep reads every target row and the draft rows of the nodes with
     # children (all K draft rows of a chain); greedy reads target rows only.
@@ -266,7 +308,8 @@ def main():
                                 ("draft tree [%s] (%d nodes)" % (args.tree, K1)),
                                 V, cfg.Hq, cfg.Hkv, cfg.D, cfg.ctx[0], cfg.ctx[1],
                                 cfg.draft_sigma, args.temp),
-                   "global_batch": B, "K": K, "V": V, "parallelism": "single GPU"},
+                   "global_batch": B, "K": K, "V": V, "parallelism": "single GPU",
+                   "window": args.window},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": {
@@ -274,6 +317,7 @@ def main():
                      "frac_hbm": round(achieved / PEAK_HBM_GBS, 4), "bytes": attn_bytes},
             "reject": {"avg_us": round(rej_us, 2), "gbs": round(rej_gbs, 1),
                        "frac_hbm": round(rej_gbs / PEAK_HBM_GBS, 4), "bytes": rej_bytes},
+            "commit": None if commit_ms is None else {"avg_us": round(float(commit_ms * 1e3), 2)},
         },
         "tokens_per_step": round(tokens / args.steps, 2),
         "positions_per_s": round(B * K1 * args.steps / (total_ms / 1e3), 1),

@@ -173,28 +173,23 @@ __device__ __forceinline__ void store_k_window(const bf16x8 (&kf)[D / 16], const
   }
 }
 
-// V operand of a pair with window keys: the window tokens' entries replaced
-// by v_new (strided there, so element loads; one pair per segment), and in
-// append mode stored into the page.
+// V of the window: v_new holds the tokens of one value coordinate strided,
+// so a segment's window rows are staged in LDS ([row][d], bf16) ahead of
+// time, and the pair with window keys takes those tokens' entries from there.
+constexpr int kWinRows = SV_MAX_K + 1;
+
 template <int D>
-__device__ __forceinline__ void window_v(bf16x8 (&vf)[2][D / 32], const int (&blk)[2],
-                                         uint16_t* __restrict__ vc, const uint16_t* __restrict__ vn,
-                                         bool store, int b, int K1, int Hkv, int g, int L0, int pr,
-                                         int l32, int hh) {
+__device__ __forceinline__ void window_v(bf16x8 (&vf)[2][D / 32], const uint16_t* s_win, int K1,
+                                         int L0, int pr, int l32, int hh) {
 #pragma unroll
   for (int sg = 0; sg < 2; ++sg)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int i = pr * kPairKeys + sg * 16 + 8 * hh + e - L0;
       if ((unsigned)i < (unsigned)K1) {
-        const uint16_t* src = vn + (((size_t)b * K1 + i) * Hkv + g) * D + l32;
-        uint16_t* dst = vc + ((size_t)blk[sg] * Hkv + g) * ((size_t)D * 16) + l32 * 16 + 8 * hh + e;
 #pragma unroll
-        for (int j = 0; j < D / 32; ++j) {
-          const uint16_t x = src[32 * j];
-          vf[sg][j][e] = __builtin_bit_cast(__bf16, x);
-          if (store) dst[32 * j * 16] = x;
-        }
+        for (int j = 0; j < D / 32; ++j)
+          vf[sg][j][e] = __builtin_bit_cast(__bf16, s_win[i * D + 32 * j + l32]);
       }
     }
 }
@@ -349,6 +344,56 @@ struct Seg {
   bool full;
 };
 
+// The window rows of segment s that lie in its pairs [p_lo, p_hi) (the rest
+// belong to another workgroup's share), as dwords (two d's of one row):
+// loaded by window_rows_load into registers, then written by
+// window_rows_store to the LDS stage and, in append mode, to the V cache.
+template <int D, int NTH>
+struct WinStage {
+  static constexpr int N = (kWinRows * D / 2 + NTH - 1) / NTH;   // dwords per thread
+  typedef uint32_t Regs[N];
+};
+
+template <int D, int NTH>
+__device__ __forceinline__ void window_rows_load(typename WinStage<D, NTH>::Regs& reg, const Seg& s, int K1,
+                                                 int Hkv, const uint16_t* __restrict__ vn, int tid) {
+  const int i_lo = max(0, s.p_lo * kPairKeys - s.L0), i_hi = min(K1, s.p_hi * kPairKeys - s.L0);
+#pragma unroll
+  for (int r = 0; r < WinStage<D, NTH>::N; ++r) {
+    const int e = i_lo * (D / 2) + tid + r * NTH;
+    reg[r] = 0u;
+    if (e < i_hi * (D / 2)) {
+      const int i = e / (D / 2), d = 2 * (e - i * (D / 2));
+      reg[r] = *reinterpret_cast<const uint32_t*>(vn + (((size_t)s.b * K1 + i) * Hkv + s.g) * D + d);
+    }
+  }
+}
+
+template <int D, int NTH>
+__device__ __forceinline__ void window_rows_store(const typename WinStage<D, NTH>::Regs& reg, const Seg& s,
+                                                  int K1, int Hkv, uint16_t* s_win,
+                                                  uint16_t* __restrict__ vc, bool store,
+                                                  const int32_t* __restrict__ bt, int mbps,
+                                                  int num_blocks, int tid) {
+  const int i_lo = max(0, s.p_lo * kPairKeys - s.L0), i_hi = min(K1, s.p_hi * kPairKeys - s.L0);
+#pragma unroll
+  for (int r = 0; r < WinStage<D, NTH>::N; ++r) {
+    const int e = i_lo * (D / 2) + tid + r * NTH;
+    if (e < i_hi * (D / 2)) {
+      const int i = e / (D / 2), d = 2 * (e - i * (D / 2));
+      *reinterpret_cast<uint32_t*>(s_win + i * D + d) = reg[r];
+      if (store) {
+        const int p = s.L0 + i;
+        const int blk = clampi(bt[(size_t)s.b * mbps + min(p >> 4, mbps - 1)], 0, num_blocks - 1);
+        uint16_t* vpage = vc + ((size_t)blk * Hkv + s.g) * ((size_t)D * 16) + (p & 15);
+        vpage[d * 16] = (uint16_t)(reg[r] & 0xffffu);
+        vpage[(d + 1) * 16] = (uint16_t)(reg[r] >> 16);
+      }
+    }
+  }
+}
+
+
 // The piece after s in the share that ends at u1, if any.
 __device__ __forceinline__ bool next_segment(const Seg& s, Seg& n, int u1, int B, int Hkv, int K1,
                                              int np_cap, const int32_t* __restrict__ kv_len) {
@@ -427,6 +472,7 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
   constexpr int TPR = kStreamThreads / 32;   // epilogue threads per output row
   constexpr int DPT = D / TPR;               // output d's per thread in the epilogue
   __shared__ float s_o[NW][32][OPAD];        // one buffer per wave for the segment merge
+  __shared__ uint16_t s_win[WIN ? 2 : 1][WIN ? kWinRows * D : 1];   // window V stage, double buffered
   __shared__ float s_m[NW][32], s_l[NW][32];
   __shared__ long long s_red[NW];
   __shared__ long long s_res[1];
@@ -521,11 +567,22 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
   bf16x8 qf[NT][KK];
   uint32_t am[NT];
   load_q<D, NT>(qf, am, q, anc, cur, K1, Hq, G, rows, l32, hh);
+  int wbuf = 0;                                    // stage of the current segment's window
+  if (WIN) {
+    uint32_t stg[WinStage<D, kStreamThreads>::N];
+    window_rows_load<D, kStreamThreads>(stg, cur, K1, Hkv, vn, tid);
+    window_rows_store<D, kStreamThreads>(stg, cur, K1, Hkv, s_win[0], vc, store_win != 0, bt, mbps,
+                                         num_blocks, tid);
+  }
   __syncthreads();
 
   while (true) {
     Seg nxt;
     const bool has_next = next_segment(cur, nxt, u1, B, Hkv, K1, np_cap, kv_len);
+    // The next segment's window rows: requested now, staged before this
+    // segment's merge (whose barrier orders them before their use).
+    uint32_t stg[WinStage<D, kStreamThreads>::N];
+    if (WIN && has_next) window_rows_load<D, kStreamThreads>(stg, nxt, K1, Hkv, vn, tid);
     const int nxt_first = nxt.p_lo + wave;        // this wave's first pair of nxt
     const bool nxt_mine = has_next && nxt_first < nxt.p_hi;
 
@@ -573,8 +630,7 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
         else
           load_k<D>(kf, nblk, kc, Hkv, ng, k_page, k_tok, hh);
       }
-      if (WIN && win_here)
-        window_v<D>(vf, cblk, vc, vn, store_win != 0, cur.b, K1, Hkv, cur.g, cur.L0, pr, l32, hh);
+      if (WIN && win_here) window_v<D>(vf, s_win[wbuf], K1, cur.L0, pr, l32, hh);
       mask_v_tail<D>(vf, pr, L, hh);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) pv_pair<D, NT>(vf, nt, pf[nt], o);
@@ -591,6 +647,10 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
         load_k<D>(kf, nblk, kc, Hkv, nxt.g, k_page, k_tok, hh);
       load_v<D>(vf, nblk, vc, Hkv, nxt.g, l32, hh);
     }
+
+    if (WIN && has_next)
+      window_rows_store<D, kStreamThreads>(stg, nxt, K1, Hkv, s_win[wbuf ^ 1], vc, store_win != 0, bt,
+                                           mbps, num_blocks, tid);
 
     // Merge the 4 waves one 32-row tile at a time: each wave stores its O,
     // rescaled to the common row max, in its own LDS buffer; the sum over
@@ -662,6 +722,7 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
 
     if (!has_next) break;
     cur = nxt;
+    wbuf ^= 1;
     // Q of the new segment (the loads of its first pair are already in flight).
     load_q<D, NT>(qf, am, q, anc, cur, K1, Hq, G, rows, l32, hh);
     pr = cur.p_lo + wave;
