@@ -20,6 +20,8 @@ tree       -- attention and the lossless verifier over a flattened draft
               tree.
 kv         -- the window's K/V in the paged cache (append, commit) and the
               host page pool.
+bandit     -- the epsilon-greedy draft-length controller and the
+              per-position acceptance statistics.
 
 Sources (the pages the method is taken from):
   [AIE]  AI Engineering from Scratch, lesson "Speculative decoding and
@@ -40,4 +42,4 @@ Parity status: every function here is pinned by the CPU tests
 attention); none is "parity unpinned".
 """
 
-from . import attention, reject, exact_law, tree, kv  # noqa: F401
+from . import attention, reject, exact_law, tree, kv, bandit  # noqa: F401
