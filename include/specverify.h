@@ -332,6 +332,34 @@ int spec_pages_seq_blocks(const sv_page_pool* pool, int seq);
 const int32_t* spec_pages_block_table(const sv_page_pool* pool);
 int spec_pages_check(const sv_page_pool* pool);
 
+/*
+ * spec_bandit_* -- host-side draft-length controller (devpost "phoenix",
+ * "How we built it", "The bandit").  Arms are indices 0..n_arms-1 into the
+ * caller's list of draft lengths (the page uses {0, 2, 4, 6, 8}).  The first
+ * warmup_rounds * n_arms decisions visit the arms in order; after that,
+ * decision t explores with probability max(0.05, 0.3 * 0.97^t) (t counts
+ * every earlier decision), picking arm floor(u_arm * n_arms), and otherwise
+ * takes the arm with the highest running-average reward (lowest index on
+ * ties).  u_explore and u_arm in [0, 1) are the caller's random numbers.
+ * update() adds one reward (the caller's measured output tokens per second)
+ * to the running mean of its arm and advances t.  select() returns the arm
+ * index or SV_ERR_INVALID_ARG.  Host memory only; not thread-safe.
+ *
+ * spec_accept_stats -- from a verify call's num_accepted (HOST copy, [B]):
+ * a[i-1] = fraction of sequences with n >= i for i = 1..K (per-position
+ * acceptance, quickscale.ai section 4) and mean_len = mean(n + 1), the
+ * tokens emitted per verify.
+ */
+typedef struct sv_bandit sv_bandit;
+sv_bandit* spec_bandit_create(int n_arms, int warmup_rounds);
+void spec_bandit_destroy(sv_bandit* bandit);
+int spec_bandit_select(const sv_bandit* bandit, double u_explore, double u_arm);
+int spec_bandit_update(sv_bandit* bandit, int arm, double reward);
+int spec_bandit_stats(const sv_bandit* bandit, long long* pulls, double* means,
+                      long long* t);
+int spec_accept_stats(const int32_t* num_accepted, int B, int K, double* a,
+                      double* mean_len);
+
 /* Static description of a status code. */
 const char* spec_status_string(int status);
 

@@ -23,7 +23,7 @@ import ctypes
 import os
 
 __all__ = ["load", "lib_path", "exported_symbols", "verify_attn", "verify_attn_tree",
-           "verify_attn_window", "kv_commit", "PagePool", "SV_WINDOW_READ", "SV_WINDOW_APPEND",
+           "verify_attn_window", "kv_commit", "PagePool", "DraftLengthBandit", "accept_stats", "SV_WINDOW_READ", "SV_WINDOW_APPEND",
            "reject_sample", "reject_sample_tree", "verify_attn_workspace_bytes",
            "reject_sample_workspace_bytes", "reject_sample_tree_workspace_bytes",
            "SpecVerifyError", "SV_F32", "SV_BF16", "STATUS", "EXPORTS"]
@@ -42,6 +42,8 @@ EXPORTS = ("spec_verify_attn", "spec_verify_attn_workspace_bytes", "spec_verify_
            "spec_pages_create", "spec_pages_destroy", "spec_pages_reserve", "spec_pages_commit",
            "spec_pages_release", "spec_pages_free_count", "spec_pages_seq_blocks",
            "spec_pages_block_table", "spec_pages_check",
+           "spec_bandit_create", "spec_bandit_destroy", "spec_bandit_select",
+           "spec_bandit_update", "spec_bandit_stats", "spec_accept_stats",
            "spec_status_string", "spec_version")
 
 
@@ -107,6 +109,19 @@ def load():
     lib.spec_pages_block_table.restype = ctypes.POINTER(ctypes.c_int32)
     lib.spec_pages_check.argtypes = [vp]
     lib.spec_pages_check.restype = i32
+    f64, i64p = ctypes.c_double, ctypes.POINTER(ctypes.c_longlong)
+    lib.spec_bandit_create.argtypes = [i32, i32]
+    lib.spec_bandit_create.restype = vp
+    lib.spec_bandit_destroy.argtypes = [vp]
+    lib.spec_bandit_destroy.restype = None
+    lib.spec_bandit_select.argtypes = [vp, f64, f64]
+    lib.spec_bandit_select.restype = i32
+    lib.spec_bandit_update.argtypes = [vp, i32, f64]
+    lib.spec_bandit_update.restype = i32
+    lib.spec_bandit_stats.argtypes = [vp, vp, vp, vp]
+    lib.spec_bandit_stats.restype = i32
+    lib.spec_accept_stats.argtypes = [vp, i32, i32, vp, vp]
+    lib.spec_accept_stats.restype = i32
     lib.spec_status_string.argtypes = [i32]
     lib.spec_status_string.restype = ctypes.c_char_p
     lib.spec_version.argtypes = []
@@ -441,3 +456,62 @@ class PagePool:
         ptr = self._lib.spec_pages_block_table(self._h)
         n = self.max_seqs * self.mbps
         return np.ctypeslib.as_array(ptr, shape=(n,)).copy().reshape(self.max_seqs, self.mbps)
+
+
+class DraftLengthBandit:
+    """Epsilon-greedy choice of the draft length (see ``spec_bandit_*``).
+
+    arms: the draft lengths (the page's {0, 2, 4, 6, 8} by default).
+    select(u_explore, u_arm) -> arm index; arms[index] is the length.
+    update(index, reward) with the measured output tokens per second.
+    """
+
+    def __init__(self, arms=(0, 2, 4, 6, 8), warmup_rounds=2):
+        self._lib = load()
+        self.arms = tuple(int(a) for a in arms)
+        self._h = self._lib.spec_bandit_create(len(self.arms), warmup_rounds)
+        if not self._h:
+            raise SpecVerifyError("spec_bandit_create", -1)
+
+    def close(self):
+        if self._h:
+            self._lib.spec_bandit_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def select(self, u_explore, u_arm):
+        r = self._lib.spec_bandit_select(self._h, float(u_explore), float(u_arm))
+        if r < 0:
+            raise SpecVerifyError("spec_bandit_select", r)
+        return r
+
+    def update(self, arm, reward):
+        _check("spec_bandit_update", self._lib.spec_bandit_update(self._h, int(arm), float(reward)))
+
+    def stats(self):
+        """(pulls [n_arms], means [n_arms], t)."""
+        k = len(self.arms)
+        pulls = (ctypes.c_longlong * k)()
+        means = (ctypes.c_double * k)()
+        t = ctypes.c_longlong()
+        _check("spec_bandit_stats", self._lib.spec_bandit_stats(
+            self._h, ctypes.cast(pulls, ctypes.c_void_p), ctypes.cast(means, ctypes.c_void_p),
+            ctypes.byref(t)))
+        return list(pulls), list(means), t.value
+
+
+def accept_stats(num_accepted, K):
+    """(a [K], mean_len) from a host array of num_accepted (see ``spec_accept_stats``)."""
+    import numpy as np
+    n = np.ascontiguousarray(num_accepted, dtype=np.int32)
+    a = np.zeros(max(K, 1), dtype=np.float64)
+    L = ctypes.c_double()
+    _check("spec_accept_stats", load().spec_accept_stats(
+        n.ctypes.data_as(ctypes.c_void_p), int(n.size), int(K), a.ctypes.data_as(ctypes.c_void_p),
+        ctypes.byref(L)))
+    return a[:K], L.value
