@@ -22,6 +22,7 @@ kv         -- the window's K/V in the paged cache (append, commit) and the
               host page pool.
 bandit     -- the epsilon-greedy draft-length controller and the
               per-position acceptance statistics.
+filter     -- top-k / top-p filtering of both laws before the verifier.
 
 Sources (the pages the method is taken from):
   [AIE]  AI Engineering from Scratch, lesson "Speculative decoding and
@@ -42,4 +43,4 @@ Parity status: every function here is pinned by the CPU tests
 attention); none is "parity unpinned".
 """
 
-from . import attention, reject, exact_law, tree, kv, bandit  # noqa: F401
+from . import attention, reject, exact_law, tree, kv, bandit, filter  # noqa: F401
