@@ -84,6 +84,10 @@ def parse():
                         "the projection output, stored into the cache by the attention kernel "
                         "(append) or committed afterwards by spec_kv_commit (scratch); or a "
                         "separate copy pass before the plain attention (separate)")
+    p.add_argument("--top-k", type=int, default=0,
+                   help="top-k filter for every sequence (spec_reject_sample_filtered; 0: off)")
+    p.add_argument("--top-p", type=float, default=1.0,
+                   help="top-p filter for every sequence (1: off)")
     p.add_argument("--tree", default="", metavar="SHAPE",
                    help="verify a draft tree instead of a chain: branching factors per level, "
                         "e.g. 2,2,2 (15 nodes); times spec_verify_attn_tree + "
@@ -164,6 +168,12 @@ def main():
     torch.cuda.synchronize()
     print("bench: inputs resident", file=sys.stderr, flush=True)
 
+    filt_k = filt_p = None
+    if args.top_k > 0 or args.top_p < 1.0:
+        # The drafts stay the generator's (unfiltered) draws: the filter's
+        # cost does not depend on them.
+        filt_k = torch.full((B,), args.top_k, dtype=torch.int32, device=dev)
+        filt_p = torch.full((B,), args.top_p, dtype=torch.float32, device=dev)
     all_acc = torch.full((B,), K, dtype=torch.int32, device=dev)
     kv_full = kv0 + K1                                   # lengths as if every row survived
 
@@ -191,7 +201,8 @@ def main():
         if parent is None:
             sv.reject_sample(r["target"], r["draft"], r["draft_tokens"], r["uniforms"],
                              r["temperature"], kv, out_tokens=out_tok[s % args.sets],
-                             num_accepted=n_acc[s % args.sets], workspace=rej_ws)
+                             num_accepted=n_acc[s % args.sets], workspace=rej_ws,
+                             top_k=filt_k, top_p=filt_p)
         else:
             sv.reject_sample_tree(r["target"], r["draft"], parent, r["tokens"], r["uniforms"],
                                   r["temperature"], kv, out_tokens=out_tok[s % args.sets],
@@ -309,7 +320,7 @@ def main():
                                 V, cfg.Hq, cfg.Hkv, cfg.D, cfg.ctx[0], cfg.ctx[1],
                                 cfg.draft_sigma, args.temp),
                    "global_batch": B, "K": K, "V": V, "parallelism": "single GPU",
-                   "window": args.window},
+                   "window": args.window, "top_k": args.top_k, "top_p": args.top_p},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": {

@@ -214,6 +214,41 @@ int spec_reject_sample(const void* target_logits, const void* draft_logits,
 size_t spec_reject_sample_workspace_bytes(int B, int K, int V);
 
 /*
+ * spec_reject_sample_filtered -- spec_reject_sample with top-k / top-p
+ * filtering of both laws before the verifier (quickscale.ai, "Quand et
+ * pourquoi utiliser le speculative decoding", "Influence du sampling": top-p
+ * and top-k shape the drafted tokens and the acceptance).
+ *
+ * Per sampling sequence b, with the logits divided by T: top-k keeps the
+ * tokens whose logit is >= the k-th largest (ties kept; top_k[b] <= 0 or
+ * >= V: off); then top-p keeps, among those, the tokens whose logit is >= v*,
+ * v* the largest logit value whose set {x >= v*} holds at least top_p[b] of
+ * the kept mass (ties kept; top_p[b] <= 0 or >= 1: off).  Every target row and
+ * every draft row is filtered with the sequence's own parameters and
+ * renormalised, and the verifier runs on the filtered laws q', p' (accept
+ * with min(1, q'(d)/p'(d)), p'(d) = 0 accepts, residual (q' - p')_+, bonus
+ * from q'): the emitted tokens follow the filtered target.  The drafts are
+ * expected to come from the filtered draft law.  Greedy sequences are
+ * unaffected (the argmax is always kept).
+ *
+ * top_k [B] int32, top_p [B] float32 device arrays; either may be NULL (off
+ * for every sequence).  The top-p set is chosen on masses summed in 40-bit
+ * fixed point from fp32 weights, so a boundary within ~1e-6 of top_p may be
+ * decided differently from an exact computation.  Everything else,
+ * including the workspace (spec_reject_sample_workspace_bytes), is as for
+ * spec_reject_sample.  Cost: two extra passes over each filtered row per
+ * active filter (bf16; four for fp32).
+ */
+int spec_reject_sample_filtered(const void* target_logits, const void* draft_logits,
+                                const int32_t* draft_tokens, const float* uniforms,
+                                const float* temperature, const int32_t* top_k,
+                                const float* top_p, int32_t* out_tokens,
+                                int32_t* num_accepted, int32_t* kv_len,
+                                unsigned long long* counters, int B, int K, int V,
+                                int dtype, void* workspace, size_t workspace_bytes,
+                                void* hip_stream);
+
+/*
  * spec_reject_sample_tree -- the lossless verifier over a flattened draft
  * tree, plus the KV commit (AI Engineering from Scratch, "Speculative
  * decoding and EAGLE-3": EAGLE-2's draft tree, the accept test and residual

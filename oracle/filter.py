@@ -23,9 +23,11 @@ filtering rule; the readings here (also in the design notes):
     under filtering.
 Filtering a row is the same as setting its dropped logits to -inf, which is
 how reject_sample_filtered calls the plain verifier.  F3 flags a sequence
-when a row's top-p boundary is within eps_filter of top_p (the set's mass
-or the mass without the boundary value); the device takes that decision on
-masses summed in fixed point, so it can differ there.
+when a row's top-p boundary is within eps_filter (1e-6) of top_p (the set's
+mass or the mass without the boundary value).  The device takes that
+decision on fp32 weights (one rounding in the exponent, ~1 ulp in exp2)
+summed in 40-bit fixed point: its cumulative masses are within ~2e-7 of the
+exact ones, so it can differ only inside that band.
 """
 
 import numpy as np
@@ -35,7 +37,7 @@ from .reject import widen, reject_sample
 __all__ = ["filter_mask", "filtered_logits", "reject_sample_filtered"]
 
 
-def filter_mask(logits, temperature, top_k=0, top_p=1.0, eps_filter=1e-5):
+def filter_mask(logits, temperature, top_k=0, top_p=1.0, eps_filter=1e-6):
     """Kept-token mask [V] of one row, and the F3 flag."""
     x = np.asarray(logits, dtype=np.float64)
     v = x.shape[0]
@@ -62,7 +64,7 @@ def filter_mask(logits, temperature, top_k=0, top_p=1.0, eps_filter=1e-5):
     return keep, flag
 
 
-def filtered_logits(logits, temperature, top_k, top_p, eps_filter=1e-5):
+def filtered_logits(logits, temperature, top_k, top_p, eps_filter=1e-6):
     """float64 copy of rows [..., V] with the dropped logits at -inf, and a flag per row."""
     x = widen(logits)
     out = x.copy()
@@ -75,7 +77,7 @@ def filtered_logits(logits, temperature, top_k, top_p, eps_filter=1e-5):
 
 
 def reject_sample_filtered(target_logits, draft_logits, draft_tokens, uniforms, temperature,
-                           top_k, top_p, eps_accept=1e-5, eps_sample=1e-10, eps_filter=1e-5):
+                           top_k, top_p, eps_accept=1e-5, eps_sample=1e-10, eps_filter=1e-6):
     """reject_sample on the filtered laws.  top_k [B] int, top_p [B] float.
 
     Returns reject_sample's dict plus flag_filter [B] (F3).  Greedy sequences

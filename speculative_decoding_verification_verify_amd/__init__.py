@@ -38,7 +38,7 @@ STATUS = {0: "SV_OK", -1: "SV_ERR_INVALID_ARG", -2: "SV_ERR_UNSUPPORTED",
 EXPORTS = ("spec_verify_attn", "spec_verify_attn_workspace_bytes", "spec_verify_attn_tree",
            "spec_verify_attn_window", "spec_kv_commit",
            "spec_reject_sample", "spec_reject_sample_workspace_bytes",
-           "spec_reject_sample_tree", "spec_reject_sample_tree_workspace_bytes",
+           "spec_reject_sample_filtered", "spec_reject_sample_tree", "spec_reject_sample_tree_workspace_bytes",
            "spec_pages_create", "spec_pages_destroy", "spec_pages_reserve", "spec_pages_commit",
            "spec_pages_release", "spec_pages_free_count", "spec_pages_seq_blocks",
            "spec_pages_block_table", "spec_pages_check",
@@ -79,6 +79,9 @@ def load():
     lib.spec_reject_sample.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                        vp, sz, vp]
     lib.spec_reject_sample.restype = i32
+    lib.spec_reject_sample_filtered.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
+                                                i32, i32, vp, sz, vp]
+    lib.spec_reject_sample_filtered.restype = i32
     lib.spec_reject_sample_workspace_bytes.argtypes = [i32, i32, i32]
     lib.spec_reject_sample_workspace_bytes.restype = sz
     lib.spec_reject_sample_tree.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
@@ -254,8 +257,10 @@ def _verify_attn(q, k_cache, v_cache, block_table, kv_len, anc, out, max_kv_len,
 
 def reject_sample(target, draft, draft_tokens, uniforms, temperature, kv_len,
                   out_tokens=None, num_accepted=None, counters=None, workspace=None,
-                  stream=None):
-    """Lossless verifier + KV commit (see ``spec_reject_sample``).
+                  stream=None, top_k=None, top_p=None):
+    """Lossless verifier + KV commit (see ``spec_reject_sample``); with
+    top_k [B] int32 and / or top_p [B] float32, on the filtered laws (see
+    ``spec_reject_sample_filtered``).
 
     target [B, K+1, V], draft [B, K, V] or None (greedy for every sequence);
     draft_tokens [B, K] int32; uniforms [B, K+1] float32; temperature [B]
@@ -284,6 +289,18 @@ def reject_sample(target, draft, draft_tokens, uniforms, temperature, kv_len,
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=target.device)
     ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if top_k is not None or top_p is not None:
+        if top_k is not None:
+            _need(top_k, "top_k", torch.int32)
+        if top_p is not None:
+            _need(top_p, "top_p", torch.float32)
+        st = lib.spec_reject_sample_filtered(_ptr(target), _ptr(draft), _ptr(draft_tokens),
+                                             _ptr(uniforms), _ptr(temperature), _ptr(top_k),
+                                             _ptr(top_p), _ptr(out_tokens), _ptr(num_accepted),
+                                             _ptr(kv_len), _ptr(counters), B, K, V, dt,
+                                             _ptr(workspace), ws_have, _stream(stream))
+        _check("spec_reject_sample_filtered", st)
+        return out_tokens, num_accepted
     st = lib.spec_reject_sample(_ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(uniforms),
                                 _ptr(temperature), _ptr(out_tokens), _ptr(num_accepted),
                                 _ptr(kv_len), _ptr(counters), B, K, V, dt, _ptr(workspace),

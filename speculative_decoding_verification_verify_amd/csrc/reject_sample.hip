@@ -92,6 +92,35 @@ struct Decision {
   double coef;       // residual coefficient (1 after the first rejection at a node)
   double coef_prev;  // the one before it: a zero-mass residual leaves the law at
                      // (q - coef_prev p)_+, which is then q (coef_prev = 0) or p
+  uint32_t kq, kp;   // top-k / top-p filters: entries whose order key is below
+                     // these weigh 0 (0: no filter)
+};
+
+// ---- Top-k / top-p filters (readings: logits / T, then top-k, then top-p
+// over the top-k set, each a threshold on the logit value with ties kept).
+// Order keys: unsigned integers that sort like the logits (bf16: 16 bits,
+// fp32: 32 bits); -inf has the smallest key but one, so key 0 never occurs
+// and 0 can mean "no filter".
+__host__ __device__ inline uint32_t order_key16(uint32_t h) {
+  h = (h == 0x8000u) ? 0u : h;                              // -0 ties with +0
+  return (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
+}
+__host__ __device__ inline uint32_t order_key32(uint32_t u) {
+  u = (u == 0x80000000u) ? 0u : u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// Key of a logit held as a float (a bf16 logit widened exactly, or fp32).
+__device__ __forceinline__ uint32_t float_key(float x, bool key16) {
+  const uint32_t u = __float_as_uint(x);
+  return key16 ? order_key16(u >> 16) : order_key32(u);
+}
+
+// What k_filter leaves per row: the kept set {key >= key_min} and its mass
+// in the sweep's frame, sum 2^(x c - fl(xmax c)).
+struct RowFilter {
+  uint32_t key_min;  // 0: the row is not filtered
+  uint32_t pad;
+  double mass;
 };
 
 // Shape of a draft tree (nodes in topological order, parent[i] < i), shared
@@ -382,6 +411,275 @@ __device__ __forceinline__ void emit(int b, int K, int n, int tok, const int* __
 }
 
 // ---------------------------------------------------------------------------
+// k_filter: grid (B * (2K+1)), block 1024: the top-k / top-p thresholds of one
+// row by radix selection over its order keys, 8 bits per pass from the top
+// (2 passes per filter for bf16, 4 for fp32).  Each pass histograms the
+// entries that match the bits chosen so far into 256 bins of counts (top-k)
+// and masses (top-p), and a wave picks the bin where the running total from
+// the top reaches the target.  Masses are 2^(x c - fl(xmax c)) in fp32, added
+// as 40-bit fixed point with integer atomics, so the sums do not depend on
+// the order of the adds (bitwise reproducible) and are exact to ~1e-7 of the
+// row's mass.
+// ---------------------------------------------------------------------------
+constexpr int kFilterThreads = 1024;
+constexpr double kFix = 1099511627776.0;          // 2^40
+
+template <typename T>
+__device__ __forceinline__ uint32_t raw_key(const T* row, int e) {
+  if constexpr (sizeof(T) == 2) return order_key16(row[e]);
+  else return order_key32(__float_as_uint(row[e]));
+}
+
+// One pass: the kept entries (key >= lo) whose key matches prefix in the bits
+// above `shift + 8` go to bin (key >> shift) & 255 of their wave's private
+// histogram (fewer conflicting atomics: the high byte of a logit's key is
+// mostly its exponent, so few bins are hot); the waves' histograms are then
+// summed into h_cnt / h_mass (integers: exact in any order).  Masses only
+// when kMass.  Each thread requests kBatch vectors before it uses any.
+constexpr int kFilterWaves = kFilterThreads / 64;
+template <typename T>
+constexpr int filter_batch() { return 32 / Vec16<T>::N; }   // vectors in flight per thread
+
+// 2^40 m as an integer, for 0 <= m < 2: the float's mantissa shifted into
+// place (truncated; weights below 2^-40 contribute 0).
+__device__ __forceinline__ unsigned long long fixed40(float m) {
+  const uint32_t u = __float_as_uint(m);
+  const int e = (int)(u >> 23) - 127 + 17;        // 2^40 m = mant 2^(e - 23 + 40)
+  const unsigned long long mant = (u & 0x7FFFFFu) | 0x800000u;
+  if ((u >> 23) == 0u || e <= -24) return 0ull;
+  return e >= 0 ? mant << e : mant >> -e;
+}
+
+template <typename T, bool kAligned, bool kMass>
+__device__ __forceinline__ void filter_hist(const T* __restrict__ row, int V, float c, float mc,
+                                            uint32_t lo, uint32_t prefix, int shift,
+                                            unsigned (*w_cnt)[256], unsigned long long (*w_mass)[256],
+                                            unsigned* h_cnt, unsigned long long* h_mass) {
+  constexpr int VN = Vec16<T>::N;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  for (int i = tid; i < kFilterWaves * 256; i += kFilterThreads) {
+    w_cnt[i >> 8][i & 255] = 0u;
+    if (kMass) w_mass[i >> 8][i & 255] = 0ull;
+  }
+  __syncthreads();
+  const int high = shift + 8;
+  for (int base = tid * VN; base < V; base += kFilterThreads * VN * filter_batch<T>()) {
+    u32x4_t raw[filter_batch<T>()];                     // 16-byte vectors, past V as -inf
+#pragma unroll
+    for (int j = 0; j < filter_batch<T>(); ++j) {
+      const int e = base + j * kFilterThreads * VN;
+      raw[j] = kAligned ? load_raw<T>(row, e, V) : load_raw_unaligned<T>(row, e, V);
+    }
+#pragma unroll
+    for (int j = 0; j < filter_batch<T>(); ++j) {
+      float x[VN];
+      widen_raw<T>(raw[j], x);
+#pragma unroll
+      for (int k = 0; k < VN; ++k) {
+        const uint32_t key = float_key(x[k], sizeof(T) == 2);
+        const bool in = (base + j * kFilterThreads * VN + k < V) && key >= lo &&
+                        (high >= 32 || (key >> high) == prefix);
+        if (in) {
+          const int bin = (key >> shift) & 255;
+          atomicAdd(&w_cnt[wave][bin], 1u);
+          if (kMass) atomicAdd(&w_mass[wave][bin], fixed40(exp2_dev(__builtin_fmaf(x[k], c, -mc))));
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < 256) {
+    unsigned cn = 0u;
+    unsigned long long ms = 0ull;
+    for (int w = 0; w < kFilterWaves; ++w) {
+      cn += w_cnt[w][tid];
+      if (kMass) ms += w_mass[w][tid];
+    }
+    h_cnt[tid] = cn;
+    h_mass[tid] = ms;
+  }
+  __syncthreads();
+}
+
+// The mass of the entries with key >= lo, in 40-bit fixed point: per-thread
+// sums, then a block sum (integers: exact in any order).
+template <typename T, bool kAligned>
+__device__ __forceinline__ unsigned long long filter_kept_mass(const T* __restrict__ row, int V,
+                                                               float c, float mc, uint32_t lo,
+                                                               unsigned long long* s_red) {
+  constexpr int VN = Vec16<T>::N;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  unsigned long long acc = 0ull;
+  for (int base = tid * VN; base < V; base += kFilterThreads * VN * filter_batch<T>()) {
+    u32x4_t raw[filter_batch<T>()];
+#pragma unroll
+    for (int j = 0; j < filter_batch<T>(); ++j) {
+      const int e = base + j * kFilterThreads * VN;
+      raw[j] = kAligned ? load_raw<T>(row, e, V) : load_raw_unaligned<T>(row, e, V);
+    }
+#pragma unroll
+    for (int j = 0; j < filter_batch<T>(); ++j) {
+      float x[VN];
+      widen_raw<T>(raw[j], x);
+#pragma unroll
+      for (int k = 0; k < VN; ++k) {
+        const bool in = (base + j * kFilterThreads * VN + k < V) &&
+                        float_key(x[k], sizeof(T) == 2) >= lo;
+        acc += in ? fixed40(exp2_dev(__builtin_fmaf(x[k], c, -mc))) : 0ull;
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  __syncthreads();
+  if (lane == 0) s_red[wave] = acc;
+  __syncthreads();
+  unsigned long long tot = 0ull;
+#pragma unroll
+  for (int w = 0; w < kFilterWaves; ++w) tot += s_red[w];
+  return tot;
+}
+
+// Wave 0: the largest bin whose running total from the top (plus the totals
+// carried in above_cnt / above_mass from the higher bits) reaches `target`,
+// by count or by mass; adds the totals of the bins above it to the carries.
+// If no bin reaches (only by rounding), the lowest nonempty bin.
+__device__ __forceinline__ int filter_pick(const unsigned* h_cnt, const unsigned long long* h_mass,
+                                           bool by_mass, double target, unsigned long long& above_cnt,
+                                           unsigned long long& above_mass, int lane) {
+  unsigned long long c[4], m[4], lc = 0, lm = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {                    // lane l holds bins 4l .. 4l + 3
+    c[k] = h_cnt[4 * lane + k];
+    m[k] = h_mass[4 * lane + k];
+    lc += c[k];
+    lm += m[k];
+  }
+  unsigned long long sc = lc, sm = lm;             // inclusive sums over lanes l..63
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned long long tc = __shfl_down(sc, off, 64);
+    const unsigned long long tm = __shfl_down(sm, off, 64);
+    if (lane + off < 64) { sc += tc; sm += tm; }
+  }
+  int hit = -1, nonempty = 256;
+  unsigned long long ac = above_cnt + sc - lc, am = above_mass + sm - lm;   // bins above this lane
+#pragma unroll
+  for (int k = 3; k >= 0; --k) {
+    ac += c[k];
+    am += m[k];
+    if (hit < 0 && (by_mass ? (double)am : (double)ac) >= target) hit = 4 * lane + k;
+    if (c[k]) nonempty = 4 * lane + k;
+  }
+  int sel = hit;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sel = max(sel, __shfl_xor(sel, off, 64));
+  if (sel < 0) {
+    sel = nonempty;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sel = min(sel, __shfl_xor(sel, off, 64));
+    if (sel > 255) sel = 0;
+  }
+  // Totals of the bins above sel.
+  unsigned long long xc = 0, xm = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (4 * lane + k > sel) { xc += c[k]; xm += m[k]; }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    xc += __shfl_xor(xc, off, 64);
+    xm += __shfl_xor(xm, off, 64);
+  }
+  above_cnt += xc;
+  above_mass += xm;
+  return sel;
+}
+
+template <typename T, bool kAligned>
+__global__ __launch_bounds__(kFilterThreads) void k_filter(
+    const T* __restrict__ tgt, const T* __restrict__ drf, const float* __restrict__ temp,
+    const int32_t* __restrict__ top_k, const float* __restrict__ top_p, int K, int V, int nc,
+    int force_greedy, const float2* __restrict__ part, RowFilter* __restrict__ filt) {
+  __shared__ unsigned w_cnt[kFilterWaves][256];
+  __shared__ unsigned long long w_mass[kFilterWaves][256];
+  __shared__ unsigned h_cnt[256];
+  __shared__ unsigned long long h_mass[256];
+  __shared__ float s_xr;
+  __shared__ int s_sel;
+  __shared__ unsigned long long s_ac, s_am;
+  __shared__ unsigned long long s_red[kFilterWaves];
+  const int R = 2 * K + 1;
+  const int row = blockIdx.x;
+  const int b = row / R;
+  const int j = row - b * R;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float t = temp_of(temp, b, force_greedy);
+  const int tk = top_k ? top_k[b] : 0;
+  const float tp = top_p ? top_p[b] : 1.f;
+  const bool k_on = tk > 0 && tk < V;
+  const bool p_on = tp > 0.f && tp < 1.f;
+  if (!(t > 0.f) || (!k_on && !p_on)) {
+    if (tid == 0) filt[row] = RowFilter{0u, 0u, 0.0};
+    return;
+  }
+  const T* src = (j <= K) ? tgt + ((size_t)b * (K + 1) + j) * (size_t)V
+                          : drf + ((size_t)b * K + (j - K - 1)) * (size_t)V;
+  const float c = kLog2e / t;
+  // The row's raw maximum, merged from the sweep's chunk maxima as k_decide does.
+  if (wave == 0) {
+    float xr = -INFINITY;
+    for (int k = lane; k < nc; k += 64) xr = fmaxf(xr, part[(size_t)row * nc + k].x);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) xr = fmaxf(xr, __shfl_xor(xr, off, 64));
+    if (lane == 0) s_xr = xr;
+  }
+  __syncthreads();
+  const float mc = s_xr * c;
+  constexpr int kBits = sizeof(T) == 2 ? 16 : 32;
+  uint32_t lo = 0u;                                // keys below this are filtered out
+  unsigned long long kept_mass = 0ull;
+  bool have_mass = false;
+  for (int f = 0; f < 2; ++f) {
+    const bool by_mass = (f == 1);
+    if (by_mass ? !p_on : !k_on) continue;
+    uint32_t prefix = 0u;
+    unsigned long long ac = 0ull, am = 0ull;
+    double target = by_mass ? 0.0 : (double)tk;
+    for (int shift = kBits - 8; shift >= 0; shift -= 8) {
+      if (by_mass)
+        filter_hist<T, kAligned, true>(src, V, c, mc, lo, prefix, shift, w_cnt, w_mass, h_cnt, h_mass);
+      else
+        filter_hist<T, kAligned, false>(src, V, c, mc, lo, prefix, shift, w_cnt, w_mass, h_cnt, h_mass);
+      if (wave == 0) {
+        if (by_mass && shift == kBits - 8) {
+          // The kept set's mass (all of the row, or its top-k set) sets the target.
+          unsigned long long tot = 0ull;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) tot += h_mass[4 * lane + k];
+#pragma unroll
+          for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off, 64);
+          target = (double)tp * (double)tot;
+        }
+        const int sel = filter_pick(h_cnt, h_mass, by_mass, target, ac, am, lane);
+        if (lane == 0) { s_sel = sel; s_ac = ac; s_am = am; }
+      }
+      __syncthreads();
+      const int sel = s_sel;
+      ac = s_ac;
+      am = s_am;
+      prefix = (prefix << 8) | (uint32_t)sel;
+      if (by_mass && shift == 0) kept_mass = am + h_mass[sel];
+      __syncthreads();
+    }
+    lo = prefix;                                   // the k-th largest key, or the top-p key
+    have_mass = by_mass;
+  }
+  // Top-k alone: the kept set's mass in one more pass (top-p's passes give it).
+  if (!have_mass) kept_mass = filter_kept_mass<T, kAligned>(src, V, c, mc, lo, s_red);
+  if (tid == 0) filt[row] = RowFilter{lo, 0u, (double)kept_mass / kFix};
+}
+
+// ---------------------------------------------------------------------------
 // k_decide: grid (B); block 1024.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kDecideThreads) void k_decide(
@@ -389,8 +687,9 @@ __global__ __launch_bounds__(kDecideThreads) void k_decide(
     int K, int V, int nc, int force_greedy, const float2* __restrict__ part,
     const float* __restrict__ xd, Decision* __restrict__ dec,
     int32_t* __restrict__ out, int32_t* __restrict__ nacc, int32_t* __restrict__ kv_len,
-    unsigned long long* counters) {
+    unsigned long long* counters, const RowFilter* __restrict__ filt, int key16) {
   __shared__ float s_a[kMaxRows], s_b[kMaxRows];
+  __shared__ uint32_t s_kmin[kMaxRows];
   __shared__ float2 s_part[kPartStage];
   __shared__ float s_xq[SV_MAX_K], s_xp[SV_MAX_K], s_u[SV_MAX_K];
   __shared__ int s_d[SV_MAX_K], s_draw[SV_MAX_K];
@@ -424,7 +723,13 @@ __global__ __launch_bounds__(kDecideThreads) void k_decide(
   for (int r = wave; r < rows; r += kDecideThreads / 64) {
     float a, bb;
     merge_row(staged ? s_part + r * nc : pb + (size_t)r * nc, nc, greedy, c, lane, a, bb);
-    if (lane == 0) { s_a[r] = a; s_b[r] = bb; }
+    if (lane == 0) {
+      // A filtered row: its law is renormalised over the kept set.
+      const RowFilter rf = (filt && !greedy) ? filt[(size_t)b * R + r] : RowFilter{0u, 0u, 0.0};
+      s_a[r] = a;
+      s_b[r] = rf.key_min ? (float)rf.mass : bb;
+      s_kmin[r] = rf.key_min;
+    }
   }
   __syncthreads();
   // Accept tests of all K drafts at once (lanes of wave 0), then the first
@@ -435,8 +740,10 @@ __global__ __launch_bounds__(kDecideThreads) void k_decide(
       const int i = lane;
       if (greedy) {
         acc = (s_d[i] == __float_as_int(s_b[i]));
-      } else if (s_xp[i] == -INFINITY) {
-        acc = true;                                   // p(d) == 0
+      } else if (s_xp[i] == -INFINITY || float_key(s_xp[i], key16) < s_kmin[K + 1 + i]) {
+        acc = true;                                   // p(d) == 0 (filtered out included)
+      } else if (float_key(s_xq[i], key16) < s_kmin[i]) {
+        acc = false;                                  // q(d) == 0: filtered out of the target
       } else {
         // q/p = 2^((xq c - mq) - (xp c - mp)) * sp / sq with m = fl(xmax c),
         // taken in the log domain so small probabilities do not underflow.
@@ -459,7 +766,8 @@ __global__ __launch_bounds__(kDecideThreads) void k_decide(
   if (tid != 0) return;
   const double cd = kLog2eD / (double)t;
   Decision dd{n < K ? kModeResid : kModeQ, n, b * (K + 1) + n, n < K ? b * K + n : 0,
-              s_a[n], n < K ? s_a[K + 1 + n] : 0.f, 0.0, 1.0, 0.0};
+              s_a[n], n < K ? s_a[K + 1 + n] : 0.f, 0.0, 1.0, 0.0, s_kmin[n],
+              n < K ? s_kmin[K + 1 + n] : 0u};
   if (n < K) {
     // The sweep's normalisers, moved from the fl(xmax c) frame to the
     // 2^((x - xmax) c) frame of the exact pass.
@@ -679,13 +987,16 @@ __device__ __forceinline__ int locate_draw(const T* __restrict__ trow, const T* 
   double w = 0.0;
   if (e < V) {
     const double c256 = cd * 256.0;
+    float xq = m == kDrawP ? 0.f : Vec16<T>::one(trow + e);
+    if (float_key(xq, sizeof(T) == 2) < d.kq) xq = -INFINITY;        // filtered out
     const double q = m == kDrawP ? 0.0
-                                 : exp2_neg(expo(Vec16<T>::one(trow + e), c256, ((double)d.xmq * cd) * 256.0),
-                                            s_exp) * isq;
+                                 : exp2_neg(expo(xq, c256, ((double)d.xmq * cd) * 256.0), s_exp) * isq;
     if (m == kDrawQ) {
       w = q;
     } else {
-      const double p = exp2_neg(expo(Vec16<T>::one(drow + e), c256, ((double)d.xmp * cd) * 256.0), s_exp) * isp;
+      float xp = Vec16<T>::one(drow + e);
+      if (float_key(xp, sizeof(T) == 2) < d.kp) xp = -INFINITY;
+      const double p = exp2_neg(expo(xp, c256, ((double)d.xmp * cd) * 256.0), s_exp) * isp;
       w = m == kDrawP ? p : fmax(0.0, q - p);
     }
   }
@@ -731,6 +1042,15 @@ __global__ __launch_bounds__(kThreads) void k_locate(
   emit(b, K, d.n, tok, s_draw, out, nacc, kv_len, counters);
 }
 
+// Filtered-out entries (order key below kmin) become -inf: weight 0, never
+// classed q > c p.
+template <typename T>
+__device__ __forceinline__ void mask_row(float (&x)[Vec16<T>::N], uint32_t kmin) {
+#pragma unroll
+  for (int k = 0; k < Vec16<T>::N; ++k)
+    x[k] = float_key(x[k], sizeof(T) == 2) < kmin ? -INFINITY : x[k];
+}
+
 // ---------------------------------------------------------------------------
 // k_residual: grid (B, ncr); block 256.  The pass each decision asks for
 // (none for greedy or finished sequences).
@@ -740,7 +1060,7 @@ __global__ __launch_bounds__(kThreads) void k_locate(
 // so an instruction of the wave still reads 8 whole lines, and a sub-chunk's
 // sums need only 3 butterfly steps.
 // ---------------------------------------------------------------------------
-template <typename T, bool kAligned>
+template <typename T, bool kAligned, bool kMask = false>
 __global__ __launch_bounds__(kThreads, 4) void k_residual(
     const T* __restrict__ tgt, const T* __restrict__ drf, const float* __restrict__ temp,
     int V, int ncr, int force_greedy, const Decision* __restrict__ dec,
@@ -787,6 +1107,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_residual(
     for (int i = 0; i < IT; ++i) {
       float xq[VN];
       widen_raw<T>(rq[i], xq);
+      if (kMask) mask_row<T>(xq, d.kq);
       Exp2Arg eq[VN];
       double tq[VN];
 #pragma unroll
@@ -804,6 +1125,10 @@ __global__ __launch_bounds__(kThreads, 4) void k_residual(
       float xq[VN], xp[VN];
       widen_raw<T>(rq[i], xq);
       widen_raw<T>(rp[i], xp);
+      if (kMask) {
+        mask_row<T>(xq, d.kq);
+        mask_row<T>(xp, d.kp);
+      }
       constexpr int HB = VN / 2;                  // entries per batch
 #pragma unroll
       for (int h = 0; h < VN; h += HB) {
@@ -1125,7 +1450,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_step(
 }
 
 struct RejectPlan {
-  size_t part_off, csum_off, csub_off, dec_off, xd_off, total;
+  size_t part_off, csum_off, csub_off, dec_off, xd_off, filt_off, total;
 };
 
 static inline RejectPlan reject_plan(int B, int K, int V) {
@@ -1137,7 +1462,8 @@ static inline RejectPlan reject_plan(int B, int K, int V) {
   p.csub_off = p.csum_off + up((size_t)B * res_chunks(V) * sizeof(ChunkSums));
   p.dec_off = p.csub_off + up((size_t)B * res_chunks(V) * kSubPerChunk * sizeof(SubSums));
   p.xd_off = p.dec_off + up((size_t)B * sizeof(Decision));
-  p.total = p.xd_off + up((size_t)B * K * 2 * sizeof(float));
+  p.filt_off = p.xd_off + up((size_t)B * K * 2 * sizeof(float));
+  p.total = p.filt_off + up((size_t)B * R * sizeof(RowFilter));
   return p;
 }
 
@@ -1145,7 +1471,8 @@ template <typename T, bool kAligned>
 static hipError_t launch_all(const void* tgt, const void* drf, const int32_t* dtok, const float* uni,
                              const float* temp, int32_t* out, int32_t* nacc, int32_t* kv_len,
                              unsigned long long* counters, int B, int K, int V, int force_greedy,
-                             char* ws, hipStream_t st) {
+                             char* ws, hipStream_t st, const int32_t* top_k = nullptr,
+                             const float* top_p = nullptr) {
   const int nc = sweep_chunks(V);
   const int ncr = res_chunks(V);
   const int R = 2 * K + 1;
@@ -1159,10 +1486,20 @@ static hipError_t launch_all(const void* tgt, const void* drf, const int32_t* dt
   const T* d = static_cast<const T*>(drf);
   hipLaunchKernelGGL((k_sweep<T, kAligned, ChainRows>), dim3(B * R, (nc + 3) / 4), dim3(kThreads), 0,
                      st, t, d, dtok, temp, ChainRows{K}, V, nc, force_greedy, part, xd);
+  const bool filtered = (top_k || top_p) && !force_greedy;
+  RowFilter* filt = filtered ? reinterpret_cast<RowFilter*>(ws + p.filt_off) : nullptr;
+  if (filtered)
+    hipLaunchKernelGGL((k_filter<T, kAligned>), dim3(B * R), dim3(kFilterThreads), 0, st, t, d, temp,
+                       top_k, top_p, K, V, nc, force_greedy, part, filt);
   hipLaunchKernelGGL(k_decide, dim3(B), dim3(kDecideThreads), 0, st, dtok, uni, temp, K, V, nc,
-                     force_greedy, part, xd, dec, out, nacc, kv_len, counters);
-  hipLaunchKernelGGL((k_residual<T, kAligned>), dim3(B, ncr), dim3(kThreads), 0, st, t, d, temp, V,
-                     ncr, force_greedy, dec, csum, csub);
+                     force_greedy, part, xd, dec, out, nacc, kv_len, counters, filt,
+                     sizeof(T) == 2 ? 1 : 0);
+  if (filtered)
+    hipLaunchKernelGGL((k_residual<T, kAligned, true>), dim3(B, ncr), dim3(kThreads), 0, st, t, d, temp,
+                       V, ncr, force_greedy, dec, csum, csub);
+  else
+    hipLaunchKernelGGL((k_residual<T, kAligned>), dim3(B, ncr), dim3(kThreads), 0, st, t, d, temp, V,
+                       ncr, force_greedy, dec, csum, csub);
   hipLaunchKernelGGL((k_locate<T>), dim3(B), dim3(kThreads), 0, st, t, d, dtok, uni, temp, K, V, ncr,
                      force_greedy, csum, csub, dec, out, nacc, kv_len, counters);
   return hipGetLastError();
@@ -1269,12 +1606,12 @@ extern "C" size_t spec_reject_sample_workspace_bytes(int B, int K, int V) {
   return sv::reject_plan(B, K, V).total;
 }
 
-extern "C" int spec_reject_sample(const void* target_logits, const void* draft_logits,
-                                  const int32_t* draft_tokens, const float* uniforms,
-                                  const float* temperature, int32_t* out_tokens,
-                                  int32_t* num_accepted, int32_t* kv_len,
-                                  unsigned long long* counters, int B, int K, int V, int dtype,
-                                  void* workspace, size_t workspace_bytes, void* hip_stream) {
+static int reject_impl(const void* target_logits, const void* draft_logits,
+                       const int32_t* draft_tokens, const float* uniforms, const float* temperature,
+                       const int32_t* top_k, const float* top_p, int32_t* out_tokens,
+                       int32_t* num_accepted, int32_t* kv_len, unsigned long long* counters, int B,
+                       int K, int V, int dtype, void* workspace, size_t workspace_bytes,
+                       void* hip_stream) {
   if (B < 0 || K < 1 || V < 1) return SV_ERR_INVALID_ARG;
   if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_INVALID_ARG;
   if (K > SV_MAX_K) return SV_ERR_UNSUPPORTED;
@@ -1300,20 +1637,44 @@ extern "C" int spec_reject_sample(const void* target_logits, const void* draft_l
     const bool al = (V % 8 == 0) && (align_bits & 15) == 0;
     e = al ? sv::launch_all<uint16_t, true>(target_logits, drf, draft_tokens, uniforms, temperature,
                                             out_tokens, num_accepted, kv_len, counters, B, K, V,
-                                            force_greedy, ws, st)
+                                            force_greedy, ws, st, top_k, top_p)
            : sv::launch_all<uint16_t, false>(target_logits, drf, draft_tokens, uniforms, temperature,
                                              out_tokens, num_accepted, kv_len, counters, B, K, V,
-                                             force_greedy, ws, st);
+                                             force_greedy, ws, st, top_k, top_p);
   } else {
     const bool al = (V % 4 == 0) && (align_bits & 15) == 0;
     e = al ? sv::launch_all<float, true>(target_logits, drf, draft_tokens, uniforms, temperature,
                                          out_tokens, num_accepted, kv_len, counters, B, K, V,
-                                         force_greedy, ws, st)
+                                         force_greedy, ws, st, top_k, top_p)
            : sv::launch_all<float, false>(target_logits, drf, draft_tokens, uniforms, temperature,
                                           out_tokens, num_accepted, kv_len, counters, B, K, V,
-                                          force_greedy, ws, st);
+                                          force_greedy, ws, st, top_k, top_p);
   }
   return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+extern "C" int spec_reject_sample(const void* target_logits, const void* draft_logits,
+                                  const int32_t* draft_tokens, const float* uniforms,
+                                  const float* temperature, int32_t* out_tokens,
+                                  int32_t* num_accepted, int32_t* kv_len,
+                                  unsigned long long* counters, int B, int K, int V, int dtype,
+                                  void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return reject_impl(target_logits, draft_logits, draft_tokens, uniforms, temperature, nullptr,
+                     nullptr, out_tokens, num_accepted, kv_len, counters, B, K, V, dtype, workspace,
+                     workspace_bytes, hip_stream);
+}
+
+extern "C" int spec_reject_sample_filtered(const void* target_logits, const void* draft_logits,
+                                           const int32_t* draft_tokens, const float* uniforms,
+                                           const float* temperature, const int32_t* top_k,
+                                           const float* top_p, int32_t* out_tokens,
+                                           int32_t* num_accepted, int32_t* kv_len,
+                                           unsigned long long* counters, int B, int K, int V,
+                                           int dtype, void* workspace, size_t workspace_bytes,
+                                           void* hip_stream) {
+  return reject_impl(target_logits, draft_logits, draft_tokens, uniforms, temperature, top_k, top_p,
+                     out_tokens, num_accepted, kv_len, counters, B, K, V, dtype, workspace,
+                     workspace_bytes, hip_stream);
 }
 
 extern "C" size_t spec_reject_sample_tree_workspace_bytes(int B, int N, int V) {

@@ -145,11 +145,13 @@ def test_tree_reject_validation(lib):
 
 def test_tree_reject_workspace_matches_chain(lib):
     # A chain of K + 1 nodes sweeps the same 2K + 1 rows as the chain call;
-    # the tree adds its walk state and merged row statistics.
+    # the tree adds its walk state and merged row statistics, the chain its
+    # per-row top-k / top-p results.
     for B, K, V in [(64, 7, 128256), (1, 1, 1000), (3, 16, 152064)]:
         t = sv.reject_sample_tree_workspace_bytes(B, K + 1, V)
         c = sv.reject_sample_workspace_bytes(B, K, V)
-        assert t >= c > 0
+        filters = (B * (2 * K + 1) * 16 + 255) // 256 * 256   # the chain's per-row filter results
+        assert t >= c - filters > 0
     assert sv.reject_sample_tree_workspace_bytes(0, 4, 100) == 0
     assert sv.reject_sample_tree_workspace_bytes(4, 0, 100) == 0
     assert sv.reject_sample_tree_workspace_bytes(4, 18, 100) == 0

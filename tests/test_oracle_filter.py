@@ -28,6 +28,7 @@ def test_top_p_by_hand():
         keep, flag = of.filter_mask(x, 1.0, top_p=p)
         assert keep.tolist() == [bool(w) for w in want], p
     assert of.filter_mask(x, 1.0, top_p=0.8)[1]            # cum mass exactly 0.8: flagged
+    assert not of.filter_mask(x, 1.0, top_p=0.79999)[1]    # 1e-5 away: outside the band
     assert not of.filter_mask(x, 1.0, top_p=0.7)[1]
     for p in (0.0, 1.0, 1.5):
         assert of.filter_mask(x, 1.0, top_p=p)[0].all()
