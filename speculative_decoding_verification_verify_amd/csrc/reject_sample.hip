@@ -109,10 +109,18 @@ __host__ __device__ inline uint32_t order_key32(uint32_t u) {
   u = (u == 0x80000000u) ? 0u : u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+// 32-bit key of a float: order_key32, written as a sign-dependent xor plus
+// the -0 fix.  For a widened bf16 logit its top 16 bits are order_key16 of
+// the bf16 bits.
+__device__ __forceinline__ uint32_t key32_of(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t k = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+  return k == 0x7FFFFFFFu ? 0x80000000u : k;
+}
 // Key of a logit held as a float (a bf16 logit widened exactly, or fp32).
 __device__ __forceinline__ uint32_t float_key(float x, bool key16) {
-  const uint32_t u = __float_as_uint(x);
-  return key16 ? order_key16(u >> 16) : order_key32(u);
+  const uint32_t k = key32_of(x);
+  return key16 ? k >> 16 : k;
 }
 
 // What k_filter leaves per row: the kept set {key >= key_min} and its mass
@@ -412,123 +420,260 @@ __device__ __forceinline__ void emit(int b, int K, int n, int tok, const int* __
 
 // ---------------------------------------------------------------------------
 // k_filter: grid (B * (2K+1)), block 1024: the top-k / top-p thresholds of one
-// row by radix selection over its order keys, 8 bits per pass from the top
-// (2 passes per filter for bf16, 4 for fp32).  Each pass histograms the
-// entries that match the bits chosen so far into 256 bins of counts (top-k)
-// and masses (top-p), and a wave picks the bin where the running total from
-// the top reaches the target.  Masses are 2^(x c - fl(xmax c)) in fp32, added
-// as 40-bit fixed point with integer atomics, so the sums do not depend on
-// the order of the adds (bitwise reproducible) and are exact to ~1e-7 of the
+// row by radix selection over its order keys, most significant digit first:
+// 12 bits, then 4 (bf16) or 12 and 8 (fp32).  Each pass histograms the
+// entries that match the digits chosen so far into up to 4096 bins of counts
+// (top-k) or masses (top-p), and the block picks the bin where the running
+// total from the top reaches the target.  The first pass takes every entry
+// (no branch around its adds); later passes test membership with two float
+// compares against the value range of the chosen bin, and only members
+// compute a key.  The wide first digit splits each exponent's entries over
+// 16 bins, so fewer threads add to the same bin at once.  For bf16 the last
+// pass works on single values: counts only, each bin's mass being its count
+// times the value's weight.  Masses are 2^(x c - fl(xmax c)) in fp32, added
+// as 40-bit fixed point with integer atomics: the sums do not depend on the
+// order of the adds (bitwise reproducible) and are exact to ~1e-7 of the
 // row's mass.
 // ---------------------------------------------------------------------------
 constexpr int kFilterThreads = 1024;
+constexpr int kFilterWaves = kFilterThreads / 64;
+constexpr int kFilterBins = 4096;
 constexpr double kFix = 1099511627776.0;          // 2^40
 
+// 16-byte vectors per batch of a thread (two batches are in registers at
+// once); half as many where each load is several (rows that do not start on
+// a 16-byte boundary).
+template <typename T, bool kAligned>
+constexpr int filter_batch() { return kAligned ? 4 : 2; }
+
+// Digit widths, most significant first.
 template <typename T>
-__device__ __forceinline__ uint32_t raw_key(const T* row, int e) {
-  if constexpr (sizeof(T) == 2) return order_key16(row[e]);
-  else return order_key32(__float_as_uint(row[e]));
+__device__ __forceinline__ int digit_bits(int level) {
+  if constexpr (sizeof(T) == 2) return level == 0 ? 12 : 4;
+  else return level == 2 ? 8 : 12;
+}
+template <typename T>
+constexpr int filter_levels() { return sizeof(T) == 2 ? 2 : 3; }
+
+// floor(2^40 w) as an integer, for 0 <= w < 2^24: t = 256 w is exact, its
+// integer part gives the high word and its fraction times 2^32 (exact,
+// truncated by the conversion) the low word (weights below 2^-40 give 0).
+__device__ __forceinline__ unsigned long long fixed40(float w) {
+  const float t = w * 256.0f;
+  const uint32_t hi = (uint32_t)t;
+  const uint32_t lo = (uint32_t)(__builtin_amdgcn_fractf(t) * 4294967296.0f);
+  return ((unsigned long long)hi << 32) | lo;
 }
 
-// One pass: the kept entries (key >= lo) whose key matches prefix in the bits
-// above `shift + 8` go to bin (key >> shift) & 255 of their wave's private
-// histogram (fewer conflicting atomics: the high byte of a logit's key is
-// mostly its exponent, so few bins are hot); the waves' histograms are then
-// summed into h_cnt / h_mass (integers: exact in any order).  Masses only
-// when kMass.  Each thread requests kBatch vectors before it uses any.
-constexpr int kFilterWaves = kFilterThreads / 64;
-template <typename T>
-constexpr int filter_batch() { return 32 / Vec16<T>::N; }   // vectors in flight per thread
-
-// 2^40 m as an integer, for 0 <= m < 2: the float's mantissa shifted into
-// place (truncated; weights below 2^-40 contribute 0).
-__device__ __forceinline__ unsigned long long fixed40(float m) {
-  const uint32_t u = __float_as_uint(m);
-  const int e = (int)(u >> 23) - 127 + 17;        // 2^40 m = mant 2^(e - 23 + 40)
-  const unsigned long long mant = (u & 0x7FFFFFu) | 0x800000u;
-  if ((u >> 23) == 0u || e <= -24) return 0ull;
-  return e >= 0 ? mant << e : mant >> -e;
+// The float with a given 32-bit key (no NaN keys are passed).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+constexpr uint32_t kKeyNegInf = 0x007FFFFFu, kKeyPosInf = 0xFF800000u;
+// Float bounds [flo, fhi] with  flo <= x <= fhi  <=>  klo <= key32_of(x) <= khi
+// for every non-NaN x.  Key 0x7FFFFFFF (-0 before the fix) never occurs, so
+// as a bound it is moved past -0: x = -0 compares equal to +0.
+__device__ __forceinline__ void key_bounds(uint32_t klo, uint32_t khi, float& flo, float& fhi) {
+  klo = max(klo, kKeyNegInf);
+  khi = min(khi, kKeyPosInf);
+  if (klo == 0x7FFFFFFFu) klo = 0x80000000u;
+  if (khi == 0x7FFFFFFFu) khi = 0x7FFFFFFEu;
+  flo = key_value(klo);
+  fhi = key_value(khi);
 }
 
-template <typename T, bool kAligned, bool kMass>
-__device__ __forceinline__ void filter_hist(const T* __restrict__ row, int V, float c, float mc,
-                                            uint32_t lo, uint32_t prefix, int shift,
-                                            unsigned (*w_cnt)[256], unsigned long long (*w_mass)[256],
-                                            unsigned* h_cnt, unsigned long long* h_mass) {
+// Streams a row through f(x, e, inb): x the VN widened logits of the vector
+// at entry e, inb whether entry k is below V (per vector where rows are
+// aligned).  Each thread keeps two batches of filter_batch vectors: the
+// next batch is requested before the current one is used.
+template <typename T, bool kAligned, class F>
+__device__ __forceinline__ void filter_scan(const T* __restrict__ row, int V, F&& f) {
   constexpr int VN = Vec16<T>::N;
-  const int tid = threadIdx.x, wave = tid >> 6;
-  for (int i = tid; i < kFilterWaves * 256; i += kFilterThreads) {
-    w_cnt[i >> 8][i & 255] = 0u;
-    if (kMass) w_mass[i >> 8][i & 255] = 0ull;
-  }
-  __syncthreads();
-  const int high = shift + 8;
-  for (int base = tid * VN; base < V; base += kFilterThreads * VN * filter_batch<T>()) {
-    u32x4_t raw[filter_batch<T>()];                     // 16-byte vectors, past V as -inf
+  constexpr int NB = filter_batch<T, kAligned>();
+  constexpr int kStep = kFilterThreads * VN * NB;
+  auto fetch = [&](u32x4_t (&r)[NB], int base) {
 #pragma unroll
-    for (int j = 0; j < filter_batch<T>(); ++j) {
+    for (int j = 0; j < NB; ++j) {
       const int e = base + j * kFilterThreads * VN;
-      raw[j] = kAligned ? load_raw<T>(row, e, V) : load_raw_unaligned<T>(row, e, V);
+      r[j] = kAligned ? load_raw<T>(row, e, V) : load_raw_unaligned<T>(row, e, V);
+    }
+  };
+  int base = threadIdx.x * VN;
+  if (base >= V) return;
+  u32x4_t cur[NB], nxt[NB];
+  fetch(cur, base);
+  for (; base < V; base += kStep) {
+    fetch(nxt, base + kStep);                      // past V: harmless, replaced by -inf
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int e = base + j * kFilterThreads * VN;
+      float x[VN];
+      widen_raw<T>(cur[j], x);
+      f(x, e);
     }
 #pragma unroll
-    for (int j = 0; j < filter_batch<T>(); ++j) {
-      float x[VN];
-      widen_raw<T>(raw[j], x);
+    for (int j = 0; j < NB; ++j) cur[j] = nxt[j];
+  }
+}
+
+// One pass over a row: each entry with flo <= x <= fhi (every entry when
+// kAll) adds to bin (key32 >> shift) & (2^width - 1) of h: 1 (top-k) or its
+// weight 2^(x c - mc) in 40-bit fixed point (top-p).  Each thread requests
+// filter_batch vectors before it uses any; with kAll the adds are not
+// branched around (entries past V add 0).
+template <typename T, bool kAligned, bool kMass, bool kAll>
+__device__ __forceinline__ void filter_hist(const T* __restrict__ row, int V, float c, float mc,
+                                            float flo, float fhi, int shift, int width,
+                                            unsigned long long* h) {
+  constexpr int VN = Vec16<T>::N;
+  for (int i = threadIdx.x; i < kFilterBins; i += kFilterThreads) h[i] = 0ull;
+  __syncthreads();
+  filter_scan<T, kAligned>(row, V, [&](const float (&x)[VN], int e) {
 #pragma unroll
-      for (int k = 0; k < VN; ++k) {
-        const uint32_t key = float_key(x[k], sizeof(T) == 2);
-        const bool in = (base + j * kFilterThreads * VN + k < V) && key >= lo &&
-                        (high >= 32 || (key >> high) == prefix);
-        if (in) {
-          const int bin = (key >> shift) & 255;
-          atomicAdd(&w_cnt[wave][bin], 1u);
-          if (kMass) atomicAdd(&w_mass[wave][bin], fixed40(exp2_dev(__builtin_fmaf(x[k], c, -mc))));
-        }
+    for (int k = 0; k < VN; ++k) {
+      const bool inb = kAligned ? e < V : e + k < V;
+      if (kAll) {
+        const uint32_t bin = __builtin_amdgcn_ubfe(key32_of(x[k]), shift, width);
+        unsigned long long v;
+        if (kMass) v = fixed40(exp2_dev(__builtin_fmaf(x[k], c, -mc)));
+        else v = 1ull;
+        atomicAdd(&h[bin], inb ? v : 0ull);
+      } else if (inb && x[k] >= flo && x[k] <= fhi) {
+        const uint32_t bin = __builtin_amdgcn_ubfe(key32_of(x[k]), shift, width);
+        if (kMass) atomicAdd(&h[bin], fixed40(exp2_dev(__builtin_fmaf(x[k], c, -mc))));
+        else atomicAdd(&h[bin], 1ull);
       }
     }
-  }
-  __syncthreads();
-  if (tid < 256) {
-    unsigned cn = 0u;
-    unsigned long long ms = 0ull;
-    for (int w = 0; w < kFilterWaves; ++w) {
-      cn += w_cnt[w][tid];
-      if (kMass) ms += w_mass[w][tid];
-    }
-    h_cnt[tid] = cn;
-    h_mass[tid] = ms;
-  }
+  });
   __syncthreads();
 }
 
-// The mass of the entries with key >= lo, in 40-bit fixed point: per-thread
+// bf16 rows, last pass: inside the chosen 12-bit bin (flo <= x <= fhi) each
+// of the 16 bins is one bf16 value, so counts suffice: the mass of a bin is
+// its count times the value's weight, the same integer as the sum of the
+// entries' weights.  bin = low 4 bits of the value's key, i.e. of the bf16
+// bits, complemented for negative values (flip = 15).  With kAbove each
+// thread also sums the weights of the entries above the bin (x > fhi).
+template <bool kAligned, bool kAbove>
+__device__ __forceinline__ unsigned long long filter_hist_exact(const uint16_t* __restrict__ row,
+                                                                int V, float c, float mc,
+                                                                float flo, float fhi, uint32_t flip,
+                                                                unsigned long long* h) {
+  constexpr int VN = Vec16<uint16_t>::N;
+  if (threadIdx.x < 16) h[threadIdx.x] = 0ull;
+  __syncthreads();
+  unsigned long long above = 0ull;
+  filter_scan<uint16_t, kAligned>(row, V, [&](const float (&x)[VN], int e) {
+#pragma unroll
+    for (int k = 0; k < VN; ++k) {
+      const bool inb = kAligned ? e < V : e + k < V;
+      if (inb && x[k] >= flo && x[k] <= fhi)
+        atomicAdd(&h[__builtin_amdgcn_ubfe(__float_as_uint(x[k]), 16, 4) ^ flip], 1ull);
+      if (kAbove && inb && x[k] > fhi) above += fixed40(exp2_dev(__builtin_fmaf(x[k], c, -mc)));
+    }
+  });
+  __syncthreads();
+  return above;
+}
+
+// The bf16 value with 16-bit key k, widened.
+__device__ __forceinline__ float key16_value(uint32_t k) {
+  const uint32_t hb = (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
+  return __uint_as_float(hb << 16);
+}
+
+// Block sum of one integer per thread (exact in any order).
+__device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v,
+                                                            unsigned long long* s_red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  __syncthreads();
+  if (lane == 0) s_red[wave] = v;
+  __syncthreads();
+  unsigned long long tot = 0ull;
+#pragma unroll
+  for (int w = 0; w < kFilterWaves; ++w) tot += s_red[w];
+  __syncthreads();
+  return tot;
+}
+
+// The block picks the largest bin whose running total from the top, plus
+// the total `above` carried from the higher digits, reaches `target`; it
+// adds the totals of the bins above the pick to `above`.  If no bin reaches
+// (only by rounding), the lowest nonempty bin.  Thread t holds bins
+// 4t .. 4t + 3.  All threads return the same values.
+__device__ __forceinline__ int filter_pick(const unsigned long long* h, int nbins, double target,
+                                           unsigned long long& above, unsigned long long* s_w,
+                                           int* s_pick, unsigned long long* s_above) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  unsigned long long v[4], loc = 0ull;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    v[k] = (4 * tid + k < nbins) ? h[4 * tid + k] : 0ull;
+    loc += v[k];
+  }
+  // Inclusive suffix sums over the lanes of a wave (lanes l..63), then over
+  // the waves above.
+  unsigned long long suf = loc;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned long long t = __shfl_down(suf, off, 64);
+    if (lane + off < 64) suf += t;
+  }
+  if (lane == 0) s_w[wave] = suf;                  // the wave's total
+  __syncthreads();
+  unsigned long long wabove = 0ull;
+  for (int w = wave + 1; w < kFilterWaves; ++w) wabove += s_w[w];
+  unsigned long long acc = above + wabove + (suf - loc);   // everything above this thread's bins
+  int hit = -1, nonempty = 1 << 30;
+#pragma unroll
+  for (int k = 3; k >= 0; --k) {
+    acc += v[k];
+    if (hit < 0 && (double)acc >= target) hit = 4 * tid + k;
+    if (v[k]) nonempty = 4 * tid + k;
+  }
+  // Block max of hit, block min of nonempty.
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    hit = max(hit, __shfl_xor(hit, off, 64));
+    nonempty = min(nonempty, __shfl_xor(nonempty, off, 64));
+  }
+  if (lane == 0) { s_pick[wave] = hit; s_pick[kFilterWaves + wave] = nonempty; }
+  __syncthreads();
+  int sel = -1, ne = 1 << 30;
+  for (int w = 0; w < kFilterWaves; ++w) { sel = max(sel, s_pick[w]); ne = min(ne, s_pick[kFilterWaves + w]); }
+  if (sel < 0) sel = ne < nbins ? ne : 0;
+  // The owner of bin sel knows the total above it.
+  if (tid == (sel >> 2)) {
+    unsigned long long ab = above + wabove + (suf - loc);
+#pragma unroll
+    for (int k = 3; k >= 0; --k)
+      if (4 * tid + k > sel) ab += v[k];
+    *s_above = ab;
+  }
+  __syncthreads();
+  above = *s_above;
+  __syncthreads();
+  return sel;
+}
+
+// The mass of the entries with x >= flo, in 40-bit fixed point: per-thread
 // sums, then a block sum (integers: exact in any order).
 template <typename T, bool kAligned>
 __device__ __forceinline__ unsigned long long filter_kept_mass(const T* __restrict__ row, int V,
-                                                               float c, float mc, uint32_t lo,
+                                                               float c, float mc, float flo,
                                                                unsigned long long* s_red) {
   constexpr int VN = Vec16<T>::N;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   unsigned long long acc = 0ull;
-  for (int base = tid * VN; base < V; base += kFilterThreads * VN * filter_batch<T>()) {
-    u32x4_t raw[filter_batch<T>()];
+  filter_scan<T, kAligned>(row, V, [&](const float (&x)[VN], int e) {
 #pragma unroll
-    for (int j = 0; j < filter_batch<T>(); ++j) {
-      const int e = base + j * kFilterThreads * VN;
-      raw[j] = kAligned ? load_raw<T>(row, e, V) : load_raw_unaligned<T>(row, e, V);
+    for (int k = 0; k < VN; ++k) {
+      const bool inb = kAligned ? e < V : e + k < V;
+      if (inb && x[k] >= flo) acc += fixed40(exp2_dev(__builtin_fmaf(x[k], c, -mc)));
     }
-#pragma unroll
-    for (int j = 0; j < filter_batch<T>(); ++j) {
-      float x[VN];
-      widen_raw<T>(raw[j], x);
-#pragma unroll
-      for (int k = 0; k < VN; ++k) {
-        const bool in = (base + j * kFilterThreads * VN + k < V) &&
-                        float_key(x[k], sizeof(T) == 2) >= lo;
-        acc += in ? fixed40(exp2_dev(__builtin_fmaf(x[k], c, -mc))) : 0ull;
-      }
-    }
-  }
+  });
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
   __syncthreads();
@@ -537,62 +682,8 @@ __device__ __forceinline__ unsigned long long filter_kept_mass(const T* __restri
   unsigned long long tot = 0ull;
 #pragma unroll
   for (int w = 0; w < kFilterWaves; ++w) tot += s_red[w];
+  __syncthreads();
   return tot;
-}
-
-// Wave 0: the largest bin whose running total from the top (plus the totals
-// carried in above_cnt / above_mass from the higher bits) reaches `target`,
-// by count or by mass; adds the totals of the bins above it to the carries.
-// If no bin reaches (only by rounding), the lowest nonempty bin.
-__device__ __forceinline__ int filter_pick(const unsigned* h_cnt, const unsigned long long* h_mass,
-                                           bool by_mass, double target, unsigned long long& above_cnt,
-                                           unsigned long long& above_mass, int lane) {
-  unsigned long long c[4], m[4], lc = 0, lm = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {                    // lane l holds bins 4l .. 4l + 3
-    c[k] = h_cnt[4 * lane + k];
-    m[k] = h_mass[4 * lane + k];
-    lc += c[k];
-    lm += m[k];
-  }
-  unsigned long long sc = lc, sm = lm;             // inclusive sums over lanes l..63
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const unsigned long long tc = __shfl_down(sc, off, 64);
-    const unsigned long long tm = __shfl_down(sm, off, 64);
-    if (lane + off < 64) { sc += tc; sm += tm; }
-  }
-  int hit = -1, nonempty = 256;
-  unsigned long long ac = above_cnt + sc - lc, am = above_mass + sm - lm;   // bins above this lane
-#pragma unroll
-  for (int k = 3; k >= 0; --k) {
-    ac += c[k];
-    am += m[k];
-    if (hit < 0 && (by_mass ? (double)am : (double)ac) >= target) hit = 4 * lane + k;
-    if (c[k]) nonempty = 4 * lane + k;
-  }
-  int sel = hit;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) sel = max(sel, __shfl_xor(sel, off, 64));
-  if (sel < 0) {
-    sel = nonempty;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) sel = min(sel, __shfl_xor(sel, off, 64));
-    if (sel > 255) sel = 0;
-  }
-  // Totals of the bins above sel.
-  unsigned long long xc = 0, xm = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    if (4 * lane + k > sel) { xc += c[k]; xm += m[k]; }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    xc += __shfl_xor(xc, off, 64);
-    xm += __shfl_xor(xm, off, 64);
-  }
-  above_cnt += xc;
-  above_mass += xm;
-  return sel;
 }
 
 template <typename T, bool kAligned>
@@ -600,14 +691,12 @@ __global__ __launch_bounds__(kFilterThreads) void k_filter(
     const T* __restrict__ tgt, const T* __restrict__ drf, const float* __restrict__ temp,
     const int32_t* __restrict__ top_k, const float* __restrict__ top_p, int K, int V, int nc,
     int force_greedy, const float2* __restrict__ part, RowFilter* __restrict__ filt) {
-  __shared__ unsigned w_cnt[kFilterWaves][256];
-  __shared__ unsigned long long w_mass[kFilterWaves][256];
-  __shared__ unsigned h_cnt[256];
-  __shared__ unsigned long long h_mass[256];
+  __shared__ unsigned long long h[kFilterBins];
+  __shared__ unsigned long long s_w[kFilterWaves];
+  __shared__ int s_pick[2 * kFilterWaves];
+  __shared__ unsigned long long s_above;
+  __shared__ unsigned long long s_wt[16];
   __shared__ float s_xr;
-  __shared__ int s_sel;
-  __shared__ unsigned long long s_ac, s_am;
-  __shared__ unsigned long long s_red[kFilterWaves];
   const int R = 2 * K + 1;
   const int row = blockIdx.x;
   const int b = row / R;
@@ -635,48 +724,98 @@ __global__ __launch_bounds__(kFilterThreads) void k_filter(
   }
   __syncthreads();
   const float mc = s_xr * c;
-  constexpr int kBits = sizeof(T) == 2 ? 16 : 32;
-  uint32_t lo = 0u;                                // keys below this are filtered out
+  // Keys are handled in the 32-bit space of the widened floats; a bf16 key
+  // is the top 16 bits, so its passes stop at bit 16.
+  constexpr int kStop = sizeof(T) == 2 ? 16 : 0;
+  uint32_t lo = 0u;                                // 32-bit keys below this are filtered out
   unsigned long long kept_mass = 0ull;
   bool have_mass = false;
   for (int f = 0; f < 2; ++f) {
     const bool by_mass = (f == 1);
     if (by_mass ? !p_on : !k_on) continue;
     uint32_t prefix = 0u;
-    unsigned long long ac = 0ull, am = 0ull;
+    unsigned long long above = 0ull;
     double target = by_mass ? 0.0 : (double)tk;
-    for (int shift = kBits - 8; shift >= 0; shift -= 8) {
-      if (by_mass)
-        filter_hist<T, kAligned, true>(src, V, c, mc, lo, prefix, shift, w_cnt, w_mass, h_cnt, h_mass);
-      else
-        filter_hist<T, kAligned, false>(src, V, c, mc, lo, prefix, shift, w_cnt, w_mass, h_cnt, h_mass);
-      if (wave == 0) {
-        if (by_mass && shift == kBits - 8) {
-          // The kept set's mass (all of the row, or its top-k set) sets the target.
-          unsigned long long tot = 0ull;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) tot += h_mass[4 * lane + k];
-#pragma unroll
-          for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off, 64);
-          target = (double)tp * (double)tot;
+    int shift = 32;
+    for (int lv = 0; lv < filter_levels<T>(); ++lv) {
+      const int width = digit_bits<T>(lv);
+      const int high = shift;                      // the bits above `high` are fixed: prefix
+      shift -= width;
+      if constexpr (sizeof(T) == 2) {
+        if (lv == 1) {
+          // One bf16 value per bin: counts, then masses from the counts.
+          float flo, fhi;
+          key_bounds(max(prefix << high, lo),
+                     (uint32_t)((((unsigned long long)prefix + 1) << high) - 1), flo, fhi);
+          const uint32_t flip = (prefix & 0x800u) ? 0u : 15u;
+          const bool need_above = !by_mass && !p_on;
+          unsigned long long ab = 0ull;
+          if (need_above) ab = filter_hist_exact<kAligned, true>(src, V, c, mc, flo, fhi, flip, h);
+          else filter_hist_exact<kAligned, false>(src, V, c, mc, flo, fhi, flip, h);
+          if (need_above) ab = block_sum_u64(ab, s_w);
+          if (tid < 16) {
+            const float xv = key16_value((prefix << 4) | (uint32_t)tid);
+            const unsigned long long w = fixed40(exp2_dev(__builtin_fmaf(xv, c, -mc)));
+            if (by_mass) h[tid] *= w;
+            else s_wt[tid] = w;
+          }
+          __syncthreads();
+          const int sel = filter_pick(h, 16, target, above, s_w, s_pick, &s_above);
+          prefix = (prefix << 4) | (uint32_t)sel;
+          if (by_mass) {
+            kept_mass = above + h[sel];
+          } else if (need_above) {
+            // Top-k alone: the mass of the kept set, {x > bin} plus the
+            // values of the bin from sel up.
+            unsigned long long m = ab;
+            for (int i = sel; i < 16; ++i) m += h[i] * s_wt[i];
+            kept_mass = m;
+            have_mass = true;
+          }
+          __syncthreads();
+          continue;
         }
-        const int sel = filter_pick(h_cnt, h_mass, by_mass, target, ac, am, lane);
-        if (lane == 0) { s_sel = sel; s_ac = ac; s_am = am; }
       }
-      __syncthreads();
-      const int sel = s_sel;
-      ac = s_ac;
-      am = s_am;
-      prefix = (prefix << 8) | (uint32_t)sel;
-      if (by_mass && shift == 0) kept_mass = am + h_mass[sel];
+      if (lv == 0 && lo == 0u) {
+        if (by_mass) filter_hist<T, kAligned, true, true>(src, V, c, mc, 0.f, 0.f, shift, width, h);
+        else filter_hist<T, kAligned, false, true>(src, V, c, mc, 0.f, 0.f, shift, width, h);
+      } else {
+        const uint32_t klo = high >= 32 ? 0u : prefix << high;
+        const uint32_t khi = high >= 32 ? 0xFFFFFFFFu
+                                        : (uint32_t)((((unsigned long long)prefix + 1) << high) - 1);
+        float flo, fhi;
+        key_bounds(max(klo, lo), khi, flo, fhi);
+        if (by_mass) filter_hist<T, kAligned, true, false>(src, V, c, mc, flo, fhi, shift, width, h);
+        else filter_hist<T, kAligned, false, false>(src, V, c, mc, flo, fhi, shift, width, h);
+      }
+      if (by_mass && lv == 0) {
+        // The kept set's mass (all of the row, or its top-k set) sets the target.
+        unsigned long long part_sum = 0ull;
+        for (int i = tid; i < kFilterBins; i += kFilterThreads) part_sum += h[i];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) part_sum += __shfl_xor(part_sum, off, 64);
+        if (lane == 0) s_w[wave] = part_sum;
+        __syncthreads();
+        unsigned long long tot = 0ull;
+        for (int w = 0; w < kFilterWaves; ++w) tot += s_w[w];
+        __syncthreads();
+        target = (double)tp * (double)tot;
+      }
+      const int sel = filter_pick(h, 1 << width, target, above, s_w, s_pick, &s_above);
+      prefix = (prefix << width) | (uint32_t)sel;
+      if (by_mass && shift == kStop) kept_mass = above + h[sel];
       __syncthreads();
     }
-    lo = prefix;                                   // the k-th largest key, or the top-p key
-    have_mass = by_mass;
+    lo = prefix << kStop;                          // the k-th largest key, or the top-p key
+    have_mass = have_mass || by_mass;
   }
   // Top-k alone: the kept set's mass in one more pass (top-p's passes give it).
-  if (!have_mass) kept_mass = filter_kept_mass<T, kAligned>(src, V, c, mc, lo, s_red);
-  if (tid == 0) filt[row] = RowFilter{lo, 0u, (double)kept_mass / kFix};
+  if (!have_mass) {
+    float flo, fhi;
+    key_bounds(lo, 0xFFFFFFFFu, flo, fhi);
+    kept_mass = filter_kept_mass<T, kAligned>(src, V, c, mc, flo, s_w);
+  }
+  if (tid == 0) filt[row] = RowFilter{lo >> kStop, 0u, (double)kept_mass / kFix};
 }
 
 // ---------------------------------------------------------------------------
