@@ -38,6 +38,17 @@
  *  - Out-of-range indices in the inputs (block ids, draft tokens) never
  *    make the kernels read outside the buffers described here: they are
  *    clamped, and the results for such inputs are unspecified.
+ *  - Validation mode: with SPECVERIFY_VALIDATE=1 in the environment (read
+ *    at every call) each compute call first waits for its stream, copies
+ *    its index, length, uniform, temperature and logit inputs to host
+ *    memory and checks the preconditions stated for it (page ids of every
+ *    page it touches in [0, num_blocks), lengths within capacity, tokens in
+ *    [0, V), uniforms in [0, 1), finite temperatures and top-p values,
+ *    logits without NaN or +inf and with a finite entry per row).  The
+ *    first violation is printed to stderr and returned as SV_ERR_BAD_INPUT
+ *    before anything is launched; after its launches the call waits for the
+ *    stream again, so a device error is returned (SV_ERR_HIP) by the call
+ *    that caused it.  A debugging aid: synchronous and slow.
  */
 #ifndef SPECVERIFY_H_
 #define SPECVERIFY_H_
@@ -55,7 +66,9 @@ typedef enum {
   SV_ERR_UNSUPPORTED = -2, /* a shape outside the supported set          */
   SV_ERR_WORKSPACE = -3,   /* workspace smaller than the *_workspace_bytes */
   SV_ERR_HIP = -4,         /* a HIP runtime call or launch failed         */
-  SV_ERR_NO_PAGES = -5     /* the page pool has too few free pages        */
+  SV_ERR_NO_PAGES = -5,    /* the page pool has too few free pages        */
+  SV_ERR_BAD_INPUT = -6    /* SPECVERIFY_VALIDATE=1: a device input breaks a
+                              precondition (message on stderr)            */
 } sv_status;
 
 typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;

@@ -34,7 +34,8 @@ _LIB = None
 SV_F32, SV_BF16 = 0, 1
 SV_WINDOW_READ, SV_WINDOW_APPEND = 0, 1
 STATUS = {0: "SV_OK", -1: "SV_ERR_INVALID_ARG", -2: "SV_ERR_UNSUPPORTED",
-          -3: "SV_ERR_WORKSPACE", -4: "SV_ERR_HIP", -5: "SV_ERR_NO_PAGES"}
+          -3: "SV_ERR_WORKSPACE", -4: "SV_ERR_HIP", -5: "SV_ERR_NO_PAGES",
+          -6: "SV_ERR_BAD_INPUT"}
 EXPORTS = ("spec_verify_attn", "spec_verify_attn_workspace_bytes", "spec_verify_attn_tree",
            "spec_verify_attn_window", "spec_kv_commit",
            "spec_reject_sample", "spec_reject_sample_workspace_bytes",

@@ -16,6 +16,7 @@
 // in place a destination can be the source of a later row.
 
 #include "common.h"
+#include "validate.h"
 
 namespace sv {
 
@@ -91,9 +92,16 @@ extern "C" int spec_kv_commit(void* k_cache, void* v_cache, const int32_t* block
   if (B == 0) return SV_OK;
   if (!k_cache || !v_cache || !block_table || !kv_len || !num_accepted) return SV_ERR_INVALID_ARG;
   if (Hkv > 65535) return SV_ERR_UNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const char* fn = "spec_kv_commit";
+  const bool chk = sv::validate_on();
+  if (chk) {
+    const int s = sv::check_commit(fn, block_table, kv_len, num_accepted, nodes, B, N, num_blocks,
+                                   max_blocks_per_seq, st);
+    if (s != SV_OK) return s;
+  }
   // A chain written in place is already where it belongs.
   if (!nodes && !k_src) return SV_OK;
-  hipStream_t st = static_cast<hipStream_t>(hip_stream);
   if (dtype == SV_BF16)
     hipLaunchKernelGGL(sv::k_kv_commit<uint16_t>, dim3(B, Hkv), dim3(sv::kCommitThreads), 0, st,
                        static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), block_table,
@@ -104,5 +112,6 @@ extern "C" int spec_kv_commit(void* k_cache, void* v_cache, const int32_t* block
                        static_cast<float*>(k_cache), static_cast<float*>(v_cache), block_table, kv_len,
                        num_accepted, nodes, static_cast<const float*>(k_src),
                        static_cast<const float*>(v_src), N, Hkv, D, num_blocks, max_blocks_per_seq);
-  return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+  const int status = hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP;
+  return chk ? sv::finish(fn, st, status) : status;
 }

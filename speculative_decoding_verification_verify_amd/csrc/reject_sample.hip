@@ -61,6 +61,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "validate.h"
 
 namespace sv {
 
@@ -1745,7 +1746,7 @@ extern "C" size_t spec_reject_sample_workspace_bytes(int B, int K, int V) {
   return sv::reject_plan(B, K, V).total;
 }
 
-static int reject_impl(const void* target_logits, const void* draft_logits,
+static int reject_impl(const char* fn, const void* target_logits, const void* draft_logits,
                        const int32_t* draft_tokens, const float* uniforms, const float* temperature,
                        const int32_t* top_k, const float* top_p, int32_t* out_tokens,
                        int32_t* num_accepted, int32_t* kv_len, unsigned long long* counters, int B,
@@ -1771,6 +1772,18 @@ static int reject_impl(const void* target_logits, const void* draft_logits,
   char* ws = static_cast<char*>(workspace);
   const uintptr_t align_bits = reinterpret_cast<uintptr_t>(target_logits) |
                                reinterpret_cast<uintptr_t>(drf);
+  const bool chk = sv::validate_on();
+  if (chk) {
+    int s = sv::check_tokens(fn, draft_tokens, (long long)B * K, V, K, 0, st);
+    if (s == SV_OK) s = sv::check_floats(fn, "uniforms", uniforms, (long long)B * (K + 1), true, st);
+    if (s == SV_OK) s = sv::check_floats(fn, "temperature", temperature, B, false, st);
+    if (s == SV_OK && top_p) s = sv::check_floats(fn, "top_p", top_p, B, false, st);
+    if (s == SV_OK)
+      s = sv::check_logits(fn, "target_logits", target_logits, (long long)B * (K + 1), V, dtype, st);
+    if (s == SV_OK && draft_logits)
+      s = sv::check_logits(fn, "draft_logits", draft_logits, (long long)B * K, V, dtype, st);
+    if (s != SV_OK) return s;
+  }
   hipError_t e;
   if (dtype == SV_BF16) {
     const bool al = (V % 8 == 0) && (align_bits & 15) == 0;
@@ -1789,7 +1802,8 @@ static int reject_impl(const void* target_logits, const void* draft_logits,
                                           out_tokens, num_accepted, kv_len, counters, B, K, V,
                                           force_greedy, ws, st, top_k, top_p);
   }
-  return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+  const int status = e == hipSuccess ? SV_OK : SV_ERR_HIP;
+  return chk ? sv::finish(fn, st, status) : status;
 }
 
 extern "C" int spec_reject_sample(const void* target_logits, const void* draft_logits,
@@ -1798,7 +1812,8 @@ extern "C" int spec_reject_sample(const void* target_logits, const void* draft_l
                                   int32_t* num_accepted, int32_t* kv_len,
                                   unsigned long long* counters, int B, int K, int V, int dtype,
                                   void* workspace, size_t workspace_bytes, void* hip_stream) {
-  return reject_impl(target_logits, draft_logits, draft_tokens, uniforms, temperature, nullptr,
+  return reject_impl("spec_reject_sample", target_logits, draft_logits, draft_tokens, uniforms,
+                     temperature, nullptr,
                      nullptr, out_tokens, num_accepted, kv_len, counters, B, K, V, dtype, workspace,
                      workspace_bytes, hip_stream);
 }
@@ -1811,7 +1826,8 @@ extern "C" int spec_reject_sample_filtered(const void* target_logits, const void
                                            unsigned long long* counters, int B, int K, int V,
                                            int dtype, void* workspace, size_t workspace_bytes,
                                            void* hip_stream) {
-  return reject_impl(target_logits, draft_logits, draft_tokens, uniforms, temperature, top_k, top_p,
+  return reject_impl("spec_reject_sample_filtered", target_logits, draft_logits, draft_tokens,
+                     uniforms, temperature, top_k, top_p,
                      out_tokens, num_accepted, kv_len, counters, B, K, V, dtype, workspace,
                      workspace_bytes, hip_stream);
 }
@@ -1849,6 +1865,18 @@ extern "C" int spec_reject_sample_tree(const void* target_logits, const void* dr
   char* ws = static_cast<char*>(workspace);
   const uintptr_t align_bits = reinterpret_cast<uintptr_t>(target_logits) |
                                reinterpret_cast<uintptr_t>(drf);
+  const char* fn = "spec_reject_sample_tree";
+  const bool chk = sv::validate_on();
+  if (chk) {
+    int s = sv::check_tokens(fn, tokens, (long long)B * N, V, N, 1, st);
+    if (s == SV_OK) s = sv::check_floats(fn, "uniforms", uniforms, (long long)B * N, true, st);
+    if (s == SV_OK) s = sv::check_floats(fn, "temperature", temperature, B, false, st);
+    if (s == SV_OK)
+      s = sv::check_logits(fn, "target_logits", target_logits, (long long)B * N, V, dtype, st);
+    if (s == SV_OK && draft_logits)
+      s = sv::check_logits(fn, "draft_logits", draft_logits, (long long)B * N, V, dtype, st);
+    if (s != SV_OK) return s;
+  }
   hipError_t e;
   if (dtype == SV_BF16) {
     const bool al = (V % 8 == 0) && (align_bits & 15) == 0;
@@ -1867,5 +1895,6 @@ extern "C" int spec_reject_sample_tree(const void* target_logits, const void* dr
                                            out_tokens, out_nodes, num_accepted, kv_len, counters, B, V,
                                            force_greedy, ws, st);
   }
-  return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+  const int status = e == hipSuccess ? SV_OK : SV_ERR_HIP;
+  return chk ? sv::finish(fn, st, status) : status;
 }

@@ -9,6 +9,7 @@ extern "C" const char* spec_status_string(int status) {
     case SV_ERR_WORKSPACE: return "workspace too small";
     case SV_ERR_HIP: return "HIP runtime error";
     case SV_ERR_NO_PAGES: return "out of KV pages";
+    case SV_ERR_BAD_INPUT: return "input breaks a precondition (validation mode)";
     default: return "unknown status";
   }
 }

@@ -40,6 +40,7 @@
 #include <atomic>
 
 #include "common.h"
+#include "validate.h"
 
 namespace sv {
 
@@ -989,7 +990,7 @@ static int verify_attn_impl(const void* q, void* k_cache, void* v_cache,
                             void* out, int B, int K, int Hq, int Hkv, int D, int block_size,
                             int num_blocks, int max_blocks_per_seq, int max_kv_len, float scale,
                             int dtype, void* workspace, size_t workspace_bytes, void* hip_stream,
-                            const WindowArgs& win = WindowArgs{nullptr, nullptr, 0}) {
+                            const WindowArgs& win, const char* fn) {
   if (B < 0 || K < 1 || Hq < 1 || Hkv < 1 || D < 1 || max_kv_len < 0 || num_blocks < 1 ||
       max_blocks_per_seq < 1)
     return SV_ERR_INVALID_ARG;
@@ -1007,16 +1008,8 @@ static int verify_attn_impl(const void* q, void* k_cache, void* v_cache,
   const float sl2 = sc * kLog2e;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const int K1 = K + 1;
-  hipError_t e;
-  if (dtype == SV_F32) {
-    hipLaunchKernelGGL(k_attn_valu, dim3(K1, Hq, B), dim3(64), 0, st,
-                       static_cast<const float*>(q), static_cast<float*>(k_cache),
-                       static_cast<float*>(v_cache), block_table, kv_len, anc,
-                       static_cast<float*>(out), K1, Hq, Hkv, D, num_blocks, max_blocks_per_seq, sl2,
-                       static_cast<const float*>(win.kn), static_cast<const float*>(win.vn), win.store);
-    e = hipGetLastError();
-  } else {
-    const AttnPlan p = attn_plan(B, K, Hq, Hkv, D, max_kv_len);
+  const AttnPlan p = attn_plan(B, K, Hq, Hkv, D, max_kv_len);
+  if (dtype == SV_BF16) {
     if (p.too_big) return SV_ERR_UNSUPPORTED;
     if (p.w_max > 1) {
       if (!workspace) return SV_ERR_INVALID_ARG;
@@ -1027,6 +1020,22 @@ static int verify_attn_impl(const void* q, void* k_cache, void* v_cache,
                          reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(out) |
                          reinterpret_cast<uintptr_t>(win.kn) | reinterpret_cast<uintptr_t>(win.vn);
     if (al & 15) return SV_ERR_INVALID_ARG;
+  }
+  const bool chk = validate_on();
+  if (chk) {
+    const int s = check_pages(fn, block_table, kv_len, B, K1, num_blocks, max_blocks_per_seq,
+                              max_kv_len, st);
+    if (s != SV_OK) return s;
+  }
+  hipError_t e;
+  if (dtype == SV_F32) {
+    hipLaunchKernelGGL(k_attn_valu, dim3(K1, Hq, B), dim3(64), 0, st,
+                       static_cast<const float*>(q), static_cast<float*>(k_cache),
+                       static_cast<float*>(v_cache), block_table, kv_len, anc,
+                       static_cast<float*>(out), K1, Hq, Hkv, D, num_blocks, max_blocks_per_seq, sl2,
+                       static_cast<const float*>(win.kn), static_cast<const float*>(win.vn), win.store);
+    e = hipGetLastError();
+  } else {
     char* ws = static_cast<char*>(workspace);
     if (D == 128) {
       e = p.tiles == 1 ? launch_stream<128, 1>(q, k_cache, v_cache, block_table, kv_len, anc, out, B,
@@ -1040,7 +1049,8 @@ static int verify_attn_impl(const void* q, void* k_cache, void* v_cache,
                                               K1, Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, win, st);
     }
   }
-  return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+  const int status = e == hipSuccess ? SV_OK : SV_ERR_HIP;
+  return chk ? finish(fn, st, status) : status;
 }
 
 }  // namespace sv
@@ -1053,7 +1063,8 @@ extern "C" int spec_verify_attn(const void* q, const void* k_cache, const void* 
   return sv::verify_attn_impl(q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), block_table,
                               kv_len, nullptr, out, B, K, Hq, Hkv,
                               D, block_size, num_blocks, max_blocks_per_seq, max_kv_len, scale, dtype,
-                              workspace, workspace_bytes, hip_stream);
+                              workspace, workspace_bytes, hip_stream,
+                              sv::WindowArgs{nullptr, nullptr, 0}, "spec_verify_attn");
 }
 
 extern "C" int spec_verify_attn_tree(const void* q, const void* k_cache, const void* v_cache,
@@ -1067,7 +1078,8 @@ extern "C" int spec_verify_attn_tree(const void* q, const void* k_cache, const v
   return sv::verify_attn_impl(q, const_cast<void*>(k_cache), const_cast<void*>(v_cache), block_table,
                               kv_len, anc, out, B, N - 1, Hq, Hkv,
                               D, block_size, num_blocks, max_blocks_per_seq, max_kv_len, scale, dtype,
-                              workspace, workspace_bytes, hip_stream);
+                              workspace, workspace_bytes, hip_stream,
+                              sv::WindowArgs{nullptr, nullptr, 0}, "spec_verify_attn_tree");
 }
 
 extern "C" int spec_verify_attn_window(const void* q, const void* k_new, const void* v_new,
@@ -1083,5 +1095,6 @@ extern "C" int spec_verify_attn_window(const void* q, const void* k_new, const v
   return sv::verify_attn_impl(q, k_cache, v_cache, block_table, kv_len, anc, out, B, N - 1, Hq, Hkv, D,
                               block_size, num_blocks, max_blocks_per_seq, max_kv_len, scale, dtype,
                               workspace, workspace_bytes, hip_stream,
-                              sv::WindowArgs{k_new, v_new, mode == SV_WINDOW_APPEND ? 1 : 0});
+                              sv::WindowArgs{k_new, v_new, mode == SV_WINDOW_APPEND ? 1 : 0},
+                              "spec_verify_attn_window");
 }

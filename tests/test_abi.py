@@ -40,6 +40,7 @@ def test_exports_every_declared_symbol(lib):
 def test_status_strings_and_version(lib):
     assert lib.spec_status_string(0) == b"ok"
     assert lib.spec_status_string(-3) == b"workspace too small"
+    assert lib.spec_status_string(-6) == b"input breaks a precondition (validation mode)"
     assert lib.spec_status_string(99) == b"unknown status"
     assert lib.spec_version() >= 100
 
