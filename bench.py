@@ -69,6 +69,9 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="llama8b_b64")
+    p.add_argument("--batch", type=int, default=0,
+                   help="batch size instead of the workload's (e.g. the low-concurrency sweep "
+                        "1, 2, 4, 8); 0: the workload's")
     p.add_argument("--temp", type=float, default=1.0)
     p.add_argument("--seed", type=int, default=2024)
     p.add_argument("--cpu-sample", type=int, default=64,
@@ -117,7 +120,7 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     cfg = CONFIGS[args.config]
-    B, K, V = cfg.B, cfg.K, cfg.V
+    B, K, V = (args.batch or cfg.B), cfg.K, cfg.V
     parent = None
     if args.tree:
         from oracle.tree import tree_parents, tree_masks
@@ -366,7 +369,8 @@ def cpu_baseline(args, cfg, attn, host_rej, from_device, parent=None):
         blas_threads = 1
     K1 = cfg.K + 1 if parent is None else len(parent)
     # The tree oracle's attention masks every node separately: a smaller sample.
-    n = min(args.cpu_sample if parent is None else max(1, args.cpu_sample // 8), cfg.B)
+    B = args.batch or cfg.B
+    n = min(args.cpu_sample if parent is None else max(1, args.cpu_sample // 8), B)
     idx = np.arange(n)
     kvl = from_device(attn["kv_len"])[:n]
     bt = from_device(attn["block_table"])[:n]
@@ -406,7 +410,7 @@ def cpu_baseline(args, cfg, attn, host_rej, from_device, parent=None):
             "cores": int(blas_threads), "kind": "oracle",
             "sample": "first %d of %d sequences of the same workload (attention + reject), %d "
                       "pass(es): float64 numpy oracle, attention %.2f s + reject %.2f s" %
-                      (n, cfg.B, passes, t_attn, t_rej),
+                      (n, B, passes, t_attn, t_rej),
             "host_cores_available": len(os.sched_getaffinity(0))}
 
 

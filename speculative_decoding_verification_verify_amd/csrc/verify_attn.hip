@@ -63,7 +63,7 @@ constexpr int kStreamMaxWG = 1024;   // workspace is sized for this many workgro
 #define SV_ATTN_NT_LOADS 1      // nontemporal K/V loads: streamed once, keep them out of L2
 #endif
 #ifndef SV_ATTN_MIN_PAIRS_PER_WG
-#define SV_ATTN_MIN_PAIRS_PER_WG 4
+#define SV_ATTN_MIN_PAIRS_PER_WG 16
 #endif
 #ifndef SV_ATTN_LAZY
 #define SV_ATTN_LAZY 8.0f       // rescale O only when the row max grows by > 2^8
@@ -731,16 +731,28 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the segments that span several workgroups.  grid (Hkv, B), block
-// 256: row = tid / 8, D/8 d's per thread.  Shares are visited in order.
+// Merge of the segments that span several workgroups.  grid (Hkv, B, z),
+// block 256: TPR threads per row, each with D / TPR of the coordinates,
+// 256 / TPR rows per block pass; the z blocks of a segment take every z-th
+// group of rows.  Two shapes: with enough segments to fill the chip (short
+// spans of partials) 8 threads per row, all rows in one pass, z = 1; with
+// few segments (long spans) D/4 threads per row and the rows spread over
+// blocks.  One pass over the partials in share order with a running
+// maximum: each thread requests the next NB partials before it adds the
+// current ones, rescales its sums when a batch raises the maximum and adds
+// the batch in order, so the result does not depend on the launch shape.
 // ---------------------------------------------------------------------------
-template <int D, int NT>
+template <int D, int NT, int TPR, int NB>
 __global__ __launch_bounds__(kCombineThreads) void k_attn_stream_combine(
     const float* __restrict__ opart, const float2* __restrict__ ml, const int32_t* __restrict__ kv_len,
     uint16_t* __restrict__ out, int B, int K1, int Hq, int Hkv, int np_cap, int W) {
   constexpr int ROWS = 32 * NT;
-  constexpr int DPT = D / 8;
+  constexpr int DPT = D / TPR;                  // coordinates per thread
+  constexpr int NV = DPT / 4;                   // float4 per partial per thread
+  constexpr int RPB = kCombineThreads / TPR;
+  static_assert(DPT % 4 == 0, "whole float4 per thread");
   __shared__ long long s_red[kCombineThreads / 64];
+  __shared__ int s_slot[kStreamMaxWG];
   const int g = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x;
   long long tot = 0, before = 0;
@@ -757,44 +769,82 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_stream_combine(
   if (wa == wb) return;                       // written whole by its workgroup
   const int G = Hq / Hkv;
   const int rows = G * K1;
-  const int d0 = (tid & 7) * DPT;
-  for (int row = tid >> 3; row < ROWS; row += kCombineThreads / 8) {
-    if (row >= rows) break;
-    float m = -INFINITY;
-    for (int ww = wa; ww <= wb; ++ww) {
-      if (stream_start(ww, U, W) >= stream_start(ww + 1, U, W)) continue;   // empty share
-      const int slot = (ww == wa && stream_start(wa, U, W) != ua) ? 1 : 0;
-      m = fmaxf(m, ml[((size_t)ww * 2 + slot) * ROWS + row].x);
-    }
-    const float mu = (m == -INFINITY) ? 0.f : m;
-    float lsum = 0.f;
+  const int d0 = (tid % TPR) * DPT;
+  // The partial slot of each share of the segment (slot 1 for a first share
+  // that starts inside it), -1 for an empty share.
+  const int nparts = wb - wa + 1;
+  for (int k = tid; k < nparts; k += kCombineThreads) {
+    const int ww = wa + k;
+    const long long s0 = stream_start(ww, U, W);
+    s_slot[k] = s0 >= stream_start(ww + 1, U, W) ? -1 : ww * 2 + ((k == 0 && s0 != ua) ? 1 : 0);
+  }
+  __syncthreads();
+  for (int row = blockIdx.z * RPB + tid / TPR; row < rows; row += gridDim.z * RPB) {
+    float m = -INFINITY, lsum = 0.f;
     float acc[DPT];
 #pragma unroll
     for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
-    for (int ww = wa; ww <= wb; ++ww) {
-      if (stream_start(ww, U, W) >= stream_start(ww + 1, U, W)) continue;
-      const int slot = (ww == wa && stream_start(wa, U, W) != ua) ? 1 : 0;
-      const size_t idx = ((size_t)ww * 2 + slot) * ROWS + row;
-      const float2 st = ml[idx];
-      const float f = exp2_dev(st.x - mu);
-      lsum += st.y * f;
-      const float* pp = opart + idx * D + d0;
+    // Batches of NB partials in two register buffers; the next batch is
+    // requested before the current one is added.
+    float2 sa[NB], sb[NB];
+    float4 va[NB][NV], vb[NB][NV];
+    auto fetch = [&](int k0, float2 (&st)[NB], float4 (&v)[NB][NV]) {
 #pragma unroll
-      for (int e = 0; e < DPT; e += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(pp + e);
-        acc[e] += v.x * f; acc[e + 1] += v.y * f; acc[e + 2] += v.z * f; acc[e + 3] += v.w * f;
+      for (int j = 0; j < NB; ++j) {
+        st[j].x = -INFINITY;                      // weight 0 unless loaded below
+        const int sl = k0 + j < nparts ? s_slot[k0 + j] : -1;
+        if (sl >= 0) {
+          const size_t ix = (size_t)sl * ROWS + row;
+          st[j] = ml[ix];
+          const float4* pp = reinterpret_cast<const float4*>(opart + ix * D + d0);
+#pragma unroll
+          for (int q = 0; q < NV; ++q) v[j][q] = pp[q];
+        }
       }
+    };
+    auto add = [&](const float2 (&st)[NB], const float4 (&v)[NB][NV]) {
+      float mb = m;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) mb = fmaxf(mb, st[j].x);
+      if (mb > m) {                               // a larger maximum: rescale the sums
+        const float r = exp2_dev(m - mb);         // 0 while nothing was added
+        lsum *= r;
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) acc[e] *= r;
+        m = mb;
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if (st[j].x == -INFINITY) continue;       // empty share, or no visible key
+        const float f = exp2_dev(st[j].x - m);
+        lsum += st[j].y * f;
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+          acc[4 * q] += v[j][q].x * f; acc[4 * q + 1] += v[j][q].y * f;
+          acc[4 * q + 2] += v[j][q].z * f; acc[4 * q + 3] += v[j][q].w * f;
+        }
+      }
+    };
+    fetch(0, sa, va);
+    for (int k0 = 0; k0 < nparts; k0 += 2 * NB) {
+      if (k0 + NB < nparts) fetch(k0 + NB, sb, vb);
+      add(sa, va);
+      if (k0 + NB >= nparts) break;
+      if (k0 + 2 * NB < nparts) fetch(k0 + 2 * NB, sa, va);
+      add(sb, vb);
     }
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     const int hq = row / K1, i = row - hq * K1;
     uint16_t* op = out + (((size_t)b * K1 + i) * Hq + (size_t)g * G + hq) * D + d0;
 #pragma unroll
-    for (int e = 0; e < DPT; e += 2) {
-      const __bf16 lo = (__bf16)(acc[e] * inv);
-      const __bf16 hi = (__bf16)(acc[e + 1] * inv);
-      const uint32_t wd = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-      *reinterpret_cast<uint32_t*>(op + e) = wd;
+    for (int e = 0; e < DPT; e += 4) {
+      const __bf16 o0 = (__bf16)(acc[e] * inv), o1 = (__bf16)(acc[e + 1] * inv);
+      const __bf16 o2 = (__bf16)(acc[e + 2] * inv), o3 = (__bf16)(acc[e + 3] * inv);
+      const uint32_t w01 = (uint32_t)__builtin_bit_cast(uint16_t, o0) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, o1) << 16);
+      const uint32_t w23 = (uint32_t)__builtin_bit_cast(uint16_t, o2) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, o3) << 16);
+      *reinterpret_cast<uint2*>(op + e) = make_uint2(w01, w23);
     }
   }
 }
@@ -957,9 +1007,20 @@ static hipError_t launch_stream_t(const void* q, void* kc, void* vc, const int32
                      K1, Hq, Hkv, num_blocks, mbps, p.np_cap, sl2, W, opart, ml,
                      static_cast<const uint16_t*>(win.kn), static_cast<const uint16_t*>(win.vn),
                      win.store);
-  if (W > 1)
-    hipLaunchKernelGGL((k_attn_stream_combine<D, NT>), dim3(Hkv, B), dim3(kCombineThreads), 0, st, opart,
-                       ml, kv_len, static_cast<uint16_t*>(out), B, K1, Hq, Hkv, p.np_cap, W);
+  if (W > 1) {
+    const int rows = (Hq / Hkv) * K1;
+    if ((long long)B * Hkv >= device_cus()) {
+      hipLaunchKernelGGL((k_attn_stream_combine<D, NT, 8, 2>), dim3(Hkv, B, 1), dim3(kCombineThreads),
+                         0, st, opart, ml, kv_len, static_cast<uint16_t*>(out), B, K1, Hq, Hkv,
+                         p.np_cap, W);
+    } else {
+      // Few segments, each spread over many workgroups: rows over blocks too.
+      constexpr int rpb = kCombineThreads / (D / 4);
+      hipLaunchKernelGGL((k_attn_stream_combine<D, NT, D / 4, 8>), dim3(Hkv, B, (rows + rpb - 1) / rpb),
+                         dim3(kCombineThreads), 0, st, opart, ml, kv_len, static_cast<uint16_t*>(out), B,
+                         K1, Hq, Hkv, p.np_cap, W);
+    }
+  }
   return hipGetLastError();
 }
 
