@@ -420,7 +420,7 @@ __device__ __forceinline__ void emit(int b, int K, int n, int tok, const int* __
 }
 
 // ---------------------------------------------------------------------------
-// k_filter: grid (B * (2K+1)), block 1024: the top-k / top-p thresholds of one
+// k_filter: grid (B * (2K+1)), block 512 (two per CU): the top-k / top-p thresholds of one
 // row by radix selection over its order keys, most significant digit first:
 // 12 bits, then 4 (bf16) or 12 and 8 (fp32).  Each pass histograms the
 // entries that match the digits chosen so far into up to 4096 bins of counts
@@ -436,9 +436,10 @@ __device__ __forceinline__ void emit(int b, int K, int n, int tok, const int* __
 // order of the adds (bitwise reproducible) and are exact to ~1e-7 of the
 // row's mass.
 // ---------------------------------------------------------------------------
-constexpr int kFilterThreads = 1024;
+constexpr int kFilterThreads = 512;
 constexpr int kFilterWaves = kFilterThreads / 64;
 constexpr int kFilterBins = 4096;
+static_assert(kFilterBins % kFilterThreads == 0, "whole bins per thread in filter_pick");
 constexpr double kFix = 1099511627776.0;          // 2^40
 
 // 16-byte vectors per batch of a thread (two batches are in registers at
@@ -483,10 +484,11 @@ __device__ __forceinline__ void key_bounds(uint32_t klo, uint32_t khi, float& fl
   fhi = key_value(khi);
 }
 
-// Streams a row through f(x, e, inb): x the VN widened logits of the vector
-// at entry e, inb whether entry k is below V (per vector where rows are
-// aligned).  Each thread keeps two batches of filter_batch vectors: the
-// next batch is requested before the current one is used.
+// Streams a row through f(x, e): x the VN widened logits of the vector at
+// entry e (past V: -inf).  Each thread alternates between two named batches
+// of filter_batch vectors, requesting the next batch before it uses the
+// current one (no register copy between them, so no wait for the batch just
+// requested).
 template <typename T, bool kAligned, class F>
 __device__ __forceinline__ void filter_scan(const T* __restrict__ row, int V, F&& f) {
   constexpr int VN = Vec16<T>::N;
@@ -499,21 +501,24 @@ __device__ __forceinline__ void filter_scan(const T* __restrict__ row, int V, F&
       r[j] = kAligned ? load_raw<T>(row, e, V) : load_raw_unaligned<T>(row, e, V);
     }
   };
-  int base = threadIdx.x * VN;
-  if (base >= V) return;
-  u32x4_t cur[NB], nxt[NB];
-  fetch(cur, base);
-  for (; base < V; base += kStep) {
-    fetch(nxt, base + kStep);                      // past V: harmless, replaced by -inf
+  auto use = [&](const u32x4_t (&r)[NB], int base) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const int e = base + j * kFilterThreads * VN;
       float x[VN];
-      widen_raw<T>(cur[j], x);
-      f(x, e);
+      widen_raw<T>(r[j], x);
+      f(x, base + j * kFilterThreads * VN);
     }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) cur[j] = nxt[j];
+  };
+  int base = threadIdx.x * VN;
+  if (base >= V) return;
+  u32x4_t ra[NB], rb[NB];
+  fetch(ra, base);
+  for (; base < V; base += 2 * kStep) {
+    if (base + kStep < V) fetch(rb, base + kStep);
+    use(ra, base);
+    if (base + kStep >= V) break;
+    if (base + 2 * kStep < V) fetch(ra, base + 2 * kStep);
+    use(rb, base + kStep);
   }
 }
 
@@ -603,15 +608,18 @@ __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v
 // the total `above` carried from the higher digits, reaches `target`; it
 // adds the totals of the bins above the pick to `above`.  If no bin reaches
 // (only by rounding), the lowest nonempty bin.  Thread t holds bins
-// 4t .. 4t + 3.  All threads return the same values.
+// P t .. P t + P - 1, P = kFilterBins / kFilterThreads.  All threads return
+// the same values.
 __device__ __forceinline__ int filter_pick(const unsigned long long* h, int nbins, double target,
                                            unsigned long long& above, unsigned long long* s_w,
                                            int* s_pick, unsigned long long* s_above) {
+  constexpr int P = kFilterBins / kFilterThreads;   // bins per thread
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  unsigned long long v[4], loc = 0ull;
+  const int b0 = P * tid;
+  unsigned long long v[P], loc = 0ull;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    v[k] = (4 * tid + k < nbins) ? h[4 * tid + k] : 0ull;
+  for (int k = 0; k < P; ++k) {
+    v[k] = (b0 + k < nbins) ? h[b0 + k] : 0ull;
     loc += v[k];
   }
   // Inclusive suffix sums over the lanes of a wave (lanes l..63), then over
@@ -629,10 +637,10 @@ __device__ __forceinline__ int filter_pick(const unsigned long long* h, int nbin
   unsigned long long acc = above + wabove + (suf - loc);   // everything above this thread's bins
   int hit = -1, nonempty = 1 << 30;
 #pragma unroll
-  for (int k = 3; k >= 0; --k) {
+  for (int k = P - 1; k >= 0; --k) {
     acc += v[k];
-    if (hit < 0 && (double)acc >= target) hit = 4 * tid + k;
-    if (v[k]) nonempty = 4 * tid + k;
+    if (hit < 0 && (double)acc >= target) hit = b0 + k;
+    if (v[k]) nonempty = b0 + k;
   }
   // Block max of hit, block min of nonempty.
 #pragma unroll
@@ -646,17 +654,51 @@ __device__ __forceinline__ int filter_pick(const unsigned long long* h, int nbin
   for (int w = 0; w < kFilterWaves; ++w) { sel = max(sel, s_pick[w]); ne = min(ne, s_pick[kFilterWaves + w]); }
   if (sel < 0) sel = ne < nbins ? ne : 0;
   // The owner of bin sel knows the total above it.
-  if (tid == (sel >> 2)) {
+  if (tid == sel / P) {
     unsigned long long ab = above + wabove + (suf - loc);
 #pragma unroll
-    for (int k = 3; k >= 0; --k)
-      if (4 * tid + k > sel) ab += v[k];
+    for (int k = P - 1; k >= 0; --k)
+      if (b0 + k > sel) ab += v[k];
     *s_above = ab;
   }
   __syncthreads();
   above = *s_above;
   __syncthreads();
   return sel;
+}
+
+// A lower bound for the k-th largest key of a row, for k no larger than the
+// number of threads that read an entry: each thread takes the largest entry
+// of one vector of a sample spread evenly over the row, and the block counts
+// those maxima in the 4096 bins of their top 12 key bits.  The bin where the
+// count from the top reaches k starts at a key that at least k maxima (so at
+// least k entries) reach.  The sample is 1/16 of a bf16 row at the llama
+// vocabulary; the selection passes that follow then only see the entries at
+// or above the bound (a few per thousand for small k).
+template <typename T, bool kAligned>
+__device__ __forceinline__ uint32_t topk_bound(const T* __restrict__ row, int V, int tk,
+                                               unsigned long long* h, unsigned long long* s_w,
+                                               int* s_pick, unsigned long long* s_above) {
+  constexpr int VN = Vec16<T>::N;
+  const int nvec = (V + VN - 1) / VN;              // vectors in the row
+  const int nt = min(kFilterThreads, nvec);        // threads that read one
+  float mx = -INFINITY;
+  if ((int)threadIdx.x < nt) {
+    const int e = (int)(((long long)threadIdx.x * nvec / nt)) * VN;
+    const u32x4_t raw = kAligned ? load_raw<T>(row, e, V) : load_raw_unaligned<T>(row, e, V);
+    float x[VN];
+    widen_raw<T>(raw, x);
+#pragma unroll
+    for (int k = 0; k < VN; ++k)
+      if (kAligned || e + k < V) mx = fmaxf(mx, x[k]);
+  }
+  for (int i = threadIdx.x; i < kFilterBins; i += kFilterThreads) h[i] = 0ull;
+  __syncthreads();
+  if ((int)threadIdx.x < nt) atomicAdd(&h[key32_of(mx) >> 20], 1ull);
+  __syncthreads();
+  unsigned long long above = 0ull;
+  const int sel = filter_pick(h, kFilterBins, (double)tk, above, s_w, s_pick, s_above);
+  return (uint32_t)sel << 20;
 }
 
 // The mass of the entries with x >= flo, in 40-bit fixed point: per-thread
@@ -688,7 +730,7 @@ __device__ __forceinline__ unsigned long long filter_kept_mass(const T* __restri
 }
 
 template <typename T, bool kAligned>
-__global__ __launch_bounds__(kFilterThreads) void k_filter(
+__global__ __launch_bounds__(kFilterThreads, 2) void k_filter(
     const T* __restrict__ tgt, const T* __restrict__ drf, const float* __restrict__ temp,
     const int32_t* __restrict__ top_k, const float* __restrict__ top_p, int K, int V, int nc,
     int force_greedy, const float2* __restrict__ part, RowFilter* __restrict__ filt) {
@@ -731,6 +773,11 @@ __global__ __launch_bounds__(kFilterThreads) void k_filter(
   uint32_t lo = 0u;                                // 32-bit keys below this are filtered out
   unsigned long long kept_mass = 0ull;
   bool have_mass = false;
+  // Small k: restrict the top-k passes to the entries at or above a bound
+  // (each of min(512, vectors in the row) threads contributes one vector's
+  // maximum, so the count from the top reaches k).
+  if (k_on && tk <= min(kFilterThreads, (V + Vec16<T>::N - 1) / Vec16<T>::N))
+    lo = topk_bound<T, kAligned>(src, V, tk, h, s_w, s_pick, &s_above);
   for (int f = 0; f < 2; ++f) {
     const bool by_mass = (f == 1);
     if (by_mass ? !p_on : !k_on) continue;
