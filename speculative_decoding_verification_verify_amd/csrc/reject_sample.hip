@@ -419,6 +419,22 @@ __device__ __forceinline__ void emit(int b, int K, int n, int tok, const int* __
   }
 }
 
+// emit() for a thread that holds its own draft token (thread i < K: d_{i+1}).
+__device__ __forceinline__ void emit_own(int b, int K, int n, int tok, int my_draw,
+                                         int32_t* __restrict__ out, int32_t* __restrict__ nacc,
+                                         int32_t* __restrict__ kv_len, unsigned long long* counters) {
+  const int i = threadIdx.x;
+  if (i <= K) out[(size_t)b * (K + 1) + i] = (i < n) ? my_draw : (i == n ? tok : -1);
+  if (i == 0) {
+    nacc[b] = n;
+    kv_len[b] = kv_len[b] + n + 1;
+    if (counters) {
+      atomicAdd(&counters[0], (unsigned long long)K);
+      atomicAdd(&counters[1], (unsigned long long)n);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // k_filter: grid (B * (2K+1)), block 512 (two per CU): the top-k / top-p thresholds of one
 // row by radix selection over its order keys, most significant digit first:
@@ -1098,16 +1114,17 @@ __device__ __forceinline__ double wave_chunk_sum(int ncr, F f, int lane) {
 
 // The draw of one sequence (a block of kThreads threads) from the pass that
 // decision d describes, given the pass's chunk sums cg [ncr] and sub-chunk
-// sums sg [ncr][32], the filled exp table and the uniform u.  Returns the
+// sums sg [ncr][32], the exp table (filled here while the sums are loading
+// when fill_table, else already filled) and the uniform u.  Returns the
 // token in every thread.
 template <typename T>
 __device__ __forceinline__ int locate_draw(const T* __restrict__ trow, const T* __restrict__ drow,
                                            const Decision& d, double u, float t, int V, int ncr,
                                            const ChunkSums* __restrict__ cg,
                                            const SubSums* __restrict__ sg,
-                                           const double* __restrict__ s_exp) {
+                                           double* __restrict__ s_exp, bool fill_table) {
   static_assert(kSub == kThreads, "one sub-chunk entry per thread");
-  constexpr int kSubStage = 512;                 // sub-chunk sums staged in LDS (16 KB)
+  constexpr int kSubStage = 1024;                // sub-chunk sums staged in LDS (32 KB)
   __shared__ ChunkSums s_cs[kThreads];
   __shared__ SubSums s_ss[kSubStage];
   __shared__ double s_wtot[kThreads / 64];
@@ -1115,14 +1132,42 @@ __device__ __forceinline__ int locate_draw(const T* __restrict__ trow, const T* 
   __shared__ double s_base, s_target, s_isq, s_isp;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const double cd = kLog2eD / (double)t;
-  // Chunk and sub-chunk sums staged in LDS together when they fit (V <= 2^17
+  // Chunk and sub-chunk sums staged in LDS together when they fit (V <= 2^18
   // for both, V <= 2^21 for the chunk sums), read in place otherwise: the
-  // sub-chunk level then needs no second round trip to memory.
+  // sub-chunk level then needs no second round trip to memory.  The loads
+  // are issued before the table is filled and stored to LDS after it.
   const bool staged = ncr <= kThreads;
   const bool sub_staged = ncr * kSubPerChunk <= kSubStage;
-  if (staged && tid < ncr) s_cs[tid] = cg[tid];
-  if (sub_staged)
-    for (int k = tid; k < ncr * kSubPerChunk; k += kThreads) s_ss[k] = sg[k];
+  // Waves 0-1 stage the sums (all loads issued before any is stored), waves
+  // 2-3 fill the table meanwhile.
+  constexpr int kHalf = kThreads / 2;
+  if (tid < kHalf) {
+    constexpr int kSubH = kSubStage / kHalf;
+    static_assert(kThreads == 2 * kHalf, "two chunk sums per staging thread");
+    // Clamped indices: every load and store is unconditional inside the
+    // block-uniform branches (a clamped duplicate stores the same value to
+    // the same slot), so the loads are all issued before the first store.
+    // Sub-chunk sums that fit imply chunk sums that fit.
+    const int c0 = min(tid, ncr - 1), c1 = min(tid + kHalf, ncr - 1);
+    if (sub_staged) {
+      const int nsub = ncr * kSubPerChunk;
+      const ChunkSums r0 = cg[c0], r1 = cg[c1];
+      SubSums rs[kSubH];
+#pragma unroll
+      for (int j = 0; j < kSubH; ++j) rs[j] = sg[min(tid + j * kHalf, nsub - 1)];
+      __builtin_amdgcn_sched_barrier(0);
+      s_cs[c0] = r0;
+      s_cs[c1] = r1;
+#pragma unroll
+      for (int j = 0; j < kSubH; ++j) s_ss[min(tid + j * kHalf, nsub - 1)] = rs[j];
+    } else if (staged) {
+      const ChunkSums r0 = cg[c0], r1 = cg[c1];
+      s_cs[c0] = r0;
+      s_cs[c1] = r1;
+    }
+  } else if (fill_table) {
+    for (int j = tid - kHalf; j < kExpTable; j += kHalf) s_exp[j] = exp2((double)j * (1.0 / 256));
+  }
   __syncthreads();
   const ChunkSums* cs = staged ? s_cs : cg;
   if (wave == 0) {
@@ -1215,18 +1260,19 @@ __global__ __launch_bounds__(kThreads) void k_locate(
     const Decision* __restrict__ dec, int32_t* __restrict__ out, int32_t* __restrict__ nacc,
     int32_t* __restrict__ kv_len, unsigned long long* counters) {
   __shared__ double s_exp[kExpTable];
-  __shared__ int s_draw[SV_MAX_K];
   const int b = blockIdx.x;
   const Decision d = dec[b];
   if (d.mode == kModeNone) return;
   const float t = temp_of(temp, b, force_greedy);
-  if ((int)threadIdx.x < K) s_draw[threadIdx.x] = dtok[(size_t)b * K + threadIdx.x];
-  fill_exp_table(s_exp);
-  // (locate_draw synchronises the block before it reads either.)
+  // Thread i < K emits draft i: it keeps its own token (no wait for it here).
+  const int my_draw = (int)threadIdx.x < K ? dtok[(size_t)b * K + threadIdx.x] : 0;
+  // (locate_draw fills the table and synchronises the block before it reads
+  // it.)
   const int tok = locate_draw<T>(tgt + (size_t)d.trow * V, drf + (size_t)d.drow * V, d,
                                  (double)uni[(size_t)b * (K + 1) + K], t, V, ncr,
-                                 csum + (size_t)b * ncr, csub + (size_t)b * ncr * kSubPerChunk, s_exp);
-  emit(b, K, d.n, tok, s_draw, out, nacc, kv_len, counters);
+                                 csum + (size_t)b * ncr, csub + (size_t)b * ncr * kSubPerChunk, s_exp,
+                                 true);
+  emit_own(b, K, d.n, tok, my_draw, out, nacc, kv_len, counters);
 }
 
 // Filtered-out entries (order key below kmin) become -inf: weight 0, never
@@ -1631,7 +1677,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_step(
   if (!s_draw) return;
   const int tk = locate_draw<T>(tgt + (size_t)d.trow * V, drf + (size_t)d.drow * V, d,
                                 (double)s_u[0], t, V, ncr, cg,
-                                csub + (size_t)b * ncr * kSubPerChunk, s_exp);
+                                csub + (size_t)b * ncr * kSubPerChunk, s_exp, false);
   emit_tree(b, N, s_n, tk, out_tok, out_node, nacc, kv_len, counters);
   if (tid == 0) dec[b].mode = kModeNone;
 }
