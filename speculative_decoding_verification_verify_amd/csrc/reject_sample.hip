@@ -457,6 +457,7 @@ constexpr int kFilterWaves = kFilterThreads / 64;
 constexpr int kFilterBins = 4096;
 static_assert(kFilterBins % kFilterThreads == 0, "whole bins per thread in filter_pick");
 constexpr double kFix = 1099511627776.0;          // 2^40
+constexpr int kWinBins = 16;                      // 12-bit bins whose single values a first pass counts
 
 // 16-byte vectors per batch of a thread (two batches are in registers at
 // once); half as many where each load is several (rows that do not start on
@@ -543,27 +544,59 @@ __device__ __forceinline__ void filter_scan(const T* __restrict__ row, int V, F&
 // weight 2^(x c - mc) in 40-bit fixed point (top-p).  Each thread requests
 // filter_batch vectors before it uses any; with kAll the adds are not
 // branched around (entries past V add 0).
-template <typename T, bool kAligned, bool kMass, bool kAll>
+// Extra counts of a bf16 first pass (12-bit digit): with kWin the single
+// values of the kWinBins bins from wlo (hx [kWinBins][16], the value's index
+// being the low 4 bits of its 16-bit key, as in the last pass), with kBinMass
+// also the masses of the counted entries per bin (hm [4096]).
+struct FirstPassExtra {
+  uint32_t wlo;
+  unsigned long long* hx;
+  unsigned long long* hm;
+};
+
+template <typename T, bool kAligned, bool kMass, bool kAll, bool kWin = false,
+          bool kBinMass = false>
 __device__ __forceinline__ void filter_hist(const T* __restrict__ row, int V, float c, float mc,
                                             float flo, float fhi, int shift, int width,
-                                            unsigned long long* h) {
+                                            unsigned long long* h,
+                                            const FirstPassExtra& ex = FirstPassExtra{0u, nullptr, nullptr}) {
   constexpr int VN = Vec16<T>::N;
-  for (int i = threadIdx.x; i < kFilterBins; i += kFilterThreads) h[i] = 0ull;
+  for (int i = threadIdx.x; i < kFilterBins; i += kFilterThreads) {
+    h[i] = 0ull;
+    if (kBinMass) ex.hm[i] = 0ull;
+  }
+  if (kWin)
+    for (int i = threadIdx.x; i < kWinBins * 16; i += kFilterThreads) ex.hx[i] = 0ull;
   __syncthreads();
+  // The single-value count of an entry with key `key` in bin `bin`.
+  auto count_value = [&](uint32_t key, uint32_t bin) {
+    const uint32_t d = bin - ex.wlo;
+    if (d < (uint32_t)kWinBins) atomicAdd(&ex.hx[d * 16 + __builtin_amdgcn_ubfe(key, 16, 4)], 1ull);
+  };
   filter_scan<T, kAligned>(row, V, [&](const float (&x)[VN], int e) {
 #pragma unroll
     for (int k = 0; k < VN; ++k) {
       const bool inb = kAligned ? e < V : e + k < V;
       if (kAll) {
-        const uint32_t bin = __builtin_amdgcn_ubfe(key32_of(x[k]), shift, width);
+        const uint32_t key = key32_of(x[k]);
+        const uint32_t bin = __builtin_amdgcn_ubfe(key, shift, width);
         unsigned long long v;
         if (kMass) v = fixed40(exp2_dev(__builtin_fmaf(x[k], c, -mc)));
         else v = 1ull;
         atomicAdd(&h[bin], inb ? v : 0ull);
+        if (kWin && inb) count_value(key, bin);
       } else if (inb && x[k] >= flo && x[k] <= fhi) {
-        const uint32_t bin = __builtin_amdgcn_ubfe(key32_of(x[k]), shift, width);
-        if (kMass) atomicAdd(&h[bin], fixed40(exp2_dev(__builtin_fmaf(x[k], c, -mc))));
-        else atomicAdd(&h[bin], 1ull);
+        const uint32_t key = key32_of(x[k]);
+        const uint32_t bin = __builtin_amdgcn_ubfe(key, shift, width);
+        if (kMass || kBinMass) {
+          const unsigned long long w = fixed40(exp2_dev(__builtin_fmaf(x[k], c, -mc)));
+          if (kMass) atomicAdd(&h[bin], w);
+          else atomicAdd(&h[bin], 1ull);
+          if (kBinMass) atomicAdd(&ex.hm[bin], w);
+        } else {
+          atomicAdd(&h[bin], 1ull);
+        }
+        if (kWin) count_value(key, bin);
       }
     }
   });
@@ -746,7 +779,7 @@ __device__ __forceinline__ unsigned long long filter_kept_mass(const T* __restri
 }
 
 template <typename T, bool kAligned>
-__global__ __launch_bounds__(kFilterThreads, 2) void k_filter(
+__global__ __launch_bounds__(kFilterThreads, 4) void k_filter(
     const T* __restrict__ tgt, const T* __restrict__ drf, const float* __restrict__ temp,
     const int32_t* __restrict__ top_k, const float* __restrict__ top_p, int K, int V, int nc,
     int force_greedy, const float2* __restrict__ part, RowFilter* __restrict__ filt) {
@@ -755,6 +788,8 @@ __global__ __launch_bounds__(kFilterThreads, 2) void k_filter(
   __shared__ int s_pick[2 * kFilterWaves];
   __shared__ unsigned long long s_above;
   __shared__ unsigned long long s_wt[16];
+  __shared__ unsigned long long hx[kWinBins * 16];   // single values of the window's bins
+  __shared__ unsigned long long hm[kFilterBins];      // top-k alone: masses per first-digit bin
   __shared__ float s_xr;
   const int R = 2 * K + 1;
   const int row = blockIdx.x;
@@ -800,6 +835,84 @@ __global__ __launch_bounds__(kFilterThreads, 2) void k_filter(
     uint32_t prefix = 0u;
     unsigned long long above = 0ull;
     double target = by_mass ? 0.0 : (double)tk;
+    if constexpr (sizeof(T) == 2) {
+      // bf16: the 12-bit first digit, then the chosen bin's single values.
+      // When the first pass only sees the entries at or above a bound (top-k
+      // with its sampled bound, top-p over the top-k set) it also counts the
+      // single values of the kWinBins bins from the bound's bin, and a chosen
+      // bin among them needs no second pass.  (Over every entry, top-p alone,
+      // those extra counts cost about as much as the pass they save.)
+      const bool need_above = !by_mass && !p_on;
+      const bool windowed = lo != 0u;
+      const uint32_t wlo = min(lo >> 20, (uint32_t)(kFilterBins - kWinBins));
+      const FirstPassExtra ex{wlo, hx, hm};
+      if (lo == 0u) {
+        if (by_mass) filter_hist<T, kAligned, true, true>(src, V, c, mc, 0.f, 0.f, 20, 12, h);
+        else filter_hist<T, kAligned, false, true>(src, V, c, mc, 0.f, 0.f, 20, 12, h);
+      } else {
+        float flo, fhi;
+        key_bounds(lo, 0xFFFFFFFFu, flo, fhi);
+        if (by_mass) filter_hist<T, kAligned, true, false, true>(src, V, c, mc, flo, fhi, 20, 12, h, ex);
+        else if (need_above)
+          filter_hist<T, kAligned, false, false, true, true>(src, V, c, mc, flo, fhi, 20, 12, h, ex);
+        else filter_hist<T, kAligned, false, false, true>(src, V, c, mc, flo, fhi, 20, 12, h, ex);
+      }
+      if (by_mass) {
+        // The kept set's mass (all of the row, or its top-k set) sets the target.
+        unsigned long long part_sum = 0ull;
+        for (int i = tid; i < kFilterBins; i += kFilterThreads) part_sum += h[i];
+        target = (double)tp * (double)block_sum_u64(part_sum, s_w);
+      }
+      const int sel0 = filter_pick(h, kFilterBins, target, above, s_w, s_pick, &s_above);
+      prefix = (uint32_t)sel0;
+      // The 16 single values of bin sel0 into h[0..15]: from the window, or
+      // by one more pass.
+      unsigned long long ab = 0ull;            // top-k alone: mass above bin sel0
+      if (windowed && (uint32_t)sel0 - wlo < (uint32_t)kWinBins) {
+        if (need_above) {
+          unsigned long long part_ab = 0ull;
+          for (int i = tid; i < kFilterBins; i += kFilterThreads)
+            if (i > sel0) part_ab += hm[i];
+          ab = block_sum_u64(part_ab, s_w);
+        }
+        if (tid < 16) h[tid] = hx[(sel0 - wlo) * 16 + tid];
+        __syncthreads();
+      } else {
+        float flo, fhi;
+        key_bounds(max(prefix << 20, lo), (uint32_t)((((unsigned long long)prefix + 1) << 20) - 1),
+                   flo, fhi);
+        const uint32_t flip = (prefix & 0x800u) ? 0u : 15u;
+        if (need_above) {
+          ab = filter_hist_exact<kAligned, true>(src, V, c, mc, flo, fhi, flip, h);
+          ab = block_sum_u64(ab, s_w);
+        } else {
+          filter_hist_exact<kAligned, false>(src, V, c, mc, flo, fhi, flip, h);
+        }
+      }
+      if (tid < 16) {
+        const float xv = key16_value((prefix << 4) | (uint32_t)tid);
+        const unsigned long long w = fixed40(exp2_dev(__builtin_fmaf(xv, c, -mc)));
+        if (by_mass) h[tid] *= w;
+        else s_wt[tid] = w;
+      }
+      __syncthreads();
+      const int sel = filter_pick(h, 16, target, above, s_w, s_pick, &s_above);
+      prefix = (prefix << 4) | (uint32_t)sel;
+      if (by_mass) {
+        kept_mass = above + h[sel];
+      } else if (need_above) {
+        // Top-k alone: the mass of the kept set, {x > bin} plus the values
+        // of the bin from sel up.
+        unsigned long long m = ab;
+        for (int i = sel; i < 16; ++i) m += h[i] * s_wt[i];
+        kept_mass = m;
+        have_mass = true;
+      }
+      __syncthreads();
+      lo = prefix << kStop;                        // the k-th largest key, or the top-p key
+      have_mass = have_mass || by_mass;
+      continue;
+    }
     int shift = 32;
     for (int lv = 0; lv < filter_levels<T>(); ++lv) {
       const int width = digit_bits<T>(lv);
