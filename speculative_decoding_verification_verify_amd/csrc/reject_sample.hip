@@ -465,14 +465,10 @@ constexpr int kWinBins = 16;                      // 12-bit bins whose single va
 template <typename T, bool kAligned>
 constexpr int filter_batch() { return kAligned ? 4 : 2; }
 
-// Digit widths, most significant first.
-template <typename T>
-__device__ __forceinline__ int digit_bits(int level) {
-  if constexpr (sizeof(T) == 2) return level == 0 ? 12 : 4;
-  else return level == 2 ? 8 : 12;
-}
-template <typename T>
-constexpr int filter_levels() { return sizeof(T) == 2 ? 2 : 3; }
+// fp32 rows: three digits of the 32-bit key, 12, 12 and 8 bits, most
+// significant first (a bf16 row takes 12 bits, then its 16 single values).
+constexpr int kF32Levels = 3;
+__device__ __forceinline__ int f32_digit_bits(int level) { return level == 2 ? 8 : 12; }
 
 // floor(2^40 w) as an integer, for 0 <= w < 2^24: t = 256 w is exact, its
 // integer part gives the high word and its fraction times 2^32 (exact,
@@ -913,46 +909,12 @@ __global__ __launch_bounds__(kFilterThreads, 4) void k_filter(
       have_mass = have_mass || by_mass;
       continue;
     }
+    // fp32: three range passes.
     int shift = 32;
-    for (int lv = 0; lv < filter_levels<T>(); ++lv) {
-      const int width = digit_bits<T>(lv);
+    for (int lv = 0; lv < kF32Levels; ++lv) {
+      const int width = f32_digit_bits(lv);
       const int high = shift;                      // the bits above `high` are fixed: prefix
       shift -= width;
-      if constexpr (sizeof(T) == 2) {
-        if (lv == 1) {
-          // One bf16 value per bin: counts, then masses from the counts.
-          float flo, fhi;
-          key_bounds(max(prefix << high, lo),
-                     (uint32_t)((((unsigned long long)prefix + 1) << high) - 1), flo, fhi);
-          const uint32_t flip = (prefix & 0x800u) ? 0u : 15u;
-          const bool need_above = !by_mass && !p_on;
-          unsigned long long ab = 0ull;
-          if (need_above) ab = filter_hist_exact<kAligned, true>(src, V, c, mc, flo, fhi, flip, h);
-          else filter_hist_exact<kAligned, false>(src, V, c, mc, flo, fhi, flip, h);
-          if (need_above) ab = block_sum_u64(ab, s_w);
-          if (tid < 16) {
-            const float xv = key16_value((prefix << 4) | (uint32_t)tid);
-            const unsigned long long w = fixed40(exp2_dev(__builtin_fmaf(xv, c, -mc)));
-            if (by_mass) h[tid] *= w;
-            else s_wt[tid] = w;
-          }
-          __syncthreads();
-          const int sel = filter_pick(h, 16, target, above, s_w, s_pick, &s_above);
-          prefix = (prefix << 4) | (uint32_t)sel;
-          if (by_mass) {
-            kept_mass = above + h[sel];
-          } else if (need_above) {
-            // Top-k alone: the mass of the kept set, {x > bin} plus the
-            // values of the bin from sel up.
-            unsigned long long m = ab;
-            for (int i = sel; i < 16; ++i) m += h[i] * s_wt[i];
-            kept_mass = m;
-            have_mass = true;
-          }
-          __syncthreads();
-          continue;
-        }
-      }
       if (lv == 0 && lo == 0u) {
         if (by_mass) filter_hist<T, kAligned, true, true>(src, V, c, mc, 0.f, 0.f, shift, width, h);
         else filter_hist<T, kAligned, false, true>(src, V, c, mc, 0.f, 0.f, shift, width, h);
@@ -969,14 +931,7 @@ __global__ __launch_bounds__(kFilterThreads, 4) void k_filter(
         // The kept set's mass (all of the row, or its top-k set) sets the target.
         unsigned long long part_sum = 0ull;
         for (int i = tid; i < kFilterBins; i += kFilterThreads) part_sum += h[i];
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) part_sum += __shfl_xor(part_sum, off, 64);
-        if (lane == 0) s_w[wave] = part_sum;
-        __syncthreads();
-        unsigned long long tot = 0ull;
-        for (int w = 0; w < kFilterWaves; ++w) tot += s_w[w];
-        __syncthreads();
-        target = (double)tp * (double)tot;
+        target = (double)tp * (double)block_sum_u64(part_sum, s_w);
       }
       const int sel = filter_pick(h, 1 << width, target, above, s_w, s_pick, &s_above);
       prefix = (prefix << width) | (uint32_t)sel;

@@ -38,7 +38,8 @@ def _filtered_drafts(inp, top_k, top_p, seed):
     return toks.astype(np.int32)
 
 
-def _case(sv, dev, seed, B, K, V, top_k, top_p, dtype="bf16", temp=1.0, sigma=0.8, idx=None):
+def _case(sv, dev, seed, B, K, V, top_k, top_p, dtype="bf16", temp=1.0, sigma=0.8, idx=None,
+          std=2.0, spikes=None):
     top_k = np.broadcast_to(np.asarray(top_k, np.int32), (B,)).copy()
     top_p = np.broadcast_to(np.asarray(top_p, np.float32), (B,)).copy()
     label = "filter seed=%d B=%d K=%d V=%d %s k=%s p=%s" % (seed, B, K, V, dtype,
@@ -46,7 +47,15 @@ def _case(sv, dev, seed, B, K, V, top_k, top_p, dtype="bf16", temp=1.0, sigma=0.
                                                            np.unique(top_p).tolist())
     _say(label)
     inp = gen.make_reject_inputs(seed=seed, B=B, K=K, V=V, dtype=dtype, draft_sigma=sigma,
-                                 temperature=temp)
+                                 temperature=temp, logit_std=std)
+    if spikes:
+        # Fixed logits at fixed entries of every target row and every draft row.
+        pos, tv, dv = spikes
+        for name, vals in (("target", tv), ("draft", dv)):
+            x = inp[name].copy()
+            for i, v in zip(pos, vals):
+                x[..., i] = gen._encode(np.float32([v]), dtype)[0]
+            inp[name] = x
     inp["draft_tokens"] = _filtered_drafts(inp, top_k, top_p, seed + 1)
     kv0 = np.full(B, 500, np.int32)
     t = {k: to_device(v, dev) for k, v in inp.items()}
@@ -127,3 +136,39 @@ def test_deterministic(gpu_lib, dev):
         outs.append((o.clone(), n.clone()))
     for o, n in outs[1:]:
         assert torch.equal(o, outs[0][0]) and torch.equal(n, outs[0][1])
+
+
+
+# Entries outside the sampled vectors of the top-k bound.  A bf16 row of V
+# entries has ceil(V / 8) vectors; the bound reads vector floor(t * nvec / 512)
+# for t < 512, so at V = 32000 (or 32003) vectors 1..6 are never read.  The
+# bulk is N(0, 0.01) (draft: plus N(0, 0.005)), so the laws over the spikes
+# stay far from one-hot and the draft's reversed spikes force rejections.
+_POS = (9, 20, 30)
+
+
+@pytest.mark.parametrize("V", [32000, 32003])
+def test_top_k_bound_far_below_the_kth(gpu_lib, dev, V):
+    """Three spikes at 0.20..0.22, none of them in the sample: the sampled
+    bound sits in the bulk (~0.03), more than 16 first-digit bins under the
+    k-th largest value, so the first pass's window misses and the chosen
+    bin's values come from the extra pass."""
+    sp = (_POS, (0.20, 0.21, 0.22), (0.22, 0.21, 0.20))
+    for seed, k in ((8, 3), (9, 2)):
+        n = _case(gpu_lib, dev, seed, 32, 3, V, k, 1.0, sigma=0.005, std=0.01, spikes=sp)
+        assert n.min() < 3                       # some drafts rejected
+
+
+def test_top_p_over_top_k_far_above_the_kth(gpu_lib, dev):
+    """Top-p over a top-200 set with most of its mass in three spikes at
+    5.0..6.0: the top-p boundary bin is far above the 200th value's bin
+    (where the window starts)."""
+    sp = (_POS, (5.0, 5.5, 6.0), (6.0, 5.5, 5.0))
+    for seed, p in ((10, 0.5), (11, 0.75)):
+        n = _case(gpu_lib, dev, seed, 32, 3, 32000, 200, p, sigma=0.005, std=0.01, spikes=sp)
+        assert n.min() < 3
+
+
+def test_top_p_alone_with_spikes(gpu_lib, dev):
+    sp = (_POS, (5.0, 5.5, 6.0), (6.0, 5.5, 5.0))
+    _case(gpu_lib, dev, 12, 32, 3, 32003, 0, 0.5, sigma=0.005, std=0.01, spikes=sp)
