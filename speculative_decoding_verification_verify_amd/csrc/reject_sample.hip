@@ -231,11 +231,20 @@ __device__ __forceinline__ void load_vec(const T* __restrict__ row, int e, int V
 // result is replaced by -inf bit patterns, so the loads of a lane can all be
 // in flight at once.
 template <typename T>
-__device__ __forceinline__ u32x4_t load_raw(const T* __restrict__ row, int e, int V) {
+__device__ __forceinline__ u32x4_t past_end_neg_inf(const u32x4_t r, bool in) {
   constexpr unsigned kNegInf = sizeof(T) == 2 ? 0xFF80FF80u : 0xFF800000u;
-  const bool in = e < V;
-  const u32x4_t r = *reinterpret_cast<const u32x4_t*>(row + (in ? e : 0));
   return in ? r : u32x4_t{kNegInf, kNegInf, kNegInf, kNegInf};
+}
+__device__ __forceinline__ u32x4_t and_raw(const u32x4_t a, const u32x4_t b) {
+  return u32x4_t{a.x & b.x, a.y & b.y, a.z & b.z, a.w & b.w};
+}
+template <typename T>
+__device__ __forceinline__ u32x4_t load_clamped(const T* __restrict__ row, int e, int V) {
+  return *reinterpret_cast<const u32x4_t*>(row + (e < V ? e : 0));
+}
+template <typename T>
+__device__ __forceinline__ u32x4_t load_raw(const T* __restrict__ row, int e, int V) {
+  return past_end_neg_inf<T>(load_clamped<T>(row, e, V), e < V);
 }
 
 template <typename T>
@@ -1384,17 +1393,36 @@ __global__ __launch_bounds__(kThreads, 4) void k_residual(
   const T* trow = tgt + (size_t)d.trow * (size_t)V;
   const T* drow = drf + (size_t)d.drow * (size_t)V;
   const int e0 = cr * kResChunk + sub_i * kSub + s * VN;
-  // Loads first, so they are in flight while the table is filled.
+  // Loads first, so they are in flight while the table is filled, target and
+  // draft vectors alternating so the first pair arrives first.  Aligned rows
+  // set the vectors past V to -inf where they are used: a select right after
+  // a load would wait for it there.
   u32x4_t rq[IT], rp[IT];
+  if constexpr (kAligned) {
+    // Without a branch: a bonus pass loads its target vectors twice (the
+    // second load finds the line in flight, no extra HBM traffic) and uses
+    // the AND of the two equal copies, so every load has a use on both paths
+    // and stays here instead of being moved into one of them, and each
+    // vector pair is waited for only where it is first used.
+    const T* prow = bonus ? trow : drow;
 #pragma unroll
-  for (int i = 0; i < IT; ++i)
-    rq[i] = kAligned ? load_raw<T>(trow, e0 + i * kLine, V) : load_raw_unaligned<T>(trow, e0 + i * kLine, V);
-  if (!bonus) {
+    for (int i = 0; i < IT; ++i) {
+      rq[i] = load_clamped<T>(trow, e0 + i * kLine, V);
+      rp[i] = load_clamped<T>(prow, e0 + i * kLine, V);
+    }
+  } else {
 #pragma unroll
-    for (int i = 0; i < IT; ++i)
-      rp[i] = kAligned ? load_raw<T>(drow, e0 + i * kLine, V) : load_raw_unaligned<T>(drow, e0 + i * kLine, V);
+    for (int i = 0; i < IT; ++i) rq[i] = load_raw_unaligned<T>(trow, e0 + i * kLine, V);
+    if (!bonus) {
+#pragma unroll
+      for (int i = 0; i < IT; ++i) rp[i] = load_raw_unaligned<T>(drow, e0 + i * kLine, V);
+    }
   }
-  fill_exp_table(s_exp);
+  const auto vec = [&](const u32x4_t r, int i) {
+    return kAligned ? past_end_neg_inf<T>(r, e0 + i * kLine < V) : r;
+  };
+  static_assert(kExpTable == kThreads, "one table entry per thread");
+  s_exp[tid] = exp2((double)tid * (1.0 / 256));
   __syncthreads();
   // Exponents scaled by 256 (see exp2_reduce); all three scalings are exact.
   const double c256 = cd * 256.0;
@@ -1407,7 +1435,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_residual(
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       float xq[VN];
-      widen_raw<T>(rq[i], xq);
+      widen_raw<T>(vec(kAligned ? and_raw(rq[i], rp[i]) : rq[i], i), xq);
       if (kMask) mask_row<T>(xq, d.kq);
       Exp2Arg eq[VN];
       double tq[VN];
@@ -1424,8 +1452,8 @@ __global__ __launch_bounds__(kThreads, 4) void k_residual(
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       float xq[VN], xp[VN];
-      widen_raw<T>(rq[i], xq);
-      widen_raw<T>(rp[i], xp);
+      widen_raw<T>(vec(rq[i], i), xq);
+      widen_raw<T>(vec(rp[i], i), xp);
       if (kMask) {
         mask_row<T>(xq, d.kq);
         mask_row<T>(xp, d.kp);
