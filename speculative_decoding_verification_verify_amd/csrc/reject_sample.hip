@@ -1118,7 +1118,39 @@ __device__ __forceinline__ double expo(float x, double c256, double xmc256) {
   return fma((double)x, c256, -xmc256);
 }
 
-__device__ __forceinline__ double shfl_xor_d(double x, int off) { return __shfl_xor(x, off, 64); }
+// Float64 cross-lane steps for the sums and scans of the draw: DPP moves
+// inside rows of 16 lanes and readlane across rows, a few cycles each where a
+// generic shuffle goes through the LDS permute unit.  Each move takes the two
+// halves of the double separately; lanes a move does not write read 0.
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int kDppRowShr = 0x110;       // + n: row_shr:n
+constexpr int kDppWaveShr1 = 0x138;     // wave_shr:1
+constexpr int kDppRowMirror = 0x140;    // lane i <- 15 - i of its row
+constexpr int kDppHalfMirror = 0x141;   // lane i <- 7 - i of its half row
+constexpr int kDppBcast15 = 0x142;      // lane 15 of row r -> row r + 1
+constexpr int kDppBcast31 = 0x143;      // lane 31 -> rows 2 and 3
+
+template <int kCtrl, int kRowMask = 0xF, bool kBound = true>
+__device__ __forceinline__ double dpp_d(double x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x), kCtrl, kRowMask, 0xF, kBound);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x), kCtrl, kRowMask, 0xF, kBound);
+  return __hiloint2double(hi, lo);
+}
+
+// Lane l's value in every lane (l wave-uniform).
+__device__ __forceinline__ double readlane_d(double x, int l) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(x), l),
+                          __builtin_amdgcn_readlane(__double2loint(x), l));
+}
+
+// Sum over each group of 8 lanes 8g..8g+7, in every lane of the group (fp
+// addition is commutative, so both lanes of every pairing get the same value).
+__device__ __forceinline__ double group8_sum_d(double x) {
+  x += dpp_d<kDppXor1>(x);
+  x += dpp_d<kDppXor2>(x);
+  return x + dpp_d<kDppHalfMirror>(x);
+}
 
 // ---------------------------------------------------------------------------
 // The final draw: narrows chunk -> sub-chunk (from the stored sums) -> entry
@@ -1135,20 +1167,24 @@ __device__ __forceinline__ double sub_mass(const SubSums& ss, int m, double isq,
   return m == kDrawQ ? ss.q * isq : (m == kDrawP ? ss.p * isp : fmax(0.0, ss.a * isq - ss.b * isp));
 }
 
-// Inclusive scan of one wave, in lane order.
-__device__ __forceinline__ double wave_scan_d(double x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
+// Inclusive scan of one wave, in lane order: a scan inside each row of 16
+// lanes, then the totals of the rows before.
+__device__ __forceinline__ double wave_scan_d(double x) {
+  x += dpp_d<kDppRowShr + 1>(x);
+  x += dpp_d<kDppRowShr + 2>(x);
+  x += dpp_d<kDppRowShr + 4>(x);
+  x += dpp_d<kDppRowShr + 8>(x);
+  x += dpp_d<kDppBcast15, 0xA, false>(x);     // rows 1 and 3
+  x += dpp_d<kDppBcast31, 0xC, false>(x);     // rows 2 and 3
   return x;
 }
 
+// Sum of the wave, in every lane: row sums, then the four rows in a fixed
+// order.
 __device__ __forceinline__ double wave_sum_d(double x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
+  x = group8_sum_d(x);
+  x += dpp_d<kDppRowMirror>(x);
+  return (readlane_d(x, 0) + readlane_d(x, 16)) + (readlane_d(x, 32) + readlane_d(x, 48));
 }
 
 // One wave walks `cnt` masses (mass(i)) in order: returns the first index
@@ -1164,18 +1200,16 @@ __device__ __forceinline__ int wave_find(int cnt, F mass, double target, double&
   for (int s0 = 0; s0 < cnt; s0 += 64) {
     const int i = s0 + lane;
     const double m = i < cnt ? mass(i) : 0.0;
-    const double incl = wave_scan_d(m, lane) + carry;
+    const double incl = wave_scan_d(m) + carry;
     const unsigned long long pos = __ballot(m > 0.0);
     if (pos) lastpos = s0 + 63 - (int)__builtin_clzll(pos);
     const unsigned long long hit = __ballot(i < cnt && incl > target);
-    const double ex = __shfl_up(incl, 1, 64);
     if (found < 0 && hit) {
       const int l = (int)__builtin_ctzll(hit);
       found = s0 + l;
-      const double exl = __shfl(ex, l, 64);
-      base = (l == 0) ? carry : exl;
+      base = (l == 0) ? carry : readlane_d(incl, l - 1);
     }
-    carry = __shfl(incl, 63, 64);
+    carry = readlane_d(incl, 63);
   }
   return found;
 }
@@ -1193,10 +1227,12 @@ __device__ __forceinline__ double wave_chunk_sum(int ncr, F f, int lane) {
 // decision d describes, given the pass's chunk sums cg [ncr] and sub-chunk
 // sums sg [ncr][32], the exp table (filled here while the sums are loading
 // when fill_table, else already filled) and the uniform u.  Returns the
-// token in every thread.
+// token in every thread, or -1 in every thread when d asks for no draw.
+// d, u and t are first read after the sums are staged, so a caller can pass
+// values whose loads are still in flight.
 template <typename T>
-__device__ __forceinline__ int locate_draw(const T* __restrict__ trow, const T* __restrict__ drow,
-                                           const Decision& d, double u, float t, int V, int ncr,
+__device__ __forceinline__ int locate_draw(const T* __restrict__ tgt, const T* __restrict__ drf,
+                                           const Decision& d, float u, float t, int V, int ncr,
                                            const ChunkSums* __restrict__ cg,
                                            const SubSums* __restrict__ sg,
                                            double* __restrict__ s_exp, bool fill_table) {
@@ -1208,7 +1244,6 @@ __device__ __forceinline__ int locate_draw(const T* __restrict__ trow, const T* 
   __shared__ int s_chunk, s_sub, s_fallback, s_mode, s_first, s_lastpos;
   __shared__ double s_base, s_target, s_isq, s_isp;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const double cd = kLog2eD / (double)t;
   // Chunk and sub-chunk sums staged in LDS together when they fit (V <= 2^18
   // for both, V <= 2^21 for the chunk sums), read in place otherwise: the
   // sub-chunk level then needs no second round trip to memory.  The loads
@@ -1246,6 +1281,10 @@ __device__ __forceinline__ int locate_draw(const T* __restrict__ trow, const T* 
     for (int j = tid - kHalf; j < kExpTable; j += kHalf) s_exp[j] = exp2((double)j * (1.0 / 256));
   }
   __syncthreads();
+  if (d.mode == kModeNone) return -1;                       // block-uniform
+  const double cd = kLog2eD / (double)t;
+  const T* trow = tgt + (size_t)d.trow * V;
+  const T* drow = drf + (size_t)d.drow * V;
   const ChunkSums* cs = staged ? s_cs : cg;
   if (wave == 0) {
     // Exact normalisers, then the masses of the chunks.
@@ -1262,7 +1301,7 @@ __device__ __forceinline__ int locate_draw(const T* __restrict__ trow, const T* 
       isp = 1.0 / sp;
       z = wave_chunk_sum(ncr, [&](int i) { return chunk_mass(cs[i], m, isq, isp); }, lane);
     }
-    const double target = u * z;
+    const double target = (double)u * z;
     double base = 0.0;
     int lastpos;
     int ch = wave_find(ncr, [&](int i) { return chunk_mass(cs[i], m, isq, isp); }, target, base,
@@ -1311,7 +1350,7 @@ __device__ __forceinline__ int locate_draw(const T* __restrict__ trow, const T* 
   }
   // Inclusive prefix over the 256 entries in vocabulary order: a wave scan
   // plus the totals of the waves before (fixed order).
-  const double incl = wave_scan_d(w, lane);
+  const double incl = wave_scan_d(w);
   if (lane == 63) s_wtot[wave] = incl;
   __syncthreads();
   double run = s_base + incl;
@@ -1338,17 +1377,20 @@ __global__ __launch_bounds__(kThreads) void k_locate(
     int32_t* __restrict__ kv_len, unsigned long long* counters) {
   __shared__ double s_exp[kExpTable];
   const int b = blockIdx.x;
-  const Decision d = dec[b];
-  if (d.mode == kModeNone) return;
-  const float t = temp_of(temp, b, force_greedy);
+  // Every load is issued before any is waited for: the decision, the
+  // temperature, the uniform and this thread's draft token fly while the
+  // sums are staged (locate_draw reads them only after that, and returns -1
+  // for sequences that need no draw).
+  if (force_greedy) return;                     // every sequence greedy: nothing to draw
+  const float t = temp[b];
   // Thread i < K emits draft i: it keeps its own token (no wait for it here).
   const int my_draw = (int)threadIdx.x < K ? dtok[(size_t)b * K + threadIdx.x] : 0;
-  // (locate_draw fills the table and synchronises the block before it reads
-  // it.)
-  const int tok = locate_draw<T>(tgt + (size_t)d.trow * V, drf + (size_t)d.drow * V, d,
-                                 (double)uni[(size_t)b * (K + 1) + K], t, V, ncr,
+  const float u = uni[(size_t)b * (K + 1) + K];
+  const Decision d = dec[b];
+  const int tok = locate_draw<T>(tgt, drf, d, u, t, V, ncr,
                                  csum + (size_t)b * ncr, csub + (size_t)b * ncr * kSubPerChunk, s_exp,
                                  true);
+  if (tok < 0) return;
   emit_own(b, K, d.n, tok, my_draw, out, nacc, kv_len, counters);
 }
 
@@ -1491,13 +1533,10 @@ __global__ __launch_bounds__(kThreads, 4) void k_residual(
       }
     }
   }
-#pragma unroll
-  for (int off = 4; off > 0; off >>= 1) {
-    sq += shfl_xor_d(sq, off);
-    sp += shfl_xor_d(sp, off);
-    sa += shfl_xor_d(sa, off);
-    sb += shfl_xor_d(sb, off);
-  }
+  sq = group8_sum_d(sq);
+  sp = group8_sum_d(sp);
+  sa = group8_sum_d(sa);
+  sb = group8_sum_d(sb);
   if (s == 0) {
     const SubSums ss{sa, sb, sq, sp};
     csub[((size_t)b * ncr + cr) * kSubPerChunk + sub_i] = ss;
@@ -1771,8 +1810,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_step(
   }
   __syncthreads();
   if (!s_draw) return;
-  const int tk = locate_draw<T>(tgt + (size_t)d.trow * V, drf + (size_t)d.drow * V, d,
-                                (double)s_u[0], t, V, ncr, cg,
+  const int tk = locate_draw<T>(tgt, drf, d, s_u[0], t, V, ncr, cg,
                                 csub + (size_t)b * ncr * kSubPerChunk, s_exp, false);
   emit_tree(b, N, s_n, tk, out_tok, out_node, nacc, kv_len, counters);
   if (tid == 0) dec[b].mode = kModeNone;
