@@ -541,7 +541,7 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
   // The share's first segment.
   Seg cur;
   cur.b = b;
-  cur.np = npairs_of(kv_len, b, K1, np_cap);
+  cur.np = npairs_from_len(L0b, K1, np_cap);     // L0b is kv_len[b], already read
   cur.g = (u0 - off_b) / cur.np;
   cur.off = off_b;
   cur.p_lo = (u0 - off_b) - cur.g * cur.np;
