@@ -46,22 +46,32 @@ def test_no_gpu_exits_nonzero():
 
 
 def test_traffic_follows_the_source_hash(tmp_path, monkeypatch):
+    """bench.py reports the recorded traffic only while the listed sources
+    still hash to the recorded value (checked on a copy, so the test does not
+    depend on the committed record being current)."""
     sys.path.insert(0, ROOT)
     import bench
     rec_path = os.path.join(ROOT, "profiles", "attn_llama8b_b64_traffic.json")
     with open(rec_path) as f:
         rec = json.load(f)
-    # Recorded on the current sources: the figure is reported.
-    assert bench._traffic() == rec["bytes_per_launch"]
-    # A record whose hash does not match its files is ignored.
-    stale = dict(rec, source_sha256_16="0" * 16)
     fake_root = tmp_path
     (fake_root / "profiles").mkdir()
-    (fake_root / "profiles" / "attn_llama8b_b64_traffic.json").write_text(json.dumps(stale))
     for p in rec["source_files"]:
         dst = fake_root / p
         dst.parent.mkdir(parents=True, exist_ok=True)
         with open(os.path.join(ROOT, p), "rb") as f:
             dst.write_bytes(f.read())
     monkeypatch.setattr(bench, "ROOT", str(fake_root))
+    rec_file = fake_root / "profiles" / "attn_llama8b_b64_traffic.json"
+    # A record taken on these very files: the figure is reported.
+    good = dict(rec, source_sha256_16=bench._files_hash(rec["source_files"]))
+    rec_file.write_text(json.dumps(good))
+    assert bench._traffic() == rec["bytes_per_launch"]
+    # A record whose hash does not match its files is ignored.
+    rec_file.write_text(json.dumps(dict(rec, source_sha256_16="0" * 16)))
+    assert bench._traffic() is None
+    # So is one whose files changed after it was taken.
+    rec_file.write_text(json.dumps(good))
+    first = fake_root / rec["source_files"][0]
+    first.write_bytes(first.read_bytes() + b"\n// edited\n")
     assert bench._traffic() is None
