@@ -20,23 +20,25 @@
 //               These statistics feed the accept tests, whose decisions are
 //               only sensitive at the 1e-5 level.  The wave whose chunk holds
 //               a row's drafted token also records that token's logit.
-//   k_decide    per sequence: merge the row statistics in a fixed order, run
+//   k_decide_residual  per (sequence, 8192-entry chunk), in two steps.
+//               The decision: merge the row statistics in a fixed order, run
 //               the K accept tests in parallel on the recorded logits and
-//               take the first rejection; finish a greedy sequence, or record
-//               the decision.
-//   k_residual  per (sequence, 8192-entry chunk): summarise its chunk of the
-//               one row pair the final draw needs (target and draft row n, or
-//               target row K for the bonus) in float64, per 256-entry
-//               sub-chunk and per chunk: sum e_q, sum e_p and the same two
-//               sums over the entries with q > c p, with e = 2^((x - xmax) c)
-//               to a few ulp.  They give the exact normalisers and residual
-//               masses, so the row pair is read only once more.
+//               take the first rejection (every block of the sequence takes
+//               the same decision; its first block finishes a greedy
+//               sequence, or records the decision for the draw).  Then the
+//               pass: summarise this chunk of the one row pair the final
+//               draw needs (target and draft row n, or target row K for the
+//               bonus) in float64, per 256-entry sub-chunk and per chunk:
+//               sum e_q, sum e_p and the same two sums over the entries with
+//               q > c p, with e = 2^((x - xmax) c) to a few ulp.  They give
+//               the exact normalisers and residual masses, so the row pair is
+//               read only once more.
 //   k_locate    per sampling sequence: float64 prefix scans over the chunk
 //               masses, then the sub-chunk masses, then one 256-entry run of
 //               exact weights; emit the tokens and commit kv_len.
 // The final draw's weights are exact to 2e-13 relative, so the draw agrees
 // with a float64 reference except within ~1e-12 of probability mass around
-// the CDF edges.  (Handing a sequence from its last k_residual block to the
+// the CDF edges.  (Handing a sequence from its last pass block to the
 // draw inside one kernel would need device-scope fences per block, which
 // write back and invalidate each XCD's L2; measured, a kernel boundary is
 // far cheaper.)
@@ -46,15 +48,16 @@
 // the first child of each node passes its test (greedy sequences finish
 // there).  After a rejection the next sibling is tested against the residual
 // q' = (q - coef p)_+ / Z, where coef starts at 1 and grows by Z with every
-// further rejection; Z needs one exact pass over the node's row pair.  So the
-// tree runs in rounds of k_residual + k_tree_step, each round one such pass
+// further rejection; Z needs one exact pass over the node's row pair (the
+// chain's pass, in k_residual).  So the tree runs in rounds of k_residual +
+// k_tree_step, each round one such pass
 // per sequence that still needs one; the host knows from the tree's shape how
 // many rounds the longest walk can take.
 // No floating-point atomics and fixed reduction orders: results are bitwise
 // reproducible run to run.
 
 // Contraction off: merges must stay symmetric in their operands, and the
-// weights of k_locate must equal those of k_residual bit for bit.  Fused
+// weights of k_locate must equal those of the pass bit for bit.  Fused
 // multiply-adds that are wanted are written out.
 #pragma clang fp contract(off)
 
@@ -409,6 +412,51 @@ __device__ __forceinline__ void merge_row(const float2* __restrict__ pr, int nc,
     a = xr;
     bb = s;
   }
+}
+
+// The same merge by a group of 16 lanes (one DPP row), for a block that
+// merges many rows at once: lane j takes chunks j, j + 16, ... in order, then
+// the group combines by DPP moves (xor 1, xor 2, mirror in 8, mirror in 16).
+// Each step is a symmetric merge, so both lanes of a pairing, and in the end
+// all 16 lanes, hold the same values.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, true));
+}
+
+template <int kCtrl>
+__device__ __forceinline__ void group16_step(bool greedy, float& x, float& y, float& xr) {
+  const float x2 = dpp_f<kCtrl>(x), y2 = dpp_f<kCtrl>(y), xr2 = dpp_f<kCtrl>(xr);
+  if (greedy) {
+    int i = __float_as_int(y);
+    am_merge(x, i, x2, __float_as_int(y2));
+    y = __int_as_float(i);
+  } else {
+    ms_merge(x, y, x2, y2);
+    xr = fmaxf(xr, xr2);
+  }
+}
+
+__device__ __forceinline__ void merge_row16(const float2* __restrict__ pr, int nc, bool greedy, float c,
+                                            int j, float& a, float& bb) {
+  float x = -INFINITY, y = greedy ? __int_as_float(INT32_MAX) : 0.f, xr = -INFINITY;
+  for (int k = j; k < nc; k += 16) {
+    const float2 p = pr[k];
+    if (greedy) {
+      int i = __float_as_int(y);
+      am_merge(x, i, p.x, __float_as_int(p.y));
+      y = __int_as_float(i);
+    } else {
+      ms_merge(x, y, p.x * c, p.y);
+      xr = fmaxf(xr, p.x);
+    }
+  }
+  group16_step<0xB1>(greedy, x, y, xr);     // quad_perm [1,0,3,2]
+  group16_step<0x4E>(greedy, x, y, xr);     // quad_perm [2,3,0,1]
+  group16_step<0x141>(greedy, x, y, xr);    // row_half_mirror
+  group16_step<0x140>(greedy, x, y, xr);    // row_mirror
+  a = greedy ? x : xr;
+  bb = y;
 }
 
 // Write the K+1 output slots (threads 0..K of the block), the accepted count
@@ -813,7 +861,7 @@ __global__ __launch_bounds__(kFilterThreads, 4) void k_filter(
   const T* src = (j <= K) ? tgt + ((size_t)b * (K + 1) + j) * (size_t)V
                           : drf + ((size_t)b * K + (j - K - 1)) * (size_t)V;
   const float c = kLog2e / t;
-  // The row's raw maximum, merged from the sweep's chunk maxima as k_decide does.
+  // The row's raw maximum, merged from the sweep's chunk maxima as the decision does.
   if (wave == 0) {
     float xr = -INFINITY;
     for (int k = lane; k < nc; k += 64) xr = fmaxf(xr, part[(size_t)row * nc + k].x);
@@ -960,56 +1008,64 @@ __global__ __launch_bounds__(kFilterThreads, 4) void k_filter(
 }
 
 // ---------------------------------------------------------------------------
-// k_decide: grid (B); block 1024.
+// The chain's decision for sequence b (a block of NTH threads): merges the
+// sweep's chunk statistics of its rows (one wave per row, fixed order), runs
+// the K accept tests on K lanes at once (q/p in the log domain, float64),
+// takes the first rejection by ballot and describes the pass that follows.
+// Every thread gets the decision.  With `outputs`, a greedy sequence is also
+// emitted and committed here, and the decision is stored to dec[b] for the
+// final draw.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kDecideThreads) void k_decide(
-    const int32_t* __restrict__ dtok, const float* __restrict__ uni, const float* __restrict__ temp,
-    int K, int V, int nc, int force_greedy, const float2* __restrict__ part,
-    const float* __restrict__ xd, Decision* __restrict__ dec,
-    int32_t* __restrict__ out, int32_t* __restrict__ nacc, int32_t* __restrict__ kv_len,
-    unsigned long long* counters, const RowFilter* __restrict__ filt, int key16) {
+template <int NTH>
+__device__ Decision decide_chain(int b, const int32_t* __restrict__ dtok, const float* __restrict__ uni,
+                                 float t, int K, int V, int nc, const float2* __restrict__ part,
+                                 const float* __restrict__ xd, const RowFilter* __restrict__ filt,
+                                 int key16, bool outputs, Decision* __restrict__ dec,
+                                 int32_t* __restrict__ out, int32_t* __restrict__ nacc,
+                                 int32_t* __restrict__ kv_len, unsigned long long* counters) {
   __shared__ float s_a[kMaxRows], s_b[kMaxRows];
   __shared__ uint32_t s_kmin[kMaxRows];
-  __shared__ float2 s_part[kPartStage];
   __shared__ float s_xq[SV_MAX_K], s_xp[SV_MAX_K], s_u[SV_MAX_K];
   __shared__ int s_d[SV_MAX_K], s_draw[SV_MAX_K];
   __shared__ int s_n;
-  const int b = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int R = 2 * K + 1;
-  const float t = temp_of(temp, b, force_greedy);
   const bool greedy = !(t > 0.f);
   const int rows = greedy ? K + 1 : R;
   const float c = greedy ? 0.f : kLog2e / t;
-  // All loads are independent: the row statistics of this sequence (into
-  // LDS when they fit), the drafted tokens, their logits (recorded by the
-  // sweep) and the uniforms.
+  // All loads are independent: the drafted tokens, their logits (recorded
+  // by the sweep), the uniforms, the filters and the row statistics.
   const float2* pb = part + (size_t)b * R * nc;
-  const bool staged = rows * nc <= kPartStage;
-  if (staged)
-    for (int k = tid; k < rows * nc; k += kDecideThreads) s_part[k] = pb[k];
+  int draw = 0;
+  float xq = 0.f, xp = 0.f, uu = 0.f;
   if (tid < K) {
-    const int draw = dtok[(size_t)b * K + tid];
-    const int d = clampi(draw, 0, V - 1);
-    s_draw[tid] = draw;
-    s_d[tid] = d;
+    draw = dtok[(size_t)b * K + tid];
     if (!greedy) {
-      s_xq[tid] = xd[((size_t)b * K + tid) * 2];
-      s_xp[tid] = xd[((size_t)b * K + tid) * 2 + 1];
-      s_u[tid] = uni[(size_t)b * (K + 1) + tid];
+      xq = xd[((size_t)b * K + tid) * 2];
+      xp = xd[((size_t)b * K + tid) * 2 + 1];
+      uu = uni[(size_t)b * (K + 1) + tid];
     }
   }
-  __syncthreads();
-  for (int r = wave; r < rows; r += kDecideThreads / 64) {
+  // Row statistics: 16 lanes per row, NTH / 16 rows at a time.
+  for (int r0 = 0; r0 < rows; r0 += NTH / 16) {
+    const int r = r0 + (tid >> 4);
+    const bool head = (tid & 15) == 0 && r < rows;
+    // A filtered row: its law is renormalised over the kept set.
+    const RowFilter rf = (filt && !greedy && head) ? filt[(size_t)b * R + r] : RowFilter{0u, 0u, 0.0};
     float a, bb;
-    merge_row(staged ? s_part + r * nc : pb + (size_t)r * nc, nc, greedy, c, lane, a, bb);
-    if (lane == 0) {
-      // A filtered row: its law is renormalised over the kept set.
-      const RowFilter rf = (filt && !greedy) ? filt[(size_t)b * R + r] : RowFilter{0u, 0u, 0.0};
+    merge_row16(pb + (size_t)min(r, rows - 1) * nc, nc, greedy, c, tid & 15, a, bb);
+    if (head) {
       s_a[r] = a;
       s_b[r] = rf.key_min ? (float)rf.mass : bb;
       s_kmin[r] = rf.key_min;
     }
+  }
+  if (tid < K) {
+    s_draw[tid] = draw;
+    s_d[tid] = clampi(draw, 0, V - 1);
+    s_xq[tid] = xq;
+    s_xp[tid] = xp;
+    s_u[tid] = uu;
   }
   __syncthreads();
   // Accept tests of all K drafts at once (lanes of wave 0), then the first
@@ -1039,11 +1095,14 @@ __global__ __launch_bounds__(kDecideThreads) void k_decide(
   __syncthreads();
   const int n = s_n;
   if (greedy) {
-    if (tid == 0) dec[b] = Decision{kModeNone, n, 0, 0, 0.f, 0.f, 0.0, 0.0, 0.0};
-    emit(b, K, n, __float_as_int(s_b[n]), s_draw, out, nacc, kv_len, counters);
-    return;
+    const Decision dd{kModeNone, n, 0, 0, 0.f, 0.f, 0.0, 0.0, 0.0};
+    if (outputs) {
+      if (tid == 0) dec[b] = dd;
+      emit(b, K, n, __float_as_int(s_b[n]), s_draw, out, nacc, kv_len, counters);
+    }
+    return dd;
   }
-  if (tid != 0) return;
+  // Every thread forms the same decision from the same LDS values.
   const double cd = kLog2eD / (double)t;
   Decision dd{n < K ? kModeResid : kModeQ, n, b * (K + 1) + n, n < K ? b * K + n : 0,
               s_a[n], n < K ? s_a[K + 1 + n] : 0.f, 0.0, 1.0, 0.0, s_kmin[n],
@@ -1055,7 +1114,8 @@ __global__ __launch_bounds__(kDecideThreads) void k_decide(
     const double sp = (double)s_b[K + 1 + n] * exp2((double)(dd.xmp * c) - (double)dd.xmp * cd);
     dd.theta = log2(sq) - log2(sp);
   }
-  dec[b] = dd;
+  if (outputs && tid == 0) dec[b] = dd;
+  return dd;
 }
 
 // Float64 2^a for a <= 0 (a slightly above 0 is fine too), to a relative
@@ -1412,25 +1472,19 @@ __device__ __forceinline__ void mask_row(float (&x)[Vec16<T>::N], uint32_t kmin)
 // so an instruction of the wave still reads 8 whole lines, and a sub-chunk's
 // sums need only 3 butterfly steps.
 // ---------------------------------------------------------------------------
-template <typename T, bool kAligned, bool kMask = false>
-__global__ __launch_bounds__(kThreads, 4) void k_residual(
-    const T* __restrict__ tgt, const T* __restrict__ drf, const float* __restrict__ temp,
-    int V, int ncr, int force_greedy, const Decision* __restrict__ dec,
-    ChunkSums* __restrict__ csum, SubSums* __restrict__ csub) {
+template <typename T, bool kAligned, bool kMask>
+__device__ __forceinline__ void residual_pass(const T* __restrict__ tgt, const T* __restrict__ drf,
+                                              const Decision& d, float t, int V, int ncr, int b, int cr,
+                                              ChunkSums* __restrict__ csum, SubSums* __restrict__ csub) {
   constexpr int VN = Vec16<T>::N;
   constexpr int kLine = 8 * VN;                   // entries per 8-lane load (128 bytes)
   constexpr int IT = kSub / kLine;                // loads per lane per row
   static_assert(kThreads / 8 == kSubPerChunk, "one 8-lane group per sub-chunk");
   __shared__ double s_exp[kExpTable];
   __shared__ SubSums s_sub[kSubPerChunk];
-  const int b = blockIdx.x;
-  const int cr = blockIdx.y;
   const int tid = threadIdx.x;
   const int sub_i = tid >> 3, s = tid & 7;
-  const Decision d = dec[b];
-  if (d.mode == kModeNone) return;
   const bool bonus = d.mode == kModeQ;
-  const float t = temp_of(temp, b, force_greedy);
   const double cd = kLog2eD / (double)t;
   const T* trow = tgt + (size_t)d.trow * (size_t)V;
   const T* drow = drf + (size_t)d.drow * (size_t)V;
@@ -1552,6 +1606,39 @@ __global__ __launch_bounds__(kThreads, 4) void k_residual(
     for (int j = 0; j < kSubPerChunk; ++j) acc += reinterpret_cast<const double*>(&s_sub[j])[comp];
     reinterpret_cast<double*>(csum + (size_t)b * ncr + cr)[tid] = acc;
   }
+}
+
+// Tree rounds: the pass the walk's decision asks for.
+template <typename T, bool kAligned>
+__global__ __launch_bounds__(kThreads, 4) void k_residual(
+    const T* __restrict__ tgt, const T* __restrict__ drf, const float* __restrict__ temp,
+    int V, int ncr, int force_greedy, const Decision* __restrict__ dec,
+    ChunkSums* __restrict__ csum, SubSums* __restrict__ csub) {
+  const int b = blockIdx.x;
+  const Decision d = dec[b];
+  if (d.mode == kModeNone) return;
+  residual_pass<T, kAligned, false>(tgt, drf, d, temp_of(temp, b, force_greedy), V, ncr, b,
+                                    blockIdx.y, csum, csub);
+}
+
+// The chain: every block first takes its sequence's decision itself (the
+// same values in each; block 0 also stores it and emits greedy sequences),
+// which saves a kernel boundary and a dependent read of the decision before
+// the rows can be requested.
+template <typename T, bool kAligned, bool kMask = false>
+__global__ __launch_bounds__(kThreads, 4) void k_decide_residual(
+    const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ dtok,
+    const float* __restrict__ uni, const float* __restrict__ temp, int K, int V, int nc, int ncr,
+    int force_greedy, const float2* __restrict__ part, const float* __restrict__ xd,
+    const RowFilter* __restrict__ filt, int key16, Decision* __restrict__ dec,
+    int32_t* __restrict__ out, int32_t* __restrict__ nacc, int32_t* __restrict__ kv_len,
+    unsigned long long* counters, ChunkSums* __restrict__ csum, SubSums* __restrict__ csub) {
+  const int b = blockIdx.x;
+  const float t = temp_of(temp, b, force_greedy);
+  const Decision d = decide_chain<kThreads>(b, dtok, uni, t, K, V, nc, part, xd, filt, key16,
+                                            blockIdx.y == 0, dec, out, nacc, kv_len, counters);
+  if (d.mode == kModeNone) return;
+  residual_pass<T, kAligned, kMask>(tgt, drf, d, t, V, ncr, b, blockIdx.y, csum, csub);
 }
 
 // ---------------------------------------------------------------------------
@@ -1858,15 +1945,15 @@ static hipError_t launch_all(const void* tgt, const void* drf, const int32_t* dt
   if (filtered)
     hipLaunchKernelGGL((k_filter<T, kAligned>), dim3(B * R), dim3(kFilterThreads), 0, st, t, d, temp,
                        top_k, top_p, K, V, nc, force_greedy, part, filt);
-  hipLaunchKernelGGL(k_decide, dim3(B), dim3(kDecideThreads), 0, st, dtok, uni, temp, K, V, nc,
-                     force_greedy, part, xd, dec, out, nacc, kv_len, counters, filt,
-                     sizeof(T) == 2 ? 1 : 0);
+  const int key16 = sizeof(T) == 2 ? 1 : 0;
   if (filtered)
-    hipLaunchKernelGGL((k_residual<T, kAligned, true>), dim3(B, ncr), dim3(kThreads), 0, st, t, d, temp,
-                       V, ncr, force_greedy, dec, csum, csub);
+    hipLaunchKernelGGL((k_decide_residual<T, kAligned, true>), dim3(B, ncr), dim3(kThreads), 0, st, t,
+                       d, dtok, uni, temp, K, V, nc, ncr, force_greedy, part, xd, filt, key16, dec, out,
+                       nacc, kv_len, counters, csum, csub);
   else
-    hipLaunchKernelGGL((k_residual<T, kAligned>), dim3(B, ncr), dim3(kThreads), 0, st, t, d, temp, V,
-                       ncr, force_greedy, dec, csum, csub);
+    hipLaunchKernelGGL((k_decide_residual<T, kAligned>), dim3(B, ncr), dim3(kThreads), 0, st, t, d,
+                       dtok, uni, temp, K, V, nc, ncr, force_greedy, part, xd, filt, key16, dec, out,
+                       nacc, kv_len, counters, csum, csub);
   hipLaunchKernelGGL((k_locate<T>), dim3(B), dim3(kThreads), 0, st, t, d, dtok, uni, temp, K, V, ncr,
                      force_greedy, csum, csub, dec, out, nacc, kv_len, counters);
   return hipGetLastError();
