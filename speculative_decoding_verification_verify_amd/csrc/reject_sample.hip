@@ -69,14 +69,13 @@
 namespace sv {
 
 constexpr int kThreads = 256;
-constexpr int kDecideThreads = 1024;  // one wave per row statistic merge
+constexpr int kDecideThreads = 1024;  // tree decision: 16 lanes per row statistic merge
 #ifndef SV_SWEEP_CHUNK
 #define SV_SWEEP_CHUNK 4096
 #endif
 constexpr int kSweepChunk = SV_SWEEP_CHUNK;   // entries per wave in k_sweep
 constexpr int kResChunk = 8192;       // entries per block in k_residual
 constexpr int kMaxRows = 2 * SV_MAX_K + 1;
-constexpr int kPartStage = 4096;      // row statistics staged in LDS per sequence (32 KB)
 constexpr double kLog2eD = 1.4426950408889634074;
 
 
@@ -385,38 +384,11 @@ __global__ __launch_bounds__(kThreads) void k_sweep(
   if (lane == 0) part[(size_t)row * nc + chunk] = res;
 }
 
-// Merge the nc chunk statistics of one row (one wave, fixed order).
-// Sampling rows give (raw max, sum relative to fl(raw max * c)).
-__device__ __forceinline__ void merge_row(const float2* __restrict__ pr, int nc, bool greedy, float c,
-                                          int lane, float& a, float& bb) {
-  if (greedy) {
-    float v = -INFINITY;
-    int i = INT32_MAX;
-    for (int k = lane; k < nc; k += 64) {
-      const float2 p = pr[k];
-      am_merge(v, i, p.x, __float_as_int(p.y));
-    }
-    wave_am_reduce(v, i);
-    a = v;
-    bb = __int_as_float(i);
-  } else {
-    float m = -INFINITY, s = 0.f, xr = -INFINITY;
-    for (int k = lane; k < nc; k += 64) {
-      const float2 p = pr[k];
-      ms_merge(m, s, p.x * c, p.y);
-      xr = fmaxf(xr, p.x);
-    }
-    wave_ms_reduce(m, s);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) xr = fmaxf(xr, __shfl_xor(xr, off, 64));
-    a = xr;
-    bb = s;
-  }
-}
-
-// The same merge by a group of 16 lanes (one DPP row), for a block that
-// merges many rows at once: lane j takes chunks j, j + 16, ... in order, then
-// the group combines by DPP moves (xor 1, xor 2, mirror in 8, mirror in 16).
+// Merge of the nc chunk statistics of one row by a group of 16 lanes (one
+// DPP row), fixed order: lane j takes chunks j, j + 16, ... in order, then the
+// group combines by DPP moves (xor 1, xor 2, mirror in 8, mirror in 16).
+// Sampling rows give (raw max, sum relative to fl(raw max * c)); greedy rows
+// (max value, lowest argmax).
 // Each step is a symmetric merge, so both lanes of a pairing, and in the end
 // all 16 lanes, hold the same values.
 template <int kCtrl>
@@ -1727,7 +1699,6 @@ __global__ __launch_bounds__(kDecideThreads) void k_tree_decide(
     TreeState* __restrict__ state, int32_t* __restrict__ out_tok, int32_t* __restrict__ out_node,
     int32_t* __restrict__ nacc, int32_t* __restrict__ kv_len, unsigned long long* counters) {
   __shared__ float2 s_rs[2 * kMaxTree];
-  __shared__ float2 s_part[kPartStage];
   __shared__ float s_xd[2 * kMaxTree], s_u[kMaxTree];
   __shared__ int s_tk[kMaxTree];
   __shared__ int s_n, s_tok;
@@ -1739,19 +1710,17 @@ __global__ __launch_bounds__(kDecideThreads) void k_tree_decide(
   const int rows = greedy ? N : R;
   const float c = greedy ? 0.f : kLog2e / t;
   const float2* pb = part + (size_t)b * R * nc;
-  const bool staged = rows * nc <= kPartStage;
-  // Every load at once: the row statistics, then this sequence's tokens,
-  // uniforms and recorded logits for the walk.
-  if (staged)
-    for (int k = tid; k < rows * nc; k += kDecideThreads) s_part[k] = pb[k];
+  // Every load at once: this sequence's tokens, uniforms and recorded logits
+  // for the walk, and the row statistics (merged by 16-lane groups, 64 rows
+  // per round).
   if (tid < N) s_tk[tid] = tok[(size_t)b * N + tid];
   if (!greedy && tid < N) s_u[tid] = uni[(size_t)b * N + tid];
   if (!greedy && tid < 2 * N) s_xd[tid] = xd[(size_t)b * N * 2 + tid];
-  __syncthreads();
-  for (int r = wave; r < rows; r += kDecideThreads / 64) {
+  for (int r0 = 0; r0 < rows; r0 += kDecideThreads / 16) {
+    const int r = r0 + (tid >> 4);
     float a, bb;
-    merge_row(staged ? s_part + r * nc : pb + (size_t)r * nc, nc, greedy, c, lane, a, bb);
-    if (lane == 0) s_rs[r] = make_float2(a, bb);
+    merge_row16(pb + (size_t)min(r, rows - 1) * nc, nc, greedy, c, tid & 15, a, bb);
+    if ((tid & 15) == 0 && r < rows) s_rs[r] = make_float2(a, bb);
   }
   __syncthreads();
   if (!greedy && tid < R) rowstat[(size_t)b * R + tid] = s_rs[tid];
