@@ -11,7 +11,8 @@
 // kept; the siblings of a node are tried one after another by recursive
 // rejection sampling, which keeps the output law exact.
 //
-// Four kernels on the caller's stream (chain):
+// Three kernels on the caller's stream (chain; four with top-k / top-p, whose
+// k_filter runs between the sweep and the decision):
 //   k_sweep     one pass over every logit row (the HBM-bound part): per 4096-
 //               entry chunk, the raw maximum and sum_v 2^(x_v c - m) in fp32
 //               (c = log2(e) / T), or the chunk argmax for greedy sequences.
@@ -21,7 +22,8 @@
 //               only sensitive at the 1e-5 level.  The wave whose chunk holds
 //               a row's drafted token also records that token's logit.
 //   k_decide_residual  per (sequence, 8192-entry chunk), in two steps.
-//               The decision: merge the row statistics in a fixed order, run
+//               The decision: merge the row statistics in a fixed order (16
+//               lanes per row, DPP steps), run
 //               the K accept tests in parallel on the recorded logits and
 //               take the first rejection (every block of the sequence takes
 //               the same decision; its first block finishes a greedy
@@ -50,9 +52,9 @@
 // q' = (q - coef p)_+ / Z, where coef starts at 1 and grows by Z with every
 // further rejection; Z needs one exact pass over the node's row pair (the
 // chain's pass, in k_residual).  So the tree runs in rounds of k_residual +
-// k_tree_step, each round one such pass
-// per sequence that still needs one; the host knows from the tree's shape how
-// many rounds the longest walk can take.
+// k_tree_step, each round one such pass per sequence that still needs one;
+// the host knows from the tree's shape how many rounds the longest walk can
+// take.
 // No floating-point atomics and fixed reduction orders: results are bitwise
 // reproducible run to run.
 
