@@ -87,6 +87,8 @@ enum : int {
   kModeNone = 0,    // nothing to do: greedy or finished
   kModeQ = 1,       // target row only: the draw is from q (bonus token)
   kModeResid = 2,   // target and draft row: weights (q - coef p)_+
+  kModePending = 3, // tree: the walk has ended; its draw (from the pass the
+                    // decision describes, mode in draw_mode) waits for k_tree_draw
 };
 struct Decision {
   int mode;
@@ -99,6 +101,7 @@ struct Decision {
                      // (q - coef_prev p)_+, which is then q (coef_prev = 0) or p
   uint32_t kq, kp;   // top-k / top-p filters: entries whose order key is below
                      // these weigh 0 (0: no filter)
+  int draw_mode;     // kModePending: the mode of the pass the draw is taken from
 };
 
 // ---- Top-k / top-p filters (readings: logits / T, then top-k, then top-p
@@ -1590,7 +1593,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_residual(
     ChunkSums* __restrict__ csum, SubSums* __restrict__ csub) {
   const int b = blockIdx.x;
   const Decision d = dec[b];
-  if (d.mode == kModeNone) return;
+  if (d.mode == kModeNone || d.mode == kModePending) return;
   residual_pass<T, kAligned, false>(tgt, drf, d, temp_of(temp, b, force_greedy), V, ncr, b,
                                     blockIdx.y, csum, csub);
 }
@@ -1762,9 +1765,12 @@ __global__ __launch_bounds__(kDecideThreads) void k_tree_decide(
 
 // ---------------------------------------------------------------------------
 // k_tree_step: grid (B); block 256.  One round after the pass k_residual made
-// for each active sequence: either the final draw (then the outputs), or the
-// next sibling's test against the exact residual, which schedules the next
-// pass (a further rejection, or a rejection or leaf below an accepted child).
+// for each active sequence: the next sibling's test against the exact
+// residual, which schedules the next pass (a further rejection, or a
+// rejection or leaf below an accepted child), or the end of the walk, whose
+// draw from this pass is left to k_tree_draw (the pass's sums stay in place:
+// no later pass of the sequence overwrites them).  So a round waits for no
+// draw, and all draws take one launch after the last round.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_tree_step(
@@ -1775,7 +1781,6 @@ __global__ __launch_bounds__(kThreads) void k_tree_step(
     Decision* __restrict__ dec, TreeState* __restrict__ state, int32_t* __restrict__ out_tok,
     int32_t* __restrict__ out_node, int32_t* __restrict__ nacc, int32_t* __restrict__ kv_len,
     unsigned long long* counters) {
-  __shared__ double s_exp[kExpTable];
   __shared__ float2 s_rs[2 * kMaxTree];
   __shared__ float s_xd[2 * kMaxTree], s_u[kMaxTree];
   __shared__ int s_tk[kMaxTree];
@@ -1791,13 +1796,12 @@ __global__ __launch_bounds__(kThreads) void k_tree_step(
   }
   if (tid < 2 * N) s_xd[tid] = xd[(size_t)b * N * 2 + tid];
   const Decision d = dec[b];
-  if (d.mode == kModeNone) return;
+  if (d.mode == kModeNone || d.mode == kModePending) return;
   const TreeState st = state[b];
   __syncthreads();
   const float t = temp_of(temp, b, force_greedy);
   const double cd = kLog2eD / (double)t;
   const ChunkSums* cg = csum + (size_t)b * ncr;
-  fill_exp_table(s_exp);
   if (wave == 0) {
     int draw = 1, n = st.n;
     if (!st.fin) {
@@ -1867,11 +1871,39 @@ __global__ __launch_bounds__(kThreads) void k_tree_step(
     if (lane == 0) { s_draw = draw; s_n = n; }
   }
   __syncthreads();
-  if (!s_draw) return;
-  const int tk = locate_draw<T>(tgt, drf, d, s_u[0], t, V, ncr, cg,
-                                csub + (size_t)b * ncr * kSubPerChunk, s_exp, false);
-  emit_tree(b, N, s_n, tk, out_tok, out_node, nacc, kv_len, counters);
-  if (tid == 0) dec[b].mode = kModeNone;
+  if (s_draw && tid == 0) {
+    Decision pd = d;
+    pd.draw_mode = d.mode;
+    pd.mode = kModePending;
+    pd.n = s_n;
+    dec[b] = pd;
+  }
+}
+
+// k_tree_draw: grid (B); block 256.  The draws of the walks that ended in
+// any round, each from the last pass of its sequence, then the outputs.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_tree_draw(
+    const T* __restrict__ tgt, const T* __restrict__ drf, const float* __restrict__ uni,
+    const float* __restrict__ temp, int N, int V, int ncr, int force_greedy,
+    const ChunkSums* __restrict__ csum, const SubSums* __restrict__ csub,
+    Decision* __restrict__ dec, int32_t* __restrict__ out_tok, int32_t* __restrict__ out_node,
+    int32_t* __restrict__ nacc, int32_t* __restrict__ kv_len, unsigned long long* counters) {
+  __shared__ double s_exp[kExpTable];
+  const int b = blockIdx.x;
+  if (force_greedy) return;                     // greedy walks finish in k_tree_decide
+  const float t = temp[b];
+  const float u = uni[(size_t)b * N];           // node 0's slot: the final draw
+  Decision d = dec[b];
+  // locate_draw reads d only after staging the sums; a sequence with no
+  // pending draw comes back as -1.
+  if (d.mode == kModePending) d.mode = d.draw_mode;
+  else d.mode = kModeNone;
+  const int tk = locate_draw<T>(tgt, drf, d, u, t, V, ncr, csum + (size_t)b * ncr,
+                                csub + (size_t)b * ncr * kSubPerChunk, s_exp, true);
+  if (tk < 0) return;
+  emit_tree(b, N, d.n, tk, out_tok, out_node, nacc, kv_len, counters);
+  if (threadIdx.x == 0) dec[b].mode = kModeNone;
 }
 
 struct RejectPlan {
@@ -2021,6 +2053,9 @@ static hipError_t launch_tree(const void* tgt, const void* drf, const TreeShape&
                        ncr, force_greedy, r == rounds ? 1 : 0, rowstat, xd, csum, csub, dec, state,
                        out_tok, out_node, nacc, kv_len, counters);
   }
+  if (rounds > 0)
+    hipLaunchKernelGGL((k_tree_draw<T>), dim3(B), dim3(kThreads), 0, st, t, d, uni, temp, shape.n, V,
+                       ncr, force_greedy, csum, csub, dec, out_tok, out_node, nacc, kv_len, counters);
   return hipGetLastError();
 }
 
