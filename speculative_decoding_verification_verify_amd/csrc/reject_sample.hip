@@ -1115,10 +1115,6 @@ __device__ Decision decide_chain(int b, const int32_t* __restrict__ dtok, const 
 // any of them.
 constexpr int kExpTable = 256;
 
-__device__ __forceinline__ void fill_exp_table(double* tab) {
-  for (int j = threadIdx.x; j < kExpTable; j += blockDim.x) tab[j] = exp2((double)j * (1.0 / 256));
-}
-
 struct Exp2Arg {
   double r;   // 256 a - k
   int k;      // round(256 a)
