@@ -417,8 +417,7 @@ __device__ __forceinline__ void group16_step(bool greedy, float& x, float& y, fl
 __device__ __forceinline__ void merge_row16(const float2* __restrict__ pr, int nc, bool greedy, float c,
                                             int j, float& a, float& bb) {
   float x = -INFINITY, y = greedy ? __int_as_float(INT32_MAX) : 0.f, xr = -INFINITY;
-  for (int k = j; k < nc; k += 16) {
-    const float2 p = pr[k];
+  auto take = [&](const float2 p) {
     if (greedy) {
       int i = __float_as_int(y);
       am_merge(x, i, p.x, __float_as_int(p.y));
@@ -427,7 +426,18 @@ __device__ __forceinline__ void merge_row16(const float2* __restrict__ pr, int n
       ms_merge(x, y, p.x * c, p.y);
       xr = fmaxf(xr, p.x);
     }
-  }
+  };
+  // The first four chunks of the lane are requested together (clamped
+  // indices, the duplicates not merged), then merged in order: one round
+  // trip for rows of up to 64 chunks (V <= 2^18 at 4096 per chunk).
+  constexpr int kPre = 4;
+  float2 pp[kPre];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) pp[u] = pr[min(j + 16 * u, nc - 1)];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u)
+    if (j + 16 * u < nc) take(pp[u]);
+  for (int k = j + 16 * kPre; k < nc; k += 16) take(pr[k]);
   group16_step<0xB1>(greedy, x, y, xr);     // quad_perm [1,0,3,2]
   group16_step<0x4E>(greedy, x, y, xr);     // quad_perm [2,3,0,1]
   group16_step<0x141>(greedy, x, y, xr);    // row_half_mirror
@@ -1079,20 +1089,28 @@ __device__ Decision decide_chain(int b, const int32_t* __restrict__ dtok, const 
     }
     return dd;
   }
-  // Every thread forms the same decision from the same LDS values.
-  const double cd = kLog2eD / (double)t;
-  Decision dd{n < K ? kModeResid : kModeQ, n, b * (K + 1) + n, n < K ? b * K + n : 0,
-              s_a[n], n < K ? s_a[K + 1 + n] : 0.f, 0.0, 1.0, 0.0, s_kmin[n],
-              n < K ? s_kmin[K + 1 + n] : 0u};
-  if (n < K) {
-    // The sweep's normalisers, moved from the fl(xmax c) frame to the
-    // 2^((x - xmax) c) frame of the exact pass.
-    const double sq = (double)s_b[n] * exp2((double)(dd.xmq * c) - (double)dd.xmq * cd);
-    const double sp = (double)s_b[K + 1 + n] * exp2((double)(dd.xmp * c) - (double)dd.xmp * cd);
-    dd.theta = log2(sq) - log2(sp);
+  // One wave forms the decision (its float64 exp2 / log2 would cost every
+  // wave of every block the same VALU time) and hands it over through LDS.
+  __shared__ Decision s_dec;
+  if (wave == 0) {
+    const double cd = kLog2eD / (double)t;
+    Decision dd{n < K ? kModeResid : kModeQ, n, b * (K + 1) + n, n < K ? b * K + n : 0,
+                s_a[n], n < K ? s_a[K + 1 + n] : 0.f, 0.0, 1.0, 0.0, s_kmin[n],
+                n < K ? s_kmin[K + 1 + n] : 0u};
+    if (n < K) {
+      // The sweep's normalisers, moved from the fl(xmax c) frame to the
+      // 2^((x - xmax) c) frame of the exact pass.
+      const double sq = (double)s_b[n] * exp2((double)(dd.xmq * c) - (double)dd.xmq * cd);
+      const double sp = (double)s_b[K + 1 + n] * exp2((double)(dd.xmp * c) - (double)dd.xmp * cd);
+      dd.theta = log2(sq) - log2(sp);
+    }
+    if (lane == 0) {
+      s_dec = dd;
+      if (outputs) dec[b] = dd;
+    }
   }
-  if (outputs && tid == 0) dec[b] = dd;
-  return dd;
+  __syncthreads();
+  return s_dec;
 }
 
 // Float64 2^a for a <= 0 (a slightly above 0 is fine too), to a relative
