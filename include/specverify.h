@@ -25,8 +25,9 @@
  *  - Every pointer argument of the compute calls is device memory owned by
  *    the caller.  The library allocates no device memory, frees nothing and
  *    keeps no mutable global state; scratch memory is the caller's
- *    workspace.  The host page pool (spec_pages_*) is host state owned by
- *    its handle.
+ *    workspace.  The one exception is spec_reject_sample_noalloc, whose
+ *    workspace is a fixed device array of the library (one per device).
+ *    The host page pool (spec_pages_*) is host state owned by its handle.
  *  - Calls are asynchronous on `hip_stream` (a hipStream_t; NULL = the
  *    default stream).  Argument errors are detected on the host and
  *    returned before anything is launched.  A failed launch returns
@@ -225,6 +226,36 @@ int spec_reject_sample(const void* target_logits, const void* draft_logits,
                        void* hip_stream);
 
 size_t spec_reject_sample_workspace_bytes(int B, int K, int V);
+
+/*
+ * spec_reject_sample_noalloc -- spec_reject_sample for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the workspace is a file-scope device
+ * array of the library instead of a caller buffer.  The call itself allocates
+ * nothing and calls no allocating routine; the caller still provides every
+ * input and output.
+ *
+ * Arguments, layouts, results and errors are those of spec_reject_sample
+ * without workspace / workspace_bytes.  Limit: spec_reject_sample_workspace_
+ * bytes(B, K, V) <= SV_NOALLOC_SCRATCH_BYTES (16 MiB: B = 256, K = 7,
+ * V = 128256 needs 5.4 MB), else SV_ERR_WORKSPACE and nothing is launched.
+ * Each device the library runs on holds its own copy of the array until the
+ * process ends; its address is looked up on the first call made with that
+ * device current (a failure there is SV_ERR_HIP).  The array keeps the last
+ * call's contents and needs no clearing.  Every call on one device shares
+ * that device's array: calls that overlap on one device (different streams,
+ * or host threads, without ordering between them) race and give undefined
+ * results; calls ordered on one stream are fine.  Validation mode
+ * (SPECVERIFY_VALIDATE) does not apply to this call: it stages inputs in
+ * host memory.
+ */
+#define SV_NOALLOC_SCRATCH_BYTES (16u << 20)
+int spec_reject_sample_noalloc(const void* target_logits, const void* draft_logits,
+                               const int32_t* draft_tokens, const float* uniforms,
+                               const float* temperature, int32_t* out_tokens,
+                               int32_t* num_accepted, int32_t* kv_len,
+                               unsigned long long* counters, int B, int K, int V, int dtype,
+                               void* hip_stream);
 
 /*
  * spec_reject_sample_filtered -- spec_reject_sample with top-k / top-p

@@ -24,7 +24,8 @@ import os
 
 __all__ = ["load", "lib_path", "exported_symbols", "verify_attn", "verify_attn_tree",
            "verify_attn_window", "kv_commit", "PagePool", "DraftLengthBandit", "accept_stats", "SV_WINDOW_READ", "SV_WINDOW_APPEND",
-           "reject_sample", "reject_sample_tree", "verify_attn_workspace_bytes",
+           "reject_sample", "reject_sample_noalloc", "reject_sample_tree",
+           "verify_attn_workspace_bytes", "NOALLOC_SCRATCH_BYTES",
            "reject_sample_workspace_bytes", "reject_sample_tree_workspace_bytes",
            "SpecVerifyError", "SV_F32", "SV_BF16", "STATUS", "EXPORTS"]
 
@@ -33,12 +34,13 @@ _LIB = None
 
 SV_F32, SV_BF16 = 0, 1
 SV_WINDOW_READ, SV_WINDOW_APPEND = 0, 1
+NOALLOC_SCRATCH_BYTES = 16 << 20     # SV_NOALLOC_SCRATCH_BYTES
 STATUS = {0: "SV_OK", -1: "SV_ERR_INVALID_ARG", -2: "SV_ERR_UNSUPPORTED",
           -3: "SV_ERR_WORKSPACE", -4: "SV_ERR_HIP", -5: "SV_ERR_NO_PAGES",
           -6: "SV_ERR_BAD_INPUT"}
 EXPORTS = ("spec_verify_attn", "spec_verify_attn_workspace_bytes", "spec_verify_attn_tree",
            "spec_verify_attn_window", "spec_kv_commit",
-           "spec_reject_sample", "spec_reject_sample_workspace_bytes",
+           "spec_reject_sample", "spec_reject_sample_workspace_bytes", "spec_reject_sample_noalloc",
            "spec_reject_sample_filtered", "spec_reject_sample_tree", "spec_reject_sample_tree_workspace_bytes",
            "spec_pages_create", "spec_pages_destroy", "spec_pages_reserve", "spec_pages_commit",
            "spec_pages_release", "spec_pages_free_count", "spec_pages_seq_blocks",
@@ -80,6 +82,9 @@ def load():
     lib.spec_reject_sample.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                        vp, sz, vp]
     lib.spec_reject_sample.restype = i32
+    lib.spec_reject_sample_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                               i32, vp]
+    lib.spec_reject_sample_noalloc.restype = i32
     lib.spec_reject_sample_filtered.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
                                                 i32, i32, vp, sz, vp]
     lib.spec_reject_sample_filtered.restype = i32
@@ -173,6 +178,11 @@ def _need(t, name, dtype=None, cuda=True):
         raise ValueError("%s must be contiguous" % name)
     if dtype is not None and t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+
+
+def _shape(t, name, shape):
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
 
 
 def verify_attn_workspace_bytes(B, K, Hq, Hkv, D, max_kv_len):
@@ -307,6 +317,46 @@ def reject_sample(target, draft, draft_tokens, uniforms, temperature, kv_len,
                                 _ptr(kv_len), _ptr(counters), B, K, V, dt, _ptr(workspace),
                                 ws_have, _stream(stream))
     _check("spec_reject_sample", st)
+    return out_tokens, num_accepted
+
+
+def reject_sample_noalloc(target, draft, draft_tokens, uniforms, temperature, kv_len,
+                          out_tokens, num_accepted, counters=None, stream=None):
+    """``spec_reject_sample_noalloc``: the verifier with the library's own
+    per-device scratch array as its workspace.  Every output is the
+    caller's (nothing is allocated here either); the shapes and results are
+    those of :func:`reject_sample`.  Returns (out_tokens, num_accepted)."""
+    import torch
+    lib = load()
+    _need(target, "target")
+    dt = _dtype_code(target)
+    if target.dim() != 3:
+        raise ValueError("target must be [B, K+1, V]")
+    B, K1, V = target.shape
+    K = K1 - 1
+    if draft is not None:
+        _need(draft, "draft", target.dtype)
+        _shape(draft, "draft", (B, K, V))
+    _need(draft_tokens, "draft_tokens", torch.int32)
+    _shape(draft_tokens, "draft_tokens", (B, K))
+    _need(uniforms, "uniforms", torch.float32)
+    _shape(uniforms, "uniforms", (B, K1))
+    _need(temperature, "temperature", torch.float32)
+    _shape(temperature, "temperature", (B,))
+    _need(kv_len, "kv_len", torch.int32)
+    _shape(kv_len, "kv_len", (B,))
+    _need(out_tokens, "out_tokens", torch.int32)
+    _shape(out_tokens, "out_tokens", (B, K1))
+    _need(num_accepted, "num_accepted", torch.int32)
+    _shape(num_accepted, "num_accepted", (B,))
+    if counters is not None:
+        _need(counters, "counters", torch.int64)
+        _shape(counters, "counters", (2,))
+    st = lib.spec_reject_sample_noalloc(_ptr(target), _ptr(draft), _ptr(draft_tokens),
+                                        _ptr(uniforms), _ptr(temperature), _ptr(out_tokens),
+                                        _ptr(num_accepted), _ptr(kv_len), _ptr(counters), B, K, V,
+                                        dt, _stream(stream))
+    _check("spec_reject_sample_noalloc", st)
     return out_tokens, num_accepted
 
 

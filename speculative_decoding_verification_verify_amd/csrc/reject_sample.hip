@@ -64,6 +64,7 @@
 #pragma clang fp contract(off)
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "validate.h"
@@ -2085,7 +2086,7 @@ static int reject_impl(const char* fn, const void* target_logits, const void* dr
                        const int32_t* top_k, const float* top_p, int32_t* out_tokens,
                        int32_t* num_accepted, int32_t* kv_len, unsigned long long* counters, int B,
                        int K, int V, int dtype, void* workspace, size_t workspace_bytes,
-                       void* hip_stream) {
+                       void* hip_stream, bool allow_validate = true) {
   if (B < 0 || K < 1 || V < 1) return SV_ERR_INVALID_ARG;
   if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_INVALID_ARG;
   if (K > SV_MAX_K) return SV_ERR_UNSUPPORTED;
@@ -2106,7 +2107,7 @@ static int reject_impl(const char* fn, const void* target_logits, const void* dr
   char* ws = static_cast<char*>(workspace);
   const uintptr_t align_bits = reinterpret_cast<uintptr_t>(target_logits) |
                                reinterpret_cast<uintptr_t>(drf);
-  const bool chk = sv::validate_on();
+  const bool chk = allow_validate && sv::validate_on();
   if (chk) {
     int s = sv::check_tokens(fn, draft_tokens, (long long)B * K, V, K, 0, st);
     if (s == SV_OK) s = sv::check_floats(fn, "uniforms", uniforms, (long long)B * (K + 1), true, st);
@@ -2164,6 +2165,67 @@ extern "C" int spec_reject_sample_filtered(const void* target_logits, const void
                      uniforms, temperature, top_k, top_p,
                      out_tokens, num_accepted, kv_len, counters, B, K, V, dtype, workspace,
                      workspace_bytes, hip_stream);
+}
+
+// ---------------------------------------------------------------------------
+// spec_reject_sample_noalloc: spec_reject_sample with its workspace in a
+// file-scope device array instead of a caller buffer, for callers that cannot
+// allocate.  Each device holds its own copy of `scratch` (the runtime places
+// it with the code object) until the process ends.  In host code `scratch`
+// names a host-side stand-in, not the device copy: its device address is
+// taken once per device with hipGetSymbolAddress, with that device current,
+// and only that address is ever handed to a kernel.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};   // device address of `scratch`, per device
+
+// The current device's copy of `scratch` (looked up on the first call made
+// with that device current), or nullptr with *status set.
+void* device_scratch(int* status) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *status = SV_ERR_HIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();   // the failure is reported here, not by a later call
+      *status = SV_ERR_HIP;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" int spec_reject_sample_noalloc(const void* target_logits, const void* draft_logits,
+                                          const int32_t* draft_tokens, const float* uniforms,
+                                          const float* temperature, int32_t* out_tokens,
+                                          int32_t* num_accepted, int32_t* kv_len,
+                                          unsigned long long* counters, int B, int K, int V,
+                                          int dtype, void* hip_stream) {
+  // Shape errors first, with the same codes as spec_reject_sample.
+  if (B < 0 || K < 1 || V < 1) return SV_ERR_INVALID_ARG;
+  if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_INVALID_ARG;
+  if (K > SV_MAX_K) return SV_ERR_UNSUPPORTED;
+  if ((long long)V >= (1LL << 31) / 4) return SV_ERR_UNSUPPORTED;
+  if (B == 0) return SV_OK;
+  const size_t need = spec_reject_sample_workspace_bytes(B, K, V);
+  if (need > (size_t)SV_NOALLOC_SCRATCH_BYTES) return SV_ERR_WORKSPACE;
+  int status = SV_OK;
+  void* ws = device_scratch(&status);
+  if (!ws) return status;
+  // The workspace needs no initial contents, so the array is not cleared.
+  return reject_impl("spec_reject_sample_noalloc", target_logits, draft_logits, draft_tokens,
+                     uniforms, temperature, nullptr, nullptr, out_tokens, num_accepted, kv_len,
+                     counters, B, K, V, dtype, ws, need, hip_stream, false);
 }
 
 extern "C" size_t spec_reject_sample_tree_workspace_bytes(int B, int N, int V) {

@@ -76,6 +76,22 @@ def test_reject_validation(lib):
     assert _reject(lib, B=0, ptrs=False) == 0            # empty batch: no-op
 
 
+def test_reject_noalloc_validation(lib):
+    # Every case returns before the scratch array is looked up (no GPU call).
+    f = lib.spec_reject_sample_noalloc
+    p = FAKE
+    assert f(p, p, p, p, p, p, p, p, None, -1, 3, 100, 1, None) == -1
+    assert f(p, p, p, p, p, p, p, p, None, 4, 0, 100, 1, None) == -1
+    assert f(p, p, p, p, p, p, p, p, None, 4, 3, 100, 9, None) == -1
+    assert f(p, p, p, p, p, p, p, p, None, 4, 17, 100, 1, None) == -2
+    assert f(None, None, None, None, None, None, None, None, None, 0, 3, 100, 1, None) == 0
+    # Beyond the fixed array: refused.
+    assert sv.reject_sample_workspace_bytes(4096, 16, 128256) > sv.NOALLOC_SCRATCH_BYTES
+    assert f(p, p, p, p, p, p, p, p, None, 4096, 16, 128256, 1, None) == -3
+    # The serving batches fit.
+    assert sv.reject_sample_workspace_bytes(256, 7, 128256) <= sv.NOALLOC_SCRATCH_BYTES
+
+
 def _attn(lib, B=2, K=7, Hq=32, Hkv=8, D=128, bs=16, nb=10, mbps=600, mkl=8192, dtype=1,
           ptrs=True, ws=1 << 30):
     p = FAKE if ptrs else None
