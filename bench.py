@@ -123,7 +123,7 @@ def main():
     B, K, V = (args.batch or cfg.B), cfg.K, cfg.V
     parent = None
     if args.tree:
-        from oracle.tree import tree_parents, tree_masks
+        from synth.tree import tree_parents, ancestor_bits
         shape = tuple(int(x) for x in args.tree.split(","))
         parent = tree_parents(shape)
         K = len(parent) - 1                       # window of N = K + 1 tree nodes
@@ -154,7 +154,7 @@ def main():
         kn, vn = to_device(kn_h, dev), to_device(vn_h, dev)
     anc = None
     if parent is not None:
-        anc = to_device(np.broadcast_to(tree_masks(parent).astype(np.uint32),
+        anc = to_device(np.broadcast_to(ancestor_bits(parent).astype(np.uint32),
                                         (B, K1)).copy().view(np.int32), dev)
     n_total = args.warmup + args.steps
     kv_bufs = [kv0.clone() for _ in range(n_total)]
@@ -393,7 +393,7 @@ def cpu_baseline(args, cfg, attn, host_rej, from_device, parent=None):
         if parent is None:
             oat.verify_attention(q, kc, vc, bt_local, kvl)
         else:
-            otr.tree_attention(q, kc, vc, bt_local, kvl, otr.tree_masks(parent))
+            otr.tree_attention(q, kc, vc, bt_local, kvl, parent)
         t_attn += time.perf_counter() - t0
         t0 = time.perf_counter()
         if parent is None:

@@ -13,11 +13,13 @@ Tree encoding (a reading: the pages fix none).  A window of N nodes,
 node 0 the root (the last accepted token x0), parent[i] < i for i >= 1
 (topological order), so node i's ancestors all precede it.  Node i's K/V
 sit at absolute position L0 + i of the cache.  anc[i] is a bit set: bit j is
-set iff node j is node i or one of its ancestors.
+set iff node j is node i or one of its ancestors (the device's input
+encoding, built by the input generators; here the path is found from
+parent[] directly).
 
 Attention.  Query node i attends keys [0, L0) and the window keys
-{L0 + j : j in anc[i]}: exactly causal attention over the path root -> i,
-for every node in one pass.  (Rotary positions follow the node's depth, not
+{L0 + j : j on the path root -> i}: exactly causal attention over that
+path, for every node in one pass.  (Rotary positions follow the node's depth, not
 its slot; they are applied to q and k before this step.)
 
 Verifier (the reading of "the surviving path is kept" that keeps the
@@ -51,43 +53,7 @@ import numpy as np
 from .reject import widen, softmax_rows, _inverse_cdf
 from .attention import gather_kv
 
-__all__ = ["tree_masks", "children_of", "tree_attention", "reject_sample_tree",
-           "chain_parents", "tree_parents"]
-
-
-def chain_parents(n):
-    """parent[] of a chain of n nodes: node i's parent is i - 1."""
-    return np.arange(-1, n - 1, dtype=np.int32)
-
-
-def tree_parents(shape):
-    """parent[] of a full tree given by branching factors per level, breadth
-    first: shape (2, 2, 2) is a root with 2 children, each with 2, each with 2
-    (15 nodes)."""
-    parents = [-1]
-    level = [0]
-    for k in shape:
-        nxt = []
-        for v in level:
-            for _ in range(k):
-                parents.append(v)
-                nxt.append(len(parents) - 1)
-        level = nxt
-    return np.asarray(parents, dtype=np.int32)
-
-
-def tree_masks(parent):
-    """Ancestor-or-self bit sets [N] (uint64) of a parent[] array."""
-    parent = np.asarray(parent, dtype=np.int64)
-    n = parent.shape[0]
-    anc = np.zeros(n, dtype=np.uint64)
-    for i in range(n):
-        a = np.uint64(1) << np.uint64(i)
-        if parent[i] >= 0:
-            assert parent[i] < i, "parents must precede their children"
-            a |= anc[parent[i]]
-        anc[i] = a
-    return anc
+__all__ = ["children_of", "path_to_root", "tree_attention", "reject_sample_tree"]
 
 
 def children_of(parent):
@@ -99,21 +65,37 @@ def children_of(parent):
     return kids
 
 
-def tree_attention(q, k_cache, v_cache, block_table, kv_len, anc, scale=None,
+def path_to_root(parent, i):
+    """Nodes on the path root -> i (both included), in increasing index
+    order, by walking parent links from i."""
+    parent = np.asarray(parent, dtype=np.int64)
+    path = [i]
+    while parent[path[-1]] >= 0:
+        p = int(parent[path[-1]])
+        if p >= path[-1]:
+            raise ValueError("parents must precede their children")
+        path.append(p)
+    if path[-1] != 0:
+        raise ValueError("node %d does not reach the root" % i)
+    return path[::-1]
+
+
+def tree_attention(q, k_cache, v_cache, block_table, kv_len, parent, scale=None,
                    batch_indices=None):
     """Attention outputs [B, N, Hq, D] (float64) for a flattened draft tree.
 
-    Args as oracle.attention.verify_attention, plus anc: [B, N] (or [N])
-    ancestor-or-self bit sets.  Node i sees keys [0, L0) and L0 + j for every
-    j in anc[i].
+    Args as oracle.attention.verify_attention, plus parent: [N] or [B, N]
+    parent arrays (one tree shape per sequence allowed).  Node i sees keys
+    [0, L0) and L0 + j for every node j on its path from the root (itself
+    included), found by walking its parent links.
     """
     qq = widen(q)
     b_sz, n, hq, d = qq.shape
     if scale is None or scale <= 0:
         scale = 1.0 / np.sqrt(d)
-    anc = np.asarray(anc, dtype=np.uint64)
-    if anc.ndim == 1:
-        anc = np.broadcast_to(anc, (b_sz, n))
+    par = np.asarray(parent, dtype=np.int64)
+    if par.ndim == 1:
+        par = np.broadcast_to(par, (b_sz, n))
     out = np.full(qq.shape, np.nan)
     idx = range(b_sz) if batch_indices is None else batch_indices
     for b in idx:
@@ -121,7 +103,7 @@ def tree_attention(q, k_cache, v_cache, block_table, kv_len, anc, scale=None,
         keys, vals = gather_kv(k_cache, v_cache, block_table, b, l0 + n)
         hkv = keys.shape[1]
         for i in range(n):
-            win = [j for j in range(n) if (int(anc[b, i]) >> j) & 1]
+            win = path_to_root(par[b], i)
             pos = np.concatenate([np.arange(l0), l0 + np.asarray(win, dtype=np.int64)])
             for h in range(hq):
                 g = h // (hq // hkv)

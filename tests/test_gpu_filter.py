@@ -39,7 +39,12 @@ def _filtered_drafts(inp, top_k, top_p, seed):
 
 
 def _case(sv, dev, seed, B, K, V, top_k, top_p, dtype="bf16", temp=1.0, sigma=0.8, idx=None,
-          std=2.0, spikes=None):
+          std=2.0, spikes=None, max_f3=None):
+    """One filtered call against the oracle.  F1 / F2 may exclude a few
+    sequences at most (as for the plain verifier); F3 at most ``max_f3``
+    (default 2 + B // 50): a row's top-p edge lies within 1e-6 of top_p only
+    when the entries at the edge carry little mass, which the cases that
+    allow more say why."""
     top_k = np.broadcast_to(np.asarray(top_k, np.int32), (B,)).copy()
     top_p = np.broadcast_to(np.asarray(top_p, np.float32), (B,)).copy()
     label = "filter seed=%d B=%d K=%d V=%d %s k=%s p=%s" % (seed, B, K, V, dtype,
@@ -76,6 +81,11 @@ def _case(sv, dev, seed, B, K, V, top_k, top_p, dtype="bf16", temp=1.0, sigma=0.
     _say("%s: mean accepted %.2f, flagged F1=%d F2=%d F3=%d" % (
         label, n.mean(), ref["flag_accept"].sum(), ref["flag_sample"].sum(),
         ref["flag_filter"].sum()))
+    n_seq = int(ref["num_accepted"].shape[0])
+    f12 = int((ref["flag_accept"] | ref["flag_sample"]).sum())
+    assert f12 <= 2 + n_seq // 1000, (label, f12)
+    f3_bound = 2 + n_seq // 50 if max_f3 is None else max_f3
+    assert int(ref["flag_filter"].sum()) <= f3_bound, (label, int(ref["flag_filter"].sum()))
     return n
 
 
@@ -86,7 +96,12 @@ def test_top_k(gpu_lib, dev, top_k):
 
 @pytest.mark.parametrize("top_p", [0.3, 0.8, 0.95, 0.999])
 def test_top_p(gpu_lib, dev, top_p):
-    _case(gpu_lib, dev, 2, 48, 4, 3000, 0, top_p)
+    # At 0.95 and 0.999 the edge of the kept set falls among tail entries of
+    # ~1e-6 .. 1e-5 mass each (V = 3000), so the 1e-6 band catches a row of
+    # 9 now and then (0.95: a few of 48 sequences) or often (0.999: about
+    # half).  Those sequences are still checked for validity.
+    bound = {0.95: 8, 0.999: 36}.get(top_p)
+    _case(gpu_lib, dev, 2, 48, 4, 3000, 0, top_p, max_f3=bound)
 
 
 def test_both_and_mixed_per_sequence(gpu_lib, dev):

@@ -10,6 +10,7 @@ import pytest
 
 from oracle import tree as otr
 from synth import gen, CONFIGS
+from synth.tree import ancestor_bits, chain_parents, tree_parents
 from synth.device import to_device, from_device, make_attn_inputs_device
 
 pytestmark = pytest.mark.gpu
@@ -41,7 +42,7 @@ def _widen(x, dtype):
 
 def _anc_batch(parents):
     """[B, N] int32 view of the uint32 ancestor sets of one parent[] per sequence."""
-    return np.stack([otr.tree_masks(p).astype(np.uint32) for p in parents]).view(np.int32)
+    return np.stack([ancestor_bits(p).astype(np.uint32) for p in parents]).view(np.int32)
 
 
 def _case(sv, dev, seed, B, parents, Hq, Hkv, D, ctx, dtype="bf16", q_scale=1.0, idx=None):
@@ -57,14 +58,14 @@ def _case(sv, dev, seed, B, parents, Hq, Hkv, D, ctx, dtype="bf16", q_scale=1.0,
                               to_device(anc, dev))
     gpu = _widen(from_device(out), dtype)
     ref = otr.tree_attention(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"],
-                             inp["kv_len"], anc.view(np.uint32), batch_indices=idx)
+                             inp["kv_len"], np.stack(parents), batch_indices=idx)
     sel = slice(None) if idx is None else idx
     _check(gpu[sel], ref[sel], dtype, label)
     return inp, t, gpu
 
 
 def test_tiny_fp32_tree(gpu_lib, dev):
-    par = otr.tree_parents((2, 2))
+    par = tree_parents((2, 2))
     _case(gpu_lib, dev, 1, 2, [par, par], 1, 1, 64, (40, 130), dtype="f32")
 
 
@@ -72,20 +73,20 @@ def test_tiny_fp32_tree(gpu_lib, dev):
 def test_llama8b_shaped_trees(gpu_lib, dev, shape):
     # 32 q / 8 kv heads: G (N) rows per KV head, one 32-row tile up to N = 8,
     # two tiles up to N = 16.
-    par = otr.tree_parents(shape)
+    par = tree_parents(shape)
     c = CONFIGS["llama8b_b64"]
     _case(gpu_lib, dev, 100 + len(par), 6, [par] * 6, c.Hq, c.Hkv, c.D, (300, 2500))
 
 
 def test_different_tree_per_sequence(gpu_lib, dev):
     shapes = [(2, 2), (1, 1, 1, 1, 1, 1), (3, 1), (6,)]           # all 7 nodes
-    pars = [otr.tree_parents(s) for s in shapes]
+    pars = [tree_parents(s) for s in shapes]
     assert len({len(p) for p in pars}) == 1
     _case(gpu_lib, dev, 7, 4, pars, 16, 8, 128, (0, 600))
 
 
 def test_fp32_tree_shapes(gpu_lib, dev):
-    par = otr.tree_parents((2, 1, 2))
+    par = tree_parents((2, 1, 2))
     _case(gpu_lib, dev, 8, 3, [par] * 3, 8, 2, 128, (10, 200), dtype="f32")
 
 
@@ -94,7 +95,7 @@ def test_chain_tree_is_bitwise_verify_attn(gpu_lib, dev):
     c = CONFIGS["llama8b_b64"]
     K = c.K
     t = make_attn_inputs_device(2024, 16, K, c.Hq, c.Hkv, c.D, (100, 3000), dev)
-    anc = _anc_batch([otr.chain_parents(K + 1)] * 16)
+    anc = _anc_batch([chain_parents(K + 1)] * 16)
     a = gpu_lib.verify_attn(t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["kv_len"])
     b = gpu_lib.verify_attn_tree(t["q"], t["k_cache"], t["v_cache"], t["block_table"],
                                  t["kv_len"], to_device(anc, dev))
@@ -105,7 +106,7 @@ def test_llama8b_b64_tree_sampled(gpu_lib, dev):
     # Full-size batch with a [2,2,2] tree (15 nodes, two tiles per KV head);
     # the oracle checks every 8th sequence.
     c = CONFIGS["llama8b_b64"]
-    par = otr.tree_parents((2, 2, 2))
+    par = tree_parents((2, 2, 2))
     n = len(par)
     _say("tree attn llama8b_b64 [2,2,2] device-drawn")
     t = make_attn_inputs_device(2025, c.B, n - 1, c.Hq, c.Hkv, c.D, c.ctx, dev)
@@ -123,6 +124,6 @@ def test_llama8b_b64_tree_sampled(gpu_lib, dev):
         vc = from_device(t["v_cache"][sel])
         ref = otr.tree_attention(from_device(t["q"][b:b + 1]), kc, vc,
                                  np.arange(len(pages), dtype=np.int32)[None],
-                                 kvl[b:b + 1], anc[b].view(np.uint32))
+                                 kvl[b:b + 1], par)
         gpu = _widen(from_device(out[b:b + 1]), "bf16")
         _check(gpu, ref, "bf16", "llama8b tree seq %d" % b)

@@ -14,6 +14,7 @@ import pytest
 
 from oracle import tree as otr
 from synth import gen, CONFIGS
+from synth.tree import chain_parents, tree_parents
 from synth.device import to_device, from_device
 
 pytestmark = pytest.mark.gpu
@@ -67,6 +68,9 @@ def _compare(ref, got, inp, kv0, idx, label):
         _valid_path(inp["parent"], tok[b], on[b], ot[b], n[b], V)
     _say("%s: %d sequences, mean accepted %.2f, flagged F1=%d F2=%d"
          % (label, len(n), n.mean(), ref["flag_accept"].sum(), ref["flag_sample"].sum()))
+    # F1 / F2 are rare for every tree (2e-5 per examined test, ~1e-4 per
+    # draw): a few flags at most, never a systematic exclusion.
+    assert int(flag.sum()) <= 2 + len(n) // 1000, (label, int(flag.sum()))
     return int(flag.sum())
 
 
@@ -89,7 +93,7 @@ def _case(sv, dev, seed, B, parent, V, dtype="bf16", sigma=0.51, temp=1.0, std=2
 
 
 def test_tiny_fp32_tree(gpu_lib, dev):
-    _case(gpu_lib, dev, 1, 64, otr.tree_parents((2, 2)), 300, dtype="f32", sigma=1.0)
+    _case(gpu_lib, dev, 1, 64, tree_parents((2, 2)), 300, dtype="f32", sigma=1.0)
 
 
 @pytest.mark.parametrize("shape", [(2, 2, 2), (3, 2), (4,), (2, 1, 2), (1, 1, 1, 1)])
@@ -97,24 +101,24 @@ def test_tiny_fp32_tree(gpu_lib, dev):
 def test_shapes_vs_oracle(gpu_lib, dev, shape, sigma):
     # sigma 2.0: the draft is far from the target, so most first children are
     # rejected and the sibling tests against the residual carry the walk.
-    _case(gpu_lib, dev, 10 + len(shape), 48, otr.tree_parents(shape), 5000, sigma=sigma)
+    _case(gpu_lib, dev, 10 + len(shape), 48, tree_parents(shape), 5000, sigma=sigma)
 
 
 @pytest.mark.parametrize("temp", [0.6, 1.5])
 def test_temperatures(gpu_lib, dev, temp):
-    _case(gpu_lib, dev, 21, 32, otr.tree_parents((2, 2, 2)), 20000, sigma=1.0, temp=temp)
+    _case(gpu_lib, dev, 21, 32, tree_parents((2, 2, 2)), 20000, sigma=1.0, temp=temp)
 
 
 def test_wide_root_every_round(gpu_lib, dev):
     # Root with 8 children and a far draft: walks reject up to all 8 siblings
     # (8 rounds of exact passes, each with a larger residual coefficient).
-    _, ref, got, _ = _case(gpu_lib, dev, 31, 64, otr.tree_parents((8,)), 4000, sigma=3.0)
+    _, ref, got, _ = _case(gpu_lib, dev, 31, 64, tree_parents((8,)), 4000, sigma=3.0)
     assert (got[2] == 0).sum() > 0
 
 
 def test_max_nodes(gpu_lib, dev):
-    _case(gpu_lib, dev, 41, 24, otr.tree_parents((16,)), 3000, sigma=2.5)      # 16 rounds
-    _case(gpu_lib, dev, 42, 24, otr.chain_parents(17), 3000, sigma=0.3)         # 17-node chain
+    _case(gpu_lib, dev, 41, 24, tree_parents((16,)), 3000, sigma=2.5)      # 16 rounds
+    _case(gpu_lib, dev, 42, 24, chain_parents(17), 3000, sigma=0.3)         # 17-node chain
 
 
 def test_root_only(gpu_lib, dev):
@@ -130,25 +134,25 @@ def test_non_bfs_order(gpu_lib, dev):
 
 @pytest.mark.parametrize("shape", [(2, 2, 2), (3, 1), (1, 1, 1, 1, 1, 1, 1)])
 def test_greedy(gpu_lib, dev, shape):
-    _case(gpu_lib, dev, 71, 32, otr.tree_parents(shape), 9000, temp=0.0, sigma=0.3,
+    _case(gpu_lib, dev, 71, 32, tree_parents(shape), 9000, temp=0.0, sigma=0.3,
           with_draft=False)
 
 
 def test_mixed_temperatures_in_one_batch(gpu_lib, dev):
     temps = np.tile(np.array([0.0, 0.7, 1.0, -1.0, 1.3], dtype=np.float32), 8)
-    _case(gpu_lib, dev, 81, 40, otr.tree_parents((2, 2)), 8000, sigma=1.0, temp=temps)
+    _case(gpu_lib, dev, 81, 40, tree_parents((2, 2)), 8000, sigma=1.0, temp=temps)
 
 
 @pytest.mark.parametrize("V,dtype", [(1001, "f32"), (33001, "bf16")])
 def test_ragged_vocab(gpu_lib, dev, V, dtype):
-    _case(gpu_lib, dev, 91, 32, otr.tree_parents((2, 2)), V, dtype=dtype, sigma=1.5)
+    _case(gpu_lib, dev, 91, 32, tree_parents((2, 2)), V, dtype=dtype, sigma=1.5)
 
 
 def test_llama8b_vocab_tree_sampled(gpu_lib, dev):
     # 64 sequences over the full 128256-entry vocabulary with a [2,2,2] tree;
     # the oracle checks every 4th sequence.
     c = CONFIGS["llama8b_b64"]
-    _case(gpu_lib, dev, 101, c.B, otr.tree_parents((2, 2, 2)), c.V, sigma=1.0,
+    _case(gpu_lib, dev, 101, c.B, tree_parents((2, 2, 2)), c.V, sigma=1.0,
           idx=list(range(0, c.B, 4)))
 
 
@@ -163,7 +167,7 @@ def _chain_as_tree(inp):
     u[:, 1:] = inp["uniforms"][:, :K]
     u[:, 0] = inp["uniforms"][:, K]
     return {"target": tgt, "draft": drf_t, "tokens": tok, "uniforms": u,
-            "parent": otr.chain_parents(K + 1), "temperature": inp["temperature"]}
+            "parent": chain_parents(K + 1), "temperature": inp["temperature"]}
 
 
 @pytest.mark.parametrize("sigma,temp", [(0.51, 1.0), (2.0, 0.8), (0.3, 0.0)])
@@ -192,7 +196,7 @@ def test_chain_tree_is_the_chain_call(gpu_lib, dev, sigma, temp):
 
 def test_counters_and_determinism(gpu_lib, dev):
     import torch
-    par = otr.tree_parents((2, 2, 2))
+    par = tree_parents((2, 2, 2))
     inp = gen.make_tree_reject_inputs(seed=121, B=32, parent=par, V=12000, draft_sigma=1.0)
     kv0 = np.full(32, 1000, dtype=np.int32)
     cnt = torch.zeros(2, dtype=torch.int64, device=dev)

@@ -15,6 +15,7 @@ from oracle import attention as oat
 from oracle import kv as okv
 from oracle import tree as otr
 from synth import gen, CONFIGS
+from synth.tree import ancestor_bits, chain_parents, children, tree_parents
 from synth.device import to_device, from_device
 
 pytestmark = pytest.mark.gpu
@@ -52,7 +53,7 @@ def _case(sv, dev, seed, B, N, Hq, Hkv, D, ctx, dtype="bf16", parents=None, chec
     kn, vn = gen.make_window_kv(seed + 1, B, N, Hkv, D, dtype)
     anc = None
     if parents is not None:
-        anc = np.stack([otr.tree_masks(p).astype(np.uint32) for p in parents]).view(np.int32)
+        anc = np.stack([ancestor_bits(p).astype(np.uint32) for p in parents]).view(np.int32)
     k_ref, v_ref = okv.append_window(inp["k_cache"], inp["v_cache"], inp["block_table"],
                                      inp["kv_len"], kn, vn)
     t = {k: to_device(v, dev) for k, v in inp.items()}
@@ -83,7 +84,7 @@ def _case(sv, dev, seed, B, N, Hq, Hkv, D, ctx, dtype="bf16", parents=None, chec
             ref = oat.verify_attention(inp["q"], k_ref, v_ref, inp["block_table"], inp["kv_len"])
         else:
             ref = otr.tree_attention(inp["q"], k_ref, v_ref, inp["block_table"], inp["kv_len"],
-                                     anc.view(np.uint32))
+                                     np.stack(parents))
         _tol(_widen(from_device(out_a), dtype), ref, dtype, label)
 
 
@@ -106,14 +107,14 @@ def test_two_tiles_and_d64(gpu_lib, dev):
 
 
 def test_tree_window(gpu_lib, dev):
-    par = otr.tree_parents((2, 2, 2))
+    par = tree_parents((2, 2, 2))
     c = CONFIGS["llama8b_b64"]
     _case(gpu_lib, dev, 31, 6, len(par), c.Hq, c.Hkv, c.D, (100, 2000), parents=[par] * 6)
 
 
 def test_fp32_window(gpu_lib, dev):
     _case(gpu_lib, dev, 41, 4, 6, 8, 2, 64, (10, 200), dtype="f32")
-    par = otr.tree_parents((2, 2))
+    par = tree_parents((2, 2))
     _case(gpu_lib, dev, 42, 3, len(par), 8, 2, 128, (5, 90), dtype="f32", parents=[par] * 3)
 
 
@@ -125,7 +126,7 @@ def test_empty_context(gpu_lib, dev):
 
 def _paths(rng, parent, B):
     """A random root path per sequence: (num_accepted [B], nodes [B, N])."""
-    kids = otr.children_of(parent)
+    kids = children(parent)
     n_out = np.zeros(B, np.int32)
     nodes = np.full((B, len(parent)), -1, np.int32)
     for b in range(B):
@@ -143,7 +144,7 @@ def _paths(rng, parent, B):
 def test_commit(gpu_lib, dev, dtype, mode):
     rng = np.random.default_rng(61)
     B, Hkv, D = 16, 4, 128
-    par = otr.tree_parents((2, 2, 2)) if "tree" in mode else otr.chain_parents(8)
+    par = tree_parents((2, 2, 2)) if "tree" in mode else chain_parents(8)
     N = len(par)
     inp = gen.make_attn_inputs(seed=62, B=B, K=N - 1, Hq=Hkv, Hkv=Hkv, D=D, ctx=(0, 100),
                                dtype=dtype)
@@ -178,7 +179,7 @@ def test_multi_step_tree_loop_with_page_pool(gpu_lib, dev):
     import torch
     rng = np.random.default_rng(71)
     B, Hq, Hkv, D, V = 4, 16, 4, 64, 4000
-    par = otr.tree_parents((2, 2))
+    par = tree_parents((2, 2))
     N = len(par)
     nb, mbps = 64, 12
     pool = gpu_lib.PagePool(nb, B, mbps)
@@ -196,7 +197,7 @@ def test_multi_step_tree_loop_with_page_pool(gpu_lib, dev):
         bt = to_device(pool.block_table(), dev)
         q = to_device(gen.bf16_bits(rng.standard_normal((B, N, Hq, D)).astype(np.float32)), dev)
         kn, vn = gen.make_window_kv(100 + step, B, N, Hkv, D)
-        anc = to_device(np.stack([otr.tree_masks(par).astype(np.uint32)] * B).view(np.int32), dev)
+        anc = to_device(np.stack([ancestor_bits(par).astype(np.uint32)] * B).view(np.int32), dev)
         d_len = to_device(kv_len, dev)
         gpu_lib.verify_attn_window(q, to_device(kn, dev), to_device(vn, dev), kc, vc, bt, d_len,
                                    anc=anc, mode=gpu_lib.SV_WINDOW_APPEND)

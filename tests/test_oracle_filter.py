@@ -82,3 +82,18 @@ def test_filtered_verifier_is_lossless_for_the_filtered_target(top_k, top_p):
     q /= q.sum()
     assert (first[q == 0] == 0).all()                       # nothing outside the kept set
     assert 0.5 * np.abs(first - q).sum() < 0.01
+
+
+def test_f3_band_edges():
+    # Masses 0.5, 0.3, 0.2 in value order: cumulative 0.5, 0.8, 1.0.  F3 flags
+    # a row when top_p is within 1e-6 of the mass of the kept set or of the
+    # set one value smaller.
+    x = np.log(np.array([0.3, 0.5, 0.2]))
+    for p, flag in [(0.8 - 0.99e-6, True), (0.8 - 1.01e-6, False), (0.8 + 0.99e-6, True),
+                    (0.8 + 1.01e-6, False), (0.5 + 0.99e-6, True), (0.5 + 1.01e-6, False),
+                    (0.65, False)]:
+        keep, f = of.filter_mask(x, 1.0, top_p=p)
+        assert bool(f) == flag, p
+    # The kept sets on both sides of the 0.8 edge.
+    assert of.filter_mask(x, 1.0, top_p=0.8 - 1.01e-6)[0].tolist() == [True, True, False]
+    assert of.filter_mask(x, 1.0, top_p=0.8 + 1.01e-6)[0].tolist() == [True, True, True]

@@ -392,3 +392,139 @@ def test_greedy_equals_target_only_decoding(k):
         calls += 1
     assert seq[:len(plain)] == plain
     assert calls < n_tokens       # some drafts were accepted
+
+
+# --------------------------------------------------------------------------
+# Parity bands.  F1 and F2 decide which sequences a GPU parity test leaves
+# out of its exact comparison, so their masks and widths are pinned here by
+# hand-built cases: an over-wide mask would hide real mismatches, a narrow
+# one would fail the GPU tests on legitimate rounding.
+# --------------------------------------------------------------------------
+
+# Three positions with q = (0.6, 0.4), p = (0.8, 0.2) and the drafted token 0:
+# every accept ratio is r = 0.6 / 0.8 = 0.75.
+_R = 0.75
+_LQ = np.log([0.6, 0.4])
+_LP = np.log([0.8, 0.2])
+
+
+def _bands(u, k=3):
+    tgt = np.stack([_LQ] * (k + 1))
+    drf = np.stack([_LP] * k)
+    res = _one(tgt, drf, [0] * k, u)
+    assert np.allclose(res["ratio"][0], _R, rtol=0, atol=1e-15)
+    return res
+
+
+def test_f1_flags_an_examined_accept_inside_the_band():
+    # Position 1 accepts with u just below r, inside the band: flagged.
+    res = _bands([_R - 0.99e-5, 0.9, 0.1, 0.5])
+    assert res["num_accepted"][0] == 1 and res["flag_accept"][0]
+    # Just outside the band: not flagged (and the same outcome).
+    res = _bands([_R - 1.01e-5, 0.9, 0.1, 0.5])
+    assert res["num_accepted"][0] == 1 and not res["flag_accept"][0]
+    # Above r, inside the band: position 1 rejects, and is flagged.
+    res = _bands([_R + 0.99e-5, 0.1, 0.1, 0.5])
+    assert res["num_accepted"][0] == 0 and res["flag_accept"][0]
+    res = _bands([_R + 1.01e-5, 0.1, 0.1, 0.5])
+    assert res["num_accepted"][0] == 0 and not res["flag_accept"][0]
+
+
+def test_f1_flags_the_rejecting_test_itself():
+    # Position 2 is the first rejection (u above r inside the band): the test
+    # that rejects was examined, so the sequence is flagged.
+    res = _bands([0.1, _R + 0.5e-5, 0.1, 0.5])
+    assert res["num_accepted"][0] == 1 and res["flag_accept"][0]
+    res = _bands([0.1, _R + 2e-5, 0.1, 0.5])
+    assert res["num_accepted"][0] == 1 and not res["flag_accept"][0]
+
+
+def test_f1_ignores_tests_after_the_first_rejection():
+    # Position 1 rejects far from the band; positions 2 and 3 sit inside the
+    # band but are never examined: not flagged.
+    res = _bands([0.9, _R - 0.5e-5, _R + 0.5e-5, 0.5])
+    assert res["num_accepted"][0] == 0 and not res["flag_accept"][0]
+    # Position 2 rejects; position 3 inside the band is not examined.
+    res = _bands([0.1, 0.9, _R - 0.5e-5, 0.5])
+    assert res["num_accepted"][0] == 1 and not res["flag_accept"][0]
+
+
+def test_f1_all_accepted_examines_every_position():
+    # n = K: all K tests were examined, the last one included.
+    res = _bands([0.1, 0.1, _R - 0.5e-5, 0.5])
+    assert res["num_accepted"][0] == 3 and res["flag_accept"][0]
+    res = _bands([0.1, 0.1, 0.2, 0.5])
+    assert res["num_accepted"][0] == 3 and not res["flag_accept"][0]
+
+
+def test_f1_never_flags_draft_probability_zero():
+    # p(d) = 0: the ratio is infinite, the test always accepts, never a flag.
+    tgt = np.stack([_LQ, _LQ])
+    drf = np.array([[0.0, -np.inf]])
+    res = _one(tgt, drf, [1], [1 - 2 ** -24, 0.5])
+    assert res["num_accepted"][0] == 1 and not res["flag_accept"][0]
+
+
+def test_f1_greedy_sequences_are_never_flagged():
+    tgt = np.array([[[0.0, 1.0], [0.0, 1.0]]])
+    res = orj.reject_sample(tgt, None, np.array([[1]]), np.full((1, 2), _R), np.array([0.0]))
+    assert not res["flag_accept"][0] and not res["flag_sample"][0]
+
+
+def test_f2_band_edges_of_the_inverse_cdf():
+    # C = (0.25, 0.5, 1.0), Z = 1: u Z is compared with the edges of the
+    # chosen token, C(t-1) and C(t).
+    w = np.array([[0.25, 0.25, 0.5]])
+    cases = [
+        (0.25 + 0.99e-10, 1, True),     # just above C(0): token 1, near its lower edge
+        (0.25 + 1.01e-10, 1, False),
+        (0.25, 1, True),                # on the edge: C(0) = u Z is not > u Z
+        (0.5 - 0.99e-10, 1, True),      # just below C(1): near token 1's upper edge
+        (0.5 - 1.01e-10, 1, False),
+        (0.5 + 0.99e-10, 2, True),      # just above C(1): token 2, near its lower edge
+        (0.375, 1, False),              # the middle of token 1's cell
+        (0.99e-10, 0, True),            # near C(-1) = 0
+        (1.01e-10, 0, False),
+    ]
+    for t, tok, flag in cases:
+        got_tok, got_flag = orj._inverse_cdf(w, np.array([t]), 1e-10)
+        assert got_tok[0] == tok and bool(got_flag[0]) == flag, (t, tok, flag)
+
+
+def test_f2_band_is_in_probability_mass_of_the_residual():
+    # Rejection at position 1 with q = (0.5, 0.3, 0.2), p = (0.2, 0.2, 0.6):
+    # the residual weights are (0.3, 0.1, 0), Z = 0.4, so u Z = C(0) = 0.3 at
+    # u = 0.75.  F2 compares u Z with the unnormalised prefix sums.
+    q = np.array([0.5, 0.3, 0.2])
+    p = np.array([0.2, 0.2, 0.6])
+    tgt = np.log(np.stack([q, q]))
+    drf = np.log(p)[None]
+    # d = 2, r = 1/3; u0 = 0.9 rejects.
+    for u_k, tok, flag in [(0.75 + 2.0e-10, 1, True),      # u Z = 0.3 + 0.8e-10
+                           (0.75 + 3.0e-10, 1, False),     # u Z = 0.3 + 1.2e-10
+                           (0.5, 0, False)]:
+        res = _one(tgt, drf, [2], [0.9, u_k])
+        assert res["num_accepted"][0] == 0
+        assert res["out_tokens"][0, 0] == tok and bool(res["flag_sample"][0]) == flag, u_k
+
+
+def test_acceptance_rate_on_exact_alpha_construction():
+    # p = a q + (1 - a) s with q, s on disjoint supports: sum min(p, q) = a.
+    rng = np.random.default_rng(5)
+    for a in (0.0, 0.3, 0.8, 0.97):
+        q = np.zeros(12)
+        s = np.zeros(12)
+        q[:6] = rng.dirichlet(np.ones(6))
+        s[6:] = rng.dirichlet(np.ones(6))
+        p = a * q + (1 - a) * s
+        with np.errstate(divide="ignore"):
+            got = orj.acceptance_rate(np.log(q), np.log(p), 1.0)
+        assert abs(got - a) < 1e-14, (a, got)
+    # Identical rows accept always, at any temperature; disjoint rows never.
+    x = rng.standard_normal(9)
+    assert abs(orj.acceptance_rate(x, x, 0.7) - 1.0) < 1e-14
+    y = np.where(np.arange(9) < 4, x, -np.inf)
+    z = np.where(np.arange(9) >= 4, x, -np.inf)
+    assert orj.acceptance_rate(y, z, 1.3) == 0.0
+    # Two entries by hand: q = (0.6, 0.4), p = (0.8, 0.2) -> 0.6 + 0.2.
+    assert abs(orj.acceptance_rate(_LQ, _LP, 1.0) - 0.8) < 1e-14

@@ -25,6 +25,7 @@ from oracle import reject as orj
 from oracle import tree as otr
 from oracle.reject import widen
 from synth import gen
+from synth.tree import ancestor_bits, chain_parents, children, tree_parents
 
 
 def _probs(logits, t=1.0):
@@ -36,15 +37,26 @@ def _probs(logits, t=1.0):
 
 
 def test_tree_helpers():
-    par = otr.tree_parents((2, 2, 2))
+    # The input encoders (synth.tree) and the oracle's own path walk, by hand.
+    par = tree_parents((2, 2, 2))
     assert par.tolist() == [-1, 0, 0, 1, 1, 2, 2, 3, 3, 4, 4, 5, 5, 6, 6]
-    anc = otr.tree_masks(par)
+    anc = ancestor_bits(par)
     assert int(anc[0]) == 0b1
     assert int(anc[9]) == (1 << 9) | (1 << 4) | (1 << 1) | 1
-    assert otr.children_of(par)[2] == [5, 6]
-    assert otr.chain_parents(4).tolist() == [-1, 0, 1, 2]
-    with pytest.raises(AssertionError):
-        otr.tree_masks(np.array([-1, 2, 0]))
+    assert children(par)[2] == [5, 6] and otr.children_of(par)[2] == [5, 6]
+    assert chain_parents(4).tolist() == [-1, 0, 1, 2]
+    assert otr.path_to_root(par, 9) == [0, 1, 4, 9]
+    assert otr.path_to_root(par, 0) == [0]
+    # The bit sets and the walked paths agree on every node of several shapes.
+    for shape in [(2, 2, 2), (3, 1, 2), (16,), (1, 1, 1, 1)]:
+        p = tree_parents(shape)
+        bits = ancestor_bits(p)
+        for i in range(len(p)):
+            assert [j for j in range(len(p)) if (int(bits[i]) >> j) & 1] == otr.path_to_root(p, i)
+    with pytest.raises(ValueError):
+        ancestor_bits(np.array([-1, 2, 0]))
+    with pytest.raises(ValueError):
+        otr.path_to_root(np.array([-1, 2, 0]), 1)
 
 
 # --------------------------------------------------------------------------
@@ -69,7 +81,7 @@ def test_chain_tree_is_the_chain_verifier(seed, B, K, V, temps):
     u = np.zeros((B, n), np.float32)
     u[:, 1:] = r["uniforms"][:, :K]
     u[:, 0] = r["uniforms"][:, K]
-    tr = otr.reject_sample_tree(r["target"], draft, otr.chain_parents(n), tokens, u,
+    tr = otr.reject_sample_tree(r["target"], draft, chain_parents(n), tokens, u,
                                 r["temperature"])
     assert np.array_equal(tr["out_tokens"], chain["out_tokens"])
     assert np.array_equal(tr["num_accepted"], chain["num_accepted"])
@@ -132,7 +144,7 @@ def test_zero_draft_probability_accepts_in_a_tree():
 # --------------------------------------------------------------------------
 
 def test_tree_losslessness_first_and_second_token():
-    par = otr.tree_parents((2, 2))                 # 7 nodes
+    par = tree_parents((2, 2))                 # 7 nodes
     v, trials = 16, 200_000
     inp = gen.make_tree_reject_inputs(seed=77, B=trials, parent=par, V=v, dtype="f32",
                                       logit_std=1.0, draft_sigma=1.0, temperature=1.0,
@@ -180,8 +192,8 @@ def _draft(prefix):
 
 @pytest.mark.parametrize("shape", [(2, 2), (3, 1, 1), (1, 1, 1, 1)])
 def test_greedy_tree_equals_target_only_decoding(shape):
-    par = otr.tree_parents(shape)
-    kids = otr.children_of(par)
+    par = tree_parents(shape)
+    kids = children(par)
     n = len(par)
     prompt = [5, 1, 7]
     n_tokens = 120
@@ -219,9 +231,8 @@ def _attn_case(seed, B, N, Hq, Hkv, D, ctx, dtype="f32"):
 
 def test_chain_mask_is_verify_attention():
     inp = _attn_case(11, 2, 6, 4, 2, 32, (10, 40))
-    anc = otr.tree_masks(otr.chain_parents(6))
     a = otr.tree_attention(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"],
-                           inp["kv_len"], anc)
+                           inp["kv_len"], chain_parents(6))
     b = oat.verify_attention(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"],
                              inp["kv_len"])
     assert np.max(np.abs(a - b)) < 1e-12
@@ -242,12 +253,12 @@ def _chain_cache(keys, vals):
 
 @pytest.mark.parametrize("shape", [(2, 2), (3, 2), (1, 3)])
 def test_every_node_is_causal_attention_over_its_path(shape):
-    par = otr.tree_parents(shape)
+    par = tree_parents(shape)
     n = len(par)
     inp = _attn_case(21, 2, n, 4, 2, 32, (5, 30))
-    anc = otr.tree_masks(par)
+    anc = ancestor_bits(par)
     out = otr.tree_attention(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"],
-                             inp["kv_len"], anc)
+                             inp["kv_len"], par)
     for b in range(2):
         l0 = int(inp["kv_len"][b])
         keys, vals = oat.gather_kv(inp["k_cache"], inp["v_cache"], inp["block_table"], b, l0 + n)
@@ -261,12 +272,11 @@ def test_every_node_is_causal_attention_over_its_path(shape):
 
 
 def test_non_ancestor_keys_do_not_matter():
-    par = otr.tree_parents((2, 2))
+    par = tree_parents((2, 2))
     n = len(par)
     inp = _attn_case(31, 1, n, 2, 1, 32, 20)
-    anc = otr.tree_masks(par)
     a = otr.tree_attention(inp["q"], inp["k_cache"], inp["v_cache"], inp["block_table"],
-                           inp["kv_len"], anc)
+                           inp["kv_len"], par)
     kc, vc = inp["k_cache"].copy(), inp["v_cache"].copy()
     l0 = int(inp["kv_len"][0])
     for j in (2, 5, 6):                                   # not ancestors of node 4
@@ -274,7 +284,39 @@ def test_non_ancestor_keys_do_not_matter():
         blk = inp["block_table"][0, pos // 16]
         kc[blk, :, :, pos % 16, :] = 7.0
         vc[blk, :, :, pos % 16] = -3.0
-    b = otr.tree_attention(inp["q"], kc, vc, inp["block_table"], inp["kv_len"], anc)
+    b = otr.tree_attention(inp["q"], kc, vc, inp["block_table"], inp["kv_len"], par)
     for i in (0, 1, 3, 4):
         assert np.max(np.abs(a[0, i] - b[0, i])) < 1e-12
     assert np.max(np.abs(a[0, 5] - b[0, 5])) > 1e-6       # node 5 does see node 2
+
+
+def test_tree_f1_band_on_sibling_tests():
+    # Root with two children (parent -1, 0, 0).  q_root = (0.5, 0.3, 0.2),
+    # p_root = (0.2, 0.2, 0.6).  Node 1 drafts token 2: r = 0.2 / 0.6 = 1/3.
+    # After it is rejected the residual is (0.3, 0.1, 0) / 0.4, so node 2's
+    # token 2 has r = 0 (always rejected): |u - 0| < 1e-5 is the band there.
+    q = np.array([0.5, 0.3, 0.2])
+    p = np.array([0.2, 0.2, 0.6])
+    tgt = np.log(np.stack([q, q, q]))[None]
+    drf = np.log(np.stack([p, p, p]))[None]
+    par = [-1, 0, 0]
+    toks = np.array([[0, 2, 2]])
+
+    def run(u1, u2):
+        return otr.reject_sample_tree(tgt, drf, par, toks, np.array([[0.5, u1, u2]]),
+                                      np.array([1.0]))
+
+    # Node 1 rejected, node 2 examined and inside the band: flagged.
+    res = run(0.9, 0.5e-5)
+    assert res["num_accepted"][0] == 0 and res["flag_accept"][0]
+    res = run(0.9, 1.01e-5)
+    assert res["num_accepted"][0] == 0 and not res["flag_accept"][0]
+    # Node 1 inside its band: flagged whichever way it goes.
+    assert run(1 / 3 + 0.5e-5, 0.5)["flag_accept"][0]
+    assert run(1 / 3 - 0.5e-5, 0.5)["flag_accept"][0]
+    assert not run(1 / 3 - 1.01e-5, 0.5)["flag_accept"][0]
+    # Node 1 accepted (a leaf: the bonus draw follows), so node 2 is never
+    # examined: its uniform inside the band does not flag.
+    res = run(0.1, 0.5e-5)
+    assert res["num_accepted"][0] == 1 and list(res["out_nodes"][0, :1]) == [1]
+    assert not res["flag_accept"][0]
