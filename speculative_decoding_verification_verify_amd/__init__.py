@@ -168,21 +168,57 @@ def _check(fn, status):
         raise SpecVerifyError(fn, status)
 
 
-def _need(t, name, dtype=None, cuda=True):
+def _need(t, name, dtype=None, shape=None):
+    """Type, dtype, shape and layout of one tensor argument (no device check:
+    _on_gpu does that after every argument's shape is known to be right)."""
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
-    if cuda and t.device.type != "cuda":
-        raise ValueError("%s must be on the GPU" % name)
-    if not t.is_contiguous():
-        raise ValueError("%s must be contiguous" % name)
     if dtype is not None and t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None:
+        _shape(t, name, shape)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
 
 
 def _shape(t, name, shape):
     if tuple(t.shape) != tuple(int(x) for x in shape):
         raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _dims(t, name, nd):
+    if t.dim() != nd:
+        raise ValueError("%s must have %d dimensions, got shape %s" % (name, nd, tuple(t.shape)))
+
+
+def _on_gpu(**tensors):
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError("%s must be on the GPU" % name)
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("%s is on %s, the other arguments on %s" % (name, t.device, dev))
+
+
+def _kv_caches(k_cache, v_cache, dtype):
+    """(NB, Hkv, D) of a paged K cache [NB, Hkv, D/X, 16, X] (X = 16 bytes /
+    element) and V cache [NB, Hkv, D, 16], after checking both."""
+    _need(k_cache, "k_cache", dtype)
+    _need(v_cache, "v_cache", dtype)
+    _dims(k_cache, "k_cache", 5)
+    _dims(v_cache, "v_cache", 4)
+    x = 16 // k_cache.element_size()
+    NB, Hkv, DX, BS, X = k_cache.shape
+    if X != x or BS != 16:
+        raise ValueError("k_cache must be [NB, Hkv, D/%d, 16, %d], got %s" % (x, x, tuple(k_cache.shape)))
+    D = DX * X
+    _shape(v_cache, "v_cache", (NB, Hkv, D, 16))
+    return NB, Hkv, D
 
 
 def verify_attn_workspace_bytes(B, K, Hq, Hkv, D, max_kv_len):
@@ -195,6 +231,16 @@ def reject_sample_workspace_bytes(B, K, V):
 
 def reject_sample_tree_workspace_bytes(B, N, V):
     return int(load().spec_reject_sample_tree_workspace_bytes(B, N, V))
+
+
+def _workspace(workspace, ws_bytes, device):
+    import torch
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+    if workspace is not None:
+        _need(workspace, "workspace")
+        _on_gpu(workspace=workspace)
+    return workspace, (0 if workspace is None else workspace.numel() * workspace.element_size())
 
 
 def verify_attn(q, k_cache, v_cache, block_table, kv_len, out=None, max_kv_len=None,
@@ -219,51 +265,74 @@ def verify_attn_tree(q, k_cache, v_cache, block_table, kv_len, anc, out=None, ma
     """
     import torch
     _need(anc, "anc", torch.int32)
-    if tuple(anc.shape) != (q.shape[0], q.shape[1]):
-        raise ValueError("anc must be [B, N]")
+    _dims(q, "q", 4)
+    _shape(anc, "anc", (q.shape[0], q.shape[1]))
     return _verify_attn(q, k_cache, v_cache, block_table, kv_len, anc, out, max_kv_len, scale,
                         workspace, stream)
+
+
+def _attn_common(q, k_cache, v_cache, block_table, kv_len, out):
+    """Checks shared by the attention calls; returns (B, N, Hq, D, NB, Hkv, dtype code)."""
+    import torch
+    _need(q, "q")
+    dt = _dtype_code(q)
+    _dims(q, "q", 4)
+    B, N, Hq, D = q.shape
+    NB, Hkv, Dk = _kv_caches(k_cache, v_cache, q.dtype)
+    if Dk != D:
+        raise ValueError("q has head dim %d, the caches %d" % (D, Dk))
+    _need(block_table, "block_table", torch.int32)
+    _dims(block_table, "block_table", 2)
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must have B = %d rows, got %d" % (B, block_table.shape[0]))
+    _need(kv_len, "kv_len", torch.int32, (B,))
+    if out is not None:
+        _need(out, "out", q.dtype, tuple(q.shape))
+    return B, N, Hq, D, NB, Hkv, dt
 
 
 def _verify_attn(q, k_cache, v_cache, block_table, kv_len, anc, out, max_kv_len, scale,
                  workspace, stream):
     import torch
     lib = load()
-    _need(q, "q")
-    dt = _dtype_code(q)
-    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
-        _need(t, name, q.dtype)
-    _need(block_table, "block_table", torch.int32)
-    _need(kv_len, "kv_len", torch.int32)
-    B, K1, Hq, D = q.shape
-    NB, Hkv = k_cache.shape[0], k_cache.shape[1]
-    if k_cache.dim() != 5 or v_cache.dim() != 4:
-        raise ValueError("k_cache must be [NB,Hkv,D/X,16,X] and v_cache [NB,Hkv,D,16]")
-    block_size = k_cache.shape[3]
+    B, K1, Hq, D, NB, Hkv, dt = _attn_common(q, k_cache, v_cache, block_table, kv_len, out)
+    _on_gpu(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table, kv_len=kv_len,
+            anc=anc, out=out)
     mbps = block_table.shape[1]
     if max_kv_len is None:
-        max_kv_len = max(0, mbps * block_size - K1)
+        max_kv_len = max(0, mbps * 16 - K1)
     if out is None:
         out = torch.empty_like(q)
-    else:
-        _need(out, "out", q.dtype)
     ws_bytes = verify_attn_workspace_bytes(B, K1 - 1, Hq, Hkv, D, max_kv_len)
-    if workspace is None and ws_bytes > 0:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, ws_have = _workspace(workspace, ws_bytes, q.device)
     if anc is None:
         st = lib.spec_verify_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-                                  _ptr(kv_len), _ptr(out), B, K1 - 1, Hq, Hkv, D, block_size, NB,
+                                  _ptr(kv_len), _ptr(out), B, K1 - 1, Hq, Hkv, D, 16, NB,
                                   mbps, int(max_kv_len), float(scale), dt, _ptr(workspace),
                                   ws_have, _stream(stream))
         _check("spec_verify_attn", st)
     else:
         st = lib.spec_verify_attn_tree(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                        _ptr(kv_len), _ptr(anc), _ptr(out), B, K1, Hq, Hkv, D,
-                                       block_size, NB, mbps, int(max_kv_len), float(scale), dt,
+                                       16, NB, mbps, int(max_kv_len), float(scale), dt,
                                        _ptr(workspace), ws_have, _stream(stream))
         _check("spec_verify_attn_tree", st)
     return out
+
+
+def _reject_outputs(B, N, device, out_tokens, num_accepted, counters, out_nodes=False):
+    import torch
+    if out_tokens is None:
+        out_tokens = torch.empty((B, N), dtype=torch.int32, device=device)
+    else:
+        _need(out_tokens, "out_tokens", torch.int32, (B, N))
+    if num_accepted is None:
+        num_accepted = torch.empty((B,), dtype=torch.int32, device=device)
+    else:
+        _need(num_accepted, "num_accepted", torch.int32, (B,))
+    if counters is not None:
+        _need(counters, "counters", torch.int64, (2,))
+    return out_tokens, num_accepted
 
 
 def reject_sample(target, draft, draft_tokens, uniforms, temperature, kv_len,
@@ -282,29 +351,33 @@ def reject_sample(target, draft, draft_tokens, uniforms, temperature, kv_len,
     lib = load()
     _need(target, "target")
     dt = _dtype_code(target)
-    if draft is not None:
-        _need(draft, "draft", target.dtype)
-    _need(draft_tokens, "draft_tokens", torch.int32)
-    _need(uniforms, "uniforms", torch.float32)
-    _need(temperature, "temperature", torch.float32)
-    _need(kv_len, "kv_len", torch.int32)
+    _dims(target, "target", 3)
     B, K1, V = target.shape
     K = K1 - 1
-    if out_tokens is None:
-        out_tokens = torch.empty((B, K1), dtype=torch.int32, device=target.device)
-    if num_accepted is None:
-        num_accepted = torch.empty((B,), dtype=torch.int32, device=target.device)
+    if draft is not None:
+        _need(draft, "draft", target.dtype, (B, K, V))
+    _need(draft_tokens, "draft_tokens", torch.int32, (B, K))
+    _need(uniforms, "uniforms", torch.float32, (B, K1))
+    _need(temperature, "temperature", torch.float32, (B,))
+    _need(kv_len, "kv_len", torch.int32, (B,))
+    if top_k is not None:
+        _need(top_k, "top_k", torch.int32, (B,))
+    if top_p is not None:
+        _need(top_p, "top_p", torch.float32, (B,))
+    if out_tokens is not None:
+        _need(out_tokens, "out_tokens", torch.int32, (B, K1))
+    if num_accepted is not None:
+        _need(num_accepted, "num_accepted", torch.int32, (B,))
     if counters is not None:
-        _need(counters, "counters", torch.int64)
+        _need(counters, "counters", torch.int64, (2,))
+    _on_gpu(target=target, draft=draft, draft_tokens=draft_tokens, uniforms=uniforms,
+            temperature=temperature, kv_len=kv_len, top_k=top_k, top_p=top_p,
+            out_tokens=out_tokens, num_accepted=num_accepted, counters=counters)
+    out_tokens, num_accepted = _reject_outputs(B, K1, target.device, out_tokens, num_accepted,
+                                               counters)
     ws_bytes = reject_sample_workspace_bytes(B, K, V)
-    if workspace is None and ws_bytes > 0:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=target.device)
-    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, ws_have = _workspace(workspace, ws_bytes, target.device)
     if top_k is not None or top_p is not None:
-        if top_k is not None:
-            _need(top_k, "top_k", torch.int32)
-        if top_p is not None:
-            _need(top_p, "top_p", torch.float32)
         st = lib.spec_reject_sample_filtered(_ptr(target), _ptr(draft), _ptr(draft_tokens),
                                              _ptr(uniforms), _ptr(temperature), _ptr(top_k),
                                              _ptr(top_p), _ptr(out_tokens), _ptr(num_accepted),
@@ -330,28 +403,22 @@ def reject_sample_noalloc(target, draft, draft_tokens, uniforms, temperature, kv
     lib = load()
     _need(target, "target")
     dt = _dtype_code(target)
-    if target.dim() != 3:
-        raise ValueError("target must be [B, K+1, V]")
+    _dims(target, "target", 3)
     B, K1, V = target.shape
     K = K1 - 1
     if draft is not None:
-        _need(draft, "draft", target.dtype)
-        _shape(draft, "draft", (B, K, V))
-    _need(draft_tokens, "draft_tokens", torch.int32)
-    _shape(draft_tokens, "draft_tokens", (B, K))
-    _need(uniforms, "uniforms", torch.float32)
-    _shape(uniforms, "uniforms", (B, K1))
-    _need(temperature, "temperature", torch.float32)
-    _shape(temperature, "temperature", (B,))
-    _need(kv_len, "kv_len", torch.int32)
-    _shape(kv_len, "kv_len", (B,))
-    _need(out_tokens, "out_tokens", torch.int32)
-    _shape(out_tokens, "out_tokens", (B, K1))
-    _need(num_accepted, "num_accepted", torch.int32)
-    _shape(num_accepted, "num_accepted", (B,))
+        _need(draft, "draft", target.dtype, (B, K, V))
+    _need(draft_tokens, "draft_tokens", torch.int32, (B, K))
+    _need(uniforms, "uniforms", torch.float32, (B, K1))
+    _need(temperature, "temperature", torch.float32, (B,))
+    _need(kv_len, "kv_len", torch.int32, (B,))
+    _need(out_tokens, "out_tokens", torch.int32, (B, K1))
+    _need(num_accepted, "num_accepted", torch.int32, (B,))
     if counters is not None:
-        _need(counters, "counters", torch.int64)
-        _shape(counters, "counters", (2,))
+        _need(counters, "counters", torch.int64, (2,))
+    _on_gpu(target=target, draft=draft, draft_tokens=draft_tokens, uniforms=uniforms,
+            temperature=temperature, kv_len=kv_len, out_tokens=out_tokens,
+            num_accepted=num_accepted, counters=counters)
     st = lib.spec_reject_sample_noalloc(_ptr(target), _ptr(draft), _ptr(draft_tokens),
                                         _ptr(uniforms), _ptr(temperature), _ptr(out_tokens),
                                         _ptr(num_accepted), _ptr(kv_len), _ptr(counters), B, K, V,
@@ -376,31 +443,35 @@ def reject_sample_tree(target, draft, parent, tokens, uniforms, temperature, kv_
     lib = load()
     _need(target, "target")
     dt = _dtype_code(target)
-    if draft is not None:
-        _need(draft, "draft", target.dtype)
-        if tuple(draft.shape) != tuple(target.shape):
-            raise ValueError("draft must have the shape of target [B, N, V]")
-    _need(tokens, "tokens", torch.int32)
-    _need(uniforms, "uniforms", torch.float32)
-    _need(temperature, "temperature", torch.float32)
-    _need(kv_len, "kv_len", torch.int32)
+    _dims(target, "target", 3)
     B, N, V = target.shape
+    if draft is not None:
+        _need(draft, "draft", target.dtype, (B, N, V))
+    _need(tokens, "tokens", torch.int32, (B, N))
+    _need(uniforms, "uniforms", torch.float32, (B, N))
+    _need(temperature, "temperature", torch.float32, (B,))
+    _need(kv_len, "kv_len", torch.int32, (B,))
+    if out_nodes is not None:
+        _need(out_nodes, "out_nodes", torch.int32, (B, N))
+    if out_tokens is not None:
+        _need(out_tokens, "out_tokens", torch.int32, (B, N))
+    if num_accepted is not None:
+        _need(num_accepted, "num_accepted", torch.int32, (B,))
+    if counters is not None:
+        _need(counters, "counters", torch.int64, (2,))
     par = [int(x) for x in parent]
     if len(par) != N:
         raise ValueError("parent must have N = %d entries" % N)
+    _on_gpu(target=target, draft=draft, tokens=tokens, uniforms=uniforms,
+            temperature=temperature, kv_len=kv_len, out_tokens=out_tokens, out_nodes=out_nodes,
+            num_accepted=num_accepted, counters=counters)
     c_par = (ctypes.c_int32 * N)(*par)
-    if out_tokens is None:
-        out_tokens = torch.empty((B, N), dtype=torch.int32, device=target.device)
+    out_tokens, num_accepted = _reject_outputs(B, N, target.device, out_tokens, num_accepted,
+                                               counters)
     if out_nodes is None:
         out_nodes = torch.empty((B, N), dtype=torch.int32, device=target.device)
-    if num_accepted is None:
-        num_accepted = torch.empty((B,), dtype=torch.int32, device=target.device)
-    if counters is not None:
-        _need(counters, "counters", torch.int64)
     ws_bytes = reject_sample_tree_workspace_bytes(B, N, V)
-    if workspace is None and ws_bytes > 0:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=target.device)
-    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, ws_have = _workspace(workspace, ws_bytes, target.device)
     st = lib.spec_reject_sample_tree(_ptr(target), _ptr(draft), ctypes.cast(c_par, ctypes.c_void_p),
                                      _ptr(tokens), _ptr(uniforms), _ptr(temperature),
                                      _ptr(out_tokens), _ptr(out_nodes), _ptr(num_accepted),
@@ -419,27 +490,20 @@ def verify_attn_window(q, k_new, v_new, k_cache, v_cache, block_table, kv_len, a
     (chain) or [B, N] int32 ancestor sets of a tree.  Returns out."""
     import torch
     lib = load()
-    _need(q, "q")
-    dt = _dtype_code(q)
-    for t, name in ((k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache")):
-        _need(t, name, q.dtype)
-    _need(block_table, "block_table", torch.int32)
-    _need(kv_len, "kv_len", torch.int32)
+    B, N, Hq, D, NB, Hkv, dt = _attn_common(q, k_cache, v_cache, block_table, kv_len, out)
+    _need(k_new, "k_new", q.dtype, (B, N, Hkv, D))
+    _need(v_new, "v_new", q.dtype, (B, N, Hkv, D))
     if anc is not None:
-        _need(anc, "anc", torch.int32)
-    B, N, Hq, D = q.shape
-    NB, Hkv = k_cache.shape[0], k_cache.shape[1]
-    if tuple(k_new.shape) != (B, N, Hkv, D) or tuple(v_new.shape) != (B, N, Hkv, D):
-        raise ValueError("k_new / v_new must be [B, N, Hkv, D]")
+        _need(anc, "anc", torch.int32, (B, N))
+    _on_gpu(q=q, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache,
+            block_table=block_table, kv_len=kv_len, anc=anc, out=out)
     mbps = block_table.shape[1]
     if max_kv_len is None:
         max_kv_len = int(kv_len.max().item()) if B > 0 else 0
     if out is None:
         out = torch.empty_like(q)
     ws_bytes = verify_attn_workspace_bytes(B, N - 1, Hq, Hkv, D, max_kv_len)
-    if workspace is None and ws_bytes > 0:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, ws_have = _workspace(workspace, ws_bytes, q.device)
     st = lib.spec_verify_attn_window(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
                                      _ptr(v_cache), _ptr(block_table), _ptr(kv_len), _ptr(anc),
                                      _ptr(out), B, N, Hq, Hkv, D, 16, NB, mbps, int(max_kv_len),
@@ -459,20 +523,26 @@ def kv_commit(k_cache, v_cache, block_table, kv_len, num_accepted, nodes=None, k
     lib = load()
     _need(k_cache, "k_cache")
     dt = _dtype_code(k_cache)
-    _need(v_cache, "v_cache", k_cache.dtype)
-    _need(block_table, "block_table", torch.int32)
-    _need(kv_len, "kv_len", torch.int32)
+    NB, Hkv, D = _kv_caches(k_cache, v_cache, k_cache.dtype)
     _need(num_accepted, "num_accepted", torch.int32)
-    if nodes is not None:
-        _need(nodes, "nodes", torch.int32)
-    if k_src is not None:
-        _need(k_src, "k_src", k_cache.dtype)
-        _need(v_src, "v_src", k_cache.dtype)
+    _dims(num_accepted, "num_accepted", 1)
     B = num_accepted.shape[0]
-    NB, Hkv = k_cache.shape[0], k_cache.shape[1]
-    D = v_cache.shape[2]
+    _need(block_table, "block_table", torch.int32)
+    _dims(block_table, "block_table", 2)
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must have B = %d rows, got %d" % (B, block_table.shape[0]))
+    _need(kv_len, "kv_len", torch.int32, (B,))
     if N is None:
         N = nodes.shape[1] if nodes is not None else (k_src.shape[1] if k_src is not None else 1)
+    if nodes is not None:
+        _need(nodes, "nodes", torch.int32, (B, N))
+    if (k_src is None) != (v_src is None):
+        raise ValueError("k_src and v_src go together")
+    if k_src is not None:
+        _need(k_src, "k_src", k_cache.dtype, (B, N, Hkv, D))
+        _need(v_src, "v_src", k_cache.dtype, (B, N, Hkv, D))
+    _on_gpu(k_cache=k_cache, v_cache=v_cache, block_table=block_table, kv_len=kv_len,
+            num_accepted=num_accepted, nodes=nodes, k_src=k_src, v_src=v_src)
     st = lib.spec_kv_commit(_ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(kv_len),
                             _ptr(num_accepted), _ptr(nodes), _ptr(k_src), _ptr(v_src), B, int(N),
                             Hkv, D, 16, NB, block_table.shape[1], dt, _stream(stream))

@@ -208,3 +208,143 @@ def test_kv_commit_validation(lib):
     assert _commit(lib, D=80) == -2
     assert _commit(lib, B=0) == 0
     assert _commit(lib, nodes=False, src=0) == 0          # chain in place: nothing to move
+
+
+# ---- the Python binding's argument checks (CPU tensors: every shape error is
+# raised before the device check, and nothing reaches the library) -----------
+
+def _rej_args(B=3, K=4, V=50, dtype=None):
+    import torch
+    dt = torch.bfloat16 if dtype is None else dtype
+    return dict(target=torch.zeros((B, K + 1, V), dtype=dt), draft=torch.zeros((B, K, V), dtype=dt),
+                draft_tokens=torch.zeros((B, K), dtype=torch.int32),
+                uniforms=torch.zeros((B, K + 1), dtype=torch.float32),
+                temperature=torch.ones((B,), dtype=torch.float32),
+                kv_len=torch.zeros((B,), dtype=torch.int32))
+
+
+def _raises_about(name, fn, **kw):
+    with pytest.raises((ValueError, TypeError)) as ei:
+        fn(**kw)
+    assert name in str(ei.value), (name, str(ei.value))
+
+
+def test_binding_reject_shapes(lib):
+    import torch
+    f = sv.reject_sample
+    a = _rej_args()
+    _raises_about("target", f, **a)                                   # right shapes: on the GPU check
+    bad = {
+        "draft": torch.zeros((3, 5, 50), dtype=torch.bfloat16),         # [B, K+1, V] instead of [B, K, V]
+        "draft_tokens": torch.zeros((3, 5), dtype=torch.int32),
+        "uniforms": torch.zeros((3, 4), dtype=torch.float32),
+        "temperature": torch.ones((4,), dtype=torch.float32),
+        "kv_len": torch.zeros((2,), dtype=torch.int32),
+        "out_tokens": torch.zeros((3, 4), dtype=torch.int32),
+        "num_accepted": torch.zeros((3, 1), dtype=torch.int32),
+        "counters": torch.zeros((3,), dtype=torch.int64),
+        "top_k": torch.zeros((2,), dtype=torch.int32),
+        "top_p": torch.zeros((3, 1), dtype=torch.float32),
+    }
+    for name, t in bad.items():
+        kw = dict(_rej_args())
+        kw[name] = t
+        _raises_about(name, f, **kw)
+    kw = dict(_rej_args())
+    kw["draft_tokens"] = torch.zeros((3, 4), dtype=torch.int64)       # wrong dtype
+    _raises_about("draft_tokens", f, **kw)
+    kw = dict(_rej_args())
+    kw["draft"] = torch.zeros((3, 4, 50), dtype=torch.float32)        # dtype differs from target
+    _raises_about("draft", f, **kw)
+    kw = dict(_rej_args())
+    kw["target"] = torch.zeros((3, 5), dtype=torch.bfloat16)
+    _raises_about("target", f, **kw)
+    # The no-allocation call takes the same shapes.
+    kw = dict(_rej_args())
+    kw.update(out_tokens=torch.zeros((3, 5), dtype=torch.int32),
+              num_accepted=torch.zeros((4,), dtype=torch.int32))
+    _raises_about("num_accepted", sv.reject_sample_noalloc, **kw)
+
+
+def test_binding_tree_reject_shapes(lib):
+    import torch
+    B, N, V = 2, 4, 30
+    base = dict(target=torch.zeros((B, N, V), dtype=torch.bfloat16),
+                draft=torch.zeros((B, N, V), dtype=torch.bfloat16), parent=[-1, 0, 0, 1],
+                tokens=torch.zeros((B, N), dtype=torch.int32),
+                uniforms=torch.zeros((B, N), dtype=torch.float32),
+                temperature=torch.ones((B,), dtype=torch.float32),
+                kv_len=torch.zeros((B,), dtype=torch.int32))
+    f = sv.reject_sample_tree
+    _raises_about("target", f, **base)
+    for name, t in {"draft": torch.zeros((B, N - 1, V), dtype=torch.bfloat16),
+                    "tokens": torch.zeros((B, N - 1), dtype=torch.int32),
+                    "uniforms": torch.zeros((B + 1, N), dtype=torch.float32),
+                    "out_nodes": torch.zeros((B, N + 1), dtype=torch.int32),
+                    "kv_len": torch.zeros((B, 1), dtype=torch.int32)}.items():
+        kw = dict(base)
+        kw[name] = t
+        _raises_about(name, f, **kw)
+    kw = dict(base)
+    kw["parent"] = [-1, 0, 0]
+    _raises_about("parent", f, **kw)
+
+
+def _attn_args(B=2, K1=8, Hq=32, Hkv=8, D=128, NB=40, mbps=20, dt=None):
+    import torch
+    dt = torch.bfloat16 if dt is None else dt
+    x = 16 // torch.zeros((), dtype=dt).element_size()
+    return dict(q=torch.zeros((B, K1, Hq, D), dtype=dt),
+                k_cache=torch.zeros((NB, Hkv, D // x, 16, x), dtype=dt),
+                v_cache=torch.zeros((NB, Hkv, D, 16), dtype=dt),
+                block_table=torch.zeros((B, mbps), dtype=torch.int32),
+                kv_len=torch.zeros((B,), dtype=torch.int32))
+
+
+def test_binding_attention_shapes(lib):
+    import torch
+    f = sv.verify_attn
+    _raises_about("q", f, **_attn_args())                             # right shapes: device check
+    a = _attn_args()
+    for name, t in {"k_cache": torch.zeros((40, 8, 16, 16, 4), dtype=torch.bfloat16),   # X = 4 for bf16
+                    "v_cache": torch.zeros((40, 8, 16, 128), dtype=torch.bfloat16),     # [NB,Hkv,16,D]
+                    "block_table": torch.zeros((3, 20), dtype=torch.int32),
+                    "kv_len": torch.zeros((3,), dtype=torch.int32),
+                    "out": torch.zeros((2, 8, 32, 64), dtype=torch.bfloat16)}.items():
+        kw = dict(a)
+        kw[name] = t
+        _raises_about(name, f, **kw)
+    kw = _attn_args(D=64)
+    kw["q"] = torch.zeros((2, 8, 32, 128), dtype=torch.bfloat16)      # q's D disagrees with the caches
+    _raises_about("head dim", f, **kw)
+    kw = _attn_args(dt=torch.float32)                                 # fp32 caches use X = 4
+    _raises_about("q", f, **kw)
+    kw = _attn_args()
+    _raises_about("anc", sv.verify_attn_tree, anc=torch.zeros((2, 7), dtype=torch.int32), **kw)
+    # Window call: k_new / v_new are [B, N, Hkv, D].
+    kw = _attn_args()
+    kn = torch.zeros((2, 8, 8, 128), dtype=torch.bfloat16)
+    _raises_about("v_new", sv.verify_attn_window, k_new=kn,
+                  v_new=torch.zeros((2, 8, 8, 64), dtype=torch.bfloat16), **kw)
+    _raises_about("anc", sv.verify_attn_window, k_new=kn, v_new=kn,
+                  anc=torch.zeros((2, 9), dtype=torch.int32), **kw)
+
+
+def test_binding_kv_commit_shapes(lib):
+    import torch
+    a = _attn_args()
+    base = dict(k_cache=a["k_cache"], v_cache=a["v_cache"], block_table=a["block_table"],
+                kv_len=a["kv_len"], num_accepted=torch.zeros((2,), dtype=torch.int32))
+    f = sv.kv_commit
+    _raises_about("k_cache", f, **base)                               # right shapes: device check
+    kw = dict(base)
+    kw["nodes"] = torch.zeros((2, 8), dtype=torch.int32)
+    kw["kv_len"] = torch.zeros((3,), dtype=torch.int32)
+    _raises_about("kv_len", f, **kw)
+    kw = dict(base)
+    kw.update(k_src=torch.zeros((2, 8, 8, 128), dtype=torch.bfloat16),
+              v_src=torch.zeros((2, 8, 4, 128), dtype=torch.bfloat16))
+    _raises_about("v_src", f, **kw)
+    kw = dict(base)
+    kw.update(k_src=torch.zeros((2, 8, 8, 128), dtype=torch.bfloat16))
+    _raises_about("v_src", f, **kw)

@@ -120,6 +120,17 @@ def test_fp32_shapes(gpu_lib, dev):
     _case(gpu_lib, dev, 71, 2, 6, 6, 3, 64, (15, 33), dtype="f32")
 
 
+@pytest.mark.parametrize("B,Hq", [(300, 64), (600, 32), (1100, 32)])
+def test_large_batch_prologue(gpu_lib, dev, B, Hq):
+    """Batches larger than a workgroup's thread count (256 threads for the
+    two-tile kernel at 64 rows, 512 for one tile at 32 rows): each workgroup
+    finds its first sequence by a looped block scan over kv_len instead of a
+    single one.  Short contexts keep the oracle fast; a spread of sequences,
+    the first and the last included, is checked element by element."""
+    idx = sorted(set(range(0, B, 23)) | {1, B // 2, B - 2, B - 1})
+    _case(gpu_lib, dev, 90 + B, B, 7, Hq, 8, 128, (16, 200), idx=idx)
+
+
 def test_split_boundaries(gpu_lib, dev):
     # Many sequences with lengths around split / pair boundaries.
     _case(gpu_lib, dev, 80, 24, 7, 32, 8, 128, (120, 2200))
@@ -164,6 +175,11 @@ def test_empty_batch_and_errors(gpu_lib, dev):
                               torch.zeros((0,), dtype=torch.int32, device=dev), max_kv_len=0)
     assert out.shape == q.shape
     q2 = torch.zeros((1, 8, 32, 96), dtype=torch.bfloat16, device=dev)     # D = 96 unsupported
+    kc2 = torch.zeros((1, 8, 12, 16, 8), dtype=torch.bfloat16, device=dev)
+    vc2 = torch.zeros((1, 8, 96, 16), dtype=torch.bfloat16, device=dev)
     with pytest.raises(gpu_lib.SpecVerifyError):
+        gpu_lib.verify_attn(q2, kc2, vc2, torch.zeros((1, 1), dtype=torch.int32, device=dev),
+                            torch.zeros((1,), dtype=torch.int32, device=dev), max_kv_len=0)
+    with pytest.raises(ValueError):                                       # q and caches disagree on D
         gpu_lib.verify_attn(q2, kc, vc, torch.zeros((1, 1), dtype=torch.int32, device=dev),
                             torch.zeros((1,), dtype=torch.int32, device=dev), max_kv_len=0)

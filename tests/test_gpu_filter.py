@@ -185,5 +185,8 @@ def test_top_p_over_top_k_far_above_the_kth(gpu_lib, dev):
 
 
 def test_top_p_alone_with_spikes(gpu_lib, dev):
+    # Top-p at 0.5 cuts through the bulk: ~2250 distinct bf16 values, so the
+    # mass steps ~1e-4 at the edge and a row is F3-flagged with probability
+    # ~2e-6 / 1e-4; with 7 rows per sequence about 15% of the sequences.
     sp = (_POS, (5.0, 5.5, 6.0), (6.0, 5.5, 5.0))
-    _case(gpu_lib, dev, 12, 32, 3, 32003, 0, 0.5, sigma=0.005, std=0.01, spikes=sp)
+    _case(gpu_lib, dev, 12, 32, 3, 32003, 0, 0.5, sigma=0.005, std=0.01, spikes=sp, max_f3=12)

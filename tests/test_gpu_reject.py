@@ -262,3 +262,57 @@ def test_multi_step_commit_loop(gpu_lib, dev):
         assert np.array_equal(nn[ok], ref["num_accepted"][ok])
         expect += nn + 1
         assert np.array_equal(from_device(kv), expect)
+
+
+def test_residual_classification_near_tied_rows(gpu_lib, dev):
+    """Draft rows equal to the target except a few entries, built so that the
+    two normalisers differ by 1e-8 .. 2e-7 of their value: then every tied
+    entry has q slightly above p, its residual weight is ~1e-8 q, and which
+    side of q = p it falls on must be decided exactly (the fp32 sweep
+    statistics cannot resolve it).  Per sequence, at row 0 (V = 128256, K = 1,
+    T = 1): the logits of entries a1 < a2 are swapped with smaller ones b1,
+    b2 (so the residual holds a1, a2 and the tied entries), and entry c is
+    raised by delta, which sets Sp - Sq; d_1 = c is rejected (u_0 = 0.99)."""
+    B, K, V = 64, 1, 128256
+    rng = np.random.default_rng(4242)
+    x = (rng.standard_normal((B, K + 1, V)) * 2).astype(np.float32)
+    tgt = gen.bf16_bits(x)
+    xt = gen.bf16_to_f32(tgt).astype(np.float64)
+    drf = tgt[:, :K].copy()
+    d = np.zeros((B, K), np.int32)
+    eps_grid = [1e-8, 2e-8, 4e-8, 8e-8, 1.6e-7, 3.2e-7]
+    for b in range(B):
+        row = xt[b, 0]
+        S = np.exp(row).sum()
+        # a1, a2 with logits near -1.5 (mass ~1e-7 each), b1, b2 about one lower.
+        cand = np.nonzero((row > -1.6) & (row < -1.4))[0]
+        a1 = int(cand[cand < V // 2][b % 7])
+        a2 = int(cand[cand > V // 2][b % 5])
+        low = np.nonzero((row > -2.6) & (row < -2.4))[0]
+        b1, b2 = int(low[3 + b % 3]), int(low[-4 - b % 3])
+        for a, bb in ((a1, b1), (a2, b2)):
+            drf[b, 0, a], drf[b, 0, bb] = tgt[b, 0, bb], tgt[b, 0, a]
+        # c with logit near -4: raise it so that (e^{x_c'} - e^{x_c}) / S ~ eps.
+        cs = np.nonzero((row > -4.1) & (row < -3.9))[0]
+        c = int(cs[b % len(cs)])
+        eps = eps_grid[b % len(eps_grid)]
+        new = np.log(np.exp(row[c]) + eps * S)
+        drf[b, 0, c] = gen.bf16_bits(np.float32([new]))[0]
+        d[b, 0] = c
+    u = np.full((B, K + 1), 0.99, np.float32)
+    u[:, K] = gen.uniforms24(rng, B)
+    inp = {"target": tgt, "draft": drf, "draft_tokens": d, "uniforms": u,
+           "temperature": np.ones(B, np.float32)}
+    kv0 = np.full(B, 1000, np.int32)
+    ref = orj.reject_sample(tgt, drf, d, u, inp["temperature"])
+    assert (ref["num_accepted"] == 0).all()
+    out, n, kv_new = _run_gpu(gpu_lib, inp, kv0, dev)
+    # Many of these draws land among the tied entries, whose CDF edges are
+    # ~1e-14 apart, so F2 flags them; the rest must agree exactly.
+    flag = ref["flag_accept"] | ref["flag_sample"]
+    ok = ~flag
+    _say("near-tied rows: %d of %d unflagged" % (int(ok.sum()), B))
+    assert ok.sum() >= B // 4
+    assert np.array_equal(n[ok], ref["num_accepted"][ok])
+    assert np.array_equal(out[ok], ref["out_tokens"][ok])
+    assert np.array_equal(kv_new, kv0 + n + 1)

@@ -118,6 +118,14 @@ def test_fp32_window(gpu_lib, dev):
     _case(gpu_lib, dev, 42, 3, len(par), 8, 2, 128, (5, 90), dtype="f32", parents=[par] * 3)
 
 
+@pytest.mark.parametrize("B,Hq", [(300, 64), (520, 32)])
+def test_large_batch_prologue(gpu_lib, dev, B, Hq):
+    # Past the thread count of a workgroup (256 two-tile, 512 one-tile): the
+    # looped prologue; outputs and caches against the plain call on the
+    # oracle-appended cache (that call's own parity is checked above).
+    _case(gpu_lib, dev, 60 + B, B, 8, Hq, 8, 128, (16, 120), check_oracle=False)
+
+
 def test_empty_context(gpu_lib, dev):
     _case(gpu_lib, dev, 51, 4, 8, 32, 8, 128, 0)                   # L0 = 0: the window alone
 
