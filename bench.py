@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verified tokens/sec at batch 64, K=7, V=128256; % of peak HBM GB/s"
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0          # dense bf16 MFMA
 
 
 def _files_hash(paths):
@@ -81,6 +82,11 @@ def parse():
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="instead of the bench: copy MIB MiB device to device 8 times (the "
                         "known-size kernel that scales the HBM byte counters), then exit")
+    p.add_argument("--peak-probe", action="store_true",
+                   help="instead of the bench: time the streaming-read probe (spec_read_probe) "
+                        "over a 2 GiB buffer and print its bandwidth, then exit")
+    p.add_argument("--no-probe", action="store_true",
+                   help="skip the streaming-read probe in the bench line (measured_peak null)")
     p.add_argument("--sets", type=int, default=3, help="rotating logit sets")
     p.add_argument("--window", default="none", choices=["none", "append", "scratch", "separate"],
                    help="where the window's K/V come from: already in the cache (none); from "
@@ -117,6 +123,9 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     sv.load()
+    if args.peak_probe:
+        print(json.dumps(read_peak(sv)), flush=True)
+        return
     dev = "cuda:0"
     torch.cuda.set_device(0)
     cfg = CONFIGS[args.config]
@@ -254,15 +263,41 @@ def main():
 
     # ---- each call alone: the same number of back-to-back launches, bracketed
     # by HIP events on the launch stream (torch's current stream) -------------
+    timing_mode = []
+
     def timed(fn):
+        """Mean GPU time of one call: the same number of back-to-back calls,
+        captured in one HIP graph and replayed between HIP events on the
+        launch stream, so the host's per-call launch cost (Python argument
+        checks, ctypes) is not in the figure; a short call is otherwise
+        limited by how fast the host enqueues it.  Falls back to eager
+        launches if the capture fails."""
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for s in range(args.steps):
-            fn(s)
-        e1.record()
-        torch.cuda.synchronize()
+        try:
+            g = torch.cuda.CUDAGraph()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                for s in range(args.steps):
+                    fn(s)
+            g.replay()                                  # warm-up replay
+            torch.cuda.synchronize()
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            timing_mode.append("graph")
+            del g
+        except Exception as exc:                        # pragma: no cover - device dependent
+            print("bench: graph capture failed (%s); timing eager launches" % exc,
+                  file=sys.stderr, flush=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for s in range(args.steps):
+                fn(s)
+            e1.record()
+            torch.cuda.synchronize()
+            timing_mode.append("eager")
         return e0.elapsed_time(e1) / args.steps
 
     attn_ms = timed(lambda s: attn_call())
@@ -282,14 +317,34 @@ def main():
     attn_bytes = kv_bytes + qo_bytes + win_write
     attn_us = float(attn_ms * 1e3)
     achieved = attn_bytes / (attn_us * 1e-6) / 1e9
+    # Algorithmic MFMA work: QK^T and PV, 2 D flops each per (query row,
+    # visible key); a chain's row i sees L0 + i + 1 keys, a tree node L0 plus
+    # its path.
+    if parent is None:
+        vis = int(sum(int(l) * K1 + K1 * (K1 + 1) // 2 for l in kvl))
+    else:
+        depth = [bin(int(a)).count("1") for a in ancestor_bits(parent)]
+        vis = int(sum(int(l) * K1 + sum(depth) for l in kvl))
+    attn_flops = 4 * cfg.D * cfg.Hq * vis
+    attn_tflops = attn_flops / (attn_us * 1e-6) / 1e12
+    probe = None if args.no_probe else read_peak(sv)
+    measured_peak = None if probe is None else probe["gbs"]
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": _traffic() if parent is None and args.window == "none" else None,
+                "traffic": (_traffic() if parent is None and args.window == "none"
+                            and cfg.name == "llama8b_b64" and B == cfg.B and args.seed == 2024
+                            else None),
                 "kernel": "%s call = k_attn_stream + k_attn_stream_combine" %
                           ("spec_verify_attn_window (%s)" % args.window
                            if args.window in ("append", "scratch") else
                            "spec_verify_attn" if parent is None else "spec_verify_attn_tree"),
-                "algorithmic_bytes": attn_bytes, "avg_us": round(attn_us, 2)}
+                "algorithmic_bytes": attn_bytes, "avg_us": round(attn_us, 2),
+                "measured_peak": measured_peak,
+                "frac_of_measured_peak": (None if not measured_peak
+                                          else round(achieved / measured_peak, 4)),
+                "mfma": {"tflops": round(attn_tflops, 1), "algorithmic_flops": attn_flops,
+                         "peak_tflops": PEAK_BF16_TFLOPS,
+                         "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4)}}
     # The sweep reads every target row and the draft rows of the nodes with
     # children (all K draft rows of a chain); greedy reads target rows only.
     # The exact passes after rejections come on top and are not counted.
@@ -297,6 +352,18 @@ def main():
     rej_bytes = B * (K1 + (n_draft_rows if args.temp > 0 else 0)) * V * 2
     rej_us = float(rej_ms * 1e3)
     rej_gbs = rej_bytes / (rej_us * 1e-6) / 1e9
+    # The rows the method itself needs: drafts after the first rejection are
+    # discarded, so a chain needs target rows 0..n and draft rows
+    # 0..min(n, K-1) (greedy: target rows 0..n), averaged over the sets the
+    # timed calls rotate through.
+    min_rows = None
+    if parent is None:
+        tot = 0
+        for j in range(args.sets):
+            n = from_device(n_acc[j]).astype(np.int64)
+            tot += int((n + 1).sum()) + (int(np.minimum(n + 1, K).sum()) if args.temp > 0 else 0)
+        min_rows = tot / args.sets
+    rej_min_bytes = None if min_rows is None else int(round(min_rows * V * 2))
 
     # ---- CPU baseline: the oracle on a bounded sample ---------------------
     cpu = None
@@ -325,20 +392,63 @@ def main():
                    "global_batch": B, "K": K, "V": V, "parallelism": "single GPU",
                    "window": args.window, "top_k": args.top_k, "top_p": args.top_p},
         "roofline": roofline,
+        "roofline_reject": {"bound": "hbm", "achieved": round(rej_gbs, 1), "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": round(rej_gbs / PEAK_HBM_GBS, 4),
+                            "traffic": None,
+                            "kernel": "spec_reject_sample%s call" % ("" if parent is None
+                                                                     else "_tree"),
+                            "algorithmic_bytes": rej_bytes, "avg_us": round(rej_us, 2)},
+        "read_probe": probe,
         "cpu_baseline": cpu,
         "kernels": {
             "attn": {"avg_us": round(attn_us, 2), "gbs": round(achieved, 1),
                      "frac_hbm": round(achieved / PEAK_HBM_GBS, 4), "bytes": attn_bytes},
             "reject": {"avg_us": round(rej_us, 2), "gbs": round(rej_gbs, 1),
-                       "frac_hbm": round(rej_gbs / PEAK_HBM_GBS, 4), "bytes": rej_bytes},
+                       "frac_hbm": round(rej_gbs / PEAK_HBM_GBS, 4), "bytes": rej_bytes,
+                       "frac_of_measured_peak": (None if not measured_peak
+                                                 else round(rej_gbs / measured_peak, 4)),
+                       "min_rows_bytes": rej_min_bytes,
+                       "min_rows_per_seq": (None if min_rows is None
+                                            else round(min_rows / B, 3)),
+                       "frac_hbm_min_rows": (None if rej_min_bytes is None else round(
+                           rej_min_bytes / (rej_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4))},
             "commit": None if commit_ms is None else {"avg_us": round(float(commit_ms * 1e3), 2)},
         },
+        "per_call_timing": "/".join(sorted(set(timing_mode))),
         "tokens_per_step": round(tokens / args.steps, 2),
         "positions_per_s": round(B * K1 * args.steps / (total_ms / 1e3), 1),
         "mean_accept_len": round(tokens / args.steps / B, 4),
         "wall_s": round(wall, 3),
     }
     print(json.dumps(rec), flush=True)
+
+
+def read_peak(sv, mib=2048, reps=5):
+    """Streaming-read bandwidth of this GPU: spec_read_probe over a 2 GiB
+    buffer (8x the last-level cache), best of a few grid sizes, each timed
+    over ``reps`` back-to-back launches with HIP events on the launch stream."""
+    import torch
+    buf = torch.zeros(mib << 20, dtype=torch.uint8, device="cuda:0")
+    best = None
+    for grid in (2048, 4096, 8192, 16384):
+        sink = torch.empty(grid, dtype=torch.int32, device="cuda:0")
+        sv.read_probe(buf, sink, grid)                  # warm-up
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            sv.read_probe(buf, sink, grid)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        gbs = buf.numel() / (us * 1e-6) / 1e9
+        if best is None or gbs > best["gbs"]:
+            best = {"gbs": round(gbs, 1), "grid": grid, "bytes": buf.numel(), "avg_us": round(us, 1)}
+    del buf
+    torch.cuda.empty_cache()
+    best["kernel"] = "spec_read_probe (16-byte nontemporal loads, 8 KB per wave step)"
+    return best
 
 
 def copy_calibration(mib):

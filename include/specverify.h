@@ -439,6 +439,19 @@ int spec_bandit_stats(const sv_bandit* bandit, long long* pulls, double* means,
 int spec_accept_stats(const int32_t* num_accepted, int B, int K, double* a,
                       double* mean_len);
 
+/*
+ * spec_read_probe -- a measurement aid, not part of the verify path: reads
+ * `bytes` of device memory at `buf` once with the sweep's access pattern
+ * (16-byte nontemporal loads, 1 KB contiguous per wave instruction, eight in
+ * flight per lane) over `grid` workgroups of 256 threads, and writes one
+ * checksum word per workgroup to `sink` [grid] (device memory).  Timing it
+ * gives the streaming-read bandwidth this chip reaches, against which the
+ * verify kernels' rates are also reported.  bytes must be a positive
+ * multiple of 8192 and buf 16-byte aligned; 1 <= grid <= 2^20; otherwise
+ * SV_ERR_INVALID_ARG.  Asynchronous on hip_stream.
+ */
+int spec_read_probe(const void* buf, size_t bytes, uint32_t* sink, int grid, void* hip_stream);
+
 /* Static description of a status code. */
 const char* spec_status_string(int status);
 

@@ -23,7 +23,7 @@ import ctypes
 import os
 
 __all__ = ["load", "lib_path", "exported_symbols", "verify_attn", "verify_attn_tree",
-           "verify_attn_window", "kv_commit", "PagePool", "DraftLengthBandit", "accept_stats", "SV_WINDOW_READ", "SV_WINDOW_APPEND",
+           "verify_attn_window", "kv_commit", "PagePool", "DraftLengthBandit", "accept_stats", "read_probe", "SV_WINDOW_READ", "SV_WINDOW_APPEND",
            "reject_sample", "reject_sample_noalloc", "reject_sample_tree",
            "verify_attn_workspace_bytes", "NOALLOC_SCRATCH_BYTES",
            "reject_sample_workspace_bytes", "reject_sample_tree_workspace_bytes",
@@ -47,7 +47,7 @@ EXPORTS = ("spec_verify_attn", "spec_verify_attn_workspace_bytes", "spec_verify_
            "spec_pages_block_table", "spec_pages_check",
            "spec_bandit_create", "spec_bandit_destroy", "spec_bandit_select",
            "spec_bandit_update", "spec_bandit_stats", "spec_accept_stats",
-           "spec_status_string", "spec_version")
+           "spec_read_probe", "spec_status_string", "spec_version")
 
 
 class SpecVerifyError(RuntimeError):
@@ -131,6 +131,8 @@ def load():
     lib.spec_bandit_stats.restype = i32
     lib.spec_accept_stats.argtypes = [vp, i32, i32, vp, vp]
     lib.spec_accept_stats.restype = i32
+    lib.spec_read_probe.argtypes = [vp, sz, vp, i32, vp]
+    lib.spec_read_probe.restype = i32
     lib.spec_status_string.argtypes = [i32]
     lib.spec_status_string.restype = ctypes.c_char_p
     lib.spec_version.argtypes = []
@@ -641,6 +643,20 @@ class DraftLengthBandit:
             self._h, ctypes.cast(pulls, ctypes.c_void_p), ctypes.cast(means, ctypes.c_void_p),
             ctypes.byref(t)))
         return list(pulls), list(means), t.value
+
+
+def read_probe(buf, sink, grid, stream=None):
+    """``spec_read_probe``: one streaming read of the bytes of ``buf`` (a
+    device tensor, size a multiple of 8192 bytes) by ``grid`` workgroups;
+    ``sink`` is a device int32 tensor of at least ``grid`` entries."""
+    import torch
+    _need(buf, "buf")
+    _need(sink, "sink", torch.int32)
+    if sink.numel() < grid:
+        raise ValueError("sink needs %d entries" % grid)
+    _on_gpu(buf=buf, sink=sink)
+    _check("spec_read_probe", load().spec_read_probe(
+        _ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), int(grid), _stream(stream)))
 
 
 def accept_stats(num_accepted, K):
