@@ -168,6 +168,7 @@ struct ChainRows {
   int K;
   __device__ __forceinline__ int count() const { return 2 * K + 1; }
   __device__ __forceinline__ bool is_draft(int j) const { return j > K; }
+  __device__ __forceinline__ int n_target() const { return K + 1; }
   __device__ __forceinline__ size_t row(int b, int j) const {
     return j <= K ? (size_t)b * (K + 1) + j : (size_t)b * K + (j - K - 1);
   }
@@ -185,6 +186,7 @@ struct TreeRows {
   TreeShape s;
   __device__ __forceinline__ int count() const { return s.n + s.n_int; }
   __device__ __forceinline__ bool is_draft(int j) const { return j >= s.n; }
+  __device__ __forceinline__ int n_target() const { return s.n; }
   __device__ __forceinline__ int node(int j) const { return j < s.n ? j : s.int_node[j - s.n]; }
   __device__ __forceinline__ size_t row(int b, int j) const { return (size_t)b * s.n + node(j); }
   template <class F>
@@ -291,12 +293,17 @@ __device__ __forceinline__ u32x4_t load_raw_unaligned(const T* __restrict__ row,
 template <typename T, bool kAligned, class Rows>
 __global__ __launch_bounds__(kThreads) void k_sweep(
     const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ dtok,
-    const float* __restrict__ temp, Rows rows, int V, int nc, int force_greedy,
+    const float* __restrict__ temp, Rows rows, int B, int V, int nc, int force_greedy,
     float2* __restrict__ part, float* __restrict__ xd) {
   const int R = rows.count();
-  const int row = blockIdx.x;
-  const int b = row / R;
-  const int j = row - b * R;
+  // Every sequence's target rows first, then the draft rows: a greedy
+  // sequence's draft-row workgroups leave at once, and in this order they are
+  // dispatched after all the rows that are read.
+  const int NT = rows.n_target(), ND = R - NT;
+  const int r = blockIdx.x;
+  const int b = r < B * NT ? r / NT : (r - B * NT) / ND;
+  const int j = r < B * NT ? r - b * NT : NT + (r - B * NT) - b * ND;
+  const int row = b * R + j;                   // row index of the statistics
   const float t = temp_of(temp, b, force_greedy);
   const bool greedy = !(t > 0.f);
   const bool is_draft = rows.is_draft(j);
@@ -1435,6 +1442,7 @@ __global__ __launch_bounds__(kThreads) void k_locate(
   // for sequences that need no draw).
   if (force_greedy) return;                     // every sequence greedy: nothing to draw
   const float t = temp[b];
+  if (!(t > 0.f)) return;                       // greedy: emitted by the decision
   // Thread i < K emits draft i: it keeps its own token (no wait for it here).
   const int my_draw = (int)threadIdx.x < K ? dtok[(size_t)b * K + threadIdx.x] : 0;
   const float u = uni[(size_t)b * (K + 1) + K];
@@ -1627,6 +1635,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_decide_residual(
     unsigned long long* counters, ChunkSums* __restrict__ csum, SubSums* __restrict__ csub) {
   const int b = blockIdx.x;
   const float t = temp_of(temp, b, force_greedy);
+  if (!(t > 0.f) && blockIdx.y != 0) return;    // greedy: block 0 decides and emits; no pass
   const Decision d = decide_chain<kThreads>(b, dtok, uni, t, K, V, nc, part, xd, filt, key16,
                                             blockIdx.y == 0, dec, out, nacc, kv_len, counters);
   if (d.mode == kModeNone) return;
@@ -1957,7 +1966,7 @@ static hipError_t launch_all(const void* tgt, const void* drf, const int32_t* dt
   const T* t = static_cast<const T*>(tgt);
   const T* d = static_cast<const T*>(drf);
   hipLaunchKernelGGL((k_sweep<T, kAligned, ChainRows>), dim3(B * R, (nc + 3) / 4), dim3(kThreads), 0,
-                     st, t, d, dtok, temp, ChainRows{K}, V, nc, force_greedy, part, xd);
+                     st, t, d, dtok, temp, ChainRows{K}, B, V, nc, force_greedy, part, xd);
   const bool filtered = (top_k || top_p) && !force_greedy;
   RowFilter* filt = filtered ? reinterpret_cast<RowFilter*>(ws + p.filt_off) : nullptr;
   if (filtered)
@@ -2056,7 +2065,7 @@ static hipError_t launch_tree(const void* tgt, const void* drf, const TreeShape&
   const T* t = static_cast<const T*>(tgt);
   const T* d = static_cast<const T*>(drf);
   hipLaunchKernelGGL((k_sweep<T, kAligned, TreeRows>), dim3(B * R, (nc + 3) / 4), dim3(kThreads), 0,
-                     st, t, d, tok, temp, TreeRows{shape}, V, nc, force_greedy, part, xd);
+                     st, t, d, tok, temp, TreeRows{shape}, B, V, nc, force_greedy, part, xd);
   hipLaunchKernelGGL(k_tree_decide, dim3(B), dim3(kDecideThreads), 0, st, tok, uni, temp, shape, V, nc,
                      force_greedy, part, xd, rowstat, dec, state, out_tok, out_node, nacc, kv_len,
                      counters);
