@@ -11,8 +11,9 @@
 // kept; the siblings of a node are tried one after another by recursive
 // rejection sampling, which keeps the output law exact.
 //
-// Three kernels on the caller's stream (chain; four with top-k / top-p, whose
-// k_filter runs between the sweep and the decision):
+// Two kernels on the caller's stream for the chain (three with top-k / top-p,
+// whose k_filter runs between the sweep and the decision; a third, k_locate,
+// takes the draw when V > 2^19):
 //   k_sweep     one pass over every logit row (the HBM-bound part): per 4096-
 //               entry chunk, the raw maximum and sum_v 2^(x_v c - m) in fp32
 //               (c = log2(e) / T), or the chunk argmax for greedy sequences.
@@ -35,15 +36,14 @@
 //               q > c p, with e = 2^((x - xmax) c) to a few ulp.  They give
 //               the exact normalisers and residual masses, so the row pair is
 //               read only once more.
-//   k_locate    per sampling sequence: float64 prefix scans over the chunk
-//               masses, then the sub-chunk masses, then one 256-entry run of
-//               exact weights; emit the tokens and commit kv_len.
+//   the draw   in the workgroup that completes a sampling sequence's pass:
+//               float64 prefix scans over the chunk masses, then the
+//               sub-chunk masses, then one 256-entry run of exact weights;
+//               emit the tokens and commit kv_len.
 // The final draw's weights are exact to 2e-13 relative, so the draw agrees
 // with a float64 reference except within ~1e-12 of probability mass around
-// the CDF edges.  (Handing a sequence from its last pass block to the
-// draw inside one kernel would need device-scope fences per block, which
-// write back and invalidate each XCD's L2; measured, a kernel boundary is
-// far cheaper.)
+// the CDF edges.  The pass workgroups hand their sums to the one that draws
+// without device-scope fences (see the hand-off helpers below).
 //
 // Tree: the same sweep over the target rows of all nodes and the draft rows
 // of the nodes with children; k_tree_decide walks down from the root while
@@ -51,15 +51,16 @@
 // there).  After a rejection the next sibling is tested against the residual
 // q' = (q - coef p)_+ / Z, where coef starts at 1 and grows by Z with every
 // further rejection; Z needs one exact pass over the node's row pair (the
-// chain's pass, in k_residual).  So the tree runs in rounds of k_residual +
-// k_tree_step, each round one such pass per sequence that still needs one;
-// the host knows from the tree's shape how many rounds the longest walk can
-// take.
+// chain's pass).  So the tree runs in rounds of k_tree_round, each round one
+// such pass per sequence that still needs one, followed in the same kernel
+// by the step after it (run by the workgroup that completes the sequence's
+// pass, from chunk sums handed over without fences, as below); the host
+// knows from the tree's shape how many rounds the longest walk can take.
 // No floating-point atomics and fixed reduction orders: results are bitwise
 // reproducible run to run.
 
 // Contraction off: merges must stay symmetric in their operands, and the
-// weights of k_locate must equal those of the pass bit for bit.  Fused
+// weights of the draw must equal those of the pass bit for bit.  Fused
 // multiply-adds that are wanted are written out.
 #pragma clang fp contract(off)
 
@@ -77,13 +78,13 @@ constexpr int kDecideThreads = 1024;  // tree decision: 16 lanes per row statist
 #define SV_SWEEP_CHUNK 4096
 #endif
 constexpr int kSweepChunk = SV_SWEEP_CHUNK;   // entries per wave in k_sweep
-constexpr int kResChunk = 8192;       // entries per block in k_residual
+constexpr int kResChunk = 8192;       // entries per block of a residual pass
 constexpr int kMaxRows = 2 * SV_MAX_K + 1;
 constexpr double kLog2eD = 1.4426950408889634074;
 
 
 // One exact pass over a row pair (and the draw that may follow it), as the
-// decide and step kernels leave it for k_residual.
+// decide and step kernels leave it for the next pass.
 enum : int {
   kModeNone = 0,    // nothing to do: greedy or finished
   kModeQ = 1,       // target row only: the draw is from q (bonus token)
@@ -210,6 +211,45 @@ struct SubSums {
   double a, b, q, p;
 };
 
+// ---- Hand-offs between workgroups of one kernel (the chain's draw and the
+// tree's rounds: the workgroup that completes a sequence's pass takes the
+// next step).  The sums one workgroup leaves for another are stored with
+// device-scope relaxed atomic stores, which write through the XCD's L2, and
+// read with device-scope relaxed atomic loads, which do not return a stale
+// L2 copy; the writer drains its memory counter before it counts itself in,
+// and the reader reads only after it has seen the count complete.  No
+// device-scope fence is used: on this chip a release fence writes back and an
+// acquire fence invalidates the whole L2 of the XCD.
+typedef unsigned long long u64;
+
+__device__ __forceinline__ double ld_agent_d(const double* p) {
+  return __longlong_as_double((long long)__hip_atomic_load(
+      reinterpret_cast<const u64*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void st_agent_d(double* p, double v) {
+  __hip_atomic_store(reinterpret_cast<u64*>(p), (u64)__double_as_longlong(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+// Every memory access this wave has issued is complete (its device-scope
+// stores are visible to every workgroup).
+__device__ __forceinline__ void vm_drain() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ __forceinline__ double ld_sum(const double* p, bool agent) {
+  return agent ? ld_agent_d(p) : *p;
+}
+__device__ __forceinline__ SubSums ld_sub_sums(const SubSums* p) {
+  const double* d = reinterpret_cast<const double*>(p);
+  return SubSums{ld_agent_d(d), ld_agent_d(d + 1), ld_agent_d(d + 2), ld_agent_d(d + 3)};
+}
+__device__ __forceinline__ ChunkSums ld_chunk_sums(const ChunkSums* p, bool agent) {
+  if (!agent) return *p;
+  const double* d = reinterpret_cast<const double*>(p);
+  return ChunkSums{ld_agent_d(d), ld_agent_d(d + 1), ld_agent_d(d + 2), ld_agent_d(d + 3)};
+}
+
 __host__ __device__ inline int sweep_chunks(int V) { return (V + kSweepChunk - 1) / kSweepChunk; }
 __host__ __device__ inline int res_chunks(int V) { return (V + kResChunk - 1) / kResChunk; }
 
@@ -288,13 +328,15 @@ __device__ __forceinline__ u32x4_t load_raw_unaligned(const T* __restrict__ row,
 // ---------------------------------------------------------------------------
 // k_sweep: grid (B * rows.count(), ceil(nc / 4)); block 256 = 4 waves, one
 // chunk each.  part[row * nc + chunk] = (raw max, sum 2^(x c - fl(max c)))
-// or, greedy, (max value, argmax index bits).
+// or, greedy, (max value, argmax index bits).  Also zeroes pcnt[0..B).
 // ---------------------------------------------------------------------------
 template <typename T, bool kAligned, class Rows>
 __global__ __launch_bounds__(kThreads) void k_sweep(
     const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ dtok,
     const float* __restrict__ temp, Rows rows, int B, int V, int nc, int force_greedy,
-    float2* __restrict__ part, float* __restrict__ xd) {
+    float2* __restrict__ part, float* __restrict__ xd, unsigned* __restrict__ pcnt) {
+  // Clears the per-sequence pass counts the later kernels count in with.
+  if (blockIdx.y == 0 && (int)blockIdx.x < B && threadIdx.x == 0) pcnt[blockIdx.x] = 0u;
   const int R = rows.count();
   // Every sequence's target rows first, then the draft rows: a greedy
   // sequence's draft-row workgroups leave at once, and in this order they are
@@ -1289,15 +1331,19 @@ __device__ __forceinline__ double wave_chunk_sum(int ncr, F f, int lane) {
 // token in every thread, or -1 in every thread when d asks for no draw.
 // d, u and t are first read after the sums are staged, so a caller can pass
 // values whose loads are still in flight.
-template <typename T>
+// kAgent: the sums were stored by other workgroups of the running kernel
+// (device-scope loads, ncr <= 64): the first wave holds chunk i's sums on
+// lane i, then the chosen chunk's sub-chunk sums, in registers; no staging.
+template <typename T, bool kAgent = false>
 __device__ __forceinline__ int locate_draw(const T* __restrict__ tgt, const T* __restrict__ drf,
                                            const Decision& d, float u, float t, int V, int ncr,
                                            const ChunkSums* __restrict__ cg,
                                            const SubSums* __restrict__ sg,
                                            double* __restrict__ s_exp, bool fill_table) {
   static_assert(kSub == kThreads, "one sub-chunk entry per thread");
-  constexpr int kSubStage = 1024;                // sub-chunk sums staged in LDS (32 KB)
-  __shared__ ChunkSums s_cs[kThreads];
+  static_assert(kSubPerChunk <= 64, "one sub-chunk per lane");
+  constexpr int kSubStage = kAgent ? 1 : 1024;   // sub-chunk sums staged in LDS (32 KB)
+  __shared__ ChunkSums s_cs[kAgent ? 1 : kThreads];
   __shared__ SubSums s_ss[kSubStage];
   __shared__ double s_wtot[kThreads / 64];
   __shared__ int s_chunk, s_sub, s_fallback, s_mode, s_first, s_lastpos;
@@ -1307,12 +1353,17 @@ __device__ __forceinline__ int locate_draw(const T* __restrict__ tgt, const T* _
   // for both, V <= 2^21 for the chunk sums), read in place otherwise: the
   // sub-chunk level then needs no second round trip to memory.  The loads
   // are issued before the table is filled and stored to LDS after it.
-  const bool staged = ncr <= kThreads;
-  const bool sub_staged = ncr * kSubPerChunk <= kSubStage;
+  const bool staged = !kAgent && ncr <= kThreads;
+  const bool sub_staged = !kAgent && ncr * kSubPerChunk <= kSubStage;
   // Waves 0-1 stage the sums (all loads issued before any is stored), waves
   // 2-3 fill the table meanwhile.
   constexpr int kHalf = kThreads / 2;
-  if (tid < kHalf) {
+  ChunkSums my_cs{};
+  if constexpr (kAgent) {
+    if (tid < min(ncr, 64)) my_cs = ld_chunk_sums(cg + tid, true);
+    if (fill_table)
+      for (int j = tid; j < kExpTable; j += kThreads) s_exp[j] = exp2((double)j * (1.0 / 256));
+  } else if (tid < kHalf) {
     constexpr int kSubH = kSubStage / kHalf;
     static_assert(kThreads == 2 * kHalf, "two chunk sums per staging thread");
     // Clamped indices: every load and store is unconditional inside the
@@ -1346,24 +1397,27 @@ __device__ __forceinline__ int locate_draw(const T* __restrict__ tgt, const T* _
   const T* drow = drf + (size_t)d.drow * V;
   const ChunkSums* cs = staged ? s_cs : cg;
   if (wave == 0) {
+    // Chunk i's sums (every caller below asks only for i = lane + 64 j; with
+    // kAgent only for i = lane).
+    const auto chunk = [&](int i) { return kAgent ? my_cs : cs[i]; };
     // Exact normalisers, then the masses of the chunks.
-    const double sq = wave_chunk_sum(ncr, [&](int i) { return cs[i].eq; }, lane);
-    const double sp = wave_chunk_sum(ncr, [&](int i) { return cs[i].ep; }, lane);
+    const double sq = wave_chunk_sum(ncr, [&](int i) { return chunk(i).eq; }, lane);
+    const double sp = wave_chunk_sum(ncr, [&](int i) { return chunk(i).ep; }, lane);
     const double isq = 1.0 / sq;
     int m = d.mode == kModeQ ? kDrawQ : kDrawResid;
     double isp = m == kDrawQ ? 0.0 : d.coef / sp;
-    double z = wave_chunk_sum(ncr, [&](int i) { return chunk_mass(cs[i], m, isq, isp); }, lane);
+    double z = wave_chunk_sum(ncr, [&](int i) { return chunk_mass(chunk(i), m, isq, isp); }, lane);
     if (m == kDrawResid && !(z > 0.0)) {
       // Zero residual mass: the law stays (q - coef_prev p)_+ normalised, and
       // with no mass above p it equals p (q itself when coef_prev = 0).
       m = d.coef_prev == 0.0 ? kDrawQ : kDrawP;
       isp = 1.0 / sp;
-      z = wave_chunk_sum(ncr, [&](int i) { return chunk_mass(cs[i], m, isq, isp); }, lane);
+      z = wave_chunk_sum(ncr, [&](int i) { return chunk_mass(chunk(i), m, isq, isp); }, lane);
     }
     const double target = (double)u * z;
     double base = 0.0;
     int lastpos;
-    int ch = wave_find(ncr, [&](int i) { return chunk_mass(cs[i], m, isq, isp); }, target, base,
+    int ch = wave_find(ncr, [&](int i) { return chunk_mass(chunk(i), m, isq, isp); }, target, base,
                        lastpos, lane);
     int fb = 0;
     if (ch < 0) {                                             // rounding at u -> 1
@@ -1372,9 +1426,12 @@ __device__ __forceinline__ int locate_draw(const T* __restrict__ tgt, const T* _
     }
     // Sub-chunk level, same wave (no crossing is looked for once in fallback).
     const SubSums* ss = (sub_staged ? s_ss : sg) + (size_t)ch * kSubPerChunk;
+    SubSums my_ss{};
+    if (kAgent && lane < kSubPerChunk) my_ss = ld_sub_sums(ss + lane);
     double base2 = base;
     int lastsub;
-    int sc = wave_find(kSubPerChunk, [&](int j) { return sub_mass(ss[j], m, isq, isp); },
+    int sc = wave_find(kSubPerChunk,
+                       [&](int j) { return sub_mass(kAgent ? my_ss : ss[j], m, isq, isp); },
                        fb ? (double)INFINITY : target, base2, lastsub, lane);
     if (sc < 0) {                                             // no crossing left: last positive run
       fb = 1;
@@ -1464,23 +1521,26 @@ __device__ __forceinline__ void mask_row(float (&x)[Vec16<T>::N], uint32_t kmin)
 }
 
 // ---------------------------------------------------------------------------
-// k_residual: grid (B, ncr); block 256.  The pass each decision asks for
-// (none for greedy or finished sequences).
+// One block's share of the exact pass a decision asks for: chunk cr of the
+// row pair, 8192 entries.
 //
 // Lane mapping: the 8 lanes of group g = lane / 8 in wave w own sub-chunk
 // w * 8 + g (256 entries).  Each of their loads covers one 128-byte line of it,
 // so an instruction of the wave still reads 8 whole lines, and a sub-chunk's
 // sums need only 3 butterfly steps.
 // ---------------------------------------------------------------------------
-template <typename T, bool kAligned, bool kMask>
+// kAgent: the sums are stored with device-scope stores, for a workgroup of
+// the same kernel that reads them.  s_exp: the block's exp table (256
+// doubles of LDS), filled here.
+template <typename T, bool kAligned, bool kMask, bool kAgent = false>
 __device__ __forceinline__ void residual_pass(const T* __restrict__ tgt, const T* __restrict__ drf,
                                               const Decision& d, float t, int V, int ncr, int b, int cr,
-                                              ChunkSums* __restrict__ csum, SubSums* __restrict__ csub) {
+                                              ChunkSums* __restrict__ csum, SubSums* __restrict__ csub,
+                                              double* __restrict__ s_exp) {
   constexpr int VN = Vec16<T>::N;
   constexpr int kLine = 8 * VN;                   // entries per 8-lane load (128 bytes)
   constexpr int IT = kSub / kLine;                // loads per lane per row
   static_assert(kThreads / 8 == kSubPerChunk, "one 8-lane group per sub-chunk");
-  __shared__ double s_exp[kExpTable];
   __shared__ SubSums s_sub[kSubPerChunk];
   const int tid = threadIdx.x;
   const int sub_i = tid >> 3, s = tid & 7;
@@ -1593,7 +1653,13 @@ __device__ __forceinline__ void residual_pass(const T* __restrict__ tgt, const T
   sb = group8_sum_d(sb);
   if (s == 0) {
     const SubSums ss{sa, sb, sq, sp};
-    csub[((size_t)b * ncr + cr) * kSubPerChunk + sub_i] = ss;
+    SubSums* dst = csub + ((size_t)b * ncr + cr) * kSubPerChunk + sub_i;
+    if (kAgent) {
+      double* dd = reinterpret_cast<double*>(dst);
+      st_agent_d(dd, sa); st_agent_d(dd + 1, sb); st_agent_d(dd + 2, sq); st_agent_d(dd + 3, sp);
+    } else {
+      *dst = ss;
+    }
     s_sub[sub_i] = ss;
   }
   __syncthreads();
@@ -1604,42 +1670,49 @@ __device__ __forceinline__ void residual_pass(const T* __restrict__ tgt, const T
     const int comp = (tid + 2) & 3;
     double acc = 0.0;
     for (int j = 0; j < kSubPerChunk; ++j) acc += reinterpret_cast<const double*>(&s_sub[j])[comp];
-    reinterpret_cast<double*>(csum + (size_t)b * ncr + cr)[tid] = acc;
+    double* dst = reinterpret_cast<double*>(csum + (size_t)b * ncr + cr) + tid;
+    if (kAgent) st_agent_d(dst, acc);
+    else *dst = acc;
   }
-}
-
-// Tree rounds: the pass the walk's decision asks for.
-template <typename T, bool kAligned>
-__global__ __launch_bounds__(kThreads, 4) void k_residual(
-    const T* __restrict__ tgt, const T* __restrict__ drf, const float* __restrict__ temp,
-    int V, int ncr, int force_greedy, const Decision* __restrict__ dec,
-    ChunkSums* __restrict__ csum, SubSums* __restrict__ csub) {
-  const int b = blockIdx.x;
-  const Decision d = dec[b];
-  if (d.mode == kModeNone || d.mode == kModePending) return;
-  residual_pass<T, kAligned, false>(tgt, drf, d, temp_of(temp, b, force_greedy), V, ncr, b,
-                                    blockIdx.y, csum, csub);
 }
 
 // The chain: every block first takes its sequence's decision itself (the
 // same values in each; block 0 also stores it and emits greedy sequences),
 // which saves a kernel boundary and a dependent read of the decision before
-// the rows can be requested.
-template <typename T, bool kAligned, bool kMask = false>
+// the rows can be requested.  kDraw (ncr <= 64): the workgroup that completes
+// a sequence's pass (its count in pcnt reaches ncr) then makes the final
+// draw and emits, from the sums handed over as described above; otherwise
+// k_locate does, in a kernel of its own.
+template <typename T, bool kAligned, bool kMask = false, bool kDraw = false>
 __global__ __launch_bounds__(kThreads, 4) void k_decide_residual(
     const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ dtok,
     const float* __restrict__ uni, const float* __restrict__ temp, int K, int V, int nc, int ncr,
     int force_greedy, const float2* __restrict__ part, const float* __restrict__ xd,
     const RowFilter* __restrict__ filt, int key16, Decision* __restrict__ dec,
     int32_t* __restrict__ out, int32_t* __restrict__ nacc, int32_t* __restrict__ kv_len,
-    unsigned long long* counters, ChunkSums* __restrict__ csum, SubSums* __restrict__ csub) {
+    unsigned long long* counters, ChunkSums* __restrict__ csum, SubSums* __restrict__ csub,
+    unsigned* __restrict__ pcnt) {
   const int b = blockIdx.x;
   const float t = temp_of(temp, b, force_greedy);
   if (!(t > 0.f) && blockIdx.y != 0) return;    // greedy: block 0 decides and emits; no pass
   const Decision d = decide_chain<kThreads>(b, dtok, uni, t, K, V, nc, part, xd, filt, key16,
                                             blockIdx.y == 0, dec, out, nacc, kv_len, counters);
   if (d.mode == kModeNone) return;
-  residual_pass<T, kAligned, kMask>(tgt, drf, d, t, V, ncr, b, blockIdx.y, csum, csub);
+  __shared__ double s_exp[kExpTable];
+  residual_pass<T, kAligned, kMask, kDraw>(tgt, drf, d, t, V, ncr, b, blockIdx.y, csum, csub, s_exp);
+  if (!kDraw) return;
+  __shared__ int s_last;
+  vm_drain();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(pcnt + b, 1u) + 1u == (unsigned)ncr ? 1 : 0;
+  __syncthreads();
+  if (!s_last) return;
+  // Thread i < K emits draft i: it keeps its own token.
+  const int my_draw = (int)threadIdx.x < K ? dtok[(size_t)b * K + threadIdx.x] : 0;
+  const float u = uni[(size_t)b * (K + 1) + K];
+  const int tok = locate_draw<T, true>(tgt, drf, d, u, t, V, ncr, csum + (size_t)b * ncr,
+                                       csub + (size_t)b * ncr * kSubPerChunk, s_exp, false);
+  emit_own(b, K, d.n, tok, my_draw, out, nacc, kv_len, counters);
 }
 
 // ---------------------------------------------------------------------------
@@ -1788,28 +1861,26 @@ __global__ __launch_bounds__(kDecideThreads) void k_tree_decide(
 }
 
 // ---------------------------------------------------------------------------
-// k_tree_step: grid (B); block 256.  One round after the pass k_residual made
-// for each active sequence: the next sibling's test against the exact
+// The step after a tree pass, for sequence b (a block of 256 threads, the one
+// that completed the pass): the next sibling's test against the exact
 // residual, which schedules the next pass (a further rejection, or a
 // rejection or leaf below an accepted child), or the end of the walk, whose
 // draw from this pass is left to k_tree_draw (the pass's sums stay in place:
 // no later pass of the sequence overwrites them).  So a round waits for no
-// draw, and all draws take one launch after the last round.
+// draw, and all draws take one launch after the last round.  kAgent: the
+// pass's chunk sums were stored by other workgroups of the running kernel.
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(kThreads) void k_tree_step(
-    const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ tok,
-    const float* __restrict__ uni, const float* __restrict__ temp, TreeShape s, int V, int ncr,
-    int force_greedy, int last, const float2* __restrict__ rowstat, const float* __restrict__ xd,
-    const ChunkSums* __restrict__ csum, const SubSums* __restrict__ csub,
-    Decision* __restrict__ dec, TreeState* __restrict__ state, int32_t* __restrict__ out_tok,
-    int32_t* __restrict__ out_node, int32_t* __restrict__ nacc, int32_t* __restrict__ kv_len,
-    unsigned long long* counters) {
+template <bool kAgent>
+__device__ void tree_step(
+    int b, const int32_t* __restrict__ tok, const float* __restrict__ uni, const float* __restrict__ temp,
+    const TreeShape& s, int ncr, int force_greedy, int last, const float2* __restrict__ rowstat,
+    const float* __restrict__ xd, const ChunkSums* __restrict__ csum, Decision* __restrict__ dec,
+    TreeState* __restrict__ state, int32_t* __restrict__ out_tok, int32_t* __restrict__ out_node,
+    int32_t* __restrict__ nacc) {
   __shared__ float2 s_rs[2 * kMaxTree];
   __shared__ float s_xd[2 * kMaxTree], s_u[kMaxTree];
   __shared__ int s_tk[kMaxTree];
   __shared__ int s_draw, s_n;
-  const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = s.n, R = s.n + s.n_int;
   // The walk's inputs, loaded together with the decision (one round trip).
@@ -1831,11 +1902,11 @@ __global__ __launch_bounds__(kThreads) void k_tree_step(
     if (!st.fin) {
       // The pass ran at coef after a rejection; its exact normalisers and the
       // residual mass Z (summed exactly as the draw sums it).
-      const double sq = wave_chunk_sum(ncr, [&](int i) { return cg[i].eq; }, lane);
-      const double sp = wave_chunk_sum(ncr, [&](int i) { return cg[i].ep; }, lane);
+      const double sq = wave_chunk_sum(ncr, [&](int i) { return ld_sum(&cg[i].eq, kAgent); }, lane);
+      const double sp = wave_chunk_sum(ncr, [&](int i) { return ld_sum(&cg[i].ep, kAgent); }, lane);
       const double isq = 1.0 / sq, isp = d.coef / sp;
-      const double z = wave_chunk_sum(ncr, [&](int i) { return chunk_mass(cg[i], kDrawResid, isq, isp); },
-                                      lane);
+      const double z = wave_chunk_sum(
+          ncr, [&](int i) { return chunk_mass(ld_chunk_sums(cg + i, kAgent), kDrawResid, isq, isp); }, lane);
       if (lane == 0) {
         // A zero-mass residual leaves the law as it was.
         const bool frozen = !(z > 0.0);
@@ -1904,6 +1975,38 @@ __global__ __launch_bounds__(kThreads) void k_tree_step(
   }
 }
 
+// ---------------------------------------------------------------------------
+// k_tree_round: grid (B, ncr); block 256.  One round of the tree walks: the
+// pass each decision asks for (none for greedy, finished or pending
+// sequences), then, in the workgroup that completes a sequence's pass (its
+// count in rcnt reaches ncr), the step that follows.  That workgroup resets
+// the count for the next round; k_sweep clears it before the first.
+// ---------------------------------------------------------------------------
+template <typename T, bool kAligned>
+__global__ __launch_bounds__(kThreads, 4) void k_tree_round(
+    const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ tok,
+    const float* __restrict__ uni, const float* __restrict__ temp, TreeShape s, int V, int ncr,
+    int force_greedy, int last, const float2* __restrict__ rowstat, const float* __restrict__ xd,
+    ChunkSums* __restrict__ csum, SubSums* __restrict__ csub, Decision* __restrict__ dec,
+    TreeState* __restrict__ state, unsigned* __restrict__ rcnt, int32_t* __restrict__ out_tok,
+    int32_t* __restrict__ out_node, int32_t* __restrict__ nacc) {
+  __shared__ double s_exp[kExpTable];
+  __shared__ int s_last;
+  const int b = blockIdx.x;
+  const Decision d = dec[b];
+  if (d.mode == kModeNone || d.mode == kModePending) return;     // block-uniform
+  residual_pass<T, kAligned, false, true>(tgt, drf, d, temp_of(temp, b, force_greedy), V, ncr, b,
+                                          blockIdx.y, csum, csub, s_exp);
+  vm_drain();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(rcnt + b, 1u) + 1u == (unsigned)ncr ? 1 : 0;
+  __syncthreads();
+  if (!s_last) return;
+  if (threadIdx.x == 0) __hip_atomic_store(rcnt + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  tree_step<true>(b, tok, uni, temp, s, ncr, force_greedy, last, rowstat, xd, csum, dec, state,
+                  out_tok, out_node, nacc);
+}
+
 // k_tree_draw: grid (B); block 256.  The draws of the walks that ended in
 // any round, each from the last pass of its sequence, then the outputs.
 template <typename T>
@@ -1931,7 +2034,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_draw(
 }
 
 struct RejectPlan {
-  size_t part_off, csum_off, csub_off, dec_off, xd_off, filt_off, total;
+  size_t part_off, csum_off, csub_off, dec_off, xd_off, filt_off, cnt_off, total;
 };
 
 static inline RejectPlan reject_plan(int B, int K, int V) {
@@ -1944,7 +2047,8 @@ static inline RejectPlan reject_plan(int B, int K, int V) {
   p.dec_off = p.csub_off + up((size_t)B * res_chunks(V) * kSubPerChunk * sizeof(SubSums));
   p.xd_off = p.dec_off + up((size_t)B * sizeof(Decision));
   p.filt_off = p.xd_off + up((size_t)B * K * 2 * sizeof(float));
-  p.total = p.filt_off + up((size_t)B * R * sizeof(RowFilter));
+  p.cnt_off = p.filt_off + up((size_t)B * R * sizeof(RowFilter));
+  p.total = p.cnt_off + up((size_t)B * sizeof(unsigned));
   return p;
 }
 
@@ -1965,31 +2069,44 @@ static hipError_t launch_all(const void* tgt, const void* drf, const int32_t* dt
   float* xd = reinterpret_cast<float*>(ws + p.xd_off);
   const T* t = static_cast<const T*>(tgt);
   const T* d = static_cast<const T*>(drf);
+  unsigned* pcnt = reinterpret_cast<unsigned*>(ws + p.cnt_off);
   hipLaunchKernelGGL((k_sweep<T, kAligned, ChainRows>), dim3(B * R, (nc + 3) / 4), dim3(kThreads), 0,
-                     st, t, d, dtok, temp, ChainRows{K}, B, V, nc, force_greedy, part, xd);
+                     st, t, d, dtok, temp, ChainRows{K}, B, V, nc, force_greedy, part, xd, pcnt);
   const bool filtered = (top_k || top_p) && !force_greedy;
   RowFilter* filt = filtered ? reinterpret_cast<RowFilter*>(ws + p.filt_off) : nullptr;
   if (filtered)
     hipLaunchKernelGGL((k_filter<T, kAligned>), dim3(B * R), dim3(kFilterThreads), 0, st, t, d, temp,
                        top_k, top_p, K, V, nc, force_greedy, part, filt);
   const int key16 = sizeof(T) == 2 ? 1 : 0;
-  if (filtered)
-    hipLaunchKernelGGL((k_decide_residual<T, kAligned, true>), dim3(B, ncr), dim3(kThreads), 0, st, t,
-                       d, dtok, uni, temp, K, V, nc, ncr, force_greedy, part, xd, filt, key16, dec, out,
-                       nacc, kv_len, counters, csum, csub);
+  // The draw joins the pass kernel while the chunk sums fit one wave.
+  const bool fused = ncr <= 64;
+  const dim3 grid(B, ncr), block(kThreads);
+  if (filtered && fused)
+    hipLaunchKernelGGL((k_decide_residual<T, kAligned, true, true>), grid, block, 0, st, t, d, dtok, uni,
+                       temp, K, V, nc, ncr, force_greedy, part, xd, filt, key16, dec, out, nacc, kv_len,
+                       counters, csum, csub, pcnt);
+  else if (filtered)
+    hipLaunchKernelGGL((k_decide_residual<T, kAligned, true, false>), grid, block, 0, st, t, d, dtok,
+                       uni, temp, K, V, nc, ncr, force_greedy, part, xd, filt, key16, dec, out, nacc,
+                       kv_len, counters, csum, csub, pcnt);
+  else if (fused)
+    hipLaunchKernelGGL((k_decide_residual<T, kAligned, false, true>), grid, block, 0, st, t, d, dtok,
+                       uni, temp, K, V, nc, ncr, force_greedy, part, xd, filt, key16, dec, out, nacc,
+                       kv_len, counters, csum, csub, pcnt);
   else
-    hipLaunchKernelGGL((k_decide_residual<T, kAligned>), dim3(B, ncr), dim3(kThreads), 0, st, t, d,
-                       dtok, uni, temp, K, V, nc, ncr, force_greedy, part, xd, filt, key16, dec, out,
-                       nacc, kv_len, counters, csum, csub);
-  hipLaunchKernelGGL((k_locate<T>), dim3(B), dim3(kThreads), 0, st, t, d, dtok, uni, temp, K, V, ncr,
-                     force_greedy, csum, csub, dec, out, nacc, kv_len, counters);
+    hipLaunchKernelGGL((k_decide_residual<T, kAligned, false, false>), grid, block, 0, st, t, d, dtok,
+                       uni, temp, K, V, nc, ncr, force_greedy, part, xd, filt, key16, dec, out, nacc,
+                       kv_len, counters, csum, csub, pcnt);
+  if (!fused)
+    hipLaunchKernelGGL((k_locate<T>), dim3(B), dim3(kThreads), 0, st, t, d, dtok, uni, temp, K, V, ncr,
+                       force_greedy, csum, csub, dec, out, nacc, kv_len, counters);
   return hipGetLastError();
 }
 
 // Tree workspace: the chain's arrays for up to 2N - 1 swept rows, plus the
 // merged row statistics and the walk states.
 struct TreePlan {
-  size_t part_off, rowstat_off, csum_off, csub_off, dec_off, state_off, xd_off, total;
+  size_t part_off, rowstat_off, csum_off, csub_off, dec_off, state_off, xd_off, rcnt_off, total;
 };
 
 static inline TreePlan tree_plan(int B, int N, int V) {
@@ -2003,7 +2120,8 @@ static inline TreePlan tree_plan(int B, int N, int V) {
   p.dec_off = p.csub_off + up((size_t)B * res_chunks(V) * kSubPerChunk * sizeof(SubSums));
   p.state_off = p.dec_off + up((size_t)B * sizeof(Decision));
   p.xd_off = p.state_off + up((size_t)B * sizeof(TreeState));
-  p.total = p.xd_off + up((size_t)B * N * 2 * sizeof(float));
+  p.rcnt_off = p.xd_off + up((size_t)B * N * 2 * sizeof(float));
+  p.total = p.rcnt_off + up((size_t)B * sizeof(unsigned));
   return p;
 }
 
@@ -2062,21 +2180,19 @@ static hipError_t launch_tree(const void* tgt, const void* drf, const TreeShape&
   Decision* dec = reinterpret_cast<Decision*>(ws + p.dec_off);
   TreeState* state = reinterpret_cast<TreeState*>(ws + p.state_off);
   float* xd = reinterpret_cast<float*>(ws + p.xd_off);
+  unsigned* rcnt = reinterpret_cast<unsigned*>(ws + p.rcnt_off);
   const T* t = static_cast<const T*>(tgt);
   const T* d = static_cast<const T*>(drf);
   hipLaunchKernelGGL((k_sweep<T, kAligned, TreeRows>), dim3(B * R, (nc + 3) / 4), dim3(kThreads), 0,
-                     st, t, d, tok, temp, TreeRows{shape}, B, V, nc, force_greedy, part, xd);
+                     st, t, d, tok, temp, TreeRows{shape}, B, V, nc, force_greedy, part, xd, rcnt);
   hipLaunchKernelGGL(k_tree_decide, dim3(B), dim3(kDecideThreads), 0, st, tok, uni, temp, shape, V, nc,
                      force_greedy, part, xd, rowstat, dec, state, out_tok, out_node, nacc, kv_len,
                      counters);
   const int rounds = force_greedy ? 0 : tree_rounds(shape, 0);
-  for (int r = 1; r <= rounds; ++r) {
-    hipLaunchKernelGGL((k_residual<T, kAligned>), dim3(B, ncr), dim3(kThreads), 0, st, t, d, temp, V,
-                       ncr, force_greedy, dec, csum, csub);
-    hipLaunchKernelGGL((k_tree_step<T>), dim3(B), dim3(kThreads), 0, st, t, d, tok, uni, temp, shape, V,
-                       ncr, force_greedy, r == rounds ? 1 : 0, rowstat, xd, csum, csub, dec, state,
-                       out_tok, out_node, nacc, kv_len, counters);
-  }
+  for (int r = 1; r <= rounds; ++r)
+    hipLaunchKernelGGL((k_tree_round<T, kAligned>), dim3(B, ncr), dim3(kThreads), 0, st, t, d, tok, uni,
+                       temp, shape, V, ncr, force_greedy, r == rounds ? 1 : 0, rowstat, xd, csum, csub,
+                       dec, state, rcnt, out_tok, out_node, nacc);
   if (rounds > 0)
     hipLaunchKernelGGL((k_tree_draw<T>), dim3(B), dim3(kThreads), 0, st, t, d, uni, temp, shape.n, V,
                        ncr, force_greedy, csum, csub, dec, out_tok, out_node, nacc, kv_len, counters);
