@@ -327,8 +327,19 @@ def main():
         vis = int(sum(int(l) * K1 + sum(depth) for l in kvl))
     attn_flops = 4 * cfg.D * cfg.Hq * vis
     attn_tflops = attn_flops / (attn_us * 1e-6) / 1e12
-    probe = None if args.no_probe else read_peak(sv)
+    # The sweep reads every target row and the draft rows of the nodes with
+    # children (all K draft rows of a chain); greedy reads target rows only.
+    # The exact passes after rejections come on top and are not counted.
+    n_draft_rows = K if parent is None else len(set(int(x) for x in parent[1:]))
+    rej_bytes = B * (K1 + (n_draft_rows if args.temp > 0 else 0)) * V * 2
+    probe = None if args.no_probe else read_peak(sv, sizes={"attn": attn_bytes,
+                                                            "reject": rej_bytes})
     measured_peak = None if probe is None else probe["gbs"]
+    same = {} if probe is None else probe["same_size"]
+
+    def vs_probe(name, us):
+        # Time of the probe over the call's bytes / time of the call.
+        return None if name not in same else round(same[name]["avg_us"] / us, 4)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": (_traffic() if parent is None and args.window == "none"
@@ -342,14 +353,10 @@ def main():
                 "measured_peak": measured_peak,
                 "frac_of_measured_peak": (None if not measured_peak
                                           else round(achieved / measured_peak, 4)),
+                "frac_of_same_size_probe": vs_probe("attn", attn_us),
                 "mfma": {"tflops": round(attn_tflops, 1), "algorithmic_flops": attn_flops,
                          "peak_tflops": PEAK_BF16_TFLOPS,
                          "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4)}}
-    # The sweep reads every target row and the draft rows of the nodes with
-    # children (all K draft rows of a chain); greedy reads target rows only.
-    # The exact passes after rejections come on top and are not counted.
-    n_draft_rows = K if parent is None else len(set(int(x) for x in parent[1:]))
-    rej_bytes = B * (K1 + (n_draft_rows if args.temp > 0 else 0)) * V * 2
     rej_us = float(rej_ms * 1e3)
     rej_gbs = rej_bytes / (rej_us * 1e-6) / 1e9
     # The rows the method itself needs: drafts after the first rejection are
@@ -397,7 +404,8 @@ def main():
                             "traffic": None,
                             "kernel": "spec_reject_sample%s call" % ("" if parent is None
                                                                      else "_tree"),
-                            "algorithmic_bytes": rej_bytes, "avg_us": round(rej_us, 2)},
+                            "algorithmic_bytes": rej_bytes, "avg_us": round(rej_us, 2),
+                            "frac_of_same_size_probe": vs_probe("reject", rej_us)},
         "read_probe": probe,
         "cpu_baseline": cpu,
         "kernels": {
@@ -407,6 +415,7 @@ def main():
                        "frac_hbm": round(rej_gbs / PEAK_HBM_GBS, 4), "bytes": rej_bytes,
                        "frac_of_measured_peak": (None if not measured_peak
                                                  else round(rej_gbs / measured_peak, 4)),
+                       "frac_of_same_size_probe": vs_probe("reject", rej_us),
                        "min_rows_bytes": rej_min_bytes,
                        "min_rows_per_seq": (None if min_rows is None
                                             else round(min_rows / B, 3)),
@@ -423,10 +432,12 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def read_peak(sv, mib=2048, reps=5):
+def read_peak(sv, mib=2048, reps=5, sizes=None):
     """Streaming-read bandwidth of this GPU: spec_read_probe over a 2 GiB
     buffer (8x the last-level cache), best of a few grid sizes, each timed
-    over ``reps`` back-to-back launches with HIP events on the launch stream."""
+    over ``reps`` back-to-back launches with HIP events on the launch stream;
+    then, per entry of ``sizes`` (name -> bytes), the probe over that many
+    bytes."""
     import torch
     buf = torch.zeros(mib << 20, dtype=torch.uint8, device="cuda:0")
     best = None
@@ -445,9 +456,44 @@ def read_peak(sv, mib=2048, reps=5):
         gbs = buf.numel() / (us * 1e-6) / 1e9
         if best is None or gbs > best["gbs"]:
             best = {"gbs": round(gbs, 1), "grid": grid, "bytes": buf.numel(), "avg_us": round(us, 1)}
+    best["kernel"] = "spec_read_probe (16-byte nontemporal loads, 8 KB per wave step)"
+    # The same probe over exactly the bytes of each timed call: short reads
+    # pay the launch ramp and drain too, so this is the ceiling a call of that
+    # size can reach.  Consecutive launches read consecutive windows of the
+    # buffer (2 GiB, 8x the last-level cache), so no window is still cached;
+    # timed like the calls, as one HIP graph of back-to-back launches.
+    best["same_size"] = {}
+    for name, nbytes in (sizes or {}).items():
+        n = (int(nbytes) + 8191) // 8192 * 8192
+        if n > buf.numel():
+            continue
+        launches = 16
+        span = buf.numel() - n
+        wins = [buf[(k * n) % (span + 1) // 8192 * 8192:][:n] for k in range(launches)]
+        res = None
+        for grid in (1024, 2048, 4096, 8192):
+            sink = torch.empty(grid, dtype=torch.int32, device="cuda:0")
+            g = torch.cuda.CUDAGraph()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                for w in wins:
+                    sv.read_probe(w, sink, grid)
+            g.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / launches
+            del g
+            if res is None or us < res["avg_us"]:
+                res = {"bytes": n, "grid": grid, "avg_us": round(us, 2),
+                       "gbs": round(n / (us * 1e-6) / 1e9, 1)}
+        best["same_size"][name] = res
     del buf
     torch.cuda.empty_cache()
-    best["kernel"] = "spec_read_probe (16-byte nontemporal loads, 8 KB per wave step)"
     return best
 
 

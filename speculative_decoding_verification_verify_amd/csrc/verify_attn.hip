@@ -179,6 +179,27 @@ __device__ __forceinline__ void store_k_window(const bf16x8 (&kf)[D / 16], const
 // time, and the pair with window keys takes those tokens' entries from there.
 constexpr int kWinRows = SV_MAX_K + 1;
 
+// Append mode: the V operand of a window pair, once the window entries are
+// in it, back into the pages: each lane's runs of 8 slots that hold a window
+// token, as whole 16-byte stores (the other slots of the run rewritten with
+// the values just read).  Stores of single 2-byte slots, one per value
+// coordinate and token, would each cost the memory a read-modify-write.
+template <int D>
+__device__ __forceinline__ void store_v_window(const bf16x8 (&vf)[2][D / 32], const int (&blk)[2],
+                                               uint16_t* __restrict__ vc, int K1, int Hkv, int g,
+                                               int L0, int pr, int l32, int hh) {
+#pragma unroll
+  for (int sg = 0; sg < 2; ++sg) {
+    const int i0 = pr * kPairKeys + sg * 16 + 8 * hh - L0;   // window index of the run's first slot
+    if (i0 + 8 > 0 && i0 < K1) {
+      uint16_t* vpage = vc + ((size_t)blk[sg] * Hkv + g) * ((size_t)D * 16);
+#pragma unroll
+      for (int j = 0; j < D / 32; ++j)
+        *reinterpret_cast<bf16x8*>(vpage + (32 * j + l32) * 16 + 8 * hh) = vf[sg][j];
+    }
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void window_v(bf16x8 (&vf)[2][D / 32], const uint16_t* s_win, int K1,
                                          int L0, int pr, int l32, int hh) {
@@ -348,7 +369,7 @@ struct Seg {
 // The window rows of segment s that lie in its pairs [p_lo, p_hi) (the rest
 // belong to another workgroup's share), as dwords (two d's of one row):
 // loaded by window_rows_load into registers, then written by
-// window_rows_store to the LDS stage and, in append mode, to the V cache.
+// window_rows_store to the LDS stage.
 template <int D, int NTH>
 struct WinStage {
   static constexpr int N = (kWinRows * D / 2 + NTH - 1) / NTH;   // dwords per thread
@@ -372,10 +393,7 @@ __device__ __forceinline__ void window_rows_load(typename WinStage<D, NTH>::Regs
 
 template <int D, int NTH>
 __device__ __forceinline__ void window_rows_store(const typename WinStage<D, NTH>::Regs& reg, const Seg& s,
-                                                  int K1, int Hkv, uint16_t* s_win,
-                                                  uint16_t* __restrict__ vc, bool store,
-                                                  const int32_t* __restrict__ bt, int mbps,
-                                                  int num_blocks, int tid) {
+                                                  int K1, uint16_t* s_win, int tid) {
   const int i_lo = max(0, s.p_lo * kPairKeys - s.L0), i_hi = min(K1, s.p_hi * kPairKeys - s.L0);
 #pragma unroll
   for (int r = 0; r < WinStage<D, NTH>::N; ++r) {
@@ -383,13 +401,6 @@ __device__ __forceinline__ void window_rows_store(const typename WinStage<D, NTH
     if (e < i_hi * (D / 2)) {
       const int i = e / (D / 2), d = 2 * (e - i * (D / 2));
       *reinterpret_cast<uint32_t*>(s_win + i * D + d) = reg[r];
-      if (store) {
-        const int p = s.L0 + i;
-        const int blk = clampi(bt[(size_t)s.b * mbps + min(p >> 4, mbps - 1)], 0, num_blocks - 1);
-        uint16_t* vpage = vc + ((size_t)blk * Hkv + s.g) * ((size_t)D * 16) + (p & 15);
-        vpage[d * 16] = (uint16_t)(reg[r] & 0xffffu);
-        vpage[(d + 1) * 16] = (uint16_t)(reg[r] >> 16);
-      }
     }
   }
 }
@@ -555,14 +566,13 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
   // First K/V as early as possible: page table, then the pages, then Q.
   bf16x8 kf[KK];
   bf16x8 vf[2][DT];
+  // (A pair with window keys taken from k_new / v_new is loaded by the loop
+  // that runs it.)
   int pr = cur.p_lo + wave;
-  if (pr < cur.p_hi) {
+  if (pr < cur.p_hi && !(WIN && pair_has_window(pr, cur.L0, K1))) {
     int blk[2];
     pair_blocks(blk, pr, bt + (size_t)cur.b * mbps, mbps, num_blocks);
-    if (WIN && pair_has_window(pr, cur.L0, K1))
-      load_k_window<D>(kf, blk, kc, kn, cur.b, K1, Hkv, cur.g, cur.L0, pr, k_page, k_tok, hh);
-    else
-      load_k<D>(kf, blk, kc, Hkv, cur.g, k_page, k_tok, hh);
+    load_k<D>(kf, blk, kc, Hkv, cur.g, k_page, k_tok, hh);
     load_v<D>(vf, blk, vc, Hkv, cur.g, l32, hh);
   }
   bf16x8 qf[NT][KK];
@@ -572,20 +582,18 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
   if (WIN) {
     uint32_t stg[WinStage<D, kStreamThreads>::N];
     window_rows_load<D, kStreamThreads>(stg, cur, K1, Hkv, vn, tid);
-    window_rows_store<D, kStreamThreads>(stg, cur, K1, Hkv, s_win[0], vc, store_win != 0, bt, mbps,
-                                         num_blocks, tid);
+    window_rows_store<D, kStreamThreads>(stg, cur, K1, s_win[0], tid);
   }
   __syncthreads();
 
   while (true) {
     Seg nxt;
     const bool has_next = next_segment(cur, nxt, u1, B, Hkv, K1, np_cap, kv_len);
-    // The next segment's window rows: requested now, staged before this
-    // segment's merge (whose barrier orders them before their use).
-    uint32_t stg[WinStage<D, kStreamThreads>::N];
-    if (WIN && has_next) window_rows_load<D, kStreamThreads>(stg, nxt, K1, Hkv, vn, tid);
     const int nxt_first = nxt.p_lo + wave;        // this wave's first pair of nxt
     const bool nxt_mine = has_next && nxt_first < nxt.p_hi;
+    // ... and whether that pair holds window keys from k_new / v_new: then
+    // it is not prefetched here.
+    const bool nxt_win = WIN && nxt_mine && pair_has_window(nxt_first, nxt.L0, K1);
 
     f32x16 o[NT][DT];
     float m_run[NT], l_run[NT];
@@ -603,13 +611,18 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
     // is requested right after this pair's scores and its V right after P.V.
     // After the last pair of the segment, the "next pair" is this wave's
     // first pair of the next segment, so its loads fly during the merge.
+    // With the window taken from k_new / v_new, the pairs that hold window
+    // keys (from L0 / 32 on: the last one or two of the sequence) run after
+    // the others in a loop of their own that also makes their loads, so the
+    // main loop keeps the plain kernel's register budget.
     const int32_t* btb = bt + (size_t)cur.b * mbps;
     const int L = cur.L0 + K1;
+    const int p_main = WIN ? min(cur.p_hi, max(cur.p_lo, cur.L0 / kPairKeys)) : cur.p_hi;
     bool prefetched = false;
-    while (pr < cur.p_hi) {
+    while (pr < p_main) {
       const int nx = pr + NW;
-      const bool in_seg = nx < cur.p_hi;
-      const bool cross = !in_seg && nxt_mine;
+      const bool in_seg = nx < p_main;
+      const bool cross = !in_seg && nx >= cur.p_hi && nxt_mine && !nxt_win;
       int nblk[2] = {0, 0};
       if (in_seg) pair_blocks(nblk, nx, btb, mbps, num_blocks);
       else if (cross) pair_blocks(nblk, nxt_first, bt + (size_t)nxt.b * mbps, mbps, num_blocks);
@@ -618,40 +631,51 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         score_pair<D, NT>(kf, pr, hh, nt, qf, am, cur.L0, sl2, o, m_run, l_run, pf[nt]);
-      const bool win_here = WIN && pair_has_window(pr, cur.L0, K1);
-      int cblk[2] = {0, 0};                        // pages of this pair (window pairs only)
-      if (WIN && win_here) pair_blocks(cblk, pr, btb, mbps, num_blocks);
-      if (WIN && win_here && store_win)
-        store_k_window<D>(kf, cblk, kc, K1, Hkv, cur.g, cur.L0, pr, k_page, k_tok, hh);
-      if (in_seg || cross) {
-        const int npr = cross ? nxt_first : nx;
-        const int nb_ = cross ? nxt.b : cur.b, nl0 = cross ? nxt.L0 : cur.L0;
-        if (WIN && pair_has_window(npr, nl0, K1))
-          load_k_window<D>(kf, nblk, kc, kn, nb_, K1, Hkv, ng, nl0, npr, k_page, k_tok, hh);
-        else
-          load_k<D>(kf, nblk, kc, Hkv, ng, k_page, k_tok, hh);
-      }
-      if (WIN && win_here) window_v<D>(vf, s_win[wbuf], K1, cur.L0, pr, l32, hh);
+      if (in_seg || cross) load_k<D>(kf, nblk, kc, Hkv, ng, k_page, k_tok, hh);
       mask_v_tail<D>(vf, pr, L, hh);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) pv_pair<D, NT>(vf, nt, pf[nt], o);
       if (in_seg || cross) load_v<D>(vf, nblk, vc, Hkv, ng, l32, hh);
       prefetched |= cross;
-      pr = in_seg ? nx : cur.p_hi;
+      pr = (in_seg || nx < cur.p_hi) ? nx : cur.p_hi;
     }
-    if (nxt_mine && !prefetched) {                 // no pair of mine in cur
+    if (WIN) {
+      // This wave's window pairs, each loaded here: K from k_new for the
+      // window keys (stored into the cache in append mode), V from the
+      // staged rows.
+      for (; pr < cur.p_hi; pr += NW) {
+        int blk[2];
+        pair_blocks(blk, pr, btb, mbps, num_blocks);
+        load_k_window<D>(kf, blk, kc, kn, cur.b, K1, Hkv, cur.g, cur.L0, pr, k_page, k_tok, hh);
+        load_v<D>(vf, blk, vc, Hkv, cur.g, l32, hh);
+        bf16x8 pf[NT][2];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          score_pair<D, NT>(kf, pr, hh, nt, qf, am, cur.L0, sl2, o, m_run, l_run, pf[nt]);
+        if (store_win) store_k_window<D>(kf, blk, kc, K1, Hkv, cur.g, cur.L0, pr, k_page, k_tok, hh);
+        window_v<D>(vf, s_win[wbuf], K1, cur.L0, pr, l32, hh);
+        if (store_win) store_v_window<D>(vf, blk, vc, K1, Hkv, cur.g, cur.L0, pr, l32, hh);
+        mask_v_tail<D>(vf, pr, L, hh);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) pv_pair<D, NT>(vf, nt, pf[nt], o);
+      }
+    }
+    if (nxt_mine && !prefetched && !nxt_win) {     // no pair of mine in cur
       int nblk[2];
       pair_blocks(nblk, nxt_first, bt + (size_t)nxt.b * mbps, mbps, num_blocks);
-      if (WIN && pair_has_window(nxt_first, nxt.L0, K1))
-        load_k_window<D>(kf, nblk, kc, kn, nxt.b, K1, Hkv, nxt.g, nxt.L0, nxt_first, k_page, k_tok, hh);
-      else
-        load_k<D>(kf, nblk, kc, Hkv, nxt.g, k_page, k_tok, hh);
+      load_k<D>(kf, nblk, kc, Hkv, nxt.g, k_page, k_tok, hh);
       load_v<D>(vf, nblk, vc, Hkv, nxt.g, l32, hh);
     }
 
-    if (WIN && has_next)
-      window_rows_store<D, kStreamThreads>(stg, nxt, K1, Hkv, s_win[wbuf ^ 1], vc, store_win != 0, bt,
-                                           mbps, num_blocks, tid);
+    // The next segment's window rows, staged before this segment's merge
+    // (whose barrier orders them before their use).  Requested only after
+    // the pair loop: held across it, they would push the loop past the
+    // register budget.
+    if (WIN && has_next) {
+      uint32_t stg[WinStage<D, kStreamThreads>::N];
+      window_rows_load<D, kStreamThreads>(stg, nxt, K1, Hkv, vn, tid);
+      window_rows_store<D, kStreamThreads>(stg, nxt, K1, s_win[wbuf ^ 1], tid);
+    }
 
     // Merge the 4 waves one 32-row tile at a time: each wave stores its O,
     // rescaled to the common row max, in its own LDS buffer; the sum over
