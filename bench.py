@@ -85,6 +85,11 @@ def parse():
     p.add_argument("--peak-probe", action="store_true",
                    help="instead of the bench: time the streaming-read probe (spec_read_probe) "
                         "over a 2 GiB buffer and print its bandwidth, then exit")
+    p.add_argument("--k-layout-ab", default="", metavar="LIB",
+                   help="instead of the bench: time spec_verify_attn with the in-tree library "
+                        "(K pages [D/8,16,8]) against LIB, a build with SV_K_TOKEN_MAJOR=1 "
+                        "(token-major K pages [16,D]) given the same cache permuted; the "
+                        "outputs must agree bit for bit")
     p.add_argument("--no-probe", action="store_true",
                    help="skip the streaming-read probe in the bench line (measured_peak null)")
     p.add_argument("--sets", type=int, default=3, help="rotating logit sets")
@@ -128,6 +133,9 @@ def main():
         return
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.k_layout_ab:
+        k_layout_ab(args, args.k_layout_ab)
+        return
     cfg = CONFIGS[args.config]
     B, K, V = (args.batch or cfg.B), cfg.K, cfg.V
     parent = None
@@ -495,6 +503,64 @@ def read_peak(sv, mib=2048, reps=5, sizes=None):
     del buf
     torch.cuda.empty_cache()
     return best
+
+
+def k_layout_ab(args, other_lib):
+    """Attention call time with each K page layout, same inputs: the in-tree
+    library reads [D/8, 16, 8] pages, ``other_lib`` (built with
+    SV_K_TOKEN_MAJOR=1) reads the same cache permuted to token-major
+    [16, D].  Each timed as a graph of ``args.steps`` calls, twice in
+    alternation; one JSON line."""
+    import torch
+    import speculative_decoding_verification_verify_amd as sv
+    from synth import CONFIGS
+    from synth.device import from_device, make_attn_inputs_device
+    cfg = CONFIGS[args.config]
+    B, K = (args.batch or cfg.B), cfg.K
+    dev = "cuda:0"
+    attn = make_attn_inputs_device(args.seed, B, K, cfg.Hq, cfg.Hkv, cfg.D, cfg.ctx, dev)
+    kv0 = attn["kv_len"]
+    max_kv = int(from_device(kv0).max())
+    kc = attn["k_cache"]
+    kc_tok = kc.permute(0, 1, 3, 2, 4).contiguous().view(kc.shape)   # [NB, Hkv, 16, D] bytes
+    out = torch.empty_like(attn["q"])
+    libs = (("chunked [D/8,16,8]", sv.lib_path(), kc), ("token-major [16,D]", other_lib, kc_tok))
+    ref, times = None, {}
+    for _ in range(2):
+        for name, path, k in libs:
+            sv._LIB = None
+            sv.lib_path = (lambda p=path: p)
+            sv.load()
+            ws = torch.empty(max(256, sv.verify_attn_workspace_bytes(B, K, cfg.Hq, cfg.Hkv, cfg.D,
+                                                                      max_kv)),
+                             dtype=torch.uint8, device=dev)
+
+            def call():
+                sv.verify_attn(attn["q"], k, attn["v_cache"], attn["block_table"], kv0, out=out,
+                               max_kv_len=max_kv, workspace=ws)
+            call()
+            torch.cuda.synchronize()
+            o = from_device(out)
+            if ref is None:
+                ref = o
+            elif not np.array_equal(o, ref):
+                raise SystemExit("k-layout A/B: outputs differ between the layouts")
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(args.steps):
+                    call()
+            g.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times.setdefault(name, []).append(round(e0.elapsed_time(e1) * 1e3 / args.steps, 2))
+            del g
+    print(json.dumps({"k_layout_ab": {"workload": cfg.name, "B": B, "K": K,
+                                      "call_us": times, "outputs_identical": True}}), flush=True)
 
 
 def copy_calibration(mib):

@@ -36,20 +36,32 @@ def sources():
     return srcs
 
 
-def build(verbose=False):
+def build(verbose=False, out=None, defines=()):
+    """Compile the library to ``out`` (default: the in-tree library).
+    ``defines``: extra NAME=VALUE macros, for measurement builds only (the
+    in-tree library is always built without them)."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"),
+    dst = out or LIB_PATH
+    tmp = dst + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, *["-D" + d for d in defines], "-I", os.path.join(ROOT, "include"),
            "-I", os.path.join(HERE, "csrc"), *sources(), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building %s" % LIB_NAME)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+        raise RuntimeError("hipcc failed building %s" % dst)
+    os.replace(tmp, dst)
+    return dst
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import argparse
+    ap = argparse.ArgumentParser(description="build libspecverify.so for gfx950")
+    ap.add_argument("--out", default=None, help="output path (default: the in-tree library)")
+    ap.add_argument("--define", action="append", default=[], metavar="NAME=VALUE",
+                    help="extra macro for a measurement build, e.g. SV_K_TOKEN_MAJOR=1")
+    a = ap.parse_args()
+    if a.define and not a.out:
+        ap.error("a build with --define needs --out: the in-tree library stays the plain build")
+    print(build(verbose=True, out=a.out, defines=a.define))

@@ -90,6 +90,17 @@ __device__ __forceinline__ void pair_blocks(int (&blk)[2], int pr, const int32_t
   blk[1] = clampi(e1, 0, num_blocks - 1);
 }
 
+// K page layout [D/8][16][8]: chunk c (8 coordinates) of the 16 tokens is
+// 256 contiguous bytes, so each load of a wave reads four whole 256-byte
+// runs.  A measurement build with SV_K_TOKEN_MAJOR=1 reads token-major pages
+// [16][D] instead through the same lanes (each load then touches 32 rows
+// of 256 bytes, 32 bytes of each): it serves only to time the two layouts
+// against each other, through spec_verify_attn (its window and commit
+// paths still write the default layout).
+#ifndef SV_K_TOKEN_MAJOR
+#define SV_K_TOKEN_MAJOR 0
+#endif
+
 // K operand of a page pair: lane holds key k_tok of page k_page, chunks 2kk+hh.
 template <int D>
 __device__ __forceinline__ void load_k(bf16x8 (&kf)[D / 16], const int (&blk)[2],
@@ -97,7 +108,9 @@ __device__ __forceinline__ void load_k(bf16x8 (&kf)[D / 16], const int (&blk)[2]
                                        int k_tok, int hh) {
   const uint16_t* kpage = kc + ((size_t)(k_page ? blk[1] : blk[0]) * Hkv + g) * ((size_t)D * 16);
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) kf[kk] = load_kv(kpage + ((2 * kk + hh) * 16 + k_tok) * 8);
+  for (int kk = 0; kk < D / 16; ++kk)
+    kf[kk] = load_kv(kpage + (SV_K_TOKEN_MAJOR ? k_tok * D + (2 * kk + hh) * 8
+                                               : ((2 * kk + hh) * 16 + k_tok) * 8));
 }
 
 // V operand of a page pair: lane holds tokens 8hh..8hh+7 of value coordinate 32j + l32.

@@ -157,11 +157,13 @@ def test_ragged_vocab(gpu_lib, dev, V, dtype):
         _case(gpu_lib, dev, 800 + V, 6, 3, V, dtype=dtype, sigma=0.8, temp=temp)
 
 
-@pytest.mark.parametrize("V", [600_000, 2_200_000])
+@pytest.mark.parametrize("V", [524_288, 600_000, 2_200_000])
 @pytest.mark.parametrize("sigma", [0.25, 1.05])
 def test_large_vocab(gpu_lib, dev, V, sigma):
-    # More than 64 residual chunks (the chunk scan spans several wave
-    # segments) and, at 2.2M, more than 256 (chunk sums read in place).
+    # 2^19 entries: 64 residual chunks, the most whose sums one wave holds
+    # (the draw is made in the pass kernel); past it the draw is a kernel of
+    # its own, the chunk scan spans several wave segments and, at 2.2M, more
+    # than 256 chunks (chunk sums read in place).
     # sigma 0.25 accepts nearly every draft, so the bonus row is drawn too.
     _case(gpu_lib, dev, 950 + V // 100_000, 3, 2, V, sigma=sigma, temp=1.0)
 

@@ -148,6 +148,13 @@ def test_ragged_vocab(gpu_lib, dev, V, dtype):
     _case(gpu_lib, dev, 91, 32, tree_parents((2, 2)), V, dtype=dtype, sigma=1.5)
 
 
+@pytest.mark.parametrize("V", [524288, 700001])
+def test_large_vocab(gpu_lib, dev, V):
+    """64 and 86 chunks of 8192 entries: the round's step reads every chunk's
+    sums in one wave at 2^19 entries, in two wave segments past it."""
+    _case(gpu_lib, dev, 95, 6, tree_parents((2, 2)), V, sigma=1.5)
+
+
 def test_llama8b_vocab_tree_sampled(gpu_lib, dev):
     # 64 sequences over the full 128256-entry vocabulary with a [2,2,2] tree;
     # the oracle checks every 4th sequence.
