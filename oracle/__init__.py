@@ -22,7 +22,8 @@ kv         -- the window's K/V in the paged cache (append, commit) and the
               host page pool.
 bandit     -- the epsilon-greedy draft-length controller and the
               per-position acceptance statistics.
-filter     -- top-k / top-p filtering of both laws before the verifier.
+filter     -- top-k / top-p filtering of both laws before the verifier
+              (chain and tree).
 
 Sources (the pages the method is taken from):
   [AIE]  AI Engineering from Scratch, lesson "Speculative decoding and

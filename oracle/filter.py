@@ -33,8 +33,10 @@ exact ones, so it can differ only inside that band.
 import numpy as np
 
 from .reject import widen, reject_sample
+from .tree import children_of, reject_sample_tree
 
-__all__ = ["filter_mask", "filtered_logits", "reject_sample_filtered"]
+__all__ = ["filter_mask", "filtered_logits", "reject_sample_filtered",
+           "reject_sample_tree_filtered"]
 
 
 def filter_mask(logits, temperature, top_k=0, top_p=1.0, eps_filter=1e-6):
@@ -102,5 +104,48 @@ def reject_sample_filtered(target_logits, draft_logits, draft_tokens, uniforms, 
             f = f or fd.any()
         f3[b] = f
     res = reject_sample(tf, df, draft_tokens, uniforms, temperature, eps_accept, eps_sample)
+    res["flag_filter"] = f3
+    return res
+
+
+def reject_sample_tree_filtered(target_logits, draft_logits, parent, tokens, uniforms, temperature,
+                                top_k, top_p, eps_accept=1e-5, eps_sample=1e-10, eps_filter=1e-6):
+    """reject_sample_tree on the filtered laws.  top_k [B] int, top_p [B] float.
+
+    The same reading as the chain's: every target row q_v, and the draft row
+    p_v of every node with children (the law its children were drawn from),
+    is filtered with the sequence's (top_k, top_p); the tree walk then runs
+    unchanged on q', p' ([QS] "Influence du sampling" with the verifier of
+    [TC] "Grading every branch in one pass").  Draft rows of leaves are never
+    used and stay as given.  Returns reject_sample_tree's dict plus
+    flag_filter [B] (F3 on any of the rows filtered).  Greedy sequences are
+    unaffected.
+    """
+    tl = widen(target_logits)
+    b_sz, n, v = tl.shape
+    par = np.asarray(parent, dtype=np.int64)
+    if par.ndim == 1:
+        par = np.broadcast_to(par, (b_sz, n))
+    t = np.asarray(temperature, dtype=np.float64).reshape(b_sz)
+    tk = np.broadcast_to(np.asarray(top_k, dtype=np.int64), (b_sz,))
+    tp = np.broadcast_to(np.asarray(top_p, dtype=np.float64), (b_sz,))
+    dl = None if draft_logits is None else widen(draft_logits).reshape(b_sz, n, v)
+    tf = tl.copy()
+    df = None if dl is None else dl.copy()
+    f3 = np.zeros(b_sz, dtype=bool)
+    for b in range(b_sz):
+        if t[b] <= 0:
+            continue
+        tf[b], ft = filtered_logits(tl[b], t[b], tk[b], tp[b], eps_filter)
+        f = ft.any()
+        if df is not None:
+            kids = children_of(par[b])
+            inner = [u for u in range(n) if kids[u]]
+            if inner:
+                rows, fd = filtered_logits(dl[b, inner], t[b], tk[b], tp[b], eps_filter)
+                df[b, inner] = rows
+                f = f or fd.any()
+        f3[b] = f
+    res = reject_sample_tree(tf, df, parent, tokens, uniforms, temperature, eps_accept, eps_sample)
     res["flag_filter"] = f3
     return res
