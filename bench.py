@@ -99,7 +99,8 @@ def parse():
                         "(append) or committed afterwards by spec_kv_commit (scratch); or a "
                         "separate copy pass before the plain attention (separate)")
     p.add_argument("--top-k", type=int, default=0,
-                   help="top-k filter for every sequence (spec_reject_sample_filtered; 0: off)")
+                   help="top-k filter for every sequence (spec_reject_sample_filtered, or "
+                        "spec_reject_sample_tree_filtered with --tree; 0: off)")
     p.add_argument("--top-p", type=float, default=1.0,
                    help="top-p filter for every sequence (1: off)")
     p.add_argument("--tree", default="", metavar="SHAPE",
@@ -227,7 +228,8 @@ def main():
             sv.reject_sample_tree(r["target"], r["draft"], parent, r["tokens"], r["uniforms"],
                                   r["temperature"], kv, out_tokens=out_tok[s % args.sets],
                                   out_nodes=out_node[s % args.sets],
-                                  num_accepted=n_acc[s % args.sets], workspace=rej_ws)
+                                  num_accepted=n_acc[s % args.sets], workspace=rej_ws,
+                                  top_k=filt_k, top_p=filt_p)
 
     def commit_call(s, kv):
         # Scratch window: the surviving rows into the cache; a tree appended in

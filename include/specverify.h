@@ -353,6 +353,35 @@ int spec_reject_sample_tree(const void* target_logits, const void* draft_logits,
 size_t spec_reject_sample_tree_workspace_bytes(int B, int N, int V);
 
 /*
+ * spec_reject_sample_tree_filtered -- spec_reject_sample_tree with top-k /
+ * top-p filtering of the laws before the walk (quickscale.ai, "Quand et
+ * pourquoi utiliser le speculative decoding", "Influence du sampling", with
+ * the tree verifier of thakicloud, "Grading every branch in one pass").
+ *
+ * The filters of spec_reject_sample_filtered, with the sequence's own
+ * (top_k[b], top_p[b]), on every target row q_v and on the draft row p_v of
+ * every node with children (leaf draft rows are never read); the walk then
+ * runs unchanged on the filtered laws q', p': a child whose token is outside
+ * p'_v's kept set passes (p'(d) = 0), one outside q'_v's set fails unless it
+ * also is outside p'_v's, the sibling residuals are (q' - p')_+ and the final
+ * draw is from the filtered law.  Greedy sequences are unaffected.
+ *
+ * top_k [B] int32, top_p [B] float32 device arrays; either may be NULL (off
+ * for every sequence).  The same top-p boundary band as the chain call.
+ * Everything else, including the workspace
+ * (spec_reject_sample_tree_workspace_bytes), is as for spec_reject_sample_tree.
+ */
+int spec_reject_sample_tree_filtered(const void* target_logits, const void* draft_logits,
+                                     const int32_t* parent, const int32_t* tokens,
+                                     const float* uniforms, const float* temperature,
+                                     const int32_t* top_k, const float* top_p,
+                                     int32_t* out_tokens, int32_t* out_nodes,
+                                     int32_t* num_accepted, int32_t* kv_len,
+                                     unsigned long long* counters, int B, int N, int V,
+                                     int dtype, void* workspace, size_t workspace_bytes,
+                                     void* hip_stream);
+
+/*
  * spec_kv_commit -- after the verifier, the surviving window rows' K/V into
  * their committed positions (AI Engineering from Scratch, "Speculative
  * decoding and EAGLE-3", "Rolling back the KV cache": a scratch buffer

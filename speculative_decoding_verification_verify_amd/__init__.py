@@ -42,6 +42,7 @@ EXPORTS = ("spec_verify_attn", "spec_verify_attn_workspace_bytes", "spec_verify_
            "spec_verify_attn_window", "spec_kv_commit",
            "spec_reject_sample", "spec_reject_sample_workspace_bytes", "spec_reject_sample_noalloc",
            "spec_reject_sample_filtered", "spec_reject_sample_tree", "spec_reject_sample_tree_workspace_bytes",
+           "spec_reject_sample_tree_filtered",
            "spec_pages_create", "spec_pages_destroy", "spec_pages_reserve", "spec_pages_commit",
            "spec_pages_release", "spec_pages_free_count", "spec_pages_seq_blocks",
            "spec_pages_block_table", "spec_pages_check",
@@ -93,6 +94,9 @@ def load():
     lib.spec_reject_sample_tree.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
                                             i32, i32, vp, sz, vp]
     lib.spec_reject_sample_tree.restype = i32
+    lib.spec_reject_sample_tree_filtered.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                     vp, i32, i32, i32, i32, vp, sz, vp]
+    lib.spec_reject_sample_tree_filtered.restype = i32
     lib.spec_reject_sample_tree_workspace_bytes.argtypes = [i32, i32, i32]
     lib.spec_reject_sample_tree_workspace_bytes.restype = sz
     lib.spec_verify_attn_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
@@ -431,8 +435,10 @@ def reject_sample_noalloc(target, draft, draft_tokens, uniforms, temperature, kv
 
 def reject_sample_tree(target, draft, parent, tokens, uniforms, temperature, kv_len,
                        out_tokens=None, out_nodes=None, num_accepted=None, counters=None,
-                       workspace=None, stream=None):
-    """Lossless verifier over a draft tree + KV commit (see ``spec_reject_sample_tree``).
+                       workspace=None, stream=None, top_k=None, top_p=None):
+    """Lossless verifier over a draft tree + KV commit (see ``spec_reject_sample_tree``);
+    with top_k [B] int32 and / or top_p [B] float32, on the filtered laws
+    (see ``spec_reject_sample_tree_filtered``).
 
     target [B, N, V], draft [B, N, V] or None (greedy for every sequence);
     parent: N host integers (parent[0] = -1, parent[i] < i), shared by the
@@ -461,12 +467,16 @@ def reject_sample_tree(target, draft, parent, tokens, uniforms, temperature, kv_
         _need(num_accepted, "num_accepted", torch.int32, (B,))
     if counters is not None:
         _need(counters, "counters", torch.int64, (2,))
+    if top_k is not None:
+        _need(top_k, "top_k", torch.int32, (B,))
+    if top_p is not None:
+        _need(top_p, "top_p", torch.float32, (B,))
     par = [int(x) for x in parent]
     if len(par) != N:
         raise ValueError("parent must have N = %d entries" % N)
     _on_gpu(target=target, draft=draft, tokens=tokens, uniforms=uniforms,
             temperature=temperature, kv_len=kv_len, out_tokens=out_tokens, out_nodes=out_nodes,
-            num_accepted=num_accepted, counters=counters)
+            num_accepted=num_accepted, counters=counters, top_k=top_k, top_p=top_p)
     c_par = (ctypes.c_int32 * N)(*par)
     out_tokens, num_accepted = _reject_outputs(B, N, target.device, out_tokens, num_accepted,
                                                counters)
@@ -474,6 +484,14 @@ def reject_sample_tree(target, draft, parent, tokens, uniforms, temperature, kv_
         out_nodes = torch.empty((B, N), dtype=torch.int32, device=target.device)
     ws_bytes = reject_sample_tree_workspace_bytes(B, N, V)
     workspace, ws_have = _workspace(workspace, ws_bytes, target.device)
+    if top_k is not None or top_p is not None:
+        st = lib.spec_reject_sample_tree_filtered(
+            _ptr(target), _ptr(draft), ctypes.cast(c_par, ctypes.c_void_p), _ptr(tokens),
+            _ptr(uniforms), _ptr(temperature), _ptr(top_k), _ptr(top_p), _ptr(out_tokens),
+            _ptr(out_nodes), _ptr(num_accepted), _ptr(kv_len), _ptr(counters), B, N, V, dt,
+            _ptr(workspace), ws_have, _stream(stream))
+        _check("spec_reject_sample_tree_filtered", st)
+        return out_tokens, out_nodes, num_accepted
     st = lib.spec_reject_sample_tree(_ptr(target), _ptr(draft), ctypes.cast(c_par, ctypes.c_void_p),
                                      _ptr(tokens), _ptr(uniforms), _ptr(temperature),
                                      _ptr(out_tokens), _ptr(out_nodes), _ptr(num_accepted),

@@ -530,8 +530,9 @@ __device__ __forceinline__ void emit_own(int b, int K, int n, int tok, int my_dr
 }
 
 // ---------------------------------------------------------------------------
-// k_filter: grid (B * (2K+1)), block 512 (two per CU): the top-k / top-p thresholds of one
-// row by radix selection over its order keys, most significant digit first:
+// k_filter: grid (B * rows.count()), block 512 (two per CU): the top-k / top-p thresholds
+// of one row (the sweep's row set and order) by radix selection over its order keys,
+// most significant digit first:
 // 12 bits, then 4 (bf16) or 12 and 8 (fp32).  Each pass histograms the
 // entries that match the digits chosen so far into up to 4096 bins of counts
 // (top-k) or masses (top-p), and the block picks the bin where the running
@@ -868,10 +869,10 @@ __device__ __forceinline__ unsigned long long filter_kept_mass(const T* __restri
   return tot;
 }
 
-template <typename T, bool kAligned>
+template <typename T, bool kAligned, class Rows>
 __global__ __launch_bounds__(kFilterThreads, 4) void k_filter(
     const T* __restrict__ tgt, const T* __restrict__ drf, const float* __restrict__ temp,
-    const int32_t* __restrict__ top_k, const float* __restrict__ top_p, int K, int V, int nc,
+    const int32_t* __restrict__ top_k, const float* __restrict__ top_p, Rows rows, int V, int nc,
     int force_greedy, const float2* __restrict__ part, RowFilter* __restrict__ filt) {
   __shared__ unsigned long long h[kFilterBins];
   __shared__ unsigned long long s_w[kFilterWaves];
@@ -881,7 +882,7 @@ __global__ __launch_bounds__(kFilterThreads, 4) void k_filter(
   __shared__ unsigned long long hx[kWinBins * 16];   // single values of the window's bins
   __shared__ unsigned long long hm[kFilterBins];      // top-k alone: masses per first-digit bin
   __shared__ float s_xr;
-  const int R = 2 * K + 1;
+  const int R = rows.count();
   const int row = blockIdx.x;
   const int b = row / R;
   const int j = row - b * R;
@@ -895,8 +896,7 @@ __global__ __launch_bounds__(kFilterThreads, 4) void k_filter(
     if (tid == 0) filt[row] = RowFilter{0u, 0u, 0.0};
     return;
   }
-  const T* src = (j <= K) ? tgt + ((size_t)b * (K + 1) + j) * (size_t)V
-                          : drf + ((size_t)b * K + (j - K - 1)) * (size_t)V;
+  const T* src = (rows.is_draft(j) ? drf : tgt) + rows.row(b, j) * (size_t)V;
   const float c = kLog2e / t;
   // The row's raw maximum, merged from the sweep's chunk maxima as the decision does.
   if (wave == 0) {
@@ -1747,8 +1747,8 @@ __device__ __forceinline__ void emit_tree(int b, int N, int n, int tok, int32_t*
 // (raw max, sum) of swept row r; xd, tok and uni are this sequence's recorded
 // logits [N][2], tokens [N] and uniforms [N], staged in LDS.
 template <class RS>
-__device__ void tree_walk(int b, int v, int n, const TreeShape& s, RS rs, const float* xd,
-                          const int* tok, const float* uni, float c, double cd,
+__device__ void tree_walk(int b, int v, int n, const TreeShape& s, RS rs, const uint32_t* km,
+                          const float* xd, const int* tok, const float* uni, float c, double cd,
                           int32_t* __restrict__ out_tok, int32_t* __restrict__ out_node,
                           Decision& dd, TreeState& st) {
   const int N = s.n;
@@ -1756,7 +1756,7 @@ __device__ void tree_walk(int b, int v, int n, const TreeShape& s, RS rs, const 
     const int k0 = s.kid_off[v], k1 = s.kid_off[v + 1];
     const float2 rq = rs(v);
     if (k0 == k1) {
-      dd = Decision{kModeQ, n, b * N + v, 0, rq.x, 0.f, 0.0, 0.0, 0.0};
+      dd = Decision{kModeQ, n, b * N + v, 0, rq.x, 0.f, 0.0, 0.0, 0.0, km[v], 0u};
       st = TreeState{v, 0, n, 1, 1.0};
       return;
     }
@@ -1783,7 +1783,8 @@ __device__ void tree_walk(int b, int v, int n, const TreeShape& s, RS rs, const 
     // Sweep normalisers moved to the exact pass's frame, for its q > p split.
     const double sq = (double)rq.y * exp2((double)(rq.x * c) - (double)rq.x * cd);
     const double sp = (double)rp.y * exp2((double)(rp.x * c) - (double)rp.x * cd);
-    dd = Decision{kModeResid, n, b * N + v, b * N + v, rq.x, rp.x, log2(sq) - log2(sp), 1.0, 0.0};
+    dd = Decision{kModeResid, n, b * N + v, b * N + v, rq.x, rp.x, log2(sq) - log2(sp), 1.0, 0.0,
+                  km[v], km[N + s.int_idx[v]]};
     st = TreeState{v, 1, n, (k1 - k0 == 1) ? 1 : 0, 1.0};
     return;
   }
@@ -1797,11 +1798,13 @@ __device__ void tree_walk(int b, int v, int n, const TreeShape& s, RS rs, const 
 __global__ __launch_bounds__(kDecideThreads) void k_tree_decide(
     const int32_t* __restrict__ tok, const float* __restrict__ uni, const float* __restrict__ temp,
     TreeShape s, int V, int nc, int force_greedy, const float2* __restrict__ part,
-    const float* __restrict__ xd, float2* __restrict__ rowstat, Decision* __restrict__ dec,
-    TreeState* __restrict__ state, int32_t* __restrict__ out_tok, int32_t* __restrict__ out_node,
-    int32_t* __restrict__ nacc, int32_t* __restrict__ kv_len, unsigned long long* counters) {
+    const RowFilter* __restrict__ filt, int key16, float* __restrict__ xd,
+    float2* __restrict__ rowstat, Decision* __restrict__ dec, TreeState* __restrict__ state,
+    int32_t* __restrict__ out_tok, int32_t* __restrict__ out_node, int32_t* __restrict__ nacc,
+    int32_t* __restrict__ kv_len, unsigned long long* counters) {
   __shared__ float2 s_rs[2 * kMaxTree];
   __shared__ float s_xd[2 * kMaxTree], s_u[kMaxTree];
+  __shared__ uint32_t s_km[2 * kMaxTree];
   __shared__ int s_tk[kMaxTree];
   __shared__ int s_n, s_tok;
   const int b = blockIdx.x;
@@ -1820,11 +1823,33 @@ __global__ __launch_bounds__(kDecideThreads) void k_tree_decide(
   if (!greedy && tid < 2 * N) s_xd[tid] = xd[(size_t)b * N * 2 + tid];
   for (int r0 = 0; r0 < rows; r0 += kDecideThreads / 16) {
     const int r = r0 + (tid >> 4);
+    const bool head = (tid & 15) == 0 && r < rows;
+    // A filtered row: its law is renormalised over the kept set.
+    const RowFilter rf = (filt && !greedy && head) ? filt[(size_t)b * R + r] : RowFilter{0u, 0u, 0.0};
     float a, bb;
     merge_row16(pb + (size_t)min(r, rows - 1) * nc, nc, greedy, c, tid & 15, a, bb);
-    if ((tid & 15) == 0 && r < rows) s_rs[r] = make_float2(a, bb);
+    if (head) {
+      s_rs[r] = make_float2(a, rf.key_min ? (float)rf.mass : bb);
+      s_km[r] = rf.key_min;
+    }
   }
   __syncthreads();
+  if (filt && !greedy) {
+    // A drafted token outside its parent's kept set has probability 0 there:
+    // its recorded logit becomes -inf (the tests then read q(d) = 0 or
+    // p(d) = 0), here and, written back, in the later rounds.
+    if (tid < N) {
+      const int v = tid;
+      for (int k = s.kid_off[v]; k < s.kid_off[v + 1]; ++k) {
+        const int ch = s.kids[k];
+        if (float_key(s_xd[ch * 2], key16 != 0) < s_km[v]) s_xd[ch * 2] = -INFINITY;
+        if (float_key(s_xd[ch * 2 + 1], key16 != 0) < s_km[N + s.int_idx[v]])
+          s_xd[ch * 2 + 1] = -INFINITY;
+      }
+    }
+    __syncthreads();
+    if (tid < 2 * N) xd[(size_t)b * N * 2 + tid] = s_xd[tid];
+  }
   if (!greedy && tid < R) rowstat[(size_t)b * R + tid] = s_rs[tid];
   if (tid == 0) {
     if (greedy) {
@@ -1848,7 +1873,7 @@ __global__ __launch_bounds__(kDecideThreads) void k_tree_decide(
     } else {
       Decision dd;
       TreeState st;
-      tree_walk(b, 0, 0, s, [&](int r) { return s_rs[r]; }, s_xd, s_tk, s_u, c,
+      tree_walk(b, 0, 0, s, [&](int r) { return s_rs[r]; }, s_km, s_xd, s_tk, s_u, c,
                 kLog2eD / (double)t, out_tok, out_node, dd, st);
       dec[b] = dd;
       state[b] = st;
@@ -1874,17 +1899,21 @@ template <bool kAgent>
 __device__ void tree_step(
     int b, const int32_t* __restrict__ tok, const float* __restrict__ uni, const float* __restrict__ temp,
     const TreeShape& s, int ncr, int force_greedy, int last, const float2* __restrict__ rowstat,
-    const float* __restrict__ xd, const ChunkSums* __restrict__ csum, Decision* __restrict__ dec,
-    TreeState* __restrict__ state, int32_t* __restrict__ out_tok, int32_t* __restrict__ out_node,
-    int32_t* __restrict__ nacc) {
+    const RowFilter* __restrict__ filt, const float* __restrict__ xd,
+    const ChunkSums* __restrict__ csum, Decision* __restrict__ dec, TreeState* __restrict__ state,
+    int32_t* __restrict__ out_tok, int32_t* __restrict__ out_node, int32_t* __restrict__ nacc) {
   __shared__ float2 s_rs[2 * kMaxTree];
   __shared__ float s_xd[2 * kMaxTree], s_u[kMaxTree];
+  __shared__ uint32_t s_km[2 * kMaxTree];
   __shared__ int s_tk[kMaxTree];
   __shared__ int s_draw, s_n;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = s.n, R = s.n + s.n_int;
   // The walk's inputs, loaded together with the decision (one round trip).
-  if (tid < R) s_rs[tid] = rowstat[(size_t)b * R + tid];
+  if (tid < R) {
+    s_rs[tid] = rowstat[(size_t)b * R + tid];
+    s_km[tid] = filt ? filt[(size_t)b * R + tid].key_min : 0u;
+  }
   if (tid < N) {
     s_tk[tid] = tok[(size_t)b * N + tid];
     s_u[tid] = uni[(size_t)b * N + tid];
@@ -1932,7 +1961,7 @@ __device__ void tree_step(
             out_tok[(size_t)b * N + n] = s_tk[ch];
             Decision dd;
             TreeState ns;
-            tree_walk(b, ch, n + 1, s, [&](int r) { return s_rs[r]; }, s_xd, s_tk, s_u, kLog2e / t,
+            tree_walk(b, ch, n + 1, s, [&](int r) { return s_rs[r]; }, s_km, s_xd, s_tk, s_u, kLog2e / t,
                       cd, out_tok, out_node, dd, ns);
             dec[b] = dd;
             state[b] = ns;
@@ -1982,11 +2011,12 @@ __device__ void tree_step(
 // count in rcnt reaches ncr), the step that follows.  That workgroup resets
 // the count for the next round; k_sweep clears it before the first.
 // ---------------------------------------------------------------------------
-template <typename T, bool kAligned>
+template <typename T, bool kAligned, bool kMask>
 __global__ __launch_bounds__(kThreads, 4) void k_tree_round(
     const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ tok,
     const float* __restrict__ uni, const float* __restrict__ temp, TreeShape s, int V, int ncr,
-    int force_greedy, int last, const float2* __restrict__ rowstat, const float* __restrict__ xd,
+    int force_greedy, int last, const float2* __restrict__ rowstat,
+    const RowFilter* __restrict__ filt, const float* __restrict__ xd,
     ChunkSums* __restrict__ csum, SubSums* __restrict__ csub, Decision* __restrict__ dec,
     TreeState* __restrict__ state, unsigned* __restrict__ rcnt, int32_t* __restrict__ out_tok,
     int32_t* __restrict__ out_node, int32_t* __restrict__ nacc) {
@@ -1995,7 +2025,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_tree_round(
   const int b = blockIdx.x;
   const Decision d = dec[b];
   if (d.mode == kModeNone || d.mode == kModePending) return;     // block-uniform
-  residual_pass<T, kAligned, false, true>(tgt, drf, d, temp_of(temp, b, force_greedy), V, ncr, b,
+  residual_pass<T, kAligned, kMask, true>(tgt, drf, d, temp_of(temp, b, force_greedy), V, ncr, b,
                                           blockIdx.y, csum, csub, s_exp);
   vm_drain();
   __syncthreads();
@@ -2003,8 +2033,8 @@ __global__ __launch_bounds__(kThreads, 4) void k_tree_round(
   __syncthreads();
   if (!s_last) return;
   if (threadIdx.x == 0) __hip_atomic_store(rcnt + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  tree_step<true>(b, tok, uni, temp, s, ncr, force_greedy, last, rowstat, xd, csum, dec, state,
-                  out_tok, out_node, nacc);
+  tree_step<true>(b, tok, uni, temp, s, ncr, force_greedy, last, rowstat, filt, xd, csum, dec,
+                  state, out_tok, out_node, nacc);
 }
 
 // k_tree_draw: grid (B); block 256.  The draws of the walks that ended in
@@ -2075,8 +2105,8 @@ static hipError_t launch_all(const void* tgt, const void* drf, const int32_t* dt
   const bool filtered = (top_k || top_p) && !force_greedy;
   RowFilter* filt = filtered ? reinterpret_cast<RowFilter*>(ws + p.filt_off) : nullptr;
   if (filtered)
-    hipLaunchKernelGGL((k_filter<T, kAligned>), dim3(B * R), dim3(kFilterThreads), 0, st, t, d, temp,
-                       top_k, top_p, K, V, nc, force_greedy, part, filt);
+    hipLaunchKernelGGL((k_filter<T, kAligned, ChainRows>), dim3(B * R), dim3(kFilterThreads), 0, st, t,
+                       d, temp, top_k, top_p, ChainRows{K}, V, nc, force_greedy, part, filt);
   const int key16 = sizeof(T) == 2 ? 1 : 0;
   // The draw joins the pass kernel while the chunk sums fit one wave.
   const bool fused = ncr <= 64;
@@ -2106,7 +2136,8 @@ static hipError_t launch_all(const void* tgt, const void* drf, const int32_t* dt
 // Tree workspace: the chain's arrays for up to 2N - 1 swept rows, plus the
 // merged row statistics and the walk states.
 struct TreePlan {
-  size_t part_off, rowstat_off, csum_off, csub_off, dec_off, state_off, xd_off, rcnt_off, total;
+  size_t part_off, rowstat_off, csum_off, csub_off, dec_off, state_off, xd_off, rcnt_off, filt_off,
+      total;
 };
 
 static inline TreePlan tree_plan(int B, int N, int V) {
@@ -2121,7 +2152,8 @@ static inline TreePlan tree_plan(int B, int N, int V) {
   p.state_off = p.dec_off + up((size_t)B * sizeof(Decision));
   p.xd_off = p.state_off + up((size_t)B * sizeof(TreeState));
   p.rcnt_off = p.xd_off + up((size_t)B * N * 2 * sizeof(float));
-  p.total = p.rcnt_off + up((size_t)B * sizeof(unsigned));
+  p.filt_off = p.rcnt_off + up((size_t)B * sizeof(unsigned));
+  p.total = p.filt_off + up((size_t)B * R * sizeof(RowFilter));
   return p;
 }
 
@@ -2167,7 +2199,7 @@ static hipError_t launch_tree(const void* tgt, const void* drf, const TreeShape&
                               const int32_t* tok, const float* uni, const float* temp,
                               int32_t* out_tok, int32_t* out_node, int32_t* nacc, int32_t* kv_len,
                               unsigned long long* counters, int B, int V, int force_greedy, char* ws,
-                              hipStream_t st) {
+                              hipStream_t st, const int32_t* top_k, const float* top_p) {
   const int N = shape.n;
   const int nc = sweep_chunks(V);
   const int ncr = res_chunks(V);
@@ -2185,14 +2217,27 @@ static hipError_t launch_tree(const void* tgt, const void* drf, const TreeShape&
   const T* d = static_cast<const T*>(drf);
   hipLaunchKernelGGL((k_sweep<T, kAligned, TreeRows>), dim3(B * R, (nc + 3) / 4), dim3(kThreads), 0,
                      st, t, d, tok, temp, TreeRows{shape}, B, V, nc, force_greedy, part, xd, rcnt);
+  // Filters: thresholds and kept masses per swept row, as for the chain.
+  const bool filtered = (top_k || top_p) && !force_greedy;
+  RowFilter* filt = filtered ? reinterpret_cast<RowFilter*>(ws + p.filt_off) : nullptr;
+  if (filtered)
+    hipLaunchKernelGGL((k_filter<T, kAligned, TreeRows>), dim3(B * R), dim3(kFilterThreads), 0, st, t,
+                       d, temp, top_k, top_p, TreeRows{shape}, V, nc, force_greedy, part, filt);
+  const int key16 = sizeof(T) == 2 ? 1 : 0;
   hipLaunchKernelGGL(k_tree_decide, dim3(B), dim3(kDecideThreads), 0, st, tok, uni, temp, shape, V, nc,
-                     force_greedy, part, xd, rowstat, dec, state, out_tok, out_node, nacc, kv_len,
-                     counters);
+                     force_greedy, part, filt, key16, xd, rowstat, dec, state, out_tok, out_node, nacc,
+                     kv_len, counters);
   const int rounds = force_greedy ? 0 : tree_rounds(shape, 0);
-  for (int r = 1; r <= rounds; ++r)
-    hipLaunchKernelGGL((k_tree_round<T, kAligned>), dim3(B, ncr), dim3(kThreads), 0, st, t, d, tok, uni,
-                       temp, shape, V, ncr, force_greedy, r == rounds ? 1 : 0, rowstat, xd, csum, csub,
-                       dec, state, rcnt, out_tok, out_node, nacc);
+  for (int r = 1; r <= rounds; ++r) {
+    if (filtered)
+      hipLaunchKernelGGL((k_tree_round<T, kAligned, true>), dim3(B, ncr), dim3(kThreads), 0, st, t, d,
+                         tok, uni, temp, shape, V, ncr, force_greedy, r == rounds ? 1 : 0, rowstat, filt,
+                         xd, csum, csub, dec, state, rcnt, out_tok, out_node, nacc);
+    else
+      hipLaunchKernelGGL((k_tree_round<T, kAligned, false>), dim3(B, ncr), dim3(kThreads), 0, st, t, d,
+                         tok, uni, temp, shape, V, ncr, force_greedy, r == rounds ? 1 : 0, rowstat,
+                         filt, xd, csum, csub, dec, state, rcnt, out_tok, out_node, nacc);
+  }
   if (rounds > 0)
     hipLaunchKernelGGL((k_tree_draw<T>), dim3(B), dim3(kThreads), 0, st, t, d, uni, temp, shape.n, V,
                        ncr, force_greedy, csum, csub, dec, out_tok, out_node, nacc, kv_len, counters);
@@ -2358,13 +2403,12 @@ extern "C" size_t spec_reject_sample_tree_workspace_bytes(int B, int N, int V) {
   return sv::tree_plan(B, N, V).total;
 }
 
-extern "C" int spec_reject_sample_tree(const void* target_logits, const void* draft_logits,
-                                       const int32_t* parent, const int32_t* tokens,
-                                       const float* uniforms, const float* temperature,
-                                       int32_t* out_tokens, int32_t* out_nodes,
-                                       int32_t* num_accepted, int32_t* kv_len,
-                                       unsigned long long* counters, int B, int N, int V, int dtype,
-                                       void* workspace, size_t workspace_bytes, void* hip_stream) {
+static int tree_impl(const char* fn, const void* target_logits, const void* draft_logits,
+                     const int32_t* parent, const int32_t* tokens, const float* uniforms,
+                     const float* temperature, const int32_t* top_k, const float* top_p,
+                     int32_t* out_tokens, int32_t* out_nodes, int32_t* num_accepted, int32_t* kv_len,
+                     unsigned long long* counters, int B, int N, int V, int dtype, void* workspace,
+                     size_t workspace_bytes, void* hip_stream) {
   if (B < 0 || N < 1 || V < 1 || !parent) return SV_ERR_INVALID_ARG;
   if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_INVALID_ARG;
   if (N > sv::kMaxTree) return SV_ERR_UNSUPPORTED;
@@ -2386,12 +2430,12 @@ extern "C" int spec_reject_sample_tree(const void* target_logits, const void* dr
   char* ws = static_cast<char*>(workspace);
   const uintptr_t align_bits = reinterpret_cast<uintptr_t>(target_logits) |
                                reinterpret_cast<uintptr_t>(drf);
-  const char* fn = "spec_reject_sample_tree";
   const bool chk = sv::validate_on();
   if (chk) {
     int s = sv::check_tokens(fn, tokens, (long long)B * N, V, N, 1, st);
     if (s == SV_OK) s = sv::check_floats(fn, "uniforms", uniforms, (long long)B * N, true, st);
     if (s == SV_OK) s = sv::check_floats(fn, "temperature", temperature, B, false, st);
+    if (s == SV_OK && top_p) s = sv::check_floats(fn, "top_p", top_p, B, false, st);
     if (s == SV_OK)
       s = sv::check_logits(fn, "target_logits", target_logits, (long long)B * N, V, dtype, st);
     if (s == SV_OK && draft_logits)
@@ -2403,19 +2447,42 @@ extern "C" int spec_reject_sample_tree(const void* target_logits, const void* dr
     const bool al = (V % 8 == 0) && (align_bits & 15) == 0;
     e = al ? sv::launch_tree<uint16_t, true>(target_logits, drf, shape, tokens, uniforms, temperature,
                                              out_tokens, out_nodes, num_accepted, kv_len, counters, B,
-                                             V, force_greedy, ws, st)
+                                             V, force_greedy, ws, st, top_k, top_p)
            : sv::launch_tree<uint16_t, false>(target_logits, drf, shape, tokens, uniforms, temperature,
                                               out_tokens, out_nodes, num_accepted, kv_len, counters, B,
-                                              V, force_greedy, ws, st);
+                                              V, force_greedy, ws, st, top_k, top_p);
   } else {
     const bool al = (V % 4 == 0) && (align_bits & 15) == 0;
     e = al ? sv::launch_tree<float, true>(target_logits, drf, shape, tokens, uniforms, temperature,
                                           out_tokens, out_nodes, num_accepted, kv_len, counters, B, V,
-                                          force_greedy, ws, st)
+                                          force_greedy, ws, st, top_k, top_p)
            : sv::launch_tree<float, false>(target_logits, drf, shape, tokens, uniforms, temperature,
                                            out_tokens, out_nodes, num_accepted, kv_len, counters, B, V,
-                                           force_greedy, ws, st);
+                                           force_greedy, ws, st, top_k, top_p);
   }
   const int status = e == hipSuccess ? SV_OK : SV_ERR_HIP;
   return chk ? sv::finish(fn, st, status) : status;
+}
+
+extern "C" int spec_reject_sample_tree(const void* target_logits, const void* draft_logits,
+                                       const int32_t* parent, const int32_t* tokens,
+                                       const float* uniforms, const float* temperature,
+                                       int32_t* out_tokens, int32_t* out_nodes,
+                                       int32_t* num_accepted, int32_t* kv_len,
+                                       unsigned long long* counters, int B, int N, int V, int dtype,
+                                       void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return tree_impl("spec_reject_sample_tree", target_logits, draft_logits, parent, tokens, uniforms,
+                   temperature, nullptr, nullptr, out_tokens, out_nodes, num_accepted, kv_len,
+                   counters, B, N, V, dtype, workspace, workspace_bytes, hip_stream);
+}
+
+extern "C" int spec_reject_sample_tree_filtered(
+    const void* target_logits, const void* draft_logits, const int32_t* parent,
+    const int32_t* tokens, const float* uniforms, const float* temperature, const int32_t* top_k,
+    const float* top_p, int32_t* out_tokens, int32_t* out_nodes, int32_t* num_accepted,
+    int32_t* kv_len, unsigned long long* counters, int B, int N, int V, int dtype, void* workspace,
+    size_t workspace_bytes, void* hip_stream) {
+  return tree_impl("spec_reject_sample_tree_filtered", target_logits, draft_logits, parent, tokens,
+                   uniforms, temperature, top_k, top_p, out_tokens, out_nodes, num_accepted, kv_len,
+                   counters, B, N, V, dtype, workspace, workspace_bytes, hip_stream);
 }

@@ -160,6 +160,26 @@ def test_tree_reject_validation(lib):
     assert _tree_reject(lib, parent=(-1,), B=0, ptrs=False) == 0 # a root alone is a valid tree
 
 
+def test_filtered_tree_reject_validation(lib):
+    """The filtered tree call checks its arguments as the plain one does
+    (nothing is launched: every return below comes before any device work)."""
+    def call(parent=(-1, 0, 0, 1), B=4, V=100, dtype=1, ws_bytes=1 << 24, ptrs=True):
+        p = FAKE if ptrs else None
+        par = None if parent is None else (ctypes.c_int32 * len(parent))(*parent)
+        n = 4 if parent is None else len(parent)
+        return lib.spec_reject_sample_tree_filtered(
+            p, p, None if par is None else ctypes.cast(par, ctypes.c_void_p), p, p, p, p, p, p, p,
+            p, p, None, B, n, V, dtype, p, ws_bytes, None)
+    need = sv.reject_sample_tree_workspace_bytes(4, 4, 100)
+    assert call(ws_bytes=need - 1) == -3
+    assert call(parent=None) == -1
+    assert call(parent=(-1, 0, 2)) == -1
+    assert call(B=-1) == -1 and call(V=0) == -1 and call(dtype=5) == -1
+    assert call(parent=tuple([-1] + list(range(17)))) == -2
+    assert call(ptrs=False) == -1
+    assert call(B=0, ptrs=False) == 0                            # an empty batch is a no-op
+
+
 def test_tree_reject_workspace_matches_chain(lib):
     # A chain of K + 1 nodes sweeps the same 2K + 1 rows as the chain call;
     # the tree adds its walk state and merged row statistics, the chain its
