@@ -144,14 +144,24 @@ struct RowFilter {
 // Shape of a draft tree (nodes in topological order, parent[i] < i), shared
 // by the batch; passed by value as a kernel argument.
 constexpr int kMaxTree = SV_MAX_K + 1;
+// Each table starts on a 4-byte boundary of the kernel arguments, so a
+// lookup with a wave-uniform index can be one scalar load of the word that
+// holds the entry (an unaligned byte would be a vector load to wait for).
 struct TreeShape {
-  int n;                           // nodes
-  int n_int;                       // nodes with children
-  int8_t kid_off[kMaxTree + 1];    // children of v: kids[kid_off[v] .. kid_off[v + 1])
-  int8_t kids[kMaxTree];           // in increasing index order
-  int8_t int_node[kMaxTree];       // node whose draft row is swept row n + i
-  int8_t int_idx[kMaxTree];        // i for a node with children, -1 for a leaf
+  int n;                                   // nodes
+  int n_int;                               // nodes with children
+  alignas(4) int8_t kid_off[kMaxTree + 1]; // children of v: kids[kid_off[v] .. kid_off[v + 1])
+  alignas(4) int8_t kids[kMaxTree];        // in increasing index order
+  alignas(4) int8_t int_node[kMaxTree];    // node whose draft row is swept row n + i
+  alignas(4) int8_t int_idx[kMaxTree];     // i for a node with children, -1 for a leaf
 };
+
+// Entry i of a byte table of the kernel arguments, i wave-uniform: the
+// 32-bit word that holds it, then the byte.
+__device__ __forceinline__ int arg_byte(const int8_t* tab, int i) {
+  const uint32_t w = reinterpret_cast<const uint32_t*>(tab)[i >> 2];
+  return (int)(int8_t)(w >> ((i & 3) * 8));
+}
 
 // Where a tree walk stands between rounds.
 struct TreeState {
@@ -188,12 +198,15 @@ struct TreeRows {
   __device__ __forceinline__ int count() const { return s.n + s.n_int; }
   __device__ __forceinline__ bool is_draft(int j) const { return j >= s.n; }
   __device__ __forceinline__ int n_target() const { return s.n; }
-  __device__ __forceinline__ int node(int j) const { return j < s.n ? j : s.int_node[j - s.n]; }
+  __device__ __forceinline__ int node(int j) const {
+    return j < s.n ? j : arg_byte(s.int_node, j - s.n);
+  }
   __device__ __forceinline__ size_t row(int b, int j) const { return (size_t)b * s.n + node(j); }
   template <class F>
   __device__ __forceinline__ void for_each_token(int b, int j, F&& f) const {
     const int v = node(j);
-    for (int k = s.kid_off[v]; k < s.kid_off[v + 1]; ++k) f((size_t)b * s.n + s.kids[k]);
+    for (int k = arg_byte(s.kid_off, v); k < arg_byte(s.kid_off, v + 1); ++k)
+      f((size_t)b * s.n + arg_byte(s.kids, k));
   }
 };
 
@@ -346,10 +359,11 @@ __global__ __launch_bounds__(kThreads) void k_sweep(
   const int b = r < B * NT ? r / NT : (r - B * NT) / ND;
   const int j = r < B * NT ? r - b * NT : NT + (r - B * NT) - b * ND;
   const int row = b * R + j;                   // row index of the statistics
-  const float t = temp_of(temp, b, force_greedy);
-  const bool greedy = !(t > 0.f);
   const bool is_draft = rows.is_draft(j);
-  if (greedy && is_draft) return;              // greedy never reads draft rows
+  // Greedy sequences never read draft rows, so a draft row waits for its
+  // sequence's temperature; a target row is read whatever it is, and its
+  // loads are issued before the temperature arrives.
+  if (is_draft && !(temp_of(temp, b, force_greedy) > 0.f)) return;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int chunk = blockIdx.y * 4 + wave;
@@ -369,6 +383,8 @@ __global__ __launch_bounds__(kThreads) void k_sweep(
 #pragma unroll
     for (int it = 0; it < IT; ++it) load_vec<T, kAligned, true>(src, base + it * 64 * VN, V, x[it]);
   }
+  const float t = temp_of(temp, b, force_greedy);
+  const bool greedy = !(t > 0.f);
   if (!greedy) {
     // The logits of the tokens this row tests, for the accept tests: each
     // written by the lane that holds it (xd[2 token + is_draft]).
@@ -1807,6 +1823,9 @@ __global__ __launch_bounds__(kDecideThreads) void k_tree_decide(
   __shared__ uint32_t s_km[2 * kMaxTree];
   __shared__ int s_tk[kMaxTree];
   __shared__ int s_n, s_tok;
+  // The shape's tables in LDS: the walk looks them up with per-thread indices.
+  __shared__ TreeShape s_sh;
+  if (threadIdx.x == 0) s_sh = s;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int N = s.n, R = s.n + s.n_int;
@@ -1840,10 +1859,10 @@ __global__ __launch_bounds__(kDecideThreads) void k_tree_decide(
     // p(d) = 0), here and, written back, in the later rounds.
     if (tid < N) {
       const int v = tid;
-      for (int k = s.kid_off[v]; k < s.kid_off[v + 1]; ++k) {
-        const int ch = s.kids[k];
+      for (int k = s_sh.kid_off[v]; k < s_sh.kid_off[v + 1]; ++k) {
+        const int ch = s_sh.kids[k];
         if (float_key(s_xd[ch * 2], key16 != 0) < s_km[v]) s_xd[ch * 2] = -INFINITY;
-        if (float_key(s_xd[ch * 2 + 1], key16 != 0) < s_km[N + s.int_idx[v]])
+        if (float_key(s_xd[ch * 2 + 1], key16 != 0) < s_km[N + s_sh.int_idx[v]])
           s_xd[ch * 2 + 1] = -INFINITY;
       }
     }
@@ -1859,8 +1878,8 @@ __global__ __launch_bounds__(kDecideThreads) void k_tree_decide(
       for (;;) {
         const int am = __float_as_int(s_rs[v].y);
         int nxt = -1;
-        for (int k = s.kid_off[v]; k < s.kid_off[v + 1]; ++k)
-          if (clampi(s_tk[s.kids[k]], 0, V - 1) == am) { nxt = s.kids[k]; break; }
+        for (int k = s_sh.kid_off[v]; k < s_sh.kid_off[v + 1]; ++k)
+          if (clampi(s_tk[s_sh.kids[k]], 0, V - 1) == am) { nxt = s_sh.kids[k]; break; }
         if (nxt < 0) { fin = am; break; }
         out_node[(size_t)b * N + n] = nxt;
         out_tok[(size_t)b * N + n] = s_tk[nxt];
@@ -1873,7 +1892,7 @@ __global__ __launch_bounds__(kDecideThreads) void k_tree_decide(
     } else {
       Decision dd;
       TreeState st;
-      tree_walk(b, 0, 0, s, [&](int r) { return s_rs[r]; }, s_km, s_xd, s_tk, s_u, c,
+      tree_walk(b, 0, 0, s_sh, [&](int r) { return s_rs[r]; }, s_km, s_xd, s_tk, s_u, c,
                 kLog2eD / (double)t, out_tok, out_node, dd, st);
       dec[b] = dd;
       state[b] = st;
@@ -1894,9 +1913,10 @@ __global__ __launch_bounds__(kDecideThreads) void k_tree_decide(
 // no later pass of the sequence overwrites them).  So a round waits for no
 // draw, and all draws take one launch after the last round.  kAgent: the
 // pass's chunk sums were stored by other workgroups of the running kernel.
+// s: the shape in LDS (the walk indexes its tables per thread).
 // ---------------------------------------------------------------------------
 template <bool kAgent>
-__device__ void tree_step(
+__device__ __forceinline__ void tree_step(
     int b, const int32_t* __restrict__ tok, const float* __restrict__ uni, const float* __restrict__ temp,
     const TreeShape& s, int ncr, int force_greedy, int last, const float2* __restrict__ rowstat,
     const RowFilter* __restrict__ filt, const float* __restrict__ xd,
@@ -2033,7 +2053,12 @@ __global__ __launch_bounds__(kThreads, 4) void k_tree_round(
   __syncthreads();
   if (!s_last) return;
   if (threadIdx.x == 0) __hip_atomic_store(rcnt + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  tree_step<true>(b, tok, uni, temp, s, ncr, force_greedy, last, rowstat, filt, xd, csum, dec,
+  // The shape's tables in LDS for the step (its walk indexes them per
+  // thread; from the kernel arguments each lookup would be a memory load).
+  __shared__ TreeShape s_sh;
+  if (threadIdx.x == 0) s_sh = s;
+  __syncthreads();
+  tree_step<true>(b, tok, uni, temp, s_sh, ncr, force_greedy, last, rowstat, filt, xd, csum, dec,
                   state, out_tok, out_node, nacc);
 }
 
