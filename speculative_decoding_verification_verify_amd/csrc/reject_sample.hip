@@ -65,6 +65,7 @@
 #pragma clang fp contract(off)
 
 #include <algorithm>
+#include <cstddef>
 #include <mutex>
 
 #include "common.h"
@@ -155,6 +156,10 @@ struct TreeShape {
   alignas(4) int8_t int_node[kMaxTree];    // node whose draft row is swept row n + i
   alignas(4) int8_t int_idx[kMaxTree];     // i for a node with children, -1 for a leaf
 };
+
+static_assert(offsetof(TreeShape, kid_off) % 4 == 0 && offsetof(TreeShape, kids) % 4 == 0 &&
+                  offsetof(TreeShape, int_node) % 4 == 0 && offsetof(TreeShape, int_idx) % 4 == 0,
+              "shape tables start on 4-byte boundaries");
 
 // Entry i of a byte table of the kernel arguments, i wave-uniform: the
 // 32-bit word that holds it, then the byte.
