@@ -159,10 +159,12 @@ int spec_verify_attn_tree(const void* q, const void* k_cache, const void* v_cach
  * mode SV_WINDOW_READ: the window keys are read from k_new / v_new and the
  *   cache is not written (the scratch-buffer variant: spec_kv_commit moves
  *   the accepted rows into the cache afterwards).
- * mode SV_WINDOW_APPEND: the same, and the kernel also stores row i into its
- *   cache slot L0 + i (pages from block_table; the caller has reserved them),
- *   so no separate write pass is needed.  Each element is stored once, by
- *   the lane that holds it for the product; the cache is never read back.
+ * mode SV_WINDOW_APPEND: row i is stored into its cache slot L0 + i (pages
+ *   from block_table; the caller has reserved them) by a copy kernel the call
+ *   launches first, and the attention then reads the whole window from the
+ *   cache, exactly as spec_verify_attn (the same output bit for bit).  The
+ *   copy moves 16-byte vectors: k_new, v_new and both caches 16-byte aligned
+ *   (either dtype), else SV_ERR_INVALID_ARG.
  * anc: NULL for a chain (N = K + 1), or [B, N] ancestor sets of a tree as for
  *   spec_verify_attn_tree.  Everything else as spec_verify_attn with
  *   K = N - 1 (same workspace).  out and the cache slots L0 .. L0 + N - 1 are
@@ -402,7 +404,9 @@ int spec_reject_sample_tree_filtered(const void* target_logits, const void* draf
  *
  * Layouts as spec_verify_attn; nodes [B, N] int32.  Sizes: 1 <= N <=
  * SV_MAX_K + 1, D in {64, 128}, block_size == 16.  Only the cache slots
- * L0 .. L0 + n are written.
+ * L0 .. L0 + n are written.  Keys, runs of values and scratch rows move as
+ * 16-byte vectors: both caches and k_src / v_src 16-byte aligned, else
+ * SV_ERR_INVALID_ARG.
  */
 int spec_kv_commit(void* k_cache, void* v_cache, const int32_t* block_table,
                    const int32_t* kv_len, const int32_t* num_accepted,

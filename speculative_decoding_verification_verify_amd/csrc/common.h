@@ -100,6 +100,12 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// The append mode of the window attention: rows 0 .. N - 1 of k_new / v_new
+// ([B, N, Hkv, D]) into cache positions kv_len[b] + j (kv_commit.hip).
+hipError_t launch_window_store(void* kc, void* vc, const int32_t* bt, const int32_t* kv_len,
+                               const void* kn, const void* vn, int B, int N, int Hkv, int D,
+                               int num_blocks, int mbps, int dtype, hipStream_t st);
+
 // Compute units of the current device (cached per device).
 static inline int device_cus() {
   static int cached[64] = {0};

@@ -142,11 +142,9 @@ __device__ __forceinline__ void mask_v_tail(bf16x8 (&vf)[2][D / 32], int pr, int
 }
 
 // ---- Window taken from the projection output (k_new / v_new [B, K1, Hkv, D])
-// instead of the cache: the pair that holds window keys reads them there,
-// and in append mode stores them into their cache slots as well.  Each
-// window element is held by exactly one lane of the wave that processes its
-// pair, in the MFMA operand layout, so each is loaded once and stored once
-// and the cache is never read back.
+// instead of the cache (read mode; append mode stores the rows into their
+// slots with a copy kernel first and then runs the plain kernel): the pair
+// that holds window keys reads them there.
 
 // True (wave-uniform) when pair pr of a sequence with committed length L0
 // holds window keys L0 .. L0 + K1 - 1.
@@ -173,45 +171,10 @@ __device__ __forceinline__ void load_k_window(bf16x8 (&kf)[D / 16], const int (&
   for (int kk = 0; kk < D / 16; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(base + kk * step);
 }
 
-// Append mode: this lane's window K chunks into their page slots.
-template <int D>
-__device__ __forceinline__ void store_k_window(const bf16x8 (&kf)[D / 16], const int (&blk)[2],
-                                               uint16_t* __restrict__ kc, int K1, int Hkv, int g,
-                                               int L0, int pr, int k_page, int k_tok, int hh) {
-  const int i = pr * kPairKeys + k_page * 16 + k_tok - L0;
-  if ((unsigned)i < (unsigned)K1) {
-    uint16_t* kpage = kc + ((size_t)(k_page ? blk[1] : blk[0]) * Hkv + g) * ((size_t)D * 16);
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-      *reinterpret_cast<bf16x8*>(kpage + ((2 * kk + hh) * 16 + k_tok) * 8) = kf[kk];
-  }
-}
-
 // V of the window: v_new holds the tokens of one value coordinate strided,
 // so a segment's window rows are staged in LDS ([row][d], bf16) ahead of
 // time, and the pair with window keys takes those tokens' entries from there.
 constexpr int kWinRows = SV_MAX_K + 1;
-
-// Append mode: the V operand of a window pair, once the window entries are
-// in it, back into the pages: each lane's runs of 8 slots that hold a window
-// token, as whole 16-byte stores (the other slots of the run rewritten with
-// the values just read).  Stores of single 2-byte slots, one per value
-// coordinate and token, would each cost the memory a read-modify-write.
-template <int D>
-__device__ __forceinline__ void store_v_window(const bf16x8 (&vf)[2][D / 32], const int (&blk)[2],
-                                               uint16_t* __restrict__ vc, int K1, int Hkv, int g,
-                                               int L0, int pr, int l32, int hh) {
-#pragma unroll
-  for (int sg = 0; sg < 2; ++sg) {
-    const int i0 = pr * kPairKeys + sg * 16 + 8 * hh - L0;   // window index of the run's first slot
-    if (i0 + 8 > 0 && i0 < K1) {
-      uint16_t* vpage = vc + ((size_t)blk[sg] * Hkv + g) * ((size_t)D * 16);
-#pragma unroll
-      for (int j = 0; j < D / 32; ++j)
-        *reinterpret_cast<bf16x8*>(vpage + (32 * j + l32) * 16 + 8 * hh) = vf[sg][j];
-    }
-  }
-}
 
 template <int D>
 __device__ __forceinline__ void window_v(bf16x8 (&vf)[2][D / 32], const uint16_t* s_win, int K1,
@@ -487,7 +450,7 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
     const uint32_t* __restrict__ anc, uint16_t* __restrict__ out,
     int B, int K1, int Hq, int Hkv, int num_blocks, int mbps, int np_cap, float sl2, int W,
     float* __restrict__ opart, float2* __restrict__ ml, const uint16_t* __restrict__ kn,
-    const uint16_t* __restrict__ vn, int store_win) {
+    const uint16_t* __restrict__ vn) {
   constexpr int KK = D / 16;         // MFMA k-steps for S
   constexpr int DT = D / 32;         // d tiles for O
   constexpr int ROWS = 32 * NT;
@@ -654,8 +617,7 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
     }
     if (WIN) {
       // This wave's window pairs, each loaded here: K from k_new for the
-      // window keys (stored into the cache in append mode), V from the
-      // staged rows.
+      // window keys, V from the staged rows.
       for (; pr < cur.p_hi; pr += NW) {
         int blk[2];
         pair_blocks(blk, pr, btb, mbps, num_blocks);
@@ -665,9 +627,7 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           score_pair<D, NT>(kf, pr, hh, nt, qf, am, cur.L0, sl2, o, m_run, l_run, pf[nt]);
-        if (store_win) store_k_window<D>(kf, blk, kc, K1, Hkv, cur.g, cur.L0, pr, k_page, k_tok, hh);
         window_v<D>(vf, s_win[wbuf], K1, cur.L0, pr, l32, hh);
-        if (store_win) store_v_window<D>(vf, blk, vc, K1, Hkv, cur.g, cur.L0, pr, l32, hh);
         mask_v_tail<D>(vf, pr, L, hh);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) pv_pair<D, NT>(vf, nt, pf[nt], o);
@@ -889,16 +849,14 @@ __global__ __launch_bounds__(kCombineThreads) void k_attn_stream_combine(
 // ---------------------------------------------------------------------------
 // fp32 VALU kernel: grid (K1, Hq, B), block 64 (one wave per query row).
 // k_cache [NB, Hkv, D/4, 16, 4], v_cache [NB, Hkv, D, 16].  With kn / vn the
-// window keys are read from there (never from the cache), and with store_win
-// the block of row 0 of each KV head's first query head also writes them
-// into the cache.
+// window keys are read from there (never from the cache).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_attn_valu(
     const float* __restrict__ q, float* __restrict__ kc, float* __restrict__ vc,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ kv_len,
     const uint32_t* __restrict__ anc, float* __restrict__ out,
     int K1, int Hq, int Hkv, int D, int num_blocks, int mbps, float sl2,
-    const float* __restrict__ kn, const float* __restrict__ vn, int store_win) {
+    const float* __restrict__ kn, const float* __restrict__ vn) {
   __shared__ float s_q[256];
   __shared__ float s_p[64];
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -912,16 +870,6 @@ __global__ __launch_bounds__(64) void k_attn_valu(
   __syncthreads();
   const int32_t* btb = bt + (size_t)b * mbps;
   const size_t page = (size_t)D * 16;
-  if (kn && store_win && i == 0 && h % (Hq / Hkv) == 0) {
-    for (int e = lane; e < K1 * D; e += 64) {
-      const int ii = e / D, d = e - ii * D;
-      const int p = L0 + ii;
-      const int blk = clampi(btb[min(p >> 4, mbps - 1)], 0, num_blocks - 1);
-      const size_t src = (((size_t)b * K1 + ii) * Hkv + g) * D + d;
-      kc[((size_t)blk * Hkv + g) * page + ((d >> 2) * 16 + (p & 15)) * 4 + (d & 3)] = kn[src];
-      vc[((size_t)blk * Hkv + g) * page + d * 16 + (p & 15)] = vn[src];
-    }
-  }
   float m_run = -INFINITY, l_run = 0.f;
   float o[4] = {0.f, 0.f, 0.f, 0.f};              // d = lane + 64 * c
   for (int j0 = 0; j0 <= t; j0 += 64) {
@@ -1042,8 +990,7 @@ static hipError_t launch_stream_t(const void* q, void* kc, void* vc, const int32
                      static_cast<const uint16_t*>(q), static_cast<uint16_t*>(kc),
                      static_cast<uint16_t*>(vc), bt, kv_len, anc, static_cast<uint16_t*>(out), B,
                      K1, Hq, Hkv, num_blocks, mbps, p.np_cap, sl2, W, opart, ml,
-                     static_cast<const uint16_t*>(win.kn), static_cast<const uint16_t*>(win.vn),
-                     win.store);
+                     static_cast<const uint16_t*>(win.kn), static_cast<const uint16_t*>(win.vn));
   if (W > 1) {
     const int rows = (Hq / Hkv) * K1;
     if ((long long)B * Hkv >= device_cus()) {
@@ -1101,6 +1048,11 @@ static int verify_attn_impl(const void* q, void* k_cache, void* v_cache,
   if (B == 0) return SV_OK;
   if (!q || !k_cache || !v_cache || !block_table || !kv_len || !out) return SV_ERR_INVALID_ARG;
   if ((win.kn == nullptr) != (win.vn == nullptr)) return SV_ERR_INVALID_ARG;
+  // The append copy moves 16-byte vectors (either dtype).
+  if (win.kn && win.store &&
+      ((reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache) |
+        reinterpret_cast<uintptr_t>(win.kn) | reinterpret_cast<uintptr_t>(win.vn)) & 15))
+    return SV_ERR_INVALID_ARG;
   if (B > 65535 || Hkv > 65535) return SV_ERR_UNSUPPORTED;
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)D);
   const float sl2 = sc * kLog2e;
@@ -1126,25 +1078,34 @@ static int verify_attn_impl(const void* q, void* k_cache, void* v_cache,
     if (s != SV_OK) return s;
   }
   hipError_t e;
+  WindowArgs win_r = win;
+  if (win.kn && win.store) {
+    // Append: the window rows go into their slots first (one small copy
+    // kernel), and the attention then reads the whole window from the cache.
+    e = launch_window_store(k_cache, v_cache, block_table, kv_len, win.kn, win.vn, B, K1, Hkv, D,
+                            num_blocks, max_blocks_per_seq, dtype, st);
+    if (e != hipSuccess) return chk ? finish(fn, st, SV_ERR_HIP) : SV_ERR_HIP;
+    win_r = WindowArgs{nullptr, nullptr, 0};
+  }
   if (dtype == SV_F32) {
     hipLaunchKernelGGL(k_attn_valu, dim3(K1, Hq, B), dim3(64), 0, st,
                        static_cast<const float*>(q), static_cast<float*>(k_cache),
                        static_cast<float*>(v_cache), block_table, kv_len, anc,
                        static_cast<float*>(out), K1, Hq, Hkv, D, num_blocks, max_blocks_per_seq, sl2,
-                       static_cast<const float*>(win.kn), static_cast<const float*>(win.vn), win.store);
+                       static_cast<const float*>(win_r.kn), static_cast<const float*>(win_r.vn));
     e = hipGetLastError();
   } else {
     char* ws = static_cast<char*>(workspace);
     if (D == 128) {
       e = p.tiles == 1 ? launch_stream<128, 1>(q, k_cache, v_cache, block_table, kv_len, anc, out, B,
-                                               K1, Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, win, st)
+                                               K1, Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, win_r, st)
                        : launch_stream<128, 2>(q, k_cache, v_cache, block_table, kv_len, anc, out, B,
-                                               K1, Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, win, st);
+                                               K1, Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, win_r, st);
     } else {
       e = p.tiles == 1 ? launch_stream<64, 1>(q, k_cache, v_cache, block_table, kv_len, anc, out, B,
-                                              K1, Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, win, st)
+                                              K1, Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, win_r, st)
                        : launch_stream<64, 2>(q, k_cache, v_cache, block_table, kv_len, anc, out, B,
-                                              K1, Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, win, st);
+                                              K1, Hq, Hkv, num_blocks, max_blocks_per_seq, sl2, p, ws, win_r, st);
     }
   }
   const int status = e == hipSuccess ? SV_OK : SV_ERR_HIP;

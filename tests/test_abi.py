@@ -230,6 +230,25 @@ def test_kv_commit_validation(lib):
     assert _commit(lib, nodes=False, src=0) == 0          # chain in place: nothing to move
 
 
+MISALIGNED = ctypes.c_void_p(0x10008)   # 8-byte but not 16-byte aligned; never dereferenced
+
+
+def test_vector_copies_need_16_byte_alignment(lib):
+    # spec_kv_commit moves keys, value runs and scratch rows as 16-byte
+    # vectors in either dtype.
+    assert lib.spec_kv_commit(FAKE, FAKE, FAKE, FAKE, FAKE, None, MISALIGNED, FAKE, 2, 8, 8, 128, 16,
+                              10, 600, 0, None) == -1
+    assert lib.spec_kv_commit(MISALIGNED, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 2, 8, 8, 128, 16,
+                              10, 600, 0, None) == -1
+    # Append mode's copy as well, fp32 included; read mode in fp32 has no
+    # such requirement, so only the append case is checked here.
+    p = FAKE
+    for dtype in (0, 1):
+        assert lib.spec_verify_attn_window(p, MISALIGNED, MISALIGNED, p, p, p, p, None, p, 2, 8, 32,
+                                           8, 128, 16, 10, 600, 8192, ctypes.c_float(0.0), dtype, 1,
+                                           p, 1 << 30, None) == -1
+
+
 # ---- the Python binding's argument checks (CPU tensors: every shape error is
 # raised before the device check, and nothing reaches the library) -----------
 
