@@ -103,6 +103,10 @@ def parse():
                         "spec_reject_sample_tree_filtered with --tree; 0: off)")
     p.add_argument("--top-p", type=float, default=1.0,
                    help="top-p filter for every sequence (1: off)")
+    p.add_argument("--tree-mix", type=int, default=0, metavar="N",
+                   help="verify one draft tree of N nodes per sequence (a mix of chains, stars, "
+                        "two-level and random trees): spec_verify_attn_tree with per-sequence "
+                        "ancestor sets + spec_reject_sample_trees")
     p.add_argument("--tree", default="", metavar="SHAPE",
                    help="verify a draft tree instead of a chain: branching factors per level, "
                         "e.g. 2,2,2 (15 nodes); times spec_verify_attn_tree + "
@@ -140,11 +144,19 @@ def main():
     cfg = CONFIGS[args.config]
     B, K, V = (args.batch or cfg.B), cfg.K, cfg.V
     parent = None
+    if args.tree and args.tree_mix:
+        raise SystemExit("--tree and --tree-mix exclude each other")
     if args.tree:
-        from synth.tree import tree_parents, ancestor_bits
+        from synth.tree import tree_parents
         shape = tuple(int(x) for x in args.tree.split(","))
         parent = tree_parents(shape)
         K = len(parent) - 1                       # window of N = K + 1 tree nodes
+    elif args.tree_mix:
+        from synth.tree import mixed_parents
+        if not 1 <= args.tree_mix <= 17:
+            raise SystemExit("--tree-mix takes 1..17 nodes")
+        parent = mixed_parents(args.seed, B, args.tree_mix)     # [B, N]: one tree per sequence
+        K = args.tree_mix - 1
     K1 = K + 1
     print("bench: %s B=%d K=%d V=%d T=%.2f steps=%d warmup=%d" %
           (cfg.name, B, K, V, args.temp, args.steps, args.warmup), file=sys.stderr, flush=True)
@@ -170,10 +182,14 @@ def main():
     if args.window != "none":
         kn_h, vn_h = gen.make_window_kv(args.seed + 99, B, K1, cfg.Hkv, cfg.D)
         kn, vn = to_device(kn_h, dev), to_device(vn_h, dev)
-    anc = None
+    anc = par_dev = None
     if parent is not None:
-        anc = to_device(np.broadcast_to(ancestor_bits(parent).astype(np.uint32),
-                                        (B, K1)).copy().view(np.int32), dev)
+        from synth.tree import ancestor_bits
+        bits = (np.stack([ancestor_bits(p) for p in parent]) if parent.ndim == 2
+                else np.broadcast_to(ancestor_bits(parent), (B, K1)))
+        anc = to_device(bits.astype(np.uint32).copy().view(np.int32), dev)
+        if parent.ndim == 2:
+            par_dev = to_device(parent.astype(np.int32), dev)
     n_total = args.warmup + args.steps
     kv_bufs = [kv0.clone() for _ in range(n_total)]
     attn_out = torch.empty_like(attn["q"])
@@ -224,6 +240,12 @@ def main():
                              r["temperature"], kv, out_tokens=out_tok[s % args.sets],
                              num_accepted=n_acc[s % args.sets], workspace=rej_ws,
                              top_k=filt_k, top_p=filt_p)
+        elif par_dev is not None:
+            sv.reject_sample_trees(r["target"], r["draft"], par_dev, r["tokens"], r["uniforms"],
+                                   r["temperature"], kv, out_tokens=out_tok[s % args.sets],
+                                   out_nodes=out_node[s % args.sets],
+                                   num_accepted=n_acc[s % args.sets], workspace=rej_ws,
+                                   top_k=filt_k, top_p=filt_p)
         else:
             sv.reject_sample_tree(r["target"], r["draft"], parent, r["tokens"], r["uniforms"],
                                   r["temperature"], kv, out_tokens=out_tok[s % args.sets],
@@ -333,15 +355,20 @@ def main():
     if parent is None:
         vis = int(sum(int(l) * K1 + K1 * (K1 + 1) // 2 for l in kvl))
     else:
-        depth = [bin(int(a)).count("1") for a in ancestor_bits(parent)]
-        vis = int(sum(int(l) * K1 + sum(depth) for l in kvl))
+        pars = parent if parent.ndim == 2 else np.broadcast_to(parent, (B, K1))
+        depth = [sum(bin(int(a)).count("1") for a in ancestor_bits(pp)) for pp in pars]
+        vis = int(sum(int(l) * K1 + dep for l, dep in zip(kvl, depth)))
     attn_flops = 4 * cfg.D * cfg.Hq * vis
     attn_tflops = attn_flops / (attn_us * 1e-6) / 1e12
     # The sweep reads every target row and the draft rows of the nodes with
     # children (all K draft rows of a chain); greedy reads target rows only.
     # The exact passes after rejections come on top and are not counted.
-    n_draft_rows = K if parent is None else len(set(int(x) for x in parent[1:]))
-    rej_bytes = B * (K1 + (n_draft_rows if args.temp > 0 else 0)) * V * 2
+    if parent is None:
+        n_draft_rows = B * K
+    else:
+        pars = parent if parent.ndim == 2 else np.broadcast_to(parent, (B, K1))
+        n_draft_rows = sum(len(set(int(x) for x in pp[1:])) for pp in pars)
+    rej_bytes = (B * K1 + (n_draft_rows if args.temp > 0 else 0)) * V * 2
     probe = None if args.no_probe else read_peak(sv, sizes={"attn": attn_bytes,
                                                             "reject": rej_bytes})
     measured_peak = None if probe is None else probe["gbs"]
@@ -387,6 +414,12 @@ def main():
     if args.cpu_sample > 0:
         cpu = cpu_baseline(args, cfg, attn, rsets[0]["host"], from_device, parent)
 
+    if parent is None:
+        window_desc = "K=%d" % K
+    elif parent.ndim == 1:
+        window_desc = "draft tree [%s] (%d nodes)" % (args.tree, K1)
+    else:
+        window_desc = "one draft tree of %d nodes per sequence (mixed shapes)" % K1
     rec = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -402,8 +435,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "%s: B=%d %s V=%d, %dq/%dkv heads D=%d, ctx U[%d,%d], "
                                "bf16 logits N(0,2), draft sigma %.2f, T=%.2f" %
-                               (cfg.name, B, ("K=%d" % K) if parent is None else
-                                ("draft tree [%s] (%d nodes)" % (args.tree, K1)),
+                               (cfg.name, B, window_desc,
                                 V, cfg.Hq, cfg.Hkv, cfg.D, cfg.ctx[0], cfg.ctx[1],
                                 cfg.draft_sigma, args.temp),
                    "global_batch": B, "K": K, "V": V, "parallelism": "single GPU",
@@ -412,8 +444,9 @@ def main():
         "roofline_reject": {"bound": "hbm", "achieved": round(rej_gbs, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(rej_gbs / PEAK_HBM_GBS, 4),
                             "traffic": None,
-                            "kernel": "spec_reject_sample%s call" % ("" if parent is None
-                                                                     else "_tree"),
+                            "kernel": "spec_reject_sample%s call" % (
+                                "" if parent is None else "_tree" if parent.ndim == 1
+                                else "_trees"),
                             "algorithmic_bytes": rej_bytes, "avg_us": round(rej_us, 2),
                             "frac_of_same_size_probe": vs_probe("reject", rej_us)},
         "read_probe": probe,
@@ -591,7 +624,7 @@ def cpu_baseline(args, cfg, attn, host_rej, from_device, parent=None):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         blas_threads = 1
-    K1 = cfg.K + 1 if parent is None else len(parent)
+    K1 = cfg.K + 1 if parent is None else parent.shape[-1]
     # The tree oracle's attention masks every node separately: a smaller sample.
     B = args.batch or cfg.B
     n = min(args.cpu_sample if parent is None else max(1, args.cpu_sample // 8), B)
@@ -610,6 +643,8 @@ def cpu_baseline(args, cfg, attn, host_rej, from_device, parent=None):
         m = (kvl[b] + K1 + 15) // 16
         bt_local[b, :m] = remap[bt[b, :m]]
     h = host_rej
+    if parent is not None and parent.ndim == 2:
+        parent = parent[:n]                       # one tree per sequence: the sample's
     t_attn = t_rej = 0.0
     passes = tokens = 0
     while passes == 0 or t_attn + t_rej < args.cpu_seconds:

@@ -384,6 +384,35 @@ int spec_reject_sample_tree_filtered(const void* target_logits, const void* draf
                                      void* hip_stream);
 
 /*
+ * spec_reject_sample_trees -- spec_reject_sample_tree_filtered with one tree
+ * per sequence (thakicloud, "Grading every branch in one pass": each request
+ * grades its own draft tree; AI Engineering from Scratch, "Speculative
+ * decoding and EAGLE-3": EAGLE-2 grows a tree per context).  Sequence b's
+ * tree is parents[b]; everything the shared-tree calls define (the walk, the
+ * outputs, the commit, the filters and their band) applies per sequence with
+ * that tree.  All trees have N nodes (the shape of spec_verify_attn_tree's
+ * ancestor sets).
+ *
+ * parents: [B, N] int32 DEVICE array, parents[b][0] = -1 and
+ *   0 <= parents[b][i] < i; a parent outside [0, i) is read as i - 1 (with
+ *   SPECVERIFY_VALIDATE=1 it is SV_ERR_BAD_INPUT).  NULL only with B == 0.
+ * top_k, top_p: as spec_reject_sample_tree_filtered, or NULL (no filter).
+ * Work: the sweep and filters skip the draft rows of a sequence's leaves; the
+ *   host cannot see the shapes, so it launches N - 1 rounds (the most a tree
+ *   of N nodes can need: a root with N - 1 children), and a sequence whose
+ *   walk has ended leaves the remaining rounds at once.
+ * workspace: spec_reject_sample_tree_workspace_bytes(B, N, V) (it includes
+ *   room for the B shapes).  Other sizes and errors as
+ *   spec_reject_sample_tree.
+ */
+int spec_reject_sample_trees(const void* target_logits, const void* draft_logits,
+                             const int32_t* parents, const int32_t* tokens, const float* uniforms,
+                             const float* temperature, const int32_t* top_k, const float* top_p,
+                             int32_t* out_tokens, int32_t* out_nodes, int32_t* num_accepted,
+                             int32_t* kv_len, unsigned long long* counters, int B, int N, int V,
+                             int dtype, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
  * spec_kv_commit -- after the verifier, the surviving window rows' K/V into
  * their committed positions (AI Engineering from Scratch, "Speculative
  * decoding and EAGLE-3", "Rolling back the KV cache": a scratch buffer

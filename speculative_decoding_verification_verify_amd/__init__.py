@@ -42,7 +42,7 @@ EXPORTS = ("spec_verify_attn", "spec_verify_attn_workspace_bytes", "spec_verify_
            "spec_verify_attn_window", "spec_kv_commit",
            "spec_reject_sample", "spec_reject_sample_workspace_bytes", "spec_reject_sample_noalloc",
            "spec_reject_sample_filtered", "spec_reject_sample_tree", "spec_reject_sample_tree_workspace_bytes",
-           "spec_reject_sample_tree_filtered",
+           "spec_reject_sample_tree_filtered", "spec_reject_sample_trees",
            "spec_pages_create", "spec_pages_destroy", "spec_pages_reserve", "spec_pages_commit",
            "spec_pages_release", "spec_pages_free_count", "spec_pages_seq_blocks",
            "spec_pages_block_table", "spec_pages_check",
@@ -97,6 +97,9 @@ def load():
     lib.spec_reject_sample_tree_filtered.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                      vp, i32, i32, i32, i32, vp, sz, vp]
     lib.spec_reject_sample_tree_filtered.restype = i32
+    lib.spec_reject_sample_trees.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                             i32, i32, i32, i32, vp, sz, vp]
+    lib.spec_reject_sample_trees.restype = i32
     lib.spec_reject_sample_tree_workspace_bytes.argtypes = [i32, i32, i32]
     lib.spec_reject_sample_tree_workspace_bytes.restype = sz
     lib.spec_verify_attn_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
@@ -433,6 +436,45 @@ def reject_sample_noalloc(target, draft, draft_tokens, uniforms, temperature, kv
     return out_tokens, num_accepted
 
 
+def _tree_inputs(target, draft, tokens, uniforms, temperature, kv_len, out_tokens, out_nodes,
+                 num_accepted, counters, top_k, top_p, parents=None):
+    """Shape and dtype checks shared by the tree calls; (B, N, V, dtype code)."""
+    import torch
+    _need(target, "target")
+    dt = _dtype_code(target)
+    _dims(target, "target", 3)
+    B, N, V = target.shape
+    if draft is not None:
+        _need(draft, "draft", target.dtype, (B, N, V))
+    _need(tokens, "tokens", torch.int32, (B, N))
+    _need(uniforms, "uniforms", torch.float32, (B, N))
+    _need(temperature, "temperature", torch.float32, (B,))
+    _need(kv_len, "kv_len", torch.int32, (B,))
+    if parents is not None:
+        _need(parents, "parents", torch.int32, (B, N))
+    if out_nodes is not None:
+        _need(out_nodes, "out_nodes", torch.int32, (B, N))
+    if out_tokens is not None:
+        _need(out_tokens, "out_tokens", torch.int32, (B, N))
+    if num_accepted is not None:
+        _need(num_accepted, "num_accepted", torch.int32, (B,))
+    if counters is not None:
+        _need(counters, "counters", torch.int64, (2,))
+    if top_k is not None:
+        _need(top_k, "top_k", torch.int32, (B,))
+    if top_p is not None:
+        _need(top_p, "top_p", torch.float32, (B,))
+    return B, N, V, dt
+
+
+def _tree_outputs(B, N, device, out_tokens, out_nodes, num_accepted, counters):
+    import torch
+    out_tokens, num_accepted = _reject_outputs(B, N, device, out_tokens, num_accepted, counters)
+    if out_nodes is None:
+        out_nodes = torch.empty((B, N), dtype=torch.int32, device=device)
+    return out_tokens, out_nodes, num_accepted
+
+
 def reject_sample_tree(target, draft, parent, tokens, uniforms, temperature, kv_len,
                        out_tokens=None, out_nodes=None, num_accepted=None, counters=None,
                        workspace=None, stream=None, top_k=None, top_p=None):
@@ -447,30 +489,9 @@ def reject_sample_tree(target, draft, parent, tokens, uniforms, temperature, kv_
     in place to kv_len + n + 1.
     Returns (out_tokens [B, N], out_nodes [B, N], num_accepted [B]), int32.
     """
-    import torch
     lib = load()
-    _need(target, "target")
-    dt = _dtype_code(target)
-    _dims(target, "target", 3)
-    B, N, V = target.shape
-    if draft is not None:
-        _need(draft, "draft", target.dtype, (B, N, V))
-    _need(tokens, "tokens", torch.int32, (B, N))
-    _need(uniforms, "uniforms", torch.float32, (B, N))
-    _need(temperature, "temperature", torch.float32, (B,))
-    _need(kv_len, "kv_len", torch.int32, (B,))
-    if out_nodes is not None:
-        _need(out_nodes, "out_nodes", torch.int32, (B, N))
-    if out_tokens is not None:
-        _need(out_tokens, "out_tokens", torch.int32, (B, N))
-    if num_accepted is not None:
-        _need(num_accepted, "num_accepted", torch.int32, (B,))
-    if counters is not None:
-        _need(counters, "counters", torch.int64, (2,))
-    if top_k is not None:
-        _need(top_k, "top_k", torch.int32, (B,))
-    if top_p is not None:
-        _need(top_p, "top_p", torch.float32, (B,))
+    B, N, V, dt = _tree_inputs(target, draft, tokens, uniforms, temperature, kv_len, out_tokens,
+                               out_nodes, num_accepted, counters, top_k, top_p)
     par = [int(x) for x in parent]
     if len(par) != N:
         raise ValueError("parent must have N = %d entries" % N)
@@ -478,10 +499,8 @@ def reject_sample_tree(target, draft, parent, tokens, uniforms, temperature, kv_
             temperature=temperature, kv_len=kv_len, out_tokens=out_tokens, out_nodes=out_nodes,
             num_accepted=num_accepted, counters=counters, top_k=top_k, top_p=top_p)
     c_par = (ctypes.c_int32 * N)(*par)
-    out_tokens, num_accepted = _reject_outputs(B, N, target.device, out_tokens, num_accepted,
-                                               counters)
-    if out_nodes is None:
-        out_nodes = torch.empty((B, N), dtype=torch.int32, device=target.device)
+    out_tokens, out_nodes, num_accepted = _tree_outputs(B, N, target.device, out_tokens, out_nodes,
+                                                        num_accepted, counters)
     ws_bytes = reject_sample_tree_workspace_bytes(B, N, V)
     workspace, ws_have = _workspace(workspace, ws_bytes, target.device)
     if top_k is not None or top_p is not None:
@@ -498,6 +517,32 @@ def reject_sample_tree(target, draft, parent, tokens, uniforms, temperature, kv_
                                      _ptr(kv_len), _ptr(counters), B, N, V, dt, _ptr(workspace),
                                      ws_have, _stream(stream))
     _check("spec_reject_sample_tree", st)
+    return out_tokens, out_nodes, num_accepted
+
+
+def reject_sample_trees(target, draft, parents, tokens, uniforms, temperature, kv_len,
+                        out_tokens=None, out_nodes=None, num_accepted=None, counters=None,
+                        workspace=None, stream=None, top_k=None, top_p=None):
+    """The tree verifier with one tree per sequence (see ``spec_reject_sample_trees``):
+    parents [B, N] int32 on the device, parents[b][0] = -1 and
+    parents[b][i] < i.  Everything else as ``reject_sample_tree``.
+    Returns (out_tokens [B, N], out_nodes [B, N], num_accepted [B]), int32.
+    """
+    lib = load()
+    B, N, V, dt = _tree_inputs(target, draft, tokens, uniforms, temperature, kv_len, out_tokens,
+                               out_nodes, num_accepted, counters, top_k, top_p, parents=parents)
+    _on_gpu(target=target, draft=draft, parents=parents, tokens=tokens, uniforms=uniforms,
+            temperature=temperature, kv_len=kv_len, out_tokens=out_tokens, out_nodes=out_nodes,
+            num_accepted=num_accepted, counters=counters, top_k=top_k, top_p=top_p)
+    out_tokens, out_nodes, num_accepted = _tree_outputs(B, N, target.device, out_tokens, out_nodes,
+                                                        num_accepted, counters)
+    ws_bytes = reject_sample_tree_workspace_bytes(B, N, V)
+    workspace, ws_have = _workspace(workspace, ws_bytes, target.device)
+    st = lib.spec_reject_sample_trees(
+        _ptr(target), _ptr(draft), _ptr(parents), _ptr(tokens), _ptr(uniforms), _ptr(temperature),
+        _ptr(top_k), _ptr(top_p), _ptr(out_tokens), _ptr(out_nodes), _ptr(num_accepted),
+        _ptr(kv_len), _ptr(counters), B, N, V, dt, _ptr(workspace), ws_have, _stream(stream))
+    _check("spec_reject_sample_trees", st)
     return out_tokens, out_nodes, num_accepted
 
 

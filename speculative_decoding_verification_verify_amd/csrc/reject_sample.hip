@@ -56,6 +56,9 @@
 // by the step after it (run by the workgroup that completes the sequence's
 // pass, from chunk sums handed over without fences, as below); the host
 // knows from the tree's shape how many rounds the longest walk can take.
+// With one tree per sequence (parents on the device), k_tree_shapes first
+// builds each sequence's shape in the workspace, the kernels read it from
+// there, and the host launches the most rounds an N-node tree can need.
 // No floating-point atomics and fixed reduction orders: results are bitwise
 // reproducible run to run.
 
@@ -183,6 +186,7 @@ struct TreeState {
 struct ChainRows {
   int K;
   __device__ __forceinline__ int count() const { return 2 * K + 1; }
+  __device__ __forceinline__ bool valid(int, int) const { return true; }
   __device__ __forceinline__ bool is_draft(int j) const { return j > K; }
   __device__ __forceinline__ int n_target() const { return K + 1; }
   __device__ __forceinline__ size_t row(int b, int j) const {
@@ -201,6 +205,7 @@ struct ChainRows {
 struct TreeRows {
   TreeShape s;
   __device__ __forceinline__ int count() const { return s.n + s.n_int; }
+  __device__ __forceinline__ bool valid(int, int) const { return true; }
   __device__ __forceinline__ bool is_draft(int j) const { return j >= s.n; }
   __device__ __forceinline__ int n_target() const { return s.n; }
   __device__ __forceinline__ int node(int j) const {
@@ -212,6 +217,30 @@ struct TreeRows {
     const int v = node(j);
     for (int k = arg_byte(s.kid_off, v); k < arg_byte(s.kid_off, v + 1); ++k)
       f((size_t)b * s.n + arg_byte(s.kids, k));
+  }
+};
+
+// A shape per sequence (shapes[b], built on the device): the same row order
+// with room for N - 1 draft rows per sequence; the rows past a sequence's
+// own count are not swept.  Lookups read the shape's words from memory (b
+// and j are uniform in a workgroup: scalar loads).
+struct TreeRowsSeq {
+  const TreeShape* shapes;
+  int N;
+  __device__ __forceinline__ int count() const { return 2 * N - 1; }
+  __device__ __forceinline__ bool valid(int b, int j) const { return j < N || j - N < shapes[b].n_int; }
+  __device__ __forceinline__ bool is_draft(int j) const { return j >= N; }
+  __device__ __forceinline__ int n_target() const { return N; }
+  __device__ __forceinline__ int node(int b, int j) const {
+    return j < N ? j : arg_byte(shapes[b].int_node, j - N);
+  }
+  __device__ __forceinline__ size_t row(int b, int j) const { return (size_t)b * N + node(b, j); }
+  template <class F>
+  __device__ __forceinline__ void for_each_token(int b, int j, F&& f) const {
+    const TreeShape& s = shapes[b];
+    const int v = node(b, j);
+    for (int k = arg_byte(s.kid_off, v); k < arg_byte(s.kid_off, v + 1); ++k)
+      f((size_t)b * N + arg_byte(s.kids, k));
   }
 };
 
@@ -369,6 +398,7 @@ __global__ __launch_bounds__(kThreads) void k_sweep(
   // sequence's temperature; a target row is read whatever it is, and its
   // loads are issued before the temperature arrives.
   if (is_draft && !(temp_of(temp, b, force_greedy) > 0.f)) return;
+  if (!rows.valid(b, j)) return;                 // a per-sequence shape with fewer rows
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int chunk = blockIdx.y * 4 + wave;
@@ -908,6 +938,7 @@ __global__ __launch_bounds__(kFilterThreads, 4) void k_filter(
   const int b = row / R;
   const int j = row - b * R;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (!rows.valid(b, j)) return;                 // a per-sequence shape with fewer rows
   const float t = temp_of(temp, b, force_greedy);
   const int tk = top_k ? top_k[b] : 0;
   const float tp = top_p ? top_p[b] : 1.f;
@@ -1818,7 +1849,8 @@ __device__ void tree_walk(int b, int v, int n, const TreeShape& s, RS rs, const 
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kDecideThreads) void k_tree_decide(
     const int32_t* __restrict__ tok, const float* __restrict__ uni, const float* __restrict__ temp,
-    TreeShape s, int V, int nc, int force_greedy, const float2* __restrict__ part,
+    TreeShape s, const TreeShape* __restrict__ shapes, int RS, int V, int nc, int force_greedy,
+    const float2* __restrict__ part,
     const RowFilter* __restrict__ filt, int key16, float* __restrict__ xd,
     float2* __restrict__ rowstat, Decision* __restrict__ dec, TreeState* __restrict__ state,
     int32_t* __restrict__ out_tok, int32_t* __restrict__ out_node, int32_t* __restrict__ nacc,
@@ -1829,11 +1861,14 @@ __global__ __launch_bounds__(kDecideThreads) void k_tree_decide(
   __shared__ int s_tk[kMaxTree];
   __shared__ int s_n, s_tok;
   // The shape's tables in LDS: the walk looks them up with per-thread indices.
+  // shapes: one per sequence (then s gives N only); RS: the rows per
+  // sequence in part / rowstat / filt (a per-sequence shape may use fewer:
+  // the statistics of the others are merged but never read).
   __shared__ TreeShape s_sh;
-  if (threadIdx.x == 0) s_sh = s;
   const int b = blockIdx.x;
+  if (threadIdx.x == 0) s_sh = shapes ? shapes[b] : s;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int N = s.n, R = s.n + s.n_int;
+  const int N = s.n, R = RS;
   const float t = temp_of(temp, b, force_greedy);
   const bool greedy = !(t > 0.f);
   const int rows = greedy ? N : R;
@@ -1923,7 +1958,7 @@ __global__ __launch_bounds__(kDecideThreads) void k_tree_decide(
 template <bool kAgent>
 __device__ __forceinline__ void tree_step(
     int b, const int32_t* __restrict__ tok, const float* __restrict__ uni, const float* __restrict__ temp,
-    const TreeShape& s, int ncr, int force_greedy, int last, const float2* __restrict__ rowstat,
+    const TreeShape& s, int RS, int ncr, int force_greedy, int last, const float2* __restrict__ rowstat,
     const RowFilter* __restrict__ filt, const float* __restrict__ xd,
     const ChunkSums* __restrict__ csum, Decision* __restrict__ dec, TreeState* __restrict__ state,
     int32_t* __restrict__ out_tok, int32_t* __restrict__ out_node, int32_t* __restrict__ nacc) {
@@ -1933,7 +1968,7 @@ __device__ __forceinline__ void tree_step(
   __shared__ int s_tk[kMaxTree];
   __shared__ int s_draw, s_n;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int N = s.n, R = s.n + s.n_int;
+  const int N = s.n, R = RS;
   // The walk's inputs, loaded together with the decision (one round trip).
   if (tid < R) {
     s_rs[tid] = rowstat[(size_t)b * R + tid];
@@ -2039,8 +2074,9 @@ __device__ __forceinline__ void tree_step(
 template <typename T, bool kAligned, bool kMask>
 __global__ __launch_bounds__(kThreads, 4) void k_tree_round(
     const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ tok,
-    const float* __restrict__ uni, const float* __restrict__ temp, TreeShape s, int V, int ncr,
-    int force_greedy, int last, const float2* __restrict__ rowstat,
+    const float* __restrict__ uni, const float* __restrict__ temp, TreeShape s,
+    const TreeShape* __restrict__ shapes, int RS, int V, int ncr, int force_greedy, int last,
+    const float2* __restrict__ rowstat,
     const RowFilter* __restrict__ filt, const float* __restrict__ xd,
     ChunkSums* __restrict__ csum, SubSums* __restrict__ csub, Decision* __restrict__ dec,
     TreeState* __restrict__ state, unsigned* __restrict__ rcnt, int32_t* __restrict__ out_tok,
@@ -2061,9 +2097,9 @@ __global__ __launch_bounds__(kThreads, 4) void k_tree_round(
   // The shape's tables in LDS for the step (its walk indexes them per
   // thread; from the kernel arguments each lookup would be a memory load).
   __shared__ TreeShape s_sh;
-  if (threadIdx.x == 0) s_sh = s;
+  if (threadIdx.x == 0) s_sh = shapes ? shapes[b] : s;
   __syncthreads();
-  tree_step<true>(b, tok, uni, temp, s_sh, ncr, force_greedy, last, rowstat, filt, xd, csum, dec,
+  tree_step<true>(b, tok, uni, temp, s_sh, RS, ncr, force_greedy, last, rowstat, filt, xd, csum, dec,
                   state, out_tok, out_node, nacc);
 }
 
@@ -2167,7 +2203,7 @@ static hipError_t launch_all(const void* tgt, const void* drf, const int32_t* dt
 // merged row statistics and the walk states.
 struct TreePlan {
   size_t part_off, rowstat_off, csum_off, csub_off, dec_off, state_off, xd_off, rcnt_off, filt_off,
-      total;
+      shape_off, total;
 };
 
 static inline TreePlan tree_plan(int B, int N, int V) {
@@ -2183,8 +2219,46 @@ static inline TreePlan tree_plan(int B, int N, int V) {
   p.xd_off = p.state_off + up((size_t)B * sizeof(TreeState));
   p.rcnt_off = p.xd_off + up((size_t)B * N * 2 * sizeof(float));
   p.filt_off = p.rcnt_off + up((size_t)B * sizeof(unsigned));
-  p.total = p.filt_off + up((size_t)B * R * sizeof(RowFilter));
+  p.shape_off = p.filt_off + up((size_t)B * R * sizeof(RowFilter));
+  p.total = p.shape_off + up((size_t)B * sizeof(TreeShape));   // shapes: one per sequence
   return p;
+}
+
+// grid (ceil(B / 64)), block 64: sequence b's shape from its parent list
+// parents[b] (one thread per sequence, tables built in LDS as on the host);
+// a parent outside [0, i) is read as i - 1.
+__global__ __launch_bounds__(64) void k_tree_shapes(const int32_t* __restrict__ parents, int B, int N,
+                                                   TreeShape* __restrict__ shapes) {
+  __shared__ TreeShape s_sh[64];
+  __shared__ int8_t s_par[64][kMaxTree], s_fill[64][kMaxTree + 1];
+  const int t = threadIdx.x, b = blockIdx.x * 64 + t;
+  if (b >= B) return;
+  TreeShape& s = s_sh[t];
+  int8_t* par = s_par[t];
+  int8_t* fill = s_fill[t];
+  s = TreeShape{};
+  s.n = N;
+  for (int v = 0; v <= N; ++v) fill[v] = 0;
+  par[0] = -1;
+  for (int i = 1; i < N; ++i) {
+    int pi = parents[(size_t)b * N + i];
+    if (pi < 0 || pi >= i) pi = i - 1;
+    par[i] = (int8_t)pi;
+    ++fill[pi];
+  }
+  s.kid_off[0] = 0;
+  for (int v = 0; v < N; ++v) s.kid_off[v + 1] = (int8_t)(s.kid_off[v] + fill[v]);
+  for (int v = 0; v < N; ++v) fill[v] = s.kid_off[v];
+  for (int i = 1; i < N; ++i) s.kids[fill[par[i]]++] = (int8_t)i;   // increasing index order
+  s.n_int = 0;
+  for (int v = 0; v < N; ++v) {
+    s.int_idx[v] = -1;
+    if (s.kid_off[v + 1] > s.kid_off[v]) {
+      s.int_idx[v] = (int8_t)s.n_int;
+      s.int_node[s.n_int++] = (int8_t)v;
+    }
+  }
+  shapes[b] = s;
 }
 
 // Children lists of parent[] (parent[0] = -1, 0 <= parent[i] < i).
@@ -2224,16 +2298,23 @@ static int tree_rounds(const TreeShape& s, int v) {
   return best;
 }
 
+// shape: the batch's tree; or, with dparents ([B, N] device array), one tree
+// per sequence (shape.n = N only), built on the device, the rows laid out
+// for 2N - 1 per sequence, and N - 1 rounds (the most any tree of N nodes
+// needs: a root with N - 1 children; a sequence whose walk has ended skips
+// the rest).
 template <typename T, bool kAligned>
 static hipError_t launch_tree(const void* tgt, const void* drf, const TreeShape& shape,
-                              const int32_t* tok, const float* uni, const float* temp,
-                              int32_t* out_tok, int32_t* out_node, int32_t* nacc, int32_t* kv_len,
-                              unsigned long long* counters, int B, int V, int force_greedy, char* ws,
-                              hipStream_t st, const int32_t* top_k, const float* top_p) {
+                              const int32_t* dparents, const int32_t* tok, const float* uni,
+                              const float* temp, int32_t* out_tok, int32_t* out_node, int32_t* nacc,
+                              int32_t* kv_len, unsigned long long* counters, int B, int V,
+                              int force_greedy, char* ws, hipStream_t st, const int32_t* top_k,
+                              const float* top_p) {
   const int N = shape.n;
   const int nc = sweep_chunks(V);
   const int ncr = res_chunks(V);
-  const int R = shape.n + shape.n_int;
+  const bool per_seq = dparents != nullptr;
+  const int R = per_seq ? 2 * N - 1 : shape.n + shape.n_int;
   const TreePlan p = tree_plan(B, N, V);
   float2* part = reinterpret_cast<float2*>(ws + p.part_off);
   float2* rowstat = reinterpret_cast<float2*>(ws + p.rowstat_off);
@@ -2243,30 +2324,41 @@ static hipError_t launch_tree(const void* tgt, const void* drf, const TreeShape&
   TreeState* state = reinterpret_cast<TreeState*>(ws + p.state_off);
   float* xd = reinterpret_cast<float*>(ws + p.xd_off);
   unsigned* rcnt = reinterpret_cast<unsigned*>(ws + p.rcnt_off);
+  TreeShape* shapes = per_seq ? reinterpret_cast<TreeShape*>(ws + p.shape_off) : nullptr;
   const T* t = static_cast<const T*>(tgt);
   const T* d = static_cast<const T*>(drf);
-  hipLaunchKernelGGL((k_sweep<T, kAligned, TreeRows>), dim3(B * R, (nc + 3) / 4), dim3(kThreads), 0,
-                     st, t, d, tok, temp, TreeRows{shape}, B, V, nc, force_greedy, part, xd, rcnt);
+  if (per_seq) {
+    hipLaunchKernelGGL(k_tree_shapes, dim3((B + 63) / 64), dim3(64), 0, st, dparents, B, N, shapes);
+    hipLaunchKernelGGL((k_sweep<T, kAligned, TreeRowsSeq>), dim3(B * R, (nc + 3) / 4), dim3(kThreads), 0,
+                       st, t, d, tok, temp, TreeRowsSeq{shapes, N}, B, V, nc, force_greedy, part, xd,
+                       rcnt);
+  } else {
+    hipLaunchKernelGGL((k_sweep<T, kAligned, TreeRows>), dim3(B * R, (nc + 3) / 4), dim3(kThreads), 0,
+                       st, t, d, tok, temp, TreeRows{shape}, B, V, nc, force_greedy, part, xd, rcnt);
+  }
   // Filters: thresholds and kept masses per swept row, as for the chain.
   const bool filtered = (top_k || top_p) && !force_greedy;
   RowFilter* filt = filtered ? reinterpret_cast<RowFilter*>(ws + p.filt_off) : nullptr;
-  if (filtered)
+  if (filtered && per_seq)
+    hipLaunchKernelGGL((k_filter<T, kAligned, TreeRowsSeq>), dim3(B * R), dim3(kFilterThreads), 0, st,
+                       t, d, temp, top_k, top_p, TreeRowsSeq{shapes, N}, V, nc, force_greedy, part, filt);
+  else if (filtered)
     hipLaunchKernelGGL((k_filter<T, kAligned, TreeRows>), dim3(B * R), dim3(kFilterThreads), 0, st, t,
                        d, temp, top_k, top_p, TreeRows{shape}, V, nc, force_greedy, part, filt);
   const int key16 = sizeof(T) == 2 ? 1 : 0;
-  hipLaunchKernelGGL(k_tree_decide, dim3(B), dim3(kDecideThreads), 0, st, tok, uni, temp, shape, V, nc,
-                     force_greedy, part, filt, key16, xd, rowstat, dec, state, out_tok, out_node, nacc,
-                     kv_len, counters);
-  const int rounds = force_greedy ? 0 : tree_rounds(shape, 0);
+  hipLaunchKernelGGL(k_tree_decide, dim3(B), dim3(kDecideThreads), 0, st, tok, uni, temp, shape, shapes,
+                     R, V, nc, force_greedy, part, filt, key16, xd, rowstat, dec, state, out_tok,
+                     out_node, nacc, kv_len, counters);
+  const int rounds = force_greedy ? 0 : per_seq ? std::max(1, N - 1) : tree_rounds(shape, 0);
   for (int r = 1; r <= rounds; ++r) {
     if (filtered)
       hipLaunchKernelGGL((k_tree_round<T, kAligned, true>), dim3(B, ncr), dim3(kThreads), 0, st, t, d,
-                         tok, uni, temp, shape, V, ncr, force_greedy, r == rounds ? 1 : 0, rowstat, filt,
-                         xd, csum, csub, dec, state, rcnt, out_tok, out_node, nacc);
+                         tok, uni, temp, shape, shapes, R, V, ncr, force_greedy, r == rounds ? 1 : 0,
+                         rowstat, filt, xd, csum, csub, dec, state, rcnt, out_tok, out_node, nacc);
     else
       hipLaunchKernelGGL((k_tree_round<T, kAligned, false>), dim3(B, ncr), dim3(kThreads), 0, st, t, d,
-                         tok, uni, temp, shape, V, ncr, force_greedy, r == rounds ? 1 : 0, rowstat,
-                         filt, xd, csum, csub, dec, state, rcnt, out_tok, out_node, nacc);
+                         tok, uni, temp, shape, shapes, R, V, ncr, force_greedy, r == rounds ? 1 : 0,
+                         rowstat, filt, xd, csum, csub, dec, state, rcnt, out_tok, out_node, nacc);
   }
   if (rounds > 0)
     hipLaunchKernelGGL((k_tree_draw<T>), dim3(B), dim3(kThreads), 0, st, t, d, uni, temp, shape.n, V,
@@ -2433,17 +2525,21 @@ extern "C" size_t spec_reject_sample_tree_workspace_bytes(int B, int N, int V) {
   return sv::tree_plan(B, N, V).total;
 }
 
+// per_seq false: parent is the batch's tree (host array); true: dparents
+// holds one per sequence ([B, N] device array, NULL only for B == 0).
 static int tree_impl(const char* fn, const void* target_logits, const void* draft_logits,
-                     const int32_t* parent, const int32_t* tokens, const float* uniforms,
-                     const float* temperature, const int32_t* top_k, const float* top_p,
-                     int32_t* out_tokens, int32_t* out_nodes, int32_t* num_accepted, int32_t* kv_len,
-                     unsigned long long* counters, int B, int N, int V, int dtype, void* workspace,
-                     size_t workspace_bytes, void* hip_stream) {
-  if (B < 0 || N < 1 || V < 1 || !parent) return SV_ERR_INVALID_ARG;
+                     bool per_seq, const int32_t* parent, const int32_t* dparents,
+                     const int32_t* tokens, const float* uniforms, const float* temperature,
+                     const int32_t* top_k, const float* top_p, int32_t* out_tokens, int32_t* out_nodes,
+                     int32_t* num_accepted, int32_t* kv_len, unsigned long long* counters, int B, int N,
+                     int V, int dtype, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (B < 0 || N < 1 || V < 1) return SV_ERR_INVALID_ARG;
+  if (per_seq ? (B > 0 && !dparents) : !parent) return SV_ERR_INVALID_ARG;
   if (dtype != SV_F32 && dtype != SV_BF16) return SV_ERR_INVALID_ARG;
   if (N > sv::kMaxTree) return SV_ERR_UNSUPPORTED;
-  sv::TreeShape shape;
-  if (!sv::build_shape(parent, N, shape)) return SV_ERR_INVALID_ARG;
+  sv::TreeShape shape{};
+  shape.n = N;
+  if (!per_seq && !sv::build_shape(parent, N, shape)) return SV_ERR_INVALID_ARG;
   if ((long long)V >= (1LL << 31) / 4) return SV_ERR_UNSUPPORTED;
   if ((long long)B * (2 * N - 1) > 0x7fffffffLL || (sv::sweep_chunks(V) + 3) / 4 > 65535 ||
       sv::res_chunks(V) > 65535)
@@ -2470,25 +2566,26 @@ static int tree_impl(const char* fn, const void* target_logits, const void* draf
       s = sv::check_logits(fn, "target_logits", target_logits, (long long)B * N, V, dtype, st);
     if (s == SV_OK && draft_logits)
       s = sv::check_logits(fn, "draft_logits", draft_logits, (long long)B * N, V, dtype, st);
+    if (s == SV_OK && dparents) s = sv::check_parents(fn, dparents, B, N, st);
     if (s != SV_OK) return s;
   }
   hipError_t e;
   if (dtype == SV_BF16) {
     const bool al = (V % 8 == 0) && (align_bits & 15) == 0;
-    e = al ? sv::launch_tree<uint16_t, true>(target_logits, drf, shape, tokens, uniforms, temperature,
-                                             out_tokens, out_nodes, num_accepted, kv_len, counters, B,
-                                             V, force_greedy, ws, st, top_k, top_p)
-           : sv::launch_tree<uint16_t, false>(target_logits, drf, shape, tokens, uniforms, temperature,
-                                              out_tokens, out_nodes, num_accepted, kv_len, counters, B,
-                                              V, force_greedy, ws, st, top_k, top_p);
+    e = al ? sv::launch_tree<uint16_t, true>(target_logits, drf, shape, dparents, tokens, uniforms,
+                                             temperature, out_tokens, out_nodes, num_accepted, kv_len,
+                                             counters, B, V, force_greedy, ws, st, top_k, top_p)
+           : sv::launch_tree<uint16_t, false>(target_logits, drf, shape, dparents, tokens, uniforms,
+                                              temperature, out_tokens, out_nodes, num_accepted, kv_len,
+                                              counters, B, V, force_greedy, ws, st, top_k, top_p);
   } else {
     const bool al = (V % 4 == 0) && (align_bits & 15) == 0;
-    e = al ? sv::launch_tree<float, true>(target_logits, drf, shape, tokens, uniforms, temperature,
-                                          out_tokens, out_nodes, num_accepted, kv_len, counters, B, V,
-                                          force_greedy, ws, st, top_k, top_p)
-           : sv::launch_tree<float, false>(target_logits, drf, shape, tokens, uniforms, temperature,
-                                           out_tokens, out_nodes, num_accepted, kv_len, counters, B, V,
-                                           force_greedy, ws, st, top_k, top_p);
+    e = al ? sv::launch_tree<float, true>(target_logits, drf, shape, dparents, tokens, uniforms,
+                                          temperature, out_tokens, out_nodes, num_accepted, kv_len,
+                                          counters, B, V, force_greedy, ws, st, top_k, top_p)
+           : sv::launch_tree<float, false>(target_logits, drf, shape, dparents, tokens, uniforms,
+                                           temperature, out_tokens, out_nodes, num_accepted, kv_len,
+                                           counters, B, V, force_greedy, ws, st, top_k, top_p);
   }
   const int status = e == hipSuccess ? SV_OK : SV_ERR_HIP;
   return chk ? sv::finish(fn, st, status) : status;
@@ -2501,7 +2598,8 @@ extern "C" int spec_reject_sample_tree(const void* target_logits, const void* dr
                                        int32_t* num_accepted, int32_t* kv_len,
                                        unsigned long long* counters, int B, int N, int V, int dtype,
                                        void* workspace, size_t workspace_bytes, void* hip_stream) {
-  return tree_impl("spec_reject_sample_tree", target_logits, draft_logits, parent, tokens, uniforms,
+  return tree_impl("spec_reject_sample_tree", target_logits, draft_logits, false, parent, nullptr,
+                   tokens, uniforms,
                    temperature, nullptr, nullptr, out_tokens, out_nodes, num_accepted, kv_len,
                    counters, B, N, V, dtype, workspace, workspace_bytes, hip_stream);
 }
@@ -2512,7 +2610,18 @@ extern "C" int spec_reject_sample_tree_filtered(
     const float* top_p, int32_t* out_tokens, int32_t* out_nodes, int32_t* num_accepted,
     int32_t* kv_len, unsigned long long* counters, int B, int N, int V, int dtype, void* workspace,
     size_t workspace_bytes, void* hip_stream) {
-  return tree_impl("spec_reject_sample_tree_filtered", target_logits, draft_logits, parent, tokens,
-                   uniforms, temperature, top_k, top_p, out_tokens, out_nodes, num_accepted, kv_len,
-                   counters, B, N, V, dtype, workspace, workspace_bytes, hip_stream);
+  return tree_impl("spec_reject_sample_tree_filtered", target_logits, draft_logits, false, parent, nullptr,
+                   tokens, uniforms, temperature, top_k, top_p, out_tokens, out_nodes, num_accepted,
+                   kv_len, counters, B, N, V, dtype, workspace, workspace_bytes, hip_stream);
+}
+
+extern "C" int spec_reject_sample_trees(
+    const void* target_logits, const void* draft_logits, const int32_t* parents,
+    const int32_t* tokens, const float* uniforms, const float* temperature, const int32_t* top_k,
+    const float* top_p, int32_t* out_tokens, int32_t* out_nodes, int32_t* num_accepted,
+    int32_t* kv_len, unsigned long long* counters, int B, int N, int V, int dtype, void* workspace,
+    size_t workspace_bytes, void* hip_stream) {
+  return tree_impl("spec_reject_sample_trees", target_logits, draft_logits, true, nullptr, parents,
+                   tokens, uniforms, temperature, top_k, top_p, out_tokens, out_nodes, num_accepted,
+                   kv_len, counters, B, N, V, dtype, workspace, workspace_bytes, hip_stream);
 }

@@ -187,6 +187,24 @@ int check_tokens(const char* fn, const int32_t* tok, long long n, int V, int str
   return SV_OK;
 }
 
+int check_parents(const char* fn, const int32_t* parents, int B, int N, hipStream_t st) {
+  if (!drain(fn, st)) return SV_ERR_HIP;
+  std::vector<int32_t> p;
+  if (!fetch(fn, parents, (long long)B * N, p)) return SV_ERR_HIP;
+  char msg[256];
+  for (int b = 0; b < B; ++b)
+    for (int i = 0; i < N; ++i) {
+      const int32_t v = p[(size_t)b * N + i];
+      if (i == 0 ? v != -1 : (v < 0 || v >= i)) {
+        std::snprintf(msg, sizeof msg, "parents[%d][%d] = %d: %s", b, i, v,
+                      i == 0 ? "the root's parent must be -1" : "a parent must precede its node");
+        fail(fn, msg);
+        return SV_ERR_BAD_INPUT;
+      }
+    }
+  return SV_OK;
+}
+
 int check_floats(const char* fn, const char* name, const float* x, long long n, bool unit,
                  hipStream_t st) {
   if (!drain(fn, st)) return SV_ERR_HIP;

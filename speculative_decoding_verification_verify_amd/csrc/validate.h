@@ -43,6 +43,10 @@ int check_logits(const char* fn, const char* name, const void* x, long long rows
 int check_tokens(const char* fn, const int32_t* tok, long long n, int V, int stride, int skip,
                  hipStream_t st);
 
+// Parent lists [B, N] of trees in topological order: parents[b][0] = -1,
+// 0 <= parents[b][i] < i.
+int check_parents(const char* fn, const int32_t* parents, int B, int N, hipStream_t st);
+
 // Floats: unit = true, in [0, 1) (uniforms); false, finite (temperature,
 // top_p).
 int check_floats(const char* fn, const char* name, const float* x, long long n, bool unit,

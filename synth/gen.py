@@ -125,7 +125,8 @@ def make_reject_inputs(seed, B, K, V, dtype="bf16", logit_std=2.0,
 
 def make_tree_reject_inputs(seed, B, parent, V, dtype="bf16", logit_std=2.0,
                             draft_sigma=0.51, temperature=1.0, shared_rows=False):
-    """Inputs of one tree-verify call over the tree given by ``parent`` (N nodes).
+    """Inputs of one tree-verify call over the tree given by ``parent`` (N nodes):
+    one tree [N] for the batch, or one per sequence [B, N].
 
     Rows as in make_reject_inputs, one target and one draft row per node
     (target [B,N,V], draft [B,N,V]).  Node i's token is a fresh draw from
@@ -135,7 +136,8 @@ def make_tree_reject_inputs(seed, B, parent, V, dtype="bf16", logit_std=2.0,
     root's) is 0 and unused.  uniforms [B,N] float32.
     """
     par = np.asarray(parent, dtype=np.int64)
-    n = par.shape[0]
+    n = par.shape[-1]
+    par2 = np.broadcast_to(par, (B, n))
     ss = np.random.SeedSequence(seed)
     r_t, r_n, r_g, r_u = [np.random.default_rng(s) for s in ss.spawn(4)]
     temps = np.broadcast_to(np.asarray(temperature, dtype=np.float32), (B,)).copy()
@@ -149,21 +151,24 @@ def make_tree_reject_inputs(seed, B, parent, V, dtype="bf16", logit_std=2.0,
         tgt_e = np.broadcast_to(tgt_e, (B, n, V))
         drf_e = np.broadcast_to(drf_e, (B, n, V))
     toks = np.zeros((B, n), dtype=np.int32)
-    rank = np.zeros(n, dtype=np.int64)          # position of node i among its siblings
-    seen = {}
-    for i in range(1, n):
-        rank[i] = seen.get(int(par[i]), 0)
-        seen[int(par[i])] = rank[i] + 1
+    rank = np.zeros((B, n), dtype=np.int64)     # position of node i among its siblings
+    for b in range(B if par.ndim == 2 else 1):
+        seen = {}
+        for i in range(1, n):
+            rank[b, i] = seen.get(int(par2[b, i]), 0)
+            seen[int(par2[b, i])] = rank[b, i] + 1
+    if par.ndim == 1:
+        rank[1:] = rank[0]
     step = max(1, (1 << 22) // max(1, (n - 1) * V))
     for s0 in range(0, B, step):
         sel = np.arange(s0, min(B, s0 + step))
         vals = _decode(drf_e[sel], dtype).astype(np.float64)          # [S, N, V]
-        pv = vals[:, par[1:], :]                                      # [S, N-1, V]
+        pv = np.take_along_axis(vals, par2[sel, 1:, None], axis=1)    # [S, N-1, V]
         t = temps[sel].astype(np.float64)
         g = -np.log(-np.log(r_g.random(pv.shape) * (1 - 2e-16) + 1e-16))
         sampled = np.argmax(pv / np.where(t > 0, t, 1.0)[:, None, None] + g, axis=-1)
         order = np.argsort(-pv, axis=-1, kind="stable")               # greedy: top-k
-        greedy_tok = np.take_along_axis(order, rank[1:][None, :, None], axis=-1)[..., 0]
+        greedy_tok = np.take_along_axis(order, rank[sel, 1:, None], axis=-1)[..., 0]
         toks[sel, 1:] = np.where((t > 0)[:, None], sampled, greedy_tok)
     u = uniforms24(r_u, (B, n))
     return {"target": tgt_e, "draft": drf_e, "tokens": toks, "parent": par.astype(np.int32),

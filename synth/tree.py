@@ -8,7 +8,8 @@ node i's word is set iff node j is node i or one of its ancestors).
 
 import numpy as np
 
-__all__ = ["chain_parents", "tree_parents", "children", "ancestor_bits"]
+__all__ = ["chain_parents", "tree_parents", "random_parents", "mixed_parents", "children",
+           "ancestor_bits"]
 
 
 def chain_parents(n):
@@ -30,6 +31,31 @@ def tree_parents(shape):
                 nxt.append(len(parents) - 1)
         level = nxt
     return np.asarray(parents, dtype=np.int32)
+
+
+def random_parents(rng, n):
+    """parent[] of a random tree of n nodes in topological order: node i's
+    parent uniform over 0 .. i - 1."""
+    par = np.full(n, -1, dtype=np.int32)
+    for i in range(1, n):
+        par[i] = rng.integers(0, i)
+    return par
+
+
+def mixed_parents(seed, B, n):
+    """[B, n] parent arrays, one tree per sequence, cycling through a chain,
+    a star (the root's n - 1 children), a two-level tree (root with two
+    children, the rest spread under them) and a random tree."""
+    rng = np.random.default_rng(seed)
+    two = np.full(n, -1, dtype=np.int32)
+    for i in range(1, n):
+        two[i] = 0 if i <= 2 else 1 + (i - 3) % 2
+    out = np.empty((B, n), dtype=np.int32)
+    for b in range(B):
+        k = b % 4
+        out[b] = (chain_parents(n) if k == 0 else np.r_[-1, np.zeros(n - 1, np.int32)]
+                  if k == 1 else two if k == 2 else random_parents(rng, n))
+    return out
 
 
 def children(parent):

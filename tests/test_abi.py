@@ -180,6 +180,22 @@ def test_filtered_tree_reject_validation(lib):
     assert call(B=0, ptrs=False) == 0                            # an empty batch is a no-op
 
 
+def test_per_sequence_tree_reject_validation(lib):
+    """spec_reject_sample_trees: parents live on the device, so only their
+    presence is checked here (nothing is launched below)."""
+    def call(B=4, N=4, V=100, dtype=1, ws_bytes=1 << 24, parents=True, ptrs=True):
+        p = FAKE if ptrs else None
+        return lib.spec_reject_sample_trees(p, p, FAKE if parents else None, p, p, p, None, None, p,
+                                            p, p, p, None, B, N, V, dtype, p, ws_bytes, None)
+    need = sv.reject_sample_tree_workspace_bytes(4, 4, 100)
+    assert call(ws_bytes=need - 1) == -3
+    assert call(parents=False) == -1                          # B > 0 needs the parents
+    assert call(B=0, parents=False, ptrs=False) == 0          # empty batch: no-op
+    assert call(N=0) == -1 and call(V=0) == -1 and call(dtype=5) == -1 and call(B=-1) == -1
+    assert call(N=18) == -2
+    assert call(ptrs=False) == -1
+
+
 def test_tree_reject_workspace_matches_chain(lib):
     # A chain of K + 1 nodes sweeps the same 2K + 1 rows as the chain call;
     # the tree adds its walk state and merged row statistics, the chain its

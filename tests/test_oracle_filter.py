@@ -84,6 +84,27 @@ def test_filtered_verifier_is_lossless_for_the_filtered_target(top_k, top_p):
     assert 0.5 * np.abs(first - q).sum() < 0.01
 
 
+def test_filtered_trees_per_sequence_are_independent_calls():
+    # One tree per sequence: each sequence's filtered walk is its own
+    # one-sequence call (filters of its rows by its own shape).
+    from synth.tree import mixed_parents
+    B, N, V = 8, 6, 70
+    par = mixed_parents(31, B, N)
+    r = gen.make_tree_reject_inputs(31, B, par, V, dtype="bf16", draft_sigma=1.0,
+                                    temperature=np.array([1.0, 0.0, 0.9, 1.2] * 2, np.float32))
+    tk = np.array([0, 5, 20, 3, 0, 40, 7, 0], np.int64)
+    tp = np.array([0.9, 1.0, 0.8, 0.95, 1.0, 0.7, 1.0, 0.6])
+    batch = of.reject_sample_tree_filtered(r["target"], r["draft"], par, r["tokens"],
+                                            r["uniforms"], r["temperature"], tk, tp)
+    for b in range(B):
+        one = of.reject_sample_tree_filtered(r["target"][b:b + 1], r["draft"][b:b + 1], par[b],
+                                              r["tokens"][b:b + 1], r["uniforms"][b:b + 1],
+                                              r["temperature"][b:b + 1], tk[b:b + 1], tp[b:b + 1])
+        for k in ("out_tokens", "out_nodes", "num_accepted", "flag_accept", "flag_sample",
+                  "flag_filter"):
+            assert np.array_equal(batch[k][b], one[k][0]), (b, k)
+
+
 def test_f3_band_edges():
     # Masses 0.5, 0.3, 0.2 in value order: cumulative 0.5, 0.8, 1.0.  F3 flags
     # a row when top_p is within 1e-6 of the mass of the kept set or of the

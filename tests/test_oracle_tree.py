@@ -3,6 +3,8 @@
 Verifier:
   * a chain-shaped tree is exactly the chain verifier (itself pinned by
     brute-force enumeration, losslessness and the closed-form mean);
+  * one tree per sequence ([B, N] parents): each sequence is its own
+    one-sequence call, and the chain-shaped ones are the chain verifier;
   * losslessness: the first emitted token has the law q_root, and after the
     path descends into a child c the next emitted token has the law q_c
     (empirically, 2e5 trials at V = 16);
@@ -25,7 +27,7 @@ from oracle import reject as orj
 from oracle import tree as otr
 from oracle.reject import widen
 from synth import gen
-from synth.tree import ancestor_bits, chain_parents, children, tree_parents
+from synth.tree import ancestor_bits, chain_parents, children, mixed_parents, tree_parents
 
 
 def _probs(logits, t=1.0):
@@ -91,6 +93,51 @@ def test_chain_tree_is_the_chain_verifier(seed, B, K, V, temps):
     for b in range(B):
         m = tr["num_accepted"][b]
         assert nodes[b, :m].tolist() == list(range(1, m + 1))
+
+
+# --------------------------------------------------------------------------
+# One tree per sequence.
+# --------------------------------------------------------------------------
+
+_KEYS = ("out_tokens", "out_nodes", "num_accepted", "flag_accept", "flag_sample")
+
+
+@pytest.mark.parametrize("seed,B,N,V", [(11, 12, 8, 60), (12, 8, 5, 40)])
+def test_per_sequence_trees_are_independent_calls(seed, B, N, V):
+    par = mixed_parents(seed, B, N)
+    temps = np.array([1.0, 0.0, 0.7, 1.3] * (B // 4), np.float32)
+    r = gen.make_tree_reject_inputs(seed, B, par, V, dtype="bf16", draft_sigma=1.0,
+                                    temperature=temps)
+    batch = otr.reject_sample_tree(r["target"], r["draft"], par, r["tokens"], r["uniforms"],
+                                   r["temperature"])
+    for b in range(B):
+        one = otr.reject_sample_tree(r["target"][b:b + 1], r["draft"][b:b + 1], par[b],
+                                     r["tokens"][b:b + 1], r["uniforms"][b:b + 1],
+                                     r["temperature"][b:b + 1])
+        for k in _KEYS:
+            assert np.array_equal(batch[k][b], one[k][0]), (b, k)
+    # The shapes differ, so the walks do: stars never accept two nodes.
+    stars = [b for b in range(B) if (par[b, 1:] == 0).all()]
+    assert stars and all(batch["num_accepted"][b] <= 1 for b in stars)
+
+
+def test_chain_sequences_of_a_mixed_batch_are_the_chain_verifier():
+    B, N, V = 16, 8, 80
+    K = N - 1
+    par = mixed_parents(21, B, N)
+    r = gen.make_tree_reject_inputs(21, B, par, V, dtype="bf16", draft_sigma=1.0,
+                                    temperature=np.array([1.0, 0.8] * (B // 2), np.float32))
+    tr = otr.reject_sample_tree(r["target"], r["draft"], par, r["tokens"], r["uniforms"],
+                                r["temperature"])
+    rows = [b for b in range(B) if np.array_equal(par[b], chain_parents(N))]
+    assert len(rows) == B // 4
+    u = np.zeros((len(rows), N), np.float32)
+    u[:, :K] = r["uniforms"][rows, 1:]
+    u[:, K] = r["uniforms"][rows, 0]
+    chain = orj.reject_sample(r["target"][rows], r["draft"][rows, :K], r["tokens"][rows, 1:], u,
+                              r["temperature"][rows])
+    assert np.array_equal(tr["out_tokens"][rows], chain["out_tokens"])
+    assert np.array_equal(tr["num_accepted"][rows], chain["num_accepted"])
 
 
 # --------------------------------------------------------------------------
