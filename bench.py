@@ -233,21 +233,26 @@ def main():
             sv.verify_attn_tree(attn["q"], attn["k_cache"], attn["v_cache"], attn["block_table"],
                                 kv0, anc, out=attn_out, max_kv_len=max_kv, workspace=attn_ws)
 
+    # Greedy verification reads no draft logits: at T <= 0 none are passed (the
+    # library then knows every sequence is greedy and sizes its grids to it).
+    greedy_only = args.temp <= 0
+
     def reject_call(s, kv):
         r = rsets[s % args.sets]["dev"]
+        drf = None if greedy_only else r["draft"]
         if parent is None:
-            sv.reject_sample(r["target"], r["draft"], r["draft_tokens"], r["uniforms"],
+            sv.reject_sample(r["target"], drf, r["draft_tokens"], r["uniforms"],
                              r["temperature"], kv, out_tokens=out_tok[s % args.sets],
                              num_accepted=n_acc[s % args.sets], workspace=rej_ws,
                              top_k=filt_k, top_p=filt_p)
         elif par_dev is not None:
-            sv.reject_sample_trees(r["target"], r["draft"], par_dev, r["tokens"], r["uniforms"],
+            sv.reject_sample_trees(r["target"], drf, par_dev, r["tokens"], r["uniforms"],
                                    r["temperature"], kv, out_tokens=out_tok[s % args.sets],
                                    out_nodes=out_node[s % args.sets],
                                    num_accepted=n_acc[s % args.sets], workspace=rej_ws,
                                    top_k=filt_k, top_p=filt_p)
         else:
-            sv.reject_sample_tree(r["target"], r["draft"], parent, r["tokens"], r["uniforms"],
+            sv.reject_sample_tree(r["target"], drf, parent, r["tokens"], r["uniforms"],
                                   r["temperature"], kv, out_tokens=out_tok[s % args.sets],
                                   out_nodes=out_node[s % args.sets],
                                   num_accepted=n_acc[s % args.sets], workspace=rej_ws,

@@ -2166,8 +2166,12 @@ static hipError_t launch_all(const void* tgt, const void* drf, const int32_t* dt
   const T* t = static_cast<const T*>(tgt);
   const T* d = static_cast<const T*>(drf);
   unsigned* pcnt = reinterpret_cast<unsigned*>(ws + p.cnt_off);
-  hipLaunchKernelGGL((k_sweep<T, kAligned, ChainRows>), dim3(B * R, (nc + 3) / 4), dim3(kThreads), 0,
-                     st, t, d, dtok, temp, ChainRows{K}, B, V, nc, force_greedy, part, xd, pcnt);
+  // Without draft logits every sequence is greedy: the grid holds the target
+  // rows only (they come first in the sweep's order), and the decision one
+  // workgroup per sequence.
+  hipLaunchKernelGGL((k_sweep<T, kAligned, ChainRows>), dim3(B * (force_greedy ? K + 1 : R), (nc + 3) / 4),
+                     dim3(kThreads), 0, st, t, d, dtok, temp, ChainRows{K}, B, V, nc, force_greedy, part,
+                     xd, pcnt);
   const bool filtered = (top_k || top_p) && !force_greedy;
   RowFilter* filt = filtered ? reinterpret_cast<RowFilter*>(ws + p.filt_off) : nullptr;
   if (filtered)
@@ -2176,7 +2180,7 @@ static hipError_t launch_all(const void* tgt, const void* drf, const int32_t* dt
   const int key16 = sizeof(T) == 2 ? 1 : 0;
   // The draw joins the pass kernel while the chunk sums fit one wave.
   const bool fused = ncr <= 64;
-  const dim3 grid(B, ncr), block(kThreads);
+  const dim3 grid(B, force_greedy ? 1 : ncr), block(kThreads);
   if (filtered && fused)
     hipLaunchKernelGGL((k_decide_residual<T, kAligned, true, true>), grid, block, 0, st, t, d, dtok, uni,
                        temp, K, V, nc, ncr, force_greedy, part, xd, filt, key16, dec, out, nacc, kv_len,
@@ -2193,7 +2197,7 @@ static hipError_t launch_all(const void* tgt, const void* drf, const int32_t* dt
     hipLaunchKernelGGL((k_decide_residual<T, kAligned, false, false>), grid, block, 0, st, t, d, dtok,
                        uni, temp, K, V, nc, ncr, force_greedy, part, xd, filt, key16, dec, out, nacc,
                        kv_len, counters, csum, csub, pcnt);
-  if (!fused)
+  if (!fused && !force_greedy)
     hipLaunchKernelGGL((k_locate<T>), dim3(B), dim3(kThreads), 0, st, t, d, dtok, uni, temp, K, V, ncr,
                        force_greedy, csum, csub, dec, out, nacc, kv_len, counters);
   return hipGetLastError();
@@ -2329,12 +2333,14 @@ static hipError_t launch_tree(const void* tgt, const void* drf, const TreeShape&
   const T* d = static_cast<const T*>(drf);
   if (per_seq) {
     hipLaunchKernelGGL(k_tree_shapes, dim3((B + 63) / 64), dim3(64), 0, st, dparents, B, N, shapes);
-    hipLaunchKernelGGL((k_sweep<T, kAligned, TreeRowsSeq>), dim3(B * R, (nc + 3) / 4), dim3(kThreads), 0,
+    hipLaunchKernelGGL((k_sweep<T, kAligned, TreeRowsSeq>), dim3(B * (force_greedy ? N : R), (nc + 3) / 4), dim3(kThreads), 0,
                        st, t, d, tok, temp, TreeRowsSeq{shapes, N}, B, V, nc, force_greedy, part, xd,
                        rcnt);
   } else {
-    hipLaunchKernelGGL((k_sweep<T, kAligned, TreeRows>), dim3(B * R, (nc + 3) / 4), dim3(kThreads), 0,
-                       st, t, d, tok, temp, TreeRows{shape}, B, V, nc, force_greedy, part, xd, rcnt);
+    // Greedy only (no draft logits): the target rows, which come first.
+    hipLaunchKernelGGL((k_sweep<T, kAligned, TreeRows>), dim3(B * (force_greedy ? N : R), (nc + 3) / 4),
+                       dim3(kThreads), 0, st, t, d, tok, temp, TreeRows{shape}, B, V, nc, force_greedy,
+                       part, xd, rcnt);
   }
   // Filters: thresholds and kept masses per swept row, as for the chain.
   const bool filtered = (top_k || top_p) && !force_greedy;

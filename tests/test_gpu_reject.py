@@ -198,6 +198,22 @@ def test_greedy_ties_lowest_index(gpu_lib, dev):
         assert np.array_equal(kv_new, kv0 + n + 1)
 
 
+@pytest.mark.parametrize("B,K,V", [(64, 7, 128256), (4, 3, 600_000)])
+def test_greedy_without_draft_logits(gpu_lib, dev, B, K, V):
+    # No draft logits: every sequence greedy, grids sized to the target rows
+    # (and past 2^19 entries no separate draw kernel); the argmax stream of
+    # the oracle, bit for bit.
+    _say("greedy without draft logits B=%d K=%d V=%d" % (B, K, V))
+    inp = gen.make_reject_inputs(seed=77 + K, B=B, K=K, V=V, draft_sigma=0.3, temperature=0.0)
+    kv0 = np.full(B, 10, np.int32)
+    ref = orj.reject_sample(inp["target"], None, inp["draft_tokens"], inp["uniforms"],
+                            inp["temperature"])
+    out, n, kv_new = _run_gpu(gpu_lib, inp, kv0, dev, with_draft=False)
+    assert np.array_equal(out, ref["out_tokens"])
+    assert np.array_equal(n, ref["num_accepted"])
+    assert np.array_equal(kv_new, kv0 + n + 1)
+
+
 def test_draft_prob_zero_and_residual_edges(gpu_lib, dev):
     # Draft logit -inf at the drafted token: always accepted.  Target -inf at
     # the drafted token: always rejected.
