@@ -196,8 +196,14 @@ def main():
     attn_ws = torch.empty(max(256, sv.verify_attn_workspace_bytes(B, K, cfg.Hq, cfg.Hkv, cfg.D,
                                                                   max_kv)),
                           dtype=torch.uint8, device=dev)
-    rej_ws = torch.empty(sv.reject_sample_workspace_bytes(B, K, V) if parent is None else
-                         sv.reject_sample_tree_workspace_bytes(B, K1, V),
+    filtered = args.top_k > 0 or args.top_p < 1.0
+    if parent is None:
+        rej_bytes = (sv.reject_sample_filtered_workspace_bytes(B, K, V) if filtered else
+                     sv.reject_sample_workspace_bytes(B, K, V))
+    else:
+        rej_bytes = (sv.reject_sample_tree_filtered_workspace_bytes(B, K1, V) if filtered else
+                     sv.reject_sample_tree_workspace_bytes(B, K1, V))
+    rej_ws = torch.empty(rej_bytes,
                          dtype=torch.uint8, device=dev)
     out_tok = [torch.empty((B, K1), dtype=torch.int32, device=dev) for _ in range(args.sets)]
     out_node = [torch.empty((B, K1), dtype=torch.int32, device=dev) for _ in range(args.sets)]

@@ -280,10 +280,19 @@ int spec_reject_sample_noalloc(const void* target_logits, const void* draft_logi
  * top_k [B] int32, top_p [B] float32 device arrays; either may be NULL (off
  * for every sequence).  The top-p set is chosen on masses summed in 40-bit
  * fixed point from fp32 weights, so a boundary within ~1e-6 of top_p may be
- * decided differently from an exact computation.  Everything else,
- * including the workspace (spec_reject_sample_workspace_bytes), is as for
- * spec_reject_sample.  Cost: two extra passes over each filtered row per
- * active filter (bf16; four for fp32).
+ * decided differently from an exact computation.  Everything else is as
+ * for spec_reject_sample.
+ *
+ * workspace: at least spec_reject_sample_workspace_bytes(B, K, V) bytes;
+ *   with spec_reject_sample_filtered_workspace_bytes(B, K, V) bytes a bf16
+ *   call whose rows start on 16-byte boundaries (V % 8 == 0) also counts, in
+ *   its one sweep over the rows, every value of a window of 1024 bf16 keys
+ *   under a fixed sample's maximum, and each filtered row whose thresholds
+ *   fall inside that window needs no pass of its own; other rows (and every
+ *   row with the smaller workspace, or fp32 logits) take the filter's radix
+ *   passes: one or two extra reads of the row per active filter (bf16; up
+ *   to four for fp32).  The results are the same either way, except inside
+ *   the top-p band above.
  */
 int spec_reject_sample_filtered(const void* target_logits, const void* draft_logits,
                                 const int32_t* draft_tokens, const float* uniforms,
@@ -293,6 +302,10 @@ int spec_reject_sample_filtered(const void* target_logits, const void* draft_log
                                 unsigned long long* counters, int B, int K, int V,
                                 int dtype, void* workspace, size_t workspace_bytes,
                                 void* hip_stream);
+
+/* Workspace of spec_reject_sample_filtered with room for the sweep's window
+ * (0 for invalid sizes). */
+size_t spec_reject_sample_filtered_workspace_bytes(int B, int K, int V);
 
 /*
  * spec_reject_sample_tree -- the lossless verifier over a flattened draft
@@ -370,8 +383,10 @@ size_t spec_reject_sample_tree_workspace_bytes(int B, int N, int V);
  *
  * top_k [B] int32, top_p [B] float32 device arrays; either may be NULL (off
  * for every sequence).  The same top-p boundary band as the chain call.
- * Everything else, including the workspace
- * (spec_reject_sample_tree_workspace_bytes), is as for spec_reject_sample_tree.
+ * workspace: spec_reject_sample_tree_workspace_bytes(B, N, V), or
+ *   spec_reject_sample_tree_filtered_workspace_bytes(B, N, V) for the
+ *   sweep's window (as spec_reject_sample_filtered).  Everything else is as
+ *   for spec_reject_sample_tree.
  */
 int spec_reject_sample_tree_filtered(const void* target_logits, const void* draft_logits,
                                      const int32_t* parent, const int32_t* tokens,
@@ -382,6 +397,10 @@ int spec_reject_sample_tree_filtered(const void* target_logits, const void* draf
                                      unsigned long long* counters, int B, int N, int V,
                                      int dtype, void* workspace, size_t workspace_bytes,
                                      void* hip_stream);
+
+/* Workspace of spec_reject_sample_tree_filtered and spec_reject_sample_trees
+ * with room for the sweep's window (0 for invalid sizes). */
+size_t spec_reject_sample_tree_filtered_workspace_bytes(int B, int N, int V);
 
 /*
  * spec_reject_sample_trees -- spec_reject_sample_tree_filtered with one tree
@@ -402,8 +421,9 @@ int spec_reject_sample_tree_filtered(const void* target_logits, const void* draf
  *   of N nodes can need: a root with N - 1 children), and a sequence whose
  *   walk has ended leaves the remaining rounds at once.
  * workspace: spec_reject_sample_tree_workspace_bytes(B, N, V) (it includes
- *   room for the B shapes).  Other sizes and errors as
- *   spec_reject_sample_tree.
+ *   room for the B shapes), or spec_reject_sample_tree_filtered_workspace_
+ *   bytes(B, N, V) for the sweep's window with filters.  Other sizes and
+ *   errors as spec_reject_sample_tree.
  */
 int spec_reject_sample_trees(const void* target_logits, const void* draft_logits,
                              const int32_t* parents, const int32_t* tokens, const float* uniforms,

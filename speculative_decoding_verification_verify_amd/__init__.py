@@ -27,6 +27,7 @@ __all__ = ["load", "lib_path", "exported_symbols", "verify_attn", "verify_attn_t
            "reject_sample", "reject_sample_noalloc", "reject_sample_tree",
            "verify_attn_workspace_bytes", "NOALLOC_SCRATCH_BYTES",
            "reject_sample_workspace_bytes", "reject_sample_tree_workspace_bytes",
+           "reject_sample_filtered_workspace_bytes", "reject_sample_tree_filtered_workspace_bytes",
            "SpecVerifyError", "SV_F32", "SV_BF16", "STATUS", "EXPORTS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -41,7 +42,9 @@ STATUS = {0: "SV_OK", -1: "SV_ERR_INVALID_ARG", -2: "SV_ERR_UNSUPPORTED",
 EXPORTS = ("spec_verify_attn", "spec_verify_attn_workspace_bytes", "spec_verify_attn_tree",
            "spec_verify_attn_window", "spec_kv_commit",
            "spec_reject_sample", "spec_reject_sample_workspace_bytes", "spec_reject_sample_noalloc",
-           "spec_reject_sample_filtered", "spec_reject_sample_tree", "spec_reject_sample_tree_workspace_bytes",
+           "spec_reject_sample_filtered", "spec_reject_sample_filtered_workspace_bytes",
+           "spec_reject_sample_tree", "spec_reject_sample_tree_workspace_bytes",
+           "spec_reject_sample_tree_filtered_workspace_bytes",
            "spec_reject_sample_tree_filtered", "spec_reject_sample_trees",
            "spec_pages_create", "spec_pages_destroy", "spec_pages_reserve", "spec_pages_commit",
            "spec_pages_release", "spec_pages_free_count", "spec_pages_seq_blocks",
@@ -102,6 +105,10 @@ def load():
     lib.spec_reject_sample_trees.restype = i32
     lib.spec_reject_sample_tree_workspace_bytes.argtypes = [i32, i32, i32]
     lib.spec_reject_sample_tree_workspace_bytes.restype = sz
+    for fn in ("spec_reject_sample_filtered_workspace_bytes",
+               "spec_reject_sample_tree_filtered_workspace_bytes"):
+        getattr(lib, fn).argtypes = [i32, i32, i32]
+        getattr(lib, fn).restype = sz
     lib.spec_verify_attn_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                             i32, i32, i32, i32, i32, f32, i32, i32, vp, sz, vp]
     lib.spec_verify_attn_window.restype = i32
@@ -240,6 +247,16 @@ def reject_sample_workspace_bytes(B, K, V):
 
 def reject_sample_tree_workspace_bytes(B, N, V):
     return int(load().spec_reject_sample_tree_workspace_bytes(B, N, V))
+
+
+def reject_sample_filtered_workspace_bytes(B, K, V):
+    """Workspace of the filtered chain call with room for the sweep's window."""
+    return int(load().spec_reject_sample_filtered_workspace_bytes(B, K, V))
+
+
+def reject_sample_tree_filtered_workspace_bytes(B, N, V):
+    """Workspace of the filtered tree calls with room for the sweep's window."""
+    return int(load().spec_reject_sample_tree_filtered_workspace_bytes(B, N, V))
 
 
 def _workspace(workspace, ws_bytes, device):
@@ -384,9 +401,11 @@ def reject_sample(target, draft, draft_tokens, uniforms, temperature, kv_len,
             out_tokens=out_tokens, num_accepted=num_accepted, counters=counters)
     out_tokens, num_accepted = _reject_outputs(B, K1, target.device, out_tokens, num_accepted,
                                                counters)
-    ws_bytes = reject_sample_workspace_bytes(B, K, V)
+    filtered = top_k is not None or top_p is not None
+    ws_bytes = (reject_sample_filtered_workspace_bytes(B, K, V) if filtered else
+                reject_sample_workspace_bytes(B, K, V))
     workspace, ws_have = _workspace(workspace, ws_bytes, target.device)
-    if top_k is not None or top_p is not None:
+    if filtered:
         st = lib.spec_reject_sample_filtered(_ptr(target), _ptr(draft), _ptr(draft_tokens),
                                              _ptr(uniforms), _ptr(temperature), _ptr(top_k),
                                              _ptr(top_p), _ptr(out_tokens), _ptr(num_accepted),
@@ -501,9 +520,11 @@ def reject_sample_tree(target, draft, parent, tokens, uniforms, temperature, kv_
     c_par = (ctypes.c_int32 * N)(*par)
     out_tokens, out_nodes, num_accepted = _tree_outputs(B, N, target.device, out_tokens, out_nodes,
                                                         num_accepted, counters)
-    ws_bytes = reject_sample_tree_workspace_bytes(B, N, V)
+    filtered = top_k is not None or top_p is not None
+    ws_bytes = (reject_sample_tree_filtered_workspace_bytes(B, N, V) if filtered else
+                reject_sample_tree_workspace_bytes(B, N, V))
     workspace, ws_have = _workspace(workspace, ws_bytes, target.device)
-    if top_k is not None or top_p is not None:
+    if filtered:
         st = lib.spec_reject_sample_tree_filtered(
             _ptr(target), _ptr(draft), ctypes.cast(c_par, ctypes.c_void_p), _ptr(tokens),
             _ptr(uniforms), _ptr(temperature), _ptr(top_k), _ptr(top_p), _ptr(out_tokens),
@@ -536,7 +557,9 @@ def reject_sample_trees(target, draft, parents, tokens, uniforms, temperature, k
             num_accepted=num_accepted, counters=counters, top_k=top_k, top_p=top_p)
     out_tokens, out_nodes, num_accepted = _tree_outputs(B, N, target.device, out_tokens, out_nodes,
                                                         num_accepted, counters)
-    ws_bytes = reject_sample_tree_workspace_bytes(B, N, V)
+    ws_bytes = (reject_sample_tree_filtered_workspace_bytes(B, N, V)
+                if top_k is not None or top_p is not None else
+                reject_sample_tree_workspace_bytes(B, N, V))
     workspace, ws_have = _workspace(workspace, ws_bytes, target.device)
     st = lib.spec_reject_sample_trees(
         _ptr(target), _ptr(draft), _ptr(parents), _ptr(tokens), _ptr(uniforms), _ptr(temperature),

@@ -137,12 +137,66 @@ __device__ __forceinline__ uint32_t float_key(float x, bool key16) {
   return key16 ? k >> 16 : k;
 }
 
+// The float with a given 32-bit key (no NaN keys are passed).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+constexpr uint32_t kKeyNegInf = 0x007FFFFFu, kKeyPosInf = 0xFF800000u;
+// Float bounds [flo, fhi] with  flo <= x <= fhi  <=>  klo <= key32_of(x) <= khi
+// for every non-NaN x.  Key 0x7FFFFFFF (-0 before the fix) never occurs, so
+// as a bound it is moved past -0: x = -0 compares equal to +0.
+__device__ __forceinline__ void key_bounds(uint32_t klo, uint32_t khi, float& flo, float& fhi) {
+  klo = max(klo, kKeyNegInf);
+  khi = min(khi, kKeyPosInf);
+  if (klo == 0x7FFFFFFFu) klo = 0x80000000u;
+  if (khi == 0x7FFFFFFFu) khi = 0x7FFFFFFEu;
+  flo = key_value(klo);
+  fhi = key_value(khi);
+}
+
 // What k_filter leaves per row: the kept set {key >= key_min} and its mass
 // in the sweep's frame, sum 2^(x c - fl(xmax c)).
 struct RowFilter {
   uint32_t key_min;  // 0: the row is not filtered
   uint32_t pad;
   double mass;
+};
+
+// The window a filtered sweep counts (bf16 rows of sampling sequences with
+// a top-k or top-p filter): kWinKeys consecutive 16-bit keys (the keys of
+// one binade of bf16 values are 128 in a row), placed from a fixed sample of
+// the row:
+//  * top-k (with or without top-p): from kWinKBelow keys under the largest
+//    entry of kWinLines 64-entry runs spread evenly over the row (k up to
+//    V / 256; all kWinKeys keys for larger k) to kWinTopMargin keys above it.
+//    Every sweep block of the row reads the same runs and derives the same
+//    window.  The k-th largest value and every value above it are usually
+//    inside; an entry above the window sends the row to k_filter's radix
+//    passes.
+//  * top-p alone: k_win_prep estimates the threshold from kPrepLines runs
+//    (the value where the sample's own mass from the top reaches top_p); the
+//    window reaches kWinPBelow keys under it.  Entries above the window only
+//    add their mass (summed in float64), entries below it only to the row's.
+// k_filter_win then reads a row's thresholds from the counts instead of
+// passes over the row; a row whose threshold is not inside takes the passes.
+constexpr int kWinKeys = 512;
+constexpr int kWinTopMargin = 192;
+constexpr int kWinKBelow = 128;
+constexpr int kWinPBelow = 128;
+constexpr int kWinLines = 8;           // runs of 64 entries sampled by each sweep block (top-k)
+constexpr int kPrepLines = 32;         // runs sampled by k_win_prep (top-p)
+constexpr uint32_t kWinMinKey = 0x80;  // just above the key of -inf (0x7F)
+
+// Where the filtered sweep leaves its window (null pointers: no window).
+struct WinArgs {
+  const int32_t* top_k;  // [B] or null
+  const float* top_p;    // [B] or null
+  double* partd;         // [rows][nc]: top-p alone: each chunk's sum 2^(x c - fl(xmax c)) in float64
+  double* parta;         // [rows][nc]: the same over the entries above the window
+  uint16_t* whist;       // [rows][nblk][kWinKeys]: entries per window value, per sweep block
+  uint32_t* wflag;       // [rows][nblk]: 1 when the block saw an entry above a top-k window
+  uint32_t* wwin;        // [rows]: the window, lowest key | highest key << 16 (0: decided)
+  int nblk;              // sweep blocks per row
 };
 
 // Shape of a draft tree (nodes in topological order, parent[i] < i), shared
@@ -372,16 +426,200 @@ __device__ __forceinline__ u32x4_t load_raw_unaligned(const T* __restrict__ row,
   }
 }
 
+// The logits of the tokens a swept row tests, for the accept tests: each
+// written by the lane that holds it (xd[2 token + is_draft]).
+template <typename T, class Rows>
+__device__ __forceinline__ void record_draft_logits(const Rows& rows, int b, int j, int chunk,
+                                                    int lane, bool is_draft, int V,
+                                                    const float (&x)[kSweepChunk / (64 * Vec16<T>::N)][Vec16<T>::N],
+                                                    const int32_t* __restrict__ dtok,
+                                                    float* __restrict__ xd) {
+  constexpr int VN = Vec16<T>::N;
+  constexpr int IT = kSweepChunk / (64 * VN);
+  rows.for_each_token(b, j, [&](size_t ti) {
+    const int dd = clampi(dtok[ti], 0, V - 1);
+    const int off = dd - chunk * kSweepChunk;
+    if (off >= 0 && off < kSweepChunk && lane == (off / VN) % 64) {
+      const int it_d = off / (64 * VN), k_d = off % VN;
+      float v = 0.f;
+#pragma unroll
+      for (int it = 0; it < IT; ++it)
+#pragma unroll
+        for (int k = 0; k < VN; ++k)
+          if (it == it_d && k == k_d) v = x[it][k];
+      xd[ti * 2 + (is_draft ? 1 : 0)] = v;
+    }
+  });
+}
+
+// The top-k window (see kWinKeys) from the maximum sm of the row's sample:
+// lowest key | highest key << 16.
+__device__ __forceinline__ uint32_t topk_window(float sm, int tk, int V) {
+  const uint32_t ksm = key32_of(sm) >> 16;
+  const uint32_t ktop = min(ksm + (uint32_t)kWinTopMargin, 0xFFFFu);
+  const uint32_t wide = ktop >= kWinMinKey + (kWinKeys - 1) ? ktop - (kWinKeys - 1) : kWinMinKey;
+  const uint32_t near = ksm >= kWinMinKey + kWinKBelow ? ksm - kWinKBelow : kWinMinKey;
+  const uint32_t kbase = (long long)tk * 256 <= (long long)V ? max(near, wide) : wide;
+  return kbase | (ktop << 16);
+}
+
+// Vector index of sampled vector i of a row of nvec vectors: runs of 8
+// vectors (64 bf16 entries, one 128-byte line), nruns of them spread evenly.
+__device__ __forceinline__ int sample_vec(int i, int nruns, int nvec) {
+  return min((int)(((long long)(i >> 3) * nvec) / nruns) + (i & 7), nvec - 1);
+}
+
+// One block of the sweep of a filtered bf16 row (16-byte aligned): each
+// chunk's raw maximum, and the count of every value of the row's window
+// (see kWinKeys) among the block's entries.  A filtered row's law is
+// normalised over its kept set, so the decision takes the kept mass from
+// k_filter instead of the sweep's sum: only top-p alone sums masses here
+// (its target needs the row's whole mass, and the entries above its window
+// add theirs), in the chunk's own frame, in fp32 per vector of 8 and float64
+// beyond (partd, parta; part.y gets the chunk's sum).  A top-k row with an
+// entry above its window sets the block's flag: k_filter then takes its
+// radix passes for the row.  All four waves reach both barriers (a wave past
+// the row's last chunk only takes part in the counts' write-out).
+template <class Rows>
+__device__ __forceinline__ void sweep_window_block(const uint16_t* __restrict__ src, const Rows& rows,
+                                                   int b, int j, int row, bool is_draft, float t,
+                                                   int tk, bool k_on, int V, int nc,
+                                                   const int32_t* __restrict__ dtok,
+                                                   float2* __restrict__ part, float* __restrict__ xd,
+                                                   const WinArgs& wa) {
+  constexpr int VN = Vec16<uint16_t>::N;
+  constexpr int IT = kSweepChunk / (64 * VN);
+  static_assert(kWinKeys == 2 * kThreads, "two window values per thread in the write-out");
+  static_assert(kWinLines * 8 == 64, "one sampled vector per lane");
+  __shared__ uint32_t s_hist[kWinKeys + 64];        // + one spare bin per lane
+  __shared__ uint32_t s_flag;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int chunk = blockIdx.y * 4 + wave;
+  const bool live = chunk < nc;
+  const int base = chunk * kSweepChunk + lane * VN;
+  const bool full = (chunk + 1) * kSweepChunk <= V;
+  // Top-k: the window from this block's read of the sample runs; top-p
+  // alone: from k_win_prep.  Requested ahead of the chunk's rows, so the
+  // window is ready while they are still arriving.
+  float xs[VN];
+  uint32_t pwin = 0u;
+  if (k_on) Vec16<uint16_t>::load(src + (size_t)sample_vec(lane, kWinLines, V / VN) * VN, xs);
+  else pwin = wa.wwin[row];
+  float x[IT][VN];
+  if (live) {
+    if (full) {
+#pragma unroll
+      for (int it = 0; it < IT; ++it) Vec16<uint16_t>::load_nt(src + base + it * 64 * VN, x[it]);
+    } else {
+#pragma unroll
+      for (int it = 0; it < IT; ++it) load_vec<uint16_t, true, true>(src, base + it * 64 * VN, V, x[it]);
+    }
+  }
+  s_hist[tid] = 0u;
+  s_hist[tid + kThreads] = 0u;
+  if (tid == 0) s_flag = 0u;
+  uint32_t win = pwin;
+  if (k_on) {
+    float sm = xs[0];
+#pragma unroll
+    for (int k = 1; k < VN; ++k) sm = fmaxf(sm, xs[k]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sm = fmaxf(sm, __shfl_xor(sm, off, 64));
+    win = topk_window(sm, tk, V);
+  }
+  const uint32_t kbase = win & 0xFFFFu, ktop = win >> 16;
+  if (live) record_draft_logits<uint16_t>(rows, b, j, chunk, lane, is_draft, V, x, dtok, xd);
+  float flo, fhi;
+  key_bounds(kbase << 16, (ktop << 16) | 0xFFFFu, flo, fhi);
+  __syncthreads();                                 // counts cleared
+  if (live) {
+    float xm = -INFINITY;
+#pragma unroll
+    for (int it = 0; it < IT; ++it)
+#pragma unroll
+      for (int k = 0; k < VN; ++k) xm = fmaxf(xm, x[it][k]);
+    float xw = xm;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) xw = fmaxf(xw, __shfl_xor(xw, off, 64));
+    // A top-k row with an entry above its window goes to the radix passes.
+    if (k_on && __ballot(xm > fhi) && lane == 0) atomicOr(&s_flag, 1u);
+    // A window of positive values above +0 (the usual case): the bin from the
+    // raw bits without a branch, as bf16 bits - lowest bits (unsigned, so
+    // negative values and values below or above the window fall outside
+    // [0, kWinKeys)), outside entries counted in the lane's spare bin.
+    const bool pos = kbase > 0x8000u;
+    if (pos) {
+      const uint32_t kb = kbase - 0x8000u;
+#pragma unroll
+      for (int it = 0; it < IT; ++it)
+#pragma unroll
+        for (int k = 0; k < VN; ++k) {
+          const uint32_t d = (__float_as_uint(x[it][k]) >> 16) - kb;
+          atomicAdd(&s_hist[d < (uint32_t)kWinKeys ? d : (uint32_t)(kWinKeys + lane)], 1u);
+        }
+    }
+    // Top-p alone: masses 2^(x c - fl(xw c)) (entries past V are -inf: 0),
+    // and apart those of the entries above the window.
+    const bool sum = !k_on;
+    const float c = kLog2e / t;
+    const float m = xw != -INFINITY ? xw * c : 0.f;
+    double sd = 0.0, sa = 0.0;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      float vs = 0.f, va = 0.f;
+#pragma unroll
+      for (int k = 0; k < VN; ++k) {
+        const float v = x[it][k];
+        if (sum) {
+          const float e = exp2_dev(__builtin_fmaf(v, c, -m));
+          vs += e;
+          va += v > fhi ? e : 0.f;
+        }
+        if (!pos && v >= flo && v <= fhi) atomicAdd(&s_hist[(key32_of(v) >> 16) - kbase], 1u);
+      }
+      if (sum) {
+        sd += (double)vs;
+        sa += (double)va;
+      }
+    }
+    if (sum) {
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        sd += __shfl_xor(sd, off, 64);
+        sa += __shfl_xor(sa, off, 64);
+      }
+    }
+    if (lane == 0) {
+      part[(size_t)row * nc + chunk] = make_float2(xw, (float)sd);
+      if (!k_on) {
+        wa.partd[(size_t)row * nc + chunk] = sd;
+        wa.parta[(size_t)row * nc + chunk] = sa;
+      }
+    }
+  }
+  __syncthreads();                                 // every entry counted
+  // A block holds at most 4 kSweepChunk = 16384 entries: counts fit 16 bits.
+  const int i0 = 2 * tid;
+  const size_t hb = ((size_t)row * wa.nblk + blockIdx.y) * kWinKeys;
+  *reinterpret_cast<uint32_t*>(wa.whist + hb + i0) = s_hist[i0] | (s_hist[i0 + 1] << 16);
+  if (tid == 0) {
+    wa.wflag[(size_t)row * wa.nblk + blockIdx.y] = s_flag;
+    if (k_on && blockIdx.y == 0) wa.wwin[row] = win;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // k_sweep: grid (B * rows.count(), ceil(nc / 4)); block 256 = 4 waves, one
 // chunk each.  part[row * nc + chunk] = (raw max, sum 2^(x c - fl(max c)))
 // or, greedy, (max value, argmax index bits).  Also zeroes pcnt[0..B).
+// kWin: rows with a filter (bf16, aligned) also count their window
+// (sweep_window_block).
 // ---------------------------------------------------------------------------
-template <typename T, bool kAligned, class Rows>
+template <typename T, bool kAligned, class Rows, bool kWin = false>
 __global__ __launch_bounds__(kThreads) void k_sweep(
     const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ dtok,
     const float* __restrict__ temp, Rows rows, int B, int V, int nc, int force_greedy,
-    float2* __restrict__ part, float* __restrict__ xd, unsigned* __restrict__ pcnt) {
+    float2* __restrict__ part, float* __restrict__ xd, unsigned* __restrict__ pcnt, WinArgs wa) {
   // Clears the per-sequence pass counts the later kernels count in with.
   if (blockIdx.y == 0 && (int)blockIdx.x < B && threadIdx.x == 0) pcnt[blockIdx.x] = 0u;
   const int R = rows.count();
@@ -399,11 +637,21 @@ __global__ __launch_bounds__(kThreads) void k_sweep(
   // loads are issued before the temperature arrives.
   if (is_draft && !(temp_of(temp, b, force_greedy) > 0.f)) return;
   if (!rows.valid(b, j)) return;                 // a per-sequence shape with fewer rows
+  const T* src = (is_draft ? drf : tgt) + rows.row(b, j) * (size_t)V;
+  if constexpr (kWin && kAligned && sizeof(T) == 2) {
+    const float tw = temp_of(temp, b, force_greedy);
+    const int tk = wa.top_k ? wa.top_k[b] : 0;
+    const float tp = wa.top_p ? wa.top_p[b] : 1.f;
+    const bool k_on = tk > 0 && tk < V, p_on = tp > 0.f && tp < 1.f;
+    if (tw > 0.f && (k_on || p_on)) {              // block-uniform
+      sweep_window_block<Rows>(src, rows, b, j, row, is_draft, tw, tk, k_on, V, nc, dtok, part, xd, wa);
+      return;
+    }
+  }
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int chunk = blockIdx.y * 4 + wave;
   if (chunk >= nc) return;
-  const T* src = (is_draft ? drf : tgt) + rows.row(b, j) * (size_t)V;
   constexpr int VN = Vec16<T>::N;
   constexpr int IT = kSweepChunk / (64 * VN);
   const int base = chunk * kSweepChunk + lane * VN;
@@ -420,24 +668,7 @@ __global__ __launch_bounds__(kThreads) void k_sweep(
   }
   const float t = temp_of(temp, b, force_greedy);
   const bool greedy = !(t > 0.f);
-  if (!greedy) {
-    // The logits of the tokens this row tests, for the accept tests: each
-    // written by the lane that holds it (xd[2 token + is_draft]).
-    rows.for_each_token(b, j, [&](size_t ti) {
-      const int dd = clampi(dtok[ti], 0, V - 1);
-      const int off = dd - chunk * kSweepChunk;
-      if (off >= 0 && off < kSweepChunk && lane == (off / VN) % 64) {
-        const int it_d = off / (64 * VN), k_d = off % VN;
-        float v = 0.f;
-#pragma unroll
-        for (int it = 0; it < IT; ++it)
-#pragma unroll
-          for (int k = 0; k < VN; ++k)
-            if (it == it_d && k == k_d) v = x[it][k];
-        xd[ti * 2 + (is_draft ? 1 : 0)] = v;
-      }
-    });
-  }
+  if (!greedy) record_draft_logits<T>(rows, b, j, chunk, lane, is_draft, V, x, dtok, xd);
   float2 res;
   if (greedy) {
     float mv = -INFINITY;
@@ -624,23 +855,6 @@ __device__ __forceinline__ unsigned long long fixed40(float w) {
   const uint32_t hi = (uint32_t)t;
   const uint32_t lo = (uint32_t)(__builtin_amdgcn_fractf(t) * 4294967296.0f);
   return ((unsigned long long)hi << 32) | lo;
-}
-
-// The float with a given 32-bit key (no NaN keys are passed).
-__device__ __forceinline__ float key_value(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-constexpr uint32_t kKeyNegInf = 0x007FFFFFu, kKeyPosInf = 0xFF800000u;
-// Float bounds [flo, fhi] with  flo <= x <= fhi  <=>  klo <= key32_of(x) <= khi
-// for every non-NaN x.  Key 0x7FFFFFFF (-0 before the fix) never occurs, so
-// as a bound it is moved past -0: x = -0 compares equal to +0.
-__device__ __forceinline__ void key_bounds(uint32_t klo, uint32_t khi, float& flo, float& fhi) {
-  klo = max(klo, kKeyNegInf);
-  khi = min(khi, kKeyPosInf);
-  if (klo == 0x7FFFFFFFu) klo = 0x80000000u;
-  if (khi == 0x7FFFFFFFu) khi = 0x7FFFFFFEu;
-  flo = key_value(klo);
-  fhi = key_value(khi);
 }
 
 // Streams a row through f(x, e): x the VN widened logits of the vector at
@@ -920,11 +1134,173 @@ __device__ __forceinline__ unsigned long long filter_kept_mass(const T* __restri
   return tot;
 }
 
+// The largest of a wave's 512 bins (8 per lane: lane l holds bins 8l ..
+// 8l + 7) whose running total from the top, plus `above`, reaches target;
+// -1 when none does.  ab_out: the running total above the bin (the same in
+// every lane).  The order of the integer adds does not matter.
+__device__ __forceinline__ int wave_pick8(const unsigned long long (&v)[8], double target,
+                                          unsigned long long above, int lane,
+                                          unsigned long long& ab_out) {
+  unsigned long long loc = 0ull;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) loc += v[k];
+  unsigned long long suf = loc;                    // lanes l .. 63
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned long long t = __shfl_down(suf, off, 64);
+    if (lane + off < 64) suf += t;
+  }
+  unsigned long long acc = above + (suf - loc);
+  int hit = -1;
+  unsigned long long ab = 0ull;
+#pragma unroll
+  for (int k = 7; k >= 0; --k) {
+    if (hit < 0 && (double)(acc + v[k]) >= target) {
+      hit = 8 * lane + k;
+      ab = acc;
+    }
+    acc += v[k];
+  }
+  int h = hit;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) h = max(h, __shfl_xor(h, off, 64));
+  if (h < 0) return -1;
+  const int owner = __builtin_amdgcn_readfirstlane(h >> 3);
+  ab_out = ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(ab >> 32), owner) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)ab, owner);
+  return h;
+}
+
+// k_filter_win: grid (B * rows.count()), one wave per row: the thresholds of
+// a row the filtered sweep counted in a window, from the sweep blocks'
+// counts.  Summed per window value, the counts from the top give the top-k
+// threshold (the largest value with at least k entries at or above it); a
+// value's mass is its count times its weight, the same integer as the sum of
+// its entries' weights in the radix passes, and the masses from the top give
+// the top-p threshold and the kept mass.  Top-p alone takes the row's mass
+// and the mass above its window from the sweep's float64 chunk sums, moved
+// into the row's frame.  A row it decides gets its RowFilter and wwin[row] =
+// 0, which k_filter, launched next, reads as "done".  It leaves a row to
+// k_filter's radix passes when the window does not decide it: a top-k row
+// with an entry above its window or fewer than k entries in it, or a top-p
+// target reached above the window or not reached at its lowest value.
+template <class Rows>
+__global__ __launch_bounds__(64) void k_filter_win(
+    const float* __restrict__ temp, const int32_t* __restrict__ top_k, const float* __restrict__ top_p,
+    Rows rows, int V, int nc, int force_greedy, const float2* __restrict__ part,
+    RowFilter* __restrict__ filt, WinArgs wa) {
+  static_assert(kWinKeys == 8 * 64, "eight window values per lane");
+  const int R = rows.count();
+  const int row = blockIdx.x;
+  const int b = row / R;
+  const int j = row - b * R;
+  const int lane = threadIdx.x;
+  if (!rows.valid(b, j)) return;
+  const float t = temp_of(temp, b, force_greedy);
+  const int tk = top_k ? top_k[b] : 0;
+  const float tp = top_p ? top_p[b] : 1.f;
+  const bool k_on = tk > 0 && tk < V;
+  const bool p_on = tp > 0.f && tp < 1.f;
+  if (!(t > 0.f) || (!k_on && !p_on)) return;
+  const float c = kLog2e / t;
+  const uint32_t kbase = wa.wwin[row] & 0xFFFFu;
+  // Every load first: the blocks' flags and counts, the chunk maxima and,
+  // for top-p alone, the chunk sums.
+  bool bad = false;
+  if (k_on)
+    for (int y = lane; y < wa.nblk; y += 64) bad = bad || wa.wflag[(size_t)row * wa.nblk + y] != 0u;
+  uint32_t cnt[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  const uint16_t* hp = wa.whist + (size_t)row * wa.nblk * kWinKeys + 8 * lane;
+  for (int y0 = 0; y0 < wa.nblk; y0 += 16) {
+    uint4 v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      v[q] = y0 + q < wa.nblk ? *reinterpret_cast<const uint4*>(hp + (size_t)(y0 + q) * kWinKeys)
+                              : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const uint32_t w4[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        cnt[2 * k] += w4[k] & 0xFFFFu;
+        cnt[2 * k + 1] += w4[k] >> 16;
+      }
+    }
+  }
+  float xr = -INFINITY;
+  for (int k = lane; k < nc; k += 64) xr = fmaxf(xr, part[(size_t)row * nc + k].x);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) xr = fmaxf(xr, __shfl_xor(xr, off, 64));
+  const float mc = xr * c;
+  if (__ballot(bad)) return;
+  unsigned long long v[8], ab = 0ull;
+  int sel = 0;
+  if (k_on) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = cnt[k];
+    sel = wave_pick8(v, (double)tk, 0ull, lane, ab);
+    if (sel < 0) return;                           // fewer than k entries in the window
+  }
+  // Masses of the values from the top-k threshold up (all of the window
+  // without top-k).
+  unsigned long long loc = 0ull;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int i = 8 * lane + k;
+    const float xv = key16_value(kbase + (uint32_t)i);
+    v[k] = i >= sel ? cnt[k] * fixed40(exp2_dev(__builtin_fmaf(xv, c, -mc))) : 0ull;
+    loc += v[k];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) loc += __shfl_xor(loc, off, 64);
+  unsigned long long kept = loc;                   // the set's mass
+  if (p_on) {
+    double target;
+    unsigned long long above = 0ull;
+    if (k_on) {
+      target = (double)tp * (double)loc;
+    } else {
+      // The row's mass and the mass above the window, in the row's frame:
+      // chunk sums in chunk order per lane, then a fixed-order wave sum.
+      double z = 0.0, za = 0.0;
+      for (int k = lane; k < nc; k += 64) {
+        const size_t i = (size_t)row * nc + k;
+        const float mk = part[i].x * c;             // the chunk's frame, as the sweep took it
+        const double f = exp2((double)mk - (double)mc);
+        z += wa.partd[i] * f;
+        za += wa.parta[i] * f;
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        z += __shfl_xor(z, off, 64);
+        za += __shfl_xor(za, off, 64);
+      }
+      target = (double)tp * z * kFix;
+      const double abv = za * kFix;
+      if (abv >= target || abv + (double)loc < target) return;
+      above = (unsigned long long)llrint(abv);
+    }
+    sel = wave_pick8(v, target, above, lane, ab);
+    if (sel < 0) return;
+    const int owner = __builtin_amdgcn_readfirstlane(sel >> 3);
+    unsigned long long vs = 0ull;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (8 * lane + k == sel) vs = v[k];
+    kept = ab + (((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(vs >> 32), owner) << 32) |
+                 (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)vs, owner));
+  }
+  if (lane == 0) {
+    filt[row] = RowFilter{kbase + (uint32_t)sel, 0u, (double)kept / kFix};
+    wa.wwin[row] = 0u;
+  }
+}
+
 template <typename T, bool kAligned, class Rows>
 __global__ __launch_bounds__(kFilterThreads, 4) void k_filter(
     const T* __restrict__ tgt, const T* __restrict__ drf, const float* __restrict__ temp,
     const int32_t* __restrict__ top_k, const float* __restrict__ top_p, Rows rows, int V, int nc,
-    int force_greedy, const float2* __restrict__ part, RowFilter* __restrict__ filt) {
+    int force_greedy, const float2* __restrict__ part, RowFilter* __restrict__ filt, WinArgs wa) {
   __shared__ unsigned long long h[kFilterBins];
   __shared__ unsigned long long s_w[kFilterWaves];
   __shared__ int s_pick[2 * kFilterWaves];
@@ -948,6 +1324,7 @@ __global__ __launch_bounds__(kFilterThreads, 4) void k_filter(
     if (tid == 0) filt[row] = RowFilter{0u, 0u, 0.0};
     return;
   }
+  if (wa.wwin && wa.wwin[row] == 0u) return;     // decided by k_filter_win from the sweep's window
   const T* src = (rows.is_draft(j) ? drf : tgt) + rows.row(b, j) * (size_t)V;
   const float c = kLog2e / t;
   // The row's raw maximum, merged from the sweep's chunk maxima as the decision does.
@@ -1338,6 +1715,95 @@ __device__ __forceinline__ double wave_sum_d(double x) {
   x = group8_sum_d(x);
   x += dpp_d<kDppRowMirror>(x);
   return (readlane_d(x, 0) + readlane_d(x, 16)) + (readlane_d(x, 32) + readlane_d(x, 48));
+}
+
+// Sum of a float over the wave in every lane, by DPP moves inside rows of
+// 16 lanes and the four row sums in a fixed order (each step is symmetric, so
+// every lane ends with the same value).
+__device__ __forceinline__ float wave_sum_f(float x) {
+  x += dpp_f<kDppXor1>(x);
+  x += dpp_f<kDppXor2>(x);
+  x += dpp_f<kDppHalfMirror>(x);
+  x += dpp_f<kDppRowMirror>(x);
+  return (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)) +
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32)) +
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48)));
+}
+
+// The sample's estimate of the top-p threshold: the largest 16-bit key whose
+// set {key(x) >= k} holds at least tp of the sample's mass 2^(x c - sm c),
+// found by bisection over the keys on one wave (each lane holds
+// kPrepLines * 64 / 64 sampled values; fixed-order sums).
+__device__ __forceinline__ uint32_t sample_topp_key(const float* __restrict__ s_samp, float sm, float c,
+                                                    float tp, int lane) {
+  constexpr int PER = kPrepLines;
+  float w[PER];
+  uint32_t kk[PER];
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const float x = s_samp[lane + 64 * i];
+    kk[i] = key32_of(x) >> 16;
+    w[i] = exp2_dev(__builtin_fmaf(x, c, -sm * c));
+    tot += w[i];
+  }
+  tot = wave_sum_f(tot);
+  const float target = tp * tot;
+  // The answer lies between the sample's smallest key (the whole mass) and
+  // its largest (the mass there is at least the top value's).
+  uint32_t kmin = 0xFFFFu;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) kmin = min(kmin, kk[i]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, 64));
+  uint32_t lo = kmin, hi = (key32_of(sm) >> 16) + 1u;  // mass(lo) >= target; hi: past the keys
+  while (hi - lo > 1u) {
+    const uint32_t mid = (lo + hi) >> 1;
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) m += kk[i] >= mid ? w[i] : 0.f;
+    if (wave_sum_f(m) >= target) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// k_win_prep: grid (B * rows.count()), block 256: the window of each bf16 row
+// of a sequence with top-p and no top-k (see kWinKeys), from kPrepLines runs
+// of the row: wwin[row] = lowest key | highest key << 16.
+template <class Rows>
+__global__ __launch_bounds__(kPrepLines * 8) void k_win_prep(
+    const uint16_t* __restrict__ tgt, const uint16_t* __restrict__ drf, const float* __restrict__ temp,
+    Rows rows, int V, int force_greedy, WinArgs wa) {
+  constexpr int VN = Vec16<uint16_t>::N;
+  __shared__ float s_samp[kPrepLines * 64];
+  const int R = rows.count();
+  const int row = blockIdx.x;
+  const int b = row / R;
+  const int j = row - b * R;
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (!rows.valid(b, j)) return;
+  const float t = temp_of(temp, b, force_greedy);
+  const int tk = wa.top_k ? wa.top_k[b] : 0;
+  const float tp = wa.top_p ? wa.top_p[b] : 1.f;
+  if (!(t > 0.f) || (tk > 0 && tk < V) || !(tp > 0.f && tp < 1.f)) return;
+  const uint16_t* src = (rows.is_draft(j) ? drf : tgt) + rows.row(b, j) * (size_t)V;
+  float xs[VN];
+  Vec16<uint16_t>::load(src + (size_t)sample_vec(tid, kPrepLines, V / VN) * VN, xs);
+#pragma unroll
+  for (int k = 0; k < VN; ++k) s_samp[tid * VN + k] = xs[k];
+  __syncthreads();
+  if (tid >= 64) return;
+  float sm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kPrepLines; ++i) sm = fmaxf(sm, s_samp[lane + 64 * i]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sm = fmaxf(sm, __shfl_xor(sm, off, 64));
+  const uint32_t kt = sample_topp_key(s_samp, sm, kLog2e / t, tp, lane);
+  uint32_t kbase = kt >= kWinMinKey + kWinPBelow ? kt - kWinPBelow : kWinMinKey;
+  kbase = min(kbase, 0xFFFFu - (kWinKeys - 1));
+  if (lane == 0) wa.wwin[row] = kbase | ((kbase + (kWinKeys - 1)) << 16);
 }
 
 // One wave walks `cnt` masses (mass(i)) in order: returns the first index
@@ -2131,7 +2597,30 @@ __global__ __launch_bounds__(kThreads) void k_tree_draw(
 
 struct RejectPlan {
   size_t part_off, csum_off, csub_off, dec_off, xd_off, filt_off, cnt_off, total;
+  size_t partd_off, parta_off, whist_off, wflag_off, wwin_off, total_filtered;   // filtered bf16 calls only
 };
+
+// The window arrays of a filtered call over `rows` swept rows, from offset
+// `at` on; returns the end.
+template <class P>
+static inline size_t win_plan(P& p, size_t at, size_t rows, int V) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t nc = (size_t)sweep_chunks(V), nblk = (nc + 3) / 4;
+  p.partd_off = at;
+  p.parta_off = p.partd_off + up(rows * nc * sizeof(double));
+  p.whist_off = p.parta_off + up(rows * nc * sizeof(double));
+  p.wflag_off = p.whist_off + up(rows * nblk * kWinKeys * sizeof(uint16_t));
+  p.wwin_off = p.wflag_off + up(rows * nblk * sizeof(uint32_t));
+  return p.wwin_off + up(rows * sizeof(uint32_t));
+}
+
+template <class P>
+static inline WinArgs win_args(const P& p, char* ws, const int32_t* top_k, const float* top_p, int V) {
+  return WinArgs{top_k, top_p, reinterpret_cast<double*>(ws + p.partd_off),
+                 reinterpret_cast<double*>(ws + p.parta_off), reinterpret_cast<uint16_t*>(ws + p.whist_off),
+                 reinterpret_cast<uint32_t*>(ws + p.wflag_off),
+                 reinterpret_cast<uint32_t*>(ws + p.wwin_off), (sweep_chunks(V) + 3) / 4};
+}
 
 static inline RejectPlan reject_plan(int B, int K, int V) {
   RejectPlan p{};
@@ -2145,6 +2634,7 @@ static inline RejectPlan reject_plan(int B, int K, int V) {
   p.filt_off = p.xd_off + up((size_t)B * K * 2 * sizeof(float));
   p.cnt_off = p.filt_off + up((size_t)B * R * sizeof(RowFilter));
   p.total = p.cnt_off + up((size_t)B * sizeof(unsigned));
+  p.total_filtered = win_plan(p, p.total, (size_t)B * R, V);
   return p;
 }
 
@@ -2153,7 +2643,7 @@ static hipError_t launch_all(const void* tgt, const void* drf, const int32_t* dt
                              const float* temp, int32_t* out, int32_t* nacc, int32_t* kv_len,
                              unsigned long long* counters, int B, int K, int V, int force_greedy,
                              char* ws, hipStream_t st, const int32_t* top_k = nullptr,
-                             const float* top_p = nullptr) {
+                             const float* top_p = nullptr, bool win_ws = false) {
   const int nc = sweep_chunks(V);
   const int ncr = res_chunks(V);
   const int R = 2 * K + 1;
@@ -2169,14 +2659,29 @@ static hipError_t launch_all(const void* tgt, const void* drf, const int32_t* dt
   // Without draft logits every sequence is greedy: the grid holds the target
   // rows only (they come first in the sweep's order), and the decision one
   // workgroup per sequence.
-  hipLaunchKernelGGL((k_sweep<T, kAligned, ChainRows>), dim3(B * (force_greedy ? K + 1 : R), (nc + 3) / 4),
-                     dim3(kThreads), 0, st, t, d, dtok, temp, ChainRows{K}, B, V, nc, force_greedy, part,
-                     xd, pcnt);
   const bool filtered = (top_k || top_p) && !force_greedy;
+  // Filtered bf16 rows (16-byte aligned) count their window in the sweep,
+  // when the workspace holds the window arrays.
+  const bool win = filtered && win_ws && kAligned && sizeof(T) == 2;
+  const WinArgs wa = win ? win_args(p, ws, top_k, top_p, V) : WinArgs{};
+  const dim3 sgrid(B * (force_greedy ? K + 1 : R), (nc + 3) / 4);
+  if (win && top_p)
+    hipLaunchKernelGGL((k_win_prep<ChainRows>), dim3(B * R), dim3(kPrepLines * 8), 0, st,
+                       reinterpret_cast<const uint16_t*>(t), reinterpret_cast<const uint16_t*>(d), temp,
+                       ChainRows{K}, V, force_greedy, wa);
+  if (win)
+    hipLaunchKernelGGL((k_sweep<T, kAligned, ChainRows, true>), sgrid, dim3(kThreads), 0, st, t, d, dtok,
+                       temp, ChainRows{K}, B, V, nc, force_greedy, part, xd, pcnt, wa);
+  else
+    hipLaunchKernelGGL((k_sweep<T, kAligned, ChainRows>), sgrid, dim3(kThreads), 0, st, t, d, dtok, temp,
+                       ChainRows{K}, B, V, nc, force_greedy, part, xd, pcnt, WinArgs{});
   RowFilter* filt = filtered ? reinterpret_cast<RowFilter*>(ws + p.filt_off) : nullptr;
+  if (win)
+    hipLaunchKernelGGL((k_filter_win<ChainRows>), dim3(B * R), dim3(64), 0, st, temp, top_k,
+                       top_p, ChainRows{K}, V, nc, force_greedy, part, filt, wa);
   if (filtered)
     hipLaunchKernelGGL((k_filter<T, kAligned, ChainRows>), dim3(B * R), dim3(kFilterThreads), 0, st, t,
-                       d, temp, top_k, top_p, ChainRows{K}, V, nc, force_greedy, part, filt);
+                       d, temp, top_k, top_p, ChainRows{K}, V, nc, force_greedy, part, filt, wa);
   const int key16 = sizeof(T) == 2 ? 1 : 0;
   // The draw joins the pass kernel while the chunk sums fit one wave.
   const bool fused = ncr <= 64;
@@ -2208,6 +2713,7 @@ static hipError_t launch_all(const void* tgt, const void* drf, const int32_t* dt
 struct TreePlan {
   size_t part_off, rowstat_off, csum_off, csub_off, dec_off, state_off, xd_off, rcnt_off, filt_off,
       shape_off, total;
+  size_t partd_off, parta_off, whist_off, wflag_off, wwin_off, total_filtered;   // filtered bf16 calls only
 };
 
 static inline TreePlan tree_plan(int B, int N, int V) {
@@ -2225,6 +2731,7 @@ static inline TreePlan tree_plan(int B, int N, int V) {
   p.filt_off = p.rcnt_off + up((size_t)B * sizeof(unsigned));
   p.shape_off = p.filt_off + up((size_t)B * R * sizeof(RowFilter));
   p.total = p.shape_off + up((size_t)B * sizeof(TreeShape));   // shapes: one per sequence
+  p.total_filtered = win_plan(p, p.total, (size_t)B * R, V);
   return p;
 }
 
@@ -2313,7 +2820,7 @@ static hipError_t launch_tree(const void* tgt, const void* drf, const TreeShape&
                               const float* temp, int32_t* out_tok, int32_t* out_node, int32_t* nacc,
                               int32_t* kv_len, unsigned long long* counters, int B, int V,
                               int force_greedy, char* ws, hipStream_t st, const int32_t* top_k,
-                              const float* top_p) {
+                              const float* top_p, bool win_ws) {
   const int N = shape.n;
   const int nc = sweep_chunks(V);
   const int ncr = res_chunks(V);
@@ -2331,26 +2838,51 @@ static hipError_t launch_tree(const void* tgt, const void* drf, const TreeShape&
   TreeShape* shapes = per_seq ? reinterpret_cast<TreeShape*>(ws + p.shape_off) : nullptr;
   const T* t = static_cast<const T*>(tgt);
   const T* d = static_cast<const T*>(drf);
+  // Filters: thresholds and kept masses per swept row, as for the chain
+  // (bf16 rows counted in a window by the sweep).
+  const bool filtered = (top_k || top_p) && !force_greedy;
+  const bool win = filtered && win_ws && kAligned && sizeof(T) == 2;
+  const WinArgs wa = win ? win_args(p, ws, top_k, top_p, V) : WinArgs{};
+  // Greedy only (no draft logits): the target rows, which come first.
+  const dim3 sgrid(B * (force_greedy ? N : R), (nc + 3) / 4);
   if (per_seq) {
     hipLaunchKernelGGL(k_tree_shapes, dim3((B + 63) / 64), dim3(64), 0, st, dparents, B, N, shapes);
-    hipLaunchKernelGGL((k_sweep<T, kAligned, TreeRowsSeq>), dim3(B * (force_greedy ? N : R), (nc + 3) / 4), dim3(kThreads), 0,
-                       st, t, d, tok, temp, TreeRowsSeq{shapes, N}, B, V, nc, force_greedy, part, xd,
-                       rcnt);
+    if (win && top_p)
+      hipLaunchKernelGGL((k_win_prep<TreeRowsSeq>), dim3(B * R), dim3(kPrepLines * 8), 0, st,
+                         reinterpret_cast<const uint16_t*>(t), reinterpret_cast<const uint16_t*>(d),
+                         temp, TreeRowsSeq{shapes, N}, V, force_greedy, wa);
+    if (win)
+      hipLaunchKernelGGL((k_sweep<T, kAligned, TreeRowsSeq, true>), sgrid, dim3(kThreads), 0, st, t, d, tok,
+                         temp, TreeRowsSeq{shapes, N}, B, V, nc, force_greedy, part, xd, rcnt, wa);
+    else
+      hipLaunchKernelGGL((k_sweep<T, kAligned, TreeRowsSeq>), sgrid, dim3(kThreads), 0, st, t, d, tok, temp,
+                         TreeRowsSeq{shapes, N}, B, V, nc, force_greedy, part, xd, rcnt, WinArgs{});
   } else {
-    // Greedy only (no draft logits): the target rows, which come first.
-    hipLaunchKernelGGL((k_sweep<T, kAligned, TreeRows>), dim3(B * (force_greedy ? N : R), (nc + 3) / 4),
-                       dim3(kThreads), 0, st, t, d, tok, temp, TreeRows{shape}, B, V, nc, force_greedy,
-                       part, xd, rcnt);
+    if (win && top_p)
+      hipLaunchKernelGGL((k_win_prep<TreeRows>), dim3(B * R), dim3(kPrepLines * 8), 0, st,
+                         reinterpret_cast<const uint16_t*>(t), reinterpret_cast<const uint16_t*>(d),
+                         temp, TreeRows{shape}, V, force_greedy, wa);
+    if (win)
+      hipLaunchKernelGGL((k_sweep<T, kAligned, TreeRows, true>), sgrid, dim3(kThreads), 0, st, t, d, tok,
+                         temp, TreeRows{shape}, B, V, nc, force_greedy, part, xd, rcnt, wa);
+    else
+      hipLaunchKernelGGL((k_sweep<T, kAligned, TreeRows>), sgrid, dim3(kThreads), 0, st, t, d, tok, temp,
+                         TreeRows{shape}, B, V, nc, force_greedy, part, xd, rcnt, WinArgs{});
   }
-  // Filters: thresholds and kept masses per swept row, as for the chain.
-  const bool filtered = (top_k || top_p) && !force_greedy;
   RowFilter* filt = filtered ? reinterpret_cast<RowFilter*>(ws + p.filt_off) : nullptr;
+  if (win && per_seq)
+    hipLaunchKernelGGL((k_filter_win<TreeRowsSeq>), dim3(B * R), dim3(64), 0, st, temp, top_k,
+                       top_p, TreeRowsSeq{shapes, N}, V, nc, force_greedy, part, filt, wa);
+  else if (win)
+    hipLaunchKernelGGL((k_filter_win<TreeRows>), dim3(B * R), dim3(64), 0, st, temp, top_k,
+                       top_p, TreeRows{shape}, V, nc, force_greedy, part, filt, wa);
   if (filtered && per_seq)
     hipLaunchKernelGGL((k_filter<T, kAligned, TreeRowsSeq>), dim3(B * R), dim3(kFilterThreads), 0, st,
-                       t, d, temp, top_k, top_p, TreeRowsSeq{shapes, N}, V, nc, force_greedy, part, filt);
+                       t, d, temp, top_k, top_p, TreeRowsSeq{shapes, N}, V, nc, force_greedy, part, filt,
+                       wa);
   else if (filtered)
     hipLaunchKernelGGL((k_filter<T, kAligned, TreeRows>), dim3(B * R), dim3(kFilterThreads), 0, st, t,
-                       d, temp, top_k, top_p, TreeRows{shape}, V, nc, force_greedy, part, filt);
+                       d, temp, top_k, top_p, TreeRows{shape}, V, nc, force_greedy, part, filt, wa);
   const int key16 = sizeof(T) == 2 ? 1 : 0;
   hipLaunchKernelGGL(k_tree_decide, dim3(B), dim3(kDecideThreads), 0, st, tok, uni, temp, shape, shapes,
                      R, V, nc, force_greedy, part, filt, key16, xd, rowstat, dec, state, out_tok,
@@ -2379,6 +2911,11 @@ extern "C" size_t spec_reject_sample_workspace_bytes(int B, int K, int V) {
   return sv::reject_plan(B, K, V).total;
 }
 
+extern "C" size_t spec_reject_sample_filtered_workspace_bytes(int B, int K, int V) {
+  if (B <= 0 || K < 1 || K > SV_MAX_K || V < 1) return 0;
+  return sv::reject_plan(B, K, V).total_filtered;
+}
+
 static int reject_impl(const char* fn, const void* target_logits, const void* draft_logits,
                        const int32_t* draft_tokens, const float* uniforms, const float* temperature,
                        const int32_t* top_k, const float* top_p, int32_t* out_tokens,
@@ -2397,7 +2934,12 @@ static int reject_impl(const char* fn, const void* target_logits, const void* dr
   if (!target_logits || !draft_tokens || !uniforms || !temperature || !out_tokens ||
       !num_accepted || !kv_len || !workspace)
     return SV_ERR_INVALID_ARG;
-  if (workspace_bytes < spec_reject_sample_workspace_bytes(B, K, V)) return SV_ERR_WORKSPACE;
+  // A filtered call given spec_reject_sample_filtered_workspace_bytes also
+  // has room for the sweep's window; with the plain size it takes k_filter's
+  // radix passes for every row.
+  const sv::RejectPlan plan = sv::reject_plan(B, K, V);
+  if (workspace_bytes < plan.total) return SV_ERR_WORKSPACE;
+  const bool win_ws = workspace_bytes >= plan.total_filtered;
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return SV_ERR_INVALID_ARG;
   const int force_greedy = draft_logits == nullptr ? 1 : 0;
   const void* drf = draft_logits ? draft_logits : target_logits;   // never read when greedy
@@ -2422,18 +2964,18 @@ static int reject_impl(const char* fn, const void* target_logits, const void* dr
     const bool al = (V % 8 == 0) && (align_bits & 15) == 0;
     e = al ? sv::launch_all<uint16_t, true>(target_logits, drf, draft_tokens, uniforms, temperature,
                                             out_tokens, num_accepted, kv_len, counters, B, K, V,
-                                            force_greedy, ws, st, top_k, top_p)
+                                            force_greedy, ws, st, top_k, top_p, win_ws)
            : sv::launch_all<uint16_t, false>(target_logits, drf, draft_tokens, uniforms, temperature,
                                              out_tokens, num_accepted, kv_len, counters, B, K, V,
-                                             force_greedy, ws, st, top_k, top_p);
+                                             force_greedy, ws, st, top_k, top_p, win_ws);
   } else {
     const bool al = (V % 4 == 0) && (align_bits & 15) == 0;
     e = al ? sv::launch_all<float, true>(target_logits, drf, draft_tokens, uniforms, temperature,
                                          out_tokens, num_accepted, kv_len, counters, B, K, V,
-                                         force_greedy, ws, st, top_k, top_p)
+                                         force_greedy, ws, st, top_k, top_p, win_ws)
            : sv::launch_all<float, false>(target_logits, drf, draft_tokens, uniforms, temperature,
                                           out_tokens, num_accepted, kv_len, counters, B, K, V,
-                                          force_greedy, ws, st, top_k, top_p);
+                                          force_greedy, ws, st, top_k, top_p, win_ws);
   }
   const int status = e == hipSuccess ? SV_OK : SV_ERR_HIP;
   return chk ? sv::finish(fn, st, status) : status;
@@ -2531,6 +3073,11 @@ extern "C" size_t spec_reject_sample_tree_workspace_bytes(int B, int N, int V) {
   return sv::tree_plan(B, N, V).total;
 }
 
+extern "C" size_t spec_reject_sample_tree_filtered_workspace_bytes(int B, int N, int V) {
+  if (B <= 0 || N < 1 || N > sv::kMaxTree || V < 1) return 0;
+  return sv::tree_plan(B, N, V).total_filtered;
+}
+
 // per_seq false: parent is the batch's tree (host array); true: dparents
 // holds one per sequence ([B, N] device array, NULL only for B == 0).
 static int tree_impl(const char* fn, const void* target_logits, const void* draft_logits,
@@ -2554,7 +3101,10 @@ static int tree_impl(const char* fn, const void* target_logits, const void* draf
   if (!target_logits || !tokens || !uniforms || !temperature || !out_tokens || !out_nodes ||
       !num_accepted || !kv_len || !workspace)
     return SV_ERR_INVALID_ARG;
-  if (workspace_bytes < spec_reject_sample_tree_workspace_bytes(B, N, V)) return SV_ERR_WORKSPACE;
+  // As for the chain: the filtered size adds the sweep's window.
+  const sv::TreePlan plan = sv::tree_plan(B, N, V);
+  if (workspace_bytes < plan.total) return SV_ERR_WORKSPACE;
+  const bool win_ws = workspace_bytes >= plan.total_filtered;
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return SV_ERR_INVALID_ARG;
   const int force_greedy = draft_logits == nullptr ? 1 : 0;
   const void* drf = draft_logits ? draft_logits : target_logits;   // never read when greedy
@@ -2580,18 +3130,18 @@ static int tree_impl(const char* fn, const void* target_logits, const void* draf
     const bool al = (V % 8 == 0) && (align_bits & 15) == 0;
     e = al ? sv::launch_tree<uint16_t, true>(target_logits, drf, shape, dparents, tokens, uniforms,
                                              temperature, out_tokens, out_nodes, num_accepted, kv_len,
-                                             counters, B, V, force_greedy, ws, st, top_k, top_p)
+                                             counters, B, V, force_greedy, ws, st, top_k, top_p, win_ws)
            : sv::launch_tree<uint16_t, false>(target_logits, drf, shape, dparents, tokens, uniforms,
                                               temperature, out_tokens, out_nodes, num_accepted, kv_len,
-                                              counters, B, V, force_greedy, ws, st, top_k, top_p);
+                                              counters, B, V, force_greedy, ws, st, top_k, top_p, win_ws);
   } else {
     const bool al = (V % 4 == 0) && (align_bits & 15) == 0;
     e = al ? sv::launch_tree<float, true>(target_logits, drf, shape, dparents, tokens, uniforms,
                                           temperature, out_tokens, out_nodes, num_accepted, kv_len,
-                                          counters, B, V, force_greedy, ws, st, top_k, top_p)
+                                          counters, B, V, force_greedy, ws, st, top_k, top_p, win_ws)
            : sv::launch_tree<float, false>(target_logits, drf, shape, dparents, tokens, uniforms,
                                            temperature, out_tokens, out_nodes, num_accepted, kv_len,
-                                           counters, B, V, force_greedy, ws, st, top_k, top_p);
+                                           counters, B, V, force_greedy, ws, st, top_k, top_p, win_ws);
   }
   const int status = e == hipSuccess ? SV_OK : SV_ERR_HIP;
   return chk ? sv::finish(fn, st, status) : status;

@@ -53,6 +53,18 @@ def test_workspace_sizes(lib):
     # 15 rows x 32 chunks x 8 B per sequence for the row statistics at least.
     assert a >= 64 * 15 * 32 * 8
     assert sv.reject_sample_workspace_bytes(128, 7, 128256) > a
+    # The filtered sizes add the sweep's window: per swept row, two float64
+    # sums per chunk and a 16-bit count per window value (512) per sweep block
+    # of 4 chunks; invalid sizes give 0 as for the plain queries.
+    f = sv.reject_sample_filtered_workspace_bytes(64, 7, 128256)
+    nc = (128256 + 4095) // 4096
+    assert f % 256 == 0 and f >= a + 64 * 15 * ((nc + 3) // 4) * 512 * 2 + 64 * 15 * nc * 16
+    assert sv.reject_sample_filtered_workspace_bytes(0, 7, 128256) == 0
+    assert sv.reject_sample_filtered_workspace_bytes(64, 17, 128256) == 0
+    t = sv.reject_sample_tree_workspace_bytes(64, 15, 128256)
+    tf = sv.reject_sample_tree_filtered_workspace_bytes(64, 15, 128256)
+    assert tf % 256 == 0 and tf >= t + 64 * 29 * ((nc + 3) // 4) * 512 * 2
+    assert sv.reject_sample_tree_filtered_workspace_bytes(4, 18, 100) == 0
     w = sv.verify_attn_workspace_bytes(64, 7, 32, 8, 128, 8192)
     assert w % 256 == 0 and w > 0
     assert sv.verify_attn_workspace_bytes(1, 1, 1, 1, 64, 0) == 0   # one split: no partials

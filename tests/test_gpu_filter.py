@@ -39,12 +39,14 @@ def _filtered_drafts(inp, top_k, top_p, seed):
 
 
 def _case(sv, dev, seed, B, K, V, top_k, top_p, dtype="bf16", temp=1.0, sigma=0.8, idx=None,
-          std=2.0, spikes=None, max_f3=None):
+          std=2.0, spikes=None, max_f3=None, ws="window"):
     """One filtered call against the oracle.  F1 / F2 may exclude a few
     sequences at most (as for the plain verifier); F3 at most ``max_f3``
     (default 2 + B // 50): a row's top-p edge lies within 1e-6 of top_p only
     when the entries at the edge carry little mass, which the cases that
-    allow more say why."""
+    allow more say why.  ws "window": the binding's workspace (room for the
+    sweep's window); "plain": spec_reject_sample_workspace_bytes only, so
+    every row takes the filter's radix passes."""
     top_k = np.broadcast_to(np.asarray(top_k, np.int32), (B,)).copy()
     top_p = np.broadcast_to(np.asarray(top_p, np.float32), (B,)).copy()
     label = "filter seed=%d B=%d K=%d V=%d %s k=%s p=%s" % (seed, B, K, V, dtype,
@@ -65,9 +67,14 @@ def _case(sv, dev, seed, B, K, V, top_k, top_p, dtype="bf16", temp=1.0, sigma=0.
     kv0 = np.full(B, 500, np.int32)
     t = {k: to_device(v, dev) for k, v in inp.items()}
     kv = to_device(kv0, dev)
+    workspace = None
+    if ws == "plain":
+        import torch
+        workspace = torch.empty(sv.reject_sample_workspace_bytes(B, K, V), dtype=torch.uint8,
+                                device=dev)
     out, n = sv.reject_sample(t["target"], t["draft"], t["draft_tokens"], t["uniforms"],
                               t["temperature"], kv, top_k=to_device(top_k, dev),
-                              top_p=to_device(top_p, dev))
+                              top_p=to_device(top_p, dev), workspace=workspace)
     out, n = from_device(out), from_device(n)
     sel = slice(None) if idx is None else idx
     ref = of.reject_sample_filtered(inp["target"][sel], inp["draft"][sel], inp["draft_tokens"][sel],
@@ -121,6 +128,17 @@ def test_dtypes_and_ragged(gpu_lib, dev, V, dtype):
 def test_llama8b_vocab(gpu_lib, dev):
     c = CONFIGS["llama8b_b64"]
     _case(gpu_lib, dev, 5, 16, c.K, c.V, 50, 0.9)
+
+
+@pytest.mark.parametrize("ws", ["window", "plain"])
+@pytest.mark.parametrize("top_k,top_p,temp", [(50, 1.0, 1.0), (0, 0.9, 1.0), (20, 0.8, 0.6),
+                                               (0, 0.9, 1.3), (0, 0.5, 1.0)])
+def test_llama8b_vocab_window_and_radix(gpu_lib, dev, top_k, top_p, temp, ws):
+    """The serving vocabulary through both ways of taking the thresholds:
+    counted in the sweep's window (the thresholds of these rows fall inside
+    it) and the filter's radix passes (the plain workspace)."""
+    c = CONFIGS["llama8b_b64"]
+    _case(gpu_lib, dev, 13, 16, c.K, c.V, top_k, top_p, temp=temp, ws=ws)
 
 
 def test_off_settings_equal_the_plain_call(gpu_lib, dev):
