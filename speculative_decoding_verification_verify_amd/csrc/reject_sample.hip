@@ -163,23 +163,23 @@ struct RowFilter {
 };
 
 // The window a filtered sweep counts (bf16 rows of sampling sequences with
-// a top-k or top-p filter): kWinKeys consecutive 16-bit keys (the keys of
-// one binade of bf16 values are 128 in a row), placed from a fixed sample of
-// the row:
-//  * top-k (with or without top-p): from kWinKBelow keys under the largest
-//    entry of kWinLines 64-entry runs spread evenly over the row (k up to
-//    V / 256; all kWinKeys keys for larger k) to kWinTopMargin keys above it.
-//    Every sweep block of the row reads the same runs and derives the same
-//    window.  The k-th largest value and every value above it are usually
-//    inside; an entry above the window sends the row to k_filter's radix
-//    passes.
-//  * top-p alone: k_win_prep estimates the threshold from kPrepLines runs
-//    (the value where the sample's own mass from the top reaches top_p); the
-//    window reaches kWinPBelow keys under it.  Entries above the window only
-//    add their mass (summed in float64), entries below it only to the row's.
-// k_filter_win then reads a row's thresholds from the counts instead of
-// passes over the row; a row whose threshold is not inside takes the passes.
+// a top-k or top-p filter): consecutive 16-bit keys (the keys of one binade
+// of bf16 values are 128 in a row), placed from a fixed sample of the row:
+//  * top-k (with or without top-p): kWinKeys keys, from kWinKBelow keys under
+//    the largest entry of kWinLines 64-entry runs spread evenly over the row
+//    (k up to V / 256; all kWinKeys keys for larger k) to kWinTopMargin keys
+//    above it.  Every sweep block of the row reads the same runs and derives
+//    the same window.
+//  * top-p alone: kWinPKeys keys from kWinPBelow keys under the threshold
+//    k_win_prep estimates from kPrepLines runs (the value where the sample's
+//    own mass from the top reaches top_p): the row's maximum is usually
+//    seven binades above the window's lowest value at most.
+// The threshold and every value above it are usually inside; an entry above
+// the window sends the row to k_filter's radix passes.  k_filter_win reads
+// a row's thresholds from the counts instead of passes over the row.
 constexpr int kWinKeys = 512;
+constexpr int kWinPKeys = 1024;
+constexpr int kWinSlot = 1024;         // counts kept per sweep block (the larger window)
 constexpr int kWinTopMargin = 192;
 constexpr int kWinKBelow = 128;
 constexpr int kWinPBelow = 128;
@@ -192,10 +192,11 @@ struct WinArgs {
   const int32_t* top_k;  // [B] or null
   const float* top_p;    // [B] or null
   double* partd;         // [rows][nc]: top-p alone: each chunk's sum 2^(x c - fl(xmax c)) in float64
-  double* parta;         // [rows][nc]: the same over the entries above the window
-  uint16_t* whist;       // [rows][nblk][kWinKeys]: entries per window value, per sweep block
-  uint32_t* wflag;       // [rows][nblk]: 1 when the block saw an entry above a top-k window
-  uint32_t* wwin;        // [rows]: the window, lowest key | highest key << 16 (0: decided)
+  uint16_t* whist;       // [rows][nblk][kWinSlot]: entries per window value, per sweep block
+  uint32_t* wflag;       // [rows][nblk]: 1 when the block saw an entry above the window
+  uint32_t* wwin;        // [rows]: the window, lowest key | highest key << 16
+  uint32_t* fall;        // [rows]: rows k_filter_win leaves to the radix passes, nfall of them
+  uint32_t* nfall;       // [1], cleared by the sweep
   int nblk;              // sweep blocks per row
 };
 
@@ -473,11 +474,10 @@ __device__ __forceinline__ int sample_vec(int i, int nruns, int nvec) {
 // chunk's raw maximum, and the count of every value of the row's window
 // (see kWinKeys) among the block's entries.  A filtered row's law is
 // normalised over its kept set, so the decision takes the kept mass from
-// k_filter instead of the sweep's sum: only top-p alone sums masses here
-// (its target needs the row's whole mass, and the entries above its window
-// add theirs), in the chunk's own frame, in fp32 per vector of 8 and float64
-// beyond (partd, parta; part.y gets the chunk's sum).  A top-k row with an
-// entry above its window sets the block's flag: k_filter then takes its
+// k_filter instead of the sweep's sum: only top-p alone sums masses here (its
+// target needs the row's whole mass), in the chunk's own frame, in fp32 per
+// vector of 8 and float64 beyond (partd; part.y gets the chunk's sum).  An
+// entry above the window sets the block's flag: k_filter then takes its
 // radix passes for the row.  All four waves reach both barriers (a wave past
 // the row's last chunk only takes part in the counts' write-out).
 template <class Rows>
@@ -489,9 +489,9 @@ __device__ __forceinline__ void sweep_window_block(const uint16_t* __restrict__ 
                                                    const WinArgs& wa) {
   constexpr int VN = Vec16<uint16_t>::N;
   constexpr int IT = kSweepChunk / (64 * VN);
-  static_assert(kWinKeys == 2 * kThreads, "two window values per thread in the write-out");
+  static_assert(kWinSlot == 4 * kThreads && kWinKeys == 2 * kThreads, "window values per thread");
   static_assert(kWinLines * 8 == 64, "one sampled vector per lane");
-  __shared__ uint32_t s_hist[kWinKeys + 64];        // + one spare bin per lane
+  __shared__ uint32_t s_hist[kWinSlot + 64];       // + one spare bin per lane
   __shared__ uint32_t s_flag;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int chunk = blockIdx.y * 4 + wave;
@@ -515,8 +515,8 @@ __device__ __forceinline__ void sweep_window_block(const uint16_t* __restrict__ 
       for (int it = 0; it < IT; ++it) load_vec<uint16_t, true, true>(src, base + it * 64 * VN, V, x[it]);
     }
   }
-  s_hist[tid] = 0u;
-  s_hist[tid + kThreads] = 0u;
+#pragma unroll
+  for (int i = 0; i < kWinSlot / kThreads; ++i) s_hist[tid + i * kThreads] = 0u;
   if (tid == 0) s_flag = 0u;
   uint32_t win = pwin;
   if (k_on) {
@@ -541,67 +541,61 @@ __device__ __forceinline__ void sweep_window_block(const uint16_t* __restrict__ 
     float xw = xm;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) xw = fmaxf(xw, __shfl_xor(xw, off, 64));
-    // A top-k row with an entry above its window goes to the radix passes.
-    if (k_on && __ballot(xm > fhi) && lane == 0) atomicOr(&s_flag, 1u);
-    // A window of positive values above +0 (the usual case): the bin from the
-    // raw bits without a branch, as bf16 bits - lowest bits (unsigned, so
-    // negative values and values below or above the window fall outside
-    // [0, kWinKeys)), outside entries counted in the lane's spare bin.
-    const bool pos = kbase > 0x8000u;
-    if (pos) {
+    // An entry above the window sends the row to the radix passes.
+    if (__ballot(xm > fhi) && lane == 0) atomicOr(&s_flag, 1u);
+    if (kbase > 0x8000u) {
+      // A window of positive values above +0 (the usual case): the bin from
+      // the raw bits without a branch, bf16 bits - lowest bits as an unsigned
+      // (negative values and values outside the window give more than the
+      // window holds), capped at the lane's spare bin.
       const uint32_t kb = kbase - 0x8000u;
 #pragma unroll
       for (int it = 0; it < IT; ++it)
 #pragma unroll
         for (int k = 0; k < VN; ++k) {
           const uint32_t d = (__float_as_uint(x[it][k]) >> 16) - kb;
-          atomicAdd(&s_hist[d < (uint32_t)kWinKeys ? d : (uint32_t)(kWinKeys + lane)], 1u);
+          atomicAdd(&s_hist[min(d, (uint32_t)(kWinSlot + lane))], 1u);
+        }
+    } else {
+#pragma unroll
+      for (int it = 0; it < IT; ++it)
+#pragma unroll
+        for (int k = 0; k < VN; ++k) {
+          const float v = x[it][k];
+          if (v >= flo && v <= fhi) atomicAdd(&s_hist[(key32_of(v) >> 16) - kbase], 1u);
         }
     }
-    // Top-p alone: masses 2^(x c - fl(xw c)) (entries past V are -inf: 0),
-    // and apart those of the entries above the window.
-    const bool sum = !k_on;
-    const float c = kLog2e / t;
-    const float m = xw != -INFINITY ? xw * c : 0.f;
-    double sd = 0.0, sa = 0.0;
+    double sd = 0.0;
+    if (!k_on && xw != -INFINITY) {
+      // Top-p alone: masses 2^(x c - fl(xw c)) (entries past V are -inf: 0).
+      const float c = kLog2e / t;
+      const float m = xw * c;
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      float vs = 0.f, va = 0.f;
+      for (int it = 0; it < IT; ++it) {
+        float vs = 0.f;
 #pragma unroll
-      for (int k = 0; k < VN; ++k) {
-        const float v = x[it][k];
-        if (sum) {
-          const float e = exp2_dev(__builtin_fmaf(v, c, -m));
-          vs += e;
-          va += v > fhi ? e : 0.f;
-        }
-        if (!pos && v >= flo && v <= fhi) atomicAdd(&s_hist[(key32_of(v) >> 16) - kbase], 1u);
-      }
-      if (sum) {
+        for (int k = 0; k < VN; ++k) vs += exp2_dev(__builtin_fmaf(x[it][k], c, -m));
         sd += (double)vs;
-        sa += (double)va;
       }
-    }
-    if (sum) {
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        sd += __shfl_xor(sd, off, 64);
-        sa += __shfl_xor(sa, off, 64);
-      }
+      for (int off = 32; off > 0; off >>= 1) sd += __shfl_xor(sd, off, 64);
     }
     if (lane == 0) {
       part[(size_t)row * nc + chunk] = make_float2(xw, (float)sd);
-      if (!k_on) {
-        wa.partd[(size_t)row * nc + chunk] = sd;
-        wa.parta[(size_t)row * nc + chunk] = sa;
-      }
+      if (!k_on) wa.partd[(size_t)row * nc + chunk] = sd;
     }
   }
   __syncthreads();                                 // every entry counted
   // A block holds at most 4 kSweepChunk = 16384 entries: counts fit 16 bits.
-  const int i0 = 2 * tid;
-  const size_t hb = ((size_t)row * wa.nblk + blockIdx.y) * kWinKeys;
-  *reinterpret_cast<uint32_t*>(wa.whist + hb + i0) = s_hist[i0] | (s_hist[i0 + 1] << 16);
+  const size_t hb = ((size_t)row * wa.nblk + blockIdx.y) * kWinSlot;
+  if (k_on) {
+    const int i0 = 2 * tid;
+    *reinterpret_cast<uint32_t*>(wa.whist + hb + i0) = s_hist[i0] | (s_hist[i0 + 1] << 16);
+  } else {
+    const int i0 = 4 * tid;
+    *reinterpret_cast<uint2*>(wa.whist + hb + i0) =
+        make_uint2(s_hist[i0] | (s_hist[i0 + 1] << 16), s_hist[i0 + 2] | (s_hist[i0 + 3] << 16));
+  }
   if (tid == 0) {
     wa.wflag[(size_t)row * wa.nblk + blockIdx.y] = s_flag;
     if (k_on && blockIdx.y == 0) wa.wwin[row] = win;
@@ -620,8 +614,10 @@ __global__ __launch_bounds__(kThreads) void k_sweep(
     const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ dtok,
     const float* __restrict__ temp, Rows rows, int B, int V, int nc, int force_greedy,
     float2* __restrict__ part, float* __restrict__ xd, unsigned* __restrict__ pcnt, WinArgs wa) {
-  // Clears the per-sequence pass counts the later kernels count in with.
+  // Clears the per-sequence pass counts the later kernels count in with (and
+  // the filter's fallback list).
   if (blockIdx.y == 0 && (int)blockIdx.x < B && threadIdx.x == 0) pcnt[blockIdx.x] = 0u;
+  if (kWin && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *wa.nfall = 0u;
   const int R = rows.count();
   // Every sequence's target rows first, then the draft rows: a greedy
   // sequence's draft-row workgroups leave at once, and in this order they are
@@ -1134,30 +1130,31 @@ __device__ __forceinline__ unsigned long long filter_kept_mass(const T* __restri
   return tot;
 }
 
-// The largest of a wave's 512 bins (8 per lane: lane l holds bins 8l ..
-// 8l + 7) whose running total from the top, plus `above`, reaches target;
-// -1 when none does.  ab_out: the running total above the bin (the same in
-// every lane).  The order of the integer adds does not matter.
-__device__ __forceinline__ int wave_pick8(const unsigned long long (&v)[8], double target,
-                                          unsigned long long above, int lane,
-                                          unsigned long long& ab_out) {
+// The largest of a wave's 64 N bins (lane l holds bins N l .. N l + N - 1)
+// whose running total from the top reaches target; -1 when none does.
+// ab_out: the running total above the bin, vs_out the bin's own value (both
+// the same in every lane).  The order of the integer adds does not matter.
+template <int N>
+__device__ __forceinline__ int wave_pick(const unsigned long long (&v)[N], double target, int lane,
+                                         unsigned long long& ab_out, unsigned long long& vs_out) {
   unsigned long long loc = 0ull;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) loc += v[k];
+  for (int k = 0; k < N; ++k) loc += v[k];
   unsigned long long suf = loc;                    // lanes l .. 63
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const unsigned long long t = __shfl_down(suf, off, 64);
     if (lane + off < 64) suf += t;
   }
-  unsigned long long acc = above + (suf - loc);
+  unsigned long long acc = suf - loc;
   int hit = -1;
-  unsigned long long ab = 0ull;
+  unsigned long long ab = 0ull, vs = 0ull;
 #pragma unroll
-  for (int k = 7; k >= 0; --k) {
+  for (int k = N - 1; k >= 0; --k) {
     if (hit < 0 && (double)(acc + v[k]) >= target) {
-      hit = 8 * lane + k;
+      hit = N * lane + k;
       ab = acc;
+      vs = v[k];
     }
     acc += v[k];
   }
@@ -1165,10 +1162,96 @@ __device__ __forceinline__ int wave_pick8(const unsigned long long (&v)[8], doub
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) h = max(h, __shfl_xor(h, off, 64));
   if (h < 0) return -1;
-  const int owner = __builtin_amdgcn_readfirstlane(h >> 3);
-  ab_out = ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(ab >> 32), owner) << 32) |
-           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)ab, owner);
+  const int owner = __builtin_amdgcn_readfirstlane(h / N);
+  auto bcast = [&](unsigned long long x) {
+    return ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(x >> 32), owner) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, owner);
+  };
+  ab_out = bcast(ab);
+  vs_out = bcast(vs);
   return h;
+}
+
+// The thresholds of one row from its window of 64 N values (one wave; see
+// k_filter_win): writes the RowFilter and returns true, or false when the
+// window does not decide the row.
+template <int N>
+__device__ __forceinline__ bool window_thresholds(int row, int nc, float c, float mc, int tk, float tp,
+                                                  bool k_on, bool p_on, uint32_t kbase,
+                                                  const float2* __restrict__ part, const WinArgs& wa,
+                                                  RowFilter* __restrict__ filt, int lane) {
+  // Every load first: the blocks' flags and counts and, for top-p alone, the
+  // chunk sums (after the caller's chunk maxima).
+  bool bad = false;
+  for (int y = lane; y < wa.nblk; y += 64) bad = bad || wa.wflag[(size_t)row * wa.nblk + y] != 0u;
+  uint32_t cnt[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) cnt[k] = 0u;
+  const uint16_t* hp = wa.whist + (size_t)row * wa.nblk * kWinSlot + N * lane;
+  for (int y0 = 0; y0 < wa.nblk; y0 += 8) {
+    uint4 v[8][N / 8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int h = 0; h < N / 8; ++h)
+        v[q][h] = y0 + q < wa.nblk
+                      ? *reinterpret_cast<const uint4*>(hp + (size_t)(y0 + q) * kWinSlot + 8 * h)
+                      : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int h = 0; h < N / 8; ++h) {
+        const uint32_t w4[4] = {v[q][h].x, v[q][h].y, v[q][h].z, v[q][h].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          cnt[8 * h + 2 * k] += w4[k] & 0xFFFFu;
+          cnt[8 * h + 2 * k + 1] += w4[k] >> 16;
+        }
+      }
+  }
+  double z = 0.0;
+  if (p_on && !k_on) {
+    // The row's mass in its frame: chunk sums in chunk order per lane, then
+    // a fixed-order wave sum.
+    for (int k = lane; k < nc; k += 64) {
+      const size_t i = (size_t)row * nc + k;
+      const float mk = part[i].x * c;             // the chunk's frame, as the sweep took it
+      z += wa.partd[i] * exp2((double)mk - (double)mc);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off, 64);
+  }
+  if (__ballot(bad)) return false;
+  unsigned long long v[N], ab = 0ull, vs = 0ull;
+  int sel = 0;
+  if (k_on) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] = cnt[k];
+    sel = wave_pick<N>(v, (double)tk, lane, ab, vs);
+    if (sel < 0) return false;                     // fewer than k entries in the window
+  }
+  // Masses of the values from the top-k threshold up (all of the window
+  // without top-k).
+  unsigned long long loc = 0ull;
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const int i = N * lane + k;
+    const float xv = key16_value(kbase + (uint32_t)i);
+    v[k] = i >= sel ? cnt[k] * fixed40(exp2_dev(__builtin_fmaf(xv, c, -mc))) : 0ull;
+    loc += v[k];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) loc += __shfl_xor(loc, off, 64);
+  unsigned long long kept = loc;                   // the set's mass
+  if (p_on) {
+    const double target = k_on ? (double)tp * (double)loc : (double)tp * z * kFix;
+    if ((double)loc < target) return false;        // the threshold lies under the window
+    sel = wave_pick<N>(v, target, lane, ab, vs);
+    if (sel < 0) return false;
+    kept = ab + vs;
+  }
+  if (lane == 0) filt[row] = RowFilter{kbase + (uint32_t)sel, 0u, (double)kept / kFix};
+  return true;
 }
 
 // k_filter_win: grid (B * rows.count()), one wave per row: the thresholds of
@@ -1178,18 +1261,17 @@ __device__ __forceinline__ int wave_pick8(const unsigned long long (&v)[8], doub
 // value's mass is its count times its weight, the same integer as the sum of
 // its entries' weights in the radix passes, and the masses from the top give
 // the top-p threshold and the kept mass.  Top-p alone takes the row's mass
-// and the mass above its window from the sweep's float64 chunk sums, moved
-// into the row's frame.  A row it decides gets its RowFilter and wwin[row] =
-// 0, which k_filter, launched next, reads as "done".  It leaves a row to
-// k_filter's radix passes when the window does not decide it: a top-k row
-// with an entry above its window or fewer than k entries in it, or a top-p
-// target reached above the window or not reached at its lowest value.
+// from the sweep's float64 chunk sums, moved into the row's frame.  Rows
+// without a filter get the empty RowFilter.  A row the window does not decide
+// (an entry above the window, fewer than k entries in it, or a top-p target
+// not reached at its lowest value) goes on the list k_filter, launched next,
+// takes through the radix passes.
 template <class Rows>
 __global__ __launch_bounds__(64) void k_filter_win(
     const float* __restrict__ temp, const int32_t* __restrict__ top_k, const float* __restrict__ top_p,
     Rows rows, int V, int nc, int force_greedy, const float2* __restrict__ part,
     RowFilter* __restrict__ filt, WinArgs wa) {
-  static_assert(kWinKeys == 8 * 64, "eight window values per lane");
+  static_assert(kWinKeys == 8 * 64 && kWinPKeys == 16 * 64, "8 or 16 window values per lane");
   const int R = rows.count();
   const int row = blockIdx.x;
   const int b = row / R;
@@ -1201,106 +1283,30 @@ __global__ __launch_bounds__(64) void k_filter_win(
   const float tp = top_p ? top_p[b] : 1.f;
   const bool k_on = tk > 0 && tk < V;
   const bool p_on = tp > 0.f && tp < 1.f;
-  if (!(t > 0.f) || (!k_on && !p_on)) return;
+  if (!(t > 0.f) || (!k_on && !p_on)) {
+    if (lane == 0) filt[row] = RowFilter{0u, 0u, 0.0};
+    return;
+  }
   const float c = kLog2e / t;
   const uint32_t kbase = wa.wwin[row] & 0xFFFFu;
-  // Every load first: the blocks' flags and counts, the chunk maxima and,
-  // for top-p alone, the chunk sums.
-  bool bad = false;
-  if (k_on)
-    for (int y = lane; y < wa.nblk; y += 64) bad = bad || wa.wflag[(size_t)row * wa.nblk + y] != 0u;
-  uint32_t cnt[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-  const uint16_t* hp = wa.whist + (size_t)row * wa.nblk * kWinKeys + 8 * lane;
-  for (int y0 = 0; y0 < wa.nblk; y0 += 16) {
-    uint4 v[16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q)
-      v[q] = y0 + q < wa.nblk ? *reinterpret_cast<const uint4*>(hp + (size_t)(y0 + q) * kWinKeys)
-                              : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const uint32_t w4[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        cnt[2 * k] += w4[k] & 0xFFFFu;
-        cnt[2 * k + 1] += w4[k] >> 16;
-      }
-    }
-  }
   float xr = -INFINITY;
   for (int k = lane; k < nc; k += 64) xr = fmaxf(xr, part[(size_t)row * nc + k].x);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) xr = fmaxf(xr, __shfl_xor(xr, off, 64));
   const float mc = xr * c;
-  if (__ballot(bad)) return;
-  unsigned long long v[8], ab = 0ull;
-  int sel = 0;
-  if (k_on) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = cnt[k];
-    sel = wave_pick8(v, (double)tk, 0ull, lane, ab);
-    if (sel < 0) return;                           // fewer than k entries in the window
-  }
-  // Masses of the values from the top-k threshold up (all of the window
-  // without top-k).
-  unsigned long long loc = 0ull;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int i = 8 * lane + k;
-    const float xv = key16_value(kbase + (uint32_t)i);
-    v[k] = i >= sel ? cnt[k] * fixed40(exp2_dev(__builtin_fmaf(xv, c, -mc))) : 0ull;
-    loc += v[k];
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) loc += __shfl_xor(loc, off, 64);
-  unsigned long long kept = loc;                   // the set's mass
-  if (p_on) {
-    double target;
-    unsigned long long above = 0ull;
-    if (k_on) {
-      target = (double)tp * (double)loc;
-    } else {
-      // The row's mass and the mass above the window, in the row's frame:
-      // chunk sums in chunk order per lane, then a fixed-order wave sum.
-      double z = 0.0, za = 0.0;
-      for (int k = lane; k < nc; k += 64) {
-        const size_t i = (size_t)row * nc + k;
-        const float mk = part[i].x * c;             // the chunk's frame, as the sweep took it
-        const double f = exp2((double)mk - (double)mc);
-        z += wa.partd[i] * f;
-        za += wa.parta[i] * f;
-      }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        z += __shfl_xor(z, off, 64);
-        za += __shfl_xor(za, off, 64);
-      }
-      target = (double)tp * z * kFix;
-      const double abv = za * kFix;
-      if (abv >= target || abv + (double)loc < target) return;
-      above = (unsigned long long)llrint(abv);
-    }
-    sel = wave_pick8(v, target, above, lane, ab);
-    if (sel < 0) return;
-    const int owner = __builtin_amdgcn_readfirstlane(sel >> 3);
-    unsigned long long vs = 0ull;
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (8 * lane + k == sel) vs = v[k];
-    kept = ab + (((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(vs >> 32), owner) << 32) |
-                 (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)vs, owner));
-  }
-  if (lane == 0) {
-    filt[row] = RowFilter{kbase + (uint32_t)sel, 0u, (double)kept / kFix};
-    wa.wwin[row] = 0u;
-  }
+  const bool done = k_on ? window_thresholds<8>(row, nc, c, mc, tk, tp, k_on, p_on, kbase, part, wa, filt, lane)
+                         : window_thresholds<16>(row, nc, c, mc, tk, tp, k_on, p_on, kbase, part, wa, filt, lane);
+  if (!done && lane == 0) wa.fall[atomicAdd(wa.nfall, 1u)] = (uint32_t)row;
 }
 
+// The radix selection of one row (k_filter).
 template <typename T, bool kAligned, class Rows>
-__global__ __launch_bounds__(kFilterThreads, 4) void k_filter(
-    const T* __restrict__ tgt, const T* __restrict__ drf, const float* __restrict__ temp,
-    const int32_t* __restrict__ top_k, const float* __restrict__ top_p, Rows rows, int V, int nc,
-    int force_greedy, const float2* __restrict__ part, RowFilter* __restrict__ filt, WinArgs wa) {
+__device__ __forceinline__ void filter_row(int row, const T* __restrict__ tgt, const T* __restrict__ drf,
+                                           const float* __restrict__ temp,
+                                           const int32_t* __restrict__ top_k,
+                                           const float* __restrict__ top_p, const Rows& rows, int V,
+                                           int nc, int force_greedy, const float2* __restrict__ part,
+                                           RowFilter* __restrict__ filt) {
   __shared__ unsigned long long h[kFilterBins];
   __shared__ unsigned long long s_w[kFilterWaves];
   __shared__ int s_pick[2 * kFilterWaves];
@@ -1310,7 +1316,6 @@ __global__ __launch_bounds__(kFilterThreads, 4) void k_filter(
   __shared__ unsigned long long hm[kFilterBins];      // top-k alone: masses per first-digit bin
   __shared__ float s_xr;
   const int R = rows.count();
-  const int row = blockIdx.x;
   const int b = row / R;
   const int j = row - b * R;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1324,7 +1329,6 @@ __global__ __launch_bounds__(kFilterThreads, 4) void k_filter(
     if (tid == 0) filt[row] = RowFilter{0u, 0u, 0.0};
     return;
   }
-  if (wa.wwin && wa.wwin[row] == 0u) return;     // decided by k_filter_win from the sweep's window
   const T* src = (rows.is_draft(j) ? drf : tgt) + rows.row(b, j) * (size_t)V;
   const float c = kLog2e / t;
   // The row's raw maximum, merged from the sweep's chunk maxima as the decision does.
@@ -1471,6 +1475,32 @@ __global__ __launch_bounds__(kFilterThreads, 4) void k_filter(
     kept_mass = filter_kept_mass<T, kAligned>(src, V, c, mc, flo, s_w);
   }
   if (tid == 0) filt[row] = RowFilter{lo >> kStop, 0u, (double)kept_mass / kFix};
+}
+
+// Without a window: one block per row (grid B * rows.count()).
+template <typename T, bool kAligned, class Rows>
+__global__ __launch_bounds__(kFilterThreads, 4) void k_filter(
+    const T* __restrict__ tgt, const T* __restrict__ drf, const float* __restrict__ temp,
+    const int32_t* __restrict__ top_k, const float* __restrict__ top_p, Rows rows, int V, int nc,
+    int force_greedy, const float2* __restrict__ part, RowFilter* __restrict__ filt) {
+  filter_row<T, kAligned, Rows>(blockIdx.x, tgt, drf, temp, top_k, top_p, rows, V, nc, force_greedy,
+                                part, filt);
+}
+
+// After k_filter_win: a grid of any size takes the rows on its list (a
+// kernel of its own: the loop's live values would spill k_filter's
+// registers).
+template <typename T, bool kAligned, class Rows>
+__global__ __launch_bounds__(kFilterThreads, 4) void k_filter_list(
+    const T* __restrict__ tgt, const T* __restrict__ drf, const float* __restrict__ temp,
+    const int32_t* __restrict__ top_k, const float* __restrict__ top_p, Rows rows, int V, int nc,
+    int force_greedy, const float2* __restrict__ part, RowFilter* __restrict__ filt, WinArgs wa) {
+  const uint32_t n = *wa.nfall;
+  for (uint32_t i = blockIdx.x; i < n; i += gridDim.x) {
+    filter_row<T, kAligned, Rows>((int)wa.fall[i], tgt, drf, temp, top_k, top_p, rows, V, nc,
+                                  force_greedy, part, filt);
+    __syncthreads();                               // the block's LDS is reused for the next row
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1802,8 +1832,8 @@ __global__ __launch_bounds__(kPrepLines * 8) void k_win_prep(
   for (int off = 32; off > 0; off >>= 1) sm = fmaxf(sm, __shfl_xor(sm, off, 64));
   const uint32_t kt = sample_topp_key(s_samp, sm, kLog2e / t, tp, lane);
   uint32_t kbase = kt >= kWinMinKey + kWinPBelow ? kt - kWinPBelow : kWinMinKey;
-  kbase = min(kbase, 0xFFFFu - (kWinKeys - 1));
-  if (lane == 0) wa.wwin[row] = kbase | ((kbase + (kWinKeys - 1)) << 16);
+  kbase = min(kbase, 0xFFFFu - (kWinPKeys - 1));
+  if (lane == 0) wa.wwin[row] = kbase | ((kbase + (kWinPKeys - 1)) << 16);
 }
 
 // One wave walks `cnt` masses (mass(i)) in order: returns the first index
@@ -2597,7 +2627,7 @@ __global__ __launch_bounds__(kThreads) void k_tree_draw(
 
 struct RejectPlan {
   size_t part_off, csum_off, csub_off, dec_off, xd_off, filt_off, cnt_off, total;
-  size_t partd_off, parta_off, whist_off, wflag_off, wwin_off, total_filtered;   // filtered bf16 calls only
+  size_t partd_off, whist_off, wflag_off, wwin_off, fall_off, nfall_off, total_filtered;   // filtered bf16 calls only
 };
 
 // The window arrays of a filtered call over `rows` swept rows, from offset
@@ -2607,19 +2637,21 @@ static inline size_t win_plan(P& p, size_t at, size_t rows, int V) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t nc = (size_t)sweep_chunks(V), nblk = (nc + 3) / 4;
   p.partd_off = at;
-  p.parta_off = p.partd_off + up(rows * nc * sizeof(double));
-  p.whist_off = p.parta_off + up(rows * nc * sizeof(double));
-  p.wflag_off = p.whist_off + up(rows * nblk * kWinKeys * sizeof(uint16_t));
+  p.whist_off = p.partd_off + up(rows * nc * sizeof(double));
+  p.wflag_off = p.whist_off + up(rows * nblk * kWinSlot * sizeof(uint16_t));
   p.wwin_off = p.wflag_off + up(rows * nblk * sizeof(uint32_t));
-  return p.wwin_off + up(rows * sizeof(uint32_t));
+  p.fall_off = p.wwin_off + up(rows * sizeof(uint32_t));
+  p.nfall_off = p.fall_off + up(rows * sizeof(uint32_t));
+  return p.nfall_off + 256;
 }
 
 template <class P>
 static inline WinArgs win_args(const P& p, char* ws, const int32_t* top_k, const float* top_p, int V) {
   return WinArgs{top_k, top_p, reinterpret_cast<double*>(ws + p.partd_off),
-                 reinterpret_cast<double*>(ws + p.parta_off), reinterpret_cast<uint16_t*>(ws + p.whist_off),
+                 reinterpret_cast<uint16_t*>(ws + p.whist_off),
                  reinterpret_cast<uint32_t*>(ws + p.wflag_off),
-                 reinterpret_cast<uint32_t*>(ws + p.wwin_off), (sweep_chunks(V) + 3) / 4};
+                 reinterpret_cast<uint32_t*>(ws + p.wwin_off), reinterpret_cast<uint32_t*>(ws + p.fall_off),
+                 reinterpret_cast<uint32_t*>(ws + p.nfall_off), (sweep_chunks(V) + 3) / 4};
 }
 
 static inline RejectPlan reject_plan(int B, int K, int V) {
@@ -2676,12 +2708,19 @@ static hipError_t launch_all(const void* tgt, const void* drf, const int32_t* dt
     hipLaunchKernelGGL((k_sweep<T, kAligned, ChainRows>), sgrid, dim3(kThreads), 0, st, t, d, dtok, temp,
                        ChainRows{K}, B, V, nc, force_greedy, part, xd, pcnt, WinArgs{});
   RowFilter* filt = filtered ? reinterpret_cast<RowFilter*>(ws + p.filt_off) : nullptr;
+  // After the window, k_filter only takes the rows left on its list: two
+  // blocks per CU (its occupancy) are one wave of launches.
+  const int fgrid = win ? std::min(B * R, 2 * device_cus()) : B * R;
   if (win)
     hipLaunchKernelGGL((k_filter_win<ChainRows>), dim3(B * R), dim3(64), 0, st, temp, top_k,
                        top_p, ChainRows{K}, V, nc, force_greedy, part, filt, wa);
   if (filtered)
-    hipLaunchKernelGGL((k_filter<T, kAligned, ChainRows>), dim3(B * R), dim3(kFilterThreads), 0, st, t,
-                       d, temp, top_k, top_p, ChainRows{K}, V, nc, force_greedy, part, filt, wa);
+    if (win)
+      hipLaunchKernelGGL((k_filter_list<T, kAligned, ChainRows>), dim3(fgrid), dim3(kFilterThreads), 0, st,
+                         t, d, temp, top_k, top_p, ChainRows{K}, V, nc, force_greedy, part, filt, wa);
+    else
+      hipLaunchKernelGGL((k_filter<T, kAligned, ChainRows>), dim3(fgrid), dim3(kFilterThreads), 0, st, t,
+                         d, temp, top_k, top_p, ChainRows{K}, V, nc, force_greedy, part, filt);
   const int key16 = sizeof(T) == 2 ? 1 : 0;
   // The draw joins the pass kernel while the chunk sums fit one wave.
   const bool fused = ncr <= 64;
@@ -2713,7 +2752,7 @@ static hipError_t launch_all(const void* tgt, const void* drf, const int32_t* dt
 struct TreePlan {
   size_t part_off, rowstat_off, csum_off, csub_off, dec_off, state_off, xd_off, rcnt_off, filt_off,
       shape_off, total;
-  size_t partd_off, parta_off, whist_off, wflag_off, wwin_off, total_filtered;   // filtered bf16 calls only
+  size_t partd_off, whist_off, wflag_off, wwin_off, fall_off, nfall_off, total_filtered;   // filtered bf16 calls only
 };
 
 static inline TreePlan tree_plan(int B, int N, int V) {
@@ -2870,19 +2909,26 @@ static hipError_t launch_tree(const void* tgt, const void* drf, const TreeShape&
                          TreeRows{shape}, B, V, nc, force_greedy, part, xd, rcnt, WinArgs{});
   }
   RowFilter* filt = filtered ? reinterpret_cast<RowFilter*>(ws + p.filt_off) : nullptr;
+  const int fgrid = win ? std::min(B * R, 2 * device_cus()) : B * R;
   if (win && per_seq)
     hipLaunchKernelGGL((k_filter_win<TreeRowsSeq>), dim3(B * R), dim3(64), 0, st, temp, top_k,
                        top_p, TreeRowsSeq{shapes, N}, V, nc, force_greedy, part, filt, wa);
   else if (win)
     hipLaunchKernelGGL((k_filter_win<TreeRows>), dim3(B * R), dim3(64), 0, st, temp, top_k,
                        top_p, TreeRows{shape}, V, nc, force_greedy, part, filt, wa);
-  if (filtered && per_seq)
-    hipLaunchKernelGGL((k_filter<T, kAligned, TreeRowsSeq>), dim3(B * R), dim3(kFilterThreads), 0, st,
-                       t, d, temp, top_k, top_p, TreeRowsSeq{shapes, N}, V, nc, force_greedy, part, filt,
-                       wa);
+  if (win && per_seq)
+    hipLaunchKernelGGL((k_filter_list<T, kAligned, TreeRowsSeq>), dim3(fgrid), dim3(kFilterThreads), 0,
+                       st, t, d, temp, top_k, top_p, TreeRowsSeq{shapes, N}, V, nc, force_greedy, part,
+                       filt, wa);
+  else if (win)
+    hipLaunchKernelGGL((k_filter_list<T, kAligned, TreeRows>), dim3(fgrid), dim3(kFilterThreads), 0, st,
+                       t, d, temp, top_k, top_p, TreeRows{shape}, V, nc, force_greedy, part, filt, wa);
+  else if (filtered && per_seq)
+    hipLaunchKernelGGL((k_filter<T, kAligned, TreeRowsSeq>), dim3(fgrid), dim3(kFilterThreads), 0, st,
+                       t, d, temp, top_k, top_p, TreeRowsSeq{shapes, N}, V, nc, force_greedy, part, filt);
   else if (filtered)
-    hipLaunchKernelGGL((k_filter<T, kAligned, TreeRows>), dim3(B * R), dim3(kFilterThreads), 0, st, t,
-                       d, temp, top_k, top_p, TreeRows{shape}, V, nc, force_greedy, part, filt, wa);
+    hipLaunchKernelGGL((k_filter<T, kAligned, TreeRows>), dim3(fgrid), dim3(kFilterThreads), 0, st, t,
+                       d, temp, top_k, top_p, TreeRows{shape}, V, nc, force_greedy, part, filt);
   const int key16 = sizeof(T) == 2 ? 1 : 0;
   hipLaunchKernelGGL(k_tree_decide, dim3(B), dim3(kDecideThreads), 0, st, tok, uni, temp, shape, shapes,
                      R, V, nc, force_greedy, part, filt, key16, xd, rowstat, dec, state, out_tok,
