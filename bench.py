@@ -90,6 +90,12 @@ def parse():
                         "(K pages [D/8,16,8]) against LIB, a build with SV_K_TOKEN_MAJOR=1 "
                         "(token-major K pages [16,D]) given the same cache permuted; the "
                         "outputs must agree bit for bit")
+    p.add_argument("--traffic-record", nargs=4, default=None,
+                   metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                   help="instead of the bench (no GPU needed): write "
+                        "profiles/attn_llama8b_b64_traffic.json from four rocprofv3 --pmc output "
+                        "folders: FETCH_SIZE and WRITE_SIZE of this bench at its defaults, then of "
+                        "--copy-calibration 1024")
     p.add_argument("--no-probe", action="store_true",
                    help="skip the streaming-read probe in the bench line (measured_peak null)")
     p.add_argument("--sets", type=int, default=3, help="rotating logit sets")
@@ -116,6 +122,9 @@ def parse():
 
 def main():
     args = parse()
+    if args.traffic_record:
+        traffic_record(*args.traffic_record)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the verify step here runs on a single "
               "MI355X (no collectives); --gpus %d is not supported." % args.gpus, file=sys.stderr)
@@ -607,6 +616,60 @@ def k_layout_ab(args, other_lib):
             del g
     print(json.dumps({"k_layout_ab": {"workload": cfg.name, "B": B, "K": K,
                                       "call_us": times, "outputs_identical": True}}), flush=True)
+
+
+def _counter_means(folder):
+    """Mean value per kernel name of the one counter in a rocprofv3 --pmc
+    output folder (its counter_collection CSV)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection CSV under %s" % folder)
+    acc = {}
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def traffic_record(fetch_dir, write_dir, cfetch_dir, cwrite_dir):
+    """HBM bytes per attention call from the FETCH_SIZE / WRITE_SIZE counter
+    runs, each scaled by the same counter on a 1 GiB device copy (reads and
+    writes 1 GiB per dispatch), with a hash of the attention sources: bench.py
+    reports the figure only while the sources still hash to it."""
+    copy_bytes = 1 << 30
+    cf = [v for k, v in _counter_means(cfetch_dir).items() if "copyBuffer" in k]
+    cw = [v for k, v in _counter_means(cwrite_dir).items() if "copyBuffer" in k]
+    if not cf or not cw:
+        raise SystemExit("no copy kernel in the calibration folders")
+    fscale = copy_bytes / (cf[0] * 1024.0)
+    wscale = copy_bytes / (cw[0] * 1024.0)
+    fetch, write = _counter_means(fetch_dir), _counter_means(write_dir)
+    per = {}
+    for name, fv in fetch.items():
+        if "sv::" not in name:
+            continue
+        short = name.split("(")[0].replace("void ", "")
+        wv = write.get(name, 0.0)
+        per[short] = {"fetch_kib": round(fv, 3), "write_kib": round(wv, 3),
+                      "fetch_bytes": int(round(fv * 1024 * fscale)),
+                      "write_bytes": int(round(wv * 1024 * wscale))}
+    attn = [k for k in per if k.startswith("sv::k_attn_stream")]
+    if not attn:
+        raise SystemExit("no attention kernel in %s" % fetch_dir)
+    files = ["speculative_decoding_verification_verify_amd/csrc/verify_attn.hip",
+             "speculative_decoding_verification_verify_amd/csrc/common.h"]
+    rec = {"workload": "llama8b_b64 (B=64 K=7, 32q/8kv, D=128, ctx U[2048,8192], seed 2024)",
+           "call": "spec_verify_attn = k_attn_stream + k_attn_stream_combine",
+           "source_files": files, "source_sha256_16": _files_hash(files),
+           "fetch_scale": fscale, "write_scale": wscale,
+           "bytes_per_launch": sum(per[k]["fetch_bytes"] + per[k]["write_bytes"] for k in attn),
+           "summary": "profiles/verify_step_llama8b_b64_counters.md", "per_kernel": per}
+    out = os.path.join(ROOT, "profiles", "attn_llama8b_b64_traffic.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps({k: rec[k] for k in ("bytes_per_launch", "fetch_scale", "write_scale")}))
 
 
 def copy_calibration(mib):

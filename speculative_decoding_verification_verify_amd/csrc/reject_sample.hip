@@ -172,8 +172,9 @@ struct RowFilter {
 //    the same window.
 //  * top-p alone: kWinPKeys keys from kWinPBelow keys under the threshold
 //    k_win_prep estimates from kPrepLines runs (the value where the sample's
-//    own mass from the top reaches top_p): the row's maximum is usually
-//    seven binades above the window's lowest value at most.
+//    own mass from the top reaches top_p).  The sample holds few of the
+//    entries that carry the mass, so the estimate can miss by a binade; the
+//    window reaches two binades under it and six above.
 // The threshold and every value above it are usually inside; an entry above
 // the window sends the row to k_filter's radix passes.  k_filter_win reads
 // a row's thresholds from the counts instead of passes over the row.
@@ -182,7 +183,7 @@ constexpr int kWinPKeys = 1024;
 constexpr int kWinSlot = 1024;         // counts kept per sweep block (the larger window)
 constexpr int kWinTopMargin = 192;
 constexpr int kWinKBelow = 128;
-constexpr int kWinPBelow = 128;
+constexpr int kWinPBelow = 256;
 constexpr int kWinLines = 8;           // runs of 64 entries sampled by each sweep block (top-k)
 constexpr int kPrepLines = 32;         // runs sampled by k_win_prep (top-p)
 constexpr uint32_t kWinMinKey = 0x80;  // just above the key of -inf (0x7F)
