@@ -164,17 +164,17 @@ struct RowFilter {
 
 // The window a filtered sweep counts (bf16 rows of sampling sequences with
 // a top-k or top-p filter): consecutive 16-bit keys (the keys of one binade
-// of bf16 values are 128 in a row), placed from a fixed sample of the row:
+// of bf16 values are 128 in a row), placed from the largest entry of
+// kWinLines 64-entry runs spread evenly over the row (every sweep block of
+// the row reads the same runs and derives the same window):
 //  * top-k (with or without top-p): kWinKeys keys, from kWinKBelow keys under
-//    the largest entry of kWinLines 64-entry runs spread evenly over the row
-//    (k up to V / 256; all kWinKeys keys for larger k) to kWinTopMargin keys
-//    above it.  Every sweep block of the row reads the same runs and derives
-//    the same window.
-//  * top-p alone: kWinPKeys keys from kWinPBelow keys under the threshold
-//    k_win_prep estimates from kPrepLines runs (the value where the sample's
-//    own mass from the top reaches top_p).  The sample holds few of the
-//    entries that carry the mass, so the estimate can miss by a binade; the
-//    window reaches two binades under it and six above.
+//    the sample's largest entry (k up to V / 256; all kWinKeys keys for
+//    larger k) to kWinTopMargin keys above it.
+//  * top-p alone: kWinPKeys keys up to kWinPTopMargin keys above the
+//    sample's largest entry, so six binades under it.  A top-p threshold
+//    lies under the bulk of the row's mass, which sits near the largest
+//    entries; the window holds it unless the row's mass is spread over
+//    values close to zero (then the radix passes take the row).
 // The threshold and every value above it are usually inside; an entry above
 // the window sends the row to k_filter's radix passes.  k_filter_win reads
 // a row's thresholds from the counts instead of passes over the row.
@@ -182,10 +182,9 @@ constexpr int kWinKeys = 512;
 constexpr int kWinPKeys = 1024;
 constexpr int kWinSlot = 1024;         // counts kept per sweep block (the larger window)
 constexpr int kWinTopMargin = 192;
+constexpr int kWinPTopMargin = 256;
 constexpr int kWinKBelow = 128;
-constexpr int kWinPBelow = 256;
-constexpr int kWinLines = 8;           // runs of 64 entries sampled by each sweep block (top-k)
-constexpr int kPrepLines = 32;         // runs sampled by k_win_prep (top-p)
+constexpr int kWinLines = 8;           // runs of 64 entries sampled by each sweep block
 constexpr uint32_t kWinMinKey = 0x80;  // just above the key of -inf (0x7F)
 
 // Where the filtered sweep leaves its window (null pointers: no window).
@@ -465,6 +464,15 @@ __device__ __forceinline__ uint32_t topk_window(float sm, int tk, int V) {
   return kbase | (ktop << 16);
 }
 
+// The top-p window (see kWinPKeys) from the maximum sm of the row's sample:
+// lowest key | highest key << 16.
+__device__ __forceinline__ uint32_t topp_window(float sm) {
+  const uint32_t ksm = key32_of(sm) >> 16;
+  const uint32_t ktop = min(ksm + (uint32_t)kWinPTopMargin, 0xFFFFu);
+  const uint32_t kbase = ktop >= kWinMinKey + (kWinPKeys - 1) ? ktop - (kWinPKeys - 1) : kWinMinKey;
+  return kbase | ((kbase + (kWinPKeys - 1)) << 16);
+}
+
 // Vector index of sampled vector i of a row of nvec vectors: runs of 8
 // vectors (64 bf16 entries, one 128-byte line), nruns of them spread evenly.
 __device__ __forceinline__ int sample_vec(int i, int nruns, int nvec) {
@@ -499,13 +507,10 @@ __device__ __forceinline__ void sweep_window_block(const uint16_t* __restrict__ 
   const bool live = chunk < nc;
   const int base = chunk * kSweepChunk + lane * VN;
   const bool full = (chunk + 1) * kSweepChunk <= V;
-  // Top-k: the window from this block's read of the sample runs; top-p
-  // alone: from k_win_prep.  Requested ahead of the chunk's rows, so the
-  // window is ready while they are still arriving.
+  // The window from this block's read of the sample runs, requested ahead
+  // of the chunk's rows, so it is ready while they are still arriving.
   float xs[VN];
-  uint32_t pwin = 0u;
-  if (k_on) Vec16<uint16_t>::load(src + (size_t)sample_vec(lane, kWinLines, V / VN) * VN, xs);
-  else pwin = wa.wwin[row];
+  Vec16<uint16_t>::load(src + (size_t)sample_vec(lane, kWinLines, V / VN) * VN, xs);
   float x[IT][VN];
   if (live) {
     if (full) {
@@ -519,15 +524,12 @@ __device__ __forceinline__ void sweep_window_block(const uint16_t* __restrict__ 
 #pragma unroll
   for (int i = 0; i < kWinSlot / kThreads; ++i) s_hist[tid + i * kThreads] = 0u;
   if (tid == 0) s_flag = 0u;
-  uint32_t win = pwin;
-  if (k_on) {
-    float sm = xs[0];
+  float sm = xs[0];
 #pragma unroll
-    for (int k = 1; k < VN; ++k) sm = fmaxf(sm, xs[k]);
+  for (int k = 1; k < VN; ++k) sm = fmaxf(sm, xs[k]);
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) sm = fmaxf(sm, __shfl_xor(sm, off, 64));
-    win = topk_window(sm, tk, V);
-  }
+  for (int off = 32; off > 0; off >>= 1) sm = fmaxf(sm, __shfl_xor(sm, off, 64));
+  const uint32_t win = k_on ? topk_window(sm, tk, V) : topp_window(sm);
   const uint32_t kbase = win & 0xFFFFu, ktop = win >> 16;
   if (live) record_draft_logits<uint16_t>(rows, b, j, chunk, lane, is_draft, V, x, dtok, xd);
   float flo, fhi;
@@ -599,7 +601,7 @@ __device__ __forceinline__ void sweep_window_block(const uint16_t* __restrict__ 
   }
   if (tid == 0) {
     wa.wflag[(size_t)row * wa.nblk + blockIdx.y] = s_flag;
-    if (k_on && blockIdx.y == 0) wa.wwin[row] = win;
+    if (blockIdx.y == 0) wa.wwin[row] = win;
   }
 }
 
@@ -1748,95 +1750,6 @@ __device__ __forceinline__ double wave_sum_d(double x) {
   return (readlane_d(x, 0) + readlane_d(x, 16)) + (readlane_d(x, 32) + readlane_d(x, 48));
 }
 
-// Sum of a float over the wave in every lane, by DPP moves inside rows of
-// 16 lanes and the four row sums in a fixed order (each step is symmetric, so
-// every lane ends with the same value).
-__device__ __forceinline__ float wave_sum_f(float x) {
-  x += dpp_f<kDppXor1>(x);
-  x += dpp_f<kDppXor2>(x);
-  x += dpp_f<kDppHalfMirror>(x);
-  x += dpp_f<kDppRowMirror>(x);
-  return (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)) +
-          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16))) +
-         (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32)) +
-          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48)));
-}
-
-// The sample's estimate of the top-p threshold: the largest 16-bit key whose
-// set {key(x) >= k} holds at least tp of the sample's mass 2^(x c - sm c),
-// found by bisection over the keys on one wave (each lane holds
-// kPrepLines * 64 / 64 sampled values; fixed-order sums).
-__device__ __forceinline__ uint32_t sample_topp_key(const float* __restrict__ s_samp, float sm, float c,
-                                                    float tp, int lane) {
-  constexpr int PER = kPrepLines;
-  float w[PER];
-  uint32_t kk[PER];
-  float tot = 0.f;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const float x = s_samp[lane + 64 * i];
-    kk[i] = key32_of(x) >> 16;
-    w[i] = exp2_dev(__builtin_fmaf(x, c, -sm * c));
-    tot += w[i];
-  }
-  tot = wave_sum_f(tot);
-  const float target = tp * tot;
-  // The answer lies between the sample's smallest key (the whole mass) and
-  // its largest (the mass there is at least the top value's).
-  uint32_t kmin = 0xFFFFu;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) kmin = min(kmin, kk[i]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, 64));
-  uint32_t lo = kmin, hi = (key32_of(sm) >> 16) + 1u;  // mass(lo) >= target; hi: past the keys
-  while (hi - lo > 1u) {
-    const uint32_t mid = (lo + hi) >> 1;
-    float m = 0.f;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) m += kk[i] >= mid ? w[i] : 0.f;
-    if (wave_sum_f(m) >= target) lo = mid;
-    else hi = mid;
-  }
-  return lo;
-}
-
-// k_win_prep: grid (B * rows.count()), block 256: the window of each bf16 row
-// of a sequence with top-p and no top-k (see kWinKeys), from kPrepLines runs
-// of the row: wwin[row] = lowest key | highest key << 16.
-template <class Rows>
-__global__ __launch_bounds__(kPrepLines * 8) void k_win_prep(
-    const uint16_t* __restrict__ tgt, const uint16_t* __restrict__ drf, const float* __restrict__ temp,
-    Rows rows, int V, int force_greedy, WinArgs wa) {
-  constexpr int VN = Vec16<uint16_t>::N;
-  __shared__ float s_samp[kPrepLines * 64];
-  const int R = rows.count();
-  const int row = blockIdx.x;
-  const int b = row / R;
-  const int j = row - b * R;
-  const int tid = threadIdx.x, lane = tid & 63;
-  if (!rows.valid(b, j)) return;
-  const float t = temp_of(temp, b, force_greedy);
-  const int tk = wa.top_k ? wa.top_k[b] : 0;
-  const float tp = wa.top_p ? wa.top_p[b] : 1.f;
-  if (!(t > 0.f) || (tk > 0 && tk < V) || !(tp > 0.f && tp < 1.f)) return;
-  const uint16_t* src = (rows.is_draft(j) ? drf : tgt) + rows.row(b, j) * (size_t)V;
-  float xs[VN];
-  Vec16<uint16_t>::load(src + (size_t)sample_vec(tid, kPrepLines, V / VN) * VN, xs);
-#pragma unroll
-  for (int k = 0; k < VN; ++k) s_samp[tid * VN + k] = xs[k];
-  __syncthreads();
-  if (tid >= 64) return;
-  float sm = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kPrepLines; ++i) sm = fmaxf(sm, s_samp[lane + 64 * i]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) sm = fmaxf(sm, __shfl_xor(sm, off, 64));
-  const uint32_t kt = sample_topp_key(s_samp, sm, kLog2e / t, tp, lane);
-  uint32_t kbase = kt >= kWinMinKey + kWinPBelow ? kt - kWinPBelow : kWinMinKey;
-  kbase = min(kbase, 0xFFFFu - (kWinPKeys - 1));
-  if (lane == 0) wa.wwin[row] = kbase | ((kbase + (kWinPKeys - 1)) << 16);
-}
-
 // One wave walks `cnt` masses (mass(i)) in order: returns the first index
 // whose running sum from `base` exceeds `target` (or -1) and leaves in `base`
 // the running sum before it; `lastpos` gets the last index of positive mass
@@ -2698,10 +2611,6 @@ static hipError_t launch_all(const void* tgt, const void* drf, const int32_t* dt
   const bool win = filtered && win_ws && kAligned && sizeof(T) == 2;
   const WinArgs wa = win ? win_args(p, ws, top_k, top_p, V) : WinArgs{};
   const dim3 sgrid(B * (force_greedy ? K + 1 : R), (nc + 3) / 4);
-  if (win && top_p)
-    hipLaunchKernelGGL((k_win_prep<ChainRows>), dim3(B * R), dim3(kPrepLines * 8), 0, st,
-                       reinterpret_cast<const uint16_t*>(t), reinterpret_cast<const uint16_t*>(d), temp,
-                       ChainRows{K}, V, force_greedy, wa);
   if (win)
     hipLaunchKernelGGL((k_sweep<T, kAligned, ChainRows, true>), sgrid, dim3(kThreads), 0, st, t, d, dtok,
                        temp, ChainRows{K}, B, V, nc, force_greedy, part, xd, pcnt, wa);
@@ -2887,10 +2796,6 @@ static hipError_t launch_tree(const void* tgt, const void* drf, const TreeShape&
   const dim3 sgrid(B * (force_greedy ? N : R), (nc + 3) / 4);
   if (per_seq) {
     hipLaunchKernelGGL(k_tree_shapes, dim3((B + 63) / 64), dim3(64), 0, st, dparents, B, N, shapes);
-    if (win && top_p)
-      hipLaunchKernelGGL((k_win_prep<TreeRowsSeq>), dim3(B * R), dim3(kPrepLines * 8), 0, st,
-                         reinterpret_cast<const uint16_t*>(t), reinterpret_cast<const uint16_t*>(d),
-                         temp, TreeRowsSeq{shapes, N}, V, force_greedy, wa);
     if (win)
       hipLaunchKernelGGL((k_sweep<T, kAligned, TreeRowsSeq, true>), sgrid, dim3(kThreads), 0, st, t, d, tok,
                          temp, TreeRowsSeq{shapes, N}, B, V, nc, force_greedy, part, xd, rcnt, wa);
@@ -2898,10 +2803,6 @@ static hipError_t launch_tree(const void* tgt, const void* drf, const TreeShape&
       hipLaunchKernelGGL((k_sweep<T, kAligned, TreeRowsSeq>), sgrid, dim3(kThreads), 0, st, t, d, tok, temp,
                          TreeRowsSeq{shapes, N}, B, V, nc, force_greedy, part, xd, rcnt, WinArgs{});
   } else {
-    if (win && top_p)
-      hipLaunchKernelGGL((k_win_prep<TreeRows>), dim3(B * R), dim3(kPrepLines * 8), 0, st,
-                         reinterpret_cast<const uint16_t*>(t), reinterpret_cast<const uint16_t*>(d),
-                         temp, TreeRows{shape}, V, force_greedy, wa);
     if (win)
       hipLaunchKernelGGL((k_sweep<T, kAligned, TreeRows, true>), sgrid, dim3(kThreads), 0, st, t, d, tok,
                          temp, TreeRows{shape}, B, V, nc, force_greedy, part, xd, rcnt, wa);
