@@ -90,6 +90,12 @@ def parse():
                         "(K pages [D/8,16,8]) against LIB, a build with SV_K_TOKEN_MAJOR=1 "
                         "(token-major K pages [16,D]) given the same cache permuted; the "
                         "outputs must agree bit for bit")
+    p.add_argument("--lib", default="", metavar="LIB",
+                   help="load LIB instead of the in-tree library (another build of it)")
+    p.add_argument("--wg-timeline", action="store_true",
+                   help="after the bench, one more attention call with a library built with "
+                        "SV_ATTN_TIMESTAMPS=1 (--lib): add the per-workgroup timeline of "
+                        "k_attn_stream to the line as wg_timeline")
     p.add_argument("--traffic-record", nargs=4, default=None,
                    metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                    help="instead of the bench (no GPU needed): write "
@@ -141,6 +147,9 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
+    if args.lib:
+        lib = os.path.abspath(args.lib)
+        sv.lib_path = lambda: lib
     sv.load()
     if args.peak_probe:
         print(json.dumps(read_peak(sv)), flush=True)
@@ -492,7 +501,56 @@ def main():
         "mean_accept_len": round(tokens / args.steps / B, 4),
         "wall_s": round(wall, 3),
     }
+    if args.wg_timeline:
+        attn_call()
+        torch.cuda.synchronize()
+        rec["wg_timeline"] = wg_timeline(sv.load())
     print(json.dumps(rec), flush=True)
+
+
+def wg_timeline(lib):
+    """Summary of the per-wave stamps of the last k_attn_stream launch (a
+    build with SV_ATTN_TIMESTAMPS=1; the device clock runs at 100 MHz).  Per
+    workgroup: its end (last merge end, from the earliest start of any
+    workgroup), the prologue (start to segment loop), the waves' wait at the
+    end-of-segment barrier (for each segment, the mean over waves of the
+    slowest wave's pair-loop end minus their own) and the merges (slowest
+    pair-loop end to merge end), summed over its segments.  Workgroup w is
+    counted on XCD w mod 8 (round-robin dispatch)."""
+    import ctypes
+    if not hasattr(lib, "spec_attn_timestamps"):
+        raise SystemExit("--wg-timeline needs a library built with SV_ATTN_TIMESTAMPS=1 (--lib)")
+    fn = lib.spec_attn_timestamps
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    fn.restype = ctypes.c_size_t
+    n = fn(None, 0)
+    buf = np.zeros(n // 8, dtype=np.uint64)
+    if fn(buf.ctypes.data_as(ctypes.c_void_p), n) != n:
+        raise SystemExit("spec_attn_timestamps failed")
+    ev = 24
+    nw = int(buf[ev - 2])
+    a = buf.reshape(-1, nw, ev).astype(np.int64)
+    wgs = [w for w in range(a.shape[0]) if a[w, 0, ev - 1] > 0]
+    t0 = min(int(a[w, :, 0].min()) for w in wgs)
+    end, pro, wait, merge, segs = [], [], [], [], []
+    for w in wgs:
+        k = min(int(a[w, 0, ev - 1]), (ev - 4) // 2)
+        le = np.array([a[w, :, 2 + 2 * j] for j in range(k)])     # [segment, wave]
+        me = np.array([a[w, :, 3 + 2 * j] for j in range(k)])
+        end.append((me[-1].max() - t0) / 100.0)
+        pro.append((a[w, :, 1].max() - a[w, :, 0].min()) / 100.0)
+        wait.append(float((le.max(1)[:, None] - le).mean(1).sum()) / 100.0)
+        merge.append(float((me.max(1) - le.max(1)).sum()) / 100.0)
+        segs.append(int(a[w, 0, ev - 1]))
+    end = np.array(end)
+    xcd = np.array(wgs) % 8
+    r = lambda v: round(float(v), 1)
+    return {"workgroups": len(wgs), "waves_per_workgroup": nw, "kernel_span_us": r(end.max()),
+            "wg_end_us": {"mean": r(end.mean()), "min": r(end.min()), "max": r(end.max()),
+                          "p10": r(np.percentile(end, 10)), "p90": r(np.percentile(end, 90))},
+            "wg_end_mean_by_xcd_us": [r(end[xcd == x].mean()) for x in range(8) if (xcd == x).any()],
+            "prologue_mean_us": r(np.mean(pro)), "barrier_wait_mean_us": r(np.mean(wait)),
+            "merge_mean_us": r(np.mean(merge)), "segments_mean": r(np.mean(segs))}
 
 
 def read_peak(sv, mib=2048, reps=5, sizes=None):

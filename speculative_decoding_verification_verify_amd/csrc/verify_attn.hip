@@ -72,6 +72,24 @@ constexpr int kStreamMaxWG = 1024;   // workspace is sized for this many workgro
 #define SV_ATTN_WAVES_1T 2      // waves per SIMD the one-tile kernel must fit
 #endif
 
+// Measurement build only (build.py --out ... --define SV_ATTN_TIMESTAMPS=1):
+// each wave of k_attn_stream stamps the device's constant 100 MHz clock at
+// its start, when its segment loop starts, and at the end of each segment's
+// pair loop and of its merge; spec_attn_timestamps copies the stamps of the
+// last launch to the host.  Per wave, kTsEv words: [0] start, [1] loop
+// start, [2 + 2k] / [3 + 2k] pair-loop end / merge end of segment k (k < 10),
+// [kTsEv - 2] waves per workgroup, [kTsEv - 1] segments.
+#ifndef SV_ATTN_TIMESTAMPS
+#define SV_ATTN_TIMESTAMPS 0
+#endif
+#if SV_ATTN_TIMESTAMPS
+constexpr int kTsEv = 24;
+constexpr int kTsSeg = (kTsEv - 4) / 2;
+__device__ unsigned long long g_attn_ts[kStreamMaxWG * 8 * kTsEv];
+#define SV_TS(slot) \
+  do { if (lane == 0) tsp[slot] = __builtin_amdgcn_s_memrealtime(); } while (0)
+#endif
+
 __device__ __forceinline__ bf16x8 load_kv(const uint16_t* p) {
   const u32x4* q = reinterpret_cast<const u32x4*>(p);
 #if SV_ATTN_NT_LOADS
@@ -473,6 +491,12 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
   const int l32 = lane & 31, hh = lane >> 5;
   const int G = Hq / Hkv;
   const int rows = G * K1;
+#if SV_ATTN_TIMESTAMPS
+  unsigned long long* tsp = g_attn_ts + ((size_t)w * NW + wave) * kTsEv;
+  int tsk = 0;
+  SV_TS(0);
+  if (lane == 0) { tsp[kTsEv - 2] = NW; tsp[kTsEv - 1] = 0ull; }
+#endif
 
   // The share [u0, u1) needs the total work U, and its first item's
   // sequence b with that sequence's first item off_b.  The host bounds the
@@ -561,6 +585,9 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
     window_rows_store<D, kStreamThreads>(stg, cur, K1, s_win[0], tid);
   }
   __syncthreads();
+#if SV_ATTN_TIMESTAMPS
+  SV_TS(1);
+#endif
 
   while (true) {
     Seg nxt;
@@ -640,6 +667,9 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
       load_v<D>(vf, nblk, vc, Hkv, nxt.g, l32, hh);
     }
 
+#if SV_ATTN_TIMESTAMPS
+    if (tsk < kTsSeg) SV_TS(2 + 2 * tsk);
+#endif
     // The next segment's window rows, staged before this segment's merge
     // (whose barrier orders them before their use).  Requested only after
     // the pair loop: held across it, they would push the loop past the
@@ -718,6 +748,11 @@ __global__ __launch_bounds__(64 * stream_waves<NT>(), NT == 1 ? SV_ATTN_WAVES_1T
       __syncthreads();
     }
 
+#if SV_ATTN_TIMESTAMPS
+    if (tsk < kTsSeg) SV_TS(3 + 2 * tsk);
+    ++tsk;
+    if (lane == 0) tsp[kTsEv - 1] = tsk;
+#endif
     if (!has_next) break;
     cur = nxt;
     wbuf ^= 1;
@@ -1020,6 +1055,21 @@ static hipError_t launch_stream(const void* q, void* kc, void* vc, const int32_t
 }
 
 }  // namespace sv
+
+#if SV_ATTN_TIMESTAMPS
+// The stamps of the last k_attn_stream launch (see SV_ATTN_TIMESTAMPS):
+// copies min(bytes, their size) bytes to host memory; returns the size.
+extern "C" size_t spec_attn_timestamps(void* host, size_t bytes) {
+  const size_t n = sizeof(sv::g_attn_ts);
+  if (host && bytes) {
+    if (hipDeviceSynchronize() != hipSuccess) return 0;
+    if (hipMemcpyFromSymbol(host, HIP_SYMBOL(sv::g_attn_ts), bytes < n ? bytes : n, 0,
+                            hipMemcpyDeviceToHost) != hipSuccess)
+      return 0;
+  }
+  return n;
+}
+#endif
 
 extern "C" size_t spec_verify_attn_workspace_bytes(int B, int K, int Hq, int Hkv, int D,
                                                    int max_kv_len) {

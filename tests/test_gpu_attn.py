@@ -166,6 +166,24 @@ def test_determinism(gpu_lib, dev):
     assert np.array_equal(o1, o2)
 
 
+def test_determinism_at_serving_size(gpu_lib, dev):
+    """Three calls at the serving size (many partial segments merged by the
+    combine kernel) give the same bits.  One tile (the chain) and two tiles
+    (8 query heads per KV head)."""
+    import torch
+    c = CONFIGS["llama8b_b64"]
+    for Hq in (c.Hq, 2 * c.Hq):
+        _say("attn determinism B=%d Hq=%d" % (c.B, Hq))
+        t = make_attn_inputs_device(43, c.B, c.K, Hq, c.Hkv, c.D, c.ctx, dev)
+        outs = [gpu_lib.verify_attn(t["q"], t["k_cache"], t["v_cache"], t["block_table"],
+                                    t["kv_len"]) for _ in range(3)]
+        torch.cuda.synchronize()
+        for o in outs[1:]:
+            assert torch.equal(o, outs[0])
+        del t, outs
+        torch.cuda.empty_cache()
+
+
 def test_empty_batch_and_errors(gpu_lib, dev):
     import torch
     q = torch.zeros((0, 8, 32, 128), dtype=torch.bfloat16, device=dev)
