@@ -425,6 +425,10 @@ def main():
                          "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4)}}
     rej_us = float(rej_ms * 1e3)
     rej_gbs = rej_bytes / (rej_us * 1e-6) / 1e9
+    # Both calls of the step against the HBM peak, and the smaller of the two.
+    by_call = {"attn": round(achieved / PEAK_HBM_GBS, 4), "reject": round(rej_gbs / PEAK_HBM_GBS, 4)}
+    roofline["frac_by_call"] = by_call
+    roofline["min_frac_by_call"] = min(by_call.values())
     # The rows the method itself needs: drafts after the first rejection are
     # discarded, so a chain needs target rows 0..n and draft rows
     # 0..min(n, K-1) (greedy: target rows 0..n), averaged over the sets the
