@@ -286,8 +286,9 @@ int spec_reject_sample_noalloc(const void* target_logits, const void* draft_logi
  * workspace: at least spec_reject_sample_workspace_bytes(B, K, V) bytes;
  *   with spec_reject_sample_filtered_workspace_bytes(B, K, V) bytes a bf16
  *   call whose rows start on 16-byte boundaries (V % 8 == 0) also counts, in
- *   its one sweep over the rows, every value of a window of 1024 bf16 keys
- *   under a fixed sample's maximum, and each filtered row whose thresholds
+ *   its one sweep over the rows, every value of a window of bf16 keys placed
+ *   from a fixed sample's maximum (512 keys with top-k, 1024 for top-p
+ *   alone, reaching six binades under it), and each filtered row whose thresholds
  *   fall inside that window needs no pass of its own; other rows (and every
  *   row with the smaller workspace, or fp32 logits) take the filter's radix
  *   passes: one or two extra reads of the row per active filter (bf16; up
