@@ -522,6 +522,7 @@ def wg_timeline(lib):
     pair-loop end to merge end), summed over its segments.  Workgroup w is
     counted on XCD w mod 8 (round-robin dispatch)."""
     import ctypes
+    import heapq
     if not hasattr(lib, "spec_attn_timestamps"):
         raise SystemExit("--wg-timeline needs a library built with SV_ATTN_TIMESTAMPS=1 (--lib)")
     fn = lib.spec_attn_timestamps
@@ -549,12 +550,27 @@ def wg_timeline(lib):
     end = np.array(end)
     xcd = np.array(wgs) % 8
     r = lambda v: round(float(v), 1)
+    # Replay with balancing: each workgroup keeps its own measured rate; the
+    # last fraction f of the work is cut into chunks of `pairs` (in units of
+    # a share's pairs per workgroup: the shares are equal), each taken by the
+    # workgroup that is free first, at a fixed cost `cost_us` per chunk.
+    share = 1.0 / len(end)
+    rate = share / end                       # work fraction per microsecond
+    replay = {}
+    for f, nchunk, cost in ((0.1, 512, 1.0), (0.1, 512, 2.0), (0.1, 512, 4.0), (0.2, 256, 2.0)):
+        heap = [((1.0 - f) * share / rate[i], i) for i in range(len(end))]
+        heapq.heapify(heap)
+        for _ in range(nchunk):
+            t, i = heapq.heappop(heap)
+            heapq.heappush(heap, (t + f / nchunk / rate[i] + cost, i))
+        replay["f%.1f_chunks%d_cost%.0fus" % (f, nchunk, cost)] = r(max(t for t, _ in heap))
     return {"workgroups": len(wgs), "waves_per_workgroup": nw, "kernel_span_us": r(end.max()),
             "wg_end_us": {"mean": r(end.mean()), "min": r(end.min()), "max": r(end.max()),
                           "p10": r(np.percentile(end, 10)), "p90": r(np.percentile(end, 90))},
             "wg_end_mean_by_xcd_us": [r(end[xcd == x].mean()) for x in range(8) if (xcd == x).any()],
             "prologue_mean_us": r(np.mean(pro)), "barrier_wait_mean_us": r(np.mean(wait)),
-            "merge_mean_us": r(np.mean(merge)), "segments_mean": r(np.mean(segs))}
+            "merge_mean_us": r(np.mean(merge)), "segments_mean": r(np.mean(segs)),
+            "balanced_end_us_replay": replay}
 
 
 def read_peak(sv, mib=2048, reps=5, sizes=None):
