@@ -132,11 +132,15 @@ def test_llama8b_vocab(gpu_lib, dev):
 
 @pytest.mark.parametrize("ws", ["window", "plain"])
 @pytest.mark.parametrize("top_k,top_p,temp", [(50, 1.0, 1.0), (0, 0.9, 1.0), (20, 0.8, 0.6),
-                                               (0, 0.9, 1.3), (0, 0.5, 1.0)])
+                                               (0, 0.9, 1.3), (0, 0.5, 1.0), (1, 1.0, 1.0),
+                                               (501, 1.0, 1.0), (502, 1.0, 1.0), (0, 0.99, 0.25)])
 def test_llama8b_vocab_window_and_radix(gpu_lib, dev, top_k, top_p, temp, ws):
     """The serving vocabulary through both ways of taking the thresholds:
     counted in the sweep's window (the thresholds of these rows fall inside
-    it) and the filter's radix passes (the plain workspace)."""
+    it) and the filter's radix passes (the plain workspace).  k = 501 and
+    502 sit on either side of V / 256, where the top-k window changes from
+    one binade under the sample's largest entry to all 512 keys under the
+    top; T = 0.25 puts the top-p edge next to the largest entries."""
     c = CONFIGS["llama8b_b64"]
     _case(gpu_lib, dev, 13, 16, c.K, c.V, top_k, top_p, temp=temp, ws=ws)
 
